@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Benchmark: GDN tree verify + persist per layer call on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config batched]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+gdn_tree_plan, then gdn_tree_verify and gdn_tree_persist for every layer of
+the workload ("batched": 32 sequences x one layer; "stress": 64 sequences x 48
+layers).  Inputs and states are resident in HBM before timing starts.  To keep
+the 256 MB Infinity Cache from serving repeated reads, the timed loop rotates
+through R independent copies of the states and inputs (each layer of the
+workload is its own copy), so consecutive steps never touch the same bytes.
+
+Prints ONE JSON line.  `value` = tree nodes verified per second per layer call
+(plan + verify + persist); `roofline` describes the dominant kernel, timed with
+HIP events on the stream it runs on; `cpu_baseline` times the fp64 CPU oracle
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="batched")
+    ap.add_argument("--rotate", type=int, default=0, help="independent copies (default: >= 512 MB in flight)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def algorithmic_bytes(cfg, T, path_lens, s_in):
+    """Bytes the method must move per layer call."""
+    B, Hk, Hv, D = cfg.num_seqs, cfg.num_k_heads, cfg.num_v_heads, cfg.head_dim
+    state = B * Hv * D * D * 4
+    verify = state + T * (2 * Hk * D + Hv * D) * s_in + T * Hv * 8 + T * Hv * D * 4 + 4 * (T + 2 * B + 1)
+    P = int(np.sum(path_lens))
+    persist = 2 * state + P * (Hk * D + Hv * D) * s_in + P * Hv * 8 + 4 * B
+    return verify, persist
+
+
+def flops(cfg, trees, path_lens):
+    """Algorithmic flops: 7 D^2 per (node, head) for verify (S k, S q, update),
+    5 D^2 per (path node, head) for persist."""
+    D, Hv = cfg.head_dim, cfg.num_v_heads
+    T = sum(len(t) for t in trees)
+    return 7 * D * D * Hv * T, 5 * D * D * Hv * int(np.sum(path_lens))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU; --gpus %d is not supported "
+                                   "(the path shards with no exchange; see DESIGN.md)" % args.gpus}))
+        sys.exit(2)
+    import torch
+    import gated_deltanet_tree_amd as G
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU"}))
+        sys.exit(1)
+    G.load_library()
+    cfg = W.get_config(args.config)
+    dev = torch.device("cuda:0")
+    trees = W.make_trees(cfg)
+    cu = W.cu_from_trees(trees)
+    T = int(cu[-1])
+    slots = W.make_slots(cfg)
+    acc = W.make_accepts(cfg, trees)
+    s_in = 2 if cfg.dtype == "bf16" else 4
+    qkv_dtype = G.GDN_BF16 if cfg.dtype == "bf16" else G.GDN_F32
+    dims = G.make_dims(cfg.num_seqs, T, cfg.max_nodes, cfg.num_k_heads, cfg.num_v_heads, cfg.head_dim,
+                       cfg.num_slots, qkv_dtype, max_depth=cfg.max_depth)
+    path_lens = [int(W.tree_depths(t)[m]) for t, m in zip(trees, acc)]
+    vbytes, pbytes = algorithmic_bytes(cfg, T, path_lens, s_in)
+    vflops, pflops = flops(cfg, trees, path_lens)
+
+    def to_dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    layers = cfg.num_layers
+    per_copy = vbytes + T * cfg.num_v_heads * cfg.head_dim * 4
+    rotate = args.rotate or max(1, int(np.ceil(512e6 / (per_copy * layers))))
+    copies = layers * rotate
+    print("# config %s: B=%d T=%d layers=%d copies=%d (%.0f MB per layer copy)"
+          % (cfg.name, cfg.num_seqs, T, layers, copies, per_copy / 1e6), file=sys.stderr, flush=True)
+
+    slot_d = to_dev(slots)
+    acc_d = to_dev(acc)
+    parent_d = to_dev(np.concatenate(trees).astype(np.int32))
+    cu_d = to_dev(cu.astype(np.int32))
+    ws = G.new_workspace(dims)
+    # committed states: each copy's cache is filled by the library's own chain
+    # kernel running that copy's prefill tokens from a zero state
+    sets = []
+    pre_cu = torch.arange(0, (cfg.num_seqs + 1) * cfg.prefill_steps, cfg.prefill_steps, dtype=torch.int32,
+                          device=dev)
+    pre_dims = G.make_dims(cfg.num_seqs, cfg.num_seqs * cfg.prefill_steps, cfg.prefill_steps, cfg.num_k_heads,
+                           cfg.num_v_heads, cfg.head_dim, cfg.num_slots, qkv_dtype)
+    zero_cache = torch.zeros((cfg.num_slots, cfg.num_v_heads, cfg.head_dim, cfg.head_dim), device=dev)
+    flen = torch.full((cfg.num_seqs,), cfg.prefill_steps, dtype=torch.int32, device=dev)
+    ident = torch.arange(cfg.num_seqs, dtype=torch.int32, device=dev)
+    for c in range(copies):
+        inp = W.make_layer_inputs(cfg, c, trees)
+        pre = W.make_prefill(cfg, c)
+        d = {k: to_dev(v) for k, v in inp.items()}
+        pk = to_dev(pre["k"].reshape(-1, cfg.num_k_heads, cfg.head_dim))
+        pv = to_dev(pre["v"].reshape(-1, cfg.num_v_heads, cfg.head_dim))
+        pa = to_dev(pre["a"].reshape(-1, cfg.num_v_heads))
+        pb = to_dev(pre["b"].reshape(-1, cfg.num_v_heads))
+        fin = torch.empty((cfg.num_seqs, cfg.num_v_heads, cfg.head_dim, cfg.head_dim), device=dev)
+        G.gdn_chain_verify(pre_dims, pre_cu, None, pk, pv, pa, pb, zero_cache, ident, None, flen, fin)
+        cache = torch.zeros((cfg.num_slots, cfg.num_v_heads, cfg.head_dim, cfg.head_dim), device=dev)
+        cache[slot_d.long()] = fin
+        d["cache"] = cache
+        d["out"] = torch.empty((T, cfg.num_v_heads, cfg.head_dim), device=dev)
+        sets.append(d)
+        del pk, pv, pa, pb, fin
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * layers + 2)] for _ in range(args.steps)]
+
+    def step(i, events=None):
+        r = i % rotate
+        if events:
+            events[0].record(stream)
+        G.gdn_tree_plan(dims, parent_d, cu_d, slot_d, ws)
+        if events:
+            events[1].record(stream)
+        for l in range(layers):
+            d = sets[r * layers + l]
+            G.gdn_tree_verify(dims, d["q"], d["k"], d["v"], d["a"], d["b"], d["cache"], slot_d, d["out"], ws)
+            if events:
+                events[2 + l].record(stream)
+        for l in range(layers):
+            d = sets[r * layers + l]
+            G.gdn_tree_persist(dims, d["k"], d["v"], d["a"], d["b"], acc_d, d["cache"], slot_d, ws)
+            if events:
+                events[2 + layers + l].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    rc, bad, code = G.gdn_tree_status(ws)
+    if rc != 0:
+        print(json.dumps({"error": "library rejected the workload: %d %d %d" % (rc, bad, code)}))
+        sys.exit(1)
+
+    # main timed loop: exactly K steps, synchronize on both sides
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, ev[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    plan_ms, ver_ms, per_ms = [], [], []
+    for e in ev:
+        plan_ms.append(e[0].elapsed_time(e[1]))
+        prev = e[1]
+        for l in range(layers):
+            ver_ms.append(prev.elapsed_time(e[2 + l]))
+            prev = e[2 + l]
+        for l in range(layers):
+            per_ms.append(prev.elapsed_time(e[2 + layers + l]))
+            prev = e[2 + layers + l]
+    t_plan = float(np.mean(plan_ms)) * 1e-3
+    t_ver = float(np.mean(ver_ms)) * 1e-3
+    t_per = float(np.mean(per_ms)) * 1e-3
+    layer_call = t_ver + t_per
+    nodes_per_s = T * layers / (ms_per_step * 1e-3)
+    hbm_gbs = (vbytes + pbytes) / layer_call / 1e9
+
+    # dominant kernel of the layer call
+    if t_ver >= t_per:
+        dom, t_dom, dom_bytes, dom_flops = "tree_verify", t_ver, vbytes, vflops
+    else:
+        dom, t_dom, dom_bytes, dom_flops = "persist", t_per, pbytes, pflops
+    intensity = dom_flops / dom_bytes
+    if intensity > FP32_VECTOR_PEAK_TFLOPS * 1e3 / HBM_PEAK_GBS:
+        roof = {"bound": "alu", "achieved": dom_flops / t_dom / 1e12, "peak": FP32_VECTOR_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": dom_bytes / t_dom / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel"] = dom
+    roof["traffic"] = measured_traffic(dom, cfg.name)
+
+    result = {
+        "metric": "GDN tree-verify nodes/sec per layer call + achieved HBM GB/s (% of peak)",
+        "value": nodes_per_s,
+        "unit": "nodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "sequences": cfg.num_seqs, "layers": layers, "nodes": T,
+                   "v_heads": cfg.num_v_heads, "k_heads": cfg.num_k_heads, "head_dim": cfg.head_dim,
+                   "qkv": cfg.dtype, "rotated_copies": rotate, "seed": cfg.seed},
+        "layer_call": {"verify_us": t_ver * 1e6, "persist_us": t_per * 1e6, "plan_us": t_plan * 1e6,
+                       "verify_bytes": vbytes, "persist_bytes": pbytes, "hbm_gbs": hbm_gbs,
+                       "hbm_frac": hbm_gbs / HBM_PEAK_GBS,
+                       "verify_gbs": vbytes / t_ver / 1e9, "persist_gbs": pbytes / t_per / 1e9,
+                       "verify_tflops": vflops / t_ver / 1e12},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, trees, cu, acc, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_deltanet_tree_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get(workload, {}).get(kernel)
+    if not ent or ent.get("source_digest") != kernel_source_digest():
+        return None
+    return ent["bytes_per_launch"]
+
+
+def cpu_baseline(cfg, trees, cu, acc, seconds):
+    """The fp64 oracle (verify + persist) on the host cores, on as many whole
+    sequences of layer 0 as fit in about `seconds` of work."""
+    import oracle
+    import workloads as W
+    inp = W.make_layer_inputs(cfg, 0, trees)
+    rng = np.random.default_rng(0)
+    done_nodes, t_total, seqs = 0, 0.0, 0
+    for s in range(cfg.num_seqs):
+        lo, hi = int(cu[s]), int(cu[s + 1])
+        S0 = (0.1 * rng.standard_normal((cfg.num_v_heads, cfg.head_dim, cfg.head_dim))).astype(np.float32)
+        sl = {k: v[lo:hi] for k, v in inp.items()}
+        t0 = time.perf_counter()
+        oracle.tree(trees[s], sl["q"], sl["k"], sl["v"], sl["a"], sl["b"], S0)
+        oracle.accept_state(trees[s], int(acc[s]), sl["k"], sl["v"], sl["a"], sl["b"], S0)
+        t_total += time.perf_counter() - t0
+        done_nodes += hi - lo
+        seqs += 1
+        if t_total >= seconds:
+            break
+    return {"value": done_nodes / t_total, "unit": "nodes/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d of %d sequences of layer 0 (%d nodes, verify + persist, fp64), %.1f s"
+                      % (seqs, cfg.num_seqs, done_nodes, t_total)}
+
+
+if __name__ == "__main__":
+    main()

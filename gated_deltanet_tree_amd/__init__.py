@@ -1,0 +1,224 @@
+"""Gated DeltaNet tree verify + accepted-path persist for MI355X (gfx950).
+
+A thin ctypes binding over ``libgdn_tree.so`` (C ABI in ``include/gdn_tree.h``).
+Every step of the path runs in the library's HIP kernels; this module only
+checks tensors and passes their device pointers and the current HIP stream.
+torch is used for device memory and streams, nothing else.
+
+Typical decode step (all on one stream)::
+
+    dims = make_dims(...)
+    ws = torch.empty(workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    gdn_tree_plan(dims, parent, cu_nodes, slot_idx, ws)
+    for layer in layers:
+        gdn_tree_verify(dims, q, k, v, a, b, cache[layer], slot_idx, out, ws)
+    # ... acceptance ...
+    for layer in layers:
+        gdn_tree_persist(dims, k, v, a, b, accepted, cache[layer], slot_idx, ws)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn_tree.so")
+
+GDN_MAX_DEPTH = 16
+GDN_MAX_NODES = 256
+GDN_MAX_CHAIN = 65536
+GDN_BF16, GDN_F32 = 0, 1
+
+SEQ_STATUS = {0: "OK", 1: "BAD_NODES", 2: "BAD_SLOT", 3: "DUP_SLOT", 4: "BAD_PARENT",
+              5: "CYCLE_OR_DEPTH", 6: "BAD_ACCEPT"}
+
+EXPORTS = ["gdn_workspace_bytes", "gdn_tree_plan", "gdn_tree_verify", "gdn_tree_persist",
+           "gdn_chain_verify", "gdn_tree_read_metadata", "gdn_tree_status", "gdn_strerror"]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__("%s failed: %s (%d)" % (where, strerror(code), code))
+        self.code = code
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "num_seqs", "total_nodes", "max_nodes", "max_depth", "num_k_heads", "num_v_heads",
+        "head_dim", "num_slots", "qkv_dtype")]
+
+    def __repr__(self):
+        return "Dims(%s)" % ", ".join("%s=%d" % (f, getattr(self, f)) for f, _ in self._fields_)
+
+
+def make_dims(num_seqs, total_nodes, max_nodes, num_k_heads, num_v_heads, head_dim, num_slots,
+              qkv_dtype=GDN_BF16, max_depth=GDN_MAX_DEPTH) -> Dims:
+    return Dims(int(num_seqs), int(total_nodes), int(max_nodes), int(max_depth), int(num_k_heads),
+                int(num_v_heads), int(head_dim), int(num_slots), int(qkv_dtype))
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libgdn_tree.so; raises if it has not been built (no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError("libgdn_tree.so is missing at %s; build it with "
+                          "`python -m gated_deltanet_tree_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    dp = ctypes.POINTER(Dims)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    lib.gdn_workspace_bytes.argtypes = [dp]
+    lib.gdn_workspace_bytes.restype = sz
+    lib.gdn_tree_plan.argtypes = [dp, vp, vp, vp, vp, sz, vp]
+    lib.gdn_tree_verify.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdn_tree_persist.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdn_chain_verify.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdn_tree_read_metadata.argtypes = [dp, vp, sz, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_tree_status.argtypes = [vp, sz, vp, ip, ip]
+    lib.gdn_strerror.argtypes = [i32]
+    lib.gdn_strerror.restype = ctypes.c_char_p
+    for f in ("gdn_tree_plan", "gdn_tree_verify", "gdn_tree_persist", "gdn_chain_verify",
+              "gdn_tree_read_metadata", "gdn_tree_status"):
+        getattr(lib, f).restype = i32
+    _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load_library().gdn_strerror(int(code)).decode()
+
+
+# ---------------------------------------------------------------- checks
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t, name, dtype=None, numel=None, allow_none=False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError("%s is required" % name)
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if numel is not None and t.numel() != numel:
+        raise ValueError("%s has %d elements, expected %d" % (name, t.numel(), numel))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _qkv_dtype(dims):
+    return torch.bfloat16 if dims.qkv_dtype == GDN_BF16 else torch.float32
+
+
+def _check(code, where):
+    if code != 0:
+        raise GdnError(code, where)
+
+
+def workspace_bytes(dims: Dims) -> int:
+    return int(load_library().gdn_workspace_bytes(ctypes.byref(dims)))
+
+
+def new_workspace(dims: Dims, device="cuda") -> torch.Tensor:
+    n = workspace_bytes(dims)
+    if n == 0:
+        raise ValueError("invalid dims %r" % dims)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------- entry points
+def gdn_tree_plan(dims, parent, cu_nodes, slot_idx, ws, stream=None):
+    T, B = dims.total_nodes, dims.num_seqs
+    _check(load_library().gdn_tree_plan(
+        ctypes.byref(dims), _ptr(parent, "parent", torch.int32, T), _ptr(cu_nodes, "cu_nodes", torch.int32, B + 1),
+        _ptr(slot_idx, "slot_idx", torch.int32, B), _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)),
+        "gdn_tree_plan")
+
+
+def gdn_tree_verify(dims, q, k, v, a, b, state_cache, slot_idx, out, ws, stream=None):
+    T, B, Hk, Hv, D = dims.total_nodes, dims.num_seqs, dims.num_k_heads, dims.num_v_heads, dims.head_dim
+    dt = _qkv_dtype(dims)
+    _check(load_library().gdn_tree_verify(
+        ctypes.byref(dims), _ptr(q, "q", dt, T * Hk * D), _ptr(k, "k", dt, T * Hk * D),
+        _ptr(v, "v", dt, T * Hv * D), _ptr(a, "a", torch.float32, T * Hv), _ptr(b, "b", torch.float32, T * Hv),
+        _ptr(state_cache, "state_cache", torch.float32, dims.num_slots * Hv * D * D),
+        _ptr(slot_idx, "slot_idx", torch.int32, B), _ptr(out, "out", torch.float32, T * Hv * D),
+        _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)), "gdn_tree_verify")
+
+
+def gdn_tree_persist(dims, k, v, a, b, accepted_node, state_cache, slot_idx, ws, stream=None):
+    T, B, Hk, Hv, D = dims.total_nodes, dims.num_seqs, dims.num_k_heads, dims.num_v_heads, dims.head_dim
+    dt = _qkv_dtype(dims)
+    _check(load_library().gdn_tree_persist(
+        ctypes.byref(dims), _ptr(k, "k", dt, T * Hk * D), _ptr(v, "v", dt, T * Hv * D),
+        _ptr(a, "a", torch.float32, T * Hv), _ptr(b, "b", torch.float32, T * Hv),
+        _ptr(accepted_node, "accepted_node", torch.int32, B),
+        _ptr(state_cache, "state_cache", torch.float32, dims.num_slots * Hv * D * D),
+        _ptr(slot_idx, "slot_idx", torch.int32, B), _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)),
+        "gdn_tree_persist")
+
+
+def gdn_chain_verify(dims, cu_nodes, q, k, v, a, b, state_cache, slot_idx, out=None, final_len=None,
+                     final_state=None, ws=None, stream=None):
+    T, B, Hk, Hv, D = dims.total_nodes, dims.num_seqs, dims.num_k_heads, dims.num_v_heads, dims.head_dim
+    dt = _qkv_dtype(dims)
+    _check(load_library().gdn_chain_verify(
+        ctypes.byref(dims), _ptr(cu_nodes, "cu_nodes", torch.int32, B + 1),
+        _ptr(q, "q", dt, T * Hk * D, allow_none=True), _ptr(k, "k", dt, T * Hk * D), _ptr(v, "v", dt, T * Hv * D),
+        _ptr(a, "a", torch.float32, T * Hv), _ptr(b, "b", torch.float32, T * Hv),
+        _ptr(state_cache, "state_cache", torch.float32, dims.num_slots * Hv * D * D),
+        _ptr(slot_idx, "slot_idx", torch.int32, B), _ptr(out, "out", torch.float32, T * Hv * D, allow_none=True),
+        _ptr(final_len, "final_len", torch.int32, B, allow_none=True),
+        _ptr(final_state, "final_state", torch.float32, B * Hv * D * D, allow_none=True),
+        _ptr(ws, "ws", torch.uint8, allow_none=True), 0 if ws is None else ws.numel(), _stream(stream)),
+        "gdn_chain_verify")
+
+
+def gdn_tree_read_metadata(dims, ws, depth=None, order=None, action=None, path=None, path_len=None,
+                           seq_status=None, stream=None):
+    T, B = dims.total_nodes, dims.num_seqs
+    _check(load_library().gdn_tree_read_metadata(
+        ctypes.byref(dims), _ptr(ws, "ws", torch.uint8), ws.numel(),
+        _ptr(depth, "depth", torch.int32, T, True), _ptr(order, "order", torch.int32, T, True),
+        _ptr(action, "action", torch.int32, T, True), _ptr(path, "path", torch.int32, B * GDN_MAX_DEPTH, True),
+        _ptr(path_len, "path_len", torch.int32, B, True), _ptr(seq_status, "seq_status", torch.int32, B, True),
+        _stream(stream)), "gdn_tree_read_metadata")
+
+
+def gdn_tree_status(ws, stream=None):
+    """Synchronizes the stream; returns (status, first_bad_seq, first_bad_code)."""
+    seq = ctypes.c_int32(-1)
+    code = ctypes.c_int32(0)
+    rc = load_library().gdn_tree_status(_ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream),
+                                        ctypes.byref(seq), ctypes.byref(code))
+    return int(rc), int(seq.value), int(code.value)
+
+
+def read_metadata(dims, ws, stream=None) -> dict:
+    """Convenience: all metadata as fresh device tensors."""
+    T, B = dims.total_nodes, dims.num_seqs
+    dev = ws.device
+    md = {
+        "depth": torch.empty(T, dtype=torch.int32, device=dev),
+        "order": torch.empty(T, dtype=torch.int32, device=dev),
+        "action": torch.empty(T, dtype=torch.int32, device=dev),
+        "path": torch.empty(B * GDN_MAX_DEPTH, dtype=torch.int32, device=dev),
+        "path_len": torch.empty(B, dtype=torch.int32, device=dev),
+        "seq_status": torch.empty(B, dtype=torch.int32, device=dev),
+    }
+    gdn_tree_read_metadata(dims, ws, stream=stream, **md)
+    md["path"] = md["path"].view(B, GDN_MAX_DEPTH)
+    return md

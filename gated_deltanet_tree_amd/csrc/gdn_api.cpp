@@ -1,0 +1,233 @@
+// gdn_api.cpp -- the C ABI: host-side argument checks, workspace sizing and
+// kernel launches.  Nothing here allocates device memory or synchronizes,
+// except gdn_tree_status.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstring>
+#include <vector>
+
+#include "gdn_internal.h"
+
+using gdn::Params;
+
+namespace {
+
+bool dims_ok(const gdn_dims *d, int max_nodes_limit) {
+    if (!d) return false;
+    if (d->num_seqs < 0 || d->total_nodes < 0) return false;
+    if (d->max_nodes < 0 || d->max_nodes > max_nodes_limit) return false;
+    if (d->max_depth < 1 || d->max_depth > GDN_MAX_DEPTH) return false;
+    if (d->num_k_heads < 1 || d->num_v_heads < 1 || d->num_v_heads % d->num_k_heads != 0) return false;
+    if (d->num_seqs > 0 && d->num_slots < 1) return false;
+    if (d->num_slots < 0) return false;
+    // index arithmetic inside the kernels stays in 64 bits, but per-launch grid sizes are int
+    if ((long long)d->num_seqs * d->num_v_heads * 16 > INT_MAX) return false;
+    return true;
+}
+
+int check_dims(const gdn_dims *d, int max_nodes_limit) {
+    if (!d) return GDN_ERR_NULL;
+    if (!dims_ok(d, max_nodes_limit)) return GDN_ERR_SHAPE;
+    if (d->head_dim != 16 && d->head_dim != 32 && d->head_dim != 64 && d->head_dim != 128)
+        return GDN_ERR_UNSUPPORTED;
+    if (d->qkv_dtype != GDN_BF16 && d->qkv_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+Params base_params(const gdn_dims *d) {
+    Params p;
+    std::memset(&p, 0, sizeof(p));
+    p.B = d->num_seqs;
+    p.T = d->total_nodes;
+    p.max_nodes = d->max_nodes;
+    p.max_depth = d->max_depth;
+    p.Hk = d->num_k_heads;
+    p.Hv = d->num_v_heads;
+    p.D = d->head_dim;
+    p.num_slots = d->num_slots;
+    p.stack_slots = gdn::stack_bound(d->max_nodes, d->max_depth);
+    return p;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH; }
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn_workspace_bytes(const gdn_dims *dims) {
+    if (!dims || !dims_ok(dims, GDN_MAX_CHAIN)) return 0;
+    return gdn::ws_layout(dims->num_seqs, dims->total_nodes).total;
+}
+
+int gdn_tree_plan(const gdn_dims *dims, const int32_t *parent, const int32_t *cu_nodes,
+                  const int32_t *slot_idx, void *ws, size_t ws_bytes, void *stream) {
+    int rc = check_dims(dims, GDN_MAX_NODES);
+    if (rc) return rc;
+    if (!ws || !cu_nodes) return GDN_ERR_NULL;
+    if (dims->num_seqs > 0 && !slot_idx) return GDN_ERR_NULL;
+    if (dims->total_nodes > 0 && !parent) return GDN_ERR_NULL;
+    if (ws_bytes < gdn_workspace_bytes(dims)) return GDN_ERR_WORKSPACE;
+    Params p = base_params(dims);
+    p.parent = parent;
+    p.cu_nodes = cu_nodes;
+    p.slot_idx = slot_idx;
+    p.ws = gdn::ws_ptrs(ws, p.B, p.T);
+    p.has_ws = 1;
+    return launched(gdn::launch_plan(p, as_stream(stream)));
+}
+
+int gdn_tree_verify(const gdn_dims *dims, const void *q, const void *k, const void *v,
+                    const float *a, const float *b, const float *state_cache,
+                    const int32_t *slot_idx, float *out, const void *ws, size_t ws_bytes,
+                    void *stream) {
+    int rc = check_dims(dims, GDN_MAX_NODES);
+    if (rc) return rc;
+    if (!ws) return GDN_ERR_NULL;
+    if (dims->total_nodes > 0 && (!q || !k || !v || !a || !b || !out)) return GDN_ERR_NULL;
+    if (dims->num_seqs > 0 && (!state_cache || !slot_idx)) return GDN_ERR_NULL;
+    if (ws_bytes < gdn_workspace_bytes(dims)) return GDN_ERR_WORKSPACE;
+    if (dims->num_seqs == 0 || dims->total_nodes == 0) return GDN_OK;
+    Params p = base_params(dims);
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.a = a;
+    p.b = b;
+    p.state_in = state_cache;
+    p.slot_idx = slot_idx;
+    p.out = out;
+    p.ws = gdn::ws_ptrs(const_cast<void *>(ws), p.B, p.T);
+    p.has_ws = 1;
+    return launched(gdn::launch_tree_verify_recurrent(p, dims->qkv_dtype, as_stream(stream)));
+}
+
+int gdn_tree_persist(const gdn_dims *dims, const void *k, const void *v, const float *a,
+                     const float *b, const int32_t *accepted_node, float *state_cache,
+                     const int32_t *slot_idx, void *ws, size_t ws_bytes, void *stream) {
+    int rc = check_dims(dims, GDN_MAX_NODES);
+    if (rc) return rc;
+    if (!ws) return GDN_ERR_NULL;
+    if (dims->total_nodes > 0 && (!k || !v || !a || !b)) return GDN_ERR_NULL;
+    if (dims->num_seqs > 0 && (!state_cache || !slot_idx || !accepted_node)) return GDN_ERR_NULL;
+    if (ws_bytes < gdn_workspace_bytes(dims)) return GDN_ERR_WORKSPACE;
+    if (dims->num_seqs == 0 || dims->total_nodes == 0) return GDN_OK;
+    Params p = base_params(dims);
+    p.k = k;
+    p.v = v;
+    p.a = a;
+    p.b = b;
+    p.accepted = accepted_node;
+    p.state_in = state_cache;
+    p.state_out = state_cache;
+    p.slot_idx = slot_idx;
+    p.ws = gdn::ws_ptrs(ws, p.B, p.T);
+    p.has_ws = 1;
+    return launched(gdn::launch_persist_recurrent(p, dims->qkv_dtype, as_stream(stream)));
+}
+
+int gdn_chain_verify(const gdn_dims *dims, const int32_t *cu_nodes, const void *q, const void *k,
+                     const void *v, const float *a, const float *b, const float *state_cache,
+                     const int32_t *slot_idx, float *out, const int32_t *final_len,
+                     float *final_state, void *ws, size_t ws_bytes, void *stream) {
+    int rc = check_dims(dims, GDN_MAX_CHAIN);
+    if (rc) return rc;
+    if (!cu_nodes) return GDN_ERR_NULL;
+    if ((q == nullptr) != (out == nullptr)) return GDN_ERR_NULL;
+    if ((final_len == nullptr) != (final_state == nullptr)) return GDN_ERR_NULL;
+    if (dims->total_nodes > 0 && (!k || !v || !a || !b)) return GDN_ERR_NULL;
+    if (dims->num_seqs > 0 && (!state_cache || !slot_idx)) return GDN_ERR_NULL;
+    if (ws && ws_bytes < gdn_workspace_bytes(dims)) return GDN_ERR_WORKSPACE;
+    if (dims->num_seqs == 0) return GDN_OK;
+    Params p = base_params(dims);
+    p.cu_nodes = cu_nodes;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.a = a;
+    p.b = b;
+    p.state_in = state_cache;
+    p.slot_idx = slot_idx;
+    p.out = out;
+    p.final_len = final_len;
+    p.final_state = final_state;
+    if (ws) {
+        p.ws = gdn::ws_ptrs(ws, p.B, p.T);
+        p.has_ws = 1;
+    }
+    return launched(gdn::launch_chain_verify_recurrent(p, dims->qkv_dtype, as_stream(stream)));
+}
+
+int gdn_tree_read_metadata(const gdn_dims *dims, const void *ws, size_t ws_bytes, int32_t *depth,
+                           int32_t *order, int32_t *action, int32_t *path, int32_t *path_len,
+                           int32_t *seq_status, void *stream) {
+    int rc = check_dims(dims, GDN_MAX_NODES);
+    if (rc) return rc;
+    if (!ws) return GDN_ERR_NULL;
+    if (ws_bytes < gdn_workspace_bytes(dims)) return GDN_ERR_WORKSPACE;
+    const gdn::WsPtrs w = gdn::ws_ptrs(const_cast<void *>(ws), dims->num_seqs, dims->total_nodes);
+    const size_t T = (size_t)dims->total_nodes, B = (size_t)dims->num_seqs;
+    hipStream_t s = as_stream(stream);
+    struct Copy {
+        void *dst;
+        const void *src;
+        size_t bytes;
+    } copies[] = {
+        {depth, w.depth, T * 4},       {order, w.order, T * 4},
+        {action, w.action, T * 4},     {path, w.path, B * GDN_MAX_DEPTH * 4},
+        {path_len, w.path_len, B * 4}, {seq_status, w.seq_status, B * 4},
+    };
+    for (const Copy &c : copies) {
+        if (!c.dst || c.bytes == 0) continue;
+        if (hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+            return GDN_ERR_LAUNCH;
+    }
+    return GDN_OK;
+}
+
+int gdn_tree_status(const void *ws, size_t ws_bytes, void *stream, int32_t *first_bad_seq,
+                    int32_t *first_bad_code) {
+    if (first_bad_seq) *first_bad_seq = -1;
+    if (first_bad_code) *first_bad_code = 0;
+    if (!ws) return GDN_ERR_NULL;
+    if (ws_bytes < gdn::ws_layout(0, 0).total) return GDN_ERR_WORKSPACE;
+    hipStream_t s = as_stream(stream);
+    if (hipStreamSynchronize(s) != hipSuccess) return GDN_ERR_DEVICE;
+    int32_t header[gdn::kHeaderInts];
+    if (hipMemcpy(header, ws, sizeof(header), hipMemcpyDeviceToHost) != hipSuccess) return GDN_ERR_DEVICE;
+    if (header[0] != gdn::kMagic || header[1] < 0 || header[2] < 0) return GDN_ERR_WORKSPACE;
+    const int B = header[1], T = header[2];
+    if (ws_bytes < gdn::ws_layout(B, T).total) return GDN_ERR_WORKSPACE;
+    if (B == 0) return GDN_OK;
+    std::vector<int32_t> st(B);
+    const gdn::WsPtrs w = gdn::ws_ptrs(const_cast<void *>(ws), B, T);
+    if (hipMemcpy(st.data(), w.seq_status, (size_t)B * 4, hipMemcpyDeviceToHost) != hipSuccess)
+        return GDN_ERR_DEVICE;
+    for (int i = 0; i < B; ++i) {
+        if (st[i] != GDN_SEQ_OK) {
+            if (first_bad_seq) *first_bad_seq = i;
+            if (first_bad_code) *first_bad_code = st[i];
+            return GDN_ERR_TREE;
+        }
+    }
+    return GDN_OK;
+}
+
+const char *gdn_strerror(int status) {
+    switch (status) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_NULL: return "a required pointer is NULL";
+        case GDN_ERR_SHAPE: return "dims out of range or inconsistent";
+        case GDN_ERR_UNSUPPORTED: return "head dim or dtype not supported";
+        case GDN_ERR_WORKSPACE: return "workspace too small or not planned for these dims";
+        case GDN_ERR_LAUNCH: return "kernel launch failed";
+        case GDN_ERR_TREE: return "a sequence was rejected (bad tree, slot or accepted node)";
+        case GDN_ERR_DEVICE: return "HIP error while synchronizing";
+        default: return "unknown gdn status";
+    }
+}
+
+}  // extern "C"

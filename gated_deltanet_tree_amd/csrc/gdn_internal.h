@@ -1,0 +1,94 @@
+// gdn_internal.h -- workspace layout, kernel parameter block and small device
+// helpers shared by the kernels and the C-ABI layer of the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gdn_tree.h"
+
+namespace gdn {
+
+constexpr int32_t kMagic = 0x67646e74;  // written by the plan into the workspace header
+constexpr int kHeaderInts = 16;          // magic, B, T, max_nodes, max_depth, stack slots, ...
+constexpr int kSeqInfoInts = 4;          // node offset, node count, max stack, reserved
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Byte offsets of the workspace regions (each 256-byte aligned).
+struct WsLayout {
+    size_t header, seq_status, seq_info, depth, order, action, nodepath, path, path_len, total;
+};
+
+__host__ __device__ inline WsLayout ws_layout(int B, int T) {
+    const size_t b = B > 0 ? (size_t)B : 1, t = T > 0 ? (size_t)T : 1;
+    WsLayout L;
+    size_t off = 0;
+    L.header = off;     off += align256(kHeaderInts * 4);
+    L.seq_status = off; off += align256(b * 4);
+    L.seq_info = off;   off += align256(b * kSeqInfoInts * 4);
+    L.depth = off;      off += align256(t * 4);
+    L.order = off;      off += align256(t * 4);
+    L.action = off;     off += align256(t * 4);
+    L.nodepath = off;   off += align256(t * GDN_MAX_DEPTH * 4);
+    L.path = off;       off += align256(b * GDN_MAX_DEPTH * 4);
+    L.path_len = off;   off += align256(b * 4);
+    L.total = off;
+    return L;
+}
+
+struct WsPtrs {
+    int32_t *header, *seq_status, *seq_info, *depth, *order, *action, *nodepath, *path, *path_len;
+};
+
+inline WsPtrs ws_ptrs(void *ws, int B, int T) {
+    const WsLayout L = ws_layout(B, T);
+    char *base = static_cast<char *>(ws);
+    WsPtrs p;
+    p.header = reinterpret_cast<int32_t *>(base + L.header);
+    p.seq_status = reinterpret_cast<int32_t *>(base + L.seq_status);
+    p.seq_info = reinterpret_cast<int32_t *>(base + L.seq_info);
+    p.depth = reinterpret_cast<int32_t *>(base + L.depth);
+    p.order = reinterpret_cast<int32_t *>(base + L.order);
+    p.action = reinterpret_cast<int32_t *>(base + L.action);
+    p.nodepath = reinterpret_cast<int32_t *>(base + L.nodepath);
+    p.path = reinterpret_cast<int32_t *>(base + L.path);
+    p.path_len = reinterpret_cast<int32_t *>(base + L.path_len);
+    return p;
+}
+
+// Everything a kernel needs; passed by value.
+struct Params {
+    int B, T, max_nodes, max_depth, Hk, Hv, D, num_slots;
+    int stack_slots;             // LDS stack entries of the recurrent tree kernel
+    const int32_t *parent;       // plan
+    const int32_t *cu_nodes;     // plan, chain
+    const int32_t *slot_idx;
+    const void *q, *k, *v;       // bf16 bits (uint16) or fp32
+    const float *a, *b;
+    const float *state_in;       // committed states (verify, chain, persist)
+    float *state_out;            // persist: same slots, written in place
+    float *out;                  // [T][Hv][D]
+    const int32_t *accepted;     // persist
+    const int32_t *final_len;    // chain
+    float *final_state;          // chain
+    WsPtrs ws;
+    int has_ws;
+};
+
+// ---- kernel launchers (defined in the .hip files) --------------------------
+hipError_t launch_plan(const Params &p, hipStream_t s);
+hipError_t launch_tree_verify_recurrent(const Params &p, int dtype, hipStream_t s);
+hipError_t launch_chain_verify_recurrent(const Params &p, int dtype, hipStream_t s);
+hipError_t launch_persist_recurrent(const Params &p, int dtype, hipStream_t s);
+
+// Largest LDS stack the heavy-last preorder can need for trees of n nodes:
+// k nested pushes need a subtree of at least 2^(k+1) - 1 nodes.
+inline int stack_bound(int max_nodes, int max_depth) {
+    int k = 0;
+    while ((1 << (k + 2)) - 1 <= max_nodes) ++k;
+    return k < max_depth - 1 ? k : (max_depth > 1 ? max_depth - 1 : 0);
+}
+
+}  // namespace gdn

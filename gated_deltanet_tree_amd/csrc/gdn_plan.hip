@@ -1,0 +1,181 @@
+// gdn_plan.hip -- device-side validation and traversal metadata of the draft
+// trees (one workgroup of 256 threads per sequence, one thread per node).
+//
+// The trees arrive in parent-pointer form from DDTree's tree builder
+// (GreenGames page, "From autoregressive to DDTree"), depth bounded by the
+// 16-token drafting block (GreenGames, "Prefill").  For each sequence the
+// plan writes: its verdict, each node's depth and root-to-node path, and a
+// depth-first preorder in which children are visited by increasing (subtree
+// size, id) -- the largest child last -- with one action word per position.
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kPlanThreads = GDN_MAX_NODES;  // one thread per node
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params P) {
+    __shared__ int s_par[kPlanThreads];
+    __shared__ int s_size[kPlanThreads];
+    __shared__ int s_nchild[kPlanThreads];
+    __shared__ int s_off[kPlanThreads];
+    __shared__ int s_later[kPlanThreads];
+    __shared__ int s_scan[kPlanThreads];
+
+    const int b = blockIdx.x;
+    const int t = threadIdx.x;
+    const WsPtrs W = P.ws;
+    if (b == 0 && t == 0) {
+        W.header[0] = kMagic;
+        W.header[1] = P.B;
+        W.header[2] = P.T;
+        W.header[3] = P.max_nodes;
+        W.header[4] = P.max_depth;
+        W.header[5] = P.stack_slots;
+    }
+    if (b >= P.B) return;
+
+    // ---- node range ---------------------------------------------------------
+    const int lo = P.cu_nodes[b], hi = P.cu_nodes[b + 1];
+    int status = GDN_SEQ_OK;
+    const bool range_ok = 0 <= lo && lo <= hi && hi <= P.T && hi - lo <= P.max_nodes;
+    if (!range_ok) status = GDN_SEQ_BAD_NODES;
+    const int n = range_ok ? hi - lo : 0;
+
+    // ---- slot: in range and not shared with another non-empty sequence ------
+    if (status == GDN_SEQ_OK && n > 0) {
+        const int slot = P.slot_idx[b];
+        if (slot < 0 || slot >= P.num_slots) {
+            status = GDN_SEQ_BAD_SLOT;
+        } else {
+            int dup = 0;
+            for (int o = t; o < P.B; o += kPlanThreads) {
+                if (o == b) continue;
+                const int lo2 = P.cu_nodes[o], hi2 = P.cu_nodes[o + 1];
+                const bool ok2 = 0 <= lo2 && lo2 <= hi2 && hi2 <= P.T && hi2 - lo2 <= P.max_nodes;
+                if (ok2 && hi2 > lo2 && P.slot_idx[o] == slot) dup = 1;
+            }
+            if (__syncthreads_or(dup)) status = GDN_SEQ_DUP_SLOT;
+        }
+    }
+
+    // ---- parent ids ------------------------------------------------------------
+    int par = -1;
+    if (status == GDN_SEQ_OK && n > 0) {
+        if (t < n) par = P.parent[lo + t];
+        const bool bad = t < n && !(par == -1 || (par >= 0 && par < n && par != t));
+        if (__syncthreads_or(bad)) status = GDN_SEQ_BAD_PARENT;
+    }
+
+    // ---- depth: every ancestor walk must reach a root within max_depth nodes -----
+    int depth = 0;
+    if (status == GDN_SEQ_OK && n > 0) {
+        s_par[t] = par;
+        s_size[t] = 0;
+        s_nchild[t] = 0;
+        __syncthreads();
+        bool deep = false;
+        if (t < n) {
+            int x = t;
+            while (x != -1 && depth < P.max_depth) {
+                ++depth;
+                x = s_par[x];
+            }
+            deep = x != -1;
+        }
+        if (__syncthreads_or(deep)) status = GDN_SEQ_CYCLE_OR_DEPTH;
+    }
+
+    int max_stack = 0;
+    if (status == GDN_SEQ_OK && n > 0) {
+        // subtree sizes (each node counts itself into every ancestor) and child counts
+        if (t < n) {
+            for (int x = t; x != -1; x = s_par[x]) atomicAdd(&s_size[x], 1);
+            if (par >= 0) atomicAdd(&s_nchild[par], 1);
+        }
+        __syncthreads();
+        // siblings visited before this node (smaller (size, id)) and after it
+        if (t < n) {
+            const int my = s_size[t];
+            int off = 0, later = 0;
+            for (int s = 0; s < n; ++s) {
+                if (s == t || s_par[s] != par) continue;
+                const int ss = s_size[s];
+                if (ss < my || (ss == my && s < t)) off += ss;
+                else ++later;
+            }
+            s_off[t] = off;
+            s_later[t] = later;
+        }
+        __syncthreads();
+        int pos = 0, act = 0;
+        if (t < n) {
+            // preorder position: every ancestor's offset plus one per non-root node on the path
+            pos = depth - 1;
+            for (int x = t; x != -1; x = s_par[x]) pos += s_off[x];
+            if (par == -1) act = GDN_ACT_INIT;
+            else if (s_off[t] == 0) act = GDN_ACT_CONTINUE;  // first child: follows its parent
+            else if (s_later[t] == 0) act = GDN_ACT_POP;     // last child
+            else act = GDN_ACT_TOP;
+            if (s_nchild[t] >= 2) act |= GDN_ACT_PUSH;
+            if (s_nchild[t] == 0) act |= GDN_ACT_LEAF;
+            W.order[lo + pos] = t;
+            W.action[lo + pos] = act;
+            W.depth[lo + t] = depth;
+            int32_t *np = W.nodepath + (size_t)(lo + t) * GDN_MAX_DEPTH;
+            int x = t;
+            for (int s = depth - 1; s >= 0; --s) {
+                np[s] = x;
+                x = s_par[x];
+            }
+            for (int s = depth; s < GDN_MAX_DEPTH; ++s) np[s] = -1;
+        }
+        // stack height after each position = inclusive prefix sum of (push - pop)
+        s_scan[t] = 0;
+        __syncthreads();
+        if (t < n) s_scan[pos] = ((act & GDN_ACT_PUSH) ? 1 : 0) - ((act & 3) == GDN_ACT_POP ? 1 : 0);
+        __syncthreads();
+        for (int step = 1; step < kPlanThreads; step <<= 1) {
+            const int add = t >= step ? s_scan[t - step] : 0;
+            __syncthreads();
+            s_scan[t] += add;
+            __syncthreads();
+        }
+        int m = t < n ? s_scan[t] : 0;
+        // block max through the same buffer
+        s_off[t] = m;
+        __syncthreads();
+        for (int step = kPlanThreads / 2; step > 0; step >>= 1) {
+            if (t < step && s_off[t + step] > s_off[t]) s_off[t] = s_off[t + step];
+            __syncthreads();
+        }
+        max_stack = s_off[0];
+    } else if (range_ok) {
+        // rejected (or empty) sequence: defined metadata
+        for (int i = t; i < n; i += kPlanThreads) {
+            W.order[lo + i] = -1;
+            W.action[lo + i] = 0;
+            W.depth[lo + i] = 0;
+            for (int s = 0; s < GDN_MAX_DEPTH; ++s) W.nodepath[(size_t)(lo + i) * GDN_MAX_DEPTH + s] = -1;
+        }
+    }
+    if (t == 0) {
+        W.seq_status[b] = status;
+        W.seq_info[b * kSeqInfoInts + 0] = range_ok ? lo : 0;
+        W.seq_info[b * kSeqInfoInts + 1] = n;
+        W.seq_info[b * kSeqInfoInts + 2] = max_stack;
+        W.seq_info[b * kSeqInfoInts + 3] = 0;
+        W.path_len[b] = 0;
+    }
+    if (t < GDN_MAX_DEPTH) W.path[b * GDN_MAX_DEPTH + t] = -1;
+}
+
+}  // namespace
+
+hipError_t launch_plan(const Params &p, hipStream_t s) {
+    const int grid = p.B > 0 ? p.B : 1;
+    hipLaunchKernelGGL(plan_kernel, dim3(grid), dim3(kPlanThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,205 @@
+/*
+ * gdn_tree.h -- C ABI of the Gated DeltaNet tree-verify / persist library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes.  A Gated DeltaNet layer keeps, per sequence and
+ * value head, a recurrent state S of D_v x D_k fp32 values next to the KV
+ * cache (GreenGames page, "Why the experiment exists": the SSM state cache of
+ * the 48 Gated DeltaNet layers of a 64-layer hybrid).  One token with key k,
+ * value v, decay a and write strength b updates it by the gated delta rule
+ *
+ *         S' = a * S * (I - b k k^T) + b * v k^T ,       o = S' q .
+ *
+ * (The pages name the kernel -- ggml_gated_delta_net, GreenGames "TL;DR" --
+ * but do not print the rule; this is the reading the library implements.)
+ *
+ * Speculative decoding with DDTree (magik.net page, "The Broader Context";
+ * GreenGames, "From autoregressive to DDTree") verifies a whole tree of draft
+ * tokens in one target forward: every node's state is the rule applied to its
+ * parent's state, the committed state for a root, so each node sees exactly
+ * the tokens on its root-to-node path.  gdn_tree_verify produces o for every
+ * node without touching the committed state.  After acceptance,
+ * gdn_tree_persist replays the accepted root-to-node path and writes its
+ * final state in place into the state cache (GreenGames, "Key wins": the
+ * persist-write kernel that replaced a per-step state copy).
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer except `dims` (and the host outputs of gdn_tree_status) is
+ *    a DEVICE pointer to contiguous memory in the layouts below.  The caller
+ *    owns all memory, including the workspace; the library allocates nothing
+ *    and keeps no mutable global state, so calls with distinct workspaces are
+ *    independent.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on it and returns without synchronizing, except
+ *    gdn_tree_status, which synchronizes `stream`.
+ *  - Errors the host can see (bad dims, NULL pointers, small workspace)
+ *    return a negative gdn_status BEFORE anything is enqueued.  Errors only
+ *    the device can see (malformed tree, bad slot, bad accepted node) mark the
+ *    sequence in the workspace; such a sequence is skipped: its verify
+ *    outputs are NaN and its cache slot is not written.  gdn_tree_status
+ *    reports them.
+ *  - Stream order per decode step: gdn_tree_plan once, then gdn_tree_verify
+ *    for each layer, then (after acceptance) gdn_tree_persist for each layer.
+ *    k, v, a and b of the step must stay alive until persist has run.
+ *
+ * Layouts (row-major, T = total nodes, B = sequences):
+ *   parent       int32 [T]        local node id of the parent inside its own
+ *                                  sequence, -1 for a root (a forest is allowed)
+ *   cu_nodes     int32 [B+1]      sequence b owns nodes [cu_nodes[b], cu_nodes[b+1])
+ *   slot_idx     int32 [B]        state-cache slot of sequence b
+ *   q, k         [T][H_k][D_k]    bf16 or fp32 (dims.qkv_dtype)
+ *   v            [T][H_v][D_v]    bf16 or fp32
+ *   a, b         fp32 [T][H_v]    decay and write strength, already activated
+ *   state_cache  fp32 [num_slots][H_v][D_v][D_k]   (row = value index)
+ *   out          fp32 [T][H_v][D_v]
+ *   Value head h reads key head h / (H_v / H_k).
+ */
+#ifndef GDN_TREE_H
+#define GDN_TREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Longest root-to-node path, in nodes: the 16-token drafting block
+   (GreenGames, "Prefill"). */
+#define GDN_MAX_DEPTH 16
+/* Largest tree (nodes per sequence) one verify call accepts. */
+#define GDN_MAX_NODES 256
+/* Longest chain gdn_chain_verify accepts (it has no depth limit). */
+#define GDN_MAX_CHAIN 65536
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_NULL = -1,        /* a required pointer is NULL */
+    GDN_ERR_SHAPE = -2,       /* dims out of range or inconsistent */
+    GDN_ERR_UNSUPPORTED = -3, /* head dim / dtype without a kernel */
+    GDN_ERR_WORKSPACE = -4,   /* workspace too small, or not planned for these dims */
+    GDN_ERR_LAUNCH = -5,      /* the HIP runtime refused a launch */
+    GDN_ERR_TREE = -6,        /* (gdn_tree_status) at least one sequence was skipped */
+    GDN_ERR_DEVICE = -7       /* (gdn_tree_status) a HIP error while synchronizing */
+} gdn_status;
+
+typedef enum gdn_dtype { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
+
+/* Per-sequence verdicts written into the workspace (first failing check wins). */
+typedef enum gdn_seq_status {
+    GDN_SEQ_OK = 0,
+    GDN_SEQ_BAD_NODES = 1,      /* [cu[b], cu[b+1]) not inside [0, T], or longer than max_nodes */
+    GDN_SEQ_BAD_SLOT = 2,       /* slot_idx[b] outside [0, num_slots) (non-empty sequences only) */
+    GDN_SEQ_DUP_SLOT = 3,       /* slot shared by two non-empty sequences (both flagged) */
+    GDN_SEQ_BAD_PARENT = 4,     /* parent outside {-1} U [0, n) or a node's own id */
+    GDN_SEQ_CYCLE_OR_DEPTH = 5, /* an ancestor walk does not reach a root within max_depth nodes */
+    GDN_SEQ_BAD_ACCEPT = 6      /* accepted_node outside {-1} U [0, n) (set by persist) */
+} gdn_seq_status;
+
+/* Traversal action word (one per visited position, see gdn_tree_plan). */
+enum {
+    GDN_ACT_CONTINUE = 0, /* parent state = the state just produced */
+    GDN_ACT_TOP = 1,      /* parent state = copy of the stack top */
+    GDN_ACT_POP = 2,      /* parent state = stack top, popped */
+    GDN_ACT_INIT = 3,     /* parent state = committed state (a root) */
+    GDN_ACT_PUSH = 4,     /* push this node's state (it has >= 2 children) */
+    GDN_ACT_LEAF = 8      /* no children: its state is never needed again */
+};
+
+typedef struct gdn_dims {
+    int32_t num_seqs;    /* B >= 0 */
+    int32_t total_nodes; /* T >= 0; must equal cu_nodes[B] */
+    int32_t max_nodes;   /* upper bound on nodes per sequence, <= GDN_MAX_NODES (trees) */
+    int32_t max_depth;   /* depth limit in nodes, 1 .. GDN_MAX_DEPTH */
+    int32_t num_k_heads; /* H_k >= 1 */
+    int32_t num_v_heads; /* H_v, a multiple of H_k */
+    int32_t head_dim;    /* D = D_k = D_v, one of 16, 32, 64, 128 */
+    int32_t num_slots;   /* slots in state_cache, >= 1 when B > 0 */
+    int32_t qkv_dtype;   /* gdn_dtype of q, k, v */
+} gdn_dims;
+
+/* Bytes of workspace gdn_tree_plan/verify/persist need for these dims
+   (0 if the dims are invalid).  The caller allocates it (device memory, no
+   initialization needed); one workspace serves one decode step. */
+size_t gdn_workspace_bytes(const gdn_dims *dims);
+
+/*
+ * gdn_tree_plan -- validate the draft trees and build traversal metadata on
+ * the device (one workgroup per sequence).  Per node: depth (root = 1) and the
+ * root-to-node path.  Per sequence: a depth-first preorder in which the
+ * children of a node (and the roots of a forest) are visited by increasing
+ * (subtree size, node id), so the largest child comes last and is entered
+ * without saving the parent's state; the per-position action words tell the
+ * recurrent verify how to obtain each node's parent state.  Also writes each
+ * sequence's verdict.  Reads parent, cu_nodes, slot_idx; writes only `ws`.
+ */
+int gdn_tree_plan(const gdn_dims *dims, const int32_t *parent, const int32_t *cu_nodes,
+                  const int32_t *slot_idx, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * gdn_tree_verify -- for every node n of every valid sequence and every value
+ * head, o_n = S^n q_n where S^n is the gated delta rule applied along n's
+ * root-to-node path starting from state_cache[slot_idx[b]].  state_cache is
+ * only read.  Sequences the plan rejected get NaN outputs.  `ws` must come
+ * from gdn_tree_plan with the same dims on the same stream.
+ */
+int gdn_tree_verify(const gdn_dims *dims, const void *q, const void *k, const void *v,
+                    const float *a, const float *b, const float *state_cache,
+                    const int32_t *slot_idx, float *out, const void *ws, size_t ws_bytes,
+                    void *stream);
+
+/*
+ * gdn_tree_persist -- for each sequence b with accepted_node[b] = m >= 0,
+ * replay the rule over the root-to-m path from state_cache[slot_idx[b]] and
+ * write the result in place into that slot.  accepted_node[b] = -1 skips the
+ * sequence.  Only the slots of valid, accepted sequences are written.  Also
+ * records the accepted path (root first) and its length in the workspace.
+ */
+int gdn_tree_persist(const gdn_dims *dims, const void *k, const void *v, const float *a,
+                     const float *b, const int32_t *accepted_node, float *state_cache,
+                     const int32_t *slot_idx, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * gdn_chain_verify -- the W = 1 case: sequence b is the linear chain of nodes
+ * [cu_nodes[b], cu_nodes[b+1]) (no parent array, no plan, no depth limit;
+ * lengths up to dims.max_nodes <= GDN_MAX_CHAIN).  Writes o for every node
+ * (q and out may both be NULL to skip outputs) and, when final_len and
+ * final_state are given, the state after the first final_len[b] nodes into
+ * final_state [B][H_v][D_v][D_k] (final_len[b] = 0 writes the committed state;
+ * a value outside [0, n_b] writes nothing).  state_cache is only read and
+ * final_state must not overlap it.  `ws` may be NULL; if given (sized by
+ * gdn_workspace_bytes for the same dims) the per-sequence verdicts are
+ * written there for gdn_tree_status.
+ */
+int gdn_chain_verify(const gdn_dims *dims, const int32_t *cu_nodes, const void *q, const void *k,
+                     const void *v, const float *a, const float *b, const float *state_cache,
+                     const int32_t *slot_idx, float *out, const int32_t *final_len,
+                     float *final_state, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * gdn_tree_read_metadata -- device-to-device copies of what the plan (and the
+ * last persist) stored: depth [T], order [T] (node ids by visit position,
+ * offset by cu_nodes), action [T], path [B][GDN_MAX_DEPTH] (root first,
+ * padded with -1), path_len [B], seq_status [B].  Any output may be NULL.
+ */
+int gdn_tree_read_metadata(const gdn_dims *dims, const void *ws, size_t ws_bytes, int32_t *depth,
+                           int32_t *order, int32_t *action, int32_t *path, int32_t *path_len,
+                           int32_t *seq_status, void *stream);
+
+/*
+ * gdn_tree_status -- synchronizes `stream`, then reads the verdicts in `ws`.
+ * Returns GDN_OK, GDN_ERR_TREE (some sequence was skipped; *first_bad_seq and
+ * *first_bad_code name the lowest such sequence and its gdn_seq_status),
+ * GDN_ERR_WORKSPACE (ws was never planned) or GDN_ERR_DEVICE.  The two
+ * outputs are HOST pointers and may be NULL.
+ */
+int gdn_tree_status(const void *ws, size_t ws_bytes, void *stream, int32_t *first_bad_seq,
+                    int32_t *first_bad_code);
+
+/* Static string for a gdn_status value. */
+const char *gdn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_TREE_H */

@@ -1,0 +1,52 @@
+"""The C-ABI library loads and exports every entry point include/gdn_tree.h
+declares; pure host-side calls behave as documented (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn_tree.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gdn_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import gated_deltanet_tree_amd as G
+    if not os.path.exists(G.LIB_PATH):
+        from gated_deltanet_tree_amd import build
+        build.build()
+    return G.load_library()
+
+
+def test_header_declares_expected_entry_points():
+    import gated_deltanet_tree_amd as G
+    assert _declared() == sorted(G.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_host_only_calls(lib):
+    import gated_deltanet_tree_amd as G
+    dims = G.make_dims(32, 736, 23, 16, 48, 128, 32, G.GDN_BF16)
+    n = G.workspace_bytes(dims)
+    assert n > 0 and n % 256 == 0
+    bad = G.make_dims(1, 4, 8, 2, 3, 128, 1, G.GDN_BF16)
+    assert G.workspace_bytes(bad) == 0
+    assert G.strerror(0) == "ok"
+    assert "workspace" in G.strerror(-4)
+    # argument errors are reported before anything touches the device
+    assert lib.gdn_tree_plan(None, None, None, None, None, 0, None) == -1
+    assert lib.gdn_tree_plan(ctypes.byref(dims), None, None, None, None, 0, None) == -1
+    rc = lib.gdn_tree_verify(ctypes.byref(bad), None, None, None, None, None, None, None, None,
+                             ctypes.c_void_p(1), 1 << 20, None)
+    assert rc == -2
+    assert lib.gdn_tree_status(None, 0, None, None, None) == -1

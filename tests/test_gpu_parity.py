@@ -1,0 +1,256 @@
+"""GPU parity: the HIP path against the fp64 oracle on the seeded workloads.
+
+Bar: per (sequence, value head) slice, max|gpu - oracle| / max|oracle| <= 2e-3
+for outputs and persisted states; integer metadata exact; GPU-internal
+invariants bitwise."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import plan as P
+from gpu_support import TOL, device_case, host_case, require_gpu, run_step, slice_rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["tiny", "chain", "ddtree22", "batched"]
+
+
+def _out_err(case, out):
+    cfg = case["cfg"]
+    worst = 0.0
+    for s in range(cfg.num_seqs):
+        lo, hi = int(case["cu"][s]), int(case["cu"][s + 1])
+        # slice = (sequence, value head): all nodes x all rows
+        x = out[lo:hi].transpose(1, 0, 2).reshape(cfg.num_v_heads, -1)
+        r = case["exp_out"][lo:hi].transpose(1, 0, 2).reshape(cfg.num_v_heads, -1)
+        worst = max(worst, slice_rel_err(x, r))
+    return worst
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_plan_metadata_exact(name):
+    G = require_gpu()
+    case = host_case(name)
+    d = device_case(G, case)
+    run_step(G, d, persist=True)
+    md = {k: v.cpu().numpy() for k, v in G.read_metadata(d["dims"], d["ws"]).items()}
+    assert (md["seq_status"] == 0).all()
+    for s, par in enumerate(case["trees"]):
+        lo, hi = int(case["cu"][s]), int(case["cu"][s + 1])
+        ref = P.plan_tree(par)
+        assert np.array_equal(md["depth"][lo:hi], ref["depth"])
+        assert np.array_equal(md["order"][lo:hi], ref["order"])
+        assert np.array_equal(md["action"][lo:hi], ref["action"])
+        _, path = case["exp_persist"][s]
+        assert md["path_len"][s] == len(path)
+        assert np.array_equal(md["path"][s][: len(path)], path)
+        assert (md["path"][s][len(path):] == -1).all()
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_verify_and_persist_parity(name):
+    G = require_gpu()
+    case = host_case(name)
+    d = device_case(G, case)
+    print("case", name, flush=True)
+    run_step(G, d, persist=False)
+    out = d["out"].cpu().numpy()
+    err = _out_err(case, out)
+    print("verify max slice rel err", err)
+    assert err <= TOL
+    # verify only reads the cache
+    assert np.array_equal(d["cache"].cpu().numpy().view(np.uint32), case["cache"].view(np.uint32))
+    G.gdn_tree_persist(d["dims"], d["k"], d["v"], d["a"], d["b"], d["acc"], d["cache"], d["slots"], d["ws"])
+    torch.cuda.synchronize()
+    cache = d["cache"].cpu().numpy()
+    touched = set()
+    worst = 0.0
+    for s in range(case["cfg"].num_seqs):
+        st, _ = case["exp_persist"][s]
+        slot = int(case["slots"][s])
+        touched.add(slot)
+        worst = max(worst, slice_rel_err(cache[slot].reshape(case["cfg"].num_v_heads, -1),
+                                         st.reshape(case["cfg"].num_v_heads, -1)))
+    print("persist max slice rel err", worst)
+    assert worst <= TOL
+    for slot in range(case["num_slots"]):
+        if slot not in touched:
+            assert np.array_equal(cache[slot].view(np.uint32), case["cache"][slot].view(np.uint32))
+
+
+def test_persist_leaves_spare_slots_untouched():
+    G = require_gpu()
+    case = host_case("ddtree22", extra_slots=3)
+    d = device_case(G, case)
+    run_step(G, d, persist=True)
+    cache = d["cache"].cpu().numpy()
+    slot = int(case["slots"][0])
+    for s in range(case["num_slots"]):
+        if s != slot:
+            assert np.array_equal(cache[s].view(np.uint32), case["cache"][s].view(np.uint32))
+    st, _ = case["exp_persist"][0]
+    assert slice_rel_err(cache[slot].reshape(48, -1), st.reshape(48, -1)) <= TOL
+
+
+def test_long_memory_gates():
+    """Gates a in [0.9, 1) keep the committed state visible deep into the tree."""
+    G = require_gpu()
+    case = host_case("ddtree22", a_low=0.9)
+    d = device_case(G, case)
+    run_step(G, d, persist=True)
+    assert _out_err(case, d["out"].cpu().numpy()) <= TOL
+    st, _ = case["exp_persist"][0]
+    got = d["cache"].cpu().numpy()[int(case["slots"][0])]
+    assert slice_rel_err(got.reshape(48, -1), st.reshape(48, -1)) <= TOL
+
+
+def _chain_call(G, d, cu, q, k, v, a, b, final_len=None, want_final=False, max_nodes=None):
+    dims = d["dims"]
+    n = int(cu[-1].item())
+    cdims = G.make_dims(num_seqs=len(cu) - 1, total_nodes=n, max_nodes=max_nodes or max(n, 1),
+                        num_k_heads=dims.num_k_heads, num_v_heads=dims.num_v_heads, head_dim=dims.head_dim,
+                        num_slots=dims.num_slots, qkv_dtype=dims.qkv_dtype, max_depth=dims.max_depth)
+    out = torch.full((n, dims.num_v_heads, dims.head_dim), float("nan"), device="cuda")
+    fin = None
+    if want_final:
+        fin = torch.full((len(cu) - 1, dims.num_v_heads, dims.head_dim, dims.head_dim), float("nan"), device="cuda")
+    G.gdn_chain_verify(cdims, cu, q, k, v, a, b, d["cache"], d["slots"], out, final_len, fin)
+    torch.cuda.synchronize()
+    return out, fin
+
+
+def test_chain_tree_bitwise_and_persist_bitwise():
+    """On the W=1 chain the tree kernel equals the chain kernel bit for bit,
+    and the persisted state equals the chain kernel's state after the
+    accepted prefix bit for bit."""
+    G = require_gpu()
+    case = host_case("chain")
+    d = device_case(G, case)
+    run_step(G, d, persist=False)
+    tree_out = d["out"].clone()
+    flen = torch.tensor([int(case["acc"][0]) + 1], dtype=torch.int32, device="cuda")
+    out, fin = _chain_call(G, d, d["cu"], d["q"], d["k"], d["v"], d["a"], d["b"], flen, True)
+    assert torch.equal(tree_out.view(torch.int32), out.view(torch.int32))
+    G.gdn_tree_persist(d["dims"], d["k"], d["v"], d["a"], d["b"], d["acc"], d["cache"], d["slots"], d["ws"])
+    torch.cuda.synchronize()
+    slot = int(case["slots"][0])
+    assert torch.equal(d["cache"][slot].view(torch.int32), fin[0].view(torch.int32))
+
+
+def test_tree_is_union_of_chains():
+    """Along every root-to-leaf path the tree's outputs equal the chain kernel
+    run over that path's tokens (bitwise), and persisting any node equals the
+    chain kernel's final state over its path (bitwise)."""
+    G = require_gpu()
+    case = host_case("ddtree22")
+    d = device_case(G, case)
+    run_step(G, d, persist=False)
+    par = case["trees"][0]
+    n = len(par)
+    leaves = [i for i in range(n) if i not in set(par.tolist())]
+    for leaf in leaves:
+        path = []
+        j = leaf
+        while j != -1:
+            path.append(j)
+            j = int(par[j])
+        path = path[::-1]
+        idx = torch.tensor(path, dtype=torch.long, device="cuda")
+        cu = torch.tensor([0, len(path)], dtype=torch.int32, device="cuda")
+        flen = torch.tensor([len(path)], dtype=torch.int32, device="cuda")
+        out, fin = _chain_call(G, d, cu, d["q"][idx].contiguous(), d["k"][idx].contiguous(),
+                               d["v"][idx].contiguous(), d["a"][idx].contiguous(), d["b"][idx].contiguous(),
+                               flen, True)
+        assert torch.equal(out.view(torch.int32), d["out"][idx].view(torch.int32)), leaf
+        # persist of this leaf (fresh cache copy) equals the chain's final state
+        cache = d["cache"].clone()
+        acc = torch.tensor([leaf], dtype=torch.int32, device="cuda")
+        G.gdn_tree_persist(d["dims"], d["k"], d["v"], d["a"], d["b"], acc, cache, d["slots"], d["ws"])
+        torch.cuda.synchronize()
+        slot = int(case["slots"][0])
+        assert torch.equal(cache[slot].view(torch.int32), fin[0].view(torch.int32)), leaf
+
+
+def test_duplicate_siblings_and_relabeling_bitwise():
+    G = require_gpu()
+    import workloads as W
+    cfg = W.get_config("ddtree22")
+    case = host_case("ddtree22")
+    d = device_case(G, case)
+    # duplicate: give node 16 (child of root) the inputs of node 1 (the chain's first draft)
+    par = case["trees"][0]
+    sib = [i for i in range(len(par)) if par[i] == 0 and i != 1][0]
+    for key in ("q", "k", "v", "a", "b"):
+        d[key][sib] = d[key][1]
+    run_step(G, d, persist=False)
+    assert torch.equal(d["out"][sib].view(torch.int32), d["out"][1].view(torch.int32))
+    base = d["out"].clone()
+    # relabel the nodes with a random permutation: outputs move with their nodes
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(len(par))
+    inv = np.argsort(perm)
+    new_par = W.relabel(par, perm)
+    invt = torch.tensor(inv, dtype=torch.long, device="cuda")
+    d2 = dict(d)
+    for key in ("q", "k", "v", "a", "b"):
+        d2[key] = d[key][invt].contiguous()
+    d2["parent"] = to_dev(new_par.astype(np.int32))
+    d2["out"] = torch.full_like(d["out"], float("nan"))
+    run_step(G, d2, persist=False)
+    permt = torch.tensor(perm, dtype=torch.long, device="cuda")
+    assert torch.equal(d2["out"][permt].view(torch.int32), base.view(torch.int32))
+    del cfg
+
+
+def test_empty_and_ragged_batch():
+    """Sequences of different sizes, an empty one and a forest, in one call."""
+    G = require_gpu()
+    import workloads as W
+    rng = np.random.default_rng(8)
+    hk, hv, d_ = 2, 6, 32
+    trees = [W.random_tree(rng, 9, 5), np.zeros(0, np.int32), np.array([-1, 0, -1, 2, 2], np.int32),
+             W.chain_tree(16), W.random_tree(rng, 40, 16)]
+    cu = W.cu_from_trees(trees)
+    T = int(cu[-1])
+    q = rng.standard_normal((T, hk, d_))
+    k = rng.standard_normal((T, hk, d_))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    inp = {"q": W.f32_to_bf16_bits(q.astype(np.float32)), "k": W.f32_to_bf16_bits(k.astype(np.float32)),
+           "v": W.f32_to_bf16_bits(rng.standard_normal((T, hv, d_)).astype(np.float32)),
+           "a": rng.uniform(0.3, 1.0, (T, hv)).astype(np.float32), "b": rng.uniform(0.0, 1.0, (T, hv)).astype(np.float32)}
+    S0 = (0.3 * rng.standard_normal((5, hv, d_, d_))).astype(np.float32)
+    slots = np.array([4, 0, 2, 1, 3], np.int32)
+    cache = np.full((6, hv, d_, d_), 7.0, np.float32)
+    for s in range(5):
+        cache[slots[s]] = S0[s]
+    acc = np.array([3, -1, 4, 15, 39], np.int32)
+    dims = G.make_dims(5, T, 40, hk, hv, d_, 6, G.GDN_BF16)
+    ws = G.new_workspace(dims)
+    dev = {k_: to_dev(v_) for k_, v_ in inp.items()}
+    cache_d = to_dev(cache.copy())
+    out = torch.full((T, hv, d_), float("nan"), device="cuda")
+    G.gdn_tree_plan(dims, to_dev(np.concatenate(trees).astype(np.int32)), to_dev(cu.astype(np.int32)),
+                    to_dev(slots), ws)
+    G.gdn_tree_verify(dims, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], cache_d, to_dev(slots), out, ws)
+    G.gdn_tree_persist(dims, dev["k"], dev["v"], dev["a"], dev["b"], to_dev(acc), cache_d, to_dev(slots), ws)
+    rc, bad, code = G.gdn_tree_status(ws)
+    assert rc == 0, (rc, bad, code)
+    exp = oracle.verify_batch(trees, cu, inp, S0)
+    got = out.cpu().numpy()
+    for s in range(5):
+        lo, hi = int(cu[s]), int(cu[s + 1])
+        if hi > lo:
+            x = got[lo:hi].transpose(1, 0, 2).reshape(hv, -1)
+            r = exp[lo:hi].transpose(1, 0, 2).reshape(hv, -1)
+            assert slice_rel_err(x, r) <= TOL, s
+    res = oracle.persist_batch(trees, cu, inp, S0, acc)
+    cache_after = cache_d.cpu().numpy()
+    for s in range(5):
+        st, _ = res[s]
+        if st is None:
+            assert np.array_equal(cache_after[slots[s]].view(np.uint32), cache[slots[s]].view(np.uint32))
+        else:
+            assert slice_rel_err(cache_after[slots[s]].reshape(hv, -1), st.reshape(hv, -1)) <= TOL
+    assert np.array_equal(cache_after[5].view(np.uint32), cache[5].view(np.uint32))
