@@ -102,6 +102,8 @@ int gdn_tree_verify(const gdn_dims *dims, const void *q, const void *k, const vo
     p.out = out;
     p.ws = gdn::ws_ptrs(const_cast<void *>(ws), p.B, p.T);
     p.has_ws = 1;
+    if (gdn::fast_path_supported(p.D, dims->qkv_dtype))
+        return launched(gdn::launch_tree_verify_fast(p, as_stream(stream)));
     return launched(gdn::launch_tree_verify_recurrent(p, dims->qkv_dtype, as_stream(stream)));
 }
 
@@ -126,6 +128,8 @@ int gdn_tree_persist(const gdn_dims *dims, const void *k, const void *v, const f
     p.slot_idx = slot_idx;
     p.ws = gdn::ws_ptrs(ws, p.B, p.T);
     p.has_ws = 1;
+    if (gdn::fast_path_supported(p.D, dims->qkv_dtype))
+        return launched(gdn::launch_persist_fast(p, as_stream(stream)));
     return launched(gdn::launch_persist_recurrent(p, dims->qkv_dtype, as_stream(stream)));
 }
 
@@ -158,6 +162,8 @@ int gdn_chain_verify(const gdn_dims *dims, const int32_t *cu_nodes, const void *
         p.ws = gdn::ws_ptrs(ws, p.B, p.T);
         p.has_ws = 1;
     }
+    if (gdn::fast_path_supported(p.D, dims->qkv_dtype))
+        return launched(gdn::launch_chain_verify_fast(p, as_stream(stream)));
     return launched(gdn::launch_chain_verify_recurrent(p, dims->qkv_dtype, as_stream(stream)));
 }
 

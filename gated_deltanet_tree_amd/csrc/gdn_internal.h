@@ -82,6 +82,12 @@ hipError_t launch_plan(const Params &p, hipStream_t s);
 hipError_t launch_tree_verify_recurrent(const Params &p, int dtype, hipStream_t s);
 hipError_t launch_chain_verify_recurrent(const Params &p, int dtype, hipStream_t s);
 hipError_t launch_persist_recurrent(const Params &p, int dtype, hipStream_t s);
+// MFMA path (D in {64, 128}, bf16 q/k/v)
+bool fast_path_supported(int D, int dtype);
+size_t fast_tree_lds_bytes(int max_nodes, int D);
+hipError_t launch_tree_verify_fast(const Params &p, hipStream_t s);
+hipError_t launch_chain_verify_fast(const Params &p, hipStream_t s);
+hipError_t launch_persist_fast(const Params &p, hipStream_t s);
 
 // Largest LDS stack the heavy-last preorder can need for trees of n nodes:
 // k nested pushes need a subtree of at least 2^(k+1) - 1 nodes.

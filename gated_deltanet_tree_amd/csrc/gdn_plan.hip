@@ -38,7 +38,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params P) {
     // ---- node range ---------------------------------------------------------
     const int lo = P.cu_nodes[b], hi = P.cu_nodes[b + 1];
     int status = GDN_SEQ_OK;
-    const bool range_ok = 0 <= lo && lo <= hi && hi <= P.T && hi - lo <= P.max_nodes;
+    // in_bounds: the range lies inside [0, T] (its outputs can be NaN-filled);
+    // range_ok: additionally no longer than max_nodes
+    const bool in_bounds = 0 <= lo && lo <= hi && hi <= P.T;
+    const bool range_ok = in_bounds && hi - lo <= P.max_nodes;
     if (!range_ok) status = GDN_SEQ_BAD_NODES;
     const int n = range_ok ? hi - lo : 0;
 
@@ -150,9 +153,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params P) {
             __syncthreads();
         }
         max_stack = s_off[0];
-    } else if (range_ok) {
+    } else if (in_bounds) {
         // rejected (or empty) sequence: defined metadata
-        for (int i = t; i < n; i += kPlanThreads) {
+        for (int i = t; i < hi - lo; i += kPlanThreads) {
             W.order[lo + i] = -1;
             W.action[lo + i] = 0;
             W.depth[lo + i] = 0;
@@ -161,8 +164,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params P) {
     }
     if (t == 0) {
         W.seq_status[b] = status;
-        W.seq_info[b * kSeqInfoInts + 0] = range_ok ? lo : 0;
-        W.seq_info[b * kSeqInfoInts + 1] = n;
+        W.seq_info[b * kSeqInfoInts + 0] = in_bounds ? lo : 0;
+        W.seq_info[b * kSeqInfoInts + 1] = in_bounds ? hi - lo : 0;
         W.seq_info[b * kSeqInfoInts + 2] = max_stack;
         W.seq_info[b * kSeqInfoInts + 3] = 0;
         W.path_len[b] = 0;

@@ -257,9 +257,10 @@ __global__ __launch_bounds__(64) void chain_verify_kernel(Params P) {
     using G = Geo<D>;
     const Tile t = tile_of<D>(P);
     const int lo = P.cu_nodes[t.b], hi = P.cu_nodes[t.b + 1];
-    const bool range_ok = 0 <= lo && lo <= hi && hi <= P.T && hi - lo <= P.max_nodes;
-    const int n = range_ok ? hi - lo : 0;
-    const int slot = n > 0 ? P.slot_idx[t.b] : 0;
+    const bool in_bounds = 0 <= lo && lo <= hi && hi <= P.T;
+    const bool range_ok = in_bounds && hi - lo <= P.max_nodes;
+    const int n = in_bounds ? hi - lo : 0;
+    const int slot = (range_ok && n > 0) ? P.slot_idx[t.b] : 0;
     int status = GDN_SEQ_OK;
     if (!range_ok) status = GDN_SEQ_BAD_NODES;
     else if (n > 0 && (slot < 0 || slot >= P.num_slots)) status = GDN_SEQ_BAD_SLOT;

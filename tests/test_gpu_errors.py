@@ -13,7 +13,9 @@ from gpu_support import TOL, require_gpu, slice_rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
-HK, HV, D = 2, 4, 16
+HK, HV = 2, 4
+# (head dim, q/k/v storage): D=16 fp32 runs the recurrent kernels, D=64 bf16 the MFMA kernels
+PATHS = {"recurrent": (16, "f32"), "mfma": (64, "bf16")}
 
 
 def _base(rng, n_each=(7, 9, 6, 8)):
@@ -21,13 +23,14 @@ def _base(rng, n_each=(7, 9, 6, 8)):
     return trees
 
 
-def _inputs(rng, T):
+def _inputs(rng, T, D, dt):
     q = rng.standard_normal((T, HK, D))
     k = rng.standard_normal((T, HK, D))
     q /= np.linalg.norm(q, axis=-1, keepdims=True)
     k /= np.linalg.norm(k, axis=-1, keepdims=True)
-    return {"q": q.astype(np.float32), "k": k.astype(np.float32),
-            "v": rng.standard_normal((T, HV, D)).astype(np.float32),
+    v = rng.standard_normal((T, HV, D))
+    cast = (lambda x: x.astype(np.float32)) if dt == "f32" else (lambda x: W.f32_to_bf16_bits(x.astype(np.float32)))
+    return {"q": cast(q), "k": cast(k), "v": cast(v),
             "a": rng.uniform(0.3, 1.0, (T, HV)).astype(np.float32),
             "b": rng.uniform(0.0, 1.0, (T, HV)).astype(np.float32)}
 
@@ -61,10 +64,12 @@ def _make(name, rng):
     return trees, slots, cu, max_depth, max_nodes
 
 
+@pytest.mark.parametrize("path", sorted(PATHS))
 @pytest.mark.parametrize("name", ["bad_parent_range", "self_parent", "cycle", "too_deep", "bad_slot",
                                   "dup_slot", "bad_range"])
-def test_rejected_sequence(name):
+def test_rejected_sequence(name, path):
     G = require_gpu()
+    D, dt = PATHS[path]
     rng = np.random.default_rng(sum(map(ord, name)))
     trees, slots, cu, max_depth, max_nodes = _make(name, rng)
     parent = np.concatenate(trees).astype(np.int32)
@@ -72,9 +77,10 @@ def test_rejected_sequence(name):
     num_slots = 4
     expect = P.validate(parent, cu, slots, num_slots, max_nodes, max_depth)
     assert (expect != 0).any()
-    inp = _inputs(rng, T)
+    inp = _inputs(rng, T, D, dt)
     cache = rng.standard_normal((num_slots, HV, D, D)).astype(np.float32)
-    dims = G.make_dims(4, T, max_nodes, HK, HV, D, num_slots, G.GDN_F32, max_depth=max_depth)
+    dims = G.make_dims(4, T, max_nodes, HK, HV, D, num_slots, G.GDN_F32 if dt == "f32" else G.GDN_BF16,
+                       max_depth=max_depth)
     ws = G.new_workspace(dims)
     dev = {k: to_dev(v) for k, v in inp.items()}
     cache_d = to_dev(cache.copy())
@@ -110,17 +116,19 @@ def test_rejected_sequence(name):
             assert slice_rel_err(after[slots[s]].reshape(HV, -1), st.reshape(HV, -1)) <= TOL
 
 
-def test_bad_accepted_node():
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_bad_accepted_node(path):
     G = require_gpu()
+    D, dt = PATHS[path]
     rng = np.random.default_rng(4)
     trees = _base(rng)
     parent = np.concatenate(trees).astype(np.int32)
     cu = W.cu_from_trees(trees)
     T = len(parent)
     slots = np.array([0, 1, 2, 3], np.int32)
-    inp = _inputs(rng, T)
+    inp = _inputs(rng, T, D, dt)
     cache = rng.standard_normal((4, HV, D, D)).astype(np.float32)
-    dims = G.make_dims(4, T, 16, HK, HV, D, 4, G.GDN_F32)
+    dims = G.make_dims(4, T, 16, HK, HV, D, 4, G.GDN_F32 if dt == "f32" else G.GDN_BF16)
     ws = G.new_workspace(dims)
     dev = {k: to_dev(v) for k, v in inp.items()}
     cache_d = to_dev(cache.copy())

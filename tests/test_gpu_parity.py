@@ -203,14 +203,16 @@ def test_duplicate_siblings_and_relabeling_bitwise():
     del cfg
 
 
-def test_empty_and_ragged_batch():
-    """Sequences of different sizes, an empty one and a forest, in one call."""
+@pytest.mark.parametrize("d_", [32, 64, 128])
+def test_empty_and_ragged_batch(d_):
+    """Sequences of different sizes, an empty one and a forest, in one call
+    (D=32 runs the recurrent kernels, D=64/128 the MFMA kernels)."""
     G = require_gpu()
     import workloads as W
     rng = np.random.default_rng(8)
-    hk, hv, d_ = 2, 6, 32
+    hk, hv = 2, 6
     trees = [W.random_tree(rng, 9, 5), np.zeros(0, np.int32), np.array([-1, 0, -1, 2, 2], np.int32),
-             W.chain_tree(16), W.random_tree(rng, 40, 16)]
+             W.chain_tree(16), W.random_tree(rng, 70, 16)]
     cu = W.cu_from_trees(trees)
     T = int(cu[-1])
     q = rng.standard_normal((T, hk, d_))
@@ -225,8 +227,8 @@ def test_empty_and_ragged_batch():
     cache = np.full((6, hv, d_, d_), 7.0, np.float32)
     for s in range(5):
         cache[slots[s]] = S0[s]
-    acc = np.array([3, -1, 4, 15, 39], np.int32)
-    dims = G.make_dims(5, T, 40, hk, hv, d_, 6, G.GDN_BF16)
+    acc = np.array([3, -1, 4, 15, 69], np.int32)
+    dims = G.make_dims(5, T, 70, hk, hv, d_, 6, G.GDN_BF16)
     ws = G.new_workspace(dims)
     dev = {k_: to_dev(v_) for k_, v_ in inp.items()}
     cache_d = to_dev(cache.copy())

@@ -1,0 +1,134 @@
+"""GPU parity at the edges: long chains (chunked), the largest tree a call
+accepts, and the stress workload at full size with sampled sequences."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_support import TOL, require_gpu, slice_rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _unit(rng, *shape):
+    g = rng.standard_normal(shape)
+    return g / np.linalg.norm(g, axis=-1, keepdims=True)
+
+
+def _bf(x):
+    return W.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+@pytest.mark.parametrize("d_", [32, 128])
+def test_long_chain_outputs_and_final_states(d_):
+    """Chains longer than one 16-node chunk, with final states taken at chunk
+    boundaries and inside chunks."""
+    G = require_gpu()
+    rng = np.random.default_rng(21)
+    hk, hv = 2, 4
+    lens = [64, 17, 5, 40]
+    fl = np.array([64, 16, 0, 33], np.int32)
+    cu = np.zeros(len(lens) + 1, np.int32)
+    cu[1:] = np.cumsum(lens)
+    T = int(cu[-1])
+    inp = {"q": _bf(_unit(rng, T, hk, d_)), "k": _bf(_unit(rng, T, hk, d_)),
+           "v": _bf(rng.standard_normal((T, hv, d_))),
+           "a": rng.uniform(0.5, 1.0, (T, hv)).astype(np.float32),
+           "b": rng.uniform(0.0, 1.0, (T, hv)).astype(np.float32)}
+    S0 = (0.3 * rng.standard_normal((len(lens), hv, d_, d_))).astype(np.float32)
+    slots = np.arange(len(lens), dtype=np.int32)
+    dims = G.make_dims(len(lens), T, max(lens), hk, hv, d_, len(lens), G.GDN_BF16)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    out = torch.full((T, hv, d_), float("nan"), device="cuda")
+    fin = torch.full((len(lens), hv, d_, d_), float("nan"), device="cuda")
+    G.gdn_chain_verify(dims, to_dev(cu), dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], to_dev(S0),
+                       to_dev(slots), out, to_dev(fl), fin)
+    torch.cuda.synchronize()
+    got, gfin = out.cpu().numpy(), fin.cpu().numpy()
+    for s, L in enumerate(lens):
+        lo, hi = int(cu[s]), int(cu[s + 1])
+        sl = {k: v[lo:hi] for k, v in inp.items()}
+        ref, _ = oracle.chain(sl["k"], sl["v"], sl["a"], sl["b"], S0[s], q=sl["q"])
+        assert slice_rel_err(got[lo:hi].transpose(1, 0, 2).reshape(hv, -1),
+                             ref.transpose(1, 0, 2).reshape(hv, -1)) <= TOL, s
+        f = int(fl[s])
+        _, ref_fin = oracle.chain(sl["k"][:f], sl["v"][:f], sl["a"][:f], sl["b"][:f], S0[s])
+        assert slice_rel_err(gfin[s].reshape(hv, -1), ref_fin.reshape(hv, -1)) <= TOL, s
+
+
+def test_largest_tree():
+    """A 256-node tree (the per-call maximum), depth up to 16."""
+    G = require_gpu()
+    rng = np.random.default_rng(22)
+    hk, hv, d_ = 1, 3, 128
+    par = W.random_tree(rng, 256, 16)
+    T = 256
+    inp = {"q": _bf(_unit(rng, T, hk, d_)), "k": _bf(_unit(rng, T, hk, d_)),
+           "v": _bf(rng.standard_normal((T, hv, d_))),
+           "a": rng.uniform(0.5, 1.0, (T, hv)).astype(np.float32),
+           "b": rng.uniform(0.0, 1.0, (T, hv)).astype(np.float32)}
+    S0 = (0.3 * rng.standard_normal((1, hv, d_, d_))).astype(np.float32)
+    dims = G.make_dims(1, T, 256, hk, hv, d_, 1, G.GDN_BF16)
+    ws = G.new_workspace(dims)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    cache = to_dev(S0.copy())
+    slots = to_dev(np.zeros(1, np.int32))
+    out = torch.full((T, hv, d_), float("nan"), device="cuda")
+    m = int(np.argmax(W.tree_depths(par)))
+    G.gdn_tree_plan(dims, to_dev(par), to_dev(np.array([0, T], np.int32)), slots, ws)
+    G.gdn_tree_verify(dims, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], cache, slots, out, ws)
+    G.gdn_tree_persist(dims, dev["k"], dev["v"], dev["a"], dev["b"], to_dev(np.array([m], np.int32)), cache,
+                       slots, ws)
+    rc, bad, code = G.gdn_tree_status(ws)
+    assert rc == 0, (rc, bad, code)
+    ref = oracle.tree(par, inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], S0[0])
+    assert slice_rel_err(out.cpu().numpy().transpose(1, 0, 2).reshape(hv, -1),
+                         ref.transpose(1, 0, 2).reshape(hv, -1)) <= TOL
+    st, _ = oracle.accept_state(par, m, inp["k"], inp["v"], inp["a"], inp["b"], S0[0])
+    assert slice_rel_err(cache.cpu().numpy()[0].reshape(hv, -1), st.reshape(hv, -1)) <= TOL
+
+
+def test_stress_full_size_sampled():
+    """The stress workload at full size (64 sequences x 65 nodes, 48/16 heads,
+    d=128), one layer call in the bench's launch configuration; sampled
+    sequences checked against the oracle, every other slot checked for being
+    written only by its own sequence."""
+    G = require_gpu()
+    cfg = W.get_config("stress")
+    trees = W.make_trees(cfg)
+    cu = W.cu_from_trees(trees)
+    T = int(cu[-1])
+    inp = W.make_layer_inputs(cfg, 0, trees)
+    acc = W.make_accepts(cfg, trees)
+    slots = W.make_slots(cfg)
+    sample = [0, 17, 42, 63]
+    rng = np.random.default_rng(23)
+    S0 = (0.2 * rng.standard_normal((cfg.num_seqs, cfg.num_v_heads, 128, 128))).astype(np.float32)
+    pre = W.make_prefill(cfg, 0, seqs=sample)
+    S0[sample] = oracle.initial_states(pre, cfg.num_v_heads, 128)
+    cache = np.empty((cfg.num_slots, cfg.num_v_heads, 128, 128), np.float32)
+    cache[slots] = S0
+    dims = G.make_dims(cfg.num_seqs, T, cfg.max_nodes, cfg.num_k_heads, cfg.num_v_heads, 128, cfg.num_slots,
+                       G.GDN_BF16)
+    ws = G.new_workspace(dims)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    cache_d = to_dev(cache)
+    slots_d = to_dev(slots)
+    out = torch.full((T, cfg.num_v_heads, 128), float("nan"), device="cuda")
+    G.gdn_tree_plan(dims, to_dev(np.concatenate(trees).astype(np.int32)), to_dev(cu.astype(np.int32)), slots_d, ws)
+    G.gdn_tree_verify(dims, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], cache_d, slots_d, out, ws)
+    G.gdn_tree_persist(dims, dev["k"], dev["v"], dev["a"], dev["b"], to_dev(acc), cache_d, slots_d, ws)
+    rc, bad, code = G.gdn_tree_status(ws)
+    assert rc == 0, (rc, bad, code)
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    after = cache_d.cpu().numpy()
+    for s in sample:
+        lo, hi = int(cu[s]), int(cu[s + 1])
+        sl = {k: v[lo:hi] for k, v in inp.items()}
+        ref = oracle.tree(trees[s], sl["q"], sl["k"], sl["v"], sl["a"], sl["b"], S0[s])
+        assert slice_rel_err(got[lo:hi].transpose(1, 0, 2).reshape(48, -1),
+                             ref.transpose(1, 0, 2).reshape(48, -1)) <= TOL, s
+        st, _ = oracle.accept_state(trees[s], int(acc[s]), sl["k"], sl["v"], sl["a"], sl["b"], S0[s])
+        assert slice_rel_err(after[slots[s]].reshape(48, -1), st.reshape(48, -1)) <= TOL, s
