@@ -161,6 +161,12 @@ def main():
 
     for i in range(args.warmup):
         step(i)
+    # calibration for memory-traffic counters: one plain device copy of a known
+    # size (256 MiB read + 256 MiB written), outside the timed region
+    cal_src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    del cal_src, cal_dst
     torch.cuda.synchronize()
     rc, bad, code = G.gdn_tree_status(ws)
     if rc != 0:

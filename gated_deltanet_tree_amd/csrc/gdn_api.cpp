@@ -102,7 +102,9 @@ int gdn_tree_verify(const gdn_dims *dims, const void *q, const void *k, const vo
     p.out = out;
     p.ws = gdn::ws_ptrs(const_cast<void *>(ws), p.B, p.T);
     p.has_ws = 1;
-    if (gdn::fast_path_supported(p.D, dims->qkv_dtype))
+    // the MFMA verify covers trees of up to 96 nodes; larger trees walk the
+    // tree recurrently
+    if (gdn::fast_tree_supported(p.D, dims->qkv_dtype, dims->max_nodes))
         return launched(gdn::launch_tree_verify_fast(p, as_stream(stream)));
     return launched(gdn::launch_tree_verify_recurrent(p, dims->qkv_dtype, as_stream(stream)));
 }
@@ -162,7 +164,9 @@ int gdn_chain_verify(const gdn_dims *dims, const int32_t *cu_nodes, const void *
         p.ws = gdn::ws_ptrs(ws, p.B, p.T);
         p.has_ws = 1;
     }
-    if (gdn::fast_path_supported(p.D, dims->qkv_dtype))
+    // chains that fit one drafting block share the tree kernels' arithmetic;
+    // longer chains (e.g. prefill) run the sequential recurrence
+    if (gdn::fast_path_supported(p.D, dims->qkv_dtype) && dims->max_nodes <= GDN_MAX_DEPTH)
         return launched(gdn::launch_chain_verify_fast(p, as_stream(stream)));
     return launched(gdn::launch_chain_verify_recurrent(p, dims->qkv_dtype, as_stream(stream)));
 }

@@ -1,29 +1,19 @@
-// gdn_fast.hip -- tree verify, chain verify and persist for D in {64, 128}
-// with bf16 q/k/v, built on MFMA.
+// gdn_fast.hip -- tree verify (MFMA) and accepted-path replay (VALU) for
+// D in {64, 128} with bf16 q/k/v.
 //
 // Unrolling the gated delta rule along a root-to-node path gives, for node n
 // with path p_0 (root) ... p_{d-1} = n and G_n = a_{p_0} ... a_{p_{d-1}}:
 //     S^n = G_n S0 + sum_e R(n,e) c_{p_e} k_{p_e}^T,   R(n,e) = a_{p_{e+1}} ... a_{p_{d-1}}
 //     c_n = b_n v_n - b_n G_n (S0 k_n) - sum_{e<d-1} b_n R(n,e) (k_{p_e} . k_n) c_{p_e}
 //     o_n = G_n (S0 q_n) + sum_{e<=d-1} R(n,e) (k_{p_e} . q_n) c_{p_e}
-// (c_n is the row vector b (v - a S^{parent} k) of the rule written as
-// S' = a S + c k^T.)  So a whole tree needs only the dense products S0 K^T
-// and S0 Q^T over all of its nodes -- one contraction per (sequence, head),
-// done on the matrix cores -- plus, per state row, a short recurrence over
-// each node's ancestors.  The state itself is never materialized in verify.
-// Persist materializes S^m for the accepted node m from the same pieces.
-//
-// Precision: S0 is fp32; it enters the bf16 MFMA as hi + lo with
-// hi = bf16(S0) and lo = bf16(S0 - hi) (two passes, ~2^-16 relative), while
-// k and q are bf16 already, so the products are exact and accumulate in fp32.
-//
-// Geometry: one workgroup per (sequence, value head), D/32 waves, wave w owns
-// state rows [32w, 32w+32).  MFMA 32x32x16: the node block (32 nodes in tree
-// preorder) is the A operand, the state rows are the B operand, so lane l of
-// a wave ends with state row l%32 for 16 of the 32 nodes; the accumulators go
-// through LDS once so each lane then walks the nodes of the block in order
-// for its row.  Both 32-lane halves of a wave run that walk for the same row
-// (half 0 writes the outputs).
+// where c_n = b_n (v_n - a_n S^{parent} k_n) is the row vector of the rule
+// written as S' = a S + c k^T.  A whole tree therefore needs only the dense
+// products S0 K^T and S0 Q^T over its nodes -- one contraction per (sequence,
+// value head), done on the matrix cores -- plus, per state row, a short
+// recurrence over each node's ancestors.  Verify never materializes a state.
+// Replay (persist) needs S^m for one root-to-node path of <= 16 nodes: it
+// reads S0 once, forms S0 k_e for the path keys with VALU dot products, runs
+// the same recurrence and writes G_m S0 + sum_e R(m,e) c_e k_e^T in place.
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -32,565 +22,624 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kTile = 32;                 // nodes per MFMA block
-constexpr int kPath = GDN_MAX_DEPTH;      // ancestors per node, chain chunk length
-
-template <int D>
-struct FG {
-    static constexpr int WAVES = D / 32;
-    static constexpr int THREADS = 64 * WAVES;
-    static constexpr int KS = D / 16;     // MFMA k-steps over the key dimension
-};
-
-// ---- LDS carve-up -----------------------------------------------------------
-struct FastLds {
-    int *order;    // [cap]      position -> local node id
-    int *pos_of;   // [cap]      local node id -> position
-    int *depth;    // [cap]
-    int *anc;      // [cap][16]  ancestor positions, root first; anc[p][d-1] = p
-    float *a, *b, *gamma, *alpha;  // [cap]
-    float *coefL;  // [cap][16]  b_p R(p,e) (k_anc . k_p)
-    float *coefM;  // [cap][16]  R(p,e) (k_anc . q_p)
-    float *xt;     // [WAVES][2][32][32]  S0 K^T / S0 Q^T blocks, node-major
-    uint16_t *kpath;  // [16][D] bf16 keys of the chunk being materialized
-};
-
-__host__ __device__ inline size_t fast_lds_bytes(int cap, int D) {
-    const size_t c = (size_t)cap;
-    return c * 4 * 3 + c * kPath * 4 + c * 4 * 4 + 2 * c * kPath * 4 + (size_t)(D / 32) * 2 * kTile * 32 * 4 +
-           (size_t)kPath * D * 2;
-}
-
-__device__ inline FastLds carve(char *base, int cap, int D) {
-    FastLds L;
-    L.xt = reinterpret_cast<float *>(base);
-    base += (size_t)(D / 32) * 2 * kTile * 32 * 4;
-    L.kpath = reinterpret_cast<uint16_t *>(base);  // 16-byte aligned: follows the float blocks
-    base += (size_t)kPath * D * 2;
-    L.coefL = reinterpret_cast<float *>(base); base += (size_t)cap * kPath * 4;
-    L.coefM = reinterpret_cast<float *>(base); base += (size_t)cap * kPath * 4;
-    L.anc = reinterpret_cast<int *>(base);     base += (size_t)cap * kPath * 4;
-    L.order = reinterpret_cast<int *>(base);   base += (size_t)cap * 4;
-    L.pos_of = reinterpret_cast<int *>(base);  base += (size_t)cap * 4;
-    L.depth = reinterpret_cast<int *>(base);   base += (size_t)cap * 4;
-    L.a = reinterpret_cast<float *>(base);     base += (size_t)cap * 4;
-    L.b = reinterpret_cast<float *>(base);     base += (size_t)cap * 4;
-    L.gamma = reinterpret_cast<float *>(base); base += (size_t)cap * 4;
-    L.alpha = reinterpret_cast<float *>(base);
-    return L;
-}
+constexpr int kTile = 32;             // nodes per MFMA block
+constexpr int kPath = GDN_MAX_DEPTH;  // max ancestors per node (incl. itself)
+constexpr int kFastMaxNodes = 96;     // largest tree the MFMA verify takes (3 node blocks)
 
 __device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float qnan_f() { return __int_as_float(0x7fc00000); }
-
-// Per-lane view of one workgroup.
-struct Lane {
-    int tid, w, lane, hf, l32, row;
-};
-template <int D>
-__device__ __forceinline__ Lane lane_of() {
-    Lane L;
-    L.tid = threadIdx.x;
-    L.w = L.tid / 64;
-    L.lane = L.tid % 64;
-    L.hf = L.lane / 32;
-    L.l32 = L.lane % 32;
-    L.row = L.w * 32 + L.l32;
-    return L;
-}
-
-// Everything the block routines need about the current sequence/head.
-struct Seq {
-    const uint16_t *k, *q, *v;  // base of node 0 of the sequence, this key / value head
-    size_t kq_stride, v_stride; // elements between consecutive nodes
-    int n;                      // positions in the current topology
-};
-
-// R(p, e) = a_{anc[e+1]} * ... * a_{anc[d-1]} (ascending, 1 when e = d-1)
-__device__ __forceinline__ float ratio(const FastLds &L, int p, int e) {
-    const int d = L.depth[p];
-    float r = 1.0f;
-    for (int t = e + 1; t < d; ++t) r *= L.a[L.anc[p * kPath + t]];
-    return r;
-}
-
-// gamma_p = a_{anc[0]} * ... * a_{anc[d-1]},  alpha_p = b_p gamma_p
-__device__ __forceinline__ void finish_tables(const FastLds &L, int n, int tid, int nthreads) {
-    for (int p = tid; p < n; p += nthreads) {
-        const int d = L.depth[p];
-        float g = 1.0f;
-        for (int t = 0; t < d; ++t) g *= L.a[L.anc[p * kPath + t]];
-        L.gamma[p] = g;
-        L.alpha[p] = L.b[p] * g;
-    }
-}
-
-// MFMA fragment: 8 bf16 of the key dimension [16 s + 8 hf, +8) of a node vector.
-__device__ __forceinline__ bf16x8 frag_of(const uint16_t *vec, int s, int hf) {
-    const uint4 raw = *reinterpret_cast<const uint4 *>(vec + 16 * s + 8 * hf);
-    return __builtin_bit_cast(bf16x8, raw);
-}
-
-__device__ __forceinline__ bf16x8 zero_frag() {
-    return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-}
-
-// State rows as B fragments: fp32 values and their bf16 hi/lo split.
-template <int D>
-struct StateFrags {
-    float f[FG<D>::KS][8];
-    bf16x8 hi[FG<D>::KS], lo[FG<D>::KS];
-
-    __device__ __forceinline__ void load(const float *row_ptr, int hf) {
-#pragma unroll
-        for (int s = 0; s < FG<D>::KS; ++s) {
-            const float4 x0 = *reinterpret_cast<const float4 *>(row_ptr + 16 * s + 8 * hf);
-            const float4 x1 = *reinterpret_cast<const float4 *>(row_ptr + 16 * s + 8 * hf + 4);
-            f[s][0] = x0.x; f[s][1] = x0.y; f[s][2] = x0.z; f[s][3] = x0.w;
-            f[s][4] = x1.x; f[s][5] = x1.y; f[s][6] = x1.z; f[s][7] = x1.w;
-        }
-    }
-    __device__ __forceinline__ void split() {
-#pragma unroll
-        for (int s = 0; s < FG<D>::KS; ++s) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const __bf16 h = static_cast<__bf16>(f[s][e]);
-                hi[s][e] = h;
-                lo[s][e] = static_cast<__bf16>(f[s][e] - static_cast<float>(h));
-            }
-        }
-    }
-    __device__ __forceinline__ void store(float *row_ptr, int hf) const {
-#pragma unroll
-        for (int s = 0; s < FG<D>::KS; ++s) {
-            *reinterpret_cast<float4 *>(row_ptr + 16 * s + 8 * hf) = make_float4(f[s][0], f[s][1], f[s][2], f[s][3]);
-            *reinterpret_cast<float4 *>(row_ptr + 16 * s + 8 * hf + 4) =
-                make_float4(f[s][4], f[s][5], f[s][6], f[s][7]);
-        }
-    }
-};
-
-// Gram entries k_anc . k_p (and k_anc . q_p) for every (ancestor, node) pair,
-// turned into the recurrence coefficients.  Block pairs (ti <= tj) are spread
-// over the waves; node blocks follow preorder so ancestors never come later.
-template <int D>
-__device__ void gram_coefficients(const FastLds &L, const Seq &S, const Lane &ln, bool want_m) {
-    const int ntiles = (S.n + kTile - 1) / kTile;
-    int pair = 0;
-    for (int tj = 0; tj < ntiles; ++tj) {
-        for (int ti = 0; ti <= tj; ++ti, ++pair) {
-            if (pair % FG<D>::WAVES != ln.w) continue;
-            const int pi = ti * kTile + ln.l32, pj = tj * kTile + ln.l32;
-            const uint16_t *ki = pi < S.n ? S.k + (size_t)L.order[pi] * S.kq_stride : nullptr;
-            const uint16_t *kj = pj < S.n ? S.k + (size_t)L.order[pj] * S.kq_stride : nullptr;
-            const uint16_t *qj = pj < S.n ? S.q + (size_t)L.order[pj] * S.kq_stride : nullptr;
-            f32x16 gkk = {}, gkq = {};
-#pragma unroll
-            for (int s = 0; s < FG<D>::KS; ++s) {
-                const bf16x8 A = ki ? frag_of(ki, s, ln.hf) : zero_frag();
-                const bf16x8 Bk = kj ? frag_of(kj, s, ln.hf) : zero_frag();
-                gkk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bk, gkk, 0, 0, 0);
-                if (want_m) {
-                    const bf16x8 Bq = qj ? frag_of(qj, s, ln.hf) : zero_frag();
-                    gkq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bq, gkq, 0, 0, 0);
-                }
-            }
-            // accumulator r holds (ancestor candidate i, node j = pj)
-            if (pj < S.n) {
-                const int dj = L.depth[pj];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int i = ti * kTile + 8 * (r / 4) + 4 * ln.hf + (r % 4);
-                    if (i >= S.n) continue;
-                    const int di = L.depth[i];
-                    if (di > dj || L.anc[pj * kPath + di - 1] != i) continue;
-                    const int e = di - 1;
-                    const float R = ratio(L, pj, e);
-                    if (e < dj - 1) L.coefL[pj * kPath + e] = L.b[pj] * R * gkk[r];
-                    if (want_m) L.coefM[pj * kPath + e] = R * gkq[r];
-                }
-            }
-        }
-    }
-}
-
-// For node block t: S0 K^T (and S0 Q^T) on the matrix cores, parked in LDS
-// node-major, then each lane walks the block's nodes for its state row.
-// cpath[e] holds c of the current node's ancestor at depth e+1 (preorder
-// keeps exactly the current path in it).
-template <int D, bool WANT_OUT>
-__device__ void block_walk(const FastLds &L, const Seq &S, const Lane &ln, const StateFrags<D> &st, int t,
-                           float (&cpath)[kPath], float *out_base, size_t out_stride) {
-    const int p0 = t * kTile;
-    const int cnt = min(kTile, S.n - p0);
-    // prefetch this row's v for the block
-    float vv[kTile];
-#pragma unroll
-    for (int i = 0; i < kTile; ++i)
-        vv[i] = i < cnt ? bf2f(S.v[(size_t)L.order[p0 + i] * S.v_stride]) : 0.0f;
-
-    const int pi = p0 + ln.l32;
-    const uint16_t *kr = pi < S.n ? S.k + (size_t)L.order[pi] * S.kq_stride : nullptr;
-    const uint16_t *qr = (WANT_OUT && pi < S.n) ? S.q + (size_t)L.order[pi] * S.kq_stride : nullptr;
-    f32x16 ax = {}, ay = {};
-#pragma unroll
-    for (int s = 0; s < FG<D>::KS; ++s) {
-        const bf16x8 A = kr ? frag_of(kr, s, ln.hf) : zero_frag();
-        ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, st.hi[s], ax, 0, 0, 0);
-        ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, st.lo[s], ax, 0, 0, 0);
-        if (WANT_OUT) {
-            const bf16x8 Aq = qr ? frag_of(qr, s, ln.hf) : zero_frag();
-            ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, st.hi[s], ay, 0, 0, 0);
-            ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, st.lo[s], ay, 0, 0, 0);
-        }
-    }
-    float *xw = L.xt + (size_t)ln.w * 2 * kTile * 32;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int i = 8 * (r / 4) + 4 * ln.hf + (r % 4);
-        xw[i * 32 + ln.l32] = ax[r];
-        if (WANT_OUT) xw[kTile * 32 + i * 32 + ln.l32] = ay[r];
-    }
-    __syncthreads();
-
-#pragma unroll
-    for (int i = 0; i < kTile; ++i) {
-        if (i >= cnt) break;
-        const int p = p0 + i;
-        const int d = L.depth[p];
-        const float x = xw[i * 32 + ln.l32];
-        const float *cl = L.coefL + p * kPath;
-        float c = fmaf(-L.alpha[p], x, L.b[p] * vv[i]);
-#pragma unroll
-        for (int e = 0; e < kPath - 1; ++e) {
-            if (e >= d - 1) break;
-            c = fmaf(-cl[e], cpath[e], c);
-        }
-        if (WANT_OUT) {
-            const float y = xw[kTile * 32 + i * 32 + ln.l32];
-            const float *cm = L.coefM + p * kPath;
-            float o = L.gamma[p] * y;
-#pragma unroll
-            for (int e = 0; e < kPath - 1; ++e) {
-                if (e >= d - 1) break;
-                o = fmaf(cm[e], cpath[e], o);
-            }
-            o = fmaf(cm[d - 1], c, o);
-            if (ln.hf == 0) out_base[(size_t)L.order[p] * out_stride] = o;
-        }
-#pragma unroll
-        for (int e = 0; e < kPath; ++e)
-            if (e == d - 1) cpath[e] = c;
-    }
-    __syncthreads();
-}
-
-// State after the first `len` positions of a chain-shaped chunk (positions
-// 0..len-1, each the parent of the next):
-//     S = G_{len-1} S0 + sum_{e < len} R(len-1, e) c_e k_e^T
-// kpath holds the chunk's keys; cpath the chunk's c values for this row.
-template <int D>
-__device__ void materialize(const FastLds &L, const Lane &ln, const float (&cpath)[kPath], int len,
-                            const StateFrags<D> &src, float (&dst)[FG<D>::KS][8]) {
-    float w[kPath];
-#pragma unroll
-    for (int e = 0; e < kPath; ++e) {
-        w[e] = 0.0f;
-        if (e < len) w[e] = ratio(L, len - 1, e) * cpath[e];
-    }
-    const float g = L.gamma[len - 1];
-#pragma unroll
-    for (int s = 0; s < FG<D>::KS; ++s) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int col = 16 * s + 8 * ln.hf + j;
-            float acc = g * src.f[s][j];
-#pragma unroll
-            for (int e = 0; e < kPath; ++e) {
-                if (e >= len) break;
-                acc = fmaf(w[e], bf2f(L.kpath[e * D + col]), acc);
-            }
-            dst[s][j] = acc;
-        }
-    }
-}
-
-// Chain-shaped tables for positions [0, cnt) = nodes first_node + pos_map(p).
-__device__ void chain_tables(const FastLds &L, const int32_t *nodes, int first, int cnt, const float *a,
-                             const float *b, size_t ab_stride, int tid, int nthreads) {
-    for (int p = tid; p < cnt; p += nthreads) {
-        const int node = nodes ? nodes[p] : first + p;
-        L.order[p] = node;
-        L.depth[p] = p + 1;
-        L.a[p] = a[(size_t)node * ab_stride];
-        L.b[p] = b[(size_t)node * ab_stride];
-        for (int e = 0; e < kPath; ++e) L.anc[p * kPath + e] = e <= p ? e : -1;
-    }
-}
-
-template <int D>
-__device__ void stage_kpath(const FastLds &L, const Seq &S, int cnt, int tid, int nthreads) {
-    for (int idx = tid; idx < kPath * D / 8; idx += nthreads) {
-        const int e = idx / (D / 8), c8 = idx % (D / 8);
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (e < cnt) v = *reinterpret_cast<const uint4 *>(S.k + (size_t)L.order[e] * S.kq_stride + 8 * c8);
-        *reinterpret_cast<uint4 *>(L.kpath + e * D + 8 * c8) = v;
-    }
-}
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 __device__ __forceinline__ bool ws_planned(const Params &P) {
     return P.ws.header[0] == kMagic && P.ws.header[1] == P.B && P.ws.header[2] == P.T;
 }
 
-// ---------------------------------------------------------------------------
+// ===========================================================================
+// Verify
+// ===========================================================================
 template <int D>
-__global__ __launch_bounds__(FG<D>::THREADS) void fast_tree_verify(Params P) {
+struct VG {
+    static constexpr int WAVES = D / 32;      // wave w owns state rows [32w, 32w+32)
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int KS = D / 16;         // MFMA 32x32x16 k-steps
+};
+
+// Per-position tables (positions = tree preorder, or chain order).
+struct VTab {
+    int *order;     // [cap] local node id
+    int *pos_of;    // [cap] position of a local node id
+    int *depth;     // [cap]
+    int *anc;       // [cap][16] ancestor positions, root first (anc[p][d-1] = p), 0 beyond
+    float *a, *b, *gamma, *alpha, *self_m;  // [cap]; self_m = k_p . q_p
+    float *R;       // [cap][16] R(p, e) for e < d
+    float *coefL;   // [cap][16] b_p R(p,e) (k_anc . k_p) for e < d-1, else 0
+    float *coefM;   // [cap][16] R(p,e) (k_anc . q_p) for e < d-1, else 0
+    float *mt;      // [np][np]  output operator (see verify_kernel), dense, 0 off-path
+    float *rt;      // [tiles-1][WAVES][16][64]  earlier blocks' right-hand sides
+};
+
+__host__ __device__ inline int pad_tiles(int cap) { return (cap + kTile - 1) / kTile; }
+
+__host__ __device__ inline size_t vtab_bytes(int cap, int D) {
+    const size_t c = (size_t)cap;
+    const size_t tiles = (size_t)pad_tiles(cap), np = tiles * kTile;
+    return np * np * 4 + (tiles - 1) * (size_t)(D / 32) * 16 * 64 * 4 + 4 * c * kPath * 4 + 3 * c * 4 + 5 * c * 4;
+}
+
+__device__ inline VTab vtab_carve(char *base, int cap, int D) {
+    VTab L;
+    const size_t c = (size_t)cap;
+    const size_t tiles = (size_t)pad_tiles(cap), np = tiles * kTile;
+    L.mt = reinterpret_cast<float *>(base);      base += np * np * 4;
+    L.rt = reinterpret_cast<float *>(base);      base += (tiles - 1) * (size_t)(D / 32) * 16 * 64 * 4;
+    L.R = reinterpret_cast<float *>(base);       base += c * kPath * 4;
+    L.coefL = reinterpret_cast<float *>(base);   base += c * kPath * 4;
+    L.coefM = reinterpret_cast<float *>(base);   base += c * kPath * 4;
+    L.anc = reinterpret_cast<int *>(base);       base += c * kPath * 4;
+    L.order = reinterpret_cast<int *>(base);     base += c * 4;
+    L.pos_of = reinterpret_cast<int *>(base);    base += c * 4;
+    L.depth = reinterpret_cast<int *>(base);     base += c * 4;
+    L.a = reinterpret_cast<float *>(base);       base += c * 4;
+    L.b = reinterpret_cast<float *>(base);       base += c * 4;
+    L.gamma = reinterpret_cast<float *>(base);   base += c * 4;
+    L.alpha = reinterpret_cast<float *>(base);   base += c * 4;
+    L.self_m = reinterpret_cast<float *>(base);
+    return L;
+}
+
+__device__ __forceinline__ bf16x8 frag_of(const uint16_t *vec, int s, int hf) {
+    const uint4 raw = *reinterpret_cast<const uint4 *>(vec + 16 * s + 8 * hf);
+    return __builtin_bit_cast(bf16x8, raw);
+}
+__device__ __forceinline__ bf16x8 zero_frag() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
+
+// After order/depth/anc/a/b are in place: ratios, gamma, alpha; zeroed coefficients.
+template <int D>
+__device__ void finish_vtab(const VTab &L, int n, int tid) {
+    for (int idx = tid; idx < n * kPath; idx += VG<D>::THREADS) {
+        const int p = idx / kPath, e = idx % kPath;
+        const int d = L.depth[p];
+        float r = 0.0f;
+        if (e < d) {
+            r = 1.0f;
+            for (int t = e + 1; t < d; ++t) r *= L.a[L.anc[p * kPath + t]];
+        }
+        L.R[idx] = r;
+        L.coefL[idx] = 0.0f;
+        L.coefM[idx] = 0.0f;
+        if (e == 0) {
+            const float g = r * L.a[L.anc[p * kPath]];
+            L.gamma[p] = g;
+            L.alpha[p] = L.b[p] * g;
+        }
+    }
+}
+
+// Gram entries for every (ancestor, node) pair -> recurrence coefficients.
+// Block pairs (ti <= tj) are spread over the waves; in preorder (and chain
+// order) an ancestor never sits at a later position than its descendant.
+template <int D>
+__device__ void gram(const VTab &L, int n, const uint16_t *kb, const uint16_t *qb, size_t kq_stride, int w,
+                     int hf, int l32) {
+    const int ntiles = (n + kTile - 1) / kTile;
+    int pair = 0;
+    for (int tj = 0; tj < ntiles; ++tj) {
+        for (int ti = 0; ti <= tj; ++ti, ++pair) {
+            if (pair % VG<D>::WAVES != w) continue;
+            const int pi = ti * kTile + l32, pj = tj * kTile + l32;
+            const uint16_t *ki = pi < n ? kb + (size_t)L.order[pi] * kq_stride : nullptr;
+            const uint16_t *kj = pj < n ? kb + (size_t)L.order[pj] * kq_stride : nullptr;
+            const uint16_t *qj = pj < n ? qb + (size_t)L.order[pj] * kq_stride : nullptr;
+            f32x16 gkk = {}, gkq = {};
+#pragma unroll
+            for (int s = 0; s < VG<D>::KS; ++s) {
+                const bf16x8 A = ki ? frag_of(ki, s, hf) : zero_frag();
+                const bf16x8 Bk = kj ? frag_of(kj, s, hf) : zero_frag();
+                const bf16x8 Bq = qj ? frag_of(qj, s, hf) : zero_frag();
+                gkk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bk, gkk, 0, 0, 0);
+                gkq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bq, gkq, 0, 0, 0);
+            }
+            if (pj < n) {  // accumulator r: (candidate ancestor i, node pj)
+                const int dj = L.depth[pj];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = ti * kTile + 8 * (r / 4) + 4 * hf + (r % 4);
+                    if (i >= n) continue;
+                    const int di = L.depth[i];
+                    if (di > dj || L.anc[pj * kPath + di - 1] != i) continue;
+                    const int e = di - 1;
+                    const float R = L.R[pj * kPath + e];
+                    if (e < dj - 1) {
+                        L.coefL[pj * kPath + e] = L.b[pj] * R * gkk[r];
+                        L.coefM[pj * kPath + e] = R * gkq[r];
+                    } else {
+                        L.self_m[pj] = gkq[r];
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Verify one sequence/head.  CHAIN: positions are nodes 0..n-1 of a chain
+// (n <= 16 per call); else the plan's preorder.
+//
+// With r_p = b_p v_p - alpha_p (S0 k_p) (a row vector), the c_p solve
+// (I + Lc) c = r along every path, and o_p = gamma_p (S0 q_p) + m_p . c over
+// p's path (m_p = coefM row plus k_p . q_p for p itself).  So
+//     O = diag(gamma) (S0 Q^T)  +  MT R,    MT[p] = m_p (I + Lc_path(p))^-1,
+// and row p of MT follows from a backward substitution over p's own path:
+//     y_{d-1} = k_p . q_p,   y_e = m_{p,e} - sum_{f>e} y_f Lc[anc_f][e].
+// X = S0 K^T, Y = S0 Q^T come from bf16 MFMA (state split hi + lo); O from
+// fp32 MFMA whose B operand is R exactly as the first MFMA left it.
+template <int D, bool CHAIN>
+__global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(3))) void verify_kernel(Params P) {
     extern __shared__ __attribute__((aligned(16))) char lds_raw[];
-    const Lane ln = lane_of<D>();
+    const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, hf = lane / 32, l32 = lane % 32;
+    const int row = w * 32 + l32;
     const int b = blockIdx.x / P.Hv, h = blockIdx.x % P.Hv;
     const int g = h / (P.Hv / P.Hk);
-    if (!ws_planned(P)) return;
-    const int lo = P.ws.seq_info[b * kSeqInfoInts + 0];
-    const int n = P.ws.seq_info[b * kSeqInfoInts + 1];
     const size_t out_stride = (size_t)P.Hv * D;
-    float *out_base = P.out + ((size_t)lo * P.Hv + h) * D + ln.row;
-    if (P.ws.seq_status[b] != GDN_SEQ_OK) {
-        if (ln.hf == 0)
+
+    int lo, n, status, slot;
+    if (CHAIN) {
+        const int c0 = P.cu_nodes[b], c1 = P.cu_nodes[b + 1];
+        const bool in_bounds = 0 <= c0 && c0 <= c1 && c1 <= P.T;
+        lo = in_bounds ? c0 : 0;
+        n = in_bounds ? c1 - c0 : 0;
+        status = (in_bounds && n <= P.max_nodes) ? GDN_SEQ_OK : GDN_SEQ_BAD_NODES;
+        slot = (status == GDN_SEQ_OK && n > 0) ? P.slot_idx[b] : 0;
+        if (status == GDN_SEQ_OK && n > 0 && (slot < 0 || slot >= P.num_slots)) status = GDN_SEQ_BAD_SLOT;
+        if (P.has_ws && h == 0 && tid == 0) {
+            if (b == 0) {
+                P.ws.header[0] = kMagic;
+                P.ws.header[1] = P.B;
+                P.ws.header[2] = P.T;
+            }
+            P.ws.seq_status[b] = status;
+        }
+        if (!P.out) return;
+    } else {
+        if (!ws_planned(P)) return;
+        lo = P.ws.seq_info[b * kSeqInfoInts + 0];
+        n = P.ws.seq_info[b * kSeqInfoInts + 1];
+        status = P.ws.seq_status[b];
+        slot = P.slot_idx[b];
+    }
+    float *out_base = P.out + ((size_t)lo * P.Hv + h) * D + row;
+    if (status != GDN_SEQ_OK) {
+        if (hf == 0)
             for (int i = 0; i < n; ++i) out_base[i * out_stride] = qnan_f();
         return;
     }
     if (n == 0) return;
-    const FastLds L = carve(lds_raw, P.max_nodes, D);
 
-    // tables in preorder positions
-    for (int p = ln.tid; p < n; p += FG<D>::THREADS) {
-        const int node = P.ws.order[lo + p];
-        L.order[p] = node;
-        L.pos_of[node] = p;
-        L.depth[p] = P.ws.depth[lo + node];
-        L.a[p] = P.a[(size_t)(lo + node) * P.Hv + h];
-        L.b[p] = P.b[(size_t)(lo + node) * P.Hv + h];
-    }
-    __syncthreads();
-    for (int idx = ln.tid; idx < n * kPath; idx += FG<D>::THREADS) {
-        const int p = idx / kPath, e = idx % kPath;
-        const int node = L.order[p];
-        L.anc[idx] = e < L.depth[p] ? L.pos_of[P.ws.nodepath[(size_t)(lo + node) * GDN_MAX_DEPTH + e]] : -1;
-    }
-    __syncthreads();
-    finish_tables(L, n, ln.tid, FG<D>::THREADS);
-
-    Seq S;
-    S.k = static_cast<const uint16_t *>(P.k) + ((size_t)lo * P.Hk + g) * D;
-    S.q = static_cast<const uint16_t *>(P.q) + ((size_t)lo * P.Hk + g) * D;
-    S.v = static_cast<const uint16_t *>(P.v) + ((size_t)lo * P.Hv + h) * D + ln.row;
-    S.kq_stride = (size_t)P.Hk * D;
-    S.v_stride = (size_t)P.Hv * D;
-    S.n = n;
-
-    StateFrags<D> st;
-    const int slot = P.slot_idx[b];
-    st.load(P.state_in + (((size_t)slot * P.Hv + h) * D + ln.row) * D, ln.hf);
-    st.split();
-    __syncthreads();
-    gram_coefficients<D>(L, S, ln, true);
-    __syncthreads();
-
-    float cpath[kPath];
+    // committed state rows as MFMA B fragments (issued first: longest latency)
+    const float *srow = P.state_in + (((size_t)slot * P.Hv + h) * D + row) * D;
+    float sf[VG<D>::KS][8];
 #pragma unroll
-    for (int e = 0; e < kPath; ++e) cpath[e] = 0.0f;
-    const int ntiles = (n + kTile - 1) / kTile;
-    for (int t = 0; t < ntiles; ++t) block_walk<D, true>(L, S, ln, st, t, cpath, out_base, out_stride);
-}
-
-// ---------------------------------------------------------------------------
-// Chain verify: chunks of up to 16 nodes; between chunks the state is
-// materialized exactly like persist does for an accepted path.
-template <int D>
-__global__ __launch_bounds__(FG<D>::THREADS) void fast_chain_verify(Params P) {
-    extern __shared__ __attribute__((aligned(16))) char lds_raw[];
-    const Lane ln = lane_of<D>();
-    const int b = blockIdx.x / P.Hv, h = blockIdx.x % P.Hv;
-    const int g = h / (P.Hv / P.Hk);
-    const int lo = P.cu_nodes[b], hi = P.cu_nodes[b + 1];
-    const bool in_bounds = 0 <= lo && lo <= hi && hi <= P.T;
-    const bool range_ok = in_bounds && hi - lo <= P.max_nodes;
-    const int n = in_bounds ? hi - lo : 0;
-    const int slot = (range_ok && n > 0) ? P.slot_idx[b] : 0;
-    int status = GDN_SEQ_OK;
-    if (!range_ok) status = GDN_SEQ_BAD_NODES;
-    else if (n > 0 && (slot < 0 || slot >= P.num_slots)) status = GDN_SEQ_BAD_SLOT;
-    if (P.has_ws && h == 0 && ln.tid == 0) {
-        if (b == 0) {
-            P.ws.header[0] = kMagic;
-            P.ws.header[1] = P.B;
-            P.ws.header[2] = P.T;
-        }
-        P.ws.seq_status[b] = status;
+    for (int s = 0; s < VG<D>::KS; ++s) {
+        const float4 x0 = *reinterpret_cast<const float4 *>(srow + 16 * s + 8 * hf);
+        const float4 x1 = *reinterpret_cast<const float4 *>(srow + 16 * s + 8 * hf + 4);
+        sf[s][0] = x0.x; sf[s][1] = x0.y; sf[s][2] = x0.z; sf[s][3] = x0.w;
+        sf[s][4] = x1.x; sf[s][5] = x1.y; sf[s][6] = x1.z; sf[s][7] = x1.w;
     }
-    const bool want_out = P.q != nullptr && P.out != nullptr;
-    const size_t out_stride = (size_t)P.Hv * D;
-    float *out_base = want_out ? P.out + ((size_t)lo * P.Hv + h) * D + ln.row : nullptr;
-    if (status != GDN_SEQ_OK) {
-        if (out_base && ln.hf == 0)
-            for (int i = 0; i < n; ++i) out_base[i * out_stride] = qnan_f();
-        return;
-    }
-    const int flen = P.final_len ? P.final_len[b] : -1;
-    float *fin = (P.final_state && flen >= 0 && flen <= n)
-                     ? P.final_state + (((size_t)b * P.Hv + h) * D + ln.row) * D
-                     : nullptr;
-    if (n == 0 && !fin) return;
-    const FastLds L = carve(lds_raw, kPath, D);
 
-    StateFrags<D> st;
-    st.load(P.state_in + (((size_t)slot * P.Hv + h) * D + ln.row) * D, ln.hf);
-    if (fin && flen == 0) st.store(fin, ln.hf);
-
-    Seq S;
-    S.kq_stride = (size_t)P.Hk * D;
-    S.v_stride = (size_t)P.Hv * D;
-    for (int c0 = 0; c0 < n; c0 += kPath) {
-        const int cnt = min(kPath, n - c0);
-        const bool need_fin = fin && flen > c0 && flen <= c0 + cnt;
-        const bool need_next = c0 + cnt < n && (want_out || (fin && flen > c0 + cnt));
-        if (!want_out && !need_fin && !need_next) break;
-        S.k = static_cast<const uint16_t *>(P.k) + ((size_t)(lo + c0) * P.Hk + g) * D;
-        S.q = want_out ? static_cast<const uint16_t *>(P.q) + ((size_t)(lo + c0) * P.Hk + g) * D : nullptr;
-        S.v = static_cast<const uint16_t *>(P.v) + ((size_t)(lo + c0) * P.Hv + h) * D + ln.row;
-        S.n = cnt;
-        __syncthreads();
-        chain_tables(L, nullptr, 0, cnt, P.a + (size_t)(lo + c0) * P.Hv + h, P.b + (size_t)(lo + c0) * P.Hv + h,
-                     P.Hv, ln.tid, FG<D>::THREADS);
-        __syncthreads();
-        finish_tables(L, cnt, ln.tid, FG<D>::THREADS);
-        stage_kpath<D>(L, S, cnt, ln.tid, FG<D>::THREADS);
-        st.split();
-        __syncthreads();
-        gram_coefficients<D>(L, S, ln, want_out);
-        __syncthreads();
-        float cpath[kPath];
-#pragma unroll
-        for (int e = 0; e < kPath; ++e) cpath[e] = 0.0f;
-        float *ob = want_out ? out_base + (size_t)c0 * out_stride : nullptr;
-        if (want_out) block_walk<D, true>(L, S, ln, st, 0, cpath, ob, out_stride);
-        else block_walk<D, false>(L, S, ln, st, 0, cpath, ob, out_stride);
-        if (need_fin) {
-            float f[FG<D>::KS][8];
-            materialize<D>(L, ln, cpath, flen - c0, st, f);
-            float *dst = fin;
-#pragma unroll
-            for (int s = 0; s < FG<D>::KS; ++s) {
-                *reinterpret_cast<float4 *>(dst + 16 * s + 8 * ln.hf) = make_float4(f[s][0], f[s][1], f[s][2], f[s][3]);
-                *reinterpret_cast<float4 *>(dst + 16 * s + 8 * ln.hf + 4) =
-                    make_float4(f[s][4], f[s][5], f[s][6], f[s][7]);
+    const int cap = CHAIN ? kPath : P.max_nodes;
+    const VTab L = vtab_carve(lds_raw, cap, D);
+    const int np = pad_tiles(cap) * kTile;
+    const float *ga = P.a + (size_t)lo * P.Hv + h;
+    const float *gb = P.b + (size_t)lo * P.Hv + h;
+    if (CHAIN) {
+        for (int idx = tid; idx < n * kPath; idx += VG<D>::THREADS) {
+            const int p = idx / kPath, e = idx % kPath;
+            L.anc[idx] = e <= p ? e : 0;
+            if (e == 0) {
+                L.order[p] = p;
+                L.depth[p] = p + 1;
+                L.a[p] = ga[(size_t)p * P.Hv];
+                L.b[p] = gb[(size_t)p * P.Hv];
             }
         }
-        if (need_next) {
-            float f[FG<D>::KS][8];
-            materialize<D>(L, ln, cpath, cnt, st, f);
+    } else {
+        for (int p = tid; p < n; p += VG<D>::THREADS) {
+            const int node = P.ws.order[lo + p];
+            L.order[p] = node;
+            L.pos_of[node] = p;
+            L.depth[p] = P.ws.depth[lo + node];
+            L.a[p] = ga[(size_t)node * P.Hv];
+            L.b[p] = gb[(size_t)node * P.Hv];
+        }
+        __syncthreads();
+        for (int idx = tid; idx < n * kPath; idx += VG<D>::THREADS) {
+            const int p = idx / kPath, e = idx % kPath;
+            L.anc[idx] = e < L.depth[p]
+                             ? L.pos_of[P.ws.nodepath[(size_t)(lo + L.order[p]) * GDN_MAX_DEPTH + e]]
+                             : 0;
+        }
+    }
+    for (int idx = tid; idx < np * np; idx += VG<D>::THREADS) L.mt[idx] = 0.0f;
+    __syncthreads();
+    finish_vtab<D>(L, n, tid);
+
+    // hi/lo split of the state for the bf16 MFMA
+    bf16x8 shi[VG<D>::KS], slo[VG<D>::KS];
 #pragma unroll
-            for (int s = 0; s < FG<D>::KS; ++s)
+    for (int s = 0; s < VG<D>::KS; ++s) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) st.f[s][j] = f[s][j];
+        for (int e = 0; e < 8; ++e) {
+            const __bf16 hb = static_cast<__bf16>(sf[s][e]);
+            shi[s][e] = hb;
+            slo[s][e] = static_cast<__bf16>(sf[s][e] - static_cast<float>(hb));
+        }
+    }
+    const uint16_t *kb = static_cast<const uint16_t *>(P.k) + ((size_t)lo * P.Hk + g) * D;
+    const uint16_t *qb = static_cast<const uint16_t *>(P.q) + ((size_t)lo * P.Hk + g) * D;
+    const uint16_t *vb = static_cast<const uint16_t *>(P.v) + ((size_t)lo * P.Hv + h) * D + row;
+    const size_t kq_stride = (size_t)P.Hk * D, v_stride = (size_t)P.Hv * D;
+    __syncthreads();
+    gram<D>(L, n, kb, qb, kq_stride, w, hf, l32);
+    __syncthreads();
+
+    // output operator rows, one position per thread
+    for (int p = tid; p < n; p += VG<D>::THREADS) {
+        const int d = L.depth[p];
+        int af[kPath];
+#pragma unroll
+        for (int f = 0; f < kPath; ++f) af[f] = L.anc[p * kPath + f];
+        float y[kPath];
+#pragma unroll
+        for (int e = kPath - 1; e >= 0; --e) {
+            float acc = e == d - 1 ? L.self_m[p] : L.coefM[p * kPath + e];
+#pragma unroll
+            for (int f = e + 1; f < kPath; ++f) acc = fmaf(-y[f], L.coefL[af[f] * kPath + e], acc);
+            y[e] = e < d ? acc : 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < kPath; ++e)
+            if (e < d) L.mt[p * np + af[e]] = y[e];
+    }
+    __syncthreads();
+
+    const int ntiles = (n + kTile - 1) / kTile;
+    for (int t = 0; t < ntiles; ++t) {
+        const int p0 = t * kTile;
+        // this lane's 16 (position, row) entries of the block: position p0 + ip(r)
+        float vv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int p = p0 + 8 * (r / 4) + 4 * hf + (r % 4);
+            vv[r] = p < n ? bf2f(vb[(size_t)L.order[p] * v_stride]) : 0.0f;
+        }
+        const int pi = p0 + l32;
+        const uint16_t *kr = pi < n ? kb + (size_t)L.order[pi] * kq_stride : nullptr;
+        const uint16_t *qr = pi < n ? qb + (size_t)L.order[pi] * kq_stride : nullptr;
+        f32x16 ax = {}, ay = {};
+#pragma unroll
+        for (int s = 0; s < VG<D>::KS; ++s) {
+            const bf16x8 Ak = kr ? frag_of(kr, s, hf) : zero_frag();
+            const bf16x8 Aq = qr ? frag_of(qr, s, hf) : zero_frag();
+            ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, shi[s], ax, 0, 0, 0);
+            ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, slo[s], ax, 0, 0, 0);
+            ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, shi[s], ay, 0, 0, 0);
+            ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, slo[s], ay, 0, 0, 0);
+        }
+        // r = b v - alpha x;  o starts as gamma y
+        f32x16 rr, oo;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int p = p0 + 8 * (r / 4) + 4 * hf + (r % 4);
+            const bool in = p < n;
+            rr[r] = in ? fmaf(-L.alpha[p], ax[r], L.b[p] * vv[r]) : 0.0f;
+            oo[r] = in ? L.gamma[p] * ay[r] : 0.0f;
+        }
+        if (t + 1 < ntiles) {
+            float *dst = L.rt + ((size_t)t * VG<D>::WAVES + w) * 16 * 64;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dst[r * 64 + lane] = rr[r];
+        }
+        // O += MT[block t, block j] R_j for j <= t
+        const float *mrow = L.mt + (size_t)(p0 + l32) * np;
+        for (int j = 0; j < t; ++j) {
+            const float *src = L.rt + ((size_t)j * VG<D>::WAVES + w) * 16 * 64;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                const float am = mrow[j * kTile + 8 * (s / 4) + 4 * hf + (s % 4)];
+                oo = __builtin_amdgcn_mfma_f32_32x32x2f32(am, src[s * 64 + lane], oo, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            const float am = mrow[p0 + 8 * (s / 4) + 4 * hf + (s % 4)];
+            oo = __builtin_amdgcn_mfma_f32_32x32x2f32(am, rr[s], oo, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int p = p0 + 8 * (r / 4) + 4 * hf + (r % 4);
+            if (p < n) out_base[(size_t)L.order[p] * out_stride] = oo[r];
         }
     }
 }
 
-// ---------------------------------------------------------------------------
-// Persist: the accepted root-to-node path as a chain chunk, materialized in place.
+// ===========================================================================
+// Replay (persist, and the state a chain reaches after its first L nodes)
+// ===========================================================================
 template <int D>
-__global__ __launch_bounds__(FG<D>::THREADS) void fast_persist(Params P) {
+struct RG {
+    static constexpr int LPR = 4;             // lanes per state row
+    static constexpr int CPL = D / LPR;       // columns per lane
+    static constexpr int NCH = CPL / 4;       // float4 chunks per lane
+    static constexpr int ROWS = D;            // rows per workgroup: the whole head
+    static constexpr int THREADS = ROWS * LPR;
+};
+
+// column of element 0 of chunk c held by lane j of a row group: the 4 lanes
+// of a row read 64 contiguous bytes per chunk
+template <int D>
+__device__ __forceinline__ int rcol(int j, int c) { return c * 4 * RG<D>::LPR + j * 4; }
+
+template <int CTRL>
+__device__ __forceinline__ float dppf(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+// sum over the 4 lanes of a row group; every lane gets the same bits
+__device__ __forceinline__ float sum4(float x) {
+    x = x + dppf<0xB1>(x);  // quad_perm [1,0,3,2]
+    x = x + dppf<0x4E>(x);  // quad_perm [2,3,0,1]
+    return x;
+}
+
+struct RTab {
+    float *k;        // [16][D] path keys (fp32)
+    float *a, *b, *gamma, *alpha, *w_r;  // [16]; w_r[e] = R(L-1, e)
+    float *coefL;    // [16][16] b_p R(p,e) (k_e . k_p) for e < p, else 0
+};
+
+__host__ __device__ inline size_t rtab_bytes(int D) {
+    return (size_t)kPath * D * 4 + kPath * kPath * 4 + 5 * kPath * 4;
+}
+
+__device__ inline RTab rtab_carve(char *base, int D) {
+    RTab L;
+    L.k = reinterpret_cast<float *>(base);     base += (size_t)kPath * D * 4;
+    L.coefL = reinterpret_cast<float *>(base); base += kPath * kPath * 4;
+    L.a = reinterpret_cast<float *>(base);     base += kPath * 4;
+    L.b = reinterpret_cast<float *>(base);     base += kPath * 4;
+    L.gamma = reinterpret_cast<float *>(base); base += kPath * 4;
+    L.alpha = reinterpret_cast<float *>(base); base += kPath * 4;
+    L.w_r = reinterpret_cast<float *>(base);
+    return L;
+}
+
+// CHAIN: the path is nodes 0..len-1 of chain b (len = final_len[b] <= 16),
+// read from state_in[slot_idx[b]] and written to final_state[b].  Otherwise
+// the accepted path of sequence b, replayed in place in the state cache.
+template <int D, bool CHAIN>
+__global__ __launch_bounds__(RG<D>::THREADS) void replay_kernel(Params P) {
     extern __shared__ __attribute__((aligned(16))) char lds_raw[];
-    const Lane ln = lane_of<D>();
+    using G = RG<D>;
+    const int tid = threadIdx.x, j = tid % G::LPR;
     const int b = blockIdx.x / P.Hv, h = blockIdx.x % P.Hv;
     const int g = h / (P.Hv / P.Hk);
-    if (!ws_planned(P)) return;
-    const int status = P.ws.seq_status[b];
-    const int lo = P.ws.seq_info[b * kSeqInfoInts + 0];
-    const int n = P.ws.seq_info[b * kSeqInfoInts + 1];
-    if (status != GDN_SEQ_OK || n == 0) return;
-    const int m = P.accepted[b];
-    if (m < -1 || m >= n) {
-        if (h == 0 && ln.tid == 0) P.ws.seq_status[b] = GDN_SEQ_BAD_ACCEPT;
+    const int row = tid / G::LPR;
+
+    int lo, len, slot;
+    const int32_t *path = nullptr;  // local node ids (null: chain 0..len-1)
+    float *dst;
+    if (CHAIN) {
+        const int c0 = P.cu_nodes[b], c1 = P.cu_nodes[b + 1];
+        if (!(0 <= c0 && c0 <= c1 && c1 <= P.T) || c1 - c0 > P.max_nodes) return;
+        const int n = c1 - c0;
+        len = P.final_len[b];
+        if (len < 0 || len > n || len > kPath) return;
+        slot = P.slot_idx[b];
+        if (slot < 0 || slot >= P.num_slots) return;
+        lo = c0;
+        dst = P.final_state + (((size_t)b * P.Hv + h) * D + row) * D;
+    } else {
+        if (!ws_planned(P)) return;
+        const int n = P.ws.seq_info[b * kSeqInfoInts + 1];
+        if (P.ws.seq_status[b] != GDN_SEQ_OK || n == 0) return;
+        const int m = P.accepted[b];
+        if (m < -1 || m >= n) {
+            if (h == 0 && tid == 0) P.ws.seq_status[b] = GDN_SEQ_BAD_ACCEPT;
+            return;
+        }
+        if (m == -1) return;
+        lo = P.ws.seq_info[b * kSeqInfoInts + 0];
+        slot = P.slot_idx[b];
+        len = P.ws.depth[lo + m];
+        path = P.ws.nodepath + (size_t)(lo + m) * GDN_MAX_DEPTH;
+        if (h == 0 && tid < GDN_MAX_DEPTH) {
+            P.ws.path[b * GDN_MAX_DEPTH + tid] = path[tid];
+            if (tid == 0) P.ws.path_len[b] = len;
+        }
+        dst = P.state_out + (((size_t)slot * P.Hv + h) * D + row) * D;
+    }
+    len = uni(len);
+
+    // state row slice: issued before anything that waits
+    const float *src = P.state_in + (((size_t)slot * P.Hv + h) * D + row) * D;
+    float S[G::CPL];
+#pragma unroll
+    for (int c = 0; c < G::NCH; ++c) {
+        const float4 f = *reinterpret_cast<const float4 *>(src + rcol<D>(j, c));
+        S[4 * c + 0] = f.x; S[4 * c + 1] = f.y; S[4 * c + 2] = f.z; S[4 * c + 3] = f.w;
+    }
+    if (len == 0) {  // chain final state after zero nodes: the committed state
+#pragma unroll
+        for (int c = 0; c < G::NCH; ++c)
+            *reinterpret_cast<float4 *>(dst + rcol<D>(j, c)) =
+                make_float4(S[4 * c + 0], S[4 * c + 1], S[4 * c + 2], S[4 * c + 3]);
         return;
     }
-    if (m == -1) return;
-    const int len = P.ws.depth[lo + m];
-    const int32_t *np = P.ws.nodepath + (size_t)(lo + m) * GDN_MAX_DEPTH;
-    if (h == 0) {
-        if (ln.tid < GDN_MAX_DEPTH) P.ws.path[b * GDN_MAX_DEPTH + ln.tid] = np[ln.tid];
-        if (ln.tid == 0) P.ws.path_len[b] = len;
+
+    const RTab L = rtab_carve(lds_raw, D);
+    const uint16_t *kb = static_cast<const uint16_t *>(P.k) + ((size_t)lo * P.Hk + g) * D;
+    const uint16_t *vb = static_cast<const uint16_t *>(P.v) + ((size_t)lo * P.Hv + h) * D + row;
+    const size_t kq_stride = (size_t)P.Hk * D, v_stride = (size_t)P.Hv * D;
+    // path keys -> LDS as fp32 (zero rows past the path), gates -> LDS
+    for (int idx = tid; idx < kPath * D / 8; idx += G::THREADS) {
+        const int e = idx / (D / 8), c8 = idx % (D / 8);
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (e < len) {
+            const int node = path ? path[e] : e;
+            v = *reinterpret_cast<const uint4 *>(kb + (size_t)node * kq_stride + 8 * c8);
+        }
+        float4 *d4 = reinterpret_cast<float4 *>(L.k + e * D + 8 * c8);
+        d4[0] = make_float4(bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y));
+        d4[1] = make_float4(bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w));
     }
-    const FastLds L = carve(lds_raw, kPath, D);
-    chain_tables(L, np, 0, len, P.a + (size_t)lo * P.Hv + h, P.b + (size_t)lo * P.Hv + h, P.Hv, ln.tid,
-                 FG<D>::THREADS);
-    __syncthreads();
-    finish_tables(L, len, ln.tid, FG<D>::THREADS);
-
-    Seq S;
-    S.k = static_cast<const uint16_t *>(P.k) + ((size_t)lo * P.Hk + g) * D;
-    S.q = nullptr;
-    S.v = static_cast<const uint16_t *>(P.v) + ((size_t)lo * P.Hv + h) * D + ln.row;
-    S.kq_stride = (size_t)P.Hk * D;
-    S.v_stride = (size_t)P.Hv * D;
-    S.n = len;
-    stage_kpath<D>(L, S, len, ln.tid, FG<D>::THREADS);
-
-    float *row_ptr = P.state_out + (((size_t)P.slot_idx[b] * P.Hv + h) * D + ln.row) * D;
-    StateFrags<D> st;
-    st.load(row_ptr, ln.hf);
-    st.split();
-    __syncthreads();
-    gram_coefficients<D>(L, S, ln, false);
-    __syncthreads();
-    float cpath[kPath];
+    if (tid < kPath) {
+        const int node = tid < len ? (path ? path[tid] : tid) : 0;
+        L.a[tid] = tid < len ? P.a[(size_t)(lo + node) * P.Hv + h] : 1.0f;
+        L.b[tid] = tid < len ? P.b[(size_t)(lo + node) * P.Hv + h] : 0.0f;
+    }
+    float vr[kPath];
 #pragma unroll
-    for (int e = 0; e < kPath; ++e) cpath[e] = 0.0f;
-    block_walk<D, false>(L, S, ln, st, 0, cpath, nullptr, 0);
-    float f[FG<D>::KS][8];
-    materialize<D>(L, ln, cpath, len, st, f);
+    for (int e = 0; e < kPath; ++e) {
+        vr[e] = 0.0f;
+        if (e < len) vr[e] = bf2f(vb[(size_t)(path ? path[e] : e) * v_stride]);
+    }
+    __syncthreads();
+    // coefficients for the pairs e < p < len: one pair per 4-lane group
+    const int npairs = len * (len - 1) / 2;
+    for (int pr = tid / G::LPR; pr < npairs; pr += G::THREADS / G::LPR) {
+        int p = 1, base = 0;
+        while (base + p <= pr) { base += p; ++p; }
+        const int e = pr - base;
+        float dot = 0.0f;
 #pragma unroll
-    for (int s = 0; s < FG<D>::KS; ++s) {
-        *reinterpret_cast<float4 *>(row_ptr + 16 * s + 8 * ln.hf) = make_float4(f[s][0], f[s][1], f[s][2], f[s][3]);
-        *reinterpret_cast<float4 *>(row_ptr + 16 * s + 8 * ln.hf + 4) = make_float4(f[s][4], f[s][5], f[s][6], f[s][7]);
+        for (int c = 0; c < G::NCH; ++c) {
+            const float4 ke = *reinterpret_cast<const float4 *>(L.k + e * D + rcol<D>(j, c));
+            const float4 kp = *reinterpret_cast<const float4 *>(L.k + p * D + rcol<D>(j, c));
+            dot = fmaf(ke.x, kp.x, dot);
+            dot = fmaf(ke.y, kp.y, dot);
+            dot = fmaf(ke.z, kp.z, dot);
+            dot = fmaf(ke.w, kp.w, dot);
+        }
+        dot = sum4(dot);
+        if (j == 0) {
+            float r = 1.0f;
+            for (int t = e + 1; t <= p; ++t) r *= L.a[t];
+            L.coefL[p * kPath + e] = L.b[p] * r * dot;
+        }
+    }
+    if (tid < kPath) {
+        float g_ = 1.0f, r = 1.0f;
+        for (int t = 0; t <= tid; ++t) g_ *= L.a[t];
+        for (int t = tid + 1; t < len; ++t) r *= L.a[t];
+        L.gamma[tid] = g_;
+        L.alpha[tid] = L.b[tid] * g_;
+        L.w_r[tid] = tid < len ? r : 0.0f;
+    }
+    __syncthreads();
+
+    // S0 k_e for the path keys (independent dot products)
+    float x[kPath];
+#pragma unroll
+    for (int e = 0; e < kPath; ++e) {
+        x[e] = 0.0f;
+        if (e < len) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int c = 0; c < G::NCH; ++c) {
+                const float4 kk = *reinterpret_cast<const float4 *>(L.k + e * D + rcol<D>(j, c));
+                acc = fmaf(S[4 * c + 0], kk.x, acc);
+                acc = fmaf(S[4 * c + 1], kk.y, acc);
+                acc = fmaf(S[4 * c + 2], kk.z, acc);
+                acc = fmaf(S[4 * c + 3], kk.w, acc);
+            }
+            x[e] = sum4(acc);
+        }
+    }
+    // c_p = b_p v_p - alpha_p x_p - sum_{e<p} coefL[p][e] c_e
+    float cv[kPath];
+#pragma unroll
+    for (int p = 0; p < kPath; ++p) {
+        float c = 0.0f;
+        if (p < len) {
+            c = fmaf(-L.alpha[p], x[p], L.b[p] * vr[p]);
+#pragma unroll
+            for (int e = 0; e < p; ++e) c = fmaf(-L.coefL[p * kPath + e], cv[e], c);
+        }
+        cv[p] = c;
+    }
+    // S_new = gamma_{L-1} S0 + sum_e R(L-1,e) c_e k_e^T
+    float wv[kPath];
+#pragma unroll
+    for (int e = 0; e < kPath; ++e) wv[e] = L.w_r[e] * cv[e];
+    const float gm = L.gamma[len - 1];
+#pragma unroll
+    for (int c = 0; c < G::NCH; ++c) {
+        float o0 = gm * S[4 * c + 0], o1 = gm * S[4 * c + 1], o2 = gm * S[4 * c + 2], o3 = gm * S[4 * c + 3];
+#pragma unroll
+        for (int e = 0; e < kPath; ++e) {
+            if (e < len) {
+                const float4 kk = *reinterpret_cast<const float4 *>(L.k + e * D + rcol<D>(j, c));
+                o0 = fmaf(wv[e], kk.x, o0);
+                o1 = fmaf(wv[e], kk.y, o1);
+                o2 = fmaf(wv[e], kk.z, o2);
+                o3 = fmaf(wv[e], kk.w, o3);
+            }
+        }
+        *reinterpret_cast<float4 *>(dst + rcol<D>(j, c)) = make_float4(o0, o1, o2, o3);
     }
 }
 
-template <int D>
-hipError_t launch_fast(int which, const Params &p, hipStream_t s) {
-    const int cap = which == 0 ? (p.max_nodes > 0 ? p.max_nodes : 1) : kPath;
-    const size_t lds = fast_lds_bytes(cap, D);
-    const dim3 grid(p.B * p.Hv), block(FG<D>::THREADS);
-    const void *fn = which == 0 ? reinterpret_cast<const void *>(&fast_tree_verify<D>)
-                   : which == 1 ? reinterpret_cast<const void *>(&fast_chain_verify<D>)
-                                : reinterpret_cast<const void *>(&fast_persist<D>);
+template <typename K>
+hipError_t launch_with_lds(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, const Params &p) {
     if (lds > 65536) {
-        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    if (which == 0) hipLaunchKernelGGL(fast_tree_verify<D>, grid, block, lds, s, p);
-    else if (which == 1) hipLaunchKernelGGL(fast_chain_verify<D>, grid, block, lds, s, p);
-    else hipLaunchKernelGGL(fast_persist<D>, grid, block, lds, s, p);
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, p);
     return hipGetLastError();
 }
 
-hipError_t launch_fast_any(int which, const Params &p, hipStream_t s) {
-    if (p.B == 0) return hipSuccess;
-    switch (p.D) {
-        case 64: return launch_fast<64>(which, p, s);
-        case 128: return launch_fast<128>(which, p, s);
-        default: return hipErrorInvalidValue;
-    }
+template <int D>
+hipError_t launch_verify_d(const Params &p, bool chain, hipStream_t s) {
+    const int cap = chain ? kPath : p.max_nodes;
+    const dim3 grid(p.B * p.Hv), block(VG<D>::THREADS);
+    return chain ? launch_with_lds(verify_kernel<D, true>, grid, block, vtab_bytes(cap, D), s, p)
+                 : launch_with_lds(verify_kernel<D, false>, grid, block, vtab_bytes(cap, D), s, p);
+}
+
+template <int D>
+hipError_t launch_replay_d(const Params &p, bool chain, hipStream_t s) {
+    const dim3 grid(p.B * p.Hv), block(RG<D>::THREADS);
+    return chain ? launch_with_lds(replay_kernel<D, true>, grid, block, rtab_bytes(D), s, p)
+                 : launch_with_lds(replay_kernel<D, false>, grid, block, rtab_bytes(D), s, p);
 }
 
 }  // namespace
 
 bool fast_path_supported(int D, int dtype) { return (D == 64 || D == 128) && dtype == GDN_BF16; }
-size_t fast_tree_lds_bytes(int max_nodes, int D) { return fast_lds_bytes(max_nodes > 0 ? max_nodes : 1, D); }
-hipError_t launch_tree_verify_fast(const Params &p, hipStream_t s) { return launch_fast_any(0, p, s); }
-hipError_t launch_chain_verify_fast(const Params &p, hipStream_t s) { return launch_fast_any(1, p, s); }
-hipError_t launch_persist_fast(const Params &p, hipStream_t s) { return launch_fast_any(2, p, s); }
+bool fast_tree_supported(int D, int dtype, int max_nodes) {
+    return fast_path_supported(D, dtype) && max_nodes <= kFastMaxNodes;
+}
+
+hipError_t launch_tree_verify_fast(const Params &p, hipStream_t s) {
+    if (p.B == 0) return hipSuccess;
+    return p.D == 64 ? launch_verify_d<64>(p, false, s) : launch_verify_d<128>(p, false, s);
+}
+hipError_t launch_persist_fast(const Params &p, hipStream_t s) {
+    if (p.B == 0) return hipSuccess;
+    return p.D == 64 ? launch_replay_d<64>(p, false, s) : launch_replay_d<128>(p, false, s);
+}
+// Chains of at most 16 nodes: outputs from the verify kernel in chain order
+// (so a chain-shaped tree and a chain give the same bits) and the final state
+// from the replay kernel (so persist and chain give the same bits).
+hipError_t launch_chain_verify_fast(const Params &p, hipStream_t s) {
+    if (p.B == 0) return hipSuccess;
+    hipError_t e = hipSuccess;
+    if (p.out || p.has_ws) e = p.D == 64 ? launch_verify_d<64>(p, true, s) : launch_verify_d<128>(p, true, s);
+    if (e != hipSuccess) return e;
+    if (p.final_state) e = p.D == 64 ? launch_replay_d<64>(p, true, s) : launch_replay_d<128>(p, true, s);
+    return e;
+}
 
 }  // namespace gdn

@@ -84,7 +84,7 @@ hipError_t launch_chain_verify_recurrent(const Params &p, int dtype, hipStream_t
 hipError_t launch_persist_recurrent(const Params &p, int dtype, hipStream_t s);
 // MFMA path (D in {64, 128}, bf16 q/k/v)
 bool fast_path_supported(int D, int dtype);
-size_t fast_tree_lds_bytes(int max_nodes, int D);
+bool fast_tree_supported(int D, int dtype, int max_nodes);
 hipError_t launch_tree_verify_fast(const Params &p, hipStream_t s);
 hipError_t launch_chain_verify_fast(const Params &p, hipStream_t s);
 hipError_t launch_persist_fast(const Params &p, hipStream_t s);

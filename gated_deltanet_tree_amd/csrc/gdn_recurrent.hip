@@ -260,10 +260,11 @@ __global__ __launch_bounds__(64) void chain_verify_kernel(Params P) {
     const bool in_bounds = 0 <= lo && lo <= hi && hi <= P.T;
     const bool range_ok = in_bounds && hi - lo <= P.max_nodes;
     const int n = in_bounds ? hi - lo : 0;
-    const int slot = (range_ok && n > 0) ? P.slot_idx[t.b] : 0;
+    const int slot = range_ok ? P.slot_idx[t.b] : 0;
+    const bool slot_ok = slot >= 0 && slot < P.num_slots;
     int status = GDN_SEQ_OK;
     if (!range_ok) status = GDN_SEQ_BAD_NODES;
-    else if (n > 0 && (slot < 0 || slot >= P.num_slots)) status = GDN_SEQ_BAD_SLOT;
+    else if (n > 0 && !slot_ok) status = GDN_SEQ_BAD_SLOT;
     if (P.has_ws && t.h == 0 && t.slice == 0 && t.lane == 0) {
         if (t.b == 0) {
             P.ws.header[0] = kMagic;
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(64) void chain_verify_kernel(Params P) {
         return;
     }
     const int flen = P.final_len ? P.final_len[t.b] : -1;
-    float *fin = (P.final_state && flen >= 0 && flen <= n)
+    float *fin = (P.final_state && slot_ok && flen >= 0 && flen <= n)
                      ? P.final_state + (((size_t)t.b * P.Hv + t.h) * D + t.row) * D
                      : nullptr;
 

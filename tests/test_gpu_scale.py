@@ -57,19 +57,21 @@ def test_long_chain_outputs_and_final_states(d_):
         assert slice_rel_err(gfin[s].reshape(hv, -1), ref_fin.reshape(hv, -1)) <= TOL, s
 
 
-def test_largest_tree():
-    """A 256-node tree (the per-call maximum), depth up to 16."""
+@pytest.mark.parametrize("nodes", [96, 97, 256])
+def test_large_trees(nodes):
+    """96 nodes (the largest tree the MFMA verify takes), 97 (the smallest the
+    recurrent walk takes at d=128) and 256 (the per-call maximum)."""
     G = require_gpu()
-    rng = np.random.default_rng(22)
+    rng = np.random.default_rng(22 + nodes)
     hk, hv, d_ = 1, 3, 128
-    par = W.random_tree(rng, 256, 16)
-    T = 256
+    par = W.random_tree(rng, nodes, 16)
+    T = nodes
     inp = {"q": _bf(_unit(rng, T, hk, d_)), "k": _bf(_unit(rng, T, hk, d_)),
            "v": _bf(rng.standard_normal((T, hv, d_))),
            "a": rng.uniform(0.5, 1.0, (T, hv)).astype(np.float32),
            "b": rng.uniform(0.0, 1.0, (T, hv)).astype(np.float32)}
     S0 = (0.3 * rng.standard_normal((1, hv, d_, d_))).astype(np.float32)
-    dims = G.make_dims(1, T, 256, hk, hv, d_, 1, G.GDN_BF16)
+    dims = G.make_dims(1, T, nodes, hk, hv, d_, 1, G.GDN_BF16)
     ws = G.new_workspace(dims)
     dev = {k: to_dev(v) for k, v in inp.items()}
     cache = to_dev(S0.copy())
