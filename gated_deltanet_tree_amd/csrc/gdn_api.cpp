@@ -60,7 +60,7 @@ extern "C" {
 
 size_t gdn_workspace_bytes(const gdn_dims *dims) {
     if (!dims || !dims_ok(dims, GDN_MAX_CHAIN)) return 0;
-    return gdn::ws_layout(dims->num_seqs, dims->total_nodes).total;
+    return gdn::ws_layout(dims->num_seqs, dims->total_nodes, dims->num_v_heads).total;
 }
 
 int gdn_tree_plan(const gdn_dims *dims, const int32_t *parent, const int32_t *cu_nodes,
@@ -75,7 +75,7 @@ int gdn_tree_plan(const gdn_dims *dims, const int32_t *parent, const int32_t *cu
     p.parent = parent;
     p.cu_nodes = cu_nodes;
     p.slot_idx = slot_idx;
-    p.ws = gdn::ws_ptrs(ws, p.B, p.T);
+    p.ws = gdn::ws_ptrs(ws, p.B, p.T, p.Hv);
     p.has_ws = 1;
     return launched(gdn::launch_plan(p, as_stream(stream)));
 }
@@ -100,7 +100,7 @@ int gdn_tree_verify(const gdn_dims *dims, const void *q, const void *k, const vo
     p.state_in = state_cache;
     p.slot_idx = slot_idx;
     p.out = out;
-    p.ws = gdn::ws_ptrs(const_cast<void *>(ws), p.B, p.T);
+    p.ws = gdn::ws_ptrs(const_cast<void *>(ws), p.B, p.T, p.Hv);
     p.has_ws = 1;
     // the MFMA verify covers trees of up to 96 nodes; larger trees walk the
     // tree recurrently
@@ -128,7 +128,7 @@ int gdn_tree_persist(const gdn_dims *dims, const void *k, const void *v, const f
     p.state_in = state_cache;
     p.state_out = state_cache;
     p.slot_idx = slot_idx;
-    p.ws = gdn::ws_ptrs(ws, p.B, p.T);
+    p.ws = gdn::ws_ptrs(ws, p.B, p.T, p.Hv);
     p.has_ws = 1;
     if (gdn::fast_path_supported(p.D, dims->qkv_dtype))
         return launched(gdn::launch_persist_fast(p, as_stream(stream)));
@@ -147,6 +147,8 @@ int gdn_chain_verify(const gdn_dims *dims, const int32_t *cu_nodes, const void *
     if (dims->total_nodes > 0 && (!k || !v || !a || !b)) return GDN_ERR_NULL;
     if (dims->num_seqs > 0 && (!state_cache || !slot_idx)) return GDN_ERR_NULL;
     if (ws && ws_bytes < gdn_workspace_bytes(dims)) return GDN_ERR_WORKSPACE;
+    const bool fast = gdn::fast_path_supported(dims->head_dim, dims->qkv_dtype) && dims->max_nodes <= GDN_MAX_DEPTH;
+    if (fast && q && !ws) return GDN_ERR_NULL;  // the outputs need the workspace for coefficients
     if (dims->num_seqs == 0) return GDN_OK;
     Params p = base_params(dims);
     p.cu_nodes = cu_nodes;
@@ -161,13 +163,12 @@ int gdn_chain_verify(const gdn_dims *dims, const int32_t *cu_nodes, const void *
     p.final_len = final_len;
     p.final_state = final_state;
     if (ws) {
-        p.ws = gdn::ws_ptrs(ws, p.B, p.T);
+        p.ws = gdn::ws_ptrs(ws, p.B, p.T, p.Hv);
         p.has_ws = 1;
     }
     // chains that fit one drafting block share the tree kernels' arithmetic;
     // longer chains (e.g. prefill) run the sequential recurrence
-    if (gdn::fast_path_supported(p.D, dims->qkv_dtype) && dims->max_nodes <= GDN_MAX_DEPTH)
-        return launched(gdn::launch_chain_verify_fast(p, as_stream(stream)));
+    if (fast) return launched(gdn::launch_chain_verify_fast(p, as_stream(stream)));
     return launched(gdn::launch_chain_verify_recurrent(p, dims->qkv_dtype, as_stream(stream)));
 }
 

@@ -14,6 +14,12 @@
 // Replay (persist) needs S^m for one root-to-node path of <= 16 nodes: it
 // reads S0 once, forms S0 k_e for the path keys with VALU dot products, runs
 // the same recurrence and writes G_m S0 + sum_e R(m,e) c_e k_e^T in place.
+#include <algorithm>
+
+#ifndef GDN_REPLAY_ROWS
+#define GDN_REPLAY_ROWS 64  // rows per replay workgroup (4 lanes each)
+#endif
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -46,135 +52,242 @@ struct VG {
     static constexpr int KS = D / 16;         // MFMA 32x32x16 k-steps
 };
 
-// Per-position tables (positions = tree preorder, or chain order).
-struct VTab {
-    int *order;     // [cap] local node id
-    int *pos_of;    // [cap] position of a local node id
-    int *depth;     // [cap]
-    int *anc;       // [cap][16] ancestor positions, root first (anc[p][d-1] = p), 0 beyond
-    float *a, *b, *gamma, *alpha, *self_m;  // [cap]; self_m = k_p . q_p
-    float *R;       // [cap][16] R(p, e) for e < d
-    float *coefL;   // [cap][16] b_p R(p,e) (k_anc . k_p) for e < d-1, else 0
-    float *coefM;   // [cap][16] R(p,e) (k_anc . q_p) for e < d-1, else 0
-    float *mt;      // [np][np]  output operator (see verify_kernel), dense, 0 off-path
-    float *rt;      // [tiles-1][WAVES][16][64]  earlier blocks' right-hand sides
-};
-
-__host__ __device__ inline int pad_tiles(int cap) { return (cap + kTile - 1) / kTile; }
-
-__host__ __device__ inline size_t vtab_bytes(int cap, int D) {
-    const size_t c = (size_t)cap;
-    const size_t tiles = (size_t)pad_tiles(cap), np = tiles * kTile;
-    return np * np * 4 + (tiles - 1) * (size_t)(D / 32) * 16 * 64 * 4 + 4 * c * kPath * 4 + 3 * c * 4 + 5 * c * 4;
-}
-
-__device__ inline VTab vtab_carve(char *base, int cap, int D) {
-    VTab L;
-    const size_t c = (size_t)cap;
-    const size_t tiles = (size_t)pad_tiles(cap), np = tiles * kTile;
-    L.mt = reinterpret_cast<float *>(base);      base += np * np * 4;
-    L.rt = reinterpret_cast<float *>(base);      base += (tiles - 1) * (size_t)(D / 32) * 16 * 64 * 4;
-    L.R = reinterpret_cast<float *>(base);       base += c * kPath * 4;
-    L.coefL = reinterpret_cast<float *>(base);   base += c * kPath * 4;
-    L.coefM = reinterpret_cast<float *>(base);   base += c * kPath * 4;
-    L.anc = reinterpret_cast<int *>(base);       base += c * kPath * 4;
-    L.order = reinterpret_cast<int *>(base);     base += c * 4;
-    L.pos_of = reinterpret_cast<int *>(base);    base += c * 4;
-    L.depth = reinterpret_cast<int *>(base);     base += c * 4;
-    L.a = reinterpret_cast<float *>(base);       base += c * 4;
-    L.b = reinterpret_cast<float *>(base);       base += c * 4;
-    L.gamma = reinterpret_cast<float *>(base);   base += c * 4;
-    L.alpha = reinterpret_cast<float *>(base);   base += c * 4;
-    L.self_m = reinterpret_cast<float *>(base);
-    return L;
-}
-
 __device__ __forceinline__ bf16x8 frag_of(const uint16_t *vec, int s, int hf) {
     const uint4 raw = *reinterpret_cast<const uint4 *>(vec + 16 * s + 8 * hf);
     return __builtin_bit_cast(bf16x8, raw);
 }
 __device__ __forceinline__ bf16x8 zero_frag() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
 
-// After order/depth/anc/a/b are in place: ratios, gamma, alpha; zeroed coefficients.
-template <int D>
-__device__ void finish_vtab(const VTab &L, int n, int tid) {
-    for (int idx = tid; idx < n * kPath; idx += VG<D>::THREADS) {
-        const int p = idx / kPath, e = idx % kPath;
-        const int d = L.depth[p];
-        float r = 0.0f;
-        if (e < d) {
-            r = 1.0f;
-            for (int t = e + 1; t < d; ++t) r *= L.a[L.anc[p * kPath + t]];
-        }
-        L.R[idx] = r;
-        L.coefL[idx] = 0.0f;
-        L.coefM[idx] = 0.0f;
-        if (e == 0) {
-            const float g = r * L.a[L.anc[p * kPath]];
-            L.gamma[p] = g;
-            L.alpha[p] = L.b[p] * g;
-        }
+// Sequence view shared by the two verify kernels.  CHAIN: sequence b is the
+// chain of nodes [cu[b], cu[b+1]) (validated here); else the plan's verdict.
+struct SeqView {
+    int lo, n, status, slot;
+};
+
+template <bool CHAIN>
+__device__ __forceinline__ SeqView seq_view(const Params &P, int b) {
+    SeqView v;
+    if (CHAIN) {
+        const int c0 = P.cu_nodes[b], c1 = P.cu_nodes[b + 1];
+        const bool in_bounds = 0 <= c0 && c0 <= c1 && c1 <= P.T;
+        v.lo = in_bounds ? c0 : 0;
+        v.n = in_bounds ? c1 - c0 : 0;
+        v.status = (in_bounds && v.n <= P.max_nodes) ? GDN_SEQ_OK : GDN_SEQ_BAD_NODES;
+        v.slot = (v.status == GDN_SEQ_OK && v.n > 0) ? P.slot_idx[b] : 0;
+        if (v.status == GDN_SEQ_OK && v.n > 0 && (v.slot < 0 || v.slot >= P.num_slots)) v.status = GDN_SEQ_BAD_SLOT;
+    } else {
+        const int4 info = *reinterpret_cast<const int4 *>(P.ws.seq_info + b * kSeqInfoInts);
+        v.lo = info.x;
+        v.n = info.y;
+        v.status = info.z;
+        v.slot = info.w;
     }
+    return v;
 }
 
-// Gram entries for every (ancestor, node) pair -> recurrence coefficients.
-// Block pairs (ti <= tj) are spread over the waves; in preorder (and chain
-// order) an ancestor never sits at a later position than its descendant.
-template <int D>
-__device__ void gram(const VTab &L, int n, const uint16_t *kb, const uint16_t *qb, size_t kq_stride, int w,
-                     int hf, int l32) {
+// Ancestor e (root first) of local node i: the plan's path, or e for a chain.
+template <bool CHAIN>
+__device__ __forceinline__ int anc_of(const Params &P, int lo, int i, int e) {
+    if (CHAIN) return e <= i ? e : 0;
+    const int a = P.ws.nodepath[(size_t)(lo + i) * GDN_MAX_DEPTH + e];
+    return a < 0 ? 0 : a;
+}
+
+// ===========================================================================
+// Verify, part 1: coefficients.  One workgroup per (sequence, key head); the
+// value heads of the group share the tree, the keys/queries and the Gram
+// entries k_anc . k_i and k_anc . q_i.  Per (node i, value head) it writes
+//   y_i[e] (e < 16), gamma_i, alpha_i = b_i gamma_i, b_i, depth_i
+// into the workspace, where, with R(i,e) = a_{anc_{e+1}} ... a_{anc_{d-1}},
+//   Lc[i][e] = b_i R(i,e) (k_{anc_e} . k_i)      (e < d-1)
+//   m_i[e]   = R(i,e) (k_{anc_e} . q_i)           (e < d-1),   m_i[d-1] = k_i . q_i
+//   y_i      = m_i (I + Lc_path(i))^-1, by back substitution over i's path:
+//   y_{d-1} = m_i[d-1],   y_e = m_i[e] - sum_{f>e} y_f Lc[anc_f][e].
+// Then o_i = gamma_i (S0 q_i) + sum_e y_i[e] r_{anc_e(i)} with
+// r_j = b_j v_j - alpha_j (S0 k_j): see the main kernel.
+// ===========================================================================
+constexpr int kCoefThreads = 256;
+constexpr int kCoefMaxHeadsPerPass = 8;
+
+struct CTab {
+    int *anc;        // [cap][16]
+    int *depth;      // [cap]
+    uint32_t *amask; // [cap][4]
+    float *gk, *gq;  // [cap][16] path-indexed Gram entries
+    float *a, *b;    // [grp][cap]
+    float *coefL;    // [hpp][cap][16]
+};
+
+__host__ __device__ inline size_t ctab_bytes(int cap, int grp, int hpp) {
+    const size_t c = (size_t)cap;
+    return c * kPath * 4 + c * 4 + c * 16 + 2 * c * kPath * 4 + 2 * (size_t)grp * c * 4 + (size_t)hpp * c * kPath * 4;
+}
+
+__device__ inline CTab ctab_carve(char *base, int cap, int grp, int hpp) {
+    CTab L;
+    const size_t c = (size_t)cap;
+    L.anc = reinterpret_cast<int *>(base);        base += c * kPath * 4;
+    L.gk = reinterpret_cast<float *>(base);       base += c * kPath * 4;
+    L.gq = reinterpret_cast<float *>(base);       base += c * kPath * 4;
+    L.coefL = reinterpret_cast<float *>(base);    base += (size_t)hpp * c * kPath * 4;
+    L.amask = reinterpret_cast<uint32_t *>(base); base += c * 16;
+    L.depth = reinterpret_cast<int *>(base);      base += c * 4;
+    L.a = reinterpret_cast<float *>(base);        base += (size_t)grp * c * 4;
+    L.b = reinterpret_cast<float *>(base);
+    return L;
+}
+
+template <int D, bool CHAIN>
+__global__ __launch_bounds__(kCoefThreads) void coef_kernel(Params P) {
+    extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+    constexpr int KS = D / 16;
+    const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, hf = lane / 32, l32 = lane % 32;
+    const int grp = P.Hv / P.Hk;
+    const int b = blockIdx.x / P.Hk, g = blockIdx.x % P.Hk;
+    const SeqView sv = seq_view<CHAIN>(P, b);
+    if (!CHAIN && !ws_planned(P)) return;
+    if (sv.status != GDN_SEQ_OK || sv.n == 0) return;
+    const int lo = sv.lo, n = sv.n;
+    const int cap = CHAIN ? kPath : P.max_nodes;
+    const int hpp = max(1, min(min(grp, kCoefMaxHeadsPerPass), kCoefThreads / n));  // value heads per pass
+    const CTab L = ctab_carve(lds_raw, cap, grp, hpp);
+
+    // tree tables and ancestor masks, gates of every head of the group
+    for (int i = tid; i < n; i += kCoefThreads) {
+        int an[kPath];
+#pragma unroll
+        for (int e = 0; e < kPath; ++e) an[e] = anc_of<CHAIN>(P, lo, i, e);
+        const int d = CHAIN ? i + 1 : P.ws.depth[lo + i];
+        uint32_t m[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < kPath; ++e) {
+            L.anc[i * kPath + e] = an[e];
+            if (e < d) m[an[e] >> 5] |= 1u << (an[e] & 31);
+        }
+        L.depth[i] = d;
+        *reinterpret_cast<uint4 *>(L.amask + i * 4) = make_uint4(m[0], m[1], m[2], m[3]);
+    }
+    for (int idx = tid; idx < grp * n; idx += kCoefThreads) {
+        const int hh = idx / n, i = idx % n;
+        const size_t at = (size_t)(lo + i) * P.Hv + g * grp + hh;
+        L.a[hh * cap + i] = P.a[at];
+        L.b[hh * cap + i] = P.b[at];
+    }
+    __syncthreads();
+
+    // Gram entries for every (ancestor, node) pair on the matrix cores
+    const uint16_t *kb = static_cast<const uint16_t *>(P.k) + ((size_t)lo * P.Hk + g) * D;
+    const uint16_t *qb = static_cast<const uint16_t *>(P.q) + ((size_t)lo * P.Hk + g) * D;
+    const size_t kq_stride = (size_t)P.Hk * D;
     const int ntiles = (n + kTile - 1) / kTile;
-    int pair = 0;
-    for (int tj = 0; tj < ntiles; ++tj) {
-        for (int ti = 0; ti <= tj; ++ti, ++pair) {
-            if (pair % VG<D>::WAVES != w) continue;
-            const int pi = ti * kTile + l32, pj = tj * kTile + l32;
-            const uint16_t *ki = pi < n ? kb + (size_t)L.order[pi] * kq_stride : nullptr;
-            const uint16_t *kj = pj < n ? kb + (size_t)L.order[pj] * kq_stride : nullptr;
-            const uint16_t *qj = pj < n ? qb + (size_t)L.order[pj] * kq_stride : nullptr;
-            f32x16 gkk = {}, gkq = {};
+    for (int pair = w; pair < ntiles * ntiles; pair += kCoefThreads / 64) {
+        const int ti = pair % ntiles, tj = pair / ntiles;
+        const int pi = ti * kTile + l32, pj = tj * kTile + l32;
+        f32x16 gkk = {}, gkq = {};
 #pragma unroll
-            for (int s = 0; s < VG<D>::KS; ++s) {
-                const bf16x8 A = ki ? frag_of(ki, s, hf) : zero_frag();
-                const bf16x8 Bk = kj ? frag_of(kj, s, hf) : zero_frag();
-                const bf16x8 Bq = qj ? frag_of(qj, s, hf) : zero_frag();
-                gkk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bk, gkk, 0, 0, 0);
-                gkq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bq, gkq, 0, 0, 0);
-            }
-            if (pj < n) {  // accumulator r: (candidate ancestor i, node pj)
-                const int dj = L.depth[pj];
+        for (int s = 0; s < KS; ++s) {
+            const bf16x8 A = pi < n ? frag_of(kb + (size_t)pi * kq_stride, s, hf) : zero_frag();
+            const bf16x8 Bk = pj < n ? frag_of(kb + (size_t)pj * kq_stride, s, hf) : zero_frag();
+            const bf16x8 Bq = pj < n ? frag_of(qb + (size_t)pj * kq_stride, s, hf) : zero_frag();
+            gkk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bk, gkk, 0, 0, 0);
+            gkq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bq, gkq, 0, 0, 0);
+        }
+        if (pj < n) {  // accumulator r: (candidate ancestor ti*32 + il, node pj)
+            const uint32_t mask = L.amask[pj * 4 + ti];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int i = ti * kTile + 8 * (r / 4) + 4 * hf + (r % 4);
-                    if (i >= n) continue;
-                    const int di = L.depth[i];
-                    if (di > dj || L.anc[pj * kPath + di - 1] != i) continue;
-                    const int e = di - 1;
-                    const float R = L.R[pj * kPath + e];
-                    if (e < dj - 1) {
-                        L.coefL[pj * kPath + e] = L.b[pj] * R * gkk[r];
-                        L.coefM[pj * kPath + e] = R * gkq[r];
-                    } else {
-                        L.self_m[pj] = gkq[r];
-                    }
+            for (int r = 0; r < 16; ++r) {
+                const int il = 8 * (r / 4) + 4 * hf + (r % 4);
+                if ((mask >> il) & 1u) {
+                    const int e = L.depth[ti * kTile + il] - 1;
+                    L.gk[pj * kPath + e] = gkk[r];
+                    L.gq[pj * kPath + e] = gkq[r];
                 }
             }
         }
     }
+    __syncthreads();
+
+    for (int h0 = 0; h0 < grp; h0 += hpp) {
+        const int hh = h0 + tid / n, i = tid % n;
+        const bool act = tid < hpp * n && hh < grp;
+        const int slot_h = tid / n;
+        float mrow[kPath], gamma = 0.0f, bi = 0.0f;
+        int an[kPath], d = 0;
+        if (act) {
+            d = L.depth[i];
+            bi = L.b[hh * cap + i];
+            float av[kPath];
+#pragma unroll
+            for (int e = 0; e < kPath; ++e) an[e] = L.anc[i * kPath + e];
+#pragma unroll
+            for (int e = 0; e < kPath; ++e) av[e] = e < d ? L.a[hh * cap + an[e]] : 1.0f;
+            float r = 1.0f;
+#pragma unroll
+            for (int e = kPath - 1; e >= 0; --e) {
+                const bool on = e < d - 1;
+                L.coefL[(slot_h * cap + i) * kPath + e] = on ? bi * r * L.gk[i * kPath + e] : 0.0f;
+                mrow[e] = on ? r * L.gq[i * kPath + e] : (e == d - 1 ? L.gq[i * kPath + e] : 0.0f);
+                r *= av[e];
+            }
+            gamma = r;
+        }
+        __syncthreads();
+        if (act) {
+            float y[kPath];
+#pragma unroll
+            for (int e = kPath - 1; e >= 0; --e) {
+                float acc = mrow[e];
+                // deepest terms first: y_{e+1}, the last one known, enters last
+#pragma unroll
+                for (int f = kPath - 1; f > e; --f)
+                    acc = fmaf(-y[f], L.coefL[(slot_h * cap + an[f]) * kPath + e], acc);
+                y[e] = e < d ? acc : 0.0f;
+            }
+            float4 *rec = reinterpret_cast<float4 *>(P.ws.coef + ((size_t)(lo + i) * P.Hv + g * grp + hh) * kCoefFloats);
+#pragma unroll
+            for (int e = 0; e < kPath; e += 4) rec[e / 4] = make_float4(y[e], y[e + 1], y[e + 2], y[e + 3]);
+            rec[4] = make_float4(gamma, bi * gamma, bi, __int_as_float(d));
+        }
+        __syncthreads();
+    }
 }
 
-// Verify one sequence/head.  CHAIN: positions are nodes 0..n-1 of a chain
-// (n <= 16 per call); else the plan's preorder.
-//
-// With r_p = b_p v_p - alpha_p (S0 k_p) (a row vector), the c_p solve
-// (I + Lc) c = r along every path, and o_p = gamma_p (S0 q_p) + m_p . c over
-// p's path (m_p = coefM row plus k_p . q_p for p itself).  So
-//     O = diag(gamma) (S0 Q^T)  +  MT R,    MT[p] = m_p (I + Lc_path(p))^-1,
-// and row p of MT follows from a backward substitution over p's own path:
-//     y_{d-1} = k_p . q_p,   y_e = m_{p,e} - sum_{f>e} y_f Lc[anc_f][e].
-// X = S0 K^T, Y = S0 Q^T come from bf16 MFMA (state split hi + lo); O from
-// fp32 MFMA whose B operand is R exactly as the first MFMA left it.
-template <int D, bool CHAIN>
+// ===========================================================================
+// Verify, part 2: one workgroup per (sequence, value head), D/32 waves; wave
+// w owns state rows [32w, 32w+32).  With the records of part 1:
+//   X = S0 K^T, Y = S0 Q^T          bf16 MFMA (state split hi + lo; keys exact)
+//   r_j = b_j v_j - alpha_j X_j     in the MFMA accumulator layout
+//   O = diag(gamma) Y + MT R        MT[i][anc_e(i)] = y_i[e]
+// MT tiles: node blocks of 32 (1: trees of <= 32 nodes; the product then
+// runs on fp32 MFMA straight from the accumulators of the first product).
+// ===========================================================================
+struct VTab {
+    uint16_t *kq;   // [2][32][D] bf16 keys / queries (single-block trees)
+    float *mt;      // [32][32] dense MT (single-block trees)
+    float *rbuf;    // [cap][D] r rows (multi-block trees)
+    float *y;       // [cap][16] path weights
+    int *anc;       // [cap][16]
+    float4 *gabd;   // [cap] gamma, alpha, b, depth
+};
+
+__host__ __device__ inline size_t vtab_bytes(int cap, int D, bool single) {
+    const size_t c = (size_t)cap;
+    return (single ? (size_t)2 * kTile * D * 2 + (size_t)kTile * kTile * 4 : c * D * 4) + 2 * c * kPath * 4 + c * 16;
+}
+
+__device__ inline VTab vtab_carve(char *base, int cap, int D, bool single) {
+    VTab L;
+    const size_t c = (size_t)cap;
+    L.gabd = reinterpret_cast<float4 *>(base);  base += c * 16;
+    L.kq = reinterpret_cast<uint16_t *>(base);  base += single ? (size_t)2 * kTile * D * 2 : 0;
+    L.mt = reinterpret_cast<float *>(base);     base += single ? (size_t)kTile * kTile * 4 : 0;
+    L.rbuf = reinterpret_cast<float *>(base);   base += single ? 0 : c * D * 4;
+    L.y = reinterpret_cast<float *>(base);      base += c * kPath * 4;
+    L.anc = reinterpret_cast<int *>(base);
+    return L;
+}
+
+template <int D, bool CHAIN, int MT>
 __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(3))) void verify_kernel(Params P) {
     extern __shared__ __attribute__((aligned(16))) char lds_raw[];
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, hf = lane / 32, l32 = lane % 32;
@@ -182,42 +295,36 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
     const int b = blockIdx.x / P.Hv, h = blockIdx.x % P.Hv;
     const int g = h / (P.Hv / P.Hk);
     const size_t out_stride = (size_t)P.Hv * D;
-
-    int lo, n, status, slot;
-    if (CHAIN) {
-        const int c0 = P.cu_nodes[b], c1 = P.cu_nodes[b + 1];
-        const bool in_bounds = 0 <= c0 && c0 <= c1 && c1 <= P.T;
-        lo = in_bounds ? c0 : 0;
-        n = in_bounds ? c1 - c0 : 0;
-        status = (in_bounds && n <= P.max_nodes) ? GDN_SEQ_OK : GDN_SEQ_BAD_NODES;
-        slot = (status == GDN_SEQ_OK && n > 0) ? P.slot_idx[b] : 0;
-        if (status == GDN_SEQ_OK && n > 0 && (slot < 0 || slot >= P.num_slots)) status = GDN_SEQ_BAD_SLOT;
-        if (P.has_ws && h == 0 && tid == 0) {
-            if (b == 0) {
-                P.ws.header[0] = kMagic;
-                P.ws.header[1] = P.B;
-                P.ws.header[2] = P.T;
-            }
-            P.ws.seq_status[b] = status;
+    const SeqView sv = seq_view<CHAIN>(P, b);  // loaded together with the header check below
+    if (!CHAIN && !ws_planned(P)) return;
+    if (CHAIN && P.has_ws && h == 0 && tid == 0) {
+        if (b == 0) {
+            P.ws.header[0] = kMagic;
+            P.ws.header[1] = P.B;
+            P.ws.header[2] = P.T;
         }
-        if (!P.out) return;
-    } else {
-        if (!ws_planned(P)) return;
-        lo = P.ws.seq_info[b * kSeqInfoInts + 0];
-        n = P.ws.seq_info[b * kSeqInfoInts + 1];
-        status = P.ws.seq_status[b];
-        slot = P.slot_idx[b];
+        P.ws.seq_status[b] = sv.status;
     }
+    if (!P.out) return;
+    const int lo = sv.lo, n = sv.n;
     float *out_base = P.out + ((size_t)lo * P.Hv + h) * D + row;
-    if (status != GDN_SEQ_OK) {
+    if (sv.status != GDN_SEQ_OK) {
         if (hf == 0)
             for (int i = 0; i < n; ++i) out_base[i * out_stride] = qnan_f();
         return;
     }
     if (n == 0) return;
 
-    // committed state rows as MFMA B fragments (issued first: longest latency)
-    const float *srow = P.state_in + (((size_t)slot * P.Hv + h) * D + row) * D;
+    constexpr bool kSingle = MT == 1;
+    const int cap = CHAIN ? kPath : P.max_nodes;
+    const VTab L = vtab_carve(lds_raw, cap, D, kSingle);
+    const uint16_t *kb = static_cast<const uint16_t *>(P.k) + ((size_t)lo * P.Hk + g) * D;
+    const uint16_t *qb = static_cast<const uint16_t *>(P.q) + ((size_t)lo * P.Hk + g) * D;
+    const uint16_t *vb = static_cast<const uint16_t *>(P.v) + ((size_t)lo * P.Hv + h) * D + row;
+    const size_t kq_stride = (size_t)P.Hk * D, v_stride = (size_t)P.Hv * D;
+
+    // ---- one round trip: every load is issued before any result is used
+    const float *srow = P.state_in + (((size_t)sv.slot * P.Hv + h) * D + row) * D;
     float sf[VG<D>::KS][8];
 #pragma unroll
     for (int s = 0; s < VG<D>::KS; ++s) {
@@ -226,45 +333,50 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         sf[s][0] = x0.x; sf[s][1] = x0.y; sf[s][2] = x0.z; sf[s][3] = x0.w;
         sf[s][4] = x1.x; sf[s][5] = x1.y; sf[s][6] = x1.z; sf[s][7] = x1.w;
     }
-
-    const int cap = CHAIN ? kPath : P.max_nodes;
-    const VTab L = vtab_carve(lds_raw, cap, D);
-    const int np = pad_tiles(cap) * kTile;
-    const float *ga = P.a + (size_t)lo * P.Hv + h;
-    const float *gb = P.b + (size_t)lo * P.Hv + h;
-    if (CHAIN) {
-        for (int idx = tid; idx < n * kPath; idx += VG<D>::THREADS) {
-            const int p = idx / kPath, e = idx % kPath;
-            L.anc[idx] = e <= p ? e : 0;
-            if (e == 0) {
-                L.order[p] = p;
-                L.depth[p] = p + 1;
-                L.a[p] = ga[(size_t)p * P.Hv];
-                L.b[p] = gb[(size_t)p * P.Hv];
-            }
-        }
-    } else {
-        for (int p = tid; p < n; p += VG<D>::THREADS) {
-            const int node = P.ws.order[lo + p];
-            L.order[p] = node;
-            L.pos_of[node] = p;
-            L.depth[p] = P.ws.depth[lo + node];
-            L.a[p] = ga[(size_t)node * P.Hv];
-            L.b[p] = gb[(size_t)node * P.Hv];
-        }
-        __syncthreads();
-        for (int idx = tid; idx < n * kPath; idx += VG<D>::THREADS) {
-            const int p = idx / kPath, e = idx % kPath;
-            L.anc[idx] = e < L.depth[p]
-                             ? L.pos_of[P.ws.nodepath[(size_t)(lo + L.order[p]) * GDN_MAX_DEPTH + e]]
-                             : 0;
+    constexpr int KQ_PER = kSingle ? (2 * kTile * D / 8 + VG<D>::THREADS - 1) / VG<D>::THREADS : 1;
+    uint4 kqv[KQ_PER];
+    if (kSingle) {
+#pragma unroll
+        for (int u = 0; u < KQ_PER; ++u) {
+            const int idx = tid + u * VG<D>::THREADS;
+            const int which = idx / (kTile * (D / 8)), rem = idx % (kTile * (D / 8));
+            const int i = rem / (D / 8), c8 = rem % (D / 8);
+            kqv[u] = (which < 2 && i < n)
+                         ? *reinterpret_cast<const uint4 *>((which ? qb : kb) + (size_t)i * kq_stride + 8 * c8)
+                         : make_uint4(0, 0, 0, 0);
         }
     }
-    for (int idx = tid; idx < np * np; idx += VG<D>::THREADS) L.mt[idx] = 0.0f;
-    __syncthreads();
-    finish_vtab<D>(L, n, tid);
-
-    // hi/lo split of the state for the bf16 MFMA
+    uint16_t vraw[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int i = 8 * (r / 4) + 4 * hf + (r % 4);
+        vraw[r] = i < n ? vb[(size_t)i * v_stride] : uint16_t(0);
+    }
+    const float *coef = P.ws.coef + ((size_t)lo * P.Hv + h) * kCoefFloats;
+    for (int i = tid; i < n; i += VG<D>::THREADS) {
+        const float4 *rec = reinterpret_cast<const float4 *>(coef + (size_t)i * P.Hv * kCoefFloats);
+        const float4 y0 = rec[0], y1 = rec[1], y2 = rec[2], y3 = rec[3], gabd = rec[4];
+        int an[kPath];
+#pragma unroll
+        for (int e = 0; e < kPath; ++e) an[e] = anc_of<CHAIN>(P, lo, i, e);
+        float4 *ydst = reinterpret_cast<float4 *>(L.y + i * kPath);
+        ydst[0] = y0;
+        ydst[1] = y1;
+        ydst[2] = y2;
+        ydst[3] = y3;
+#pragma unroll
+        for (int e = 0; e < kPath; e += 4)
+            *reinterpret_cast<int4 *>(L.anc + i * kPath + e) = make_int4(an[e], an[e + 1], an[e + 2], an[e + 3]);
+        L.gabd[i] = gabd;
+    }
+    if (kSingle) {
+#pragma unroll
+        for (int u = 0; u < KQ_PER; ++u) {
+            const int idx = tid + u * VG<D>::THREADS;
+            if (idx < 2 * kTile * (D / 8)) reinterpret_cast<uint4 *>(L.kq)[idx] = kqv[u];
+        }
+        for (int idx = tid; idx < kTile * kTile; idx += VG<D>::THREADS) L.mt[idx] = 0.0f;
+    }
     bf16x8 shi[VG<D>::KS], slo[VG<D>::KS];
 #pragma unroll
     for (int s = 0; s < VG<D>::KS; ++s) {
@@ -275,104 +387,121 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
             slo[s][e] = static_cast<__bf16>(sf[s][e] - static_cast<float>(hb));
         }
     }
-    const uint16_t *kb = static_cast<const uint16_t *>(P.k) + ((size_t)lo * P.Hk + g) * D;
-    const uint16_t *qb = static_cast<const uint16_t *>(P.q) + ((size_t)lo * P.Hk + g) * D;
-    const uint16_t *vb = static_cast<const uint16_t *>(P.v) + ((size_t)lo * P.Hv + h) * D + row;
-    const size_t kq_stride = (size_t)P.Hk * D, v_stride = (size_t)P.Hv * D;
-    __syncthreads();
-    gram<D>(L, n, kb, qb, kq_stride, w, hf, l32);
     __syncthreads();
 
-    // output operator rows, one position per thread
-    for (int p = tid; p < n; p += VG<D>::THREADS) {
-        const int d = L.depth[p];
-        int af[kPath];
-#pragma unroll
-        for (int f = 0; f < kPath; ++f) af[f] = L.anc[p * kPath + f];
-        float y[kPath];
-#pragma unroll
-        for (int e = kPath - 1; e >= 0; --e) {
-            float acc = e == d - 1 ? L.self_m[p] : L.coefM[p * kPath + e];
-#pragma unroll
-            for (int f = e + 1; f < kPath; ++f) acc = fmaf(-y[f], L.coefL[af[f] * kPath + e], acc);
-            y[e] = e < d ? acc : 0.0f;
+    if (kSingle) {
+        // dense MT from the path weights
+        for (int idx = tid; idx < n * kPath; idx += VG<D>::THREADS) {
+            const int i = idx / kPath, e = idx % kPath;
+            if (e < __float_as_int(L.gabd[i].w)) L.mt[i * kTile + L.anc[idx]] = L.y[idx];
         }
-#pragma unroll
-        for (int e = 0; e < kPath; ++e)
-            if (e < d) L.mt[p * np + af[e]] = y[e];
-    }
-    __syncthreads();
-
-    const int ntiles = (n + kTile - 1) / kTile;
-    for (int t = 0; t < ntiles; ++t) {
-        const int p0 = t * kTile;
-        // this lane's 16 (position, row) entries of the block: position p0 + ip(r)
-        float vv[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int p = p0 + 8 * (r / 4) + 4 * hf + (r % 4);
-            vv[r] = p < n ? bf2f(vb[(size_t)L.order[p] * v_stride]) : 0.0f;
-        }
-        const int pi = p0 + l32;
-        const uint16_t *kr = pi < n ? kb + (size_t)L.order[pi] * kq_stride : nullptr;
-        const uint16_t *qr = pi < n ? qb + (size_t)L.order[pi] * kq_stride : nullptr;
+        const uint16_t *kr = L.kq + (size_t)l32 * D;
+        const uint16_t *qr = L.kq + (size_t)(kTile + l32) * D;
         f32x16 ax = {}, ay = {};
 #pragma unroll
         for (int s = 0; s < VG<D>::KS; ++s) {
-            const bf16x8 Ak = kr ? frag_of(kr, s, hf) : zero_frag();
-            const bf16x8 Aq = qr ? frag_of(qr, s, hf) : zero_frag();
+            const bf16x8 Ak = frag_of(kr, s, hf);
+            const bf16x8 Aq = frag_of(qr, s, hf);
             ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, shi[s], ax, 0, 0, 0);
             ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, slo[s], ax, 0, 0, 0);
             ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, shi[s], ay, 0, 0, 0);
             ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, slo[s], ay, 0, 0, 0);
         }
-        // r = b v - alpha x;  o starts as gamma y
         f32x16 rr, oo;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int p = p0 + 8 * (r / 4) + 4 * hf + (r % 4);
-            const bool in = p < n;
-            rr[r] = in ? fmaf(-L.alpha[p], ax[r], L.b[p] * vv[r]) : 0.0f;
-            oo[r] = in ? L.gamma[p] * ay[r] : 0.0f;
+            const int i = 8 * (r / 4) + 4 * hf + (r % 4);
+            const float4 gabd = L.gabd[min(i, n - 1)];
+            rr[r] = i < n ? fmaf(-gabd.y, ax[r], gabd.z * bf2f(vraw[r])) : 0.0f;
+            oo[r] = i < n ? gabd.x * ay[r] : 0.0f;
         }
-        if (t + 1 < ntiles) {
-            float *dst = L.rt + ((size_t)t * VG<D>::WAVES + w) * 16 * 64;
+        __syncthreads();
+        // O += MT R: k-step s pairs the nodes held in accumulator slot s by the two half-waves
+        const float *mrow = L.mt + l32 * kTile;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) dst[r * 64 + lane] = rr[r];
-        }
-        // O += MT[block t, block j] R_j for j <= t
-        const float *mrow = L.mt + (size_t)(p0 + l32) * np;
-        for (int j = 0; j < t; ++j) {
-            const float *src = L.rt + ((size_t)j * VG<D>::WAVES + w) * 16 * 64;
-#pragma unroll
-            for (int s = 0; s < 16; ++s) {
-                const float am = mrow[j * kTile + 8 * (s / 4) + 4 * hf + (s % 4)];
-                oo = __builtin_amdgcn_mfma_f32_32x32x2f32(am, src[s * 64 + lane], oo, 0, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < 16; ++s) {
-            const float am = mrow[p0 + 8 * (s / 4) + 4 * hf + (s % 4)];
-            oo = __builtin_amdgcn_mfma_f32_32x32x2f32(am, rr[s], oo, 0, 0, 0);
-        }
+        for (int s = 0; s < 16; ++s)
+            oo = __builtin_amdgcn_mfma_f32_32x32x2f32(mrow[8 * (s / 4) + 4 * hf + (s % 4)], rr[s], oo, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int p = p0 + 8 * (r / 4) + 4 * hf + (r % 4);
-            if (p < n) out_base[(size_t)L.order[p] * out_stride] = oo[r];
+            const int i = 8 * (r / 4) + 4 * hf + (r % 4);
+            if (i < n) out_base[(size_t)i * out_stride] = oo[r];
+        }
+        return;
+    }
+
+    // ---- multi-block trees: r rows through LDS, output on VALU
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        if (t * kTile < n) {
+            if (t > 0) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = t * kTile + 8 * (r / 4) + 4 * hf + (r % 4);
+                    vraw[r] = i < n ? vb[(size_t)i * v_stride] : uint16_t(0);
+                }
+            }
+            const int pi = t * kTile + l32;
+            f32x16 ax = {};
+#pragma unroll
+            for (int s = 0; s < VG<D>::KS; ++s) {
+                const bf16x8 Ak = pi < n ? frag_of(kb + (size_t)pi * kq_stride, s, hf) : zero_frag();
+                ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, shi[s], ax, 0, 0, 0);
+                ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, slo[s], ax, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = t * kTile + 8 * (r / 4) + 4 * hf + (r % 4);
+                if (i < n) {
+                    const float4 gabd = L.gabd[i];
+                    L.rbuf[(size_t)i * D + row] = fmaf(-gabd.y, ax[r], gabd.z * bf2f(vraw[r]));
+                }
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        if (t * kTile < n) {
+            const int pi = t * kTile + l32;
+            f32x16 ay = {};
+#pragma unroll
+            for (int s = 0; s < VG<D>::KS; ++s) {
+                const bf16x8 Aq = pi < n ? frag_of(qb + (size_t)pi * kq_stride, s, hf) : zero_frag();
+                ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, shi[s], ay, 0, 0, 0);
+                ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, slo[s], ay, 0, 0, 0);
+            }
+            // 16 nodes per lane; weights are zero past each node's depth
+            float o[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = min(t * kTile + 8 * (r / 4) + 4 * hf + (r % 4), n - 1);
+                o[r] = L.gabd[i].x * ay[r];
+            }
+#pragma unroll 1
+            for (int e = 0; e < kPath; ++e) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = min(t * kTile + 8 * (r / 4) + 4 * hf + (r % 4), n - 1);
+                    o[r] = fmaf(L.y[i * kPath + e], L.rbuf[(size_t)L.anc[i * kPath + e] * D + row], o[r]);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = t * kTile + 8 * (r / 4) + 4 * hf + (r % 4);
+                if (i < n) out_base[(size_t)i * out_stride] = o[r];
+            }
         }
     }
 }
 
-// ===========================================================================
-// Replay (persist, and the state a chain reaches after its first L nodes)
-// ===========================================================================
 template <int D>
 struct RG {
     static constexpr int LPR = 4;             // lanes per state row
     static constexpr int CPL = D / LPR;       // columns per lane
     static constexpr int NCH = CPL / 4;       // float4 chunks per lane
-    static constexpr int ROWS = D;            // rows per workgroup: the whole head
+    static constexpr int ROWS = GDN_REPLAY_ROWS;  // rows per workgroup
     static constexpr int THREADS = ROWS * LPR;
+    static constexpr int SLICES = D / ROWS;   // workgroups per (sequence, value head)
 };
 
 // column of element 0 of chunk c held by lane j of a row group: the 4 lanes
@@ -421,9 +550,10 @@ __global__ __launch_bounds__(RG<D>::THREADS) void replay_kernel(Params P) {
     extern __shared__ __attribute__((aligned(16))) char lds_raw[];
     using G = RG<D>;
     const int tid = threadIdx.x, j = tid % G::LPR;
-    const int b = blockIdx.x / P.Hv, h = blockIdx.x % P.Hv;
+    const int slice = blockIdx.x % G::SLICES;
+    const int b = blockIdx.x / G::SLICES / P.Hv, h = blockIdx.x / G::SLICES % P.Hv;
     const int g = h / (P.Hv / P.Hk);
-    const int row = tid / G::LPR;
+    const int row = slice * G::ROWS + tid / G::LPR;
 
     int lo, len, slot;
     const int32_t *path = nullptr;  // local node ids (null: chain 0..len-1)
@@ -444,7 +574,7 @@ __global__ __launch_bounds__(RG<D>::THREADS) void replay_kernel(Params P) {
         if (P.ws.seq_status[b] != GDN_SEQ_OK || n == 0) return;
         const int m = P.accepted[b];
         if (m < -1 || m >= n) {
-            if (h == 0 && tid == 0) P.ws.seq_status[b] = GDN_SEQ_BAD_ACCEPT;
+            if (h == 0 && slice == 0 && tid == 0) P.ws.seq_status[b] = GDN_SEQ_BAD_ACCEPT;
             return;
         }
         if (m == -1) return;
@@ -452,7 +582,7 @@ __global__ __launch_bounds__(RG<D>::THREADS) void replay_kernel(Params P) {
         slot = P.slot_idx[b];
         len = P.ws.depth[lo + m];
         path = P.ws.nodepath + (size_t)(lo + m) * GDN_MAX_DEPTH;
-        if (h == 0 && tid < GDN_MAX_DEPTH) {
+        if (h == 0 && slice == 0 && tid < GDN_MAX_DEPTH) {
             P.ws.path[b * GDN_MAX_DEPTH + tid] = path[tid];
             if (tid == 0) P.ws.path_len[b] = len;
         }
@@ -603,14 +733,22 @@ hipError_t launch_with_lds(K kernel, dim3 grid, dim3 block, size_t lds, hipStrea
 template <int D>
 hipError_t launch_verify_d(const Params &p, bool chain, hipStream_t s) {
     const int cap = chain ? kPath : p.max_nodes;
+    const int grp = p.Hv / p.Hk;
+    // LDS for the most value heads a pass can take (a one-node sequence)
+    const size_t clds = ctab_bytes(cap, grp, std::min(grp, kCoefMaxHeadsPerPass));
+    hipError_t e = chain ? launch_with_lds(coef_kernel<D, true>, dim3(p.B * p.Hk), dim3(kCoefThreads), clds, s, p)
+                         : launch_with_lds(coef_kernel<D, false>, dim3(p.B * p.Hk), dim3(kCoefThreads), clds, s, p);
+    if (e != hipSuccess) return e;
     const dim3 grid(p.B * p.Hv), block(VG<D>::THREADS);
-    return chain ? launch_with_lds(verify_kernel<D, true>, grid, block, vtab_bytes(cap, D), s, p)
-                 : launch_with_lds(verify_kernel<D, false>, grid, block, vtab_bytes(cap, D), s, p);
+    if (chain) return launch_with_lds(verify_kernel<D, true, 1>, grid, block, vtab_bytes(kPath, D, true), s, p);
+    if (p.max_nodes <= kTile)
+        return launch_with_lds(verify_kernel<D, false, 1>, grid, block, vtab_bytes(p.max_nodes, D, true), s, p);
+    return launch_with_lds(verify_kernel<D, false, 3>, grid, block, vtab_bytes(p.max_nodes, D, false), s, p);
 }
 
 template <int D>
 hipError_t launch_replay_d(const Params &p, bool chain, hipStream_t s) {
-    const dim3 grid(p.B * p.Hv), block(RG<D>::THREADS);
+    const dim3 grid(p.B * p.Hv * RG<D>::SLICES), block(RG<D>::THREADS);
     return chain ? launch_with_lds(replay_kernel<D, true>, grid, block, rtab_bytes(D), s, p)
                  : launch_with_lds(replay_kernel<D, false>, grid, block, rtab_bytes(D), s, p);
 }

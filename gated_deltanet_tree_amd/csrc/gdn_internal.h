@@ -12,16 +12,20 @@ namespace gdn {
 
 constexpr int32_t kMagic = 0x67646e74;  // written by the plan into the workspace header
 constexpr int kHeaderInts = 16;          // magic, B, T, max_nodes, max_depth, stack slots, ...
-constexpr int kSeqInfoInts = 4;          // node offset, node count, max stack, reserved
+constexpr int kSeqInfoInts = 8;          // node offset, node count, verdict, slot, max stack, reserved x3
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Byte offsets of the workspace regions (each 256-byte aligned).
+constexpr int kCoefFloats = 20;         // per (node, value head): 16 path weights, gamma, alpha, b, depth
+
+// Byte offsets of the workspace regions (each 256-byte aligned).  The
+// per-(node, head) coefficient records come last, so the other offsets do
+// not depend on the head count.
 struct WsLayout {
-    size_t header, seq_status, seq_info, depth, order, action, nodepath, path, path_len, total;
+    size_t header, seq_status, seq_info, depth, order, action, nodepath, path, path_len, coef, total;
 };
 
-__host__ __device__ inline WsLayout ws_layout(int B, int T) {
+__host__ __device__ inline WsLayout ws_layout(int B, int T, int Hv = 0) {
     const size_t b = B > 0 ? (size_t)B : 1, t = T > 0 ? (size_t)T : 1;
     WsLayout L;
     size_t off = 0;
@@ -34,16 +38,18 @@ __host__ __device__ inline WsLayout ws_layout(int B, int T) {
     L.nodepath = off;   off += align256(t * GDN_MAX_DEPTH * 4);
     L.path = off;       off += align256(b * GDN_MAX_DEPTH * 4);
     L.path_len = off;   off += align256(b * 4);
+    L.coef = off;       off += align256(t * (size_t)(Hv > 0 ? Hv : 0) * kCoefFloats * 4);
     L.total = off;
     return L;
 }
 
 struct WsPtrs {
     int32_t *header, *seq_status, *seq_info, *depth, *order, *action, *nodepath, *path, *path_len;
+    float *coef;
 };
 
-inline WsPtrs ws_ptrs(void *ws, int B, int T) {
-    const WsLayout L = ws_layout(B, T);
+inline WsPtrs ws_ptrs(void *ws, int B, int T, int Hv = 0) {
+    const WsLayout L = ws_layout(B, T, Hv);
     char *base = static_cast<char *>(ws);
     WsPtrs p;
     p.header = reinterpret_cast<int32_t *>(base + L.header);
@@ -55,6 +61,7 @@ inline WsPtrs ws_ptrs(void *ws, int B, int T) {
     p.nodepath = reinterpret_cast<int32_t *>(base + L.nodepath);
     p.path = reinterpret_cast<int32_t *>(base + L.path);
     p.path_len = reinterpret_cast<int32_t *>(base + L.path_len);
+    p.coef = reinterpret_cast<float *>(base + L.coef);
     return p;
 }
 

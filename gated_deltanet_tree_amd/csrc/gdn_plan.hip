@@ -13,6 +13,7 @@ namespace gdn {
 namespace {
 
 constexpr int kPlanThreads = GDN_MAX_NODES;  // one thread per node
+constexpr int kPlanDupPer = 2;               // other sequences checked per thread from registers
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params P) {
     __shared__ int s_par[kPlanThreads];
@@ -35,8 +36,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params P) {
     }
     if (b >= P.B) return;
 
-    // ---- node range ---------------------------------------------------------
+    // ---- node range (the other sequences' ranges and slots are fetched in the
+    // same round trip, for the duplicate-slot check) --------------------------
     const int lo = P.cu_nodes[b], hi = P.cu_nodes[b + 1];
+    int o_lo[kPlanDupPer], o_hi[kPlanDupPer], o_slot[kPlanDupPer];
+#pragma unroll
+    for (int u = 0; u < kPlanDupPer; ++u) {
+        const int o = t + u * kPlanThreads;
+        o_lo[u] = o < P.B ? P.cu_nodes[o] : 0;
+        o_hi[u] = o < P.B ? P.cu_nodes[o + 1] : 0;
+        o_slot[u] = o < P.B ? P.slot_idx[o] : -1;
+    }
     int status = GDN_SEQ_OK;
     // in_bounds: the range lies inside [0, T] (its outputs can be NaN-filled);
     // range_ok: additionally no longer than max_nodes
@@ -52,11 +62,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params P) {
             status = GDN_SEQ_BAD_SLOT;
         } else {
             int dup = 0;
-            for (int o = t; o < P.B; o += kPlanThreads) {
-                if (o == b) continue;
+#pragma unroll
+            for (int u = 0; u < kPlanDupPer; ++u) {
+                const int o = t + u * kPlanThreads;
+                const int lo2 = o_lo[u], hi2 = o_hi[u];
+                const bool ok2 = 0 <= lo2 && lo2 <= hi2 && hi2 <= P.T && hi2 - lo2 <= P.max_nodes;
+                if (o < P.B && o != b && ok2 && hi2 > lo2 && o_slot[u] == slot) dup = 1;
+            }
+            for (int o = t + kPlanDupPer * kPlanThreads; o < P.B; o += kPlanThreads) {  // very large batches
                 const int lo2 = P.cu_nodes[o], hi2 = P.cu_nodes[o + 1];
                 const bool ok2 = 0 <= lo2 && lo2 <= hi2 && hi2 <= P.T && hi2 - lo2 <= P.max_nodes;
-                if (ok2 && hi2 > lo2 && P.slot_idx[o] == slot) dup = 1;
+                if (o != b && ok2 && hi2 > lo2 && P.slot_idx[o] == slot) dup = 1;
             }
             if (__syncthreads_or(dup)) status = GDN_SEQ_DUP_SLOT;
         }
@@ -133,26 +149,23 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params P) {
             }
             for (int s = depth; s < GDN_MAX_DEPTH; ++s) np[s] = -1;
         }
-        // stack height after each position = inclusive prefix sum of (push - pop)
-        s_scan[t] = 0;
+        // stack height after each position: pushes minus pops up to it
+        __syncthreads();  // every thread is done reading s_off / s_later above
+        s_scan[t] = t < n ? pos : -1;
+        s_off[t] = t < n ? act : 0;
+        if (t == 0) s_later[0] = 0;
         __syncthreads();
-        if (t < n) s_scan[pos] = ((act & GDN_ACT_PUSH) ? 1 : 0) - ((act & 3) == GDN_ACT_POP ? 1 : 0);
-        __syncthreads();
-        for (int step = 1; step < kPlanThreads; step <<= 1) {
-            const int add = t >= step ? s_scan[t - step] : 0;
-            __syncthreads();
-            s_scan[t] += add;
-            __syncthreads();
+        if (t < n) {
+            int height = 0;
+            for (int s2 = 0; s2 < n; ++s2) {
+                if (s_scan[s2] > pos) continue;
+                const int a2 = s_off[s2];
+                height += ((a2 & GDN_ACT_PUSH) ? 1 : 0) - ((a2 & 3) == GDN_ACT_POP ? 1 : 0);
+            }
+            atomicMax(&s_later[0], height);
         }
-        int m = t < n ? s_scan[t] : 0;
-        // block max through the same buffer
-        s_off[t] = m;
         __syncthreads();
-        for (int step = kPlanThreads / 2; step > 0; step >>= 1) {
-            if (t < step && s_off[t + step] > s_off[t]) s_off[t] = s_off[t + step];
-            __syncthreads();
-        }
-        max_stack = s_off[0];
+        max_stack = s_later[0];
     } else if (in_bounds) {
         // rejected (or empty) sequence: defined metadata
         for (int i = t; i < hi - lo; i += kPlanThreads) {
@@ -166,8 +179,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params P) {
         W.seq_status[b] = status;
         W.seq_info[b * kSeqInfoInts + 0] = in_bounds ? lo : 0;
         W.seq_info[b * kSeqInfoInts + 1] = in_bounds ? hi - lo : 0;
-        W.seq_info[b * kSeqInfoInts + 2] = max_stack;
-        W.seq_info[b * kSeqInfoInts + 3] = 0;
+        W.seq_info[b * kSeqInfoInts + 2] = status;
+        W.seq_info[b * kSeqInfoInts + 3] = (status == GDN_SEQ_OK && n > 0) ? P.slot_idx[b] : 0;
+        W.seq_info[b * kSeqInfoInts + 4] = max_stack;
+        for (int r = 5; r < kSeqInfoInts; ++r) W.seq_info[b * kSeqInfoInts + r] = 0;
         W.path_len[b] = 0;
     }
     if (t < GDN_MAX_DEPTH) W.path[b * GDN_MAX_DEPTH + t] = -1;

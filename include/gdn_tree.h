@@ -167,9 +167,11 @@ int gdn_tree_persist(const gdn_dims *dims, const void *k, const void *v, const f
  * final_state are given, the state after the first final_len[b] nodes into
  * final_state [B][H_v][D_v][D_k] (final_len[b] = 0 writes the committed state;
  * a value outside [0, n_b] writes nothing).  state_cache is only read and
- * final_state must not overlap it.  `ws` may be NULL; if given (sized by
- * gdn_workspace_bytes for the same dims) the per-sequence verdicts are
- * written there for gdn_tree_status.
+ * final_state must not overlap it.  `ws` (sized by gdn_workspace_bytes for
+ * the same dims) receives the per-sequence verdicts for gdn_tree_status; it
+ * is required when outputs are requested for bf16 inputs with head_dim 64 or
+ * 128 and chains of at most GDN_MAX_DEPTH nodes (the kernels keep per-node
+ * coefficients there), and may be NULL otherwise.
  */
 int gdn_chain_verify(const gdn_dims *dims, const int32_t *cu_nodes, const void *q, const void *k,
                      const void *v, const float *a, const float *b, const float *state_cache,

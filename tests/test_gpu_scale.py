@@ -43,7 +43,7 @@ def test_long_chain_outputs_and_final_states(d_):
     out = torch.full((T, hv, d_), float("nan"), device="cuda")
     fin = torch.full((len(lens), hv, d_, d_), float("nan"), device="cuda")
     G.gdn_chain_verify(dims, to_dev(cu), dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], to_dev(S0),
-                       to_dev(slots), out, to_dev(fl), fin)
+                       to_dev(slots), out, to_dev(fl), fin, ws=G.new_workspace(dims))
     torch.cuda.synchronize()
     got, gfin = out.cpu().numpy(), fin.cpu().numpy()
     for s, L in enumerate(lens):
