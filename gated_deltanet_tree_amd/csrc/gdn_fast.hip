@@ -494,6 +494,311 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
     }
 }
 
+// ===========================================================================
+// Verify for trees of at most 32 nodes: one workgroup per (sequence, key
+// head), D/32 waves.  The workgroup computes the coefficients of its value
+// heads once (Gram entries shared through the key head) while the first
+// head's state is in flight, then walks its value heads with the next head's
+// state already loading into registers while the current head computes on
+// the matrix cores; the head loop has no barrier.  Same algebra as the
+// two-kernel path (coef_kernel + verify_kernel).
+// ===========================================================================
+constexpr int kGroupMaxHeads = 4;  // value heads per key head this kernel takes
+
+// LDS row strides padded so that lanes walking consecutive rows hit distinct banks.
+template <int D>
+struct GPad {
+    static constexpr int KQ = D + 8;       // bf16 per key/query row
+    static constexpr int PS = kPath + 1;   // per-node path tables
+    static constexpr int MT = kTile + 1;   // output-operator rows
+};
+
+template <int D>
+struct GTab {
+    uint16_t *kq;     // [2][32][KQ] keys / queries (bf16)
+    uint16_t *v;      // [32][grp][D] values of the group's heads (bf16), node-major as in memory
+    float4 *gab;      // [grp][32] gamma, alpha, b
+    float *mt;        // [grp][32][MT] dense output operator
+    float *coefL;     // [grp][32][PS]
+    float *gk, *gq;   // [32][PS] path-indexed Gram entries
+    int *anc;         // [32][PS]
+    float *a, *b;     // [grp][32]
+    int *depth;       // [32]
+    uint32_t *amask;  // [32] ancestors of node i within the block (bit j)
+};
+
+template <int D>
+__host__ __device__ inline size_t gtab_bytes(int grp) {
+    using Q = GPad<D>;
+    return (size_t)2 * kTile * Q::KQ * 2 + (size_t)kTile * grp * D * 2 + (size_t)grp * kTile * 16 +
+           (size_t)grp * kTile * Q::MT * 4 + (size_t)grp * kTile * Q::PS * 4 + 3 * kTile * Q::PS * 4 +
+           2 * (size_t)grp * kTile * 4 + 2 * kTile * 4;
+}
+
+template <int D>
+__device__ inline GTab<D> gtab_carve(char *base, int grp) {
+    using Q = GPad<D>;
+    GTab<D> L;
+    L.kq = reinterpret_cast<uint16_t *>(base);     base += (size_t)2 * kTile * Q::KQ * 2;
+    L.v = reinterpret_cast<uint16_t *>(base);      base += (size_t)kTile * grp * D * 2;
+    L.gab = reinterpret_cast<float4 *>(base);      base += (size_t)grp * kTile * 16;
+    L.mt = reinterpret_cast<float *>(base);        base += (size_t)grp * kTile * Q::MT * 4;
+    L.coefL = reinterpret_cast<float *>(base);     base += (size_t)grp * kTile * Q::PS * 4;
+    L.gk = reinterpret_cast<float *>(base);        base += kTile * Q::PS * 4;
+    L.gq = reinterpret_cast<float *>(base);        base += kTile * Q::PS * 4;
+    L.anc = reinterpret_cast<int *>(base);         base += kTile * Q::PS * 4;
+    L.a = reinterpret_cast<float *>(base);         base += (size_t)grp * kTile * 4;
+    L.b = reinterpret_cast<float *>(base);         base += (size_t)grp * kTile * 4;
+    L.depth = reinterpret_cast<int *>(base);       base += kTile * 4;
+    L.amask = reinterpret_cast<uint32_t *>(base);
+    return L;
+}
+
+// Loads lane's state fragments: uniform head base + one 32-bit lane offset, so
+// the 2*KS loads share a single address register.
+template <int D>
+__device__ __forceinline__ void load_state_frags(const float *head, unsigned lane_off, float (&sf)[VG<D>::KS][8]) {
+    const float *p = head + lane_off;
+#pragma unroll
+    for (int s = 0; s < VG<D>::KS; ++s) {
+        const float4 x0 = *reinterpret_cast<const float4 *>(p + 16 * s);
+        const float4 x1 = *reinterpret_cast<const float4 *>(p + 16 * s + 4);
+        sf[s][0] = x0.x; sf[s][1] = x0.y; sf[s][2] = x0.z; sf[s][3] = x0.w;
+        sf[s][4] = x1.x; sf[s][5] = x1.y; sf[s][6] = x1.z; sf[s][7] = x1.w;
+    }
+}
+
+template <int D, bool CHAIN, int GRP>
+__global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2))) void verify_group_kernel(
+    Params P) {
+    extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+    constexpr int KS = VG<D>::KS, NT = VG<D>::THREADS;
+    const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, hf = lane / 32, l32 = lane % 32;
+    const int row = w * 32 + l32;
+    constexpr int grp = GRP;
+    const int b = blockIdx.x / P.Hk, g = blockIdx.x % P.Hk;
+    const int h0 = g * grp;
+    const SeqView sv = seq_view<CHAIN>(P, b);
+    if (!CHAIN && !ws_planned(P)) return;
+    if (CHAIN && P.has_ws && g == 0 && tid == 0) {
+        if (b == 0) {
+            P.ws.header[0] = kMagic;
+            P.ws.header[1] = P.B;
+            P.ws.header[2] = P.T;
+        }
+        P.ws.seq_status[b] = sv.status;
+    }
+    if (!P.out) return;
+    const int lo = sv.lo, n = sv.n;
+    // out[node][h0 + hh][row]: uniform base per (node, head) + this lane's offset
+    const unsigned out_lane = (unsigned)(4 * hf * P.Hv * D + row);
+    if (sv.status != GDN_SEQ_OK) {
+        for (int t = tid; t < n * grp * D; t += NT)
+            P.out[((size_t)(lo + t / (grp * D)) * P.Hv + h0) * D + t % (grp * D)] = qnan_f();
+        return;
+    }
+    if (n == 0) return;
+    using Q = GPad<D>;
+    const GTab<D> L = gtab_carve<D>(lds_raw, grp);
+    const uint16_t *kb = static_cast<const uint16_t *>(P.k) + ((size_t)lo * P.Hk + g) * D;
+    const uint16_t *qb = static_cast<const uint16_t *>(P.q) + ((size_t)lo * P.Hk + g) * D;
+    const size_t kq_stride = (size_t)P.Hk * D;
+    const float *s0 = P.state_in + ((size_t)sv.slot * P.Hv + h0) * D * D;
+    const unsigned s_lane = (unsigned)(row * D + 8 * hf);
+
+    // ---- one round trip: keys/queries, all heads' values, tree, gates, then the first two
+    // heads' states (issued last: the tables below wait only for what was issued before them)
+    constexpr int KQ_PER = (2 * kTile * D / 8 + NT - 1) / NT;
+    uint4 kqv[KQ_PER];
+#pragma unroll
+    for (int u = 0; u < KQ_PER; ++u) {
+        const int idx = tid + u * NT;
+        const int which = idx / (kTile * (D / 8)), rem = idx % (kTile * (D / 8));
+        const int i = rem / (D / 8), c8 = rem % (D / 8);
+        kqv[u] = (which < 2 && i < n)
+                     ? *reinterpret_cast<const uint4 *>((which ? qb : kb) + (size_t)i * kq_stride + 8 * c8)
+                     : make_uint4(0, 0, 0, 0);
+    }
+    // values: node i's group heads are contiguous (grp*D bf16); kGroupMaxHeads*32*D/8/NT chunks at most
+    const uint16_t *vg = static_cast<const uint16_t *>(P.v) + ((size_t)lo * P.Hv + h0) * D;
+    const int vchunks = grp * D / 8;  // 16-byte chunks per node
+    constexpr int V_PER = (kGroupMaxHeads * kTile * D / 8 + NT - 1) / NT;
+    static_assert(kGroupMaxHeads * kTile <= NT, "one thread per (head, node) gate");
+    uint4 vv[V_PER];
+#pragma unroll
+    for (int u = 0; u < V_PER; ++u) {
+        const int idx = tid + u * NT;
+        const int i = idx / vchunks, c = idx % vchunks;
+        vv[u] = i < n ? *reinterpret_cast<const uint4 *>(vg + (size_t)i * P.Hv * D + 8 * c) : make_uint4(0, 0, 0, 0);
+    }
+    int an[kPath], d = 0;  // raw path entries (-1 past the depth), clamped once the states are issued
+    if (tid < n) {
+#pragma unroll
+        for (int e = 0; e < kPath; ++e)
+            an[e] = CHAIN ? (e <= tid ? e : -1) : P.ws.nodepath[(size_t)(lo + tid) * GDN_MAX_DEPTH + e];
+        d = CHAIN ? tid + 1 : P.ws.depth[lo + tid];
+    }
+    float ga = 0.0f, gb = 0.0f;  // gates of (head tid / n, node tid % n); grp * n <= NT
+    if (tid < grp * n) {
+        const size_t at = (size_t)(lo + tid % n) * P.Hv + h0 + tid / n;
+        ga = P.a[at];
+        gb = P.b[at];
+    }
+    float sA[KS][8], sB[KS][8];
+    load_state_frags<D>(s0, s_lane, sA);
+    if (grp > 1) load_state_frags<D>(s0 + (size_t)D * D, s_lane, sB);
+    if (tid < n) {
+        uint32_t m = 0u;
+#pragma unroll
+        for (int e = 0; e < kPath; ++e) {
+            const int ae = an[e] < 0 ? 0 : an[e];
+            L.anc[tid * Q::PS + e] = ae;
+            if (e < d) m |= 1u << (ae & 31);
+        }
+        L.depth[tid] = d;
+        L.amask[tid] = m;
+    }
+    if (tid < grp * n) {
+        L.a[(tid / n) * kTile + tid % n] = ga;
+        L.b[(tid / n) * kTile + tid % n] = gb;
+    }
+#pragma unroll
+    for (int u = 0; u < KQ_PER; ++u) {
+        const int idx = tid + u * NT;
+        if (idx < 2 * kTile * (D / 8))
+            *reinterpret_cast<uint4 *>(L.kq + (idx / (D / 8)) * Q::KQ + 8 * (idx % (D / 8))) = kqv[u];
+    }
+#pragma unroll
+    for (int u = 0; u < V_PER; ++u) {
+        const int idx = tid + u * NT;
+        if (idx < kTile * vchunks) reinterpret_cast<uint4 *>(L.v)[idx] = vv[u];
+    }
+    for (int idx = tid; idx < grp * kTile * Q::MT; idx += NT) L.mt[idx] = 0.0f;
+    __syncthreads();
+
+    // ---- Gram entries of the block (one wave)
+    if (w == 0) {
+        f32x16 gkk = {}, gkq = {};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const bf16x8 A = frag_of(L.kq + l32 * Q::KQ, s, hf);
+            const bf16x8 Bq = frag_of(L.kq + (kTile + l32) * Q::KQ, s, hf);
+            gkk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, A, gkk, 0, 0, 0);
+            gkq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bq, gkq, 0, 0, 0);
+        }
+        if (l32 < n) {  // accumulator r: (candidate ancestor il, node l32)
+            const uint32_t mask = L.amask[l32];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int il = 8 * (r / 4) + 4 * hf + (r % 4);
+                if ((mask >> il) & 1u) {
+                    const int e = L.depth[il] - 1;
+                    L.gk[l32 * Q::PS + e] = gkk[r];
+                    L.gq[l32 * Q::PS + e] = gkq[r];
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- per (value head, node): ratios, coefficients, output weights
+    const bool act = tid < grp * n;
+    const int hh_t = act ? tid / n : 0, i_t = act ? tid % n : 0;
+    float mrow[kPath];
+    int an_t[kPath];
+    int d_t = 0;
+    if (act) {
+        d_t = L.depth[i_t];
+        const float bi = L.b[hh_t * kTile + i_t];
+        float av[kPath];
+#pragma unroll
+        for (int e = 0; e < kPath; ++e) an_t[e] = L.anc[i_t * Q::PS + e];
+#pragma unroll
+        for (int e = 0; e < kPath; ++e) av[e] = e < d_t ? L.a[hh_t * kTile + an_t[e]] : 1.0f;
+        float r = 1.0f;
+#pragma unroll
+        for (int e = kPath - 1; e >= 0; --e) {
+            const bool on = e < d_t - 1;
+            L.coefL[(hh_t * kTile + i_t) * Q::PS + e] = on ? bi * r * L.gk[i_t * Q::PS + e] : 0.0f;
+            mrow[e] = on ? r * L.gq[i_t * Q::PS + e] : (e == d_t - 1 ? L.gq[i_t * Q::PS + e] : 0.0f);
+            r *= av[e];
+        }
+        L.gab[hh_t * kTile + i_t] = make_float4(r, bi * r, bi, 0.0f);
+    }
+    __syncthreads();
+    if (act) {
+        float y[kPath];
+#pragma unroll
+        for (int e = kPath - 1; e >= 0; --e) {
+            float acc = mrow[e];
+            // deepest terms first: y_{e+1}, the last one known, enters last
+#pragma unroll
+            for (int f = kPath - 1; f > e; --f)
+                acc = fmaf(-y[f], L.coefL[(hh_t * kTile + an_t[f]) * Q::PS + e], acc);
+            y[e] = e < d_t ? acc : 0.0f;
+        }
+        float *mrow_out = L.mt + (hh_t * kTile + i_t) * Q::MT;
+#pragma unroll
+        for (int e = 0; e < kPath; ++e)
+            if (e < d_t) mrow_out[an_t[e]] = y[e];
+    }
+    __syncthreads();
+
+    // ---- value heads: the next head's state loads while this one computes
+    auto head = [&](const float (&st)[KS][8], int hh) {
+        f32x16 ax = {}, ay = {};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {  // the state as bf16 hi + lo, split one k-step at a time
+            bf16x8 shi, slo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const __bf16 hb = static_cast<__bf16>(st[s][e]);
+                shi[e] = hb;
+                slo[e] = static_cast<__bf16>(st[s][e] - static_cast<float>(hb));
+            }
+            const bf16x8 Ak = frag_of(L.kq + l32 * Q::KQ, s, hf);
+            const bf16x8 Aq = frag_of(L.kq + (kTile + l32) * Q::KQ, s, hf);
+            ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, shi, ax, 0, 0, 0);
+            ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, slo, ax, 0, 0, 0);
+            ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, shi, ay, 0, 0, 0);
+            ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, slo, ay, 0, 0, 0);
+        }
+        const float4 *gab = L.gab + hh * kTile;
+        const uint16_t *vh = L.v + hh * D + row;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = 8 * (r / 4) + 4 * hf + (r % 4);
+            const float4 q4 = gab[min(i, n - 1)];
+            const float vi = bf2f(vh[i * grp * D]);
+            ax[r] = i < n ? fmaf(-q4.y, ax[r], q4.z * vi) : 0.0f;  // r = b v - alpha x
+            ay[r] = i < n ? q4.x * ay[r] : 0.0f;                   // gamma y
+        }
+        // O = gamma y + MT R: k-step s pairs the nodes in accumulator slot s of the two half-waves
+        const float *mrow2 = L.mt + (hh * kTile + l32) * Q::MT;
+#pragma unroll
+        for (int s = 0; s < 16; ++s)
+            ay = __builtin_amdgcn_mfma_f32_32x32x2f32(mrow2[8 * (s / 4) + 4 * hf + (s % 4)], ax[s], ay, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int ir = 8 * (r / 4) + (r % 4);  // node of half-wave 0; half-wave 1 adds 4
+            if (ir + 4 * hf < n) {
+                float *ob = P.out + ((size_t)(lo + ir) * P.Hv + h0 + hh) * D;
+                ob[out_lane] = ay[r];
+            }
+        }
+    };
+    // two heads in flight: a register set is refilled as soon as its head is done
+#pragma unroll
+    for (int hh = 0; hh < grp; hh += 2) {
+        head(sA, hh);
+        if (hh + 2 < grp) load_state_frags<D>(s0 + (size_t)(hh + 2) * D * D, s_lane, sA);
+        if (hh + 1 < grp) {
+            head(sB, hh + 1);
+            if (hh + 3 < grp) load_state_frags<D>(s0 + (size_t)(hh + 3) * D * D, s_lane, sB);
+        }
+    }
+}
+
 template <int D>
 struct RG {
     static constexpr int LPR = 4;             // lanes per state row
@@ -732,8 +1037,22 @@ hipError_t launch_with_lds(K kernel, dim3 grid, dim3 block, size_t lds, hipStrea
 
 template <int D>
 hipError_t launch_verify_d(const Params &p, bool chain, hipStream_t s) {
-    const int cap = chain ? kPath : p.max_nodes;
     const int grp = p.Hv / p.Hk;
+    if ((chain || p.max_nodes <= kTile) && grp <= kGroupMaxHeads) {
+        const dim3 grid(p.B * p.Hk), block(VG<D>::THREADS);
+        switch (grp) {
+#define GDN_GROUP_CASE(G)                                                                                    \
+    case G:                                                                                                  \
+        return chain ? launch_with_lds(verify_group_kernel<D, true, G>, grid, block, gtab_bytes<D>(G), s, p) \
+                     : launch_with_lds(verify_group_kernel<D, false, G>, grid, block, gtab_bytes<D>(G), s, p);
+            GDN_GROUP_CASE(1)
+            GDN_GROUP_CASE(2)
+            GDN_GROUP_CASE(3)
+            GDN_GROUP_CASE(4)
+#undef GDN_GROUP_CASE
+        }
+    }
+    const int cap = chain ? kPath : p.max_nodes;
     // LDS for the most value heads a pass can take (a one-node sequence)
     const size_t clds = ctab_bytes(cap, grp, std::min(grp, kCoefMaxHeadsPerPass));
     hipError_t e = chain ? launch_with_lds(coef_kernel<D, true>, dim3(p.B * p.Hk), dim3(kCoefThreads), clds, s, p)
