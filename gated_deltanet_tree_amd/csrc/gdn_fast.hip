@@ -521,10 +521,9 @@ struct GTab {
     float *mt;        // [grp][32][MT] dense output operator
     float *coefL;     // [grp][32][PS]
     float *gk, *gq;   // [32][PS] path-indexed Gram entries
-    int *anc;         // [32][PS]
+    int *anc;         // [32][PS] root-to-node path, -1 past the depth
     float *a, *b;     // [grp][32]
     int *depth;       // [32]
-    uint32_t *amask;  // [32] ancestors of node i within the block (bit j)
 };
 
 template <int D>
@@ -532,7 +531,7 @@ __host__ __device__ inline size_t gtab_bytes(int grp) {
     using Q = GPad<D>;
     return (size_t)2 * kTile * Q::KQ * 2 + (size_t)kTile * grp * D * 2 + (size_t)grp * kTile * 16 +
            (size_t)grp * kTile * Q::MT * 4 + (size_t)grp * kTile * Q::PS * 4 + 3 * kTile * Q::PS * 4 +
-           2 * (size_t)grp * kTile * 4 + 2 * kTile * 4;
+           2 * (size_t)grp * kTile * 4 + kTile * 4;
 }
 
 template <int D>
@@ -549,8 +548,7 @@ __device__ inline GTab<D> gtab_carve(char *base, int grp) {
     L.anc = reinterpret_cast<int *>(base);         base += kTile * Q::PS * 4;
     L.a = reinterpret_cast<float *>(base);         base += (size_t)grp * kTile * 4;
     L.b = reinterpret_cast<float *>(base);         base += (size_t)grp * kTile * 4;
-    L.depth = reinterpret_cast<int *>(base);       base += kTile * 4;
-    L.amask = reinterpret_cast<uint32_t *>(base);
+    L.depth = reinterpret_cast<int *>(base);
     return L;
 }
 
@@ -606,8 +604,7 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
     const float *s0 = P.state_in + ((size_t)sv.slot * P.Hv + h0) * D * D;
     const unsigned s_lane = (unsigned)(row * D + 8 * hf);
 
-    // ---- one round trip: keys/queries, all heads' values, tree, gates, then the first two
-    // heads' states (issued last: the tables below wait only for what was issued before them)
+    // ---- one round trip: keys/queries, all heads' values, tree, gates
     constexpr int KQ_PER = (2 * kTile * D / 8 + NT - 1) / NT;
     uint4 kqv[KQ_PER];
 #pragma unroll
@@ -631,32 +628,24 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         const int i = idx / vchunks, c = idx % vchunks;
         vv[u] = i < n ? *reinterpret_cast<const uint4 *>(vg + (size_t)i * P.Hv * D + 8 * c) : make_uint4(0, 0, 0, 0);
     }
-    int an[kPath], d = 0;  // raw path entries (-1 past the depth), clamped once the states are issued
-    if (tid < n) {
-#pragma unroll
-        for (int e = 0; e < kPath; ++e)
-            an[e] = CHAIN ? (e <= tid ? e : -1) : P.ws.nodepath[(size_t)(lo + tid) * GDN_MAX_DEPTH + e];
-        d = CHAIN ? tid + 1 : P.ws.depth[lo + tid];
-    }
     float ga = 0.0f, gb = 0.0f;  // gates of (head tid / n, node tid % n); grp * n <= NT
     if (tid < grp * n) {
         const size_t at = (size_t)(lo + tid % n) * P.Hv + h0 + tid / n;
         ga = P.a[at];
         gb = P.b[at];
     }
-    float sA[KS][8], sB[KS][8];
-    load_state_frags<D>(s0, s_lane, sA);
-    if (grp > 1) load_state_frags<D>(s0 + (size_t)D * D, s_lane, sB);
+    // the path rows last: whatever waits on them waits on the loads above as well
+    int an[kPath], d = 0;  // path entries, -1 past the depth
     if (tid < n) {
-        uint32_t m = 0u;
+        d = CHAIN ? tid + 1 : P.ws.depth[lo + tid];
 #pragma unroll
-        for (int e = 0; e < kPath; ++e) {
-            const int ae = an[e] < 0 ? 0 : an[e];
-            L.anc[tid * Q::PS + e] = ae;
-            if (e < d) m |= 1u << (ae & 31);
-        }
+        for (int e = 0; e < kPath; ++e)
+            an[e] = CHAIN ? (e <= tid ? e : -1) : P.ws.nodepath[(size_t)(lo + tid) * GDN_MAX_DEPTH + e];
+    }
+    if (tid < n) {  // stored as loaded: no arithmetic on them before the states are out
+#pragma unroll
+        for (int e = 0; e < kPath; ++e) L.anc[tid * Q::PS + e] = an[e];
         L.depth[tid] = d;
-        L.amask[tid] = m;
     }
     if (tid < grp * n) {
         L.a[(tid / n) * kTile + tid % n] = ga;
@@ -674,6 +663,11 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         if (idx < kTile * vchunks) reinterpret_cast<uint4 *>(L.v)[idx] = vv[u];
     }
     for (int idx = tid; idx < grp * kTile * Q::MT; idx += NT) L.mt[idx] = 0.0f;
+    // the states go out only now: issued together with the small loads above they would queue
+    // ahead of them and hold back the coefficients, which gate every output
+    float sA[KS][8], sB[KS][8];
+    load_state_frags<D>(s0, s_lane, sA);
+    if (grp > 1) load_state_frags<D>(s0 + (size_t)D * D, s_lane, sB);
     __syncthreads();
 
     // ---- Gram entries of the block (one wave)
@@ -687,7 +681,11 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
             gkq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bq, gkq, 0, 0, 0);
         }
         if (l32 < n) {  // accumulator r: (candidate ancestor il, node l32)
-            const uint32_t mask = L.amask[l32];
+            const int dl = L.depth[l32];
+            uint32_t mask = 0u;  // ancestors of node l32 within the block
+#pragma unroll
+            for (int e = 0; e < kPath; ++e)
+                if (e < dl) mask |= 1u << (L.anc[l32 * Q::PS + e] & 31);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int il = 8 * (r / 4) + 4 * hf + (r % 4);
@@ -712,7 +710,7 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         const float bi = L.b[hh_t * kTile + i_t];
         float av[kPath];
 #pragma unroll
-        for (int e = 0; e < kPath; ++e) an_t[e] = L.anc[i_t * Q::PS + e];
+        for (int e = 0; e < kPath; ++e) an_t[e] = max(L.anc[i_t * Q::PS + e], 0);
 #pragma unroll
         for (int e = 0; e < kPath; ++e) av[e] = e < d_t ? L.a[hh_t * kTile + an_t[e]] : 1.0f;
         float r = 1.0f;
@@ -744,9 +742,10 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
     }
     __syncthreads();
 
-    // ---- value heads: the next head's state loads while this one computes
-    auto head = [&](const float (&st)[KS][8], int hh) {
-        f32x16 ax = {}, ay = {};
+    // ---- value heads: X, Y from the state and K/Q; outputs from X, Y and the coefficients
+    auto xy = [&](const float (&st)[KS][8], f32x16 &ax, f32x16 &ay) {
+        ax = f32x16{};
+        ay = f32x16{};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {  // the state as bf16 hi + lo, split one k-step at a time
             bf16x8 shi, slo;
@@ -763,6 +762,8 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
             ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, shi, ay, 0, 0, 0);
             ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, slo, ay, 0, 0, 0);
         }
+    };
+    auto finish = [&](f32x16 ax, f32x16 ay, int hh) {
         const float4 *gab = L.gab + hh * kTile;
         const uint16_t *vh = L.v + hh * D + row;
 #pragma unroll
@@ -787,15 +788,26 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
             }
         }
     };
-    // two heads in flight: a register set is refilled as soon as its head is done
-#pragma unroll
-    for (int hh = 0; hh < grp; hh += 2) {
-        head(sA, hh);
-        if (hh + 2 < grp) load_state_frags<D>(s0 + (size_t)(hh + 2) * D * D, s_lane, sA);
-        if (hh + 1 < grp) {
-            head(sB, hh + 1);
-            if (hh + 3 < grp) load_state_frags<D>(s0 + (size_t)(hh + 3) * D * D, s_lane, sB);
-        }
+    // each register set is refilled as soon as its products are taken
+    f32x16 x0, y0;
+    xy(sA, x0, y0);
+    if (grp > 2) load_state_frags<D>(s0 + (size_t)2 * D * D, s_lane, sA);
+    finish(x0, y0, 0);
+    if (grp > 1) {
+        f32x16 x1, y1;
+        xy(sB, x1, y1);
+        if (grp > 3) load_state_frags<D>(s0 + (size_t)3 * D * D, s_lane, sB);
+        finish(x1, y1, 1);
+    }
+    if (grp > 2) {
+        f32x16 x2, y2;
+        xy(sA, x2, y2);
+        finish(x2, y2, 2);
+    }
+    if (grp > 3) {
+        f32x16 x3, y3;
+        xy(sB, x3, y3);
+        finish(x3, y3, 3);
     }
 }
 
@@ -1024,6 +1036,320 @@ __global__ __launch_bounds__(RG<D>::THREADS) void replay_kernel(Params P) {
     }
 }
 
+// ===========================================================================
+// Replay on the matrix cores: one workgroup per (sequence, key head), D/32
+// waves, wave w owning state rows [32w, 32w+32) of each value head of the
+// group.  With L path tokens (keys k_e, L <= 16):
+//   x_e   = S0 k_e                                   (X = S0 K^T, MFMA)
+//   c_p   = b_p v_p - alpha_p x_p - sum_{e<p} Lc[p][e] c_e   (per row, VALU)
+//   S_new = gamma_{L-1} S0 + sum_e w_e c_e k_e^T     (rank-L update, MFMA
+//                                                     accumulating onto the
+//                                                     scaled state in place)
+// with Lc[p][e] = b_p R(p,e) (k_e . k_p), R(p,e) = a_{e+1} ... a_p,
+// gamma_p = a_0 ... a_p, alpha_p = b_p gamma_p, w_e = R(L-1, e).
+// The lane's state registers follow the 32x32 accumulator layout of the
+// transposed tile (lane: one row; register r of tile t: column
+// 32t + 8(r/4) + 4*half + r%4), which is also a valid k-ordering of the B
+// operand of X, so the state is loaded once and updated in place.  The next
+// value head's state is in flight while the current one computes.
+// ===========================================================================
+template <int D>
+struct PTab {
+    uint16_t *k;      // [16][KP] path keys (bf16), rows >= L zero
+    uint16_t *kt;     // [D][KT] the same keys transposed
+    uint16_t *v;      // [16][grp][D] path values of the group's heads
+    float *gram;      // [16][17] k_e . k_p
+    float *coefL;     // [grp][16][17]
+    float4 *gaw;      // [grp][16] gamma, alpha, b, w
+    float *a, *b;     // [grp][16]
+    static constexpr int KP = D + 8;
+    static constexpr int KT = kPath + 8;
+};
+
+template <int D>
+__host__ __device__ inline size_t ptab_bytes(int grp) {
+    return (size_t)kPath * PTab<D>::KP * 2 + (size_t)D * PTab<D>::KT * 2 + (size_t)kPath * grp * D * 2 +
+           kPath * (kPath + 1) * 4 + (size_t)grp * kPath * (kPath + 1) * 4 + (size_t)grp * kPath * 16 +
+           2 * (size_t)grp * kPath * 4;
+}
+
+template <int D>
+__device__ inline PTab<D> ptab_carve(char *base, int grp) {
+    PTab<D> L;
+    L.gaw = reinterpret_cast<float4 *>(base);      base += (size_t)grp * kPath * 16;
+    L.k = reinterpret_cast<uint16_t *>(base);      base += (size_t)kPath * PTab<D>::KP * 2;
+    L.kt = reinterpret_cast<uint16_t *>(base);     base += (size_t)D * PTab<D>::KT * 2;
+    L.v = reinterpret_cast<uint16_t *>(base);      base += (size_t)kPath * grp * D * 2;
+    L.gram = reinterpret_cast<float *>(base);      base += kPath * (kPath + 1) * 4;
+    L.coefL = reinterpret_cast<float *>(base);     base += (size_t)grp * kPath * (kPath + 1) * 4;
+    L.a = reinterpret_cast<float *>(base);         base += (size_t)grp * kPath * 4;
+    L.b = reinterpret_cast<float *>(base);
+    return L;
+}
+
+// the lane's state tiles: S[t][r] = state[row][32t + 8(r/4) + 4*half + r%4]
+template <int D>
+__device__ __forceinline__ void load_state_tiles(const float *head, unsigned lane_off, f32x16 (&S)[D / 32]) {
+    const float *p = head + lane_off;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 x = *reinterpret_cast<const float4 *>(p + 32 * t + 8 * q);
+            S[t][4 * q + 0] = x.x; S[t][4 * q + 1] = x.y; S[t][4 * q + 2] = x.z; S[t][4 * q + 3] = x.w;
+        }
+}
+
+template <int D, bool CHAIN, int GRP>
+__global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2))) void replay_group_kernel(
+    Params P) {
+    extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+    constexpr int NT = VG<D>::THREADS, NTILE = D / 32;
+    constexpr int grp = GRP;
+    const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, hf = lane / 32, l32 = lane % 32;
+    const int row = w * 32 + l32;
+    const int b = blockIdx.x / P.Hk, g = blockIdx.x % P.Hk;
+    const int h0 = g * grp;
+
+    // ---- the path: local ids path[e] (root first), its length, source and destination
+    int lo, len, slot;
+    const int32_t *path = nullptr;  // null: a chain, path[e] = e
+    float *dst;
+    if (CHAIN) {
+        const int c0 = P.cu_nodes[b], c1 = P.cu_nodes[b + 1];
+        len = P.final_len[b];
+        slot = P.slot_idx[b];
+        if (!(0 <= c0 && c0 <= c1 && c1 <= P.T) || c1 - c0 > P.max_nodes) return;
+        if (len < 0 || len > c1 - c0 || len > kPath) return;
+        if (slot < 0 || slot >= P.num_slots) return;
+        lo = c0;
+        dst = P.final_state + (size_t)b * P.Hv * D * D;
+    } else {
+        if (!ws_planned(P)) return;
+        const int4 info = *reinterpret_cast<const int4 *>(P.ws.seq_info + b * kSeqInfoInts);
+        const int m = P.accepted[b];
+        if (info.z != GDN_SEQ_OK || info.y == 0) return;
+        if (m < -1 || m >= info.y) {
+            if (g == 0 && tid == 0) P.ws.seq_status[b] = GDN_SEQ_BAD_ACCEPT;
+            return;
+        }
+        if (m == -1) return;
+        lo = info.x;
+        slot = info.w;
+        path = P.ws.nodepath + (size_t)(lo + m) * GDN_MAX_DEPTH;
+        len = P.ws.depth[lo + m];
+        if (g == 0 && tid < GDN_MAX_DEPTH) {
+            P.ws.path[b * GDN_MAX_DEPTH + tid] = path[tid];
+            if (tid == 0) P.ws.path_len[b] = len;
+        }
+        dst = P.state_out + (size_t)slot * P.Hv * D * D;
+    }
+    len = uni(len);
+    const float *s0 = P.state_in + ((size_t)slot * P.Hv + h0) * D * D;
+    dst += (size_t)h0 * D * D;
+    const unsigned s_lane = (unsigned)(row * D + 4 * hf);
+
+    f32x16 SA[NTILE], SB[NTILE];
+    if (len == 0) {  // chain final state after zero tokens: the committed state
+#pragma unroll 1
+        for (int hh = 0; hh < grp; ++hh) {
+            load_state_tiles<D>(s0 + (size_t)hh * D * D, s_lane, SA);
+#pragma unroll
+            for (int t = 0; t < NTILE; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<float4 *>(dst + (size_t)hh * D * D + s_lane + 32 * t + 8 * q) =
+                        make_float4(SA[t][4 * q], SA[t][4 * q + 1], SA[t][4 * q + 2], SA[t][4 * q + 3]);
+        }
+        return;
+    }
+
+    // ---- tables: path keys (both ways), values and gates of the group's heads
+    const PTab<D> L = ptab_carve<D>(lds_raw, grp);
+    const uint16_t *kb = static_cast<const uint16_t *>(P.k) + ((size_t)lo * P.Hk + g) * D;
+    const uint16_t *vg = static_cast<const uint16_t *>(P.v) + ((size_t)lo * P.Hv + h0) * D;
+    constexpr int KC = kPath * D / 8;  // 16-byte chunks of the path keys
+    constexpr int K_PER = (KC + NT - 1) / NT;
+    constexpr int VC = kPath * grp * D / 8;
+    constexpr int V_PER = (VC + NT - 1) / NT;
+    uint4 kr[K_PER], vr[V_PER];
+#pragma unroll
+    for (int u = 0; u < K_PER; ++u) {
+        const int idx = tid + u * NT, e = idx / (D / 8), c8 = idx % (D / 8);
+        kr[u] = make_uint4(0, 0, 0, 0);
+        if (idx < KC && e < len) {
+            const int node = path ? path[e] : e;
+            kr[u] = *reinterpret_cast<const uint4 *>(kb + (size_t)node * P.Hk * D + 8 * c8);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < V_PER; ++u) {
+        const int idx = tid + u * NT, e = idx / (grp * D / 8), c = idx % (grp * D / 8);
+        vr[u] = make_uint4(0, 0, 0, 0);
+        if (idx < VC && e < len) {
+            const int node = path ? path[e] : e;
+            vr[u] = *reinterpret_cast<const uint4 *>(vg + (size_t)node * P.Hv * D + 8 * c);
+        }
+    }
+    float ga = 1.0f, gb = 0.0f;  // gates of (head tid / 16, path entry tid % 16)
+    if (tid < grp * kPath && tid % kPath < len) {
+        const int node = path ? path[tid % kPath] : tid % kPath;
+        const size_t at = (size_t)(lo + node) * P.Hv + h0 + tid / kPath;
+        ga = P.a[at];
+        gb = P.b[at];
+    }
+    // first two heads' states, issued after the tables so that waiting for the tables
+    // does not wait for them
+    load_state_tiles<D>(s0, s_lane, SA);
+    if (grp > 1) load_state_tiles<D>(s0 + (size_t)D * D, s_lane, SB);
+#pragma unroll
+    for (int u = 0; u < K_PER; ++u) {
+        const int idx = tid + u * NT, e = idx / (D / 8), c8 = idx % (D / 8);
+        if (idx < KC) {
+            *reinterpret_cast<uint4 *>(L.k + e * PTab<D>::KP + 8 * c8) = kr[u];
+            const uint16_t *hv = reinterpret_cast<const uint16_t *>(&kr[u]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) L.kt[(8 * c8 + i) * PTab<D>::KT + e] = hv[i];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < V_PER; ++u) {
+        const int idx = tid + u * NT;
+        if (idx < VC) reinterpret_cast<uint4 *>(L.v)[idx] = vr[u];
+    }
+    if (tid < grp * kPath) {
+        L.a[tid] = ga;
+        L.b[tid] = gb;
+    }
+    __syncthreads();
+
+    // ---- Gram entries of the path keys (one wave, one 32x32 tile, 16 rows used)
+    if (w == 0) {
+        f32x16 gk = {};
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            const bf16x8 A = l32 < kPath ? frag_of(L.k + l32 * PTab<D>::KP, s, hf) : zero_frag();
+            gk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, A, gk, 0, 0, 0);
+        }
+        if (l32 < kPath) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) L.gram[l32 * (kPath + 1) + 8 * (r / 4) + 4 * hf + (r % 4)] = gk[r];
+        }
+    }
+    __syncthreads();
+    // ---- per (head, path entry p): ratios, coefficients
+    if (tid < grp * kPath) {
+        const int hh = tid / kPath, p = tid % kPath;
+        const float *ah = L.a + hh * kPath;
+        const float bp = L.b[tid];
+        float r = 1.0f;  // R(p, e), e from p-1 down
+#pragma unroll
+        for (int e = kPath - 1; e >= 0; --e) {
+            float v = 0.0f;
+            if (e < p) {
+                r *= ah[e + 1];
+                v = p < len ? bp * r * L.gram[p * (kPath + 1) + e] : 0.0f;
+            }
+            L.coefL[(hh * kPath + p) * (kPath + 1) + e] = v;
+        }
+        float gm = 1.0f, wr = 1.0f;
+#pragma unroll
+        for (int t = 0; t < kPath; ++t) {
+            if (t <= p) gm *= ah[t];
+            if (t > p && t < len) wr *= ah[t];
+        }
+        L.gaw[tid] = make_float4(gm, bp * gm, bp, p < len ? wr : 0.0f);
+    }
+    __syncthreads();
+
+    // ---- value heads
+    auto head = [&](f32x16 (&S)[NTILE], int hh) {
+        // X = S0 K^T: k-step s takes tile s/2, registers 8(s%2) .. 8(s%2)+7 (columns
+        // 32t + 16u + 8(e/4) + 4*half + e%4), the keys read in the same column order
+        f32x16 ax = {};
+        const uint16_t *krow = L.k + l32 * PTab<D>::KP;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            const int t = s / 2, u = s % 2;
+            bf16x8 shi, slo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = S[t][8 * u + e];
+                const __bf16 hb = static_cast<__bf16>(x);
+                shi[e] = hb;
+                slo[e] = static_cast<__bf16>(x - static_cast<float>(hb));
+            }
+            bf16x8 A = zero_frag();
+            if (l32 < kPath) {
+                const uint2 k0 = *reinterpret_cast<const uint2 *>(krow + 32 * t + 16 * u + 4 * hf);
+                const uint2 k1 = *reinterpret_cast<const uint2 *>(krow + 32 * t + 16 * u + 8 + 4 * hf);
+                A = __builtin_bit_cast(bf16x8, make_uint4(k0.x, k0.y, k1.x, k1.y));
+            }
+            ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, shi, ax, 0, 0, 0);
+            ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, slo, ax, 0, 0, 0);
+        }
+        // x_e of this row: accumulator r < 8 holds e = 8(r/4) + 4*half + r%4, the other
+        // half-wave the rest
+        float x[kPath];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const float mine = ax[r];
+            const float other = __shfl_xor(mine, 32);
+            const int e_mine = 8 * (r / 4) + (r % 4);  // + 4*half
+            x[e_mine] = hf ? other : mine;
+            x[e_mine + 4] = hf ? mine : other;
+        }
+        // c_p = b_p v_p - alpha_p x_p - sum_{e<p} Lc[p][e] c_e
+        const float4 *gaw = L.gaw + hh * kPath;
+        const float *cl = L.coefL + hh * kPath * (kPath + 1);
+        const uint16_t *vh = L.v + hh * D + row;
+        float c[kPath];
+#pragma unroll
+        for (int p = 0; p < kPath; ++p) {
+            const float4 q4 = gaw[p];
+            float acc = fmaf(-q4.y, x[p], q4.z * bf2f(vh[p * grp * D]));
+#pragma unroll
+            for (int e = 0; e < p; ++e) acc = fmaf(-cl[p * (kPath + 1) + e], c[e], acc);
+            c[p] = p < len ? acc : 0.0f;
+        }
+        // B operand of the update: this half-wave's entries w_e c_e, e = 8*half .. 8*half+7
+        bf16x8 whi, wlo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int ee = e;  // entry 8*half + e
+            const float wc = (hf ? gaw[8 + ee].w * c[8 + ee] : gaw[ee].w * c[ee]);
+            const __bf16 hb = static_cast<__bf16>(wc);
+            whi[e] = hb;
+            wlo[e] = static_cast<__bf16>(wc - static_cast<float>(hb));
+        }
+        const float gl = gaw[len - 1].x;
+        float *dh = dst + (size_t)hh * D * D + s_lane;
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) {
+            // A: k_e[32t + l32] for e = 8*half .. 8*half+7 (transposed keys)
+            const bf16x8 A = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const uint4 *>(L.kt + (32 * t + l32) * PTab<D>::KT + 8 * hf));
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S[t][r] *= gl;
+            S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, whi, S[t], 0, 0, 0);
+            S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wlo, S[t], 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<float4 *>(dh + 32 * t + 8 * q) =
+                    make_float4(S[t][4 * q], S[t][4 * q + 1], S[t][4 * q + 2], S[t][4 * q + 3]);
+        }
+    };
+#pragma unroll
+    for (int hh = 0; hh < grp; hh += 2) {
+        head(SA, hh);
+        if (hh + 2 < grp) load_state_tiles<D>(s0 + (size_t)(hh + 2) * D * D, s_lane, SA);
+        if (hh + 1 < grp) {
+            head(SB, hh + 1);
+            if (hh + 3 < grp) load_state_tiles<D>(s0 + (size_t)(hh + 3) * D * D, s_lane, SB);
+        }
+    }
+}
+
 template <typename K>
 hipError_t launch_with_lds(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, const Params &p) {
     if (lds > 65536) {
@@ -1067,6 +1393,21 @@ hipError_t launch_verify_d(const Params &p, bool chain, hipStream_t s) {
 
 template <int D>
 hipError_t launch_replay_d(const Params &p, bool chain, hipStream_t s) {
+    const int grp = p.Hv / p.Hk;
+    if (grp <= kGroupMaxHeads) {
+        const dim3 grid(p.B * p.Hk), block(VG<D>::THREADS);
+        switch (grp) {
+#define GDN_GROUP_CASE(G)                                                                                     \
+    case G:                                                                                                   \
+        return chain ? launch_with_lds(replay_group_kernel<D, true, G>, grid, block, ptab_bytes<D>(G), s, p) \
+                     : launch_with_lds(replay_group_kernel<D, false, G>, grid, block, ptab_bytes<D>(G), s, p);
+            GDN_GROUP_CASE(1)
+            GDN_GROUP_CASE(2)
+            GDN_GROUP_CASE(3)
+            GDN_GROUP_CASE(4)
+#undef GDN_GROUP_CASE
+        }
+    }
     const dim3 grid(p.B * p.Hv * RG<D>::SLICES), block(RG<D>::THREADS);
     return chain ? launch_with_lds(replay_kernel<D, true>, grid, block, rtab_bytes(D), s, p)
                  : launch_with_lds(replay_kernel<D, false>, grid, block, rtab_bytes(D), s, p);

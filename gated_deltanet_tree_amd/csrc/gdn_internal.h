@@ -12,7 +12,7 @@ namespace gdn {
 
 constexpr int32_t kMagic = 0x67646e74;  // written by the plan into the workspace header
 constexpr int kHeaderInts = 16;          // magic, B, T, max_nodes, max_depth, stack slots, ...
-constexpr int kSeqInfoInts = 8;          // node offset, node count, verdict, slot, max stack, reserved x3
+constexpr int kSeqInfoInts = 8;          // node offset, node count, verdict, slot, reserved x4
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 

@@ -21,7 +21,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params P) {
     __shared__ int s_nchild[kPlanThreads];
     __shared__ int s_off[kPlanThreads];
     __shared__ int s_later[kPlanThreads];
-    __shared__ int s_scan[kPlanThreads];
 
     const int b = blockIdx.x;
     const int t = threadIdx.x;
@@ -39,6 +38,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params P) {
     // ---- node range (the other sequences' ranges and slots are fetched in the
     // same round trip, for the duplicate-slot check) --------------------------
     const int lo = P.cu_nodes[b], hi = P.cu_nodes[b + 1];
+    const int my_slot = P.slot_idx[b];
     int o_lo[kPlanDupPer], o_hi[kPlanDupPer], o_slot[kPlanDupPer];
 #pragma unroll
     for (int u = 0; u < kPlanDupPer; ++u) {
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params P) {
 
     // ---- slot: in range and not shared with another non-empty sequence ------
     if (status == GDN_SEQ_OK && n > 0) {
-        const int slot = P.slot_idx[b];
+        const int slot = my_slot;
         if (slot < 0 || slot >= P.num_slots) {
             status = GDN_SEQ_BAD_SLOT;
         } else {
@@ -87,7 +87,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params P) {
     }
 
     // ---- depth: every ancestor walk must reach a root within max_depth nodes -----
+    // anc[j] is the ancestor j steps up from this node (anc[0] = the node), j < depth
     int depth = 0;
+    int anc[GDN_MAX_DEPTH];
     if (status == GDN_SEQ_OK && n > 0) {
         s_par[t] = par;
         s_size[t] = 0;
@@ -96,20 +98,24 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params P) {
         bool deep = false;
         if (t < n) {
             int x = t;
-            while (x != -1 && depth < P.max_depth) {
-                ++depth;
-                x = s_par[x];
+#pragma unroll
+            for (int j = 0; j < GDN_MAX_DEPTH; ++j) {
+                anc[j] = x;
+                const bool step = x != -1 && depth < P.max_depth;
+                depth += step ? 1 : 0;
+                x = step ? s_par[x < 0 ? 0 : x] : x;
             }
             deep = x != -1;
         }
         if (__syncthreads_or(deep)) status = GDN_SEQ_CYCLE_OR_DEPTH;
     }
 
-    int max_stack = 0;
     if (status == GDN_SEQ_OK && n > 0) {
         // subtree sizes (each node counts itself into every ancestor) and child counts
         if (t < n) {
-            for (int x = t; x != -1; x = s_par[x]) atomicAdd(&s_size[x], 1);
+#pragma unroll
+            for (int j = 0; j < GDN_MAX_DEPTH; ++j)
+                if (j < depth) atomicAdd(&s_size[anc[j]], 1);
             if (par >= 0) atomicAdd(&s_nchild[par], 1);
         }
         __syncthreads();
@@ -117,11 +123,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params P) {
         if (t < n) {
             const int my = s_size[t];
             int off = 0, later = 0;
-            for (int s = 0; s < n; ++s) {
-                if (s == t || s_par[s] != par) continue;
-                const int ss = s_size[s];
-                if (ss < my || (ss == my && s < t)) off += ss;
-                else ++later;
+#pragma unroll 8
+            for (int s2 = 0; s2 < n; ++s2) {
+                const int ps = s_par[s2], ss = s_size[s2];
+                const bool sib = ps == par && s2 != t;
+                const bool before = ss < my || (ss == my && s2 < t);
+                off += (sib && before) ? ss : 0;
+                later += (sib && !before) ? 1 : 0;
             }
             s_off[t] = off;
             s_later[t] = later;
@@ -131,7 +139,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params P) {
         if (t < n) {
             // preorder position: every ancestor's offset plus one per non-root node on the path
             pos = depth - 1;
-            for (int x = t; x != -1; x = s_par[x]) pos += s_off[x];
+#pragma unroll
+            for (int j = 0; j < GDN_MAX_DEPTH; ++j)
+                if (j < depth) pos += s_off[anc[j]];
             if (par == -1) act = GDN_ACT_INIT;
             else if (s_off[t] == 0) act = GDN_ACT_CONTINUE;  // first child: follows its parent
             else if (s_later[t] == 0) act = GDN_ACT_POP;     // last child
@@ -141,31 +151,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params P) {
             W.order[lo + pos] = t;
             W.action[lo + pos] = act;
             W.depth[lo + t] = depth;
-            int32_t *np = W.nodepath + (size_t)(lo + t) * GDN_MAX_DEPTH;
-            int x = t;
-            for (int s = depth - 1; s >= 0; --s) {
-                np[s] = x;
-                x = s_par[x];
-            }
-            for (int s = depth; s < GDN_MAX_DEPTH; ++s) np[s] = -1;
+            int32_t *np = W.nodepath + (size_t)(lo + t) * GDN_MAX_DEPTH;  // root first
+#pragma unroll
+            for (int j = 0; j < GDN_MAX_DEPTH; ++j)
+                if (j < depth) np[depth - 1 - j] = anc[j];
+#pragma unroll
+            for (int s2 = 0; s2 < GDN_MAX_DEPTH; ++s2)
+                if (s2 >= depth) np[s2] = -1;
         }
-        // stack height after each position: pushes minus pops up to it
-        __syncthreads();  // every thread is done reading s_off / s_later above
-        s_scan[t] = t < n ? pos : -1;
-        s_off[t] = t < n ? act : 0;
-        if (t == 0) s_later[0] = 0;
-        __syncthreads();
-        if (t < n) {
-            int height = 0;
-            for (int s2 = 0; s2 < n; ++s2) {
-                if (s_scan[s2] > pos) continue;
-                const int a2 = s_off[s2];
-                height += ((a2 & GDN_ACT_PUSH) ? 1 : 0) - ((a2 & 3) == GDN_ACT_POP ? 1 : 0);
-            }
-            atomicMax(&s_later[0], height);
-        }
-        __syncthreads();
-        max_stack = s_later[0];
     } else if (in_bounds) {
         // rejected (or empty) sequence: defined metadata
         for (int i = t; i < hi - lo; i += kPlanThreads) {
@@ -180,9 +173,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params P) {
         W.seq_info[b * kSeqInfoInts + 0] = in_bounds ? lo : 0;
         W.seq_info[b * kSeqInfoInts + 1] = in_bounds ? hi - lo : 0;
         W.seq_info[b * kSeqInfoInts + 2] = status;
-        W.seq_info[b * kSeqInfoInts + 3] = (status == GDN_SEQ_OK && n > 0) ? P.slot_idx[b] : 0;
-        W.seq_info[b * kSeqInfoInts + 4] = max_stack;
-        for (int r = 5; r < kSeqInfoInts; ++r) W.seq_info[b * kSeqInfoInts + r] = 0;
+        W.seq_info[b * kSeqInfoInts + 3] = (status == GDN_SEQ_OK && n > 0) ? my_slot : 0;
+        for (int r = 4; r < kSeqInfoInts; ++r) W.seq_info[b * kSeqInfoInts + r] = 0;
         W.path_len[b] = 0;
     }
     if (t < GDN_MAX_DEPTH) W.path[b * GDN_MAX_DEPTH + t] = -1;
