@@ -38,8 +38,10 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 __device__ __forceinline__ float qnan_f() { return __int_as_float(0x7fc00000); }
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// one load, no short-circuit: the test does not hold back the loads issued next to it
 __device__ __forceinline__ bool ws_planned(const Params &P) {
-    return P.ws.header[0] == kMagic && P.ws.header[1] == P.B && P.ws.header[2] == P.T;
+    const int4 h = *reinterpret_cast<const int4 *>(P.ws.header);
+    return (h.x == (int)kMagic) & (h.y == P.B) & (h.z == P.T);
 }
 
 // ===========================================================================
@@ -1037,9 +1039,9 @@ __global__ __launch_bounds__(RG<D>::THREADS) void replay_kernel(Params P) {
 }
 
 // ===========================================================================
-// Replay on the matrix cores: one workgroup per (sequence, key head), D/32
-// waves, wave w owning state rows [32w, 32w+32) of each value head of the
-// group.  With L path tokens (keys k_e, L <= 16):
+// Replay on the matrix cores: one workgroup per (sequence, run of HPW value
+// heads that read one key head), D/32 waves, wave w owning state rows
+// [32w, 32w+32) of each of its heads.  With L path tokens (keys k_e, L <= 16):
 //   x_e   = S0 k_e                                   (X = S0 K^T, MFMA)
 //   c_p   = b_p v_p - alpha_p x_p - sum_{e<p} Lc[p][e] c_e   (per row, VALU)
 //   S_new = gamma_{L-1} S0 + sum_e w_e c_e k_e^T     (rank-L update, MFMA
@@ -1100,20 +1102,21 @@ __device__ __forceinline__ void load_state_tiles(const float *head, unsigned lan
         }
 }
 
-template <int D, bool CHAIN, int GRP>
-__global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2))) void replay_group_kernel(
+template <int D, bool CHAIN, int HPW>
+__global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(HPW == 1 ? 3 : 2))) void replay_group_kernel(
     Params P) {
     extern __shared__ __attribute__((aligned(16))) char lds_raw[];
     constexpr int NT = VG<D>::THREADS, NTILE = D / 32;
-    constexpr int grp = GRP;
+    constexpr int grp = HPW;  // value heads of this workgroup, all reading one key head
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, hf = lane / 32, l32 = lane % 32;
     const int row = w * 32 + l32;
-    const int b = blockIdx.x / P.Hk, g = blockIdx.x % P.Hk;
-    const int h0 = g * grp;
+    const int nhg = P.Hv / grp;
+    const int b = blockIdx.x / nhg, h0 = blockIdx.x % nhg * grp;
+    const int g = h0 / (P.Hv / P.Hk);
 
-    // ---- the path: local ids path[e] (root first), its length, source and destination
-    int lo, len, slot;
-    const int32_t *path = nullptr;  // null: a chain, path[e] = e
+    // ---- the path: lane e < 16 of every wave holds path entry e (local id, root first);
+    // its length, source and destination.  Each step's loads are issued before any test.
+    int lo, len, slot, pl;
     float *dst;
     if (CHAIN) {
         const int c0 = P.cu_nodes[b], c1 = P.cu_nodes[b + 1];
@@ -1123,23 +1126,26 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         if (len < 0 || len > c1 - c0 || len > kPath) return;
         if (slot < 0 || slot >= P.num_slots) return;
         lo = c0;
+        pl = lane % kPath;
         dst = P.final_state + (size_t)b * P.Hv * D * D;
     } else {
-        if (!ws_planned(P)) return;
+        const bool planned = ws_planned(P);
         const int4 info = *reinterpret_cast<const int4 *>(P.ws.seq_info + b * kSeqInfoInts);
         const int m = P.accepted[b];
+        if (!planned) return;
         if (info.z != GDN_SEQ_OK || info.y == 0) return;
         if (m < -1 || m >= info.y) {
             if (g == 0 && tid == 0) P.ws.seq_status[b] = GDN_SEQ_BAD_ACCEPT;
             return;
         }
         if (m == -1) return;
-        lo = info.x;
-        slot = info.w;
-        path = P.ws.nodepath + (size_t)(lo + m) * GDN_MAX_DEPTH;
-        len = P.ws.depth[lo + m];
+        lo = uni(info.x);
+        slot = uni(info.w);
+        const int mu = uni(m);
+        pl = P.ws.nodepath[(size_t)(lo + mu) * GDN_MAX_DEPTH + lane % kPath];
+        len = P.ws.depth[lo + mu];
         if (g == 0 && tid < GDN_MAX_DEPTH) {
-            P.ws.path[b * GDN_MAX_DEPTH + tid] = path[tid];
+            P.ws.path[b * GDN_MAX_DEPTH + tid] = pl;
             if (tid == 0) P.ws.path_len[b] = len;
         }
         dst = P.state_out + (size_t)slot * P.Hv * D * D;
@@ -1172,54 +1178,55 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
     constexpr int K_PER = (KC + NT - 1) / NT;
     constexpr int VC = kPath * grp * D / 8;
     constexpr int V_PER = (VC + NT - 1) / NT;
+    // the nodes each thread fetches for, looked up before any fetch is issued; every
+    // fetch is unconditional (entries past the path read node 0 and are dropped), so
+    // nothing waits for one before the states are issued
+    static_assert(KC % NT == 0 && VC % NT == 0, "whole table rounds");
+    // node of path entry e, and node 0 for every e >= len: a chain shorter than 16
+    // tokens may end its buffers right after its last token
+    auto node_of = [&](int e) {
+        const int x = __shfl(pl, e);  // every lane takes part in the shuffle
+        return e < len ? max(x, 0) : 0;
+    };
+    int nk[K_PER], nv[V_PER];
+#pragma unroll
+    for (int u = 0; u < K_PER; ++u) nk[u] = node_of(((tid + u * NT) / (D / 8)) % kPath);
+#pragma unroll
+    for (int u = 0; u < V_PER; ++u) nv[u] = node_of(((tid + u * NT) / (grp * D / 8)) % kPath);
+    const int ng = node_of(tid % kPath);
     uint4 kr[K_PER], vr[V_PER];
 #pragma unroll
-    for (int u = 0; u < K_PER; ++u) {
-        const int idx = tid + u * NT, e = idx / (D / 8), c8 = idx % (D / 8);
-        kr[u] = make_uint4(0, 0, 0, 0);
-        if (idx < KC && e < len) {
-            const int node = path ? path[e] : e;
-            kr[u] = *reinterpret_cast<const uint4 *>(kb + (size_t)node * P.Hk * D + 8 * c8);
-        }
-    }
+    for (int u = 0; u < K_PER; ++u)
+        kr[u] = *reinterpret_cast<const uint4 *>(kb + (size_t)nk[u] * P.Hk * D + 8 * ((tid + u * NT) % (D / 8)));
 #pragma unroll
-    for (int u = 0; u < V_PER; ++u) {
-        const int idx = tid + u * NT, e = idx / (grp * D / 8), c = idx % (grp * D / 8);
-        vr[u] = make_uint4(0, 0, 0, 0);
-        if (idx < VC && e < len) {
-            const int node = path ? path[e] : e;
-            vr[u] = *reinterpret_cast<const uint4 *>(vg + (size_t)node * P.Hv * D + 8 * c);
-        }
-    }
-    float ga = 1.0f, gb = 0.0f;  // gates of (head tid / 16, path entry tid % 16)
-    if (tid < grp * kPath && tid % kPath < len) {
-        const int node = path ? path[tid % kPath] : tid % kPath;
-        const size_t at = (size_t)(lo + node) * P.Hv + h0 + tid / kPath;
-        ga = P.a[at];
-        gb = P.b[at];
-    }
+    for (int u = 0; u < V_PER; ++u)
+        vr[u] = *reinterpret_cast<const uint4 *>(vg + (size_t)nv[u] * P.Hv * D + 8 * ((tid + u * NT) % (grp * D / 8)));
+    const bool gate_t = tid < grp * kPath;
+    const size_t at = (size_t)(lo + ng) * P.Hv + h0 + (gate_t ? tid / kPath : 0);
+    float ga = P.a[at], gb = P.b[at];
     // first two heads' states, issued after the tables so that waiting for the tables
     // does not wait for them
     load_state_tiles<D>(s0, s_lane, SA);
     if (grp > 1) load_state_tiles<D>(s0 + (size_t)D * D, s_lane, SB);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < K_PER; ++u) {
         const int idx = tid + u * NT, e = idx / (D / 8), c8 = idx % (D / 8);
-        if (idx < KC) {
-            *reinterpret_cast<uint4 *>(L.k + e * PTab<D>::KP + 8 * c8) = kr[u];
-            const uint16_t *hv = reinterpret_cast<const uint16_t *>(&kr[u]);
+        const uint4 kv = e < len ? kr[u] : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(L.k + e * PTab<D>::KP + 8 * c8) = kv;
+        const uint16_t *hv = reinterpret_cast<const uint16_t *>(&kv);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) L.kt[(8 * c8 + i) * PTab<D>::KT + e] = hv[i];
-        }
+        for (int i = 0; i < 8; ++i) L.kt[(8 * c8 + i) * PTab<D>::KT + e] = hv[i];
     }
 #pragma unroll
     for (int u = 0; u < V_PER; ++u) {
         const int idx = tid + u * NT;
-        if (idx < VC) reinterpret_cast<uint4 *>(L.v)[idx] = vr[u];
+        reinterpret_cast<uint4 *>(L.v)[idx] = idx / (grp * D / 8) < len ? vr[u] : make_uint4(0, 0, 0, 0);
     }
-    if (tid < grp * kPath) {
-        L.a[tid] = ga;
-        L.b[tid] = gb;
+    if (gate_t) {
+        const bool on = tid % kPath < len;
+        L.a[tid] = on ? ga : 1.0f;
+        L.b[tid] = on ? gb : 0.0f;
     }
     __syncthreads();
 
@@ -1391,12 +1398,16 @@ hipError_t launch_verify_d(const Params &p, bool chain, hipStream_t s) {
     return launch_with_lds(verify_kernel<D, false, 3>, grid, block, vtab_bytes(p.max_nodes, D, false), s, p);
 }
 
+#ifndef GDN_REPLAY_HPW
+#define GDN_REPLAY_HPW 1  // value heads per replay workgroup (a divisor of H_v / H_k); 0: all of them
+#endif
 template <int D>
 hipError_t launch_replay_d(const Params &p, bool chain, hipStream_t s) {
     const int grp = p.Hv / p.Hk;
-    if (grp <= kGroupMaxHeads) {
-        const dim3 grid(p.B * p.Hk), block(VG<D>::THREADS);
-        switch (grp) {
+    const int hpw = GDN_REPLAY_HPW > 0 && grp % GDN_REPLAY_HPW == 0 ? GDN_REPLAY_HPW : grp;
+    if (hpw <= kGroupMaxHeads) {
+        const dim3 grid(p.B * (p.Hv / hpw)), block(VG<D>::THREADS);
+        switch (hpw) {
 #define GDN_GROUP_CASE(G)                                                                                     \
     case G:                                                                                                   \
         return chain ? launch_with_lds(replay_group_kernel<D, true, G>, grid, block, ptab_bytes<D>(G), s, p) \
