@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0, help="independent copies (default: >= 512 MB in flight)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--path", choices=["auto", "recurrent"], default="auto",
+                    help="recurrent: run the per-node recurrent kernels on every call (GDN_KERNEL_PATH)")
     return ap.parse_args()
 
 
@@ -61,6 +63,8 @@ def main():
         print(json.dumps({"error": "this build measures one GPU; --gpus %d is not supported "
                                    "(the path shards with no exchange; see DESIGN.md)" % args.gpus}))
         sys.exit(2)
+    if args.path == "recurrent":
+        os.environ["GDN_KERNEL_PATH"] = "recurrent"
     import torch
     import gated_deltanet_tree_amd as G
     import workloads as W
@@ -217,7 +221,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "sequences": cfg.num_seqs, "layers": layers, "nodes": T,
                    "v_heads": cfg.num_v_heads, "k_heads": cfg.num_k_heads, "head_dim": cfg.head_dim,
-                   "qkv": cfg.dtype, "rotated_copies": rotate, "seed": cfg.seed},
+                   "qkv": cfg.dtype, "rotated_copies": rotate, "seed": cfg.seed, "kernels": args.path},
         "layer_call": {"verify_us": t_ver * 1e6, "persist_us": t_per * 1e6, "plan_us": t_plan * 1e6,
                        "verify_bytes": vbytes, "persist_bytes": pbytes, "hbm_gbs": hbm_gbs,
                        "hbm_frac": hbm_gbs / HBM_PEAK_GBS,

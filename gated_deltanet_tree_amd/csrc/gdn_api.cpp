@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -51,6 +52,12 @@ Params base_params(const gdn_dims *d) {
 }
 
 int launched(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH; }
+
+// GDN_KERNEL_PATH=recurrent selects the per-node recurrent kernels for every call
+bool recurrent_forced() {
+    const char *v = std::getenv("GDN_KERNEL_PATH");
+    return v && std::strcmp(v, "recurrent") == 0;
+}
 
 hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
 
@@ -104,7 +111,7 @@ int gdn_tree_verify(const gdn_dims *dims, const void *q, const void *k, const vo
     p.has_ws = 1;
     // the MFMA verify covers trees of up to 96 nodes; larger trees walk the
     // tree recurrently
-    if (gdn::fast_tree_supported(p.D, dims->qkv_dtype, dims->max_nodes))
+    if (!recurrent_forced() && gdn::fast_tree_supported(p.D, dims->qkv_dtype, dims->max_nodes))
         return launched(gdn::launch_tree_verify_fast(p, as_stream(stream)));
     return launched(gdn::launch_tree_verify_recurrent(p, dims->qkv_dtype, as_stream(stream)));
 }
@@ -130,7 +137,7 @@ int gdn_tree_persist(const gdn_dims *dims, const void *k, const void *v, const f
     p.slot_idx = slot_idx;
     p.ws = gdn::ws_ptrs(ws, p.B, p.T, p.Hv);
     p.has_ws = 1;
-    if (gdn::fast_path_supported(p.D, dims->qkv_dtype))
+    if (!recurrent_forced() && gdn::fast_path_supported(p.D, dims->qkv_dtype))
         return launched(gdn::launch_persist_fast(p, as_stream(stream)));
     return launched(gdn::launch_persist_recurrent(p, dims->qkv_dtype, as_stream(stream)));
 }
@@ -147,7 +154,8 @@ int gdn_chain_verify(const gdn_dims *dims, const int32_t *cu_nodes, const void *
     if (dims->total_nodes > 0 && (!k || !v || !a || !b)) return GDN_ERR_NULL;
     if (dims->num_seqs > 0 && (!state_cache || !slot_idx)) return GDN_ERR_NULL;
     if (ws && ws_bytes < gdn_workspace_bytes(dims)) return GDN_ERR_WORKSPACE;
-    const bool fast = gdn::fast_path_supported(dims->head_dim, dims->qkv_dtype) && dims->max_nodes <= GDN_MAX_DEPTH;
+    const bool fast = !recurrent_forced() && gdn::fast_path_supported(dims->head_dim, dims->qkv_dtype) &&
+                      dims->max_nodes <= GDN_MAX_DEPTH;
     if (fast && q && !ws) return GDN_ERR_NULL;  // the outputs need the workspace for coefficients
     if (dims->num_seqs == 0) return GDN_OK;
     Params p = base_params(dims);

@@ -16,9 +16,6 @@
 // the same recurrence and writes G_m S0 + sum_e R(m,e) c_e k_e^T in place.
 #include <algorithm>
 
-#ifndef GDN_REPLAY_ROWS
-#define GDN_REPLAY_ROWS 64  // rows per replay workgroup (4 lanes each)
-#endif
 
 #include "gdn_internal.h"
 
@@ -497,8 +494,8 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
 }
 
 // ===========================================================================
-// Verify for trees of at most 32 nodes: one workgroup per (sequence, key
-// head), D/32 waves.  The workgroup computes the coefficients of its value
+// Verify for trees of at most 32 nodes: one workgroup per (sequence, run of
+// HPW value heads that read one key head), D/32 waves.  The workgroup computes the coefficients of its value
 // heads once (Gram entries shared through the key head) while the first
 // head's state is in flight, then walks its value heads with the next head's
 // state already loading into registers while the current head computes on
@@ -568,19 +565,20 @@ __device__ __forceinline__ void load_state_frags(const float *head, unsigned lan
     }
 }
 
-template <int D, bool CHAIN, int GRP>
-__global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2))) void verify_group_kernel(
-    Params P) {
+template <int D, bool CHAIN, int HPW>
+__global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(HPW == 1 ? 3 : 2))) void
+verify_group_kernel(Params P) {
     extern __shared__ __attribute__((aligned(16))) char lds_raw[];
     constexpr int KS = VG<D>::KS, NT = VG<D>::THREADS;
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, hf = lane / 32, l32 = lane % 32;
     const int row = w * 32 + l32;
-    constexpr int grp = GRP;
-    const int b = blockIdx.x / P.Hk, g = blockIdx.x % P.Hk;
-    const int h0 = g * grp;
+    constexpr int grp = HPW;  // value heads of this workgroup, all reading one key head
+    const int nhg = P.Hv / grp;
+    const int b = blockIdx.x / nhg, h0 = blockIdx.x % nhg * grp;
+    const int g = h0 / (P.Hv / P.Hk);
     const SeqView sv = seq_view<CHAIN>(P, b);
     if (!CHAIN && !ws_planned(P)) return;
-    if (CHAIN && P.has_ws && g == 0 && tid == 0) {
+    if (CHAIN && P.has_ws && h0 == 0 && tid == 0) {
         if (b == 0) {
             P.ws.header[0] = kMagic;
             P.ws.header[1] = P.B;
@@ -813,235 +811,11 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
     }
 }
 
-template <int D>
-struct RG {
-    static constexpr int LPR = 4;             // lanes per state row
-    static constexpr int CPL = D / LPR;       // columns per lane
-    static constexpr int NCH = CPL / 4;       // float4 chunks per lane
-    static constexpr int ROWS = GDN_REPLAY_ROWS;  // rows per workgroup
-    static constexpr int THREADS = ROWS * LPR;
-    static constexpr int SLICES = D / ROWS;   // workgroups per (sequence, value head)
-};
-
-// column of element 0 of chunk c held by lane j of a row group: the 4 lanes
-// of a row read 64 contiguous bytes per chunk
-template <int D>
-__device__ __forceinline__ int rcol(int j, int c) { return c * 4 * RG<D>::LPR + j * 4; }
-
-template <int CTRL>
-__device__ __forceinline__ float dppf(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-// sum over the 4 lanes of a row group; every lane gets the same bits
-__device__ __forceinline__ float sum4(float x) {
-    x = x + dppf<0xB1>(x);  // quad_perm [1,0,3,2]
-    x = x + dppf<0x4E>(x);  // quad_perm [2,3,0,1]
-    return x;
-}
-
-struct RTab {
-    float *k;        // [16][D] path keys (fp32)
-    float *a, *b, *gamma, *alpha, *w_r;  // [16]; w_r[e] = R(L-1, e)
-    float *coefL;    // [16][16] b_p R(p,e) (k_e . k_p) for e < p, else 0
-};
-
-__host__ __device__ inline size_t rtab_bytes(int D) {
-    return (size_t)kPath * D * 4 + kPath * kPath * 4 + 5 * kPath * 4;
-}
-
-__device__ inline RTab rtab_carve(char *base, int D) {
-    RTab L;
-    L.k = reinterpret_cast<float *>(base);     base += (size_t)kPath * D * 4;
-    L.coefL = reinterpret_cast<float *>(base); base += kPath * kPath * 4;
-    L.a = reinterpret_cast<float *>(base);     base += kPath * 4;
-    L.b = reinterpret_cast<float *>(base);     base += kPath * 4;
-    L.gamma = reinterpret_cast<float *>(base); base += kPath * 4;
-    L.alpha = reinterpret_cast<float *>(base); base += kPath * 4;
-    L.w_r = reinterpret_cast<float *>(base);
-    return L;
-}
-
-// CHAIN: the path is nodes 0..len-1 of chain b (len = final_len[b] <= 16),
-// read from state_in[slot_idx[b]] and written to final_state[b].  Otherwise
-// the accepted path of sequence b, replayed in place in the state cache.
-template <int D, bool CHAIN>
-__global__ __launch_bounds__(RG<D>::THREADS) void replay_kernel(Params P) {
-    extern __shared__ __attribute__((aligned(16))) char lds_raw[];
-    using G = RG<D>;
-    const int tid = threadIdx.x, j = tid % G::LPR;
-    const int slice = blockIdx.x % G::SLICES;
-    const int b = blockIdx.x / G::SLICES / P.Hv, h = blockIdx.x / G::SLICES % P.Hv;
-    const int g = h / (P.Hv / P.Hk);
-    const int row = slice * G::ROWS + tid / G::LPR;
-
-    int lo, len, slot;
-    const int32_t *path = nullptr;  // local node ids (null: chain 0..len-1)
-    float *dst;
-    if (CHAIN) {
-        const int c0 = P.cu_nodes[b], c1 = P.cu_nodes[b + 1];
-        if (!(0 <= c0 && c0 <= c1 && c1 <= P.T) || c1 - c0 > P.max_nodes) return;
-        const int n = c1 - c0;
-        len = P.final_len[b];
-        if (len < 0 || len > n || len > kPath) return;
-        slot = P.slot_idx[b];
-        if (slot < 0 || slot >= P.num_slots) return;
-        lo = c0;
-        dst = P.final_state + (((size_t)b * P.Hv + h) * D + row) * D;
-    } else {
-        if (!ws_planned(P)) return;
-        const int n = P.ws.seq_info[b * kSeqInfoInts + 1];
-        if (P.ws.seq_status[b] != GDN_SEQ_OK || n == 0) return;
-        const int m = P.accepted[b];
-        if (m < -1 || m >= n) {
-            if (h == 0 && slice == 0 && tid == 0) P.ws.seq_status[b] = GDN_SEQ_BAD_ACCEPT;
-            return;
-        }
-        if (m == -1) return;
-        lo = P.ws.seq_info[b * kSeqInfoInts + 0];
-        slot = P.slot_idx[b];
-        len = P.ws.depth[lo + m];
-        path = P.ws.nodepath + (size_t)(lo + m) * GDN_MAX_DEPTH;
-        if (h == 0 && slice == 0 && tid < GDN_MAX_DEPTH) {
-            P.ws.path[b * GDN_MAX_DEPTH + tid] = path[tid];
-            if (tid == 0) P.ws.path_len[b] = len;
-        }
-        dst = P.state_out + (((size_t)slot * P.Hv + h) * D + row) * D;
-    }
-    len = uni(len);
-
-    // state row slice: issued before anything that waits
-    const float *src = P.state_in + (((size_t)slot * P.Hv + h) * D + row) * D;
-    float S[G::CPL];
-#pragma unroll
-    for (int c = 0; c < G::NCH; ++c) {
-        const float4 f = *reinterpret_cast<const float4 *>(src + rcol<D>(j, c));
-        S[4 * c + 0] = f.x; S[4 * c + 1] = f.y; S[4 * c + 2] = f.z; S[4 * c + 3] = f.w;
-    }
-    if (len == 0) {  // chain final state after zero nodes: the committed state
-#pragma unroll
-        for (int c = 0; c < G::NCH; ++c)
-            *reinterpret_cast<float4 *>(dst + rcol<D>(j, c)) =
-                make_float4(S[4 * c + 0], S[4 * c + 1], S[4 * c + 2], S[4 * c + 3]);
-        return;
-    }
-
-    const RTab L = rtab_carve(lds_raw, D);
-    const uint16_t *kb = static_cast<const uint16_t *>(P.k) + ((size_t)lo * P.Hk + g) * D;
-    const uint16_t *vb = static_cast<const uint16_t *>(P.v) + ((size_t)lo * P.Hv + h) * D + row;
-    const size_t kq_stride = (size_t)P.Hk * D, v_stride = (size_t)P.Hv * D;
-    // path keys -> LDS as fp32 (zero rows past the path), gates -> LDS
-    for (int idx = tid; idx < kPath * D / 8; idx += G::THREADS) {
-        const int e = idx / (D / 8), c8 = idx % (D / 8);
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (e < len) {
-            const int node = path ? path[e] : e;
-            v = *reinterpret_cast<const uint4 *>(kb + (size_t)node * kq_stride + 8 * c8);
-        }
-        float4 *d4 = reinterpret_cast<float4 *>(L.k + e * D + 8 * c8);
-        d4[0] = make_float4(bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y));
-        d4[1] = make_float4(bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w));
-    }
-    if (tid < kPath) {
-        const int node = tid < len ? (path ? path[tid] : tid) : 0;
-        L.a[tid] = tid < len ? P.a[(size_t)(lo + node) * P.Hv + h] : 1.0f;
-        L.b[tid] = tid < len ? P.b[(size_t)(lo + node) * P.Hv + h] : 0.0f;
-    }
-    float vr[kPath];
-#pragma unroll
-    for (int e = 0; e < kPath; ++e) {
-        vr[e] = 0.0f;
-        if (e < len) vr[e] = bf2f(vb[(size_t)(path ? path[e] : e) * v_stride]);
-    }
-    __syncthreads();
-    // coefficients for the pairs e < p < len: one pair per 4-lane group
-    const int npairs = len * (len - 1) / 2;
-    for (int pr = tid / G::LPR; pr < npairs; pr += G::THREADS / G::LPR) {
-        int p = 1, base = 0;
-        while (base + p <= pr) { base += p; ++p; }
-        const int e = pr - base;
-        float dot = 0.0f;
-#pragma unroll
-        for (int c = 0; c < G::NCH; ++c) {
-            const float4 ke = *reinterpret_cast<const float4 *>(L.k + e * D + rcol<D>(j, c));
-            const float4 kp = *reinterpret_cast<const float4 *>(L.k + p * D + rcol<D>(j, c));
-            dot = fmaf(ke.x, kp.x, dot);
-            dot = fmaf(ke.y, kp.y, dot);
-            dot = fmaf(ke.z, kp.z, dot);
-            dot = fmaf(ke.w, kp.w, dot);
-        }
-        dot = sum4(dot);
-        if (j == 0) {
-            float r = 1.0f;
-            for (int t = e + 1; t <= p; ++t) r *= L.a[t];
-            L.coefL[p * kPath + e] = L.b[p] * r * dot;
-        }
-    }
-    if (tid < kPath) {
-        float g_ = 1.0f, r = 1.0f;
-        for (int t = 0; t <= tid; ++t) g_ *= L.a[t];
-        for (int t = tid + 1; t < len; ++t) r *= L.a[t];
-        L.gamma[tid] = g_;
-        L.alpha[tid] = L.b[tid] * g_;
-        L.w_r[tid] = tid < len ? r : 0.0f;
-    }
-    __syncthreads();
-
-    // S0 k_e for the path keys (independent dot products)
-    float x[kPath];
-#pragma unroll
-    for (int e = 0; e < kPath; ++e) {
-        x[e] = 0.0f;
-        if (e < len) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int c = 0; c < G::NCH; ++c) {
-                const float4 kk = *reinterpret_cast<const float4 *>(L.k + e * D + rcol<D>(j, c));
-                acc = fmaf(S[4 * c + 0], kk.x, acc);
-                acc = fmaf(S[4 * c + 1], kk.y, acc);
-                acc = fmaf(S[4 * c + 2], kk.z, acc);
-                acc = fmaf(S[4 * c + 3], kk.w, acc);
-            }
-            x[e] = sum4(acc);
-        }
-    }
-    // c_p = b_p v_p - alpha_p x_p - sum_{e<p} coefL[p][e] c_e
-    float cv[kPath];
-#pragma unroll
-    for (int p = 0; p < kPath; ++p) {
-        float c = 0.0f;
-        if (p < len) {
-            c = fmaf(-L.alpha[p], x[p], L.b[p] * vr[p]);
-#pragma unroll
-            for (int e = 0; e < p; ++e) c = fmaf(-L.coefL[p * kPath + e], cv[e], c);
-        }
-        cv[p] = c;
-    }
-    // S_new = gamma_{L-1} S0 + sum_e R(L-1,e) c_e k_e^T
-    float wv[kPath];
-#pragma unroll
-    for (int e = 0; e < kPath; ++e) wv[e] = L.w_r[e] * cv[e];
-    const float gm = L.gamma[len - 1];
-#pragma unroll
-    for (int c = 0; c < G::NCH; ++c) {
-        float o0 = gm * S[4 * c + 0], o1 = gm * S[4 * c + 1], o2 = gm * S[4 * c + 2], o3 = gm * S[4 * c + 3];
-#pragma unroll
-        for (int e = 0; e < kPath; ++e) {
-            if (e < len) {
-                const float4 kk = *reinterpret_cast<const float4 *>(L.k + e * D + rcol<D>(j, c));
-                o0 = fmaf(wv[e], kk.x, o0);
-                o1 = fmaf(wv[e], kk.y, o1);
-                o2 = fmaf(wv[e], kk.z, o2);
-                o3 = fmaf(wv[e], kk.w, o3);
-            }
-        }
-        *reinterpret_cast<float4 *>(dst + rcol<D>(j, c)) = make_float4(o0, o1, o2, o3);
-    }
-}
-
 // ===========================================================================
-// Replay on the matrix cores: one workgroup per (sequence, run of HPW value
-// heads that read one key head), D/32 waves, wave w owning state rows
-// [32w, 32w+32) of each of its heads.  With L path tokens (keys k_e, L <= 16):
+// Replay on the matrix cores: one workgroup per (sequence, value head), D/32
+// waves, wave w owning state rows [32w, 32w+32).  Four workgroups fit a CU,
+// so one's table and state loads overlap another's arithmetic and stores.
+// With L path tokens (keys k_e, L <= 16):
 //   x_e   = S0 k_e                                   (X = S0 K^T, MFMA)
 //   c_p   = b_p v_p - alpha_p x_p - sum_{e<p} Lc[p][e] c_e   (per row, VALU)
 //   S_new = gamma_{L-1} S0 + sum_e w_e c_e k_e^T     (rank-L update, MFMA
@@ -1052,14 +826,13 @@ __global__ __launch_bounds__(RG<D>::THREADS) void replay_kernel(Params P) {
 // The lane's state registers follow the 32x32 accumulator layout of the
 // transposed tile (lane: one row; register r of tile t: column
 // 32t + 8(r/4) + 4*half + r%4), which is also a valid k-ordering of the B
-// operand of X, so the state is loaded once and updated in place.  The next
-// value head's state is in flight while the current one computes.
+// operand of X, so the state is loaded once and updated in place.
 // ===========================================================================
 template <int D>
 struct PTab {
     uint16_t *k;      // [16][KP] path keys (bf16), rows >= L zero
     uint16_t *kt;     // [D][KT] the same keys transposed
-    uint16_t *v;      // [16][grp][D] path values of the group's heads
+    uint16_t *v;      // [16][grp][D] path values of the workgroup's heads
     float *gram;      // [16][17] k_e . k_p
     float *coefL;     // [grp][16][17]
     float4 *gaw;      // [grp][16] gamma, alpha, b, w
@@ -1102,12 +875,12 @@ __device__ __forceinline__ void load_state_tiles(const float *head, unsigned lan
         }
 }
 
-template <int D, bool CHAIN, int HPW>
-__global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(HPW == 1 ? 3 : 2))) void replay_group_kernel(
+template <int D, bool CHAIN>
+__global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(3))) void replay_kernel(
     Params P) {
     extern __shared__ __attribute__((aligned(16))) char lds_raw[];
     constexpr int NT = VG<D>::THREADS, NTILE = D / 32;
-    constexpr int grp = HPW;  // value heads of this workgroup, all reading one key head
+    constexpr int grp = 1;  // value heads of this workgroup
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, hf = lane / 32, l32 = lane % 32;
     const int row = w * 32 + l32;
     const int nhg = P.Hv / grp;
@@ -1155,7 +928,7 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
     dst += (size_t)h0 * D * D;
     const unsigned s_lane = (unsigned)(row * D + 4 * hf);
 
-    f32x16 SA[NTILE], SB[NTILE];
+    f32x16 SA[NTILE];
     if (len == 0) {  // chain final state after zero tokens: the committed state
 #pragma unroll 1
         for (int hh = 0; hh < grp; ++hh) {
@@ -1170,7 +943,7 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         return;
     }
 
-    // ---- tables: path keys (both ways), values and gates of the group's heads
+    // ---- tables: path keys (both ways), values and gates of the workgroup's head
     const PTab<D> L = ptab_carve<D>(lds_raw, grp);
     const uint16_t *kb = static_cast<const uint16_t *>(P.k) + ((size_t)lo * P.Hk + g) * D;
     const uint16_t *vg = static_cast<const uint16_t *>(P.v) + ((size_t)lo * P.Hv + h0) * D;
@@ -1204,10 +977,8 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
     const bool gate_t = tid < grp * kPath;
     const size_t at = (size_t)(lo + ng) * P.Hv + h0 + (gate_t ? tid / kPath : 0);
     float ga = P.a[at], gb = P.b[at];
-    // first two heads' states, issued after the tables so that waiting for the tables
-    // does not wait for them
+    // the state, issued after the tables so that waiting for the tables does not wait for it
     load_state_tiles<D>(s0, s_lane, SA);
-    if (grp > 1) load_state_tiles<D>(s0 + (size_t)D * D, s_lane, SB);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < K_PER; ++u) {
@@ -1346,15 +1117,7 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
                     make_float4(S[t][4 * q], S[t][4 * q + 1], S[t][4 * q + 2], S[t][4 * q + 3]);
         }
     };
-#pragma unroll
-    for (int hh = 0; hh < grp; hh += 2) {
-        head(SA, hh);
-        if (hh + 2 < grp) load_state_tiles<D>(s0 + (size_t)(hh + 2) * D * D, s_lane, SA);
-        if (hh + 1 < grp) {
-            head(SB, hh + 1);
-            if (hh + 3 < grp) load_state_tiles<D>(s0 + (size_t)(hh + 3) * D * D, s_lane, SB);
-        }
-    }
+    head(SA, 0);
 }
 
 template <typename K>
@@ -1368,12 +1131,15 @@ hipError_t launch_with_lds(K kernel, dim3 grid, dim3 block, size_t lds, hipStrea
     return hipGetLastError();
 }
 
+// trees of at most 32 nodes (and chains): one workgroup per key head and all its value
+// heads, which share the coefficients' Gram entries; else coefficients + verify
 template <int D>
 hipError_t launch_verify_d(const Params &p, bool chain, hipStream_t s) {
     const int grp = p.Hv / p.Hk;
-    if ((chain || p.max_nodes <= kTile) && grp <= kGroupMaxHeads) {
-        const dim3 grid(p.B * p.Hk), block(VG<D>::THREADS);
-        switch (grp) {
+    const int hpw = grp;
+    if ((chain || p.max_nodes <= kTile) && hpw <= kGroupMaxHeads) {
+        const dim3 grid(p.B * (p.Hv / hpw)), block(VG<D>::THREADS);
+        switch (hpw) {
 #define GDN_GROUP_CASE(G)                                                                                    \
     case G:                                                                                                  \
         return chain ? launch_with_lds(verify_group_kernel<D, true, G>, grid, block, gtab_bytes<D>(G), s, p) \
@@ -1398,30 +1164,13 @@ hipError_t launch_verify_d(const Params &p, bool chain, hipStream_t s) {
     return launch_with_lds(verify_kernel<D, false, 3>, grid, block, vtab_bytes(p.max_nodes, D, false), s, p);
 }
 
-#ifndef GDN_REPLAY_HPW
-#define GDN_REPLAY_HPW 1  // value heads per replay workgroup (a divisor of H_v / H_k); 0: all of them
-#endif
+// one workgroup per value head: four fit a CU, and their independent rounds overlap
+// reading and writing better than a key head's workgroup walking its value heads
 template <int D>
 hipError_t launch_replay_d(const Params &p, bool chain, hipStream_t s) {
-    const int grp = p.Hv / p.Hk;
-    const int hpw = GDN_REPLAY_HPW > 0 && grp % GDN_REPLAY_HPW == 0 ? GDN_REPLAY_HPW : grp;
-    if (hpw <= kGroupMaxHeads) {
-        const dim3 grid(p.B * (p.Hv / hpw)), block(VG<D>::THREADS);
-        switch (hpw) {
-#define GDN_GROUP_CASE(G)                                                                                     \
-    case G:                                                                                                   \
-        return chain ? launch_with_lds(replay_group_kernel<D, true, G>, grid, block, ptab_bytes<D>(G), s, p) \
-                     : launch_with_lds(replay_group_kernel<D, false, G>, grid, block, ptab_bytes<D>(G), s, p);
-            GDN_GROUP_CASE(1)
-            GDN_GROUP_CASE(2)
-            GDN_GROUP_CASE(3)
-            GDN_GROUP_CASE(4)
-#undef GDN_GROUP_CASE
-        }
-    }
-    const dim3 grid(p.B * p.Hv * RG<D>::SLICES), block(RG<D>::THREADS);
-    return chain ? launch_with_lds(replay_kernel<D, true>, grid, block, rtab_bytes(D), s, p)
-                 : launch_with_lds(replay_kernel<D, false>, grid, block, rtab_bytes(D), s, p);
+    const dim3 grid(p.B * p.Hv), block(VG<D>::THREADS);
+    return chain ? launch_with_lds(replay_kernel<D, true>, grid, block, ptab_bytes<D>(1), s, p)
+                 : launch_with_lds(replay_kernel<D, false>, grid, block, ptab_bytes<D>(1), s, p);
 }
 
 }  // namespace

@@ -41,6 +41,11 @@
  *  - Stream order per decode step: gdn_tree_plan once, then gdn_tree_verify
  *    for each layer, then (after acceptance) gdn_tree_persist for each layer.
  *    k, v, a and b of the step must stay alive until persist has run.
+ *  - Kernel choice is automatic: bf16 inputs with head_dim 64 or 128 run the
+ *    matrix-core kernels (trees of up to 96 nodes), everything else the
+ *    per-node recurrent kernels.  Setting the environment variable
+ *    GDN_KERNEL_PATH=recurrent makes every call use the recurrent kernels
+ *    (read on each call); both agree to within the stated tolerance.
  *
  * Layouts (row-major, T = total nodes, B = sequences):
  *   parent       int32 [T]        local node id of the parent inside its own
