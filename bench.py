@@ -234,11 +234,18 @@ def main():
 
 
 def kernel_source_digest() -> str:
+    """Hash of the library sources with comments and whitespace removed: a
+    change of code invalidates recorded counters, a change of comments not."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_deltanet_tree_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        text = re.sub(r"\s+", " ", text).strip()
+        h.update(name.encode() + b"\0" + text.encode())
     return h.hexdigest()[:16]
 
 

@@ -494,13 +494,16 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
 }
 
 // ===========================================================================
-// Verify for trees of at most 32 nodes: one workgroup per (sequence, run of
-// HPW value heads that read one key head), D/32 waves.  The workgroup computes the coefficients of its value
-// heads once (Gram entries shared through the key head) while the first
-// head's state is in flight, then walks its value heads with the next head's
-// state already loading into registers while the current head computes on
-// the matrix cores; the head loop has no barrier.  Same algebra as the
-// two-kernel path (coef_kernel + verify_kernel).
+// Verify for trees of at most 32 nodes: one workgroup per (sequence, key head)
+// and its HPW value heads, D/32 waves.  One round trip brings the keys,
+// queries, values, gates and paths into LDS; the first two heads' states are
+// issued as soon as those have landed (issued with them they would queue ahead
+// of them).  While the states arrive the workgroup forms the coefficients once
+// for all its heads (the Gram entries are shared through the key head); then
+// each head's products are taken as its state lands, and a register set takes
+// the next head's state as soon as its products are done.  No barrier after
+// the coefficients.  Same algebra as the two-kernel path (coef_kernel +
+// verify_kernel).
 // ===========================================================================
 constexpr int kGroupMaxHeads = 4;  // value heads per key head this kernel takes
 
