@@ -512,7 +512,7 @@ template <int D>
 struct GPad {
     static constexpr int KQ = D + 8;       // bf16 per key/query row
     static constexpr int PS = kPath + 1;   // per-node path tables
-    static constexpr int MT = kTile + 1;   // output-operator rows
+    static constexpr int MT = kTile + 8;   // output-operator rows, bf16 (80 bytes: conflict-free 8-byte reads)
 };
 
 template <int D>
@@ -520,7 +520,7 @@ struct GTab {
     uint16_t *kq;     // [2][32][KQ] keys / queries (bf16)
     uint16_t *v;      // [32][grp][D] values of the group's heads (bf16), node-major as in memory
     float4 *gab;      // [grp][32] gamma, alpha, b
-    float *mt;        // [grp][32][MT] dense output operator
+    uint16_t *mth, *mtl;  // [grp][32][MT] dense output operator, bf16 hi and lo parts
     float *coefL;     // [grp][32][PS]
     float *gk, *gq;   // [32][PS] path-indexed Gram entries
     int *anc;         // [32][PS] root-to-node path, -1 past the depth
@@ -543,7 +543,8 @@ __device__ inline GTab<D> gtab_carve(char *base, int grp) {
     L.kq = reinterpret_cast<uint16_t *>(base);     base += (size_t)2 * kTile * Q::KQ * 2;
     L.v = reinterpret_cast<uint16_t *>(base);      base += (size_t)kTile * grp * D * 2;
     L.gab = reinterpret_cast<float4 *>(base);      base += (size_t)grp * kTile * 16;
-    L.mt = reinterpret_cast<float *>(base);        base += (size_t)grp * kTile * Q::MT * 4;
+    L.mth = reinterpret_cast<uint16_t *>(base);    base += (size_t)grp * kTile * Q::MT * 2;
+    L.mtl = reinterpret_cast<uint16_t *>(base);    base += (size_t)grp * kTile * Q::MT * 2;
     L.coefL = reinterpret_cast<float *>(base);     base += (size_t)grp * kTile * Q::PS * 4;
     L.gk = reinterpret_cast<float *>(base);        base += kTile * Q::PS * 4;
     L.gq = reinterpret_cast<float *>(base);        base += kTile * Q::PS * 4;
@@ -665,7 +666,10 @@ verify_group_kernel(Params P) {
         const int idx = tid + u * NT;
         if (idx < kTile * vchunks) reinterpret_cast<uint4 *>(L.v)[idx] = vv[u];
     }
-    for (int idx = tid; idx < grp * kTile * Q::MT; idx += NT) L.mt[idx] = 0.0f;
+    for (int idx = tid; idx < grp * kTile * Q::MT / 2; idx += NT) {
+        reinterpret_cast<uint32_t *>(L.mth)[idx] = 0u;
+        reinterpret_cast<uint32_t *>(L.mtl)[idx] = 0u;
+    }
     // the states go out only now: issued together with the small loads above they would queue
     // ahead of them and hold back the coefficients, which gate every output
     float sA[KS][8], sB[KS][8];
@@ -738,10 +742,14 @@ verify_group_kernel(Params P) {
                 acc = fmaf(-y[f], L.coefL[(hh_t * kTile + an_t[f]) * Q::PS + e], acc);
             y[e] = e < d_t ? acc : 0.0f;
         }
-        float *mrow_out = L.mt + (hh_t * kTile + i_t) * Q::MT;
+        uint16_t *mh = L.mth + (hh_t * kTile + i_t) * Q::MT, *ml = L.mtl + (hh_t * kTile + i_t) * Q::MT;
 #pragma unroll
         for (int e = 0; e < kPath; ++e)
-            if (e < d_t) mrow_out[an_t[e]] = y[e];
+            if (e < d_t) {  // stored as bf16 hi + lo for the matrix cores
+                const __bf16 yh = static_cast<__bf16>(y[e]);
+                mh[an_t[e]] = __builtin_bit_cast(uint16_t, yh);
+                ml[an_t[e]] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(y[e] - static_cast<float>(yh)));
+            }
     }
     __syncthreads();
 
@@ -777,11 +785,30 @@ verify_group_kernel(Params P) {
             ax[r] = i < n ? fmaf(-q4.y, ax[r], q4.z * vi) : 0.0f;  // r = b v - alpha x
             ay[r] = i < n ? q4.x * ay[r] : 0.0f;                   // gamma y
         }
-        // O = gamma y + MT R: k-step s pairs the nodes in accumulator slot s of the two half-waves
-        const float *mrow2 = L.mt + (hh * kTile + l32) * Q::MT;
+        // O = gamma y + MT R on bf16 MFMA with both operands split hi + lo (the lo x lo
+        // term, ~2^-32 relative, is dropped).  k-step u takes R from accumulator slots
+        // 8u .. 8u+7, i.e. nodes 16u + 8(e/4) + 4*half + e%4, and MT's columns in that order.
+        const uint16_t *mh = L.mth + (hh * kTile + l32) * Q::MT, *ml = L.mtl + (hh * kTile + l32) * Q::MT;
 #pragma unroll
-        for (int s = 0; s < 16; ++s)
-            ay = __builtin_amdgcn_mfma_f32_32x32x2f32(mrow2[8 * (s / 4) + 4 * hf + (s % 4)], ax[s], ay, 0, 0, 0);
+        for (int u = 0; u < 2; ++u) {
+            const uint2 h0 = *reinterpret_cast<const uint2 *>(mh + 16 * u + 4 * hf);
+            const uint2 h1 = *reinterpret_cast<const uint2 *>(mh + 16 * u + 8 + 4 * hf);
+            const uint2 l0 = *reinterpret_cast<const uint2 *>(ml + 16 * u + 4 * hf);
+            const uint2 l1 = *reinterpret_cast<const uint2 *>(ml + 16 * u + 8 + 4 * hf);
+            const bf16x8 ahi = __builtin_bit_cast(bf16x8, make_uint4(h0.x, h0.y, h1.x, h1.y));
+            const bf16x8 alo = __builtin_bit_cast(bf16x8, make_uint4(l0.x, l0.y, l1.x, l1.y));
+            bf16x8 bhi, blo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float rv = ax[8 * u + e];
+                const __bf16 rb = static_cast<__bf16>(rv);
+                bhi[e] = rb;
+                blo[e] = static_cast<__bf16>(rv - static_cast<float>(rb));
+            }
+            ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bhi, ay, 0, 0, 0);
+            ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, blo, ay, 0, 0, 0);
+            ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bhi, ay, 0, 0, 0);
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int ir = 8 * (r / 4) + (r % 4);  // node of half-wave 0; half-wave 1 adds 4
@@ -794,13 +821,13 @@ verify_group_kernel(Params P) {
     // each register set is refilled as soon as its products are taken
     f32x16 x0, y0;
     xy(sA, x0, y0);
-    if (grp > 2) load_state_frags<D>(s0 + (size_t)2 * D * D, s_lane, sA);
     finish(x0, y0, 0);
+    if (grp > 2) load_state_frags<D>(s0 + (size_t)2 * D * D, s_lane, sA);
     if (grp > 1) {
         f32x16 x1, y1;
         xy(sB, x1, y1);
-        if (grp > 3) load_state_frags<D>(s0 + (size_t)3 * D * D, s_lane, sB);
         finish(x1, y1, 1);
+        if (grp > 3) load_state_frags<D>(s0 + (size_t)3 * D * D, s_lane, sB);
     }
     if (grp > 2) {
         f32x16 x2, y2;
