@@ -842,6 +842,375 @@ verify_group_kernel(Params P) {
 }
 
 // ===========================================================================
+// Verify for trees of 33 .. 96 nodes: NB node blocks of 32, one workgroup per
+// (sequence, key head) and its value heads, one workgroup per CU (the keys and
+// queries of all blocks stay in LDS).  The Gram entries k.k and k.q of every
+// block pair and the per-(head, node) coefficients are formed once; ancestors
+// may sit in any block, so each head first takes X_j = K_j S0^T for all blocks
+// (R_j = diag(b)V_j - diag(alpha)X_j kept in registers), then per block t
+// O_t = diag(gamma)Y_t + sum_j MT_tj R_j, with MT (the output operator, rows
+// from the 16-step back substitution) rebuilt densely in LDS for each head.
+// All products run on bf16 MFMA with fp32 operands split hi + lo.
+// ===========================================================================
+template <int D, int NB>
+struct BPad {
+    static constexpr int NN = NB * kTile;  // node slots
+    static constexpr int KQ = D + 8;       // bf16 per key/query row
+    static constexpr int PS = kPath + 1;   // per-node path tables
+    static constexpr int MS = NN + 8;      // bf16 per output-operator row
+};
+
+template <int D, int NB>
+struct BTab {
+    uint16_t *kq;         // [2][NN][KQ] keys, queries
+    uint16_t *vst;        // [NN][D] values of the current head
+    float4 *gab;          // [grp][NN] gamma, alpha, b
+    float *ysp;           // [grp][NN][16] output weights by path position
+    float *gk, *gq;       // [NN][PS]       (these three and the next share one region:
+    float *coefL;         // [grp][NN][PS]   the Gram entries and coefficients die before
+    uint16_t *mth, *mtl;  // [NN][MS]        the output operator is built)
+    int *anc;             // [NN][PS] root-to-node path, -1 past the depth
+    float *a, *b;         // [grp][NN]
+    int *depth;           // [NN]
+};
+
+template <int D, int NB>
+__host__ __device__ inline size_t btab_bytes(int grp) {
+    using Q = BPad<D, NB>;
+    const size_t u1 = (size_t)2 * Q::NN * Q::PS * 4 + (size_t)grp * Q::NN * Q::PS * 4;
+    const size_t u2 = (size_t)2 * Q::NN * Q::MS * 2;
+    return (size_t)2 * Q::NN * Q::KQ * 2 + (size_t)Q::NN * D * 2 + (size_t)grp * Q::NN * 16 +
+           (size_t)grp * Q::NN * kPath * 4 + (u1 > u2 ? u1 : u2) + (size_t)Q::NN * Q::PS * 4 +
+           2 * (size_t)grp * Q::NN * 4 + (size_t)Q::NN * 4;
+}
+
+template <int D, int NB>
+__device__ inline BTab<D, NB> btab_carve(char *base, int grp) {
+    using Q = BPad<D, NB>;
+    BTab<D, NB> L;
+    L.kq = reinterpret_cast<uint16_t *>(base);   base += (size_t)2 * Q::NN * Q::KQ * 2;
+    L.vst = reinterpret_cast<uint16_t *>(base);  base += (size_t)Q::NN * D * 2;
+    L.gab = reinterpret_cast<float4 *>(base);    base += (size_t)grp * Q::NN * 16;
+    L.ysp = reinterpret_cast<float *>(base);     base += (size_t)grp * Q::NN * kPath * 4;
+    char *u = base;
+    const size_t u1 = (size_t)2 * Q::NN * Q::PS * 4 + (size_t)grp * Q::NN * Q::PS * 4;
+    const size_t u2 = (size_t)2 * Q::NN * Q::MS * 2;
+    base += u1 > u2 ? u1 : u2;
+    L.gk = reinterpret_cast<float *>(u);
+    L.gq = L.gk + Q::NN * Q::PS;
+    L.coefL = L.gq + Q::NN * Q::PS;
+    L.mth = reinterpret_cast<uint16_t *>(u);
+    L.mtl = L.mth + Q::NN * Q::MS;
+    L.anc = reinterpret_cast<int *>(base);       base += (size_t)Q::NN * Q::PS * 4;
+    L.a = reinterpret_cast<float *>(base);       base += (size_t)grp * Q::NN * 4;
+    L.b = reinterpret_cast<float *>(base);       base += (size_t)grp * Q::NN * 4;
+    L.depth = reinterpret_cast<int *>(base);
+    return L;
+}
+
+template <int D, int NB, int GRP>
+__global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(1))) void verify_blocks_kernel(
+    Params P) {
+    extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+    using Q = BPad<D, NB>;
+    constexpr int KS = VG<D>::KS, NT = VG<D>::THREADS, WAVES = VG<D>::WAVES, NN = Q::NN;
+    constexpr int grp = GRP;
+    const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, hf = lane / 32, l32 = lane % 32;
+    const int row = w * 32 + l32;
+    const int b = blockIdx.x / P.Hk, g = blockIdx.x % P.Hk;
+    const int h0 = g * grp;
+    const SeqView sv = seq_view<false>(P, b);
+    if (!ws_planned(P)) return;
+    const int lo = sv.lo, n = sv.n;
+    if (sv.status != GDN_SEQ_OK) {
+        for (int t = tid; t < n * grp * D; t += NT)
+            P.out[((size_t)(lo + t / (grp * D)) * P.Hv + h0) * D + t % (grp * D)] = qnan_f();
+        return;
+    }
+    if (n == 0) return;
+    const int nb = (n + kTile - 1) / kTile;  // node blocks in use (n <= NN)
+    const BTab<D, NB> L = btab_carve<D, NB>(lds_raw, grp);
+    const uint16_t *kb = static_cast<const uint16_t *>(P.k) + ((size_t)lo * P.Hk + g) * D;
+    const uint16_t *qb = static_cast<const uint16_t *>(P.q) + ((size_t)lo * P.Hk + g) * D;
+    const uint16_t *vg = static_cast<const uint16_t *>(P.v) + ((size_t)lo * P.Hv + h0) * D;
+    const size_t kq_stride = (size_t)P.Hk * D;
+    const float *s0 = P.state_in + ((size_t)sv.slot * P.Hv + h0) * D * D;
+    const unsigned s_lane = (unsigned)(row * D + 8 * hf);
+    constexpr int V_PER = (NN * (D / 8) + NT - 1) / NT;  // 16-byte chunks of one head's values
+    auto fetch_v = [&](int hh, uint4 (&vr)[V_PER]) {
+#pragma unroll
+        for (int u = 0; u < V_PER; ++u) {
+            const int c = tid + u * NT;
+            vr[u] = c < n * (D / 8) ? *reinterpret_cast<const uint4 *>(vg + (size_t)(c / (D / 8)) * P.Hv * D + hh * D +
+                                                                        8 * (c % (D / 8)))
+                                    : make_uint4(0, 0, 0, 0);
+        }
+    };
+
+    // ---- one round trip: keys/queries of all blocks, gates, paths
+    constexpr int KQ_PER = 2 * NN * (D / 8) / NT;
+    static_assert(2 * NN * (D / 8) % NT == 0, "whole key/query rounds");
+    uint4 kqv[KQ_PER];
+#pragma unroll
+    for (int u = 0; u < KQ_PER; ++u) {
+        const int idx = tid + u * NT;
+        const int which = idx / (NN * (D / 8)), rem = idx % (NN * (D / 8));
+        const int i = rem / (D / 8), c8 = rem % (D / 8);
+        kqv[u] = i < n ? *reinterpret_cast<const uint4 *>((which ? qb : kb) + (size_t)i * kq_stride + 8 * c8)
+                       : make_uint4(0, 0, 0, 0);
+    }
+    constexpr int GA_PER = (GRP * NN + NT - 1) / NT;
+    float ga[GA_PER], gb[GA_PER];
+#pragma unroll
+    for (int u = 0; u < GA_PER; ++u) {
+        const int t = tid + u * NT;
+        ga[u] = 1.0f;
+        gb[u] = 0.0f;
+        if (t < grp * n) {
+            const size_t at = (size_t)(lo + t % n) * P.Hv + h0 + t / n;
+            ga[u] = P.a[at];
+            gb[u] = P.b[at];
+        }
+    }
+    static_assert(NN <= NT, "one thread per node");
+    int an[kPath], d = 0;
+    if (tid < n) {
+        d = P.ws.depth[lo + tid];
+#pragma unroll
+        for (int e = 0; e < kPath; ++e) an[e] = P.ws.nodepath[(size_t)(lo + tid) * GDN_MAX_DEPTH + e];
+    }
+    if (tid < n) {
+#pragma unroll
+        for (int e = 0; e < kPath; ++e) L.anc[tid * Q::PS + e] = an[e];
+        L.depth[tid] = d;
+    }
+#pragma unroll
+    for (int u = 0; u < GA_PER; ++u) {
+        const int t = tid + u * NT;
+        if (t < grp * n) {
+            L.a[(t / n) * NN + t % n] = ga[u];
+            L.b[(t / n) * NN + t % n] = gb[u];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < KQ_PER; ++u) {
+        const int idx = tid + u * NT;
+        *reinterpret_cast<uint4 *>(L.kq + (idx / (D / 8)) * Q::KQ + 8 * (idx % (D / 8))) = kqv[u];
+    }
+    // the first head's state and values go out once the tables have landed; the second
+    // head's after the coefficients (registers are scarce while those are formed)
+    float sA[KS][8], sB[KS][8];
+    uint4 vA[V_PER], vB[V_PER];
+    load_state_frags<D>(s0, s_lane, sA);
+    fetch_v(0, vA);
+    __syncthreads();
+
+    // ---- Gram entries of every block pair: node j's ancestor i at path position
+    // depth(i) - 1 gets k_i . k_j and k_i . q_j
+    for (int pr = w; pr < nb * nb; pr += WAVES) {
+        const int ti = pr / nb, tj = pr % nb;
+        f32x16 gkk = {}, gkq = {};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const bf16x8 A = frag_of(L.kq + (ti * kTile + l32) * Q::KQ, s, hf);
+            const bf16x8 Bk = frag_of(L.kq + (tj * kTile + l32) * Q::KQ, s, hf);
+            const bf16x8 Bq = frag_of(L.kq + (NN + tj * kTile + l32) * Q::KQ, s, hf);
+            gkk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bk, gkk, 0, 0, 0);
+            gkq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bq, gkq, 0, 0, 0);
+        }
+        const int j = tj * kTile + l32;
+        if (j < n) {
+            const int dj = L.depth[j];
+            int er[16], ar[16];  // candidate i's path position in j's path, and who sits there
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = ti * kTile + 8 * (r / 4) + 4 * hf + (r % 4);
+                er[r] = i < n ? L.depth[i] - 1 : kPath;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ar[r] = L.anc[j * Q::PS + min(er[r], kPath - 1)];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = ti * kTile + 8 * (r / 4) + 4 * hf + (r % 4);
+                if (er[r] < dj && ar[r] == i) {
+                    L.gk[j * Q::PS + er[r]] = gkk[r];
+                    L.gq[j * Q::PS + er[r]] = gkq[r];
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- per (head, node): ratios, coefficients, the output weights' right-hand sides
+    for (int t = tid; t < grp * n; t += NT) {
+        const int hh = t / n, i = t % n;
+        const int di = L.depth[i];
+        const float bi = L.b[hh * NN + i];
+        float r = 1.0f;
+#pragma unroll
+        for (int e = kPath - 1; e >= 0; --e) {
+            const bool on = e < di - 1;
+            L.coefL[(hh * NN + i) * Q::PS + e] = on ? bi * r * L.gk[i * Q::PS + e] : 0.0f;
+            L.ysp[(hh * NN + i) * kPath + e] =
+                on ? r * L.gq[i * Q::PS + e] : (e == di - 1 ? L.gq[i * Q::PS + e] : 0.0f);
+            if (e < di) r *= L.a[hh * NN + max(L.anc[i * Q::PS + e], 0)];
+        }
+        L.gab[hh * NN + i] = make_float4(r, bi * r, bi, 0.0f);
+    }
+    __syncthreads();
+    // back substitution, deepest weight first, in place
+    for (int t = tid; t < grp * n; t += NT) {
+        const int hh = t / n, i = t % n;
+        const int di = L.depth[i];
+        int an_t[kPath];
+#pragma unroll
+        for (int e = 0; e < kPath; ++e) an_t[e] = max(L.anc[i * Q::PS + e], 0);
+        float *yr = L.ysp + (hh * NN + i) * kPath;
+        float y[kPath];
+#pragma unroll
+        for (int e = kPath - 1; e >= 0; --e) {
+            float acc = yr[e];
+#pragma unroll
+            for (int f = kPath - 1; f > e; --f) acc = fmaf(-y[f], L.coefL[(hh * NN + an_t[f]) * Q::PS + e], acc);
+            y[e] = e < di ? acc : 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < kPath; ++e) yr[e] = y[e];
+    }
+
+    // ---- value heads
+    auto head = [&](const float (&st)[KS][8], int hh, const uint4 (&vr)[V_PER]) {
+        __syncthreads();  // the previous head is done with the operator and the values
+        // this head's values, and its dense output operator (bf16 hi + lo)
+#pragma unroll
+        for (int u = 0; u < V_PER; ++u) {
+            const int c = tid + u * NT;
+            if (c < NN * (D / 8)) reinterpret_cast<uint4 *>(L.vst)[c] = vr[u];
+        }
+        for (int c = tid; c < nb * kTile * Q::MS / 2; c += NT) {
+            reinterpret_cast<uint32_t *>(L.mth)[c] = 0u;
+            reinterpret_cast<uint32_t *>(L.mtl)[c] = 0u;
+        }
+        __syncthreads();
+        for (int t = tid; t < n * kPath; t += NT) {
+            const int i = t / kPath, e = t % kPath;
+            if (e < L.depth[i]) {
+                const int col = L.anc[i * Q::PS + e];
+                const float y = L.ysp[(hh * NN + i) * kPath + e];
+                const __bf16 yh = static_cast<__bf16>(y);
+                L.mth[i * Q::MS + col] = __builtin_bit_cast(uint16_t, yh);
+                L.mtl[i * Q::MS + col] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(y - static_cast<float>(yh)));
+            }
+        }
+        __syncthreads();
+        // X_j for every block in one pass over the state (independent MFMA chains)
+        f32x16 X[NB];
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) X[jb] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            bf16x8 shi, slo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const __bf16 hb = static_cast<__bf16>(st[s][e]);
+                shi[e] = hb;
+                slo[e] = static_cast<__bf16>(st[s][e] - static_cast<float>(hb));
+            }
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb) {
+                if (jb < nb) {
+                    const bf16x8 Ak = frag_of(L.kq + (jb * kTile + l32) * Q::KQ, s, hf);
+                    X[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, shi, X[jb], 0, 0, 0);
+                    X[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, slo, X[jb], 0, 0, 0);
+                }
+            }
+        }
+        // R_j = b v - alpha X_j, kept as bf16 hi + lo in the k-order of the output products
+        // (k-step u of block j: accumulator slots 8u .. 8u+7)
+        const float4 *gab = L.gab + hh * NN;
+        bf16x8 rhi[NB][2], rlo[NB][2];
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = jb * kTile + 8 * (r / 4) + 4 * hf + (r % 4);
+                const float4 q4 = gab[min(i, n - 1)];
+                const float vi = bf2f(L.vst[min(i, NN - 1) * D + row]);
+                const float rv = i < n ? fmaf(-q4.y, X[jb][r], q4.z * vi) : 0.0f;
+                const __bf16 rb = static_cast<__bf16>(rv);
+                rhi[jb][r / 8][r % 8] = rb;
+                rlo[jb][r / 8][r % 8] = static_cast<__bf16>(rv - static_cast<float>(rb));
+            }
+        }
+        // O_t = gamma Y_t + sum_j MT_tj R_j, Y_t taken just before its outputs
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+            if (t < nb) {
+                f32x16 ay = {};
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    bf16x8 shi, slo;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const __bf16 hb = static_cast<__bf16>(st[s][e]);
+                        shi[e] = hb;
+                        slo[e] = static_cast<__bf16>(st[s][e] - static_cast<float>(hb));
+                    }
+                    const bf16x8 Aq = frag_of(L.kq + (NN + t * kTile + l32) * Q::KQ, s, hf);
+                    ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, shi, ay, 0, 0, 0);
+                    ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, slo, ay, 0, 0, 0);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = t * kTile + 8 * (r / 4) + 4 * hf + (r % 4);
+                    ay[r] = i < n ? gab[min(i, n - 1)].x * ay[r] : 0.0f;
+                }
+                const uint16_t *mh = L.mth + (t * kTile + l32) * Q::MS, *ml = L.mtl + (t * kTile + l32) * Q::MS;
+#pragma unroll
+                for (int jb = 0; jb < NB; ++jb) {
+                    if (jb < nb) {
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            const int c0 = jb * kTile + 16 * u + 4 * hf;
+                            const uint2 x0 = *reinterpret_cast<const uint2 *>(mh + c0);
+                            const uint2 x1 = *reinterpret_cast<const uint2 *>(mh + c0 + 8);
+                            const uint2 y0 = *reinterpret_cast<const uint2 *>(ml + c0);
+                            const uint2 y1 = *reinterpret_cast<const uint2 *>(ml + c0 + 8);
+                            const bf16x8 ahi = __builtin_bit_cast(bf16x8, make_uint4(x0.x, x0.y, x1.x, x1.y));
+                            const bf16x8 alo = __builtin_bit_cast(bf16x8, make_uint4(y0.x, y0.y, y1.x, y1.y));
+                            ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, rhi[jb][u], ay, 0, 0, 0);
+                            ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, rlo[jb][u], ay, 0, 0, 0);
+                            ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, rhi[jb][u], ay, 0, 0, 0);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = t * kTile + 8 * (r / 4) + 4 * hf + (r % 4);
+                    if (i < n) P.out[((size_t)(lo + i) * P.Hv + h0 + hh) * D + row] = ay[r];
+                }
+            }
+        }
+    };
+    if (grp > 1) {
+        load_state_frags<D>(s0 + (size_t)D * D, s_lane, sB);
+        fetch_v(1, vB);
+    }
+    head(sA, 0, vA);
+    if (grp > 2) {
+        load_state_frags<D>(s0 + (size_t)2 * D * D, s_lane, sA);
+        fetch_v(2, vA);
+    }
+    if (grp > 1) head(sB, 1, vB);
+    if (grp > 3) {
+        load_state_frags<D>(s0 + (size_t)3 * D * D, s_lane, sB);
+        fetch_v(3, vB);
+    }
+    if (grp > 2) head(sA, 2, vA);
+    if (grp > 3) head(sB, 3, vB);
+}
+
+// ===========================================================================
 // Replay on the matrix cores: one workgroup per (sequence, value head), D/32
 // waves, wave w owning state rows [32w, 32w+32).  Four workgroups fit a CU,
 // so one's table and state loads overlap another's arithmetic and stores.
@@ -1179,6 +1548,21 @@ hipError_t launch_verify_d(const Params &p, bool chain, hipStream_t s) {
             GDN_GROUP_CASE(3)
             GDN_GROUP_CASE(4)
 #undef GDN_GROUP_CASE
+        }
+    }
+    if (!chain && p.max_nodes <= 3 * kTile && grp <= kGroupMaxHeads) {
+        const dim3 grid(p.B * p.Hk), block(VG<D>::THREADS);
+        const bool two = p.max_nodes <= 2 * kTile;
+        switch (grp) {
+#define GDN_BLOCKS_CASE(G)                                                                                          \
+    case G:                                                                                                         \
+        return two ? launch_with_lds(verify_blocks_kernel<D, 2, G>, grid, block, btab_bytes<D, 2>(G), s, p) \
+                   : launch_with_lds(verify_blocks_kernel<D, 3, G>, grid, block, btab_bytes<D, 3>(G), s, p);
+            GDN_BLOCKS_CASE(1)
+            GDN_BLOCKS_CASE(2)
+            GDN_BLOCKS_CASE(3)
+            GDN_BLOCKS_CASE(4)
+#undef GDN_BLOCKS_CASE
         }
     }
     const int cap = chain ? kPath : p.max_nodes;
