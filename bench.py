@@ -10,6 +10,9 @@ layers).  Inputs and states are resident in HBM before timing starts.  To keep
 the 256 MB Infinity Cache from serving repeated reads, the timed loop rotates
 through R independent copies of the states and inputs (each layer of the
 workload is its own copy), so consecutive steps never touch the same bytes.
+A one-layer workload (R >= 4) persists on the copy half a rotation away from
+the one verify read: in a model, the other layers' verify calls separate a
+layer's verify from its persist.
 
 Prints ONE JSON line.  `value` = tree nodes verified per second per layer call
 (plan + verify + persist); `roofline` describes the dominant kernel, timed with
@@ -94,7 +97,7 @@ def main():
 
     layers = cfg.num_layers
     per_copy = vbytes + T * cfg.num_v_heads * cfg.head_dim * 4
-    rotate = args.rotate or max(1, int(np.ceil(512e6 / (per_copy * layers))))
+    rotate = args.rotate or max(4 if layers == 1 else 1, int(np.ceil(512e6 / (per_copy * layers))))
     copies = layers * rotate
     print("# config %s: B=%d T=%d layers=%d copies=%d (%.0f MB per layer copy)"
           % (cfg.name, cfg.num_seqs, T, layers, copies, per_copy / 1e6), file=sys.stderr, flush=True)
@@ -147,8 +150,12 @@ def main():
             G.gdn_tree_verify(dims, d["q"], d["k"], d["v"], d["a"], d["b"], d["cache"], slot_d, d["out"], ws)
             if events:
                 events[2 + l].record(stream)
+        # one-layer workloads persist on the copy half a rotation ahead: in a model every other
+        # layer's verify runs between a layer's verify and its persist, so its states are no
+        # longer cached, and no copy is read again within two steps of being written
+        rp = (r + rotate // 2) % rotate if layers == 1 else r
         for l in range(layers):
-            d = sets[r * layers + l]
+            d = sets[rp * layers + l]
             G.gdn_tree_persist(dims, d["k"], d["v"], d["a"], d["b"], acc_d, d["cache"], slot_d, ws)
             if events:
                 events[2 + layers + l].record(stream)

@@ -124,3 +124,37 @@ def test_chain_head_groups(d_, grp):
             assert np.array_equal(fin_h[s], S0[s])
         else:
             assert slice_rel_err(fin_h[s].reshape(hv, -1), st.reshape(hv, -1)) <= TOL, s
+
+
+@pytest.mark.parametrize("d_", [64, 128])
+@pytest.mark.parametrize("n_nodes", [40, 65, 96])
+def test_relabelled_multi_block_trees(d_, n_nodes):
+    """Trees of 33-96 nodes with shuffled labels, so ancestors sit in later node
+    blocks than their descendants; outputs checked against the oracle."""
+    G = require_gpu()
+    rng = np.random.default_rng(3000 + n_nodes + d_)
+    hk, hv = 2, 6
+    trees = []
+    for _ in range(3):
+        par = W.random_tree(rng, n_nodes, 16)
+        trees.append(W.relabel(par, rng.permutation(n_nodes)))
+    B = len(trees)
+    cu = W.cu_from_trees(trees)
+    T = int(cu[-1])
+    inp = _inputs(rng, T, hk, hv, d_)
+    S0 = (0.3 * rng.standard_normal((B, hv, d_, d_))).astype(np.float32)
+    slots = np.array([1, 2, 0], np.int32)
+    cache = np.zeros((B, hv, d_, d_), np.float32)
+    for s in range(B):
+        cache[slots[s]] = S0[s]
+    dims = G.make_dims(B, T, n_nodes, hk, hv, d_, B, G.GDN_BF16)
+    ws = G.new_workspace(dims)
+    dev = {k_: to_dev(v_) for k_, v_ in inp.items()}
+    out = torch.full((T, hv, d_), float("nan"), device="cuda")
+    print("relabelled multi-block d=%d n=%d" % (d_, n_nodes), flush=True)
+    G.gdn_tree_plan(dims, to_dev(np.concatenate(trees).astype(np.int32)), to_dev(cu.astype(np.int32)),
+                    to_dev(slots), ws)
+    G.gdn_tree_verify(dims, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], to_dev(cache), to_dev(slots), out, ws)
+    rc, bad, code = G.gdn_tree_status(ws)
+    assert rc == 0, (rc, bad, code)
+    _check_out(out.cpu().numpy(), oracle.verify_batch(trees, cu, inp, S0), cu, hv)
