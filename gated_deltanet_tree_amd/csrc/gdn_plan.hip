@@ -1,5 +1,5 @@
 // gdn_plan.hip -- device-side validation and traversal metadata of the draft
-// trees (one workgroup of 256 threads per sequence, one thread per node).
+// trees (one workgroup per sequence, one thread per node).
 //
 // The trees arrive in parent-pointer form from DDTree's tree builder
 // (GreenGames page, "From autoregressive to DDTree"), depth bounded by the
@@ -12,10 +12,13 @@
 namespace gdn {
 namespace {
 
-constexpr int kPlanThreads = GDN_MAX_NODES;  // one thread per node
-constexpr int kPlanDupPer = 2;               // other sequences checked per thread from registers
+constexpr int kPlanDupPer = 2;  // other sequences checked per thread from registers
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params P) {
+// NT threads, one per node: NT = 64 (a single wave, whose barriers cost nothing)
+// when every tree fits, else NT = GDN_MAX_NODES
+template <int NT>
+__global__ __launch_bounds__(NT) void plan_kernel(Params P) {
+    constexpr int kPlanThreads = NT;
     __shared__ int s_par[kPlanThreads];
     __shared__ int s_size[kPlanThreads];
     __shared__ int s_nchild[kPlanThreads];
@@ -184,7 +187,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Params P) {
 
 hipError_t launch_plan(const Params &p, hipStream_t s) {
     const int grid = p.B > 0 ? p.B : 1;
-    hipLaunchKernelGGL(plan_kernel, dim3(grid), dim3(kPlanThreads), 0, s, p);
+    if (p.max_nodes <= 64)
+        hipLaunchKernelGGL(plan_kernel<64>, dim3(grid), dim3(64), 0, s, p);
+    else
+        hipLaunchKernelGGL(plan_kernel<GDN_MAX_NODES>, dim3(grid), dim3(GDN_MAX_NODES), 0, s, p);
     return hipGetLastError();
 }
 
