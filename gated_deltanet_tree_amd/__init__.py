@@ -12,7 +12,7 @@ Typical decode step (all on one stream)::
     gdn_tree_plan(dims, parent, cu_nodes, slot_idx, ws)
     for layer in layers:
         gdn_tree_verify(dims, q, k, v, a, b, cache[layer], slot_idx, out, ws)
-    # ... acceptance ...
+    gdn_tree_accept(dims, logits, draft_token, accepted, accept_len, next_token, ws)
     for layer in layers:
         gdn_tree_persist(dims, k, v, a, b, accepted, cache[layer], slot_idx, ws)
 """
@@ -35,7 +35,7 @@ SEQ_STATUS = {0: "OK", 1: "BAD_NODES", 2: "BAD_SLOT", 3: "DUP_SLOT", 4: "BAD_PAR
               5: "CYCLE_OR_DEPTH", 6: "BAD_ACCEPT"}
 
 EXPORTS = ["gdn_workspace_bytes", "gdn_tree_plan", "gdn_tree_verify", "gdn_tree_persist",
-           "gdn_chain_verify", "gdn_tree_read_metadata", "gdn_tree_status", "gdn_strerror"]
+           "gdn_chain_verify", "gdn_tree_accept", "gdn_tree_read_metadata", "gdn_tree_status", "gdn_strerror"]
 
 
 class GdnError(RuntimeError):
@@ -80,12 +80,13 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_tree_verify.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdn_tree_persist.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdn_chain_verify.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdn_tree_accept.argtypes = [dp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdn_tree_read_metadata.argtypes = [dp, vp, sz, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_tree_status.argtypes = [vp, sz, vp, ip, ip]
     lib.gdn_strerror.argtypes = [i32]
     lib.gdn_strerror.restype = ctypes.c_char_p
     for f in ("gdn_tree_plan", "gdn_tree_verify", "gdn_tree_persist", "gdn_chain_verify",
-              "gdn_tree_read_metadata", "gdn_tree_status"):
+              "gdn_tree_accept", "gdn_tree_read_metadata", "gdn_tree_status"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -185,6 +186,22 @@ def gdn_chain_verify(dims, cu_nodes, q, k, v, a, b, state_cache, slot_idx, out=N
         _ptr(final_state, "final_state", torch.float32, B * Hv * D * D, allow_none=True),
         _ptr(ws, "ws", torch.uint8, allow_none=True), 0 if ws is None else ws.numel(), _stream(stream)),
         "gdn_chain_verify")
+
+
+def gdn_tree_accept(dims, logits, draft_token, accepted_node, accept_len, next_token, ws, target_token=None,
+                    stream=None):
+    """Greedy acceptance: logits fp32 [T][vocab]; writes accepted_node, accept_len,
+    next_token (int32 [B]) and, if given, target_token (int32 [T])."""
+    T, B = dims.total_nodes, dims.num_seqs
+    if logits is None or logits.dim() != 2 or logits.shape[0] != T:
+        raise ValueError("logits must be a [T, vocab] tensor")
+    vocab = int(logits.shape[1])
+    _check(load_library().gdn_tree_accept(
+        ctypes.byref(dims), _ptr(logits, "logits", torch.float32, T * vocab), vocab,
+        _ptr(draft_token, "draft_token", torch.int32, T), _ptr(accepted_node, "accepted_node", torch.int32, B),
+        _ptr(accept_len, "accept_len", torch.int32, B), _ptr(next_token, "next_token", torch.int32, B),
+        _ptr(target_token, "target_token", torch.int32, T, allow_none=True),
+        _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)), "gdn_tree_accept")
 
 
 def gdn_tree_read_metadata(dims, ws, depth=None, order=None, action=None, path=None, path_len=None,

@@ -3,6 +3,7 @@
 // except gdn_tree_status.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cstdlib>
 #include <cstring>
@@ -178,6 +179,34 @@ int gdn_chain_verify(const gdn_dims *dims, const int32_t *cu_nodes, const void *
     // longer chains (e.g. prefill) run the sequential recurrence
     if (fast) return launched(gdn::launch_chain_verify_fast(p, as_stream(stream)));
     return launched(gdn::launch_chain_verify_recurrent(p, dims->qkv_dtype, as_stream(stream)));
+}
+
+int gdn_tree_accept(const gdn_dims *dims, const float *logits, int32_t vocab, const int32_t *draft_token,
+                    int32_t *accepted_node, int32_t *accept_len, int32_t *next_token, int32_t *target_token,
+                    void *ws, size_t ws_bytes, void *stream) {
+    if (!dims) return GDN_ERR_NULL;
+    if (!dims_ok(dims, GDN_MAX_NODES)) return GDN_ERR_SHAPE;
+    if (vocab < 1) return GDN_ERR_SHAPE;
+    if ((long long)dims->total_nodes * gdn::kAcceptChunks > INT_MAX) return GDN_ERR_SHAPE;
+    if (!ws) return GDN_ERR_NULL;
+    if (dims->total_nodes > 0 && (!logits || !draft_token)) return GDN_ERR_NULL;
+    if (dims->num_seqs > 0 && (!accepted_node || !accept_len || !next_token)) return GDN_ERR_NULL;
+    if (ws_bytes < gdn_workspace_bytes(dims)) return GDN_ERR_WORKSPACE;
+    Params p = base_params(dims);
+    p.logits = logits;
+    p.vocab = vocab;
+    p.draft_token = draft_token;
+    p.accepted_out = accepted_node;
+    p.accept_len_out = accept_len;
+    p.next_token_out = next_token;
+    p.target_out = target_token;
+    // a row is cut into up to kAcceptChunks slices of >= 8192 entries (a multiple
+    // of 4, so 16-byte loads stay inside their slice)
+    p.chunks = std::min(gdn::kAcceptChunks, std::max(1, (vocab + 8191) / 8192));
+    p.chunk_len = ((vocab + p.chunks - 1) / p.chunks + 3) & ~3;
+    p.ws = gdn::ws_ptrs(ws, p.B, p.T, p.Hv);
+    p.has_ws = 1;
+    return launched(gdn::launch_accept(p, as_stream(stream)));
 }
 
 int gdn_tree_read_metadata(const gdn_dims *dims, const void *ws, size_t ws_bytes, int32_t *depth,

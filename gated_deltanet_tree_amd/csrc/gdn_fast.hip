@@ -30,8 +30,6 @@ constexpr int kPath = GDN_MAX_DEPTH;  // max ancestors per node (incl. itself)
 constexpr int kFastMaxNodes = 96;     // largest tree the MFMA verify takes (3 node blocks)
 
 __device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float qnan_f() { return __int_as_float(0x7fc00000); }
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 

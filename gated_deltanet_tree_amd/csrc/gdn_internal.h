@@ -17,12 +17,13 @@ constexpr int kSeqInfoInts = 8;          // node offset, node count, verdict, sl
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 constexpr int kCoefFloats = 20;         // per (node, value head): 16 path weights, gamma, alpha, b, depth
+constexpr int kAcceptChunks = 8;        // most slices one logits row is split into for the argmax
 
 // Byte offsets of the workspace regions (each 256-byte aligned).  The
 // per-(node, head) coefficient records come last, so the other offsets do
 // not depend on the head count.
 struct WsLayout {
-    size_t header, seq_status, seq_info, depth, order, action, nodepath, path, path_len, coef, total;
+    size_t header, seq_status, seq_info, depth, order, action, nodepath, path, path_len, amax, coef, total;
 };
 
 __host__ __device__ inline WsLayout ws_layout(int B, int T, int Hv = 0) {
@@ -38,6 +39,7 @@ __host__ __device__ inline WsLayout ws_layout(int B, int T, int Hv = 0) {
     L.nodepath = off;   off += align256(t * GDN_MAX_DEPTH * 4);
     L.path = off;       off += align256(b * GDN_MAX_DEPTH * 4);
     L.path_len = off;   off += align256(b * 4);
+    L.amax = off;       off += align256(t * kAcceptChunks * 8);
     L.coef = off;       off += align256(t * (size_t)(Hv > 0 ? Hv : 0) * kCoefFloats * 4);
     L.total = off;
     return L;
@@ -45,6 +47,7 @@ __host__ __device__ inline WsLayout ws_layout(int B, int T, int Hv = 0) {
 
 struct WsPtrs {
     int32_t *header, *seq_status, *seq_info, *depth, *order, *action, *nodepath, *path, *path_len;
+    int2 *amax;  // per (node, row slice): largest logit (bits) and its index
     float *coef;
 };
 
@@ -61,6 +64,7 @@ inline WsPtrs ws_ptrs(void *ws, int B, int T, int Hv = 0) {
     p.nodepath = reinterpret_cast<int32_t *>(base + L.nodepath);
     p.path = reinterpret_cast<int32_t *>(base + L.path);
     p.path_len = reinterpret_cast<int32_t *>(base + L.path_len);
+    p.amax = reinterpret_cast<int2 *>(base + L.amax);
     p.coef = reinterpret_cast<float *>(base + L.coef);
     return p;
 }
@@ -82,6 +86,11 @@ struct Params {
     float *final_state;          // chain
     WsPtrs ws;
     int has_ws;
+    // greedy acceptance
+    const float *logits;         // [T][vocab]
+    const int32_t *draft_token;  // [T]
+    int32_t *accepted_out, *accept_len_out, *next_token_out, *target_out;
+    int vocab, chunks, chunk_len;
 };
 
 // ---- kernel launchers (defined in the .hip files) --------------------------
@@ -95,6 +104,8 @@ bool fast_tree_supported(int D, int dtype, int max_nodes);
 hipError_t launch_tree_verify_fast(const Params &p, hipStream_t s);
 hipError_t launch_chain_verify_fast(const Params &p, hipStream_t s);
 hipError_t launch_persist_fast(const Params &p, hipStream_t s);
+// greedy acceptance over the verify logits
+hipError_t launch_accept(const Params &p, hipStream_t s);
 
 // Largest LDS stack the heavy-last preorder can need for trees of n nodes:
 // k nested pushes need a subtree of at least 2^(k+1) - 1 nodes.

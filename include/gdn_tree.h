@@ -184,6 +184,32 @@ int gdn_chain_verify(const gdn_dims *dims, const int32_t *cu_nodes, const void *
                      float *final_state, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * gdn_tree_accept -- greedy (temperature-0) acceptance of each planned tree
+ * against the target's verify logits.  Row n of `logits` (fp32 [T][vocab],
+ * one row per node, the verify logits buffer of the GreenGames page, "Key
+ * wins") is the target's prediction for the token after node n; the target's
+ * token there is the first index of the row's largest entry, a NaN counting
+ * as largest (numpy argmax order; +0 equals -0).  From the sequence's root
+ * (the smallest-id root of a forest) the walk moves to the smallest-id child
+ * c with draft_token[c] equal to the target's token after the current node,
+ * until no child qualifies.  Outputs per sequence: accepted_node[b] (local id
+ * of the stop node; feed it to gdn_tree_persist), accept_len[b] (its depth,
+ * root = 1) and next_token[b] (the target's token after it).  A sequence the
+ * plan rejected, or an empty one, gets -1, 0, -1.  target_token (int32 [T],
+ * may be NULL) receives every row's argmax.  Draft tokens outside [0, vocab)
+ * never match; the roots' draft tokens are not read.  Verification at
+ * temperature 0 must reproduce plain greedy decoding token for token
+ * (dflash-caddtree-integrations README, "The shared method"; greedy-only
+ * verify, GreenGames "What comes next").  `ws` comes from gdn_tree_plan with
+ * the same dims on the same stream; the call reuses a per-node region of it.
+ * logits may be any 4-byte-aligned address; 16-byte alignment and vocab % 4
+ * == 0 take the vector loads.
+ */
+int gdn_tree_accept(const gdn_dims *dims, const float *logits, int32_t vocab, const int32_t *draft_token,
+                    int32_t *accepted_node, int32_t *accept_len, int32_t *next_token, int32_t *target_token,
+                    void *ws, size_t ws_bytes, void *stream);
+
+/*
  * gdn_tree_read_metadata -- device-to-device copies of what the plan (and the
  * last persist) stored: depth [T], order [T] (node ids by visit position,
  * offset by cu_nodes), action [T], path [B][GDN_MAX_DEPTH] (root first,

@@ -50,3 +50,16 @@ def test_host_only_calls(lib):
                              ctypes.c_void_p(1), 1 << 20, None)
     assert rc == -2
     assert lib.gdn_tree_status(None, 0, None, None, None) == -1
+
+
+def test_accept_host_checks(lib):
+    import gated_deltanet_tree_amd as G
+    dims = G.make_dims(2, 10, 8, 1, 1, 16, 2, G.GDN_F32)
+    one = ctypes.c_void_p(16)
+    n = G.workspace_bytes(dims)
+    assert lib.gdn_tree_accept(None, one, 10, one, one, one, one, None, one, n, None) == -1
+    assert lib.gdn_tree_accept(ctypes.byref(dims), one, 0, one, one, one, one, None, one, n, None) == -2
+    assert lib.gdn_tree_accept(ctypes.byref(dims), None, 10, one, one, one, one, None, one, n, None) == -1
+    assert lib.gdn_tree_accept(ctypes.byref(dims), one, 10, one, None, one, one, None, one, n, None) == -1
+    assert lib.gdn_tree_accept(ctypes.byref(dims), one, 10, one, one, one, one, None, None, n, None) == -1
+    assert lib.gdn_tree_accept(ctypes.byref(dims), one, 10, one, one, one, one, None, one, n - 1, None) == -4
