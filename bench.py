@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0, help="independent copies (default: >= 512 MB in flight)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-accept", action="store_true", help="skip the greedy-acceptance measurement")
+    ap.add_argument("--accept-steps", type=int, default=50)
     ap.add_argument("--path", choices=["auto", "recurrent"], default="auto",
                     help="recurrent: run the per-node recurrent kernels on every call (GDN_KERNEL_PATH)")
     return ap.parse_args()
@@ -235,18 +237,65 @@ def main():
                        "verify_gbs": vbytes / t_ver / 1e9, "persist_gbs": pbytes / t_per / 1e9},
         "roofline": roof,
     }
+    if not args.no_accept:
+        result["accept"] = bench_accept(G, W, cfg, trees, dims, parent_d, cu_d, slot_d, args.accept_steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, trees, cu, acc, args.cpu_seconds)
     print(json.dumps(result))
 
 
-def kernel_source_digest() -> str:
-    """Hash of the library sources with comments and whitespace removed: a
+def bench_accept(G, W, cfg, trees, dims, parent_d, cu_d, slot_d, steps):
+    """Greedy acceptance over the step's verify logits (one fp32 row of the
+    vocabulary per node), timed per call with HIP events on its stream.  Not
+    part of the step: it runs once per decode step after the last layer."""
+    import torch
+    from workloads import draft
+    T = dims.total_nodes
+    tok = draft.make_draft_tokens(cfg, trees)
+    logits = torch.from_numpy(draft.make_verify_logits(cfg, trees, tok)).cuda()
+    tok_d = torch.from_numpy(tok).cuda()
+    B = cfg.num_seqs
+    acc, alen, nxt = (torch.empty(B, dtype=torch.int32, device="cuda") for _ in range(3))
+    ws = G.new_workspace(dims)
+    G.gdn_tree_plan(dims, parent_d, cu_d, slot_d, ws)
+    stream = torch.cuda.current_stream()
+    for _ in range(5):
+        G.gdn_tree_accept(dims, logits, tok_d, acc, alen, nxt, ws)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        e0.record(stream)
+        G.gdn_tree_accept(dims, logits, tok_d, acc, alen, nxt, ws)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    vocab = int(logits.shape[1])
+    # algorithmic bytes: every logit once, the draft tokens, the plan's depth and
+    # path rows read by the walk, three int32 outputs per sequence
+    nbytes = T * vocab * 4 + T * 4 + T * (4 + 4) + B * 12
+    gbs = nbytes / t / 1e9
+    return {"vocab": vocab, "nodes": T, "call_us": t * 1e6, "bytes": nbytes,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("accept", cfg.name)},
+            "mean_accept_len": float(alen.float().mean().item())}
+
+
+# the sources each measured kernel is built from: counters recorded for one of
+# them stay valid while these files keep their code
+KERNEL_SOURCES = {
+    "tree_verify": ("gdn_fast.hip", "gdn_internal.h"),
+    "persist": ("gdn_fast.hip", "gdn_internal.h"),
+    "accept": ("gdn_accept.hip", "gdn_internal.h"),
+}
+
+
+def kernel_source_digest(kernel: str) -> str:
+    """Hash of a kernel's sources with comments and whitespace removed: a
     change of code invalidates recorded counters, a change of comments not."""
     import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_deltanet_tree_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(KERNEL_SOURCES[kernel]):
         with open(os.path.join(csrc, name)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -258,14 +307,14 @@ def kernel_source_digest() -> str:
 
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when the kernels changed since it was taken."""
+    None when the kernel's sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     ent = rec.get(workload, {}).get(kernel)
-    if not ent or ent.get("source_digest") != kernel_source_digest():
+    if not ent or ent.get("source_digest") != kernel_source_digest(kernel):
         return None
     return ent["bytes_per_launch"]
 

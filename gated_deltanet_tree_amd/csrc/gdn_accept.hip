@@ -156,15 +156,18 @@ __global__ __launch_bounds__(kArgThreads) void argmax_kernel(Params P) {
 }
 
 // argmax of a whole row from its slices (slices past the row end hold
-// (-inf, INT_MAX), which never wins)
+// (-inf, INT_MAX), which never wins); all slice loads are issued before the
+// first comparison
 __device__ __forceinline__ int row_argmax(const Params &P, int row) {
     const int2 *pr = P.ws.amax + (size_t)row * kAcceptChunks;
-    float bv = -INFINITY;
-    int bi = INT_MAX;
-    for (int c = 0; c < P.chunks; ++c) {
-        const int2 e = pr[c];
-        take(__int_as_float(e.x), e.y, bv, bi);
-    }
+    int2 e[kAcceptChunks];
+#pragma unroll
+    for (int c = 0; c < kAcceptChunks; ++c) e[c] = c < P.chunks ? pr[c] : make_int2(0, INT_MAX);
+    float bv = __int_as_float(e[0].x);
+    int bi = e[0].y;
+#pragma unroll
+    for (int c = 1; c < kAcceptChunks; ++c)
+        if (c < P.chunks) take(__int_as_float(e[c].x), e[c].y, bv, bi);
     return bi;
 }
 
@@ -193,18 +196,37 @@ __global__ __launch_bounds__(64) void walk_kernel(Params P) {
         return;
     }
     const int lo = info.x, n = info.y;
-    // node t = lane + 64 k: its parent (from the plan's path rows) and draft token
+    // node t = lane + 64 k: its parent (from the plan's path row, fetched whole
+    // next to its depth) and draft token
     int par[kNodesPerLane], tok[kNodesPerLane];
 #pragma unroll
     for (int k = 0; k < kNodesPerLane; ++k) {
         const int t = lane + 64 * k;
         par[k] = -2;
         tok[k] = 0;
-        if (t < n) {
-            const int d = P.ws.depth[lo + t];
-            par[k] = d >= 2 ? P.ws.nodepath[(size_t)(lo + t) * GDN_MAX_DEPTH + d - 2] : -1;
-            tok[k] = P.draft_token[lo + t];
-            s_tgt[t] = row_argmax(P, lo + t);
+        if (64 * k < n) {  // uniform: the whole wave takes part in this group
+            const int tt = t < n ? t : n - 1;
+            const int4 *np = reinterpret_cast<const int4 *>(P.ws.nodepath + (size_t)(lo + tt) * GDN_MAX_DEPTH);
+            int4 row[GDN_MAX_DEPTH / 4];
+#pragma unroll
+            for (int q = 0; q < GDN_MAX_DEPTH / 4; ++q) row[q] = np[q];
+            const int d = P.ws.depth[lo + tt];
+            const int tk = P.draft_token[lo + tt];
+            const int tg = row_argmax(P, lo + tt);
+            // the parent is path entry d - 2 (root first); a root has none
+            int pp = -1;
+#pragma unroll
+            for (int q = 0; q < GDN_MAX_DEPTH / 4; ++q) {
+                pp = (4 * q + 0 == d - 2) ? row[q].x : pp;
+                pp = (4 * q + 1 == d - 2) ? row[q].y : pp;
+                pp = (4 * q + 2 == d - 2) ? row[q].z : pp;
+                pp = (4 * q + 3 == d - 2) ? row[q].w : pp;
+            }
+            if (t < n) {
+                par[k] = pp;
+                tok[k] = tk;
+                s_tgt[t] = tg;
+            }
         }
     }
     __syncthreads();

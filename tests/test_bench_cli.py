@@ -18,5 +18,7 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 def test_source_digest_ignores_comments_only():
     sys.path.insert(0, ROOT)
     import bench
-    d = bench.kernel_source_digest()
-    assert len(d) == 16 and d == bench.kernel_source_digest()
+    for kernel in bench.KERNEL_SOURCES:
+        d = bench.kernel_source_digest(kernel)
+        assert len(d) == 16 and d == bench.kernel_source_digest(kernel)
+    assert bench.kernel_source_digest("persist") != bench.kernel_source_digest("accept")
