@@ -18,7 +18,14 @@ Recipe.
   token of the node's rank-r child with probability ``match[r-1]``, else a
   uniform token that no child carries.  Leaves always get a uniform token.
 
-Streams: numpy PCG64 from ``SeedSequence(cfg.seed, spawn_key=(4|5, seq))``.
+  Draft logits (the drafter's scores over the vocabulary at each of the
+  DRAFT_LEVELS = 15 drafted positions of a 16-token block, GreenGames
+  "Prefill"): every row N(0, 1) in float32, plus ``width`` distinct uniform
+  tokens planted at 20 + z with z ~ N(0, 2^2) -- the per-level candidate
+  logits of the tree recipe, lifted far enough above the noise that the
+  drafter's mass sits on them.  Root tokens: uniform in [0, V).
+
+Streams: numpy PCG64 from ``SeedSequence(cfg.seed, spawn_key=(4|5|6|7, seq))``.
 """
 from __future__ import annotations
 
@@ -28,7 +35,8 @@ from .configs import Config
 from .inputs import _rng
 
 VOCAB = 248320
-_DRAFT, _LOGITS = 4, 5
+DRAFT_LEVELS = 15
+_DRAFT, _LOGITS, _DLOGITS, _ROOT = 4, 5, 6, 7
 MATCH = (0.7, 0.1, 0.05, 0.03)
 
 
@@ -104,3 +112,22 @@ def make_verify_logits(cfg: Config, trees: list[np.ndarray], draft_tokens: np.nd
             logits[lo + u, pick] = planted
         lo += n
     return logits
+
+
+def make_draft_logits(cfg: Config, vocab: int = VOCAB, levels: int = DRAFT_LEVELS, width: int | None = None) -> np.ndarray:
+    """float32 [B][levels][vocab]: the drafter's logits per drafted position."""
+    width = cfg.tree[2] if width is None and cfg.tree[0] == "ddtree" else (width or 4)
+    out = np.empty((cfg.num_seqs, levels, vocab), dtype=np.float32)
+    for s in range(cfg.num_seqs):
+        rng = _rng(cfg, _DLOGITS, s)
+        out[s] = rng.standard_normal((levels, vocab), dtype=np.float32)
+        for lvl in range(levels):
+            w = min(width, vocab)
+            toks = rng.choice(vocab, size=w, replace=False)
+            out[s, lvl, toks] = (20.0 + rng.normal(0.0, 2.0, size=w)).astype(np.float32)
+    return out
+
+
+def make_root_tokens(cfg: Config, vocab: int = VOCAB) -> np.ndarray:
+    """int32 [B]: each sequence's last committed token (the tree roots)."""
+    return _rng(cfg, _ROOT, 0).integers(0, vocab, size=cfg.num_seqs).astype(np.int32)
