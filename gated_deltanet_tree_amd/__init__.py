@@ -29,13 +29,15 @@ LIB_PATH = os.path.join(_HERE, "libgdn_tree.so")
 GDN_MAX_DEPTH = 16
 GDN_MAX_NODES = 256
 GDN_MAX_CHAIN = 65536
+GDN_MAX_DRAFT_WIDTH = 16
 GDN_BF16, GDN_F32 = 0, 1
 
 SEQ_STATUS = {0: "OK", 1: "BAD_NODES", 2: "BAD_SLOT", 3: "DUP_SLOT", 4: "BAD_PARENT",
               5: "CYCLE_OR_DEPTH", 6: "BAD_ACCEPT"}
 
 EXPORTS = ["gdn_workspace_bytes", "gdn_tree_plan", "gdn_tree_verify", "gdn_tree_persist",
-           "gdn_chain_verify", "gdn_tree_accept", "gdn_tree_read_metadata", "gdn_tree_status", "gdn_strerror"]
+           "gdn_chain_verify", "gdn_tree_accept", "gdn_draft_topk", "gdn_ddtree_nodes", "gdn_ddtree_build",
+           "gdn_tree_read_metadata", "gdn_tree_status", "gdn_strerror"]
 
 
 class GdnError(RuntimeError):
@@ -81,12 +83,18 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_tree_persist.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdn_chain_verify.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdn_tree_accept.argtypes = [dp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, sz, vp]
+    i32c = ctypes.c_int32
+    lib.gdn_draft_topk.argtypes = [i32c, i32c, i32c, vp, vp, vp, vp]
+    lib.gdn_ddtree_nodes.argtypes = [i32c, i32c, i32c, i32c]
+    lib.gdn_ddtree_nodes.restype = i32c
+    lib.gdn_ddtree_build.argtypes = [i32c, i32c, i32c, i32c, i32c, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_tree_read_metadata.argtypes = [dp, vp, sz, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_tree_status.argtypes = [vp, sz, vp, ip, ip]
     lib.gdn_strerror.argtypes = [i32]
     lib.gdn_strerror.restype = ctypes.c_char_p
     for f in ("gdn_tree_plan", "gdn_tree_verify", "gdn_tree_persist", "gdn_chain_verify",
-              "gdn_tree_accept", "gdn_tree_read_metadata", "gdn_tree_status"):
+              "gdn_tree_accept", "gdn_draft_topk", "gdn_ddtree_build", "gdn_tree_read_metadata",
+              "gdn_tree_status"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -202,6 +210,36 @@ def gdn_tree_accept(dims, logits, draft_token, accepted_node, accept_len, next_t
         _ptr(accept_len, "accept_len", torch.int32, B), _ptr(next_token, "next_token", torch.int32, B),
         _ptr(target_token, "target_token", torch.int32, T, allow_none=True),
         _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)), "gdn_tree_accept")
+
+
+def gdn_draft_topk(logits, width, tokens, logp, stream=None):
+    """logits fp32 [rows, vocab] -> tokens int32 [rows, width], logp fp32 [rows, width]."""
+    if logits is None or logits.dim() != 2:
+        raise ValueError("logits must be a [rows, vocab] tensor")
+    rows, vocab = int(logits.shape[0]), int(logits.shape[1])
+    _check(load_library().gdn_draft_topk(
+        rows, vocab, int(width), _ptr(logits, "logits", torch.float32, rows * vocab),
+        _ptr(tokens, "tokens", torch.int32, rows * width), _ptr(logp, "logp", torch.float32, rows * width),
+        _stream(stream)), "gdn_draft_topk")
+
+
+def ddtree_nodes(levels, width, budget, max_depth=GDN_MAX_DEPTH) -> int:
+    """Nodes of every tree gdn_ddtree_build grows (0 for invalid arguments)."""
+    return int(load_library().gdn_ddtree_nodes(int(levels), int(width), int(budget), int(max_depth)))
+
+
+def gdn_ddtree_build(root_token, tokens, logp, budget, parent, node_token, cu_nodes, max_depth=GDN_MAX_DEPTH,
+                     stream=None):
+    """tokens int32 / logp fp32 [B, levels, width] -> parent, node_token int32 [B*N], cu_nodes [B+1]."""
+    if tokens is None or tokens.dim() != 3:
+        raise ValueError("tokens must be a [B, levels, width] tensor")
+    B, L, Wd = (int(x) for x in tokens.shape)
+    n = ddtree_nodes(L, Wd, budget, max_depth)
+    _check(load_library().gdn_ddtree_build(
+        B, L, Wd, int(budget), int(max_depth), _ptr(root_token, "root_token", torch.int32, B, allow_none=True),
+        _ptr(tokens, "tokens", torch.int32, B * L * Wd), _ptr(logp, "logp", torch.float32, B * L * Wd),
+        _ptr(parent, "parent", torch.int32, B * n), _ptr(node_token, "node_token", torch.int32, B * n),
+        _ptr(cu_nodes, "cu_nodes", torch.int32, B + 1), _stream(stream)), "gdn_ddtree_build")
 
 
 def gdn_tree_read_metadata(dims, ws, depth=None, order=None, action=None, path=None, path_len=None,

@@ -209,6 +209,38 @@ int gdn_tree_accept(const gdn_dims *dims, const float *logits, int32_t vocab, co
     return launched(gdn::launch_accept(p, as_stream(stream)));
 }
 
+int gdn_draft_topk(int32_t rows, int32_t vocab, int32_t width, const float *logits, int32_t *tokens,
+                   float *logp, void *stream) {
+    if (rows < 0 || vocab < 1 || width < 1 || width > GDN_MAX_DRAFT_WIDTH) return GDN_ERR_SHAPE;
+    if (rows == 0) return GDN_OK;
+    if (!logits || !tokens || !logp) return GDN_ERR_NULL;
+    return launched(gdn::launch_draft_topk(rows, vocab, width, logits, tokens, logp, as_stream(stream)));
+}
+
+int32_t gdn_ddtree_nodes(int32_t levels, int32_t width, int32_t budget, int32_t max_depth) {
+    if (levels < 1 || width < 1 || width > GDN_MAX_DRAFT_WIDTH || budget < 0 || max_depth < 1 ||
+        max_depth > GDN_MAX_DEPTH)
+        return 0;
+    return gdn::ddtree_nodes(levels, width, budget, max_depth);
+}
+
+int gdn_ddtree_build(int32_t num_seqs, int32_t levels, int32_t width, int32_t budget, int32_t max_depth,
+                     const int32_t *root_token, const int32_t *tokens, const float *logp, int32_t *parent,
+                     int32_t *node_token, int32_t *cu_nodes, void *stream) {
+    const int32_t n = gdn_ddtree_nodes(levels, width, budget, max_depth);
+    if (num_seqs < 0 || n < 1 || n > GDN_MAX_NODES) return GDN_ERR_SHAPE;
+    if (!cu_nodes) return GDN_ERR_NULL;
+    if (num_seqs > 0 && (!tokens || !logp || !parent || !node_token)) return GDN_ERR_NULL;
+    if ((long long)num_seqs * n > INT_MAX) return GDN_ERR_SHAPE;
+    if (num_seqs == 0) {  // cu_nodes = {0}
+        const int32_t zero = 0;
+        return hipMemcpyAsync(cu_nodes, &zero, 4, hipMemcpyHostToDevice, as_stream(stream)) == hipSuccess
+                   ? GDN_OK : GDN_ERR_LAUNCH;
+    }
+    return launched(gdn::launch_ddtree_build(num_seqs, levels, width, budget, max_depth, root_token, tokens, logp,
+                                             parent, node_token, cu_nodes, as_stream(stream)));
+}
+
 int gdn_tree_read_metadata(const gdn_dims *dims, const void *ws, size_t ws_bytes, int32_t *depth,
                            int32_t *order, int32_t *action, int32_t *path, int32_t *path_len,
                            int32_t *seq_status, void *stream) {

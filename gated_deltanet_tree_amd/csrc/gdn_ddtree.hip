@@ -1,0 +1,391 @@
+// gdn_ddtree.hip -- the drafter's top-k candidates and the DDTree builder.
+//
+// The drafter scores the whole vocabulary at each position of its block; the
+// tree builder keeps each position's W best candidates in descending order
+// (rank 1 first: the GreenGames page, "Key wins", traces a slowdown to that
+// order being reversed, which put the worst candidate at the tree root) with
+// their log-probabilities, pre-seeds the rank-1 chain ("From autoregressive to
+// DDTree") and grows the rest of the budget best first by path score.
+//
+//   topk_kernel   one workgroup per row: streams the row once (16-byte loads
+//                 when the layout allows), keeping per thread its WT best
+//                 entries in argmax order (a NaN counts as largest, equal
+//                 values keep the smaller id) and a running (max, sum of
+//                 exp(x - max)) for the log-softmax; the waves merge their
+//                 lists by repeated wave-wide extraction.  HBM-bound.
+//   build_kernel  one wave per sequence: the chain, then one candidate per
+//                 node (its next unused rank) and a wave-wide extraction of
+//                 the best candidate per added node.  Latency-bound.
+#include <algorithm>
+#include <cfloat>
+#include <climits>
+
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+// argmax order: a NaN before any number (smaller id first among NaNs), else the
+// larger value, then the smaller id; (-inf, INT_MAX) is an empty slot
+__device__ __forceinline__ bool before(float v1, int i1, float v2, int i2) {
+    const bool n1 = v1 != v1, n2 = v2 != v2;
+    if (n1 | n2) return n1 && (!n2 || i1 < i2);
+    return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+constexpr int kTopkThreads = 512;
+constexpr int kTopkUnroll = 4;
+
+template <int WT>
+struct TopList {
+    float v[WT];
+    int i[WT];
+    __device__ __forceinline__ void clear() {
+#pragma unroll
+        for (int k = 0; k < WT; ++k) {
+            v[k] = -INFINITY;
+            i[k] = INT_MAX;
+        }
+    }
+    // entries are offered in increasing id order per thread
+    __device__ __forceinline__ void offer(float x, int id) {
+        if (before(x, id, v[WT - 1], i[WT - 1])) {
+            float cv = x;
+            int ci = id;
+#pragma unroll
+            for (int k = 0; k < WT; ++k) {
+                const bool sw = before(cv, ci, v[k], i[k]);
+                const float tv = v[k];
+                const int ti = i[k];
+                v[k] = sw ? cv : tv;
+                i[k] = sw ? ci : ti;
+                cv = sw ? tv : cv;
+                ci = sw ? ti : ci;
+            }
+        }
+    }
+    __device__ __forceinline__ void pop() {
+#pragma unroll
+        for (int k = 0; k < WT - 1; ++k) {
+            v[k] = v[k + 1];
+            i[k] = i[k + 1];
+        }
+        v[WT - 1] = -INFINITY;
+        i[WT - 1] = INT_MAX;
+    }
+};
+
+// running log-sum-exp state: m starts at -FLT_MAX (finite) so that -inf
+// entries add exp(-inf) = 0; a NaN or a +inf entry makes s NaN
+__device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2) {
+    const float mm = fmaxf(m, m2);
+    s = s * __expf(m - mm) + s2 * __expf(m2 - mm);
+    m = mm;
+}
+
+// the best entry among the wave's list heads; its owner pops it
+template <int WT>
+__device__ __forceinline__ void wave_take(TopList<WT> &L, float &bv, int &bi) {
+    bv = L.v[0];
+    bi = L.i[0];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oi = __shfl_xor(bi, off);
+        if (before(ov, oi, bv, bi)) {
+            bv = ov;
+            bi = oi;
+        }
+    }
+    if (bi != INT_MAX && L.i[0] == bi) L.pop();
+}
+
+template <int WT, bool VEC>
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(int vocab, int width, const float *logits,
+                                                             int32_t *tokens, float *logp) {
+    constexpr int NW = kTopkThreads / 64;
+    __shared__ float s_v[NW][WT];
+    __shared__ int s_i[NW][WT];
+    __shared__ float s_m[NW], s_s[NW];
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid % 64, w = tid / 64;
+    const float *x = logits + (size_t)row * vocab;
+    TopList<WT> L;
+    L.clear();
+    float m = -FLT_MAX, s = 0.0f;
+    if (VEC) {
+        const float4 *x4 = reinterpret_cast<const float4 *>(x);
+        const int n4 = vocab / 4;
+        auto eat = [&](const float4 r, int j) {
+            const float g = fmaxf(fmaxf(r.x, r.y), fmaxf(r.z, r.w));
+            if (g > m) {
+                s *= __expf(m - g);
+                m = g;
+            }
+            s += (__expf(r.x - m) + __expf(r.y - m)) + (__expf(r.z - m) + __expf(r.w - m));
+            L.offer(r.x, 4 * j);
+            L.offer(r.y, 4 * j + 1);
+            L.offer(r.z, 4 * j + 2);
+            L.offer(r.w, 4 * j + 3);
+        };
+        int j = tid;
+        for (; j + (kTopkUnroll - 1) * kTopkThreads < n4; j += kTopkUnroll * kTopkThreads) {
+            float4 r[kTopkUnroll];
+#pragma unroll
+            for (int u = 0; u < kTopkUnroll; ++u) r[u] = x4[j + u * kTopkThreads];
+#pragma unroll
+            for (int u = 0; u < kTopkUnroll; ++u) eat(r[u], j + u * kTopkThreads);
+        }
+        for (; j < n4; j += kTopkThreads) eat(x4[j], j);
+    } else {
+        auto eat = [&](float r, int j) {
+            if (r > m) {
+                s *= __expf(m - r);
+                m = r;
+            }
+            s += __expf(r - m);
+            L.offer(r, j);
+        };
+        int j = tid;
+        for (; j + (kTopkUnroll - 1) * kTopkThreads < vocab; j += kTopkUnroll * kTopkThreads) {
+            float r[kTopkUnroll];
+#pragma unroll
+            for (int u = 0; u < kTopkUnroll; ++u) r[u] = x[j + u * kTopkThreads];
+#pragma unroll
+            for (int u = 0; u < kTopkUnroll; ++u) eat(r[u], j + u * kTopkThreads);
+        }
+        for (; j < vocab; j += kTopkThreads) eat(x[j], j);
+    }
+    // log-sum-exp over the wave, then the workgroup
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) lse_merge(m, s, __shfl_xor(m, off), __shfl_xor(s, off));
+    // each wave's best WT entries, in order
+#pragma unroll 1
+    for (int r = 0; r < WT; ++r) {
+        float bv;
+        int bi;
+        wave_take(L, bv, bi);
+        if (lane == 0) {
+            s_v[w][r] = bv;
+            s_i[w][r] = bi;
+        }
+    }
+    if (lane == 0) {
+        s_m[w] = m;
+        s_s[w] = s;
+    }
+    __syncthreads();
+    if (w != 0) return;
+    // wave 0 merges the NW lists (lane k < NW holds wave k's list)
+    TopList<WT> M;
+    M.clear();
+    if (lane < NW) {
+#pragma unroll
+        for (int k = 0; k < WT; ++k) {
+            M.v[k] = s_v[lane][k];
+            M.i[k] = s_i[lane][k];
+        }
+    }
+    float gm = s_m[0], gs = s_s[0];
+    for (int k = 1; k < NW; ++k) lse_merge(gm, gs, s_m[k], s_s[k]);
+    // every entry equal to -inf: no finite mass (all log p -inf); NaN mass: no distribution
+    const float lse = gm + logf(gs);
+#pragma unroll 1
+    for (int r = 0; r < width; ++r) {
+        float bv;
+        int bi;
+        wave_take(M, bv, bi);
+        if (lane == 0) {
+            const bool none = bi == INT_MAX;
+            tokens[(size_t)row * width + r] = none ? -1 : bi;
+            float lp;
+            if (none || gs == 0.0f) lp = -INFINITY;
+            else if (gs != gs) lp = __int_as_float(0x7fc00000);
+            else lp = bv - lse;
+            logp[(size_t)row * width + r] = lp;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Builder
+// ---------------------------------------------------------------------------
+constexpr int kSlots = GDN_MAX_NODES / 64;  // nodes per lane
+
+struct BuildArgs {
+    int B, levels, width, budget, depth_cap, nodes;
+    const int32_t *root_token, *tokens;
+    const float *logp;
+    int32_t *parent, *node_token, *cu_nodes;
+};
+
+// candidate key: higher score first, then (child depth, rank, parent id) packed
+// ascending; an exhausted node offers (-inf, INT_MAX)
+__device__ __forceinline__ bool cand_before(float s1, int k1, float s2, int k2) {
+    return s1 > s2 || (s1 == s2 && k1 < k2);
+}
+
+__global__ __launch_bounds__(64) void build_kernel(BuildArgs A) {
+    __shared__ float s_lp[GDN_MAX_DEPTH][kMaxDraftWidth];
+    __shared__ int s_tok[GDN_MAX_DEPTH][kMaxDraftWidth];
+    __shared__ int s_par[GDN_MAX_NODES], s_ntok[GDN_MAX_NODES];
+    const int lane = threadIdx.x, b = blockIdx.x;
+    const int W = A.width, cap = A.depth_cap, N = A.nodes;
+    const int rows = min(A.levels, cap - 1);  // levels a node can occupy
+    for (int e = lane; e < rows * W; e += 64) {
+        const int l = e / W, r = e % W;
+        const size_t at = ((size_t)b * A.levels + l) * W + r;
+        const float v = A.logp[at];
+        s_lp[l][r] = v != v ? -INFINITY : v;
+        s_tok[l][r] = A.tokens[at];
+    }
+    __syncthreads();
+
+    // node state, node = lane + 64 k: score, depth, children taken; and its candidate
+    float sc[kSlots], cs[kSlots];
+    int dp[kSlots], nc[kSlots], ck[kSlots];
+#pragma unroll
+    for (int k = 0; k < kSlots; ++k) {
+        sc[k] = 0.0f;
+        dp[k] = 0;
+        nc[k] = 0;
+        cs[k] = -INFINITY;
+        ck[k] = INT_MAX;
+    }
+    auto refresh = [&](int k, int node) {
+        const bool open = dp[k] > 0 && dp[k] < cap && nc[k] < W;
+        cs[k] = open ? sc[k] + s_lp[open ? dp[k] - 1 : 0][open ? nc[k] : 0] : -INFINITY;
+        ck[k] = open ? ((dp[k] + 1) << 14) | (nc[k] << 9) | node : INT_MAX;
+    };
+    // the root, then the rank-1 chain: node i is the first child of node i - 1
+    const int chain = min(A.budget, cap - 1);
+    float score = 0.0f;
+    if (lane == 0) {
+        s_par[0] = -1;
+        s_ntok[0] = A.root_token ? A.root_token[b] : -1;
+    }
+    for (int i = 0; i <= chain; ++i) {
+        if (i > 0) {
+            score = score + s_lp[i - 1][0];
+            if (lane == 0) {
+                s_par[i] = i - 1;
+                s_ntok[i] = s_tok[i - 1][0];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kSlots; ++k) {
+            if (lane + 64 * k == i) {
+                sc[k] = score;
+                dp[k] = i + 1;
+                nc[k] = i < chain ? 1 : 0;
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kSlots; ++k) refresh(k, lane + 64 * k);
+
+    // best first: one node per round
+    for (int n = chain + 1; n < N; ++n) {
+        float bs = cs[0];
+        int bk = ck[0];
+#pragma unroll
+        for (int k = 1; k < kSlots; ++k)
+            if (cand_before(cs[k], ck[k], bs, bk)) {
+                bs = cs[k];
+                bk = ck[k];
+            }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float os = __shfl_xor(bs, off);
+            const int ok = __shfl_xor(bk, off);
+            if (cand_before(os, ok, bs, bk)) {
+                bs = os;
+                bk = ok;
+            }
+        }
+        if (bk == INT_MAX) break;  // cannot happen: the node count is what the limits allow
+        const int d = bk >> 14, r = (bk >> 9) & 31, p = bk & 511;
+        if (lane == 0) {
+            s_par[n] = p;
+            s_ntok[n] = s_tok[d - 2][r];
+        }
+#pragma unroll
+        for (int k = 0; k < kSlots; ++k) {
+            const int node = lane + 64 * k;
+            if (node == p) {
+                nc[k] += 1;
+                refresh(k, node);
+            }
+            if (node == n) {
+                sc[k] = bs;
+                dp[k] = d;
+                nc[k] = 0;
+                refresh(k, node);
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = lane; i < N; i += 64) {
+        A.parent[(size_t)b * N + i] = s_par[i];
+        A.node_token[(size_t)b * N + i] = s_ntok[i];
+    }
+    if (lane == 0) {
+        A.cu_nodes[b] = b * N;
+        if (b == A.B - 1) A.cu_nodes[A.B] = A.B * N;
+    }
+}
+
+}  // namespace
+
+int ddtree_nodes(int levels, int width, int budget, int max_depth) {
+    const int cap = std::min(levels + 1, max_depth);
+    long long total = 0, layer = 1;
+    for (int d = 1; d < cap && total < budget; ++d) {
+        layer *= width;
+        total += layer;
+    }
+    return 1 + (int)std::min<long long>(budget, total);
+}
+
+hipError_t launch_draft_topk(int rows, int vocab, int width, const float *logits, int32_t *tokens, float *logp,
+                             hipStream_t s) {
+    const bool vec = vocab % 4 == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0;
+    const dim3 grid(rows), block(kTopkThreads);
+#define GDN_TOPK_CASE(WT)                                                                                     \
+    if (width <= WT) {                                                                                        \
+        if (vec)                                                                                              \
+            hipLaunchKernelGGL((topk_kernel<WT, true>), grid, block, 0, s, vocab, width, logits, tokens, logp);  \
+        else                                                                                                  \
+            hipLaunchKernelGGL((topk_kernel<WT, false>), grid, block, 0, s, vocab, width, logits, tokens, logp); \
+        return hipGetLastError();                                                                             \
+    }
+    GDN_TOPK_CASE(1)
+    GDN_TOPK_CASE(2)
+    GDN_TOPK_CASE(4)
+    GDN_TOPK_CASE(8)
+    GDN_TOPK_CASE(16)
+#undef GDN_TOPK_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_ddtree_build(int B, int levels, int width, int budget, int max_depth, const int32_t *root_token,
+                               const int32_t *tokens, const float *logp, int32_t *parent, int32_t *node_token,
+                               int32_t *cu_nodes, hipStream_t s) {
+    BuildArgs A;
+    A.B = B;
+    A.levels = levels;
+    A.width = width;
+    A.budget = budget;
+    A.depth_cap = std::min(levels + 1, max_depth);
+    A.nodes = ddtree_nodes(levels, width, budget, max_depth);
+    A.root_token = root_token;
+    A.tokens = tokens;
+    A.logp = logp;
+    A.parent = parent;
+    A.node_token = node_token;
+    A.cu_nodes = cu_nodes;
+    hipLaunchKernelGGL(build_kernel, dim3(B), dim3(64), 0, s, A);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

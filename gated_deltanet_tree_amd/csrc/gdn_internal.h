@@ -18,6 +18,7 @@ __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_
 
 constexpr int kCoefFloats = 20;         // per (node, value head): 16 path weights, gamma, alpha, b, depth
 constexpr int kAcceptChunks = 8;        // most slices one logits row is split into for the argmax
+constexpr int kMaxDraftWidth = GDN_MAX_DRAFT_WIDTH;  // candidates per drafted position
 
 // Byte offsets of the workspace regions (each 256-byte aligned).  The
 // per-(node, head) coefficient records come last, so the other offsets do
@@ -106,6 +107,13 @@ hipError_t launch_chain_verify_fast(const Params &p, hipStream_t s);
 hipError_t launch_persist_fast(const Params &p, hipStream_t s);
 // greedy acceptance over the verify logits
 hipError_t launch_accept(const Params &p, hipStream_t s);
+// draft candidates and the DDTree builder
+int ddtree_nodes(int levels, int width, int budget, int max_depth);
+hipError_t launch_draft_topk(int rows, int vocab, int width, const float *logits, int32_t *tokens, float *logp,
+                             hipStream_t s);
+hipError_t launch_ddtree_build(int B, int levels, int width, int budget, int max_depth, const int32_t *root_token,
+                               const int32_t *tokens, const float *logp, int32_t *parent, int32_t *node_token,
+                               int32_t *cu_nodes, hipStream_t s);
 
 // Largest LDS stack the heavy-last preorder can need for trees of n nodes:
 // k nested pushes need a subtree of at least 2^(k+1) - 1 nodes.

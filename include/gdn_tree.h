@@ -76,6 +76,8 @@ extern "C" {
 #define GDN_MAX_NODES 256
 /* Longest chain gdn_chain_verify accepts (it has no depth limit). */
 #define GDN_MAX_CHAIN 65536
+/* Most draft candidates kept per drafted position (gdn_draft_topk, gdn_ddtree_build). */
+#define GDN_MAX_DRAFT_WIDTH 16
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -208,6 +210,51 @@ int gdn_chain_verify(const gdn_dims *dims, const int32_t *cu_nodes, const void *
 int gdn_tree_accept(const gdn_dims *dims, const float *logits, int32_t vocab, const int32_t *draft_token,
                     int32_t *accepted_node, int32_t *accept_len, int32_t *next_token, int32_t *target_token,
                     void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * gdn_draft_topk -- the drafter's candidates per drafted position: for each of
+ * `rows` rows of fp32 logits [rows][vocab], the `width` (1 .. 16) best entries
+ * in argmax order (a NaN counts as largest, equal values keep the smaller id,
+ * +0 equals -0) into tokens [rows][width], and their log-softmax values
+ * x - log(sum(exp(row))) into logp [rows][width] (fp32; all NaN when the row
+ * holds a NaN or +inf, all -inf when every entry is -inf; ranks past the
+ * vocabulary get token -1 and log p -inf).  The descending order is the one
+ * DDTree's builder expects: rank 1 first (GreenGames page, "Key wins": a
+ * reversed order sent the worst candidate to the tree root).  One workgroup
+ * per row; logits may be any 4-byte-aligned address.  No workspace.
+ */
+int gdn_draft_topk(int32_t rows, int32_t vocab, int32_t width, const float *logits, int32_t *tokens,
+                   float *logp, void *stream);
+
+/*
+ * gdn_ddtree_nodes -- nodes of every tree gdn_ddtree_build grows: 1 + min(budget,
+ * all nodes a depth of min(levels + 1, max_depth) and `width` children per node
+ * allow); 0 for arguments out of range.
+ */
+int32_t gdn_ddtree_nodes(int32_t levels, int32_t width, int32_t budget, int32_t max_depth);
+
+/*
+ * gdn_ddtree_build -- grow one draft tree per sequence (GreenGames page, "From
+ * autoregressive to DDTree": budgeted best-first trees with a chain pre-seed).
+ * tokens/logp [B][levels][width] hold each drafted position's candidates in
+ * rank order (as gdn_draft_topk writes them); position l (1-based) is tree
+ * level l, the children of a depth-l node (root depth 1).  Node 0 is the root
+ * carrying root_token[b] (NULL: -1).  Nodes 1 .. min(budget, levels,
+ * max_depth - 1) form the rank-1 chain; then, until budget drafts exist, the
+ * next node is the best candidate among every node's next unused rank r <
+ * width at the node's level (child depth <= min(levels + 1, max_depth)): the
+ * higher path score (the fp32 sum of log p along the path, parent's score
+ * plus the candidate's log p; NaN log p counts as -inf), then the smaller
+ * depth, the smaller rank, the smaller parent id.  Node ids are insertion
+ * order, so parent ids precede their children.  Outputs (N =
+ * gdn_ddtree_nodes(...), at most GDN_MAX_NODES): parent [B*N] (local ids, -1
+ * for the root), node_token [B*N] and cu_nodes [B+1] = b*N -- the inputs of
+ * gdn_tree_plan and the draft tokens of gdn_tree_accept.  log p values are
+ * log-probabilities (<= 0) or -inf.  One wave per sequence.
+ */
+int gdn_ddtree_build(int32_t num_seqs, int32_t levels, int32_t width, int32_t budget, int32_t max_depth,
+                     const int32_t *root_token, const int32_t *tokens, const float *logp, int32_t *parent,
+                     int32_t *node_token, int32_t *cu_nodes, void *stream);
 
 /*
  * gdn_tree_read_metadata -- device-to-device copies of what the plan (and the

@@ -74,9 +74,12 @@ def tree_size(levels: int, width: int, budget: int, max_depth: int = 16) -> int:
     return 1 + min(budget, cap)
 
 
-def build_tree(root_token: int, tokens: np.ndarray, logp: np.ndarray, budget: int, max_depth: int = 16):
+def build_tree(root_token: int, tokens: np.ndarray, logp: np.ndarray, budget: int, max_depth: int = 16,
+               margins: list | None = None):
     """One sequence.  tokens/logp [L][W] (level l = 1 .. L in row l - 1).
-    Returns (parent, token, score) of the built tree, root first."""
+    Returns (parent, token, score) of the built tree, root first.  If a list is
+    given as ``margins``, each best-first choice appends the score gap to the
+    best other live candidate (inf when it had none)."""
     tokens = np.asarray(tokens)
     L, W = tokens.shape
     lp = np.asarray(logp, dtype=np.float32)
@@ -119,9 +122,12 @@ def build_tree(root_token: int, tokens: np.ndarray, logp: np.ndarray, budget: in
     for node in range(len(parent)):
         offer(node)
     while len(parent) - 1 < budget and heap:
-        _, _, r, par = heapq.heappop(heap)
+        neg, _, r, par = heapq.heappop(heap)
         if nchild[par] != r:
             continue
+        if margins is not None:
+            live = [-e[0] for e in heap if nchild[e[3]] == e[2]]
+            margins.append(-neg - max(live) if live else np.inf)
         child = add(par)
         offer(par)
         offer(child)

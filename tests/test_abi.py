@@ -63,3 +63,19 @@ def test_accept_host_checks(lib):
     assert lib.gdn_tree_accept(ctypes.byref(dims), one, 10, one, None, one, one, None, one, n, None) == -1
     assert lib.gdn_tree_accept(ctypes.byref(dims), one, 10, one, one, one, one, None, None, n, None) == -1
     assert lib.gdn_tree_accept(ctypes.byref(dims), one, 10, one, one, one, one, None, one, n - 1, None) == -4
+
+
+def test_draft_and_builder_host_checks(lib):
+    one = ctypes.c_void_p(16)
+    assert lib.gdn_draft_topk(4, 100, 0, one, one, one, None) == -2
+    assert lib.gdn_draft_topk(4, 100, 17, one, one, one, None) == -2
+    assert lib.gdn_draft_topk(4, 0, 4, one, one, one, None) == -2
+    assert lib.gdn_draft_topk(4, 100, 4, None, one, one, None) == -1
+    assert lib.gdn_draft_topk(0, 100, 4, None, None, None, None) == 0
+    import oracle.ddtree as dd
+    for args in [(15, 4, 22, 16), (15, 8, 64, 16), (3, 2, 100, 16), (15, 1, 40, 16), (5, 3, 0, 16), (15, 4, 22, 6)]:
+        assert lib.gdn_ddtree_nodes(*args) == dd.tree_size(*args), args
+    assert lib.gdn_ddtree_nodes(0, 4, 22, 16) == 0 and lib.gdn_ddtree_nodes(15, 17, 22, 16) == 0
+    assert lib.gdn_ddtree_nodes(15, 4, 22, 17) == 0
+    assert lib.gdn_ddtree_build(2, 15, 4, 300, 16, None, one, one, one, one, one, None) == -2
+    assert lib.gdn_ddtree_build(2, 15, 4, 22, 16, None, None, one, one, one, one, None) == -1
