@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-accept", action="store_true", help="skip the greedy-acceptance measurement")
     ap.add_argument("--accept-steps", type=int, default=50)
+    ap.add_argument("--no-draft", action="store_true", help="skip the draft top-k / tree-builder measurement")
     ap.add_argument("--path", choices=["auto", "recurrent"], default="auto",
                     help="recurrent: run the per-node recurrent kernels on every call (GDN_KERNEL_PATH)")
     return ap.parse_args()
@@ -239,6 +240,8 @@ def main():
     }
     if not args.no_accept:
         result["accept"] = bench_accept(G, W, cfg, trees, dims, parent_d, cu_d, slot_d, args.accept_steps)
+    if not args.no_draft and cfg.tree[0] == "ddtree":
+        result["draft"] = bench_draft(G, W, cfg, args.accept_steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, trees, cu, acc, args.cpu_seconds)
     print(json.dumps(result))
@@ -280,12 +283,60 @@ def bench_accept(G, W, cfg, trees, dims, parent_d, cu_d, slot_d, steps):
             "mean_accept_len": float(alen.float().mean().item())}
 
 
+def bench_draft(G, W, cfg, steps):
+    """The drafter side of a decode step: top-W candidates of every drafted
+    position over the full vocabulary (gdn_draft_topk), then the trees
+    (gdn_ddtree_build), each timed per call with HIP events on its stream.  Not
+    part of the step: both run once per decode step before the plan."""
+    import torch
+    from workloads import draft
+    B, L = cfg.num_seqs, draft.DRAFT_LEVELS
+    _, budget, width, _ = cfg.tree
+    x = torch.from_numpy(draft.make_draft_logits(cfg).reshape(B * L, draft.VOCAB)).cuda()
+    roots = torch.from_numpy(draft.make_root_tokens(cfg)).cuda()
+    tk = torch.empty((B * L, width), dtype=torch.int32, device="cuda")
+    lp = torch.empty((B * L, width), dtype=torch.float32, device="cuda")
+    n = G.ddtree_nodes(L, width, budget)
+    par = torch.empty(B * n, dtype=torch.int32, device="cuda")
+    ntok = torch.empty(B * n, dtype=torch.int32, device="cuda")
+    cu = torch.empty(B + 1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def topk():
+        G.gdn_draft_topk(x, width, tk, lp)
+
+    def build():
+        G.gdn_ddtree_build(roots, tk.view(B, L, width), lp.view(B, L, width), budget, par, ntok, cu)
+
+    times = {}
+    for name, fn in (("topk", topk), ("build", build)):
+        for _ in range(5):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        times[name] = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    # algorithmic bytes of the top-k: every logit once, W (token, log p) pairs per row out
+    nbytes = B * L * draft.VOCAB * 4 + B * L * width * 8
+    gbs = nbytes / times["topk"] / 1e9
+    return {"rows": B * L, "vocab": draft.VOCAB, "width": width, "budget": budget, "tree_nodes": n,
+            "topk_us": times["topk"] * 1e6, "topk_bytes": nbytes,
+            "topk_roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("draft_topk", cfg.name)},
+            "build_us": times["build"] * 1e6}
+
+
 # the sources each measured kernel is built from: counters recorded for one of
 # them stay valid while these files keep their code
 KERNEL_SOURCES = {
     "tree_verify": ("gdn_fast.hip", "gdn_internal.h"),
     "persist": ("gdn_fast.hip", "gdn_internal.h"),
     "accept": ("gdn_accept.hip", "gdn_internal.h"),
+    "draft_topk": ("gdn_ddtree.hip", "gdn_internal.h"),
 }
 
 

@@ -8,11 +8,12 @@
 // DDTree") and grows the rest of the budget best first by path score.
 //
 //   topk_kernel   one workgroup per row: streams the row once (16-byte loads
-//                 when the layout allows), keeping per thread its WT best
-//                 entries in argmax order (a NaN counts as largest, equal
-//                 values keep the smaller id) and a running (max, sum of
-//                 exp(x - max)) for the log-softmax; the waves merge their
-//                 lists by repeated wave-wide extraction.  HBM-bound.
+//                 when the layout allows) with a running (max, sum of
+//                 exp(x - max)) for the log-softmax; entries at or above a
+//                 wave-wide floor go through an LDS candidate buffer into
+//                 per-lane lists of the WT best in argmax order (a NaN counts
+//                 as largest, equal values keep the smaller id), which the
+//                 waves merge by repeated wave-wide extraction.  HBM-bound.
 //   build_kernel  one wave per sequence: the chain, then one candidate per
 //                 node (its next unused rank) and a wave-wide extraction of
 //                 the best candidate per added node.  Latency-bound.
@@ -47,7 +48,7 @@ struct TopList {
             i[k] = INT_MAX;
         }
     }
-    // entries are offered in increasing id order per thread
+    // keeps the WT best offers in argmax order, whatever the order of offers
     __device__ __forceinline__ void offer(float x, int id) {
         if (before(x, id, v[WT - 1], i[WT - 1])) {
             float cv = x;
@@ -100,6 +101,19 @@ __device__ __forceinline__ void wave_take(TopList<WT> &L, float &bv, int &bi) {
     if (bi != INT_MAX && L.i[0] == bi) L.pop();
 }
 
+// A wave-wide lower bound of the row's W-th best value: the largest of the
+// lanes' own W-th best entries (that lane holds W entries at least as good).
+// Entries below it can never enter the row's top W.
+template <int WT>
+__device__ __forceinline__ float wave_floor(const TopList<WT> &L) {
+    float t = L.v[WT - 1];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) t = fmaxf(t, __shfl_xor(t, off));
+    return t;
+}
+
+constexpr int kCandBuf = 512;  // per-wave candidate buffer (LDS entries)
+
 template <int WT, bool VEC>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(int vocab, int width, const float *logits,
                                                              int32_t *tokens, float *logp) {
@@ -107,55 +121,96 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(int vocab, int width
     __shared__ float s_v[NW][WT];
     __shared__ int s_i[NW][WT];
     __shared__ float s_m[NW], s_s[NW];
+    __shared__ float c_v[NW][kCandBuf];
+    __shared__ int c_i[NW][kCandBuf];
     const int row = blockIdx.x;
     const int tid = threadIdx.x, lane = tid % 64, w = tid / 64;
     const float *x = logits + (size_t)row * vocab;
     TopList<WT> L;
     L.clear();
     float m = -FLT_MAX, s = 0.0f;
+    // Entries at or above the wave's floor (and NaNs) are appended to the wave's
+    // candidate buffer; a full buffer is folded into the lanes' lists (each lane
+    // takes every 64th entry; the lists compare ids on equal values, so the
+    // order of offers does not matter) and the floor is raised.  With a good floor almost
+    // every entry is dismissed by one comparison.
+    float floor_v = -INFINITY;  // wave-uniform
+    int cnt = 0;                // wave-uniform
+    const unsigned long long below = (1ull << lane) - 1ull;
+    auto fold = [&]() {
+        for (int k = lane; k < cnt; k += 64) L.offer(c_v[w][k], c_i[w][k]);
+        cnt = 0;
+        floor_v = wave_floor(L);
+    };
+    // every lane runs the same number of steps (the buffer count and the floor
+    // must stay uniform across the wave); entries past the row are not offered
+    auto take = [&](float e, int id, bool valid) {
+        const bool pass = valid && !(e < floor_v);
+        const unsigned long long mask = __ballot(pass);
+        if (mask) {
+            if (pass) {
+                const int pos = cnt + __popcll(mask & below);
+                c_v[w][pos] = e;
+                c_i[w][pos] = id;
+            }
+            cnt += __popcll(mask);
+            if (cnt > kCandBuf - 64) fold();
+        }
+    };
     if (VEC) {
         const float4 *x4 = reinterpret_cast<const float4 *>(x);
         const int n4 = vocab / 4;
-        auto eat = [&](const float4 r, int j) {
+        auto eat = [&](const float4 r, int j, bool valid) {
             const float g = fmaxf(fmaxf(r.x, r.y), fmaxf(r.z, r.w));
             if (g > m) {
                 s *= __expf(m - g);
                 m = g;
             }
             s += (__expf(r.x - m) + __expf(r.y - m)) + (__expf(r.z - m) + __expf(r.w - m));
-            L.offer(r.x, 4 * j);
-            L.offer(r.y, 4 * j + 1);
-            L.offer(r.z, 4 * j + 2);
-            L.offer(r.w, 4 * j + 3);
+            take(r.x, 4 * j, valid);
+            take(r.y, 4 * j + 1, valid);
+            take(r.z, 4 * j + 2, valid);
+            take(r.w, 4 * j + 3, valid);
         };
-        int j = tid;
-        for (; j + (kTopkUnroll - 1) * kTopkThreads < n4; j += kTopkUnroll * kTopkThreads) {
+        constexpr int step = kTopkUnroll * kTopkThreads;
+        int base = 0;
+        for (; base + step <= n4; base += step) {  // whole blocks: no lane idles
             float4 r[kTopkUnroll];
 #pragma unroll
-            for (int u = 0; u < kTopkUnroll; ++u) r[u] = x4[j + u * kTopkThreads];
+            for (int u = 0; u < kTopkUnroll; ++u) r[u] = x4[base + u * kTopkThreads + tid];
 #pragma unroll
-            for (int u = 0; u < kTopkUnroll; ++u) eat(r[u], j + u * kTopkThreads);
+            for (int u = 0; u < kTopkUnroll; ++u) eat(r[u], base + u * kTopkThreads + tid, true);
         }
-        for (; j < n4; j += kTopkThreads) eat(x4[j], j);
+        for (int u = 0; u < kTopkUnroll; ++u) {  // the ragged last block, one load at a time
+            const int j = base + u * kTopkThreads + tid;
+            const bool valid = j < n4;
+            eat(valid ? x4[j] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY), j, valid);
+        }
     } else {
-        auto eat = [&](float r, int j) {
+        auto eat = [&](float r, int j, bool valid) {
             if (r > m) {
                 s *= __expf(m - r);
                 m = r;
             }
             s += __expf(r - m);
-            L.offer(r, j);
+            take(r, j, valid);
         };
-        int j = tid;
-        for (; j + (kTopkUnroll - 1) * kTopkThreads < vocab; j += kTopkUnroll * kTopkThreads) {
+        constexpr int step = kTopkUnroll * kTopkThreads;
+        int base = 0;
+        for (; base + step <= vocab; base += step) {
             float r[kTopkUnroll];
 #pragma unroll
-            for (int u = 0; u < kTopkUnroll; ++u) r[u] = x[j + u * kTopkThreads];
+            for (int u = 0; u < kTopkUnroll; ++u) r[u] = x[base + u * kTopkThreads + tid];
 #pragma unroll
-            for (int u = 0; u < kTopkUnroll; ++u) eat(r[u], j + u * kTopkThreads);
+            for (int u = 0; u < kTopkUnroll; ++u) eat(r[u], base + u * kTopkThreads + tid, true);
         }
-        for (; j < vocab; j += kTopkThreads) eat(x[j], j);
+        for (int u = 0; u < kTopkUnroll; ++u) {
+            const int j = base + u * kTopkThreads + tid;
+            const bool valid = j < vocab;
+            eat(valid ? x[j] : -INFINITY, j, valid);
+        }
     }
+    fold();
     // log-sum-exp over the wave, then the workgroup
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) lse_merge(m, s, __shfl_xor(m, off), __shfl_xor(s, off));
