@@ -48,6 +48,7 @@ def parse():
     ap.add_argument("--no-accept", action="store_true", help="skip the greedy-acceptance measurement")
     ap.add_argument("--accept-steps", type=int, default=50)
     ap.add_argument("--no-draft", action="store_true", help="skip the draft top-k / tree-builder measurement")
+    ap.add_argument("--no-snapshot", action="store_true", help="skip the prefix-cache snapshot measurement")
     ap.add_argument("--path", choices=["auto", "recurrent"], default="auto",
                     help="recurrent: run the per-node recurrent kernels on every call (GDN_KERNEL_PATH)")
     return ap.parse_args()
@@ -242,6 +243,8 @@ def main():
         result["accept"] = bench_accept(G, W, cfg, trees, dims, parent_d, cu_d, slot_d, args.accept_steps)
     if not args.no_draft and cfg.tree[0] == "ddtree":
         result["draft"] = bench_draft(G, W, cfg, args.accept_steps)
+    if not args.no_snapshot:
+        result["snapshot"] = bench_snapshot(G, cfg, sets, slot_d, rotate, layers, args.accept_steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, trees, cu, acc, args.cpu_seconds)
     print(json.dumps(result))
@@ -328,6 +331,33 @@ def bench_draft(G, W, cfg, steps):
             "topk_roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("draft_topk", cfg.name)},
             "build_us": times["build"] * 1e6}
+
+
+def bench_snapshot(G, cfg, sets, slot_d, rotate, layers, steps):
+    """Prefix-cache restore: every sequence's committed state of one layer copied
+    from a prefix pool into its cache slot (gdn_state_copy), timed per call with
+    HIP events, rotating over the workload's independent cache copies."""
+    import torch
+    B = cfg.num_seqs
+    copies = [sets[r * layers]["cache"] for r in range(rotate)]
+    pools = [c[slot_d.long()].clone() for c in copies]
+    pool_slots = torch.arange(B, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for i in range(5):
+        G.gdn_state_copy(pools[i % rotate], pool_slots, copies[i % rotate], slot_d)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i, (e0, e1) in enumerate(ev):
+        e0.record(stream)
+        G.gdn_state_copy(pools[i % rotate], pool_slots, copies[i % rotate], slot_d)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    nbytes = 2 * B * cfg.num_v_heads * cfg.head_dim * cfg.head_dim * 4 + 8 * B
+    gbs = nbytes / t / 1e9
+    return {"slots": B, "call_us": t * 1e6, "bytes": nbytes,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
 
 
 # the sources each measured kernel is built from: counters recorded for one of

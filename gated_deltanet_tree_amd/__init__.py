@@ -37,7 +37,7 @@ SEQ_STATUS = {0: "OK", 1: "BAD_NODES", 2: "BAD_SLOT", 3: "DUP_SLOT", 4: "BAD_PAR
 
 EXPORTS = ["gdn_workspace_bytes", "gdn_tree_plan", "gdn_tree_verify", "gdn_tree_persist",
            "gdn_chain_verify", "gdn_tree_accept", "gdn_draft_topk", "gdn_ddtree_nodes", "gdn_ddtree_build",
-           "gdn_tree_read_metadata", "gdn_tree_status", "gdn_strerror"]
+           "gdn_state_copy", "gdn_tree_read_metadata", "gdn_tree_status", "gdn_strerror"]
 
 
 class GdnError(RuntimeError):
@@ -88,12 +88,13 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_ddtree_nodes.argtypes = [i32c, i32c, i32c, i32c]
     lib.gdn_ddtree_nodes.restype = i32c
     lib.gdn_ddtree_build.argtypes = [i32c, i32c, i32c, i32c, i32c, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_state_copy.argtypes = [i32c, i32c, vp, i32c, vp, vp, i32c, vp, i32c, vp]
     lib.gdn_tree_read_metadata.argtypes = [dp, vp, sz, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_tree_status.argtypes = [vp, sz, vp, ip, ip]
     lib.gdn_strerror.argtypes = [i32]
     lib.gdn_strerror.restype = ctypes.c_char_p
     for f in ("gdn_tree_plan", "gdn_tree_verify", "gdn_tree_persist", "gdn_chain_verify",
-              "gdn_tree_accept", "gdn_draft_topk", "gdn_ddtree_build", "gdn_tree_read_metadata",
+              "gdn_tree_accept", "gdn_draft_topk", "gdn_ddtree_build", "gdn_state_copy", "gdn_tree_read_metadata",
               "gdn_tree_status"):
         getattr(lib, f).restype = i32
     _lib = lib
@@ -240,6 +241,19 @@ def gdn_ddtree_build(root_token, tokens, logp, budget, parent, node_token, cu_no
         _ptr(tokens, "tokens", torch.int32, B * L * Wd), _ptr(logp, "logp", torch.float32, B * L * Wd),
         _ptr(parent, "parent", torch.int32, B * n), _ptr(node_token, "node_token", torch.int32, B * n),
         _ptr(cu_nodes, "cu_nodes", torch.int32, B + 1), _stream(stream)), "gdn_ddtree_build")
+
+
+def gdn_state_copy(src_cache, src_slot, dst_cache, dst_slot, stream=None):
+    """Prefix-cache snapshot: dst_cache[dst_slot[i]] = src_cache[src_slot[i]] (whole slots,
+    caches fp32 [slots, H_v, D, D])."""
+    if src_cache.dim() != 4 or dst_cache.dim() != 4 or src_cache.shape[1:] != dst_cache.shape[1:]:
+        raise ValueError("caches must be [slots, H_v, D, D] tensors of the same slot shape")
+    hv, d = int(src_cache.shape[1]), int(src_cache.shape[2])
+    n = int(src_slot.numel())
+    _check(load_library().gdn_state_copy(
+        hv, d, _ptr(src_cache, "src_cache", torch.float32), int(src_cache.shape[0]),
+        _ptr(src_slot, "src_slot", torch.int32, n), _ptr(dst_cache, "dst_cache", torch.float32),
+        int(dst_cache.shape[0]), _ptr(dst_slot, "dst_slot", torch.int32, n), n, _stream(stream)), "gdn_state_copy")
 
 
 def gdn_tree_read_metadata(dims, ws, depth=None, order=None, action=None, path=None, path_len=None,

@@ -241,6 +241,21 @@ int gdn_ddtree_build(int32_t num_seqs, int32_t levels, int32_t width, int32_t bu
                                              parent, node_token, cu_nodes, as_stream(stream)));
 }
 
+int gdn_state_copy(int32_t num_v_heads, int32_t head_dim, const float *src_cache, int32_t src_slots_total,
+                   const int32_t *src_slot, float *dst_cache, int32_t dst_slots_total, const int32_t *dst_slot,
+                   int32_t count, void *stream) {
+    if (num_v_heads < 1 || head_dim < 1 || (head_dim & 3) || count < 0 || count > 65535 || src_slots_total < 0 ||
+        dst_slots_total < 0)
+        return GDN_ERR_SHAPE;
+    if (count == 0) return GDN_OK;
+    if (!src_cache || !src_slot || !dst_cache || !dst_slot) return GDN_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(src_cache) % 16 || reinterpret_cast<uintptr_t>(dst_cache) % 16)
+        return GDN_ERR_SHAPE;
+    const size_t slot_floats = (size_t)num_v_heads * head_dim * head_dim;
+    return launched(gdn::launch_state_copy(src_cache, src_slots_total, src_slot, dst_cache, dst_slots_total,
+                                           dst_slot, count, slot_floats, as_stream(stream)));
+}
+
 int gdn_tree_read_metadata(const gdn_dims *dims, const void *ws, size_t ws_bytes, int32_t *depth,
                            int32_t *order, int32_t *action, int32_t *path, int32_t *path_len,
                            int32_t *seq_status, void *stream) {

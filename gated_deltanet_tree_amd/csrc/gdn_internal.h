@@ -114,6 +114,9 @@ hipError_t launch_draft_topk(int rows, int vocab, int width, const float *logits
 hipError_t launch_ddtree_build(int B, int levels, int width, int budget, int max_depth, const int32_t *root_token,
                                const int32_t *tokens, const float *logp, int32_t *parent, int32_t *node_token,
                                int32_t *cu_nodes, hipStream_t s);
+// prefix-cache snapshots
+hipError_t launch_state_copy(const float *src, int src_total, const int32_t *src_slot, float *dst, int dst_total,
+                             const int32_t *dst_slot, int count, size_t slot_floats, hipStream_t s);
 
 // Largest LDS stack the heavy-last preorder can need for trees of n nodes:
 // k nested pushes need a subtree of at least 2^(k+1) - 1 nodes.

@@ -1,0 +1,59 @@
+// gdn_snapshot.hip -- prefix-cache snapshots of the recurrent state: whole-slot
+// copies between a state cache and a prefix pool (or within one cache).
+//
+// Automatic prefix caching on a recurrent hybrid (dflash-caddtree-integrations
+// README, "What's in here": gdn_apc, prefix caching under speculative decoding
+// with a warm start bitwise equal to a cold one) saves the committed state a
+// sequence reached after a shared prefix and later restores it into another
+// sequence's slot.  The copy is exact, so a restored state continues bit for
+// bit like the recomputed one.  Pure data movement: 16-byte loads and stores,
+// one grid row per copied slot.
+#include <algorithm>
+
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;  // 16-byte loads in flight per thread
+
+__global__ __launch_bounds__(kCopyThreads) void slot_copy_kernel(const float4 *src, int src_total,
+                                                                 const int32_t *src_slot, float4 *dst,
+                                                                 int dst_total, const int32_t *dst_slot,
+                                                                 size_t slot4) {
+    const int e = blockIdx.y;
+    const int s = src_slot[e], d = dst_slot[e];
+    if (s < 0 || s >= src_total || d < 0 || d >= dst_total) return;
+    const float4 *from = src + (size_t)s * slot4;
+    float4 *to = dst + (size_t)d * slot4;
+    const size_t per_block = (size_t)kCopyThreads * kCopyUnroll;
+    for (size_t base = (size_t)blockIdx.x * per_block; base < slot4; base += (size_t)gridDim.x * per_block) {
+        float4 r[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            const size_t i = base + (size_t)u * kCopyThreads + threadIdx.x;
+            if (i < slot4) r[u] = from[i];
+        }
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            const size_t i = base + (size_t)u * kCopyThreads + threadIdx.x;
+            if (i < slot4) to[i] = r[u];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_state_copy(const float *src, int src_total, const int32_t *src_slot, float *dst, int dst_total,
+                             const int32_t *dst_slot, int count, size_t slot_floats, hipStream_t s) {
+    const size_t slot4 = slot_floats / 4;
+    const size_t per_block = (size_t)kCopyThreads * kCopyUnroll;
+    const size_t blocks = (slot4 + per_block - 1) / per_block;
+    const dim3 grid((unsigned)std::min<size_t>(blocks, 65535), (unsigned)count);
+    hipLaunchKernelGGL(slot_copy_kernel, grid, dim3(kCopyThreads), 0, s, reinterpret_cast<const float4 *>(src),
+                       src_total, src_slot, reinterpret_cast<float4 *>(dst), dst_total, dst_slot, slot4);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -257,6 +257,23 @@ int gdn_ddtree_build(int32_t num_seqs, int32_t levels, int32_t width, int32_t bu
                      int32_t *node_token, int32_t *cu_nodes, void *stream);
 
 /*
+ * gdn_state_copy -- prefix-cache snapshots (dflash-caddtree-integrations
+ * README, "What's in here": gdn_apc, automatic prefix caching under
+ * speculative decoding, warm start bitwise equal to a cold one).  For each
+ * entry i < count: dst_cache[dst_slot[i]] = src_cache[src_slot[i]], a whole
+ * slot of num_v_heads x head_dim x head_dim fp32 values, copied exactly.  Save
+ * a sequence's committed state into a prefix pool, or restore it from the pool
+ * into a new sequence's slot.  src_slots_total / dst_slots_total are the slot
+ * counts of the two caches; an entry with a slot outside its cache is skipped.
+ * The destination slots must be distinct, and when both caches are the same
+ * memory no destination slot may be another entry's source (such calls race).
+ * Slot arrays are device int32 [count]; caches are 16-byte aligned.
+ */
+int gdn_state_copy(int32_t num_v_heads, int32_t head_dim, const float *src_cache, int32_t src_slots_total,
+                   const int32_t *src_slot, float *dst_cache, int32_t dst_slots_total, const int32_t *dst_slot,
+                   int32_t count, void *stream);
+
+/*
  * gdn_tree_read_metadata -- device-to-device copies of what the plan (and the
  * last persist) stored: depth [T], order [T] (node ids by visit position,
  * offset by cu_nodes), action [T], path [B][GDN_MAX_DEPTH] (root first,

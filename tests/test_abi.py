@@ -79,3 +79,13 @@ def test_draft_and_builder_host_checks(lib):
     assert lib.gdn_ddtree_nodes(15, 4, 22, 17) == 0
     assert lib.gdn_ddtree_build(2, 15, 4, 300, 16, None, one, one, one, one, one, None) == -2
     assert lib.gdn_ddtree_build(2, 15, 4, 22, 16, None, None, one, one, one, one, None) == -1
+
+
+def test_state_copy_host_checks(lib):
+    one = ctypes.c_void_p(16)
+    assert lib.gdn_state_copy(48, 128, one, 4, one, one, 4, one, 0, None) == 0
+    assert lib.gdn_state_copy(0, 128, one, 4, one, one, 4, one, 2, None) == -2
+    assert lib.gdn_state_copy(48, 126, one, 4, one, one, 4, one, 2, None) == -2
+    assert lib.gdn_state_copy(48, 128, one, 4, one, one, 4, one, -1, None) == -2
+    assert lib.gdn_state_copy(48, 128, None, 4, one, one, 4, one, 2, None) == -1
+    assert lib.gdn_state_copy(48, 128, ctypes.c_void_p(20), 4, one, one, 4, one, 2, None) == -2
