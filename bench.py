@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--accept-steps", type=int, default=50)
     ap.add_argument("--no-draft", action="store_true", help="skip the draft top-k / tree-builder measurement")
     ap.add_argument("--no-snapshot", action="store_true", help="skip the prefix-cache snapshot measurement")
+    ap.add_argument("--no-store-path", action="store_true",
+                    help="skip the per-node fp16 state path (verify-and-store + persist-by-copy) comparison")
     ap.add_argument("--path", choices=["auto", "recurrent"], default="auto",
                     help="recurrent: run the per-node recurrent kernels on every call (GDN_KERNEL_PATH)")
     return ap.parse_args()
@@ -243,6 +245,9 @@ def main():
         result["accept"] = bench_accept(G, W, cfg, trees, dims, parent_d, cu_d, slot_d, args.accept_steps)
     if not args.no_draft and cfg.tree[0] == "ddtree":
         result["draft"] = bench_draft(G, W, cfg, args.accept_steps)
+    if not args.no_store_path and layers == 1:
+        result["store_path"] = bench_store_path(G, cfg, dims, sets, slot_d, acc_d, ws, rotate, args.accept_steps,
+                                                vbytes, pbytes, t_ver, t_per)
     if not args.no_snapshot:
         result["snapshot"] = bench_snapshot(G, cfg, sets, slot_d, rotate, layers, args.accept_steps)
     if not args.no_cpu_baseline:
@@ -331,6 +336,44 @@ def bench_draft(G, W, cfg, steps):
             "topk_roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("draft_topk", cfg.name)},
             "build_us": times["build"] * 1e6}
+
+
+def bench_store_path(G, cfg, dims, sets, slot_d, acc_d, ws, rotate, steps, vbytes, pbytes, t_ver, t_per):
+    """The pages' own tree path for comparison: verify that also stores every
+    node's state in fp16 (gdn_tree_verify_store), and a commit that copies the
+    accepted node's stored state (gdn_tree_persist_copy), each timed per call
+    with HIP events, beside this library's replay path."""
+    import torch
+    T, Hv, D, B = dims.total_nodes, cfg.num_v_heads, cfg.head_dim, cfg.num_seqs
+    node_states = torch.empty((T, Hv, D, D), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream()
+    t = {}
+    for name in ("verify_store", "persist_copy"):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps + 3):
+            d = sets[i % rotate]
+            if name == "persist_copy":
+                # the stored states must be this copy's: store first, outside the events
+                G.gdn_tree_verify_store(dims, d["q"], d["k"], d["v"], d["a"], d["b"], d["cache"], slot_d, d["out"],
+                                        node_states, ws)
+            e = ev[i - 3] if i >= 3 else None
+            if e:
+                e[0].record(stream)
+            if name == "verify_store":
+                G.gdn_tree_verify_store(dims, d["q"], d["k"], d["v"], d["a"], d["b"], d["cache"], slot_d, d["out"],
+                                        node_states, ws)
+            else:
+                G.gdn_tree_persist_copy(dims, acc_d, node_states, d["cache"], slot_d, ws)
+            if e:
+                e[1].record(stream)
+        torch.cuda.synchronize()
+        t[name] = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    stored = T * Hv * D * D * 2
+    return {"verify_store_us": t["verify_store"] * 1e6, "persist_copy_us": t["persist_copy"] * 1e6,
+            "verify_store_bytes": vbytes + stored, "persist_copy_bytes": B * Hv * D * D * (2 + 4),
+            "replay_verify_us": t_ver * 1e6, "replay_persist_us": t_per * 1e6,
+            "replay_bytes": vbytes + pbytes,
+            "store_path_over_replay": (t["verify_store"] + t["persist_copy"]) / (t_ver + t_per)}
 
 
 def bench_snapshot(G, cfg, sets, slot_d, rotate, layers, steps):

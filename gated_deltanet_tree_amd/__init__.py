@@ -37,7 +37,8 @@ SEQ_STATUS = {0: "OK", 1: "BAD_NODES", 2: "BAD_SLOT", 3: "DUP_SLOT", 4: "BAD_PAR
 
 EXPORTS = ["gdn_workspace_bytes", "gdn_tree_plan", "gdn_tree_verify", "gdn_tree_persist",
            "gdn_chain_verify", "gdn_tree_accept", "gdn_draft_topk", "gdn_ddtree_nodes", "gdn_ddtree_build",
-           "gdn_state_copy", "gdn_tree_read_metadata", "gdn_tree_status", "gdn_strerror"]
+           "gdn_state_copy", "gdn_tree_verify_store", "gdn_tree_persist_copy", "gdn_tree_read_metadata",
+           "gdn_tree_status", "gdn_strerror"]
 
 
 class GdnError(RuntimeError):
@@ -89,13 +90,15 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_ddtree_nodes.restype = i32c
     lib.gdn_ddtree_build.argtypes = [i32c, i32c, i32c, i32c, i32c, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_state_copy.argtypes = [i32c, i32c, vp, i32c, vp, vp, i32c, vp, i32c, vp]
+    lib.gdn_tree_verify_store.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdn_tree_persist_copy.argtypes = [dp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdn_tree_read_metadata.argtypes = [dp, vp, sz, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_tree_status.argtypes = [vp, sz, vp, ip, ip]
     lib.gdn_strerror.argtypes = [i32]
     lib.gdn_strerror.restype = ctypes.c_char_p
     for f in ("gdn_tree_plan", "gdn_tree_verify", "gdn_tree_persist", "gdn_chain_verify",
-              "gdn_tree_accept", "gdn_draft_topk", "gdn_ddtree_build", "gdn_state_copy", "gdn_tree_read_metadata",
-              "gdn_tree_status"):
+              "gdn_tree_accept", "gdn_draft_topk", "gdn_ddtree_build", "gdn_state_copy", "gdn_tree_verify_store",
+              "gdn_tree_persist_copy", "gdn_tree_read_metadata", "gdn_tree_status"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -179,6 +182,30 @@ def gdn_tree_persist(dims, k, v, a, b, accepted_node, state_cache, slot_idx, ws,
         _ptr(state_cache, "state_cache", torch.float32, dims.num_slots * Hv * D * D),
         _ptr(slot_idx, "slot_idx", torch.int32, B), _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)),
         "gdn_tree_persist")
+
+
+def gdn_tree_verify_store(dims, q, k, v, a, b, state_cache, slot_idx, out, node_states, ws, stream=None):
+    """gdn_tree_verify plus every node's state in fp16 (node_states: torch.float16 [T, H_v, D, D])."""
+    T, B, Hk, Hv, D = dims.total_nodes, dims.num_seqs, dims.num_k_heads, dims.num_v_heads, dims.head_dim
+    dt = _qkv_dtype(dims)
+    _check(load_library().gdn_tree_verify_store(
+        ctypes.byref(dims), _ptr(q, "q", dt, T * Hk * D), _ptr(k, "k", dt, T * Hk * D),
+        _ptr(v, "v", dt, T * Hv * D), _ptr(a, "a", torch.float32, T * Hv), _ptr(b, "b", torch.float32, T * Hv),
+        _ptr(state_cache, "state_cache", torch.float32, dims.num_slots * Hv * D * D),
+        _ptr(slot_idx, "slot_idx", torch.int32, B), _ptr(out, "out", torch.float32, T * Hv * D),
+        _ptr(node_states, "node_states", torch.float16, T * Hv * D * D),
+        _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)), "gdn_tree_verify_store")
+
+
+def gdn_tree_persist_copy(dims, accepted_node, node_states, state_cache, slot_idx, ws, stream=None):
+    """Commit by copy: the accepted node's stored fp16 state into each sequence's slot."""
+    T, B, Hv, D = dims.total_nodes, dims.num_seqs, dims.num_v_heads, dims.head_dim
+    _check(load_library().gdn_tree_persist_copy(
+        ctypes.byref(dims), _ptr(accepted_node, "accepted_node", torch.int32, B),
+        _ptr(node_states, "node_states", torch.float16, T * Hv * D * D),
+        _ptr(state_cache, "state_cache", torch.float32, dims.num_slots * Hv * D * D),
+        _ptr(slot_idx, "slot_idx", torch.int32, B), _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)),
+        "gdn_tree_persist_copy")
 
 
 def gdn_chain_verify(dims, cu_nodes, q, k, v, a, b, state_cache, slot_idx, out=None, final_len=None,

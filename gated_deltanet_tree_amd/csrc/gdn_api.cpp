@@ -143,6 +143,50 @@ int gdn_tree_persist(const gdn_dims *dims, const void *k, const void *v, const f
     return launched(gdn::launch_persist_recurrent(p, dims->qkv_dtype, as_stream(stream)));
 }
 
+int gdn_tree_verify_store(const gdn_dims *dims, const void *q, const void *k, const void *v, const float *a,
+                          const float *b, const float *state_cache, const int32_t *slot_idx, float *out,
+                          uint16_t *node_states, const void *ws, size_t ws_bytes, void *stream) {
+    int rc = check_dims(dims, GDN_MAX_NODES);
+    if (rc) return rc;
+    if (!ws) return GDN_ERR_NULL;
+    if (dims->total_nodes > 0 && (!q || !k || !v || !a || !b || !out || !node_states)) return GDN_ERR_NULL;
+    if (dims->num_seqs > 0 && (!state_cache || !slot_idx)) return GDN_ERR_NULL;
+    if (ws_bytes < gdn_workspace_bytes(dims)) return GDN_ERR_WORKSPACE;
+    if (dims->num_seqs == 0 || dims->total_nodes == 0) return GDN_OK;
+    Params p = base_params(dims);
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.a = a;
+    p.b = b;
+    p.state_in = state_cache;
+    p.slot_idx = slot_idx;
+    p.out = out;
+    p.node_states = node_states;
+    p.ws = gdn::ws_ptrs(const_cast<void *>(ws), p.B, p.T, p.Hv);
+    p.has_ws = 1;
+    return launched(gdn::launch_tree_verify_store(p, dims->qkv_dtype, as_stream(stream)));
+}
+
+int gdn_tree_persist_copy(const gdn_dims *dims, const int32_t *accepted_node, const uint16_t *node_states,
+                          float *state_cache, const int32_t *slot_idx, void *ws, size_t ws_bytes, void *stream) {
+    int rc = check_dims(dims, GDN_MAX_NODES);
+    if (rc) return rc;
+    if (!ws) return GDN_ERR_NULL;
+    if (dims->num_seqs > 0 && (!accepted_node || !state_cache || !slot_idx)) return GDN_ERR_NULL;
+    if (dims->total_nodes > 0 && !node_states) return GDN_ERR_NULL;
+    if (ws_bytes < gdn_workspace_bytes(dims)) return GDN_ERR_WORKSPACE;
+    if (dims->num_seqs == 0 || dims->total_nodes == 0) return GDN_OK;
+    Params p = base_params(dims);
+    p.accepted = accepted_node;
+    p.node_states = const_cast<uint16_t *>(node_states);
+    p.state_out = state_cache;
+    p.slot_idx = slot_idx;
+    p.ws = gdn::ws_ptrs(ws, p.B, p.T, p.Hv);
+    p.has_ws = 1;
+    return launched(gdn::launch_persist_copy(p, as_stream(stream)));
+}
+
 int gdn_chain_verify(const gdn_dims *dims, const int32_t *cu_nodes, const void *q, const void *k,
                      const void *v, const float *a, const float *b, const float *state_cache,
                      const int32_t *slot_idx, float *out, const int32_t *final_len,

@@ -92,6 +92,8 @@ struct Params {
     const int32_t *draft_token;  // [T]
     int32_t *accepted_out, *accept_len_out, *next_token_out, *target_out;
     int vocab, chunks, chunk_len;
+    // per-node states stored in fp16 (verify-and-store / persist-by-copy)
+    uint16_t *node_states;       // [T][Hv][D][D] fp16 bits
 };
 
 // ---- kernel launchers (defined in the .hip files) --------------------------
@@ -99,6 +101,10 @@ hipError_t launch_plan(const Params &p, hipStream_t s);
 hipError_t launch_tree_verify_recurrent(const Params &p, int dtype, hipStream_t s);
 hipError_t launch_chain_verify_recurrent(const Params &p, int dtype, hipStream_t s);
 hipError_t launch_persist_recurrent(const Params &p, int dtype, hipStream_t s);
+// the per-node-state design: recurrent verify that also stores every node's
+// state in fp16, and a persist that copies the accepted node's stored state
+hipError_t launch_tree_verify_store(const Params &p, int dtype, hipStream_t s);
+hipError_t launch_persist_copy(const Params &p, hipStream_t s);
 // MFMA path (D in {64, 128}, bf16 q/k/v)
 bool fast_path_supported(int D, int dtype);
 bool fast_tree_supported(int D, int dtype, int max_nodes);

@@ -14,6 +14,8 @@
 // verified by the tree kernel, by the chain kernel, and the state the persist
 // kernel writes for a path are bitwise identical.  Compiled without FP
 // contraction; every fused multiply-add is an explicit fmaf.
+#include <hip/hip_fp16.h>
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -76,6 +78,18 @@ __device__ __forceinline__ void store_state(float *row_base, int j, const float 
     for (int c = 0; c < Geo<D>::NCH; ++c)
         *reinterpret_cast<float4 *>(row_base + col_of<D>(j, c)) =
             make_float4(S[4 * c + 0], S[4 * c + 1], S[4 * c + 2], S[4 * c + 3]);
+}
+
+// the lane's columns of a state row, rounded to fp16 (nearest, ties to even)
+template <int D>
+__device__ __forceinline__ void store_state_f16(uint16_t *row_base, int j, const float (&S)[Geo<D>::CPL]) {
+#pragma unroll
+    for (int c = 0; c < Geo<D>::NCH; ++c) {
+        const __half2 lo = __floats2half2_rn(S[4 * c + 0], S[4 * c + 1]);
+        const __half2 hi = __floats2half2_rn(S[4 * c + 2], S[4 * c + 3]);
+        *reinterpret_cast<uint2 *>(row_base + col_of<D>(j, c)) =
+            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+    }
 }
 
 // DPP lane exchange inside a row of 16 lanes.
@@ -148,9 +162,12 @@ __device__ __forceinline__ Tile tile_of(const Params &P) {
 
 // ---------------------------------------------------------------------------
 // Tree verify: walk the plan's preorder, keep the state in VGPRs, save
-// states that later siblings need on an LDS stack.
+// states that later siblings need on an LDS stack.  STORE also writes every
+// node's state (leaves included) in fp16 to P.node_states: the pages' own
+// tree path, which keeps per-node states for the later commit (GreenGames
+// page, "Key wins": the f16 intermediate cache).
 // ---------------------------------------------------------------------------
-template <int D, typename Tin>
+template <int D, typename Tin, bool STORE>
 __global__ __launch_bounds__(64) void tree_verify_kernel(Params P) {
     using G = Geo<D>;
     extern __shared__ float4 lds_stack[];  // [stack_slots][NCH][64 lanes]
@@ -234,8 +251,12 @@ __global__ __launch_bounds__(64) void tree_verify_kernel(Params P) {
         const float c = write_coef(v, a, bb, u);
         const float o = fmaf(c, kq, a * w);
         if (t.j == 0) out[cur * out_stride] = o;
-        if (!(act & GDN_ACT_LEAF)) {
+        // a leaf's state is never a parent state (the next position restores
+        // or reloads), so updating it for the store changes nothing else
+        if (STORE || !(act & GDN_ACT_LEAF)) {
             update_row<G::CPL>(S, k, a, c);
+            if (STORE)
+                store_state_f16<D>(P.node_states + (((size_t)(lo + cur) * P.Hv + t.h) * D + t.row) * D, t.j, S);
             if ((act & GDN_ACT_PUSH) && sp < P.stack_slots) {  // the plan's order never exceeds the bound
                 __syncthreads();
                 float4 *dst = lds_stack + (size_t)sp * G::NCH * 64;
@@ -400,8 +421,48 @@ int grid_of(const Params &p) {
 template <int D, typename Tin>
 hipError_t launch_tree_d(const Params &p, hipStream_t s) {
     const size_t lds = (size_t)p.stack_slots * Geo<D>::NCH * 64 * sizeof(float4);
-    hipLaunchKernelGGL((tree_verify_kernel<D, Tin>), dim3(grid_of<D>(p)), dim3(64), lds, s, p);
+    hipLaunchKernelGGL((tree_verify_kernel<D, Tin, false>), dim3(grid_of<D>(p)), dim3(64), lds, s, p);
     return hipGetLastError();
+}
+template <int D, typename Tin>
+hipError_t launch_tree_store_d(const Params &p, hipStream_t s) {
+    const size_t lds = (size_t)p.stack_slots * Geo<D>::NCH * 64 * sizeof(float4);
+    hipLaunchKernelGGL((tree_verify_kernel<D, Tin, true>), dim3(grid_of<D>(p)), dim3(64), lds, s, p);
+    return hipGetLastError();
+}
+
+// Persist by copy: the accepted node's stored fp16 state, widened exactly to
+// fp32, into the sequence's slot; one workgroup per (sequence, value head)
+constexpr int kCopyThreads = 256;
+__global__ __launch_bounds__(kCopyThreads) void persist_copy_kernel(Params P) {
+    const int b = blockIdx.x / P.Hv, h = blockIdx.x % P.Hv;
+    if (!planned(P)) return;
+    const int lo = P.ws.seq_info[b * kSeqInfoInts + 0];
+    const int n = P.ws.seq_info[b * kSeqInfoInts + 1];
+    if (P.ws.seq_status[b] != GDN_SEQ_OK || n == 0) return;
+    const int m = P.accepted[b];
+    if (m < -1 || m >= n) {
+        if (h == 0 && threadIdx.x == 0) P.ws.seq_status[b] = GDN_SEQ_BAD_ACCEPT;
+        return;
+    }
+    if (m == -1) return;
+    const int slot = P.slot_idx[b];
+    const size_t dd = (size_t)P.D * P.D;
+    const uint4 *src = reinterpret_cast<const uint4 *>(P.node_states + ((size_t)(lo + m) * P.Hv + h) * dd);
+    float4 *dst = reinterpret_cast<float4 *>(P.state_out + ((size_t)slot * P.Hv + h) * dd);
+    for (size_t i = threadIdx.x; i < dd / 8; i += kCopyThreads) {  // 8 values per step
+        const uint4 w = src[i];
+        const uint32_t e[4] = {w.x, w.y, w.z, w.w};
+        float f[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float2 two = __half22float2(__builtin_bit_cast(__half2, e[k]));
+            f[2 * k] = two.x;
+            f[2 * k + 1] = two.y;
+        }
+        dst[2 * i] = make_float4(f[0], f[1], f[2], f[3]);
+        dst[2 * i + 1] = make_float4(f[4], f[5], f[6], f[7]);
+    }
 }
 template <int D, typename Tin>
 hipError_t launch_chain_d(const Params &p, hipStream_t s) {
@@ -439,6 +500,15 @@ hipError_t launch_chain_verify_recurrent(const Params &p, int dtype, hipStream_t
 hipError_t launch_persist_recurrent(const Params &p, int dtype, hipStream_t s) {
     if (p.B == 0) return hipSuccess;
     GDN_DISPATCH(launch_persist_d, p, dtype, s);
+}
+hipError_t launch_tree_verify_store(const Params &p, int dtype, hipStream_t s) {
+    if (p.B == 0) return hipSuccess;
+    GDN_DISPATCH(launch_tree_store_d, p, dtype, s);
+}
+hipError_t launch_persist_copy(const Params &p, hipStream_t s) {
+    if (p.B == 0) return hipSuccess;
+    hipLaunchKernelGGL(persist_copy_kernel, dim3(p.B * p.Hv), dim3(kCopyThreads), 0, s, p);
+    return hipGetLastError();
 }
 
 }  // namespace gdn

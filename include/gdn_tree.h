@@ -167,6 +167,29 @@ int gdn_tree_persist(const gdn_dims *dims, const void *k, const void *v, const f
                      const int32_t *slot_idx, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * gdn_tree_verify_store and gdn_tree_persist_copy -- the pages' own tree path,
+ * kept for comparison (GreenGames page, "Key wins": verify writes every node's
+ * state to an f16 intermediate cache and the commit copies the accepted one;
+ * "half the bandwidth" of fp32 states, about 1.5 MiB per node per layer at
+ * 48 value heads of 128 x 128).  gdn_tree_verify_store computes the same
+ * outputs as gdn_tree_verify with the per-node recurrent kernel (any head dim
+ * and dtype) and also writes each node's post-update state, rounded to fp16
+ * (nearest, ties to even), into node_states (fp16 bits, [T][H_v][D_v][D_k]).
+ * gdn_tree_persist_copy then writes, for each sequence b with
+ * accepted_node[b] = m >= 0, the stored state of node m widened to fp32 into
+ * state_cache[slot_idx[b]] (-1 skips; an out-of-range m marks the sequence
+ * GDN_SEQ_BAD_ACCEPT).  The fp16 rounding makes the persisted state differ
+ * from gdn_tree_persist's fp32 replay (relative error up to 2^-11 per value),
+ * so the chain bit-identity of the replay path does not hold here.  Both
+ * calls need `ws` from gdn_tree_plan; persist_copy does not record the path.
+ */
+int gdn_tree_verify_store(const gdn_dims *dims, const void *q, const void *k, const void *v, const float *a,
+                          const float *b, const float *state_cache, const int32_t *slot_idx, float *out,
+                          uint16_t *node_states, const void *ws, size_t ws_bytes, void *stream);
+int gdn_tree_persist_copy(const gdn_dims *dims, const int32_t *accepted_node, const uint16_t *node_states,
+                          float *state_cache, const int32_t *slot_idx, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * gdn_chain_verify -- the W = 1 case: sequence b is the linear chain of nodes
  * [cu_nodes[b], cu_nodes[b+1]) (no parent array, no plan, no depth limit;
  * lengths up to dims.max_nodes <= GDN_MAX_CHAIN).  Writes o for every node
