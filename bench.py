@@ -400,7 +400,7 @@ def bench_snapshot(G, cfg, sets, slot_d, rotate, layers, steps):
     gbs = nbytes / t / 1e9
     return {"slots": B, "call_us": t * 1e6, "bytes": nbytes,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("snapshot", cfg.name)}}
 
 
 # the sources each measured kernel is built from: counters recorded for one of
@@ -410,6 +410,7 @@ KERNEL_SOURCES = {
     "persist": ("gdn_fast.hip", "gdn_internal.h"),
     "accept": ("gdn_accept.hip", "gdn_internal.h"),
     "draft_topk": ("gdn_ddtree.hip", "gdn_internal.h"),
+    "snapshot": ("gdn_snapshot.hip", "gdn_internal.h"),
 }
 
 
