@@ -14,6 +14,11 @@ A one-layer workload (R >= 4) persists on the copy half a rotation away from
 the one verify read: in a model, the other layers' verify calls separate a
 layer's verify from its persist.
 
+The timed loop replays the step as a HIP graph per rotation copy (the same
+library calls, captured once; `--eager` times host launches instead).  A
+separate eager pass with an event pair around every call gives the per-call
+breakdown.
+
 Prints ONE JSON line.  `value` = tree nodes verified per second per layer call
 (plan + verify + persist); `roofline` describes the dominant kernel, timed with
 HIP events on the stream it runs on; `cpu_baseline` times the fp64 CPU oracle
@@ -51,6 +56,7 @@ def parse():
     ap.add_argument("--no-snapshot", action="store_true", help="skip the prefix-cache snapshot measurement")
     ap.add_argument("--no-store-path", action="store_true",
                     help="skip the per-node fp16 state path (verify-and-store + persist-by-copy) comparison")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of HIP graph replays")
     ap.add_argument("--path", choices=["auto", "recurrent"], default="auto",
                     help="recurrent: run the per-node recurrent kernels on every call (GDN_KERNEL_PATH)")
     return ap.parse_args()
@@ -180,11 +186,39 @@ def main():
         print(json.dumps({"error": "library rejected the workload: %d %d %d" % (rc, bad, code)}))
         sys.exit(1)
 
-    # main timed loop: exactly K steps, synchronize on both sides
+    # per-call breakdown: K eager steps with an event pair around every call
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(args.warmup + i, ev[i])
+    torch.cuda.synchronize()
+    eager_ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # main timed loop: exactly K steps, each one HIP graph replay of the step for
+    # its rotation copy (the same calls, without the host's launch gaps)
+    graphs = []
+    if not args.eager:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for r in range(rotate):
+                step(r)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        for r in range(rotate):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(r)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % rotate].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if graphs:
+            graphs[(args.warmup + i) % rotate].replay()
+        else:
+            step(args.warmup + i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
@@ -234,7 +268,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "sequences": cfg.num_seqs, "layers": layers, "nodes": T,
                    "v_heads": cfg.num_v_heads, "k_heads": cfg.num_k_heads, "head_dim": cfg.head_dim,
-                   "qkv": cfg.dtype, "rotated_copies": rotate, "seed": cfg.seed, "kernels": args.path},
+                   "qkv": cfg.dtype, "rotated_copies": rotate, "seed": cfg.seed, "kernels": args.path,
+                   "launch": "eager" if args.eager else "hip_graph"},
+        "eager_ms_per_step": eager_ms_per_step,
         "layer_call": {"verify_us": t_ver * 1e6, "persist_us": t_per * 1e6, "plan_us": t_plan * 1e6,
                        "verify_bytes": vbytes, "persist_bytes": pbytes, "hbm_gbs": hbm_gbs,
                        "hbm_frac": hbm_gbs / HBM_PEAK_GBS,
