@@ -14,8 +14,9 @@ A one-layer workload (R >= 4) persists on the copy half a rotation away from
 the one verify read: in a model, the other layers' verify calls separate a
 layer's verify from its persist.
 
-The timed loop replays the step as a HIP graph per rotation copy (the same
-library calls, captured once; `--eager` times host launches instead).  A
+The timed loop replays the steps as a HIP graph holding one rotation cycle of
+consecutive steps (the same library calls, captured once; `--eager` times host
+launches instead).  A
 separate eager pass with an event pair around every call gives the per-call
 breakdown.
 
@@ -194,9 +195,11 @@ def main():
     torch.cuda.synchronize()
     eager_ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
-    # main timed loop: exactly K steps, each one HIP graph replay of the step for
-    # its rotation copy (the same calls, without the host's launch gaps)
-    graphs = []
+    # main timed loop: exactly K steps as HIP graph replays (the same calls, without
+    # the host's launch gaps).  One graph holds one rotation cycle of consecutive
+    # steps (copies 0 .. R-1): each graph launch costs the GPU several microseconds,
+    # which a decode loop pays per launch, not per step.
+    cycle = None
     if not args.eager:
         side = torch.cuda.Stream()
         side.wait_stream(stream)
@@ -205,19 +208,21 @@ def main():
                 step(r)
         stream.wait_stream(side)
         torch.cuda.synchronize()
-        for r in range(rotate):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
+        cycle = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cycle):
+            for r in range(rotate):
                 step(r)
-            graphs.append(g)
-        for i in range(args.warmup):
-            graphs[i % rotate].replay()
+        cycle.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        if graphs:
-            graphs[(args.warmup + i) % rotate].replay()
-        else:
+    if cycle is not None:
+        full, rest = divmod(args.steps, rotate)
+        for _ in range(full):
+            cycle.replay()
+        for i in range(rest):  # a partial cycle runs eagerly
+            step(i)
+    else:
+        for i in range(args.steps):
             step(args.warmup + i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -269,7 +274,7 @@ def main():
         "config": {"workload": cfg.name, "sequences": cfg.num_seqs, "layers": layers, "nodes": T,
                    "v_heads": cfg.num_v_heads, "k_heads": cfg.num_k_heads, "head_dim": cfg.head_dim,
                    "qkv": cfg.dtype, "rotated_copies": rotate, "seed": cfg.seed, "kernels": args.path,
-                   "launch": "eager" if args.eager else "hip_graph"},
+                   "launch": "eager" if args.eager else "hip_graph_per_%d_steps" % rotate},
         "eager_ms_per_step": eager_ms_per_step,
         "layer_call": {"verify_us": t_ver * 1e6, "persist_us": t_per * 1e6, "plan_us": t_plan * 1e6,
                        "verify_bytes": vbytes, "persist_bytes": pbytes, "hbm_gbs": hbm_gbs,

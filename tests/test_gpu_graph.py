@@ -1,6 +1,7 @@
-"""The decode step captured in a HIP graph (plan -> verify -> persist), as the
-bench replays it: every replay, with eager work and synchronizations in
-between, must reproduce the eager step bit for bit."""
+"""Decode steps captured in a HIP graph (plan -> verify -> persist, two
+consecutive steps per graph, as the bench replays a cycle of steps): every
+replay, with eager work and synchronizations in between, must reproduce the
+eager steps bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -24,6 +25,7 @@ def test_graph_replays_match_eager(name):
         G.gdn_tree_persist(d["dims"], d["k"], d["v"], d["a"], d["b"], d["acc"], d["cache"], d["slots"], d["ws"])
 
     step()
+    step()  # the second step verifies against the first one's persisted states
     torch.cuda.synchronize()
     want_out = d["out"].cpu().numpy().copy()
     want_cache = d["cache"].cpu().numpy().copy()
@@ -37,6 +39,7 @@ def test_graph_replays_match_eager(name):
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
+        step()
         step()
     for rep in range(4):
         d["cache"].copy_(pristine)
