@@ -1101,10 +1101,15 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
             }
         }
         __syncthreads();
-        // X_j for every block in one pass over the state (independent MFMA chains)
-        f32x16 X[NB];
+        // X_j = K_j S0^T and Y_t = Q_t S0^T for every block in one pass over the state:
+        // the state is split once per k-step and the 2 NB accumulations are independent
+        // MFMA chains
+        f32x16 X[NB], Y[NB];
 #pragma unroll
-        for (int jb = 0; jb < NB; ++jb) X[jb] = f32x16{};
+        for (int jb = 0; jb < NB; ++jb) {
+            X[jb] = f32x16{};
+            Y[jb] = f32x16{};
+        }
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             bf16x8 shi, slo;
@@ -1118,8 +1123,11 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
             for (int jb = 0; jb < NB; ++jb) {
                 if (jb < nb) {
                     const bf16x8 Ak = frag_of(L.kq + (jb * kTile + l32) * Q::KQ, s, hf);
+                    const bf16x8 Aq = frag_of(L.kq + (NN + jb * kTile + l32) * Q::KQ, s, hf);
                     X[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, shi, X[jb], 0, 0, 0);
+                    Y[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, shi, Y[jb], 0, 0, 0);
                     X[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, slo, X[jb], 0, 0, 0);
+                    Y[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, slo, Y[jb], 0, 0, 0);
                 }
             }
         }
@@ -1138,37 +1146,22 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
                 const __bf16 rb = static_cast<__bf16>(rv);
                 rhi[jb][r / 8][r % 8] = rb;
                 rlo[jb][r / 8][r % 8] = static_cast<__bf16>(rv - static_cast<float>(rb));
+                // gamma Y_t, the start of block t's outputs
+                Y[jb][r] = i < n ? q4.x * Y[jb][r] : 0.0f;
             }
         }
-        // O_t = gamma Y_t + sum_j MT_tj R_j, Y_t taken just before its outputs
+        // O_t = gamma Y_t + sum_j MT_tj R_j: for each operand block j, the NB output
+        // blocks' accumulations are independent chains
 #pragma unroll
-        for (int t = 0; t < NB; ++t) {
-            if (t < nb) {
-                f32x16 ay = {};
+        for (int jb = 0; jb < NB; ++jb) {
+            if (jb < nb) {
 #pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    bf16x8 shi, slo;
+                for (int u = 0; u < 2; ++u) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const __bf16 hb = static_cast<__bf16>(st[s][e]);
-                        shi[e] = hb;
-                        slo[e] = static_cast<__bf16>(st[s][e] - static_cast<float>(hb));
-                    }
-                    const bf16x8 Aq = frag_of(L.kq + (NN + t * kTile + l32) * Q::KQ, s, hf);
-                    ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, shi, ay, 0, 0, 0);
-                    ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, slo, ay, 0, 0, 0);
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int i = t * kTile + 8 * (r / 4) + 4 * hf + (r % 4);
-                    ay[r] = i < n ? gab[min(i, n - 1)].x * ay[r] : 0.0f;
-                }
-                const uint16_t *mh = L.mth + (t * kTile + l32) * Q::MS, *ml = L.mtl + (t * kTile + l32) * Q::MS;
-#pragma unroll
-                for (int jb = 0; jb < NB; ++jb) {
-                    if (jb < nb) {
-#pragma unroll
-                        for (int u = 0; u < 2; ++u) {
+                    for (int t = 0; t < NB; ++t) {
+                        if (t < nb) {
+                            const uint16_t *mh = L.mth + (t * kTile + l32) * Q::MS;
+                            const uint16_t *ml = L.mtl + (t * kTile + l32) * Q::MS;
                             const int c0 = jb * kTile + 16 * u + 4 * hf;
                             const uint2 x0 = *reinterpret_cast<const uint2 *>(mh + c0);
                             const uint2 x1 = *reinterpret_cast<const uint2 *>(mh + c0 + 8);
@@ -1176,16 +1169,21 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
                             const uint2 y1 = *reinterpret_cast<const uint2 *>(ml + c0 + 8);
                             const bf16x8 ahi = __builtin_bit_cast(bf16x8, make_uint4(x0.x, x0.y, x1.x, x1.y));
                             const bf16x8 alo = __builtin_bit_cast(bf16x8, make_uint4(y0.x, y0.y, y1.x, y1.y));
-                            ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, rhi[jb][u], ay, 0, 0, 0);
-                            ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, rlo[jb][u], ay, 0, 0, 0);
-                            ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, rhi[jb][u], ay, 0, 0, 0);
+                            Y[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, rhi[jb][u], Y[t], 0, 0, 0);
+                            Y[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, rlo[jb][u], Y[t], 0, 0, 0);
+                            Y[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, rhi[jb][u], Y[t], 0, 0, 0);
                         }
                     }
                 }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+            if (t < nb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int i = t * kTile + 8 * (r / 4) + 4 * hf + (r % 4);
-                    if (i < n) P.out[((size_t)(lo + i) * P.Hv + h0 + hh) * D + row] = ay[r];
+                    if (i < n) P.out[((size_t)(lo + i) * P.Hv + h0 + hh) * D + row] = Y[t][r];
                 }
             }
         }
