@@ -1,4 +1,4 @@
-// gdn_fast.hip -- tree verify (MFMA) and accepted-path replay (VALU) for
+// gdn_fast.hip -- tree verify and accepted-path replay on the matrix cores for
 // D in {64, 128} with bf16 q/k/v.
 //
 // Unrolling the gated delta rule along a root-to-node path gives, for node n
@@ -12,10 +12,10 @@
 // value head), done on the matrix cores -- plus, per state row, a short
 // recurrence over each node's ancestors.  Verify never materializes a state.
 // Replay (persist) needs S^m for one root-to-node path of <= 16 nodes: it
-// reads S0 once, forms S0 k_e for the path keys with VALU dot products, runs
-// the same recurrence and writes G_m S0 + sum_e R(m,e) c_e k_e^T in place.
+// reads S0 once, forms S0 k_e for the path keys on the matrix cores, runs the
+// same recurrence per row and writes G_m S0 + sum_e R(m,e) c_e k_e^T in place
+// as a rank-16 update accumulated onto the scaled state.
 #include <algorithm>
-
 
 #include "gdn_internal.h"
 
