@@ -276,11 +276,6 @@ int gdn_ddtree_build(int32_t num_seqs, int32_t levels, int32_t width, int32_t bu
     if (!cu_nodes) return GDN_ERR_NULL;
     if (num_seqs > 0 && (!tokens || !logp || !parent || !node_token)) return GDN_ERR_NULL;
     if ((long long)num_seqs * n > INT_MAX) return GDN_ERR_SHAPE;
-    if (num_seqs == 0) {  // cu_nodes = {0}
-        const int32_t zero = 0;
-        return hipMemcpyAsync(cu_nodes, &zero, 4, hipMemcpyHostToDevice, as_stream(stream)) == hipSuccess
-                   ? GDN_OK : GDN_ERR_LAUNCH;
-    }
     return launched(gdn::launch_ddtree_build(num_seqs, levels, width, budget, max_depth, root_token, tokens, logp,
                                              parent, node_token, cu_nodes, as_stream(stream)));
 }

@@ -390,6 +390,8 @@ __global__ __launch_bounds__(64) void build_kernel(BuildArgs A) {
     }
 }
 
+__global__ void cu_zero_kernel(int32_t *cu_nodes) { cu_nodes[0] = 0; }
+
 }  // namespace
 
 int ddtree_nodes(int levels, int width, int budget, int max_depth) {
@@ -439,6 +441,10 @@ hipError_t launch_ddtree_build(int B, int levels, int width, int budget, int max
     A.parent = parent;
     A.node_token = node_token;
     A.cu_nodes = cu_nodes;
+    if (B == 0) {  // no trees: cu_nodes = {0}
+        hipLaunchKernelGGL(cu_zero_kernel, dim3(1), dim3(1), 0, s, cu_nodes);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(build_kernel, dim3(B), dim3(64), 0, s, A);
     return hipGetLastError();
 }

@@ -125,7 +125,7 @@ typedef struct gdn_dims {
     int32_t qkv_dtype;   /* gdn_dtype of q, k, v */
 } gdn_dims;
 
-/* Bytes of workspace gdn_tree_plan/verify/persist need for these dims
+/* Bytes of workspace gdn_tree_plan/verify/persist/accept need for these dims
    (0 if the dims are invalid).  The caller allocates it (device memory, no
    initialization needed); one workspace serves one decode step. */
 size_t gdn_workspace_bytes(const gdn_dims *dims);

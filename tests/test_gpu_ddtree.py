@@ -209,3 +209,13 @@ def test_pipeline_topk_build_plan_accept():
     for g, e in zip(outs, ea[:3]):
         g = g.cpu().numpy()
         assert np.array_equal(g[exact_seqs], e[exact_seqs])
+
+
+def test_builder_no_sequences():
+    G = require_gpu()
+    cu = torch.full((1,), -9, dtype=torch.int32, device="cuda")
+    e = torch.empty(0, dtype=torch.int32, device="cuda")
+    G.gdn_ddtree_build(None, torch.empty((0, 15, 4), dtype=torch.int32, device="cuda"),
+                       torch.empty((0, 15, 4), dtype=torch.float32, device="cuda"), 22, e, e, cu)
+    torch.cuda.synchronize()
+    assert cu.item() == 0
