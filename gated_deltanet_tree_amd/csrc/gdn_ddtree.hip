@@ -178,6 +178,33 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(int vocab, int width
             float4 r[kTopkUnroll];
 #pragma unroll
             for (int u = 0; u < kTopkUnroll; ++u) r[u] = x4[base + u * kTopkThreads + tid];
+            if (base == 0) {
+                // a first floor from the first block: the WT-th largest of the lanes' own
+                // maxima (WT distinct entries at least that large)
+                float lm = -INFINITY;
+#pragma unroll
+                for (int u = 0; u < kTopkUnroll; ++u)
+                    lm = fmaxf(lm, fmaxf(fmaxf(r[u].x, r[u].y), fmaxf(r[u].z, r[u].w)));
+                float f = -INFINITY;
+                bool taken = false;
+#pragma unroll 1
+                for (int k = 0; k < WT; ++k) {
+                    float bv = taken ? -INFINITY : lm;
+                    int bl = taken ? 64 : lane;
+#pragma unroll
+                    for (int off = 32; off >= 1; off >>= 1) {
+                        const float ov = __shfl_xor(bv, off);
+                        const int ol = __shfl_xor(bl, off);
+                        if (ov > bv || (ov == bv && ol < bl)) {
+                            bv = ov;
+                            bl = ol;
+                        }
+                    }
+                    taken = taken || bl == lane;
+                    f = bv;
+                }
+                floor_v = f;
+            }
 #pragma unroll
             for (int u = 0; u < kTopkUnroll; ++u) eat(r[u], base + u * kTopkThreads + tid, true);
         }
