@@ -132,10 +132,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(int vocab, int width
     // Entries at or above the wave's floor (and NaNs) are appended to the wave's
     // candidate buffer; a full buffer is folded into the lanes' lists (each lane
     // takes every 64th entry; the lists compare ids on equal values, so the
-    // order of offers does not matter) and the floor is raised.  With a good floor almost
-    // every entry is dismissed by one comparison.
-    float floor_v = -INFINITY;  // wave-uniform
-    int cnt = 0;                // wave-uniform
+    // order of offers does not matter) and the floor is raised.  With a good
+    // floor almost every entry is dismissed by one comparison.
+    // floor_v is the same on every lane except after a lane saw only NaNs, when at
+    // least W NaNs lead the row and any floor keeps them (a NaN always passes)
+    float floor_v = -INFINITY;
+    int cnt = 0;  // wave-uniform
     const unsigned long long below = (1ull << lane) - 1ull;
     auto fold = [&]() {
         for (int k = lane; k < cnt; k += 64) L.offer(c_v[w][k], c_i[w][k]);
