@@ -65,7 +65,10 @@ def parse():
 
 
 def algorithmic_bytes(cfg, T, path_lens, s_in):
-    """Bytes the method must move per layer call."""
+    """Bytes the method must move per layer call: verify reads every sequence's
+    committed state once, the node inputs (q, k, v at s_in bytes, gates at 4) and the
+    tree indices, and writes one output row per (node, value head); persist reads and
+    writes each state once and reads the inputs of the accepted path's nodes (no q)."""
     B, Hk, Hv, D = cfg.num_seqs, cfg.num_k_heads, cfg.num_v_heads, cfg.head_dim
     state = B * Hv * D * D * 4
     verify = state + T * (2 * Hk * D + Hv * D) * s_in + T * Hv * 8 + T * Hv * D * 4 + 4 * (T + 2 * B + 1)
@@ -77,8 +80,9 @@ def algorithmic_bytes(cfg, T, path_lens, s_in):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; --gpus %d is not supported "
-                                   "(the path shards with no exchange; see DESIGN.md)" % args.gpus}))
+        print(json.dumps({"error": "this benchmark measures one GPU; --gpus %d is not supported "
+                                   "(sequences shard across GPUs with no exchange, so one GPU's "
+                                   "share at its real shape is the measured unit)" % args.gpus}))
         sys.exit(2)
     if args.path == "recurrent":
         os.environ["GDN_KERNEL_PATH"] = "recurrent"
