@@ -14,6 +14,13 @@ namespace {
 
 constexpr int kPlanDupPer = 2;  // other sequences checked per thread from registers
 
+// workgroup-wide "any": a ballot when the workgroup is one wave (no LDS round trip)
+template <int NT>
+__device__ __forceinline__ bool wg_any(bool pred) {
+    if constexpr (NT == 64) return __ballot(pred) != 0ull;
+    else return __syncthreads_or(pred) != 0;
+}
+
 // NT threads, one per node: NT = 64 (a single wave, whose barriers cost nothing)
 // when every tree fits, else NT = GDN_MAX_NODES
 template <int NT>
@@ -77,7 +84,7 @@ __global__ __launch_bounds__(NT) void plan_kernel(Params P) {
                 const bool ok2 = 0 <= lo2 && lo2 <= hi2 && hi2 <= P.T && hi2 - lo2 <= P.max_nodes;
                 if (o != b && ok2 && hi2 > lo2 && P.slot_idx[o] == slot) dup = 1;
             }
-            if (__syncthreads_or(dup)) status = GDN_SEQ_DUP_SLOT;
+            if (wg_any<NT>(dup)) status = GDN_SEQ_DUP_SLOT;
         }
     }
 
@@ -86,7 +93,7 @@ __global__ __launch_bounds__(NT) void plan_kernel(Params P) {
     if (status == GDN_SEQ_OK && n > 0) {
         if (t < n) par = P.parent[lo + t];
         const bool bad = t < n && !(par == -1 || (par >= 0 && par < n && par != t));
-        if (__syncthreads_or(bad)) status = GDN_SEQ_BAD_PARENT;
+        if (wg_any<NT>(bad)) status = GDN_SEQ_BAD_PARENT;
     }
 
     // ---- depth: every ancestor walk must reach a root within max_depth nodes -----
@@ -110,7 +117,7 @@ __global__ __launch_bounds__(NT) void plan_kernel(Params P) {
             }
             deep = x != -1;
         }
-        if (__syncthreads_or(deep)) status = GDN_SEQ_CYCLE_OR_DEPTH;
+        if (wg_any<NT>(deep)) status = GDN_SEQ_CYCLE_OR_DEPTH;
     }
 
     if (status == GDN_SEQ_OK && n > 0) {
@@ -123,7 +130,22 @@ __global__ __launch_bounds__(NT) void plan_kernel(Params P) {
         }
         __syncthreads();
         // siblings visited before this node (smaller (size, id)) and after it
-        if (t < n) {
+        if constexpr (NT == 64) {
+            // one wave: node s2's parent and size come from lane s2's registers
+            const int my = s_size[t];
+            int off = 0, later = 0;
+            for (int s2 = 0; s2 < n; ++s2) {
+                const int ps = __builtin_amdgcn_readlane(par, s2), ss = __builtin_amdgcn_readlane(my, s2);
+                const bool sib = ps == par && s2 != t;
+                const bool before = ss < my || (ss == my && s2 < t);
+                off += (sib && before) ? ss : 0;
+                later += (sib && !before) ? 1 : 0;
+            }
+            if (t < n) {
+                s_off[t] = off;
+                s_later[t] = later;
+            }
+        } else if (t < n) {
             const int my = s_size[t];
             int off = 0, later = 0;
 #pragma unroll 8
