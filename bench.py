@@ -41,6 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published (256 CUs, 2.4 GHz, packed FMA)
 
 
 def parse():
@@ -77,6 +78,23 @@ def algorithmic_bytes(cfg, T, path_lens, s_in):
     return verify, persist
 
 
+def verify_flops(cfg, trees):
+    """Arithmetic of the rule itself per layer call, as a node-by-node walk would do it
+    in fp32: per (node, value head) S k and S q (2 D^2 each) and the rank-1 update
+    (3 D^2) where the node has children, or just S k, S q and o = a (S q) + c (k . q)
+    (4 D^2) at a leaf, whose updated state is never needed."""
+    D2, Hv = cfg.head_dim * cfg.head_dim, cfg.num_v_heads
+    total = 0
+    for par in trees:
+        n = len(par)
+        has_child = np.zeros(n, dtype=bool)
+        for p in par:
+            if p >= 0:
+                has_child[int(p)] = True
+        total += (7 * int(has_child.sum()) + 4 * int(n - has_child.sum())) * D2 * Hv
+    return total
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -107,6 +125,7 @@ def main():
                        cfg.num_slots, qkv_dtype, max_depth=cfg.max_depth)
     path_lens = [int(W.tree_depths(t)[m]) for t, m in zip(trees, acc)]
     vbytes, pbytes = algorithmic_bytes(cfg, T, path_lens, s_in)
+    vflops = verify_flops(cfg, trees)
 
     def to_dev(x):
         if x.dtype == np.uint16:
@@ -314,6 +333,11 @@ def main():
     roof["kernel"] = dom
     roof["bytes_per_launch"] = dom_bytes
     roof["launch_us"] = t_dom * 1e6
+    # the rule's own arithmetic in verify against the fp32 vector peak: what a node-by-node
+    # fp32 walk of the same trees would need at least this long for
+    roof_alu = {"kernel": "tree_verify", "bound": "alu", "achieved": vflops / g_ver / 1e12,
+                "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s", "flops_per_launch": vflops}
+    roof_alu["frac"] = roof_alu["achieved"] / roof_alu["peak"]
     roof["launch_us_eager"] = t_dom_eager * 1e6
 
     result = {
@@ -345,6 +369,7 @@ def main():
                        "timing": "graph replay of each call alone over the rotation",
                        "eager": {"verify_us": t_ver * 1e6, "persist_us": t_per * 1e6, "plan_us": t_plan * 1e6}},
         "roofline": roof,
+        "roofline_verify_alu": roof_alu,
     }
     if not args.no_accept:
         result["accept"] = bench_accept(G, W, cfg, trees, dims, parent_d, cu_d, slot_d, args.accept_steps)
