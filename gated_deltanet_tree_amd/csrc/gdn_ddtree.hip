@@ -34,7 +34,10 @@ __device__ __forceinline__ bool before(float v1, int i1, float v2, int i2) {
     return v1 > v2 || (v1 == v2 && i1 < i2);
 }
 
-constexpr int kTopkThreads = 512;
+// threads per row: 1024 for the short lists (more loads in flight per row), 512 from
+// W = 8 on, where the lists' own work grows with the wave count
+template <int WT>
+constexpr int topk_threads() { return WT <= 4 ? 1024 : 512; }
 constexpr int kTopkUnroll = 4;
 
 template <int WT>
@@ -114,7 +117,7 @@ __device__ __forceinline__ float wave_floor(const TopList<WT> &L) {
 
 constexpr int kCandBuf = 512;  // per-wave candidate buffer (LDS entries)
 
-template <int WT, bool VEC>
+template <int WT, bool VEC, int kTopkThreads = topk_threads<WT>()>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(int vocab, int width, const float *logits,
                                                              int32_t *tokens, float *logp) {
     constexpr int NW = kTopkThreads / 64;
@@ -436,9 +439,10 @@ int ddtree_nodes(int levels, int width, int budget, int max_depth) {
 hipError_t launch_draft_topk(int rows, int vocab, int width, const float *logits, int32_t *tokens, float *logp,
                              hipStream_t s) {
     const bool vec = vocab % 4 == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0;
-    const dim3 grid(rows), block(kTopkThreads);
+    const dim3 grid(rows);
 #define GDN_TOPK_CASE(WT)                                                                                     \
     if (width <= WT) {                                                                                        \
+        const dim3 block(topk_threads<WT>());                                                                 \
         if (vec)                                                                                              \
             hipLaunchKernelGGL((topk_kernel<WT, true>), grid, block, 0, s, vocab, width, logits, tokens, logp);  \
         else                                                                                                  \

@@ -69,7 +69,7 @@ def test_topk_special_rows():
     G = require_gpu()
     rng = np.random.default_rng(1)
     V = 20000
-    x = rng.standard_normal((9, V)).astype(np.float32)
+    x = rng.standard_normal((10, V)).astype(np.float32)
     x[0, [17, 9000, 19999]] = np.nan
     x[1, :] = -np.inf
     x[2, 5000] = np.inf
@@ -80,12 +80,14 @@ def test_topk_special_rows():
     x[6, 100] = -3e38
     x[7, :] = np.float32(-1e30)
     x[7, 6] = np.nan
-    # every value one thread reads in the first block is NaN (16 of them), and a larger
-    # finite value elsewhere: the NaNs still lead
-    for u in range(4):
-        for c in range(4):
-            x[8, 4 * (u * 512 + 5) + c] = np.nan
-    x[8, 3] = 1e30
+    # every value one thread reads in the first block is NaN (16 of them: four 16-byte
+    # loads, one per 1024- or 512-thread stride for the short or the long lists), and a
+    # larger finite value elsewhere: the NaNs still lead
+    for row, threads in ((8, 1024), (9, 512)):
+        for u in range(4):
+            for c in range(4):
+                x[row, 4 * (u * threads + 5) + c] = np.nan
+        x[row, 3] = 1e30
     for width in (1, 4, 16):
         _check_topk(x, *_topk(G, x, width), width)
 
