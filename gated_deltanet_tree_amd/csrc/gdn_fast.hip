@@ -1085,9 +1085,15 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
             const int c = tid + u * NT;
             if (c < NN * (D / 8)) reinterpret_cast<uint4 *>(L.vst)[c] = vr[u];
         }
-        for (int c = tid; c < nb * kTile * Q::MS / 2; c += NT) {
-            reinterpret_cast<uint32_t *>(L.mth)[c] = 0u;
-            reinterpret_cast<uint32_t *>(L.mtl)[c] = 0u;
+        if (hh == 0) {
+            // every head's operator has its nonzeros at the same places (the ancestors), so
+            // clearing once, before the first head, leaves each later head's scatter a
+            // complete operator
+            static_assert(Q::MS % 8 == 0, "16-byte operator rows");
+            for (int c = tid; c < nb * kTile * Q::MS / 8; c += NT) {
+                reinterpret_cast<uint4 *>(L.mth)[c] = make_uint4(0u, 0u, 0u, 0u);
+                reinterpret_cast<uint4 *>(L.mtl)[c] = make_uint4(0u, 0u, 0u, 0u);
+            }
         }
         __syncthreads();
         for (int t = tid; t < n * kPath; t += NT) {
