@@ -78,6 +78,15 @@ def algorithmic_bytes(cfg, T, path_lens, s_in):
     return verify, persist
 
 
+def rotation(per_copy, layers):
+    """Independent copies the timed loop rotates through: enough that >= 512 MB separate
+    two reads of the same bytes (the Infinity Cache holds 256 MB), at least 4 for a
+    one-layer workload, and at most 128: below ~4 MB per copy (the batch-1 and tiny
+    workloads) the data is cache-sized whatever the rotation, and a graph of tens of
+    thousands of steps is more than the runtime should be asked to capture."""
+    return min(128, max(4 if layers == 1 else 1, int(np.ceil(512e6 / (per_copy * layers)))))
+
+
 def verify_flops(cfg, trees):
     """Arithmetic of the rule itself per layer call, as a node-by-node walk would do it
     in fp32: per (node, value head) S k and S q (2 D^2 each) and the rank-1 update
@@ -134,7 +143,7 @@ def main():
 
     layers = cfg.num_layers
     per_copy = vbytes + T * cfg.num_v_heads * cfg.head_dim * 4
-    rotate = args.rotate or max(4 if layers == 1 else 1, int(np.ceil(512e6 / (per_copy * layers))))
+    rotate = args.rotate or rotation(per_copy, layers)
     copies = layers * rotate
     print("# config %s: B=%d T=%d layers=%d copies=%d (%.0f MB per layer copy)"
           % (cfg.name, cfg.num_seqs, T, layers, copies, per_copy / 1e6), file=sys.stderr, flush=True)

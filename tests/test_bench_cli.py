@@ -22,3 +22,17 @@ def test_source_digest_ignores_comments_only():
         d = bench.kernel_source_digest(kernel)
         assert len(d) == 16 and d == bench.kernel_source_digest(kernel)
     assert bench.kernel_source_digest("persist") != bench.kernel_source_digest("accept")
+
+
+def test_rotation_bounds():
+    """Copies the timed loop rotates through: >= 512 MB between reuses for the big
+    workloads, at least 4 for one layer, at most 128 for cache-sized ones."""
+    sys.path.insert(0, ROOT)
+    import bench
+    assert bench.rotation(152e6, 1) == 4        # the 32-sequence workload
+    assert bench.rotation(404e6, 48) == 1       # 48 layers already exceed the cache
+    assert bench.rotation(4.3e6, 1) == 120      # one sequence of 16 nodes
+    assert bench.rotation(7e3, 1) == 128        # the tiny tree: capped
+    for per_copy in (1e3, 1e6, 5e6, 1e8, 1e9):
+        r = bench.rotation(per_copy, 1)
+        assert 4 <= r <= 128 and (r == 128 or r * per_copy >= 512e6 or r == 4)
