@@ -134,3 +134,51 @@ def test_stress_full_size_sampled():
                              ref.transpose(1, 0, 2).reshape(48, -1)) <= TOL, s
         st, _ = oracle.accept_state(trees[s], int(acc[s]), sl["k"], sl["v"], sl["a"], sl["b"], S0[s])
         assert slice_rel_err(after[slots[s]].reshape(48, -1), st.reshape(48, -1)) <= TOL, s
+
+
+def test_many_sequences():
+    """4096 sequences of 1-6 nodes in one call (8192 verify and 16384 persist
+    workgroups, 4096 plan workgroups each checking every other sequence's slot),
+    d=64 with two value heads per key head: sampled sequences against the oracle,
+    every output finite, spare slots untouched."""
+    G = require_gpu()
+    rng = np.random.default_rng(24)
+    B, hk, hv, d_ = 4096, 2, 4, 64
+    sizes = rng.integers(1, 7, size=B)
+    trees = [W.random_tree(rng, int(n), 16) for n in sizes]
+    cu = np.zeros(B + 1, np.int32)
+    cu[1:] = np.cumsum(sizes)
+    T = int(cu[-1])
+    inp = {"q": _bf(_unit(rng, T, hk, d_)), "k": _bf(_unit(rng, T, hk, d_)),
+           "v": _bf(rng.standard_normal((T, hv, d_))),
+           "a": rng.uniform(0.5, 1.0, (T, hv)).astype(np.float32),
+           "b": rng.uniform(0.0, 1.0, (T, hv)).astype(np.float32)}
+    n_slots = B + 4
+    slots = rng.permutation(n_slots)[:B].astype(np.int32)
+    cache = (0.3 * rng.standard_normal((n_slots, hv, d_, d_))).astype(np.float32)
+    acc = np.array([rng.integers(0, n) for n in sizes], np.int32)
+    dims = G.make_dims(B, T, int(sizes.max()), hk, hv, d_, n_slots, G.GDN_BF16)
+    ws = G.new_workspace(dims)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    cache_d = to_dev(cache)
+    slots_d = to_dev(slots)
+    out = torch.full((T, hv, d_), float("nan"), device="cuda")
+    G.gdn_tree_plan(dims, to_dev(np.concatenate(trees).astype(np.int32)), to_dev(cu), slots_d, ws)
+    G.gdn_tree_verify(dims, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], cache_d, slots_d, out, ws)
+    G.gdn_tree_persist(dims, dev["k"], dev["v"], dev["a"], dev["b"], to_dev(acc), cache_d, slots_d, ws)
+    rc, bad, code = G.gdn_tree_status(ws)
+    assert rc == 0, (rc, bad, code)
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    after = cache_d.cpu().numpy()
+    spare = np.setdiff1d(np.arange(n_slots), slots)
+    assert np.array_equal(after[spare].view(np.uint32), cache[spare].view(np.uint32))
+    for s in [0, 1, 2047, 4094, 4095] + list(rng.choice(B, 27, replace=False)):
+        lo, hi = int(cu[s]), int(cu[s + 1])
+        sl = {k: v[lo:hi] for k, v in inp.items()}
+        S0 = cache[slots[s]]
+        ref = oracle.tree(trees[s], sl["q"], sl["k"], sl["v"], sl["a"], sl["b"], S0)
+        assert slice_rel_err(got[lo:hi].transpose(1, 0, 2).reshape(hv, -1),
+                             ref.transpose(1, 0, 2).reshape(hv, -1)) <= TOL, s
+        st, _ = oracle.accept_state(trees[s], int(acc[s]), sl["k"], sl["v"], sl["a"], sl["b"], S0)
+        assert slice_rel_err(after[slots[s]].reshape(hv, -1), st.reshape(hv, -1)) <= TOL, s
