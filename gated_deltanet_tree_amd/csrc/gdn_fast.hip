@@ -847,7 +847,8 @@ verify_group_kernel(Params P) {
 // may sit in any block, so each head first takes X_j = K_j S0^T for all blocks
 // (R_j = diag(b)V_j - diag(alpha)X_j kept in registers), then per block t
 // O_t = diag(gamma)Y_t + sum_j MT_tj R_j, with MT (the output operator, rows
-// from the 16-step back substitution) rebuilt densely in LDS for each head.
+// from the 16-step back substitution) dense in LDS: cleared once, its entries
+// (the same places, the ancestors, for every head) rewritten per head.
 // All products run on bf16 MFMA with fp32 operands split hi + lo.
 // ===========================================================================
 template <int D, int NB>
