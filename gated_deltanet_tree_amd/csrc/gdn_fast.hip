@@ -934,6 +934,8 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
     const uint16_t *vg = static_cast<const uint16_t *>(P.v) + ((size_t)lo * P.Hv + h0) * D;
     const size_t kq_stride = (size_t)P.Hk * D;
     const float *s0 = P.state_in + ((size_t)sv.slot * P.Hv + h0) * D * D;
+    // out[node][h0 + hh][row]: uniform base per (node, head) + this lane's offset
+    const unsigned out_lane = (unsigned)(4 * hf * P.Hv * D + row);
     const unsigned s_lane = (unsigned)(row * D + 8 * hf);
     constexpr int V_PER = (NN * (D / 8) + NT - 1) / NT;  // 16-byte chunks of one head's values
     auto fetch_v = [&](int hh, uint4 (&vr)[V_PER]) {
@@ -1189,8 +1191,13 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
             if (t < nb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int i = t * kTile + 8 * (r / 4) + 4 * hf + (r % 4);
-                    if (i < n) P.out[((size_t)(lo + i) * P.Hv + h0 + hh) * D + row] = Y[t][r];
+                    // node of half-wave 0 (uniform; half-wave 1 adds 4): a uniform base
+                    // per (node, head) plus the lane's fixed offset
+                    const int ir = t * kTile + 8 * (r / 4) + (r % 4);
+                    if (ir + 4 * hf < n) {
+                        float *ob = P.out + ((size_t)(lo + ir) * P.Hv + h0 + hh) * D;
+                        ob[out_lane] = Y[t][r];
+                    }
                 }
             }
         }
