@@ -20,6 +20,15 @@ from oracle.literal import literal_rule, path_replay, path_of
 TINY_PARENT = np.array([-1, 0, 0, 1, 1, 2, 4], dtype=np.int32)
 
 
+def golden_example():
+    """The hand-worked 2x2 root-and-child example stored under tests/golden/."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                           "rule_2x2_worked_example.json")) as f:
+        return json.load(f)
+
+
 def unit(rng, *shape):
     g = rng.standard_normal(shape)
     return g / np.linalg.norm(g, axis=-1, keepdims=True)

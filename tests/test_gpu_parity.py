@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import oracle
+import workloads as W
 from oracle import plan as P
 from gpu_support import TOL, device_case, host_case, require_gpu, run_step, slice_rel_err, to_dev
 
@@ -265,3 +266,60 @@ def test_empty_and_ragged_batch(d_):
         else:
             assert slice_rel_err(cache_after[slots[s]].reshape(hv, -1), st.reshape(hv, -1)) <= TOL
     assert np.array_equal(cache_after[5].view(np.uint32), cache[5].view(np.uint32))
+
+
+@pytest.mark.parametrize("d_,qkv,path", [(16, "f32", "auto"), (64, "bf16", "auto"), (128, "bf16", "auto"),
+                                         (128, "bf16", "recurrent")])
+def test_hand_worked_example_exact(d_, qkv, path, monkeypatch):
+    """The hand-worked 2x2 root-and-child example (tests/golden), embedded in the
+    top-left corner of a d x d head: every number is a dyadic rational with a few
+    significant bits, so the tree kernels, the persist kernels and the chain kernel
+    must all reproduce the hand-derived outputs and states exactly, and leave zeros
+    everywhere else."""
+    from pins import golden_example
+    if path == "recurrent":
+        monkeypatch.setenv("GDN_KERNEL_PATH", "recurrent")
+    G = require_gpu()
+    ex = golden_example()
+    nodes = ex["nodes"]
+    T = len(nodes)
+
+    def pad(rows):
+        x = np.zeros((T, 1, d_), np.float32)
+        for i, r in enumerate(rows):
+            x[i, 0, :2] = r
+        return x
+
+    q, k, v = (pad([nd[key] for nd in nodes]) for key in ("q", "k", "v"))
+    if qkv == "bf16":
+        q, k, v = (W.f32_to_bf16_bits(x) for x in (q, k, v))
+    a = np.array([[nd["a"]] for nd in nodes], np.float32)
+    b = np.array([[nd["b"]] for nd in nodes], np.float32)
+    S0 = np.zeros((1, 1, d_, d_), np.float32)
+    S0[0, 0, :2, :2] = ex["S0"]
+    dims = G.make_dims(1, T, T, 1, 1, d_, 1, G.GDN_BF16 if qkv == "bf16" else G.GDN_F32)
+    ws = G.new_workspace(dims)
+    dq, dk, dv, da, db = (to_dev(x) for x in (q, k, v, a, b))
+    slots = to_dev(np.zeros(1, np.int32))
+    cu = to_dev(np.array([0, T], np.int32))
+    cache = to_dev(S0.copy())
+    out = torch.full((T, 1, d_), float("nan"), device="cuda")
+    G.gdn_tree_plan(dims, to_dev(np.array([nd["parent"] for nd in nodes], np.int32)), cu, slots, ws)
+    G.gdn_tree_verify(dims, dq, dk, dv, da, db, cache, slots, out, ws)
+    G.gdn_tree_persist(dims, dk, dv, da, db, to_dev(np.array([T - 1], np.int32)), cache, slots, ws)
+    assert G.gdn_tree_status(ws)[0] == 0
+    # the two nodes form a chain: the chain kernel from the same committed state
+    cout = torch.full((T, 1, d_), float("nan"), device="cuda")
+    fin = torch.full((1, 1, d_, d_), float("nan"), device="cuda")
+    G.gdn_chain_verify(dims, cu, dq, dk, dv, da, db, to_dev(S0.copy()), slots, cout,
+                       to_dev(np.array([T], np.int32)), fin, ws=G.new_workspace(dims))
+    torch.cuda.synchronize()
+    want_o = np.zeros((T, 1, d_))
+    for i, nd in enumerate(nodes):
+        want_o[i, 0, :2] = nd["o"]
+    want_s = np.zeros((d_, d_))
+    want_s[:2, :2] = nodes[-1]["state"]
+    assert np.array_equal(out.cpu().numpy(), want_o)
+    assert np.array_equal(cout.cpu().numpy(), want_o)
+    assert np.array_equal(cache.cpu().numpy()[0, 0], want_s)
+    assert np.array_equal(fin.cpu().numpy()[0, 0], want_s)

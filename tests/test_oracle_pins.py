@@ -4,6 +4,7 @@ import pytest
 
 import oracle
 import pins
+from pins import golden_example
 
 
 @pytest.mark.parametrize("pin", [
@@ -22,28 +23,19 @@ def test_brute_force_all_small_trees():
 
 
 def test_exact_rational_example():
-    """A 2x2 example whose every number is exact in binary, so fp64 must
-    reproduce the hand-derived result exactly.
-
-    S0 = [[1, 2], [3, 4]], k = (1, 0), v = (2, -2), a = 1/2, b = 1/4, q = (1, 1):
-      S0 (I - b k k^T) = [[3/4, 2], [9/4, 4]]
-      a * that         = [[3/8, 1], [9/8, 2]]
-      + b v k^T        = [[3/8 + 1/2, 1], [9/8 - 1/2, 2]] = [[7/8, 1], [5/8, 2]]
-      o = S' q         = (15/8, 21/8).
-    A child with k = (0, 1), v = (1, 1), a = 1, b = 1/2, q = (0, 1):
-      S' (I - b k k^T) = [[7/8, 1/2], [5/8, 1]];  + b v k^T = [[7/8, 1], [5/8, 3/2]]
-      o = (1, 3/2)."""
-    S0 = np.array([[[1.0, 2.0], [3.0, 4.0]]])
-    k = np.array([[[1.0, 0.0]], [[0.0, 1.0]]])
-    v = np.array([[[2.0, -2.0]], [[1.0, 1.0]]])
-    q = np.array([[[1.0, 1.0]], [[0.0, 1.0]]])
-    a = np.array([[0.5], [1.0]])
-    b = np.array([[0.25], [0.5]])
-    out, st = oracle.tree(np.array([-1, 0], np.int32), q, k, v, a, b, S0, return_states=True)
-    assert np.array_equal(st[0, 0], [[7 / 8, 1.0], [5 / 8, 2.0]])
-    assert np.array_equal(out[0, 0], [15 / 8, 21 / 8])
-    assert np.array_equal(st[1, 0], [[7 / 8, 1.0], [5 / 8, 1.5]])
-    assert np.array_equal(out[1, 0], [1.0, 1.5])
+    """The hand-worked 2x2 example of tests/golden/rule_2x2_worked_example.json: every
+    number is exact in binary, so fp64 must reproduce the hand-derived states and
+    outputs exactly."""
+    ex = golden_example()
+    nodes = ex["nodes"]
+    parent = np.array([nd["parent"] for nd in nodes], np.int32)
+    vec = lambda key: np.array([[nd[key]] for nd in nodes])          # [node][head][dim]
+    gate = lambda key: np.array([[nd[key]] for nd in nodes])         # [node][head]
+    out, st = oracle.tree(parent, vec("q"), vec("k"), vec("v"), gate("a"), gate("b"),
+                          np.array([ex["S0"]]), return_states=True)
+    for i, nd in enumerate(nodes):
+        assert np.array_equal(st[i, 0], nd["state"]), i
+        assert np.array_equal(out[i, 0], nd["o"]), i
 
 
 def test_initial_state_is_prefill_recurrence():
