@@ -188,5 +188,32 @@ def pin_rejected_and_empty(impl):
     assert list(tgt) == [1, 0, 0]
 
 
+def pin_hand_worked(impl):
+    """The hand-worked example under tests/golden/."""
+    ex, logits = golden_accept_example()
+    got = impl.accept(np.array(ex["parent"], np.int32), np.array(ex["cu_nodes"]),
+                      np.array(ex["draft_token"], np.int32), logits, np.zeros(len(ex["cu_nodes"]) - 1, np.int32))
+    for g, key in zip(got, ("accepted_node", "accept_len", "next_token", "target")):
+        assert np.array_equal(g, ex[key]), key
+
+
 ALL_PINS = [pin_autoregressive_equivalence, pin_chain_prefix_length, pin_argmax_special_values,
-            pin_forest_and_duplicates, pin_rejected_and_empty]
+            pin_forest_and_duplicates, pin_rejected_and_empty, pin_hand_worked]
+
+
+def golden_accept_example():
+    """The hand-worked acceptance example under tests/golden/: its inputs (logits
+    rebuilt from the stated background, entries and NaNs) and the hand-derived
+    results."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                           "accept_worked_example.json")) as f:
+        ex = json.load(f)
+    V, T = ex["vocab"], len(ex["parent"])
+    logits = np.tile(-1.0 - np.arange(V) / 16.0, (T, 1)).astype(np.float32)
+    for r, c, v in ex["set"]:
+        logits[r, c] = v
+    for r, c in ex["nan_at"]:
+        logits[r, c] = np.nan
+    return ex, logits

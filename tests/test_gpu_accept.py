@@ -209,3 +209,16 @@ def test_accept_feeds_persist():
     assert len(path) == exp[1][0]
     got = d["cache"].cpu().numpy()[case["slots"][0]]
     assert slice_rel_err(got.reshape(cfg.num_v_heads, -1), state.reshape(cfg.num_v_heads, -1)) <= TOL
+
+
+def test_hand_worked_example():
+    """The acceptance example worked by hand (tests/golden) on the GPU: exactly the
+    hand-derived targets, accepted nodes, lengths and next tokens."""
+    import accept_pins
+    G = require_gpu()
+    ex, logits = accept_pins.golden_accept_example()
+    cu = np.array(ex["cu_nodes"], np.int32)
+    trees = [np.array(ex["parent"][cu[s]:cu[s + 1]], np.int32) for s in range(len(cu) - 1)]
+    got = _run(G, trees, ex["draft_token"], logits)
+    for g, key in zip(got, ("accepted_node", "accept_len", "next_token", "target")):
+        assert np.array_equal(g, ex[key]), (key, g)

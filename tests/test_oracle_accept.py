@@ -88,3 +88,14 @@ def test_logits_recipe_accepts_plausible_lengths():
     assert (alen >= 1).all() and alen.max() > 1
     for s in range(len(trees)):
         assert nxt[s] == tgt[cu[s] + acc[s]]
+
+
+def test_hand_worked_example():
+    """The acceptance example worked by hand (tests/golden): the oracle must give
+    exactly the hand-derived targets, accepted nodes, lengths and next tokens."""
+    import oracle.accept as acc
+    ex, logits = accept_pins.golden_accept_example()
+    got = acc.accept(np.array(ex["parent"], np.int32), np.array(ex["cu_nodes"]),
+                     np.array(ex["draft_token"], np.int32), logits, np.zeros(len(ex["cu_nodes"]) - 1, np.int32))
+    for g, key in zip(got, ("accepted_node", "accept_len", "next_token", "target")):
+        assert np.array_equal(g, ex[key]), key
