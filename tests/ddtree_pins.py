@@ -148,3 +148,23 @@ def pin_topk_special_rows(impl):
 
 ALL_PINS = [pin_builder_is_global_order, pin_builder_limits, pin_topk_is_stable_sort, pin_topk_logp_closed_forms,
             pin_topk_special_rows]
+
+
+def golden_ddtree_example():
+    """The hand-worked builder example under tests/golden/."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                           "ddtree_worked_example.json")) as f:
+        return json.load(f)
+
+
+def pin_hand_worked_builder(impl):
+    """The builder on the hand-worked example: parents and tokens id for id."""
+    ex = golden_ddtree_example()
+    par, tok = impl.build_tree(ex["root_token"], np.array(ex["tokens"], np.int32),
+                               np.array(ex["logp"], np.float32), ex["budget"], ex["max_depth"])[:2]
+    assert list(map(int, par)) == ex["parent"] and list(map(int, tok)) == ex["node_token"]
+
+
+ALL_PINS.append(pin_hand_worked_builder)

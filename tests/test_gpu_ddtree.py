@@ -227,3 +227,18 @@ def test_builder_no_sequences():
                        torch.empty((0, 15, 4), dtype=torch.float32, device="cuda"), 22, e, e, cu)
     torch.cuda.synchronize()
     assert cu.item() == 0
+
+
+def test_builder_hand_worked_example():
+    """The builder on the hand-worked example (tests/golden), twice in one batch:
+    parents, node tokens and cu_nodes exactly as derived by hand."""
+    import ddtree_pins
+    G = require_gpu()
+    ex = ddtree_pins.golden_ddtree_example()
+    tokens = np.array([ex["tokens"]] * 2, np.int32)
+    logp = np.array([ex["logp"]] * 2, np.float32)
+    roots = np.array([ex["root_token"]] * 2, np.int32)
+    par, tok, cu = _build(G, roots, tokens, logp, ex["budget"], ex["max_depth"])
+    n = len(ex["parent"])
+    assert list(cu) == [0, n, 2 * n]
+    assert list(par) == ex["parent"] * 2 and list(tok) == ex["node_token"] * 2
