@@ -323,3 +323,41 @@ def test_hand_worked_example_exact(d_, qkv, path, monkeypatch):
     assert np.array_equal(cout.cpu().numpy(), want_o)
     assert np.array_equal(cache.cpu().numpy()[0, 0], want_s)
     assert np.array_equal(fin.cpu().numpy()[0, 0], want_s)
+
+
+@pytest.mark.parametrize("path", ["auto", "recurrent"])
+def test_plan_hand_worked_example(path, monkeypatch):
+    """The traversal metadata worked by hand (tests/golden/plan_worked_example.json)
+    from the device plan, and the accepted path the persist kernels record, twice
+    in one batch with the second copy's ids shifted by the first's node count."""
+    import json
+    import os
+    if path == "recurrent":
+        monkeypatch.setenv("GDN_KERNEL_PATH", "recurrent")
+    G = require_gpu()
+    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "plan_worked_example.json")) as f:
+        ex = json.load(f)
+    n, d_ = len(ex["parent"]), 128
+    T = 2 * n
+    rng = np.random.default_rng(25)
+    dims = G.make_dims(2, T, n, 1, 1, d_, 2, G.GDN_BF16)
+    ws = G.new_workspace(dims)
+    k = W.f32_to_bf16_bits(rng.standard_normal((T, 1, d_)).astype(np.float32) / np.sqrt(d_))
+    v = W.f32_to_bf16_bits(rng.standard_normal((T, 1, d_)).astype(np.float32))
+    a = np.full((T, 1), 0.9, np.float32)
+    b = np.full((T, 1), 0.1, np.float32)
+    cache = torch.zeros((2, 1, d_, d_), device="cuda")
+    slots = to_dev(np.array([1, 0], np.int32))
+    G.gdn_tree_plan(dims, to_dev(np.array(ex["parent"] * 2, np.int32)), to_dev(np.array([0, n, T], np.int32)),
+                    slots, ws)
+    G.gdn_tree_persist(dims, to_dev(k), to_dev(v), to_dev(a), to_dev(b),
+                       to_dev(np.array([ex["accepted_node"]] * 2, np.int32)), cache, slots, ws)
+    md = {key: val.cpu().numpy() for key, val in G.read_metadata(dims, ws).items()}
+    torch.cuda.synchronize()
+    assert (md["seq_status"] == 0).all()
+    for s in range(2):
+        assert md["depth"][s * n:(s + 1) * n].tolist() == ex["depth"]
+        assert md["order"][s * n:(s + 1) * n].tolist() == ex["order"]
+        assert md["action"][s * n:(s + 1) * n].tolist() == ex["action"]
+        assert md["path_len"][s] == len(ex["path"])
+        assert md["path"][s].tolist() == ex["path"] + [-1] * (16 - len(ex["path"]))

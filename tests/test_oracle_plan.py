@@ -125,3 +125,18 @@ def test_validate_verdicts():
     assert list(V(ok, [0, 4, 4], [0, 99], 2, 8, 16)) == [P.SEQ_OK, P.SEQ_OK]
     assert list(V(ok, [0, 5], [0], 1, 8, 16)) == [P.SEQ_BAD_NODES]
     assert list(V(ok, [2, 1, 4], [0, 1], 2, 8, 16))[0] == P.SEQ_BAD_NODES
+
+
+def test_hand_worked_example():
+    """The traversal metadata worked by hand (tests/golden/plan_worked_example.json)."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "plan_worked_example.json")) as f:
+        ex = json.load(f)
+    r = P.plan_tree(np.array(ex["parent"], np.int32))
+    assert np.asarray(r["depth"]).tolist() == ex["depth"]
+    assert np.asarray(r["size"]).tolist() == ex["subtree_size"]
+    assert np.asarray(r["order"]).tolist() == ex["order"]
+    assert np.asarray(r["action"]).tolist() == ex["action"]
+    m = ex["accepted_node"]
+    assert [x for x in np.asarray(r["nodepath"])[m].tolist() if x >= 0] == ex["path"]
