@@ -89,3 +89,26 @@ def test_state_copy_host_checks(lib):
     assert lib.gdn_state_copy(48, 128, one, 4, one, one, 4, one, -1, None) == -2
     assert lib.gdn_state_copy(48, 128, None, 4, one, one, 4, one, 2, None) == -1
     assert lib.gdn_state_copy(48, 128, ctypes.c_void_p(20), 4, one, one, 4, one, 2, None) == -2
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """With no built library every entry point raises: there is no fallback path."""
+    import gated_deltanet_tree_amd as G
+    saved = G._lib
+    G._lib = None
+    try:
+        with pytest.raises(ImportError, match="missing"):
+            G.load_library(str(tmp_path / "libgdn_tree.so"))
+    finally:
+        G._lib = saved
+
+
+def test_package_never_imports_the_oracle():
+    """The product package holds no reference to the CPU oracle."""
+    pkg = os.path.join(ROOT, "gated_deltanet_tree_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
+                assert "oracle/" not in text, f
