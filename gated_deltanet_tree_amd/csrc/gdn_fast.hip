@@ -16,6 +16,8 @@
 // same recurrence per row and writes G_m S0 + sum_e R(m,e) c_e k_e^T in place
 // as a rank-16 update accumulated onto the scaled state.
 #include <algorithm>
+#include <cstdlib>
+#include <cstring>
 
 #include "gdn_internal.h"
 
@@ -492,8 +494,9 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
 }
 
 // ===========================================================================
-// Verify for trees of at most 32 nodes: one workgroup per (sequence, key head)
-// and its HPW value heads, D/32 waves.  One round trip brings the keys,
+// Verify for trees of at most 32 nodes: one workgroup per (sequence, group of
+// HPW value heads of one key head), D/32 waves; HPW is all of the key head's
+// value heads, or one when a small batch leaves room for a workgroup per head.  One round trip brings the keys,
 // queries, values, gates and paths into LDS; the first two heads' states are
 // issued as soon as those have landed (issued with them they would queue ahead
 // of them).  While the states arrive the workgroup forms the coefficients once
@@ -841,8 +844,9 @@ verify_group_kernel(Params P) {
 
 // ===========================================================================
 // Verify for trees of 33 .. 96 nodes: NB node blocks of 32, one workgroup per
-// (sequence, key head) and its value heads, one workgroup per CU (the keys and
-// queries of all blocks stay in LDS).  The Gram entries k.k and k.q of every
+// (sequence, group of GRP value heads of one key head: all of them, or one for a
+// small batch), one workgroup per CU (the keys and queries of all blocks stay in
+// LDS).  The Gram entries k.k and k.q of every
 // block pair and the per-(head, node) coefficients are formed once; ancestors
 // may sit in any block, so each head first takes X_j = K_j S0^T for all blocks
 // (R_j = diag(b)V_j - diag(alpha)X_j kept in registers), then per block t
@@ -916,8 +920,9 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
     constexpr int grp = GRP;
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, hf = lane / 32, l32 = lane % 32;
     const int row = w * 32 + l32;
-    const int b = blockIdx.x / P.Hk, g = blockIdx.x % P.Hk;
-    const int h0 = g * grp;
+    const int nhg = P.Hv / grp;  // workgroups per sequence
+    const int b = blockIdx.x / nhg, h0 = blockIdx.x % nhg * grp;
+    const int g = h0 / (P.Hv / P.Hk);
     const SeqView sv = seq_view<false>(P, b);
     if (!ws_planned(P)) return;
     const int lo = sv.lo, n = sv.n;
@@ -1540,12 +1545,52 @@ hipError_t launch_with_lds(K kernel, dim3 grid, dim3 block, size_t lds, hipStrea
     return hipGetLastError();
 }
 
-// trees of at most 32 nodes (and chains): one workgroup per key head and all its value
-// heads, which share the coefficients' Gram entries; else coefficients + verify
+// Workgroups of `kernel` (threads, dynamic LDS) resident at once on the current device:
+// compute units x workgroups per unit, queried once per device.  0 when unknown.
+constexpr int kMaxDevices = 64;
+template <typename K>
+int resident_workgroups(K kernel, int threads, size_t lds) {
+    static int cache[kMaxDevices];  // a race here only writes the same value twice
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    if (cache[dev] == 0) {
+        int cus = 0, per_cu = 0;
+        if (lds > 65536 && hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+            return 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kernel), threads,
+                                                         lds) != hipSuccess)
+            return 0;
+        cache[dev] = cus * per_cu;
+    }
+    return cache[dev];
+}
+
+// Value heads per verify workgroup.  A key head's value heads share its Gram entries and
+// coefficient tables, so a workgroup normally takes all of them; when a batch is small
+// enough that one workgroup per value head are all resident at once, the heads run side by
+// side instead of one after another (the shared tables are then formed once per head).
+// GDN_VERIFY_HEADS=shared or =split fixes the choice (read on each call).
+template <typename K>
+int heads_per_workgroup(const Params &p, K one_head_kernel, int threads, size_t lds) {
+    const int grp = p.Hv / p.Hk;
+    if (grp == 1) return 1;
+    const char *env = std::getenv("GDN_VERIFY_HEADS");
+    if (env && std::strcmp(env, "shared") == 0) return grp;
+    if (env && std::strcmp(env, "split") == 0) return 1;
+    const int resident = resident_workgroups(one_head_kernel, threads, lds);
+    return resident > 0 && (long long)p.B * p.Hv <= resident ? 1 : grp;
+}
+
+// trees of at most 32 nodes (and chains): one workgroup per key head and its value
+// heads, which share the coefficients' Gram entries; trees of up to 96 nodes: the same
+// over node blocks; else coefficients + verify
 template <int D>
 hipError_t launch_verify_d(const Params &p, bool chain, hipStream_t s) {
     const int grp = p.Hv / p.Hk;
-    const int hpw = grp;
+    const int hpw = heads_per_workgroup(p, chain ? verify_group_kernel<D, true, 1> : verify_group_kernel<D, false, 1>,
+                                        VG<D>::THREADS, gtab_bytes<D>(1));
     if ((chain || p.max_nodes <= kTile) && hpw <= kGroupMaxHeads) {
         const dim3 grid(p.B * (p.Hv / hpw)), block(VG<D>::THREADS);
         switch (hpw) {
@@ -1560,10 +1605,14 @@ hipError_t launch_verify_d(const Params &p, bool chain, hipStream_t s) {
 #undef GDN_GROUP_CASE
         }
     }
-    if (!chain && p.max_nodes <= 3 * kTile && grp <= kGroupMaxHeads) {
-        const dim3 grid(p.B * p.Hk), block(VG<D>::THREADS);
-        const bool two = p.max_nodes <= 2 * kTile;
-        switch (grp) {
+    const bool two = p.max_nodes <= 2 * kTile;
+    const int gb = !chain && p.max_nodes <= 3 * kTile
+                       ? (two ? heads_per_workgroup(p, verify_blocks_kernel<D, 2, 1>, VG<D>::THREADS, btab_bytes<D, 2>(1))
+                              : heads_per_workgroup(p, verify_blocks_kernel<D, 3, 1>, VG<D>::THREADS, btab_bytes<D, 3>(1)))
+                       : grp;
+    if (!chain && p.max_nodes <= 3 * kTile && gb <= kGroupMaxHeads) {
+        const dim3 grid(p.B * (p.Hv / gb)), block(VG<D>::THREADS);
+        switch (gb) {
 #define GDN_BLOCKS_CASE(G)                                                                                          \
     case G:                                                                                                         \
         return two ? launch_with_lds(verify_blocks_kernel<D, 2, G>, grid, block, btab_bytes<D, 2>(G), s, p) \

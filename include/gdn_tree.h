@@ -27,8 +27,9 @@
  *  - Every pointer except `dims` (and the host outputs of gdn_tree_status) is
  *    a DEVICE pointer to contiguous memory in the layouts below.  The caller
  *    owns all memory, including the workspace; the library allocates nothing
- *    and keeps no mutable global state, so calls with distinct workspaces are
- *    independent.
+ *    and keeps no mutable global state (apart from a per-device count of how
+ *    many verify workgroups fit the device at once, a fixed property of the
+ *    part), so calls with distinct workspaces are independent.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work on it and returns without synchronizing, except
  *    gdn_tree_status, which synchronizes `stream`.
@@ -45,7 +46,12 @@
  *    matrix-core kernels (trees of up to 96 nodes), everything else the
  *    per-node recurrent kernels.  Setting the environment variable
  *    GDN_KERNEL_PATH=recurrent makes every call use the recurrent kernels
- *    (read on each call); both agree to within the stated tolerance.
+ *    (read on each call); both agree to within the stated tolerance.  The
+ *    matrix-core verify gives one workgroup all value heads of a key head,
+ *    or, when a batch is small enough that one workgroup per value head all
+ *    fit the device at once, one value head each; GDN_VERIFY_HEADS=shared or
+ *    =split fixes that choice (read on each call; the results are identical
+ *    bit for bit).
  *
  * Layouts (row-major, T = total nodes, B = sequences):
  *   parent       int32 [T]        local node id of the parent inside its own

@@ -1,10 +1,13 @@
 """Parity across value-heads-per-key-head ratios (1..5) and head sizes 64/128.
 
-Trees of at most 32 nodes run the per-key-head kernel for 1..4 value heads per
-key head and the coefficient + verify pair beyond; 40-node trees always run the
-pair.  Chains of at most 16 nodes run the per-key-head kernel through
-gdn_chain_verify.  Each case is a ragged batch with an empty sequence and a
-forest, checked against the oracle to the per-slice tolerance."""
+Trees of at most 32 nodes run the group kernel and trees of 33-96 nodes the
+node-block kernel; chains of at most 16 nodes run the group kernel through
+gdn_chain_verify.  Under GDN_VERIFY_HEADS=shared a workgroup takes all value
+heads of its key head (1..4; the coefficient + verify pair beyond); these
+batches are small, so the automatic choice gives each value head its own
+workgroup (any ratio).  Both are run.  Each case is a ragged batch with an
+empty sequence and a forest, checked against the oracle to the per-slice
+tolerance."""
 import numpy as np
 import pytest
 import torch
@@ -39,8 +42,13 @@ def _check_out(got, exp, cu, hv):
 @pytest.mark.parametrize("d_", [64, 128])
 @pytest.mark.parametrize("grp", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("big", [False, True])
-def test_tree_head_groups(d_, grp, big):
+@pytest.mark.parametrize("heads", ["auto", "shared"])
+def test_tree_head_groups(d_, grp, big, heads, monkeypatch):
     G = require_gpu()
+    if heads == "auto":  # this batch is small: one value head per verify workgroup
+        monkeypatch.delenv("GDN_VERIFY_HEADS", raising=False)
+    else:
+        monkeypatch.setenv("GDN_VERIFY_HEADS", heads)
     rng = np.random.default_rng(1000 * grp + d_ + (7 if big else 0))
     hk = 2
     hv = hk * grp
@@ -63,7 +71,7 @@ def test_tree_head_groups(d_, grp, big):
     cache_d = to_dev(cache.copy())
     slots_d = to_dev(slots)
     out = torch.full((T, hv, d_), float("nan"), device="cuda")
-    print("tree head groups d=%d grp=%d nmax=%d" % (d_, grp, nmax), flush=True)
+    print("tree head groups d=%d grp=%d nmax=%d heads=%s" % (d_, grp, nmax, heads), flush=True)
     G.gdn_tree_plan(dims, to_dev(np.concatenate(trees).astype(np.int32)), to_dev(cu.astype(np.int32)), slots_d, ws)
     G.gdn_tree_verify(dims, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], cache_d, slots_d, out, ws)
     G.gdn_tree_persist(dims, dev["k"], dev["v"], dev["a"], dev["b"], to_dev(acc), cache_d, slots_d, ws)
@@ -83,8 +91,13 @@ def test_tree_head_groups(d_, grp, big):
 
 @pytest.mark.parametrize("d_", [64, 128])
 @pytest.mark.parametrize("grp", [1, 2, 3, 4, 5])
-def test_chain_head_groups(d_, grp):
+@pytest.mark.parametrize("heads", ["auto", "shared"])
+def test_chain_head_groups(d_, grp, heads, monkeypatch):
     G = require_gpu()
+    if heads == "auto":
+        monkeypatch.delenv("GDN_VERIFY_HEADS", raising=False)
+    else:
+        monkeypatch.setenv("GDN_VERIFY_HEADS", heads)
     rng = np.random.default_rng(2000 * grp + d_)
     hk = 2
     hv = hk * grp
@@ -104,7 +117,7 @@ def test_chain_head_groups(d_, grp):
     dev = {k_: to_dev(v_) for k_, v_ in inp.items()}
     out = torch.full((T, hv, d_), float("nan"), device="cuda")
     fin = torch.full((B, hv, d_, d_), float("nan"), device="cuda")
-    print("chain head groups d=%d grp=%d" % (d_, grp), flush=True)
+    print("chain head groups d=%d grp=%d heads=%s" % (d_, grp, heads), flush=True)
     G.gdn_chain_verify(dims, to_dev(cu.astype(np.int32)), dev["q"], dev["k"], dev["v"], dev["a"], dev["b"],
                        to_dev(cache), to_dev(slots), out, to_dev(final_len), fin, ws)
     rc, bad, code = G.gdn_tree_status(ws)

@@ -63,11 +63,18 @@ def _case(seed):
 
 
 @pytest.mark.parametrize("seed", range(CASES))
-def test_sweep(seed):
+def test_sweep(seed, monkeypatch):
     G = require_gpu()
     c = _case(seed)
+    # odd cases fix the verify's head grouping to shared workgroups (the automatic
+    # choice at these batch sizes is one value head per workgroup)
+    heads = "shared" if seed % 2 else "auto"
+    if heads == "auto":
+        monkeypatch.delenv("GDN_VERIFY_HEADS", raising=False)
+    else:
+        monkeypatch.setenv("GDN_VERIFY_HEADS", heads)
     print("sweep case", seed, "d", c["d"], c["qkv"], "heads", c["hk"], c["hv"], "B", c["B"],
-          "nodes", [len(t) for t in c["trees"]], flush=True)
+          "nodes", [len(t) for t in c["trees"]], "grouping", heads, flush=True)
     T, hv, d_ = c["T"], c["hv"], c["d"]
     dims = G.make_dims(c["B"], T, c["max_nodes"], c["hk"], hv, d_, len(c["cache"]),
                        G.GDN_BF16 if c["qkv"] == "bf16" else G.GDN_F32)
