@@ -1545,12 +1545,13 @@ hipError_t launch_with_lds(K kernel, dim3 grid, dim3 block, size_t lds, hipStrea
     return hipGetLastError();
 }
 
-// Workgroups of `kernel` (threads, dynamic LDS) resident at once on the current device:
-// compute units x workgroups per unit, queried once per device.  0 when unknown.
+// Workgroups of Kernel (threads, dynamic LDS) resident at once on the current device:
+// compute units x workgroups per unit, queried once per (kernel, device).  0 when unknown.
 constexpr int kMaxDevices = 64;
-template <typename K>
-int resident_workgroups(K kernel, int threads, size_t lds) {
-    static int cache[kMaxDevices];  // a race here only writes the same value twice
+template <void (*Kernel)(Params)>
+int resident_workgroups(int threads, size_t lds) {
+    const auto kernel = Kernel;
+    static int cache[kMaxDevices];  // one per kernel; a race only writes the same value twice
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
     if (cache[dev] == 0) {
@@ -1572,14 +1573,14 @@ int resident_workgroups(K kernel, int threads, size_t lds) {
 // enough that one workgroup per value head are all resident at once, the heads run side by
 // side instead of one after another (the shared tables are then formed once per head).
 // GDN_VERIFY_HEADS=shared or =split fixes the choice (read on each call).
-template <typename K>
-int heads_per_workgroup(const Params &p, K one_head_kernel, int threads, size_t lds) {
+template <void (*OneHeadKernel)(Params)>
+int heads_per_workgroup(const Params &p, int threads, size_t lds) {
     const int grp = p.Hv / p.Hk;
     if (grp == 1) return 1;
     const char *env = std::getenv("GDN_VERIFY_HEADS");
     if (env && std::strcmp(env, "shared") == 0) return grp;
     if (env && std::strcmp(env, "split") == 0) return 1;
-    const int resident = resident_workgroups(one_head_kernel, threads, lds);
+    const int resident = resident_workgroups<OneHeadKernel>(threads, lds);
     return resident > 0 && (long long)p.B * p.Hv <= resident ? 1 : grp;
 }
 
@@ -1589,8 +1590,8 @@ int heads_per_workgroup(const Params &p, K one_head_kernel, int threads, size_t 
 template <int D>
 hipError_t launch_verify_d(const Params &p, bool chain, hipStream_t s) {
     const int grp = p.Hv / p.Hk;
-    const int hpw = heads_per_workgroup(p, chain ? verify_group_kernel<D, true, 1> : verify_group_kernel<D, false, 1>,
-                                        VG<D>::THREADS, gtab_bytes<D>(1));
+    const int hpw = chain ? heads_per_workgroup<verify_group_kernel<D, true, 1>>(p, VG<D>::THREADS, gtab_bytes<D>(1))
+                          : heads_per_workgroup<verify_group_kernel<D, false, 1>>(p, VG<D>::THREADS, gtab_bytes<D>(1));
     if ((chain || p.max_nodes <= kTile) && hpw <= kGroupMaxHeads) {
         const dim3 grid(p.B * (p.Hv / hpw)), block(VG<D>::THREADS);
         switch (hpw) {
@@ -1607,8 +1608,8 @@ hipError_t launch_verify_d(const Params &p, bool chain, hipStream_t s) {
     }
     const bool two = p.max_nodes <= 2 * kTile;
     const int gb = !chain && p.max_nodes <= 3 * kTile
-                       ? (two ? heads_per_workgroup(p, verify_blocks_kernel<D, 2, 1>, VG<D>::THREADS, btab_bytes<D, 2>(1))
-                              : heads_per_workgroup(p, verify_blocks_kernel<D, 3, 1>, VG<D>::THREADS, btab_bytes<D, 3>(1)))
+                       ? (two ? heads_per_workgroup<verify_blocks_kernel<D, 2, 1>>(p, VG<D>::THREADS, btab_bytes<D, 2>(1))
+                              : heads_per_workgroup<verify_blocks_kernel<D, 3, 1>>(p, VG<D>::THREADS, btab_bytes<D, 3>(1)))
                        : grp;
     if (!chain && p.max_nodes <= 3 * kTile && gb <= kGroupMaxHeads) {
         const dim3 grid(p.B * (p.Hv / gb)), block(VG<D>::THREADS);
