@@ -16,6 +16,7 @@
 // same recurrence per row and writes G_m S0 + sum_e R(m,e) c_e k_e^T in place
 // as a rank-16 update accumulated onto the scaled state.
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 
@@ -1551,10 +1552,11 @@ constexpr int kMaxDevices = 64;
 template <void (*Kernel)(Params)>
 int resident_workgroups(int threads, size_t lds) {
     const auto kernel = Kernel;
-    static int cache[kMaxDevices];  // one per kernel; a race only writes the same value twice
+    static std::atomic<int> cache[kMaxDevices];  // one per kernel; threads that race store the same value
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-    if (cache[dev] == 0) {
+    int known = cache[dev].load(std::memory_order_relaxed);
+    if (known == 0) {
         int cus = 0, per_cu = 0;
         if (lds > 65536 && hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
@@ -1563,9 +1565,10 @@ int resident_workgroups(int threads, size_t lds) {
             hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kernel), threads,
                                                          lds) != hipSuccess)
             return 0;
-        cache[dev] = cus * per_cu;
+        known = cus * per_cu;
+        cache[dev].store(known, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return known;
 }
 
 // Value heads per verify workgroup.  A key head's value heads share its Gram entries and
