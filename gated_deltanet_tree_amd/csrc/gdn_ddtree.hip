@@ -38,7 +38,10 @@ __device__ __forceinline__ bool before(float v1, int i1, float v2, int i2) {
 // W = 8 on, where the lists' own work grows with the wave count
 template <int WT>
 constexpr int topk_threads() { return WT <= 4 ? 1024 : 512; }
-constexpr int kTopkUnroll = 4;
+// 16-byte loads in flight per thread: 4 for the short lists (1024 threads), 8 at W = 8,
+// 6 at W = 16 (8 there spills the larger lists)
+template <int WT>
+constexpr int topk_unroll() { return WT <= 4 ? 4 : WT <= 8 ? 8 : 6; }
 
 template <int WT>
 struct TopList {
@@ -121,6 +124,7 @@ template <int WT, bool VEC, int kTopkThreads = topk_threads<WT>()>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(int vocab, int width, const float *logits,
                                                              int32_t *tokens, float *logp) {
     constexpr int NW = kTopkThreads / 64;
+    constexpr int kTopkUnroll = topk_unroll<WT>();
     __shared__ float s_v[NW][WT];
     __shared__ int s_i[NW][WT];
     __shared__ float s_m[NW], s_s[NW];
