@@ -41,7 +41,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published (256 CUs, 2.4 GHz, packed FMA)
 
 
 def parse():
@@ -62,6 +61,13 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of HIP graph replays")
     ap.add_argument("--path", choices=["auto", "recurrent"], default="auto",
                     help="recurrent: run the per-node recurrent kernels on every call (GDN_KERNEL_PATH)")
+    ap.add_argument("--distinct", type=int, default=0,
+                    help="generate this many layers' inputs and place each in several copies (0: every copy)")
+    ap.add_argument("--no-stress", action="store_true", help="skip the stress-workload sub-object")
+    ap.add_argument("--stress-steps", type=int, default=10)
+    ap.add_argument("--stress-warmup", type=int, default=3)
+    ap.add_argument("--stress-distinct", type=int, default=4,
+                    help="independently generated layers of the stress sub-object (the rest are copies)")
     return ap.parse_args()
 
 
@@ -87,41 +93,57 @@ def rotation(per_copy, layers):
     return min(128, max(4 if layers == 1 else 1, int(np.ceil(512e6 / (per_copy * layers)))))
 
 
-def verify_flops(cfg, trees):
-    """Arithmetic of the rule itself per layer call, as a node-by-node walk would do it
-    in fp32: per (node, value head) S k and S q (2 D^2 each) and the rank-1 update
-    (3 D^2) where the node has children, or just S k, S q and o = a (S q) + c (k . q)
-    (4 D^2) at a leaf, whose updated state is never needed."""
-    D2, Hv = cfg.head_dim * cfg.head_dim, cfg.num_v_heads
-    total = 0
-    for par in trees:
-        n = len(par)
-        has_child = np.zeros(n, dtype=bool)
-        for p in par:
-            if p >= 0:
-                has_child[int(p)] = True
-        total += (7 * int(has_child.sum()) + 4 * int(n - has_child.sum())) * D2 * Hv
-    return total
+def pct(xs):
+    """median, p10 and p90 of a list of timings"""
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)), "p90": float(np.percentile(a, 90)),
+            "mean": float(a.mean()), "samples": int(a.size)}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark measures one GPU; --gpus %d is not supported "
-                                   "(sequences shard across GPUs with no exchange, so one GPU's "
-                                   "share at its real shape is the measured unit)" % args.gpus}))
-        sys.exit(2)
-    if args.path == "recurrent":
-        os.environ["GDN_KERNEL_PATH"] = "recurrent"
+def cpu_model_name():
+    """The host CPU's model name (the `lscpu` "Model name" line, read from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def memory_ceilings(dev):
+    """Plain streaming rates on this part for scale, measured with torch's own
+    kernels (not this library): a sum over 1 GiB of fp32 (read) and a 1 GiB
+    device copy (read + write), median of 10 launches timed with events."""
     import torch
-    import gated_deltanet_tree_amd as G
-    import workloads as W
+    x = torch.empty(256 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, fn, nbytes in (("read", lambda: x.sum(), x.numel() * 4),
+                             ("copy", lambda: y.copy_(x), 2 * x.numel() * 4)):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        res[name + "_gbs"] = nbytes / float(np.median(ts)) / 1e9
+    del x, y
+    torch.cuda.synchronize()
+    res["how"] = "torch sum over 1 GiB fp32 (read) and torch copy of 1 GiB (read + write), median of 10"
+    return res
 
-    if not torch.cuda.is_available():
-        print(json.dumps({"error": "no GPU"}))
-        sys.exit(1)
-    G.load_library()
-    cfg = W.get_config(args.config)
+
+def measure(G, W, cfg, args, steps, warmup, distinct=0, path_label="auto"):
+    """Times one workload: a step = plan + verify and persist for each layer.
+    Returns the workload's result fields and the state the extra measurements use."""
+    import torch
     dev = torch.device("cuda:0")
     trees = W.make_trees(cfg)
     cu = W.cu_from_trees(trees)
@@ -134,7 +156,6 @@ def main():
                        cfg.num_slots, qkv_dtype, max_depth=cfg.max_depth)
     path_lens = [int(W.tree_depths(t)[m]) for t, m in zip(trees, acc)]
     vbytes, pbytes = algorithmic_bytes(cfg, T, path_lens, s_in)
-    vflops = verify_flops(cfg, trees)
 
     def to_dev(x):
         if x.dtype == np.uint16:
@@ -145,17 +166,20 @@ def main():
     per_copy = vbytes + T * cfg.num_v_heads * cfg.head_dim * 4
     rotate = args.rotate or rotation(per_copy, layers)
     copies = layers * rotate
-    print("# config %s: B=%d T=%d layers=%d copies=%d (%.0f MB per layer copy)"
-          % (cfg.name, cfg.num_seqs, T, layers, copies, per_copy / 1e6), file=sys.stderr, flush=True)
+    # distinct > 0: that many independently generated layers' inputs and prefills,
+    # each placed in several copies (every copy is its own HBM buffer; only the
+    # values repeat, which the kernels' timing does not depend on)
+    n_gen = copies if distinct <= 0 else min(distinct, copies)
+    print("# config %s: B=%d T=%d layers=%d copies=%d (%d generated, %.0f MB per layer copy)"
+          % (cfg.name, cfg.num_seqs, T, layers, copies, n_gen, per_copy / 1e6), file=sys.stderr, flush=True)
 
     slot_d = to_dev(slots)
     acc_d = to_dev(acc)
     parent_d = to_dev(np.concatenate(trees).astype(np.int32))
     cu_d = to_dev(cu.astype(np.int32))
     ws = G.new_workspace(dims)
-    # committed states: each copy's cache is filled by the library's own chain
-    # kernel running that copy's prefill tokens from a zero state
-    sets = []
+    # committed states: each generated copy's cache is filled by the library's own
+    # chain kernel running that copy's prefill tokens from a zero state
     pre_cu = torch.arange(0, (cfg.num_seqs + 1) * cfg.prefill_steps, cfg.prefill_steps, dtype=torch.int32,
                           device=dev)
     pre_dims = G.make_dims(cfg.num_seqs, cfg.num_seqs * cfg.prefill_steps, cfg.prefill_steps, cfg.num_k_heads,
@@ -163,26 +187,30 @@ def main():
     zero_cache = torch.zeros((cfg.num_slots, cfg.num_v_heads, cfg.head_dim, cfg.head_dim), device=dev)
     flen = torch.full((cfg.num_seqs,), cfg.prefill_steps, dtype=torch.int32, device=dev)
     ident = torch.arange(cfg.num_seqs, dtype=torch.int32, device=dev)
+    sets = []
     for c in range(copies):
-        inp = W.make_layer_inputs(cfg, c, trees)
-        pre = W.make_prefill(cfg, c)
-        d = {k: to_dev(v) for k, v in inp.items()}
-        pk = to_dev(pre["k"].reshape(-1, cfg.num_k_heads, cfg.head_dim))
-        pv = to_dev(pre["v"].reshape(-1, cfg.num_v_heads, cfg.head_dim))
-        pa = to_dev(pre["a"].reshape(-1, cfg.num_v_heads))
-        pb = to_dev(pre["b"].reshape(-1, cfg.num_v_heads))
-        fin = torch.empty((cfg.num_seqs, cfg.num_v_heads, cfg.head_dim, cfg.head_dim), device=dev)
-        G.gdn_chain_verify(pre_dims, pre_cu, None, pk, pv, pa, pb, zero_cache, ident, None, flen, fin)
-        cache = torch.zeros((cfg.num_slots, cfg.num_v_heads, cfg.head_dim, cfg.head_dim), device=dev)
-        cache[slot_d.long()] = fin
-        d["cache"] = cache
+        if c < n_gen:
+            inp = W.make_layer_inputs(cfg, c, trees)
+            pre = W.make_prefill(cfg, c)
+            d = {k: to_dev(v) for k, v in inp.items()}
+            pk = to_dev(pre["k"].reshape(-1, cfg.num_k_heads, cfg.head_dim))
+            pv = to_dev(pre["v"].reshape(-1, cfg.num_v_heads, cfg.head_dim))
+            pa = to_dev(pre["a"].reshape(-1, cfg.num_v_heads))
+            pb = to_dev(pre["b"].reshape(-1, cfg.num_v_heads))
+            fin = torch.empty((cfg.num_seqs, cfg.num_v_heads, cfg.head_dim, cfg.head_dim), device=dev)
+            G.gdn_chain_verify(pre_dims, pre_cu, None, pk, pv, pa, pb, zero_cache, ident, None, flen, fin)
+            cache = torch.zeros((cfg.num_slots, cfg.num_v_heads, cfg.head_dim, cfg.head_dim), device=dev)
+            cache[slot_d.long()] = fin
+            d["cache"] = cache
+            del pk, pv, pa, pb, fin
+        else:
+            d = {k: v.clone() for k, v in sets[c % n_gen].items() if k != "out"}
         d["out"] = torch.empty((T, cfg.num_v_heads, cfg.head_dim), device=dev)
         sets.append(d)
-        del pk, pv, pa, pb, fin
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * layers + 2)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * layers + 2)] for _ in range(steps)]
 
     def step(i, events=None):
         r = i % rotate
@@ -206,32 +234,27 @@ def main():
             if events:
                 events[2 + layers + l].record(stream)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
-    # calibration for memory-traffic counters: one plain device copy of a known
-    # size (256 MiB read + 256 MiB written), outside the timed region
-    cal_src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
-    cal_dst = torch.empty_like(cal_src)
-    cal_dst.copy_(cal_src)
-    del cal_src, cal_dst
     torch.cuda.synchronize()
     rc, bad, code = G.gdn_tree_status(ws)
     if rc != 0:
-        print(json.dumps({"error": "library rejected the workload: %d %d %d" % (rc, bad, code)}))
+        print(json.dumps({"error": "library rejected the %s workload: %d %d %d" % (cfg.name, rc, bad, code)}))
         sys.exit(1)
 
     # per-call breakdown: K eager steps with an event pair around every call
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, ev[i])
+    for i in range(steps):
+        step(warmup + i, ev[i])
     torch.cuda.synchronize()
-    eager_ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    eager_ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
 
-    # main timed loop: exactly K steps as HIP graph replays (the same calls, without
-    # the host's launch gaps).  One graph holds one rotation cycle of consecutive
-    # steps (copies 0 .. R-1): each graph launch costs the GPU several microseconds,
-    # which a decode loop pays per launch, not per step.
+    # main timed loop: exactly K steps as HIP graph replays (the same calls, without the
+    # host's launch gaps).  One graph holds one rotation cycle of consecutive steps
+    # (copies 0 .. R-1): each graph launch costs the GPU several microseconds, which a
+    # decode loop pays per launch, not per step.  Each cycle's replay sits between two
+    # events, which give the per-step spread.
     cycle = None
     if not args.eager:
         side = torch.cuda.Stream()
@@ -247,24 +270,29 @@ def main():
                 step(r)
         cycle.replay()
     torch.cuda.synchronize()
+    full, rest = divmod(steps, rotate) if cycle is not None else (0, steps)
+    cyc_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(full)]
     t0 = time.perf_counter()
-    if cycle is not None:
-        full, rest = divmod(args.steps, rotate)
-        for _ in range(full):
-            cycle.replay()
-        for i in range(rest):  # a partial cycle runs eagerly
-            step(i)
-    else:
-        for i in range(args.steps):
-            step(args.warmup + i)
+    for e0, e1 in cyc_ev:
+        e0.record(stream)
+        cycle.replay()
+        e1.record(stream)
+    for i in range(rest):  # a partial cycle (or every step with --eager) runs eagerly
+        step(warmup + i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
+    ms_per_step = elapsed * 1e3 / steps
+    if cyc_ev:
+        step_samples = [a.elapsed_time(b) / rotate for a, b in cyc_ev]
+        step_how = "one sample per graph replay of %d consecutive steps (events on the kernels' stream)" % rotate
+    else:
+        step_samples = [e[0].elapsed_time(e[-1]) for e in ev]
+        step_how = "eager steps, first to last event"
 
     # per-kernel launch durations under graph replay, the launch mode of the timed loop:
-    # one graph per call kind holding that call alone over the rotation, replayed with an
-    # event pair around the replays on the stream the kernels run on (events cannot sit
-    # inside a graph here).  Each graph holds enough launches that the graph launch's own
+    # one graph per call kind holding that call alone over the rotation, each replay
+    # between two events on the stream the kernels run on (events cannot sit inside a
+    # graph here).  Each graph holds enough launches that the graph launch's own
     # start-up (several microseconds) adds little per launch.
     def graph_us(call, per_cycle):
         cycles = max(1, 32 // per_cycle)
@@ -282,16 +310,16 @@ def main():
                     call(r)
         g.replay()
         torch.cuda.synchronize()
-        reps = max(2, 200 // (cycles * per_cycle))
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
+        reps = max(5, 400 // (cycles * per_cycle))
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in evs:
+            e0.record(stream)
             g.replay()
-        e1.record(stream)
+            e1.record(stream)
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (reps * cycles * per_cycle)
+        per_launch = [a.elapsed_time(b) * 1e3 / (cycles * per_cycle) for a, b in evs]
         del g
-        return us
+        return pct(per_launch)
 
     def plan_call(r):
         G.gdn_tree_plan(dims, parent_d, cu_d, slot_d, ws)
@@ -306,9 +334,10 @@ def main():
             d = sets[r * layers + l]
             G.gdn_tree_persist(dims, d["k"], d["v"], d["a"], d["b"], acc_d, d["cache"], slot_d, ws)
 
-    g_plan = graph_us(plan_call, rotate) * 1e-6
-    g_ver = graph_us(verify_call, rotate * layers) * 1e-6
-    g_per = graph_us(persist_call, rotate * layers) * 1e-6
+    gp = graph_us(plan_call, rotate)
+    gv = graph_us(verify_call, rotate * layers)
+    gs = graph_us(persist_call, rotate * layers)
+    g_plan, g_ver, g_per = gp["mean"] * 1e-6, gv["mean"] * 1e-6, gs["mean"] * 1e-6
     G.gdn_tree_plan(dims, parent_d, cu_d, slot_d, ws)
     torch.cuda.synchronize()
 
@@ -330,44 +359,33 @@ def main():
 
     # dominant kernel of the layer call: both stream the state cache and run far below the
     # ridge point of the matrix cores, so the bound is HBM bandwidth.  Its launch duration
-    # is the graph-replay one (the timed loop's launch mode); the eager figure, which adds
+    # is the graph-replay mean (the timed loop's launch mode); the eager figure, which adds
     # the host launch gap, is reported beside it.
     if g_ver >= g_per:
-        dom, t_dom, t_dom_eager, dom_bytes = "tree_verify", g_ver, t_ver, vbytes
+        dom, t_dom, t_dom_eager, dom_bytes, dom_pct = "tree_verify", g_ver, t_ver, vbytes, gv
     else:
-        dom, t_dom, t_dom_eager, dom_bytes = "persist", g_per, t_per, pbytes
+        dom, t_dom, t_dom_eager, dom_bytes, dom_pct = "persist", g_per, t_per, pbytes, gs
     roof = {"bound": "hbm", "achieved": dom_bytes / t_dom / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(dom, cfg.name)
     roof["kernel"] = dom
     roof["bytes_per_launch"] = dom_bytes
     roof["launch_us"] = t_dom * 1e6
-    # the rule's own arithmetic in verify against the fp32 vector peak: what a node-by-node
-    # fp32 walk of the same trees would need at least this long for
-    roof_alu = {"kernel": "tree_verify", "bound": "alu", "achieved": vflops / g_ver / 1e12,
-                "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s", "flops_per_launch": vflops}
-    roof_alu["frac"] = roof_alu["achieved"] / roof_alu["peak"]
+    roof["launch_us_pct"] = dom_pct
     roof["launch_us_eager"] = t_dom_eager * 1e6
 
-    result = {
-        "metric": "GDN tree-verify nodes/sec per layer call + achieved HBM GB/s (% of peak)",
+    res = {
         "value": nodes_per_s,
-        "unit": "nodes/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
+        "step_ms": dict(pct(step_samples), how=step_how),
+        "eager_ms_per_step": eager_ms_per_step,
         "config": {"workload": cfg.name, "sequences": cfg.num_seqs, "layers": layers, "nodes": T,
                    "v_heads": cfg.num_v_heads, "k_heads": cfg.num_k_heads, "head_dim": cfg.head_dim,
-                   "qkv": cfg.dtype, "rotated_copies": rotate, "seed": cfg.seed, "kernels": args.path,
+                   "qkv": cfg.dtype, "rotated_copies": rotate, "generated_copies": n_gen, "seed": cfg.seed,
+                   "kernels": path_label,
                    "launch": "eager" if args.eager else "hip_graph_per_%d_steps" % rotate},
-        "eager_ms_per_step": eager_ms_per_step,
         "layer_call": {"verify_us": g_ver * 1e6, "persist_us": g_per * 1e6, "plan_us": g_plan * 1e6,
+                       "verify_us_pct": gv, "persist_us_pct": gs, "plan_us_pct": gp,
                        # one plan per decode step serves every GDN layer; 48 layers as in the
                        # 64-sequence stress workload
                        "plan_amortized_us": g_plan * 1e6 / 48, "plan_amortized_over_layers": 48,
@@ -375,21 +393,98 @@ def main():
                        "hbm_frac": hbm_gbs / HBM_PEAK_GBS,
                        "verify_gbs": vbytes / g_ver / 1e9, "persist_gbs": pbytes / g_per / 1e9,
                        "nodes_per_s": T / (g_ver + g_per),
-                       "timing": "graph replay of each call alone over the rotation",
+                       "timing": "graph replay of each call alone over the rotation (mean; spread in *_pct)",
                        "eager": {"verify_us": t_ver * 1e6, "persist_us": t_per * 1e6, "plan_us": t_plan * 1e6}},
         "roofline": roof,
-        "roofline_verify_alu": roof_alu,
     }
+    ctx = dict(trees=trees, cu=cu, acc=acc, dims=dims, parent_d=parent_d, cu_d=cu_d, slot_d=slot_d, acc_d=acc_d,
+               ws=ws, sets=sets, rotate=rotate, layers=layers, vbytes=vbytes, pbytes=pbytes, t_ver=t_ver,
+               t_per=t_per)
+    return res, ctx
+
+
+PRECISION = ("bf16 q/k/v; fp32 gates, state and outputs.  The dense products (S0 K^T, S0 Q^T, the output "
+             "operator and the persist update) run on bf16 MFMA with each fp32 operand split into bf16 hi + lo "
+             "(about 16 significant bits per product) and fp32 accumulation; the per-path recurrences run in "
+             "fp32 on the vector ALU")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU; --gpus %d is not supported "
+                                   "(sequences shard across GPUs with no exchange, so one GPU's "
+                                   "share at its real shape is the measured unit)" % args.gpus}))
+        sys.exit(2)
+    if args.path == "recurrent":
+        os.environ["GDN_KERNEL_PATH"] = "recurrent"
+    import torch
+    import gated_deltanet_tree_amd as G
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU"}))
+        sys.exit(1)
+    G.load_library()
+    cfg = W.get_config(args.config)
+    res, ctx = measure(G, W, cfg, args, args.steps, args.warmup, distinct=args.distinct, path_label=args.path)
+    # calibration for memory-traffic counters: one plain device copy of a known size
+    # (256 MiB read + 256 MiB written), outside the timed region
+    cal_src = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    del cal_src, cal_dst
+    torch.cuda.synchronize()
+
+    result = {
+        "metric": "GDN tree-verify nodes/sec per layer call + achieved HBM GB/s (% of peak)",
+        "value": res["value"],
+        "unit": "nodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "split-bf16 MFMA (fp32 state as bf16 hi + lo), fp32 accumulate" if cfg.dtype == "bf16"
+                 and args.path == "auto" else "f32",
+        "precision": PRECISION,
+        "data": "synthetic",
+    }
+    result.update({k: v for k, v in res.items() if k not in ("value", "ms_per_step")})
+    result["memory_ceilings"] = memory_ceilings("cuda")
     if not args.no_accept:
-        result["accept"] = bench_accept(G, W, cfg, trees, dims, parent_d, cu_d, slot_d, args.accept_steps)
+        result["accept"] = bench_accept(G, W, cfg, ctx["trees"], ctx["dims"], ctx["parent_d"], ctx["cu_d"],
+                                        ctx["slot_d"], args.accept_steps)
     if not args.no_draft and cfg.tree[0] == "ddtree":
         result["draft"] = bench_draft(G, W, cfg, args.accept_steps)
-    if not args.no_store_path and layers == 1:
-        result["store_path"] = bench_store_path(G, cfg, dims, sets, slot_d, acc_d, ws, rotate, args.accept_steps,
-                                                vbytes, pbytes, t_ver, t_per)
+    if not args.no_store_path and ctx["layers"] == 1:
+        result["store_path"] = bench_store_path(G, cfg, ctx["dims"], ctx["sets"], ctx["slot_d"], ctx["acc_d"],
+                                                ctx["ws"], ctx["rotate"], args.accept_steps, ctx["vbytes"],
+                                                ctx["pbytes"], ctx["t_ver"], ctx["t_per"])
     if not args.no_snapshot:
-        result["snapshot"] = bench_snapshot(G, cfg, sets, slot_d, rotate, layers, args.accept_steps)
+        result["snapshot"] = bench_snapshot(G, cfg, ctx["sets"], ctx["slot_d"], ctx["rotate"], ctx["layers"],
+                                            args.accept_steps)
+    del ctx
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    # the largest single-GPU workload, as its own sub-object: 64 sequences x 65-node
+    # trees x 48 layer calls per step, a few steps
+    if not args.no_stress and cfg.name != "stress":
+        scfg = W.get_config("stress")
+        sres, sctx = measure(G, W, scfg, args, args.stress_steps, args.stress_warmup, distinct=args.stress_distinct,
+                             path_label=args.path)
+        sres["nodes_per_s"] = sres.pop("value")
+        if not args.no_cpu_baseline:
+            sres["cpu_baseline"] = cpu_baseline(scfg, sctx["trees"], sctx["cu"], sctx["acc"], args.cpu_seconds / 2,
+                                                layer_calls=1, single_thread=False)
+        del sctx
+        result["stress"] = sres
     if not args.no_cpu_baseline:
+        trees, cu, acc = W.make_trees(cfg), None, None
+        cu = W.cu_from_trees(trees)
+        acc = W.make_accepts(cfg, trees)
         result["cpu_baseline"] = cpu_baseline(cfg, trees, cu, acc, args.cpu_seconds)
     print(json.dumps(result))
 
@@ -583,35 +678,67 @@ def measured_traffic(kernel: str, workload: str):
     return ent["bytes_per_launch"]
 
 
-def cpu_baseline(cfg, trees, cu, acc, seconds):
-    """The fp64 oracle (verify + persist) on the host cores, on whole sequences
-    of the workload (cycling over the inputs of four layers, with
-    one committed state per sequence), until about `seconds` of oracle work has run."""
+def cpu_baseline(cfg, trees, cu, acc, seconds, layer_calls=None, single_thread=True):
+    """The fp64 oracle (verify + persist) on the host cores.  One layer call is
+    every sequence of the workload on one layer's inputs, each sequence from its
+    own committed state.  After one warm-up sequence, whole layer calls run while
+    about `seconds` of oracle work lasts (at most `layer_calls` of them); `value`
+    is the median rate over the calls, a call cut short by the budget counting
+    the sequences it finished.  With `single_thread` the same is done again on
+    one thread, the budget split between the two runs."""
     import oracle
     import workloads as W
     rng = np.random.default_rng(0)
-    inputs = [W.make_layer_inputs(cfg, layer, trees) for layer in range(4)]
+    inputs = [W.make_layer_inputs(cfg, layer, trees) for layer in range(2)]
     states = [(0.1 * rng.standard_normal((cfg.num_v_heads, cfg.head_dim, cfg.head_dim))).astype(np.float32)
               for _ in range(cfg.num_seqs)]
-    done_nodes, t_total, seqs, layer = 0, 0.0, 0, 0
-    while t_total < seconds:
-        inp = inputs[layer % len(inputs)]
-        for s in range(cfg.num_seqs):
-            lo, hi = int(cu[s]), int(cu[s + 1])
-            S0 = states[s]
-            sl = {k: v[lo:hi] for k, v in inp.items()}
-            t0 = time.perf_counter()
-            oracle.tree(trees[s], sl["q"], sl["k"], sl["v"], sl["a"], sl["b"], S0)
-            oracle.accept_state(trees[s], int(acc[s]), sl["k"], sl["v"], sl["a"], sl["b"], S0)
-            t_total += time.perf_counter() - t0
-            done_nodes += hi - lo
-            seqs += 1
-            if t_total >= seconds:
-                break
-        layer += 1
-    return {"value": done_nodes / t_total, "unit": "nodes/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "%d sequence trees of the %s workload in %d passes over 4 layers' inputs (%d nodes, "
-                      "verify + persist, fp64), %.1f s" % (seqs, cfg.name, layer, done_nodes, t_total)}
+    T = int(cu[-1])
+
+    def one_seq(inp, s):
+        lo, hi = int(cu[s]), int(cu[s + 1])
+        sl = {k: v[lo:hi] for k, v in inp.items()}
+        t0 = time.perf_counter()
+        oracle.tree(trees[s], sl["q"], sl["k"], sl["v"], sl["a"], sl["b"], states[s])
+        oracle.accept_state(trees[s], int(acc[s]), sl["k"], sl["v"], sl["a"], sl["b"], states[s])
+        return time.perf_counter() - t0, hi - lo
+
+    def run(budget):
+        one_seq(inputs[0], 0)
+        rates, nodes, t_total, calls, whole = [], 0, 0.0, 0, 0
+        while t_total < budget and (layer_calls is None or calls < layer_calls):
+            inp = inputs[calls % len(inputs)]
+            t_call, n_call = 0.0, 0
+            for s in range(cfg.num_seqs):
+                dt, n = one_seq(inp, s)
+                t_call, n_call = t_call + dt, n_call + n
+                if t_total + t_call >= budget:
+                    break
+            whole += n_call == T
+            rates.append(n_call / t_call)
+            nodes, t_total, calls = nodes + n_call, t_total + t_call, calls + 1
+        return float(np.median(rates)), nodes, t_total, calls, whole
+
+    share = seconds / 2 if single_thread else seconds
+    rate, nodes, t_total, calls, whole = run(share)
+    res = {"value": rate, "unit": "nodes/s", "cores": oracle.num_threads(), "kind": "oracle",
+           "sample": "%d layer calls (%d whole) of the %s workload, each every sequence's tree on one layer's "
+                     "inputs (%d nodes in all, verify + persist, fp64), %.1f s; median rate over the calls"
+                     % (calls, whole, cfg.name, nodes, t_total),
+           "nproc": os.cpu_count(), "model_name": cpu_model_name(),
+           "layer_call_ms": T / rate * 1e3}
+    if cfg.num_layers > 1:
+        res["step_ms_extrapolated"] = T / rate * 1e3 * cfg.num_layers
+        res["extrapolation"] = "one layer call's rate times %d layer calls per step" % cfg.num_layers
+    if single_thread:
+        oracle.set_threads(1)
+        try:
+            rate1, nodes1, t1, calls1, whole1 = run(share)
+        finally:
+            oracle.set_threads(0)
+        res["single_thread"] = {
+            "value": rate1, "unit": "nodes/s", "cores": 1,
+            "sample": "%d layer calls (%d whole), %d nodes, %.1f s" % (calls1, whole1, nodes1, t1)}
+    return res
 
 
 if __name__ == "__main__":

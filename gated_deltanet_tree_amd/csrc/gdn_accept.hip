@@ -184,10 +184,11 @@ __global__ __launch_bounds__(64) void walk_kernel(Params P) {
         if (row < P.T) P.target_out[row] = row_argmax(P, row);
         return;
     }
-    const int4 h = *reinterpret_cast<const int4 *>(P.ws.header);
-    const bool planned = (h.x == (int)kMagic) & (h.y == P.B) & (h.z == P.T);
+    const bool planned = ws_plan_matches(P);
     const int4 info = *reinterpret_cast<const int4 *>(P.ws.seq_info + b * kSeqInfoInts);
     if (!planned || info.z != GDN_SEQ_OK || info.y <= 0 || info.y > GDN_MAX_NODES) {
+        // a plan made for other dims: nothing is accepted, and gdn_tree_status reports the misuse
+        if (!planned && b == 0 && lane == 0) P.ws.header[kHdrMisuse] = 1;
         if (lane == 0) {
             P.accepted_out[b] = -1;
             P.accept_len_out[b] = 0;

@@ -332,7 +332,10 @@ int gdn_tree_status(const void *ws, size_t ws_bytes, void *stream, int32_t *firs
     if (hipStreamSynchronize(s) != hipSuccess) return GDN_ERR_DEVICE;
     int32_t header[gdn::kHeaderInts];
     if (hipMemcpy(header, ws, sizeof(header), hipMemcpyDeviceToHost) != hipSuccess) return GDN_ERR_DEVICE;
-    if (header[0] != gdn::kMagic || header[1] < 0 || header[2] < 0) return GDN_ERR_WORKSPACE;
+    if ((header[0] != gdn::kMagic && header[0] != gdn::kChainMagic) || header[1] < 0 || header[2] < 0)
+        return GDN_ERR_WORKSPACE;
+    // a persist or accept call that found the plan made for other dims wrote nothing else
+    if (header[gdn::kHdrMisuse] != 0) return GDN_ERR_WORKSPACE;
     const int B = header[1], T = header[2];
     if (ws_bytes < gdn::ws_layout(B, T).total) return GDN_ERR_WORKSPACE;
     if (B == 0) return GDN_OK;

@@ -36,11 +36,6 @@ __device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float(stati
 __device__ __forceinline__ float qnan_f() { return __int_as_float(0x7fc00000); }
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// one load, no short-circuit: the test does not hold back the loads issued next to it
-__device__ __forceinline__ bool ws_planned(const Params &P) {
-    const int4 h = *reinterpret_cast<const int4 *>(P.ws.header);
-    return (h.x == (int)kMagic) & (h.y == P.B) & (h.z == P.T);
-}
 
 // ===========================================================================
 // Verify
@@ -145,7 +140,7 @@ __global__ __launch_bounds__(kCoefThreads) void coef_kernel(Params P) {
     const int grp = P.Hv / P.Hk;
     const int b = blockIdx.x / P.Hk, g = blockIdx.x % P.Hk;
     const SeqView sv = seq_view<CHAIN>(P, b);
-    if (!CHAIN && !ws_planned(P)) return;
+    if (!CHAIN && !ws_plan_matches(P)) return;
     if (sv.status != GDN_SEQ_OK || sv.n == 0) return;
     const int lo = sv.lo, n = sv.n;
     const int cap = CHAIN ? kPath : P.max_nodes;
@@ -296,12 +291,13 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
     const int g = h / (P.Hv / P.Hk);
     const size_t out_stride = (size_t)P.Hv * D;
     const SeqView sv = seq_view<CHAIN>(P, b);  // loaded together with the header check below
-    if (!CHAIN && !ws_planned(P)) return;
+    if (!CHAIN && !ws_plan_matches(P)) return;
     if (CHAIN && P.has_ws && h == 0 && tid == 0) {
         if (b == 0) {
-            P.ws.header[0] = kMagic;
+            P.ws.header[0] = kChainMagic;
             P.ws.header[1] = P.B;
             P.ws.header[2] = P.T;
+            P.ws.header[kHdrMisuse] = 0;
         }
         P.ws.seq_status[b] = sv.status;
     }
@@ -583,12 +579,13 @@ verify_group_kernel(Params P) {
     const int b = blockIdx.x / nhg, h0 = blockIdx.x % nhg * grp;
     const int g = h0 / (P.Hv / P.Hk);
     const SeqView sv = seq_view<CHAIN>(P, b);
-    if (!CHAIN && !ws_planned(P)) return;
+    if (!CHAIN && !ws_plan_matches(P)) return;
     if (CHAIN && P.has_ws && h0 == 0 && tid == 0) {
         if (b == 0) {
-            P.ws.header[0] = kMagic;
+            P.ws.header[0] = kChainMagic;
             P.ws.header[1] = P.B;
             P.ws.header[2] = P.T;
+            P.ws.header[kHdrMisuse] = 0;
         }
         P.ws.seq_status[b] = sv.status;
     }
@@ -925,7 +922,7 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
     const int b = blockIdx.x / nhg, h0 = blockIdx.x % nhg * grp;
     const int g = h0 / (P.Hv / P.Hk);
     const SeqView sv = seq_view<false>(P, b);
-    if (!ws_planned(P)) return;
+    if (!ws_plan_matches(P)) return;
     const int lo = sv.lo, n = sv.n;
     if (sv.status != GDN_SEQ_OK) {
         for (int t = tid; t < n * grp * D; t += NT)
@@ -1317,10 +1314,13 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         pl = lane % kPath;
         dst = P.final_state + (size_t)b * P.Hv * D * D;
     } else {
-        const bool planned = ws_planned(P);
+        const bool planned = ws_plan_matches(P);
         const int4 info = *reinterpret_cast<const int4 *>(P.ws.seq_info + b * kSeqInfoInts);
         const int m = P.accepted[b];
-        if (!planned) return;
+        if (!planned) {  // no slot is written; gdn_tree_status reports the misuse
+            if (blockIdx.x == 0 && tid == 0) P.ws.header[kHdrMisuse] = 1;
+            return;
+        }
         if (info.z != GDN_SEQ_OK || info.y == 0) return;
         if (m < -1 || m >= info.y) {
             if (g == 0 && tid == 0) P.ws.seq_status[b] = GDN_SEQ_BAD_ACCEPT;

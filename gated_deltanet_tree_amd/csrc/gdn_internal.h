@@ -10,8 +10,10 @@
 
 namespace gdn {
 
-constexpr int32_t kMagic = 0x67646e74;  // written by the plan into the workspace header
-constexpr int kHeaderInts = 16;          // magic, B, T, max_nodes, max_depth, stack slots, ...
+constexpr int32_t kMagic = 0x67646e74;       // written by the plan into the workspace header
+constexpr int32_t kChainMagic = 0x67646e63;  // written by gdn_chain_verify instead: no plan in it
+constexpr int kHeaderInts = 16;  // magic, B, T, max_nodes, max_depth, stack slots, misuse flag, ...
+constexpr int kHdrMisuse = 6;    // set when a persist or accept found the plan made for other dims
 constexpr int kSeqInfoInts = 8;          // node offset, node count, verdict, slot, reserved x4
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -95,6 +97,18 @@ struct Params {
     // per-node states stored in fp16 (verify-and-store / persist-by-copy)
     uint16_t *node_states;       // [T][Hv][D][D] fp16 bits
 };
+
+// The plan in the workspace was made for exactly these dims: the header's magic,
+// B, T, max_nodes and max_depth match.  A workspace last written by a chain call
+// (kChainMagic) holds no tree metadata and fails; so does a plan for a larger
+// max_nodes, whose trees could overflow tables sized from these dims.  Two
+// vector loads, no short-circuit, so the test does not hold back loads issued
+// next to it.
+__device__ __forceinline__ bool ws_plan_matches(const Params &P) {
+    const int4 h = *reinterpret_cast<const int4 *>(P.ws.header);
+    const int4 e = *reinterpret_cast<const int4 *>(P.ws.header + 4);
+    return (h.x == kMagic) & (h.y == P.B) & (h.z == P.T) & (h.w == P.max_nodes) & (e.x == P.max_depth);
+}
 
 // ---- kernel launchers (defined in the .hip files) --------------------------
 hipError_t launch_plan(const Params &p, hipStream_t s);

@@ -42,6 +42,7 @@ __global__ __launch_bounds__(NT) void plan_kernel(Params P) {
         W.header[3] = P.max_nodes;
         W.header[4] = P.max_depth;
         W.header[5] = P.stack_slots;
+        W.header[kHdrMisuse] = 0;
     }
     if (b >= P.B) return;
 

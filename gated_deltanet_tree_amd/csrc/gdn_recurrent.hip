@@ -136,8 +136,9 @@ __device__ __forceinline__ void update_row(float (&S)[CPL], const float (&k)[CPL
 
 __device__ __forceinline__ float qnan() { return __int_as_float(0x7fc00000); }
 
+// the plan was made for these dims, including the stack size its preorder assumes
 __device__ __forceinline__ bool planned(const Params &P) {
-    return P.ws.header[0] == kMagic && P.ws.header[1] == P.B && P.ws.header[2] == P.T;
+    return ws_plan_matches(P) && P.ws.header[5] == P.stack_slots;
 }
 
 struct Tile {
@@ -288,9 +289,10 @@ __global__ __launch_bounds__(64) void chain_verify_kernel(Params P) {
     else if (n > 0 && !slot_ok) status = GDN_SEQ_BAD_SLOT;
     if (P.has_ws && t.h == 0 && t.slice == 0 && t.lane == 0) {
         if (t.b == 0) {
-            P.ws.header[0] = kMagic;
+            P.ws.header[0] = kChainMagic;
             P.ws.header[1] = P.B;
             P.ws.header[2] = P.T;
+            P.ws.header[kHdrMisuse] = 0;
         }
         P.ws.seq_status[t.b] = status;
     }
@@ -362,7 +364,10 @@ template <int D, typename Tin>
 __global__ __launch_bounds__(64) void persist_kernel(Params P) {
     using G = Geo<D>;
     const Tile t = tile_of<D>(P);
-    if (!planned(P)) return;
+    if (!planned(P)) {  // no slot is written; gdn_tree_status reports the misuse
+        if (blockIdx.x == 0 && t.lane == 0) P.ws.header[kHdrMisuse] = 1;
+        return;
+    }
     const int status = P.ws.seq_status[t.b];
     const int lo = P.ws.seq_info[t.b * kSeqInfoInts + 0];
     const int n = P.ws.seq_info[t.b * kSeqInfoInts + 1];
@@ -436,7 +441,10 @@ hipError_t launch_tree_store_d(const Params &p, hipStream_t s) {
 constexpr int kCopyThreads = 256;
 __global__ __launch_bounds__(kCopyThreads) void persist_copy_kernel(Params P) {
     const int b = blockIdx.x / P.Hv, h = blockIdx.x % P.Hv;
-    if (!planned(P)) return;
+    if (!planned(P)) {  // no slot is written; gdn_tree_status reports the misuse
+        if (blockIdx.x == 0 && threadIdx.x == 0) P.ws.header[kHdrMisuse] = 1;
+        return;
+    }
     const int lo = P.ws.seq_info[b * kSeqInfoInts + 0];
     const int n = P.ws.seq_info[b * kSeqInfoInts + 1];
     if (P.ws.seq_status[b] != GDN_SEQ_OK || n == 0) return;

@@ -138,7 +138,11 @@ size_t gdn_workspace_bytes(const gdn_dims *dims);
 
 /*
  * gdn_tree_plan -- validate the draft trees and build traversal metadata on
- * the device (one workgroup per sequence).  Per node: depth (root = 1) and the
+ * the device (one workgroup per sequence).  The trees are the parent-pointer
+ * trees DDTree's builder grows from the drafter's candidates (GreenGames page,
+ * "From autoregressive to DDTree": the budgeted tree of build_ddtree, seeded
+ * with a chain), at most one drafting block deep (GreenGames, "Prefill": 16
+ * tokens).  Per node: depth (root = 1) and the
  * root-to-node path.  Per sequence: a depth-first preorder in which the
  * children of a node (and the roots of a forest) are visited by increasing
  * (subtree size, node id), so the largest child comes last and is entered
@@ -154,7 +158,9 @@ int gdn_tree_plan(const gdn_dims *dims, const int32_t *parent, const int32_t *cu
  * head, o_n = S^n q_n where S^n is the gated delta rule applied along n's
  * root-to-node path starting from state_cache[slot_idx[b]].  state_cache is
  * only read.  Sequences the plan rejected get NaN outputs.  `ws` must come
- * from gdn_tree_plan with the same dims on the same stream.
+ * from gdn_tree_plan with the same dims on the same stream; a workspace planned
+ * for other dims (B, T, max_nodes or max_depth differ), or last written by
+ * gdn_chain_verify, makes the call write nothing at all.
  */
 int gdn_tree_verify(const gdn_dims *dims, const void *q, const void *k, const void *v,
                     const float *a, const float *b, const float *state_cache,
@@ -166,7 +172,10 @@ int gdn_tree_verify(const gdn_dims *dims, const void *q, const void *k, const vo
  * replay the rule over the root-to-m path from state_cache[slot_idx[b]] and
  * write the result in place into that slot.  accepted_node[b] = -1 skips the
  * sequence.  Only the slots of valid, accepted sequences are written.  Also
- * records the accepted path (root first) and its length in the workspace.
+ * records the accepted path (root first) and its length in the workspace.  On a
+ * workspace planned for other dims (or last written by gdn_chain_verify) no
+ * slot is written and the workspace is marked so that gdn_tree_status returns
+ * GDN_ERR_WORKSPACE.
  */
 int gdn_tree_persist(const gdn_dims *dims, const void *k, const void *v, const float *a,
                      const float *b, const int32_t *accepted_node, float *state_cache,
@@ -187,7 +196,9 @@ int gdn_tree_persist(const gdn_dims *dims, const void *k, const void *v, const f
  * GDN_SEQ_BAD_ACCEPT).  The fp16 rounding makes the persisted state differ
  * from gdn_tree_persist's fp32 replay (relative error up to 2^-11 per value),
  * so the chain bit-identity of the replay path does not hold here.  Both
- * calls need `ws` from gdn_tree_plan; persist_copy does not record the path.
+ * calls need `ws` from gdn_tree_plan with the same dims (otherwise neither
+ * writes anything, and after persist_copy gdn_tree_status returns
+ * GDN_ERR_WORKSPACE); persist_copy does not record the path.
  */
 int gdn_tree_verify_store(const gdn_dims *dims, const void *q, const void *k, const void *v, const float *a,
                           const float *b, const float *state_cache, const int32_t *slot_idx, float *out,
@@ -196,7 +207,12 @@ int gdn_tree_persist_copy(const gdn_dims *dims, const int32_t *accepted_node, co
                           float *state_cache, const int32_t *slot_idx, void *ws, size_t ws_bytes, void *stream);
 
 /*
- * gdn_chain_verify -- the W = 1 case: sequence b is the linear chain of nodes
+ * gdn_chain_verify -- the W = 1 case, linear DFlash verification of one
+ * drafted block (dflash-caddtree-integrations README, "What's in here": a tree
+ * of width 1 must reproduce the chain path byte for byte; GreenGames page,
+ * "From autoregressive to DDTree": chain DFlash, the baseline DDTree is
+ * measured against).  A chain-shaped tree given to gdn_tree_verify and
+ * gdn_tree_persist gives the same bits as this call.  Sequence b is the linear chain of nodes
  * [cu_nodes[b], cu_nodes[b+1]) (no parent array, no plan, no depth limit;
  * lengths up to dims.max_nodes <= GDN_MAX_CHAIN).  Writes o for every node
  * (q and out may both be NULL to skip outputs) and, when final_len and
@@ -207,7 +223,9 @@ int gdn_tree_persist_copy(const gdn_dims *dims, const int32_t *accepted_node, co
  * the same dims) receives the per-sequence verdicts for gdn_tree_status; it
  * is required when outputs are requested for bf16 inputs with head_dim 64 or
  * 128 and chains of at most GDN_MAX_DEPTH nodes (the kernels keep per-node
- * coefficients there), and may be NULL otherwise.
+ * coefficients there), and may be NULL otherwise.  The call marks the
+ * workspace as a chain workspace: gdn_tree_status reads its verdicts, and the
+ * tree calls reject it until gdn_tree_plan runs on it again.
  */
 int gdn_chain_verify(const gdn_dims *dims, const int32_t *cu_nodes, const void *q, const void *k,
                      const void *v, const float *a, const float *b, const float *state_cache,
@@ -233,6 +251,8 @@ int gdn_chain_verify(const gdn_dims *dims, const int32_t *cu_nodes, const void *
  * (dflash-caddtree-integrations README, "The shared method"; greedy-only
  * verify, GreenGames "What comes next").  `ws` comes from gdn_tree_plan with
  * the same dims on the same stream; the call reuses a per-node region of it.
+ * On a workspace planned for other dims every sequence gets -1, 0, -1 and
+ * gdn_tree_status returns GDN_ERR_WORKSPACE.
  * logits may be any 4-byte-aligned address; 16-byte alignment and vocab % 4
  * == 0 take the vector loads.
  */
@@ -316,8 +336,10 @@ int gdn_tree_read_metadata(const gdn_dims *dims, const void *ws, size_t ws_bytes
  * gdn_tree_status -- synchronizes `stream`, then reads the verdicts in `ws`.
  * Returns GDN_OK, GDN_ERR_TREE (some sequence was skipped; *first_bad_seq and
  * *first_bad_code name the lowest such sequence and its gdn_seq_status),
- * GDN_ERR_WORKSPACE (ws was never planned) or GDN_ERR_DEVICE.  The two
- * outputs are HOST pointers and may be NULL.
+ * GDN_ERR_WORKSPACE (ws was never planned, or a persist or accept call found
+ * it planned for other dims) or GDN_ERR_DEVICE.  Workspaces written by
+ * gdn_chain_verify are read the same way.  The two outputs are HOST pointers
+ * and may be NULL.
  */
 int gdn_tree_status(const void *ws, size_t ws_bytes, void *stream, int32_t *first_bad_seq,
                     int32_t *first_bad_code);

@@ -55,6 +55,8 @@ def _declare(lib):
     lib.oracle_tree.argtypes = [i, ip, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, dp]
     lib.oracle_accept_state.argtypes = [i, ip, i, i, i, i, i, dp, dp, dp, dp, dp, dp, ip]
     lib.oracle_num_threads.argtypes = []
+    lib.oracle_set_threads.argtypes = [i]
+    lib.oracle_set_threads.restype = None
     for f in (lib.oracle_chain, lib.oracle_tree, lib.oracle_accept_state, lib.oracle_num_threads):
         f.restype = ctypes.c_int
     return lib
@@ -91,6 +93,11 @@ class using_library:
 
 def num_threads() -> int:
     return _load().oracle_num_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads the oracle's loops use from now on; 0 restores the default."""
+    _load().oracle_set_threads(int(n))
 
 
 def widen(x) -> np.ndarray:

@@ -257,3 +257,13 @@ int oracle_num_threads(void)
     }
     return t;
 }
+
+/* Threads the loops above use from now on (the CPU baseline times one thread
+   and all of them); n < 1 restores the OpenMP default. */
+void oracle_set_threads(int n)
+{
+    static int dflt = 0;
+    if (dflt == 0)
+        dflt = omp_get_max_threads();
+    omp_set_num_threads(n >= 1 ? n : dflt);
+}

@@ -264,8 +264,54 @@ def pin_forest():
             assert rel(out[i, h], S @ c["q"][i, h]) < 1e-12
 
 
+def pin_batch_wrappers():
+    """verify_batch and persist_batch, which give every multi-sequence GPU test its
+    expected values: each sequence's node state is the rule over its own
+    root-to-node path from its own committed state (magik.net page, "The Broader
+    Context"; GreenGames page, "From autoregressive to DDTree").  Checked node by
+    node against the literal per-path replay on a ragged batch: sizes 5, 0, 7 (a
+    forest of three roots), 1 and 4; a distinct committed state per sequence;
+    value head h reading key head h // 2; one sequence skipped (accepted -1)."""
+    rng = np.random.default_rng(21)
+    trees = [np.array([-1, 0, 0, 1, 3], np.int32), np.zeros(0, np.int32),
+             np.array([-1, 0, -1, 2, -1, 4, 5], np.int32), np.array([-1], np.int32),
+             np.array([-1, 0, 1, 1], np.int32)]
+    sizes = [len(t) for t in trees]
+    cu = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    T, hk, hv, d = int(cu[-1]), 2, 4, 5
+    inputs = dict(q=unit(rng, T, hk, d), k=unit(rng, T, hk, d), v=rng.standard_normal((T, hv, d)),
+                  a=rng.uniform(0.2, 1.0, (T, hv)), b=rng.uniform(0.05, 1.0, (T, hv)))
+    S0_seq = rng.standard_normal((len(trees), hv, d, d))
+    accepted = np.array([4, -1, 6, 0, -1], np.int32)
+    accepted[4] = -1  # a non-empty sequence skipped
+    out = oracle.verify_batch(trees, cu, inputs, S0_seq)
+    res = oracle.persist_batch(trees, cu, inputs, S0_seq, accepted)
+    assert out.shape == (T, hv, d) and len(res) == len(trees)
+    for s, par in enumerate(trees):
+        lo = int(cu[s])
+        for i in range(len(par)):
+            for h in range(hv):
+                g = h // (hv // hk)
+                sl = slice(lo, lo + len(par))
+                S = path_replay(par, i, S0_seq[s][h], inputs["k"][sl, g], inputs["v"][sl, h], inputs["a"][sl, h],
+                                inputs["b"][sl, h])
+                assert rel(out[lo + i, h], S @ inputs["q"][lo + i, g]) < 1e-12, (s, i, h)
+        st, path = res[s]
+        m = int(accepted[s])
+        if m < 0 or len(par) == 0:
+            assert st is None and len(path) == 0, s
+            continue
+        assert list(path) == path_of(par, m), s
+        for h in range(hv):
+            g = h // (hv // hk)
+            sl = slice(lo, lo + len(par))
+            S = path_replay(par, m, S0_seq[s][h], inputs["k"][sl, g], inputs["v"][sl, h], inputs["a"][sl, h],
+                            inputs["b"][sl, h])
+            assert rel(st[h], S) < 1e-12, (s, h)
+
+
 ALL_PINS = [
     pin_tiny_unrolled, pin_closed_forms, pin_chain_equals_sequential, pin_superposition,
     pin_duplicate_siblings, pin_ancestor_only, pin_permutation, pin_persist_replay, pin_forest,
-    lambda: pin_brute_force_small_trees(limit=60),
+    pin_batch_wrappers, lambda: pin_brute_force_small_trees(limit=60),
 ]

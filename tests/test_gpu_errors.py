@@ -173,3 +173,84 @@ def test_host_side_errors():
     fresh = torch.zeros_like(ws)
     rc, _, _ = G.gdn_tree_status(fresh)
     assert rc == -4  # never planned
+
+
+def _misuse_case(G, D, dt, rng):
+    trees = _base(rng)
+    parent = np.concatenate(trees).astype(np.int32)
+    cu = W.cu_from_trees(trees).astype(np.int32)
+    T = len(parent)
+    slots = np.array([2, 0, 3, 1], np.int32)
+    inp = _inputs(rng, T, D, dt)
+    cache = rng.standard_normal((4, HV, D, D)).astype(np.float32)
+    qkv = G.GDN_F32 if dt == "f32" else G.GDN_BF16
+    return parent, cu, T, slots, inp, cache, qkv
+
+
+def _tree_calls_write_nothing(G, dims, ws, T, D, dev, cache, cache_d, slots, accept_vocab=37):
+    """verify, persist and accept on a workspace whose plan does not match `dims`:
+    outputs keep their sentinel, no slot changes, acceptance reports nothing, and
+    gdn_tree_status names the workspace."""
+    sentinel = 123.25
+    out = torch.full((T, HV, D), sentinel, device="cuda")
+    acc = to_dev(np.zeros(4, np.int32))
+    G.gdn_tree_verify(dims, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], cache_d, to_dev(slots), out, ws)
+    G.gdn_tree_persist(dims, dev["k"], dev["v"], dev["a"], dev["b"], acc, cache_d, to_dev(slots), ws)
+    logits = torch.zeros((T, accept_vocab), device="cuda")
+    tok = torch.zeros(T, dtype=torch.int32, device="cuda")
+    a_out, l_out, n_out = (torch.full((4,), 77, dtype=torch.int32, device="cuda") for _ in range(3))
+    G.gdn_tree_accept(dims, logits, tok, a_out, l_out, n_out, ws)
+    rc, _, _ = G.gdn_tree_status(ws)
+    assert rc == -4
+    assert (out.cpu().numpy() == sentinel).all()
+    assert np.array_equal(cache_d.cpu().numpy().view(np.uint32), cache.view(np.uint32))
+    assert a_out.cpu().tolist() == [-1] * 4 and l_out.cpu().tolist() == [0] * 4
+    assert n_out.cpu().tolist() == [-1] * 4
+
+
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_plan_for_other_dims_is_rejected(path):
+    """A plan made with a larger max_nodes (or another max_depth) than the calls
+    that read it: verify, persist and accept write nothing, and the status call
+    reports the workspace; the same calls with the plan's own dims work."""
+    G = require_gpu()
+    D, dt = PATHS[path]
+    rng = np.random.default_rng(31)
+    parent, cu, T, slots, inp, cache, qkv = _misuse_case(G, D, dt, rng)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    for plan_nodes, plan_depth, call_nodes, call_depth in ((64, 16, 16, 16), (16, 12, 16, 16)):
+        plan_dims = G.make_dims(4, T, plan_nodes, HK, HV, D, 4, qkv, max_depth=plan_depth)
+        dims = G.make_dims(4, T, call_nodes, HK, HV, D, 4, qkv, max_depth=call_depth)
+        ws = G.new_workspace(dims)
+        cache_d = to_dev(cache.copy())
+        G.gdn_tree_plan(plan_dims, to_dev(parent), to_dev(cu), to_dev(slots), ws)
+        _tree_calls_write_nothing(G, dims, ws, T, D, dev, cache, cache_d, slots)
+        # planned again for the calls' dims, the same workspace works
+        G.gdn_tree_plan(dims, to_dev(parent), to_dev(cu), to_dev(slots), ws)
+        out = torch.full((T, HV, D), float("nan"), device="cuda")
+        G.gdn_tree_verify(dims, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], cache_d, to_dev(slots), out, ws)
+        assert G.gdn_tree_status(ws)[0] == 0
+        assert np.isfinite(out.cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_chain_workspace_is_not_a_plan(path):
+    """gdn_chain_verify marks its workspace as a chain workspace: the status call
+    reads its verdicts, and the tree calls refuse it (it holds no paths or
+    preorder) until it is planned again."""
+    G = require_gpu()
+    D, dt = PATHS[path]
+    rng = np.random.default_rng(32)
+    parent, cu, T, slots, inp, cache, qkv = _misuse_case(G, D, dt, rng)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    dims = G.make_dims(4, T, 16, HK, HV, D, 4, qkv)
+    ws = G.new_workspace(dims)
+    cache_d = to_dev(cache.copy())
+    # a real plan first, so the chain call overwrites a valid header
+    G.gdn_tree_plan(dims, to_dev(parent), to_dev(cu), to_dev(slots), ws)
+    cout = torch.full((T, HV, D), float("nan"), device="cuda")
+    G.gdn_chain_verify(dims, to_dev(cu), dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], cache_d, to_dev(slots),
+                       cout, ws=ws)
+    assert G.gdn_tree_status(ws)[0] == 0
+    assert np.isfinite(cout.cpu().numpy()).all()
+    _tree_calls_write_nothing(G, dims, ws, T, D, dev, cache, cache_d, slots)

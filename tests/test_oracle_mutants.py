@@ -50,3 +50,47 @@ def test_unmutated_copy_passes_all_pins(tmp_path):
     with oracle.using_library(lib):
         for pin in pins.ALL_PINS:
             pin()
+
+
+def _wrong_seq_state(trees, cu, inputs, S0_seq):
+    """Mistake: every sequence starts from the first sequence's committed state."""
+    return _orig_verify(trees, cu, inputs, [S0_seq[0]] * len(trees))
+
+
+def _shifted_ranges(trees, cu, inputs, S0_seq):
+    """Mistake: node ranges taken one sequence late (cu[s + 1] as the start)."""
+    import numpy as np
+    cu2 = np.concatenate([[0], cu[2:], [cu[-1]]])[: len(cu)]
+    return _orig_verify(trees, cu2, inputs, S0_seq)
+
+
+def _persist_skip_ignored(trees, cu, inputs, S0_seq, accepted):
+    """Mistake: a skipped sequence (accepted -1) persists its last node."""
+    import numpy as np
+    acc = np.array([m if m >= 0 else len(t) - 1 for m, t in zip(accepted, trees)], np.int32)
+    return _orig_persist(trees, cu, inputs, S0_seq, acc)
+
+
+def _persist_wrong_state(trees, cu, inputs, S0_seq, accepted):
+    """Mistake: persist replays from the last sequence's committed state."""
+    return _orig_persist(trees, cu, inputs, [S0_seq[-1]] * len(trees), accepted)
+
+
+_orig_verify = oracle.verify_batch
+_orig_persist = oracle.persist_batch
+WRAPPER_MUTANTS = {
+    "verify_wrong_seq_state": ("verify_batch", _wrong_seq_state),
+    "verify_shifted_ranges": ("verify_batch", _shifted_ranges),
+    "persist_skip_ignored": ("persist_batch", _persist_skip_ignored),
+    "persist_wrong_state": ("persist_batch", _persist_wrong_state),
+}
+
+
+@pytest.mark.parametrize("name", sorted(WRAPPER_MUTANTS))
+def test_batch_wrapper_mutant_fails_its_pin(name, monkeypatch):
+    """Plausible mistakes in the batch wrappers (the per-sequence slicing, state
+    selection and skip handling) each fail pin_batch_wrappers."""
+    attr, fn = WRAPPER_MUTANTS[name]
+    monkeypatch.setattr(oracle, attr, fn)
+    with pytest.raises((AssertionError, ValueError, IndexError)):
+        pins.pin_batch_wrappers()

@@ -10,7 +10,7 @@ from pins import golden_example
 @pytest.mark.parametrize("pin", [
     pins.pin_tiny_unrolled, pins.pin_closed_forms, pins.pin_chain_equals_sequential,
     pins.pin_superposition, pins.pin_duplicate_siblings, pins.pin_ancestor_only,
-    pins.pin_permutation, pins.pin_persist_replay, pins.pin_forest,
+    pins.pin_permutation, pins.pin_persist_replay, pins.pin_forest, pins.pin_batch_wrappers,
 ], ids=lambda f: f.__name__)
 def test_pin(pin):
     pin()
