@@ -112,17 +112,18 @@ def cpu_model_name():
     return None
 
 
-def memory_ceilings(dev):
-    """Plain streaming rates on this part for scale, measured with torch's own
-    kernels (not this library): a sum over 1 GiB of fp32 (read) and a 1 GiB
-    device copy (read + write), median of 10 launches timed with events."""
+def memory_ceilings(G, dev):
+    """Plain streaming rates of this part, the practical ceilings beside the 8 TB/s
+    peak: the library's diagnostic pass reading 1 GiB, and copying 1 GiB into another
+    buffer (read + write), median of 10 launches timed with events."""
     import torch
     x = torch.empty(256 << 20, dtype=torch.float32, device=dev).fill_(1.0)
     y = torch.empty_like(x)
+    partial = torch.empty((x.numel() * 4 + 65535) // 65536 * 4, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     res = {}
-    for name, fn, nbytes in (("read", lambda: x.sum(), x.numel() * 4),
-                             ("copy", lambda: y.copy_(x), 2 * x.numel() * 4)):
+    for name, fn, nbytes in (("read", lambda: G.gdn_probe_stream("read", x, partial), x.numel() * 4),
+                             ("copy", lambda: G.gdn_probe_stream("copy", x, y), 2 * x.numel() * 4)):
         for _ in range(3):
             fn()
         ts = []
@@ -134,9 +135,9 @@ def memory_ceilings(dev):
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1) * 1e-3)
         res[name + "_gbs"] = nbytes / float(np.median(ts)) / 1e9
-    del x, y
+    del x, y, partial
     torch.cuda.synchronize()
-    res["how"] = "torch sum over 1 GiB fp32 (read) and torch copy of 1 GiB (read + write), median of 10"
+    res["how"] = "gdn_probe_stream reading 1 GiB (read) and copying 1 GiB (read + write bytes), median of 10"
     return res
 
 
@@ -453,7 +454,7 @@ def main():
         "data": "synthetic",
     }
     result.update({k: v for k, v in res.items() if k not in ("value", "ms_per_step")})
-    result["memory_ceilings"] = memory_ceilings("cuda")
+    result["memory_ceilings"] = memory_ceilings(G, "cuda")
     if not args.no_accept:
         result["accept"] = bench_accept(G, W, cfg, ctx["trees"], ctx["dims"], ctx["parent_d"], ctx["cu_d"],
                                         ctx["slot_d"], args.accept_steps)

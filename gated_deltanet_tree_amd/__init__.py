@@ -38,7 +38,7 @@ SEQ_STATUS = {0: "OK", 1: "BAD_NODES", 2: "BAD_SLOT", 3: "DUP_SLOT", 4: "BAD_PAR
 EXPORTS = ["gdn_workspace_bytes", "gdn_tree_plan", "gdn_tree_verify", "gdn_tree_persist",
            "gdn_chain_verify", "gdn_tree_accept", "gdn_draft_topk", "gdn_ddtree_nodes", "gdn_ddtree_build",
            "gdn_state_copy", "gdn_tree_verify_store", "gdn_tree_persist_copy", "gdn_tree_read_metadata",
-           "gdn_tree_status", "gdn_strerror"]
+           "gdn_tree_status", "gdn_strerror", "gdn_probe_stream"]
 
 
 class GdnError(RuntimeError):
@@ -82,6 +82,7 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_tree_plan.argtypes = [dp, vp, vp, vp, vp, sz, vp]
     lib.gdn_tree_verify.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdn_tree_persist.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdn_probe_stream.argtypes = [ctypes.c_int32, vp, vp, sz, sz, vp]
     lib.gdn_chain_verify.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdn_tree_accept.argtypes = [dp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, sz, vp]
     i32c = ctypes.c_int32
@@ -98,7 +99,7 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_strerror.restype = ctypes.c_char_p
     for f in ("gdn_tree_plan", "gdn_tree_verify", "gdn_tree_persist", "gdn_chain_verify",
               "gdn_tree_accept", "gdn_draft_topk", "gdn_ddtree_build", "gdn_state_copy", "gdn_tree_verify_store",
-              "gdn_tree_persist_copy", "gdn_tree_read_metadata", "gdn_tree_status"):
+              "gdn_tree_persist_copy", "gdn_tree_read_metadata", "gdn_tree_status", "gdn_probe_stream"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -170,6 +171,15 @@ def gdn_tree_verify(dims, q, k, v, a, b, state_cache, slot_idx, out, ws, stream=
         _ptr(state_cache, "state_cache", torch.float32, dims.num_slots * Hv * D * D),
         _ptr(slot_idx, "slot_idx", torch.int32, B), _ptr(out, "out", torch.float32, T * Hv * D),
         _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)), "gdn_tree_verify")
+
+
+def gdn_probe_stream(mode, src, dst, stream=None):
+    """Diagnostic streaming pass: mode "read" reads all of src (partial sums into
+    dst), mode "copy" copies src into dst."""
+    m = {"read": 0, "copy": 1}[mode]
+    nbytes = src.numel() * src.element_size()
+    _check(load_library().gdn_probe_stream(m, _ptr(src, "src"), _ptr(dst, "dst"), nbytes,
+                                           dst.numel() * dst.element_size(), _stream(stream)), "gdn_probe_stream")
 
 
 def gdn_tree_persist(dims, k, v, a, b, accepted_node, state_cache, slot_idx, ws, stream=None):

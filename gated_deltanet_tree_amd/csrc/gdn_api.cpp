@@ -295,6 +295,17 @@ int gdn_state_copy(int32_t num_v_heads, int32_t head_dim, const float *src_cache
                                            dst_slot, count, slot_floats, as_stream(stream)));
 }
 
+int gdn_probe_stream(int32_t mode, const void *src, void *dst, size_t bytes, size_t dst_bytes, void *stream) {
+    if (mode != 0 && mode != 1) return GDN_ERR_SHAPE;
+    if (bytes == 0) return GDN_OK;
+    if (!src || !dst) return GDN_ERR_NULL;
+    if (bytes % 16 || reinterpret_cast<uintptr_t>(src) % 16 || reinterpret_cast<uintptr_t>(dst) % 16)
+        return GDN_ERR_SHAPE;
+    if (bytes / (64 * 1024) >= (size_t)INT_MAX) return GDN_ERR_SHAPE;
+    if (dst_bytes < (mode == 0 ? gdn::probe_partials_bytes(bytes) : bytes)) return GDN_ERR_WORKSPACE;
+    return launched(gdn::launch_probe(mode, src, dst, bytes, as_stream(stream)));
+}
+
 int gdn_tree_read_metadata(const gdn_dims *dims, const void *ws, size_t ws_bytes, int32_t *depth,
                            int32_t *order, int32_t *action, int32_t *path, int32_t *path_len,
                            int32_t *seq_status, void *stream) {

@@ -134,6 +134,10 @@ hipError_t launch_draft_topk(int rows, int vocab, int width, const float *logits
 hipError_t launch_ddtree_build(int B, int levels, int width, int budget, int max_depth, const int32_t *root_token,
                                const int32_t *tokens, const float *logp, int32_t *parent, int32_t *node_token,
                                int32_t *cu_nodes, hipStream_t s);
+// streaming diagnostic: mode 0 reads `bytes` (one partial sum per wave into dst),
+// mode 1 copies them
+size_t probe_partials_bytes(size_t bytes);
+hipError_t launch_probe(int mode, const void *src, void *dst, size_t bytes, hipStream_t s);
 // prefix-cache snapshots
 hipError_t launch_state_copy(const float *src, int src_total, const int32_t *src_slot, float *dst, int dst_total,
                              const int32_t *dst_slot, int count, size_t slot_floats, hipStream_t s);

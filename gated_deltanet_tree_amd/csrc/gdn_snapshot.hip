@@ -57,3 +57,63 @@ hipError_t launch_state_copy(const float *src, int src_total, const int32_t *src
 }
 
 }  // namespace gdn
+
+// ---------------------------------------------------------------------------
+// Streaming diagnostic: the plain read and copy rates of this part, the
+// ceilings the state streams above are measured against.  64 KiB per
+// 256-thread workgroup, 16-byte accesses, four in flight per thread; the read
+// keeps one partial sum per workgroup so no load can be dropped.
+// ---------------------------------------------------------------------------
+namespace gdn {
+namespace {
+
+constexpr int kProbeThreads = 256;
+constexpr size_t kProbeBlockBytes = 64 * 1024;
+
+template <bool COPY>
+__global__ __launch_bounds__(kProbeThreads) void probe_kernel(const float4 *src, float4 *dst, size_t n16) {
+    const size_t base = (size_t)blockIdx.x * (kProbeBlockBytes / 16);
+    float acc = 0.0f;
+#pragma unroll 1
+    for (size_t off = threadIdx.x; off < kProbeBlockBytes / 16; off += 4 * kProbeThreads) {
+        float4 x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const size_t i = base + off + (size_t)u * kProbeThreads;
+            x[u] = i < n16 ? src[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const size_t i = base + off + (size_t)u * kProbeThreads;
+            if (COPY) {
+                if (i < n16) dst[i] = x[u];
+            } else {
+                acc += (x[u].x + x[u].y) + (x[u].z + x[u].w);
+            }
+        }
+    }
+    if (!COPY) {
+        for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+        if (threadIdx.x % 64 == 0) reinterpret_cast<float *>(dst)[blockIdx.x * (kProbeThreads / 64) + threadIdx.x / 64] = acc;
+    }
+}
+
+}  // namespace
+
+size_t probe_partials_bytes(size_t bytes) {
+    return (bytes + kProbeBlockBytes - 1) / kProbeBlockBytes * (kProbeThreads / 64) * sizeof(float);
+}
+
+hipError_t launch_probe(int mode, const void *src, void *dst, size_t bytes, hipStream_t s) {
+    const size_t n16 = bytes / 16;
+    const size_t blocks = (bytes + kProbeBlockBytes - 1) / kProbeBlockBytes;
+    if (mode == 0)
+        hipLaunchKernelGGL(probe_kernel<false>, dim3((unsigned)blocks), dim3(kProbeThreads), 0, s,
+                           static_cast<const float4 *>(src), static_cast<float4 *>(dst), n16);
+    else
+        hipLaunchKernelGGL(probe_kernel<true>, dim3((unsigned)blocks), dim3(kProbeThreads), 0, s,
+                           static_cast<const float4 *>(src), static_cast<float4 *>(dst), n16);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -344,6 +344,16 @@ int gdn_tree_read_metadata(const gdn_dims *dims, const void *ws, size_t ws_bytes
 int gdn_tree_status(const void *ws, size_t ws_bytes, void *stream, int32_t *first_bad_seq,
                     int32_t *first_bad_code);
 
+/*
+ * gdn_probe_stream -- diagnostic, not part of a decode step: the plain
+ * streaming rates of the device, the practical ceilings the state streams of
+ * verify and persist are measured against.  mode 0 reads `bytes` of src and
+ * writes one partial sum per 64 lanes of each 64 KiB block into dst (dst_bytes
+ * >= 16 * ceil(bytes / 65536)); mode 1 copies `bytes` from src to dst
+ * (dst_bytes >= bytes).  bytes and both addresses are multiples of 16.
+ */
+int gdn_probe_stream(int32_t mode, const void *src, void *dst, size_t bytes, size_t dst_bytes, void *stream);
+
 /* Static string for a gdn_status value. */
 const char *gdn_strerror(int status);
 
