@@ -38,7 +38,7 @@ SEQ_STATUS = {0: "OK", 1: "BAD_NODES", 2: "BAD_SLOT", 3: "DUP_SLOT", 4: "BAD_PAR
 EXPORTS = ["gdn_workspace_bytes", "gdn_tree_plan", "gdn_tree_verify", "gdn_tree_persist",
            "gdn_chain_verify", "gdn_tree_accept", "gdn_draft_topk", "gdn_ddtree_nodes", "gdn_ddtree_build",
            "gdn_state_copy", "gdn_tree_verify_store", "gdn_tree_persist_copy", "gdn_tree_read_metadata",
-           "gdn_tree_status", "gdn_strerror", "gdn_probe_stream"]
+           "gdn_tree_status", "gdn_strerror", "gdn_tree_verify_static", "gdn_probe_stream"]
 
 
 class GdnError(RuntimeError):
@@ -82,6 +82,7 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_tree_plan.argtypes = [dp, vp, vp, vp, vp, sz, vp]
     lib.gdn_tree_verify.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdn_tree_persist.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdn_tree_verify_static.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_probe_stream.argtypes = [ctypes.c_int32, vp, vp, sz, sz, vp]
     lib.gdn_chain_verify.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdn_tree_accept.argtypes = [dp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -99,7 +100,8 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_strerror.restype = ctypes.c_char_p
     for f in ("gdn_tree_plan", "gdn_tree_verify", "gdn_tree_persist", "gdn_chain_verify",
               "gdn_tree_accept", "gdn_draft_topk", "gdn_ddtree_build", "gdn_state_copy", "gdn_tree_verify_store",
-              "gdn_tree_persist_copy", "gdn_tree_read_metadata", "gdn_tree_status", "gdn_probe_stream"):
+              "gdn_tree_persist_copy", "gdn_tree_read_metadata", "gdn_tree_status", "gdn_tree_verify_static",
+              "gdn_probe_stream"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -171,6 +173,21 @@ def gdn_tree_verify(dims, q, k, v, a, b, state_cache, slot_idx, out, ws, stream=
         _ptr(state_cache, "state_cache", torch.float32, dims.num_slots * Hv * D * D),
         _ptr(slot_idx, "slot_idx", torch.int32, B), _ptr(out, "out", torch.float32, T * Hv * D),
         _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)), "gdn_tree_verify")
+
+
+def gdn_tree_verify_static(dims, parent, cu_nodes, slot_idx, q, k, v, a, b, state_cache, out, seq_status=None,
+                           stream=None):
+    """Plan + verify with no workspace: the plan's metadata lives in the library's
+    static per-GPU scratch.  seq_status (int32 [B]) receives the verdicts if given."""
+    T, B, Hk, Hv, D = dims.total_nodes, dims.num_seqs, dims.num_k_heads, dims.num_v_heads, dims.head_dim
+    dt = _qkv_dtype(dims)
+    _check(load_library().gdn_tree_verify_static(
+        ctypes.byref(dims), _ptr(parent, "parent", torch.int32, T), _ptr(cu_nodes, "cu_nodes", torch.int32, B + 1),
+        _ptr(slot_idx, "slot_idx", torch.int32, B), _ptr(q, "q", dt, T * Hk * D), _ptr(k, "k", dt, T * Hk * D),
+        _ptr(v, "v", dt, T * Hv * D), _ptr(a, "a", torch.float32, T * Hv), _ptr(b, "b", torch.float32, T * Hv),
+        _ptr(state_cache, "state_cache", torch.float32, dims.num_slots * Hv * D * D),
+        _ptr(out, "out", torch.float32, T * Hv * D), _ptr(seq_status, "seq_status", torch.int32, B, allow_none=True),
+        _stream(stream)), "gdn_tree_verify_static")
 
 
 def gdn_probe_stream(mode, src, dst, stream=None):

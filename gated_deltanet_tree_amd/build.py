@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgdn_tree.so")
 ARCH = "gfx950"
 
-SOURCES = ["gdn_api.cpp", "gdn_plan.hip", "gdn_recurrent.hip", "gdn_fast.hip", "gdn_accept.hip", "gdn_ddtree.hip", "gdn_snapshot.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_plan.hip", "gdn_recurrent.hip", "gdn_fast.hip", "gdn_accept.hip", "gdn_ddtree.hip", "gdn_snapshot.hip", "gdn_static.hip"]
 
 
 def hipcc() -> str:

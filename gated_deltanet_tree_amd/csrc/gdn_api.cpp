@@ -117,6 +117,42 @@ int gdn_tree_verify(const gdn_dims *dims, const void *q, const void *k, const vo
     return launched(gdn::launch_tree_verify_recurrent(p, dims->qkv_dtype, as_stream(stream)));
 }
 
+int gdn_tree_verify_static(const gdn_dims *dims, const int32_t *parent, const int32_t *cu_nodes,
+                           const int32_t *slot_idx, const void *q, const void *k, const void *v, const float *a,
+                           const float *b, const float *state_cache, float *out, int32_t *seq_status,
+                           void *stream) {
+    int rc = check_dims(dims, GDN_MAX_NODES);
+    if (rc) return rc;
+    if (!cu_nodes) return GDN_ERR_NULL;
+    if (dims->total_nodes > 0 && (!parent || !q || !k || !v || !a || !b || !out)) return GDN_ERR_NULL;
+    if (dims->num_seqs > 0 && (!state_cache || !slot_idx)) return GDN_ERR_NULL;
+    // the plan's metadata must fit the library's static scratch
+    if (gdn_workspace_bytes(dims) > gdn::static_scratch_bytes()) return GDN_ERR_WORKSPACE;
+    if (dims->num_seqs == 0) return GDN_OK;
+    void *ws = nullptr;
+    if (gdn::static_scratch(&ws) != hipSuccess) return GDN_ERR_LAUNCH;
+    Params p = base_params(dims);
+    p.parent = parent;
+    p.cu_nodes = cu_nodes;
+    p.slot_idx = slot_idx;
+    p.ws = gdn::ws_ptrs(ws, p.B, p.T, p.Hv);
+    if (seq_status) p.ws.seq_status = seq_status;  // the verdicts go to the caller
+    p.has_ws = 1;
+    hipStream_t s = as_stream(stream);
+    if (gdn::launch_plan(p, s) != hipSuccess) return GDN_ERR_LAUNCH;
+    if (dims->total_nodes == 0) return GDN_OK;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.a = a;
+    p.b = b;
+    p.state_in = state_cache;
+    p.out = out;
+    if (!recurrent_forced() && gdn::fast_tree_supported(p.D, dims->qkv_dtype, dims->max_nodes))
+        return launched(gdn::launch_tree_verify_fast(p, s));
+    return launched(gdn::launch_tree_verify_recurrent(p, dims->qkv_dtype, s));
+}
+
 int gdn_tree_persist(const gdn_dims *dims, const void *k, const void *v, const float *a,
                      const float *b, const int32_t *accepted_node, float *state_cache,
                      const int32_t *slot_idx, void *ws, size_t ws_bytes, void *stream) {

@@ -138,6 +138,10 @@ hipError_t launch_ddtree_build(int B, int levels, int width, int budget, int max
 // mode 1 copies them
 size_t probe_partials_bytes(size_t bytes);
 hipError_t launch_probe(int mode, const void *src, void *dst, size_t bytes, hipStream_t s);
+// the static scratch of gdn_tree_verify_static: its size, and this GPU's device
+// address of it (looked up on the first call on each device)
+size_t static_scratch_bytes();
+hipError_t static_scratch(void **out);
 // prefix-cache snapshots
 hipError_t launch_state_copy(const float *src, int src_total, const int32_t *src_slot, float *dst, int dst_total,
                              const int32_t *dst_slot, int count, size_t slot_floats, hipStream_t s);

@@ -168,6 +168,29 @@ int gdn_tree_verify(const gdn_dims *dims, const void *q, const void *k, const vo
                     void *stream);
 
 /*
+ * gdn_tree_verify_static -- gdn_tree_plan followed by gdn_tree_verify in one
+ * call with no caller workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  The plan's metadata goes to a scratch array of
+ * 32 MiB in device memory that the library holds per GPU until the process
+ * ends; dims whose gdn_workspace_bytes exceed it return GDN_ERR_WORKSPACE
+ * before anything is enqueued.  The call allocates nothing (the first call on
+ * each device looks up that device's scratch address; make it outside graph
+ * capture).  Arguments are those of the two calls it replaces; the outputs are
+ * the same bits gdn_tree_verify writes after gdn_tree_plan.  seq_status
+ * (device int32 [B], may be NULL) receives the per-sequence verdicts that
+ * gdn_tree_status would report.  Every call on one GPU uses that GPU's single
+ * scratch array: calls that overlap on one GPU (other streams, other threads)
+ * race and must be serialized by the caller.  The scratch is not readable
+ * through gdn_tree_status, gdn_tree_read_metadata or gdn_tree_persist; a
+ * decode step that persists plans into a workspace of its own.
+ */
+int gdn_tree_verify_static(const gdn_dims *dims, const int32_t *parent, const int32_t *cu_nodes,
+                           const int32_t *slot_idx, const void *q, const void *k, const void *v, const float *a,
+                           const float *b, const float *state_cache, float *out, int32_t *seq_status,
+                           void *stream);
+
+/*
  * gdn_tree_persist -- for each sequence b with accepted_node[b] = m >= 0,
  * replay the rule over the root-to-m path from state_cache[slot_idx[b]] and
  * write the result in place into that slot.  accepted_node[b] = -1 skips the
