@@ -26,6 +26,7 @@ namespace gdn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTile = 32;             // nodes per MFMA block
@@ -35,6 +36,13 @@ constexpr int kFastMaxNodes = 96;     // largest tree the MFMA verify takes (3 n
 __device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
 __device__ __forceinline__ float qnan_f() { return __int_as_float(0x7fc00000); }
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Buffer resource over `bytes` bytes from `base`: loads past the end return zero and
+// stores past the end are dropped by the hardware's range check (the byte offset is
+// the VGPR offset; it must hold all of it, the scalar offset is not range-checked).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
 
 
 // ===========================================================================
@@ -843,78 +851,72 @@ verify_group_kernel(Params P) {
 // ===========================================================================
 // Verify for trees of 33 .. 96 nodes: NB node blocks of 32, one workgroup per
 // (sequence, group of GRP value heads of one key head: all of them, or one for a
-// small batch), one workgroup per CU (the keys and queries of all blocks stay in
-// LDS).  The Gram entries k.k and k.q of every
-// block pair and the per-(head, node) coefficients are formed once; ancestors
-// may sit in any block, so each head first takes X_j = K_j S0^T for all blocks
-// (R_j = diag(b)V_j - diag(alpha)X_j kept in registers), then per block t
-// O_t = diag(gamma)Y_t + sum_j MT_tj R_j, with MT (the output operator, rows
-// from the 16-step back substitution) dense in LDS: cleared once, its entries
-// (the same places, the ancestors, for every head) rewritten per head.
-// All products run on bf16 MFMA with fp32 operands split hi + lo.
+// small batch).  The Gram entries k.k and k.q of every block pair and the
+// per-(head, node) coefficients are formed once; ancestors may sit in any block,
+// so each head takes Y_t = Q_t S0^T and X_j = K_j S0^T for all blocks, then
+// R_j = diag(b)V_j - diag(alpha)X_j and O_t = diag(gamma)Y_t + sum_j MT_tj R_j
+// with MT (the output operator, rows from the 16-step back substitution) dense
+// in LDS: cleared once, its entries (the same places, the ancestors, for every
+// head) rewritten per head.  All products run on bf16 MFMA with fp32 operands
+// split hi + lo.  LDS and registers are kept small enough that two workgroups
+// share a CU (a 65-node tree: 79 KB, at most 256 registers), so one's table,
+// Gram and coefficient phases run under the other's state stream:
+//  - keys and queries are staged for the tree's own nodes only (max_nodes rows;
+//    rows past the last node enter the products as zero fragments);
+//  - the values are read from memory into registers per head, not staged;
+//  - the dense output operator has max_nodes rows and as many columns, rounded
+//    up to the 16 of one k-step, and shares its LDS with the Gram entries,
+//    coefficients and gates, which are dead once the path weights are formed;
+//  - one state register set: the next head's state is issued as soon as this
+//    head's products with the state are taken, and streams in while this head's
+//    R = diag(b)V - diag(alpha)X and output products are formed;
+//  - k-steps and node blocks past the last node are skipped.
 // ===========================================================================
-template <int D, int NB>
+template <int D>
 struct BPad {
-    static constexpr int NN = NB * kTile;  // node slots
-    static constexpr int KQ = D + 8;       // bf16 per key/query row
-    static constexpr int PS = kPath + 1;   // per-node path tables
-    static constexpr int MS = NN + 8;      // bf16 per output-operator row
+    static constexpr int KQ = D + 8;      // bf16 per key/query row
+    static constexpr int PS = kPath + 1;  // per-node path tables
 };
 
-template <int D, int NB>
-struct BTab {
-    uint16_t *kq;         // [2][NN][KQ] keys, queries
-    uint16_t *vst;        // [NN][D] values of the current head
-    float4 *gab;          // [grp][NN] gamma, alpha, b
-    float *ysp;           // [grp][NN][16] output weights by path position
-    float *gk, *gq;       // [NN][PS]       (these three and the next share one region:
-    float *coefL;         // [grp][NN][PS]   the Gram entries and coefficients die before
-    uint16_t *mth, *mtl;  // [NN][MS]        the output operator is built)
-    int *anc;             // [NN][PS] root-to-node path, -1 past the depth
-    float *a, *b;         // [grp][NN]
-    int *depth;           // [NN]
+struct BLayout {
+    size_t kq, gab, ysp, anc, depth, gk, gq, coefL, a, b, mth, mtl, total;
+    int ms;  // bf16 per output-operator row
 };
 
-template <int D, int NB>
-__host__ __device__ inline size_t btab_bytes(int grp) {
-    using Q = BPad<D, NB>;
-    const size_t u1 = (size_t)2 * Q::NN * Q::PS * 4 + (size_t)grp * Q::NN * Q::PS * 4;
-    const size_t u2 = (size_t)2 * Q::NN * Q::MS * 2;
-    return (size_t)2 * Q::NN * Q::KQ * 2 + (size_t)Q::NN * D * 2 + (size_t)grp * Q::NN * 16 +
-           (size_t)grp * Q::NN * kPath * 4 + (u1 > u2 ? u1 : u2) + (size_t)Q::NN * Q::PS * 4 +
-           2 * (size_t)grp * Q::NN * 4 + (size_t)Q::NN * 4;
-}
-
-template <int D, int NB>
-__device__ inline BTab<D, NB> btab_carve(char *base, int grp) {
-    using Q = BPad<D, NB>;
-    BTab<D, NB> L;
-    L.kq = reinterpret_cast<uint16_t *>(base);   base += (size_t)2 * Q::NN * Q::KQ * 2;
-    L.vst = reinterpret_cast<uint16_t *>(base);  base += (size_t)Q::NN * D * 2;
-    L.gab = reinterpret_cast<float4 *>(base);    base += (size_t)grp * Q::NN * 16;
-    L.ysp = reinterpret_cast<float *>(base);     base += (size_t)grp * Q::NN * kPath * 4;
-    char *u = base;
-    const size_t u1 = (size_t)2 * Q::NN * Q::PS * 4 + (size_t)grp * Q::NN * Q::PS * 4;
-    const size_t u2 = (size_t)2 * Q::NN * Q::MS * 2;
-    base += u1 > u2 ? u1 : u2;
-    L.gk = reinterpret_cast<float *>(u);
-    L.gq = L.gk + Q::NN * Q::PS;
-    L.coefL = L.gq + Q::NN * Q::PS;
-    L.mth = reinterpret_cast<uint16_t *>(u);
-    L.mtl = L.mth + Q::NN * Q::MS;
-    L.anc = reinterpret_cast<int *>(base);       base += (size_t)Q::NN * Q::PS * 4;
-    L.a = reinterpret_cast<float *>(base);       base += (size_t)grp * Q::NN * 4;
-    L.b = reinterpret_cast<float *>(base);       base += (size_t)grp * Q::NN * 4;
-    L.depth = reinterpret_cast<int *>(base);
+template <int D>
+__host__ __device__ inline BLayout blocks_layout(int cap, int grp) {
+    using Q = BPad<D>;
+    const size_t c = (size_t)cap;
+    BLayout L;
+    L.ms = (cap + 15) / 16 * 16 + 8;
+    size_t off = 0;
+    L.kq = off;    off += 2 * c * Q::KQ * 2;
+    L.gab = off;   off += (size_t)grp * c * 16;
+    L.ysp = off;   off += (size_t)grp * c * kPath * 4;
+    L.anc = off;   off += c * Q::PS * 4;
+    L.depth = off; off += c * 4;
+    off = (off + 15) & ~size_t(15);
+    // the coefficient phase's tables and the output operator share one region
+    L.gk = off;
+    L.gq = L.gk + c * Q::PS * 4;
+    L.coefL = L.gq + c * Q::PS * 4;
+    L.a = L.coefL + (size_t)grp * c * Q::PS * 4;
+    L.b = L.a + (size_t)grp * c * 4;
+    const size_t u1 = L.b + (size_t)grp * c * 4 - off;
+    L.mth = off;
+    L.mtl = L.mth + c * L.ms * 2;
+    const size_t u2 = 2 * c * L.ms * 2;
+    off += u1 > u2 ? u1 : u2;
+    L.total = off;
     return L;
 }
 
 template <int D, int NB, int GRP>
-__global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(1))) void verify_blocks_kernel(
+__global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2))) void verify_blocks_kernel(
     Params P) {
     extern __shared__ __attribute__((aligned(16))) char lds_raw[];
-    using Q = BPad<D, NB>;
-    constexpr int KS = VG<D>::KS, NT = VG<D>::THREADS, WAVES = VG<D>::WAVES, NN = Q::NN;
+    using Q = BPad<D>;
+    constexpr int KS = VG<D>::KS, NT = VG<D>::THREADS, WAVES = VG<D>::WAVES, NN = NB * kTile;
     constexpr int grp = GRP;
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, hf = lane / 32, l32 = lane % 32;
     const int row = w * 32 + l32;
@@ -930,28 +932,35 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         return;
     }
     if (n == 0) return;
-    const int nb = (n + kTile - 1) / kTile;  // node blocks in use (n <= NN)
-    const BTab<D, NB> L = btab_carve<D, NB>(lds_raw, grp);
+    // n <= max_nodes <= NN: the plan rejects longer sequences, and its max_nodes is ours
+    const int cap = P.max_nodes;
+    const int nb = (n + kTile - 1) / kTile;  // node blocks in use
+    const BLayout SL = blocks_layout<D>(cap, grp);
+    uint16_t *const Lkq = reinterpret_cast<uint16_t *>(lds_raw + SL.kq);
+    float4 *const Lgab = reinterpret_cast<float4 *>(lds_raw + SL.gab);
+    float *const Lysp = reinterpret_cast<float *>(lds_raw + SL.ysp);
+    int *const Lanc = reinterpret_cast<int *>(lds_raw + SL.anc);
+    int *const Ldepth = reinterpret_cast<int *>(lds_raw + SL.depth);
+    float *const Lgk = reinterpret_cast<float *>(lds_raw + SL.gk);
+    float *const Lgq = reinterpret_cast<float *>(lds_raw + SL.gq);
+    float *const LcoefL = reinterpret_cast<float *>(lds_raw + SL.coefL);
+    float *const La = reinterpret_cast<float *>(lds_raw + SL.a);
+    float *const Lb = reinterpret_cast<float *>(lds_raw + SL.b);
+    uint16_t *const Lmth = reinterpret_cast<uint16_t *>(lds_raw + SL.mth);
+    uint16_t *const Lmtl = reinterpret_cast<uint16_t *>(lds_raw + SL.mtl);
+    const int MS = SL.ms;
     const uint16_t *kb = static_cast<const uint16_t *>(P.k) + ((size_t)lo * P.Hk + g) * D;
     const uint16_t *qb = static_cast<const uint16_t *>(P.q) + ((size_t)lo * P.Hk + g) * D;
-    const uint16_t *vg = static_cast<const uint16_t *>(P.v) + ((size_t)lo * P.Hv + h0) * D;
     const size_t kq_stride = (size_t)P.Hk * D;
     const float *s0 = P.state_in + ((size_t)sv.slot * P.Hv + h0) * D * D;
-    // out[node][h0 + hh][row]: uniform base per (node, head) + this lane's offset
+    // out[node][h0 + hh][row] and v[node][h0 + hh][row]: a uniform base per (node, head)
+    // plus this lane's offset
     const unsigned out_lane = (unsigned)(4 * hf * P.Hv * D + row);
     const unsigned s_lane = (unsigned)(row * D + 8 * hf);
-    constexpr int V_PER = (NN * (D / 8) + NT - 1) / NT;  // 16-byte chunks of one head's values
-    auto fetch_v = [&](int hh, uint4 (&vr)[V_PER]) {
-#pragma unroll
-        for (int u = 0; u < V_PER; ++u) {
-            const int c = tid + u * NT;
-            vr[u] = c < n * (D / 8) ? *reinterpret_cast<const uint4 *>(vg + (size_t)(c / (D / 8)) * P.Hv * D + hh * D +
-                                                                        8 * (c % (D / 8)))
-                                    : make_uint4(0, 0, 0, 0);
-        }
-    };
+    const uint16_t *vb = static_cast<const uint16_t *>(P.v) + ((size_t)lo * P.Hv + h0) * D;
+    const int hvd = P.Hv * D;  // elements between consecutive nodes' rows of out and v
 
-    // ---- one round trip: keys/queries of all blocks, gates, paths
+    // ---- one round trip: keys/queries of the tree's nodes, gates, paths
     constexpr int KQ_PER = 2 * NN * (D / 8) / NT;
     static_assert(2 * NN * (D / 8) % NT == 0, "whole key/query rounds");
     uint4 kqv[KQ_PER];
@@ -977,250 +986,291 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         }
     }
     static_assert(NN <= NT, "one thread per node");
-    int an[kPath], d = 0;
+    int4 an4[kPath / 4];
+    int d = 0;
     if (tid < n) {
         d = P.ws.depth[lo + tid];
+        const int4 *np = reinterpret_cast<const int4 *>(P.ws.nodepath + (size_t)(lo + tid) * GDN_MAX_DEPTH);
 #pragma unroll
-        for (int e = 0; e < kPath; ++e) an[e] = P.ws.nodepath[(size_t)(lo + tid) * GDN_MAX_DEPTH + e];
+        for (int e = 0; e < kPath / 4; ++e) an4[e] = np[e];
     }
     if (tid < n) {
 #pragma unroll
-        for (int e = 0; e < kPath; ++e) L.anc[tid * Q::PS + e] = an[e];
-        L.depth[tid] = d;
+        for (int e = 0; e < kPath / 4; ++e) {
+            Lanc[tid * Q::PS + 4 * e + 0] = an4[e].x;
+            Lanc[tid * Q::PS + 4 * e + 1] = an4[e].y;
+            Lanc[tid * Q::PS + 4 * e + 2] = an4[e].z;
+            Lanc[tid * Q::PS + 4 * e + 3] = an4[e].w;
+        }
+        Ldepth[tid] = d;
     }
 #pragma unroll
     for (int u = 0; u < GA_PER; ++u) {
         const int t = tid + u * NT;
         if (t < grp * n) {
-            L.a[(t / n) * NN + t % n] = ga[u];
-            L.b[(t / n) * NN + t % n] = gb[u];
+            La[(t / n) * cap + t % n] = ga[u];
+            Lb[(t / n) * cap + t % n] = gb[u];
         }
     }
 #pragma unroll
     for (int u = 0; u < KQ_PER; ++u) {
         const int idx = tid + u * NT;
-        *reinterpret_cast<uint4 *>(L.kq + (idx / (D / 8)) * Q::KQ + 8 * (idx % (D / 8))) = kqv[u];
+        const int which = idx / (NN * (D / 8)), rem = idx % (NN * (D / 8));
+        const int i = rem / (D / 8), c8 = rem % (D / 8);
+        if (i < n) *reinterpret_cast<uint4 *>(Lkq + (which * cap + i) * Q::KQ + 8 * c8) = kqv[u];
     }
-    // the first head's state and values go out once the tables have landed; the second
-    // head's after the coefficients (registers are scarce while those are formed)
-    float sA[KS][8], sB[KS][8];
-    uint4 vA[V_PER], vB[V_PER];
-    load_state_frags<D>(s0, s_lane, sA);
-    fetch_v(0, vA);
+    float st[KS][8];
+    // values of head hh in the R layout: block jb, accumulator slot r holds node
+    // jb*32 + 8(r/4) + 4*half + r%4 at this lane's row; two bf16 per register.  Read
+    // through a buffer resource over the sequence's nodes: past the last node the
+    // hardware returns zero, so no load is clamped or guarded and all are in flight at once.
+    uint32_t vv[NB][8];
+    auto load_v = [&](int hh, int nn, unsigned lane_v) {
+        const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vb + (size_t)hh * D, (unsigned)(nn * hvd) * 2u);
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb)
+#pragma unroll
+            for (int r2 = 0; r2 < 8; ++r2) {
+                uint32_t x[2];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int ir = jb * kTile + 8 * (r2 / 2) + 2 * (r2 % 2) + q;  // node of half-wave 0
+                    x[q] = __builtin_amdgcn_raw_buffer_load_b16(rv, (unsigned)(ir * hvd) * 2u + lane_v, 0, 0);
+                }
+                vv[jb][r2] = x[0] | (x[1] << 16);
+            }
+    };
     __syncthreads();
 
-    // ---- Gram entries of every block pair: node j's ancestor i at path position
-    // depth(i) - 1 gets k_i . k_j and k_i . q_j
-    for (int pr = w; pr < nb * nb; pr += WAVES) {
-        const int ti = pr / nb, tj = pr % nb;
-        f32x16 gkk = {}, gkq = {};
+    // key / query fragments of node block jb, k-step s.  A row past the last node reads
+    // the last node's row: what it produces lands only in accumulator rows of nodes that
+    // do not exist, which are masked (R) or never stored (outputs, Gram entries).
+    auto kfrag = [&](int jb, int s) { return frag_of(Lkq + min(jb * kTile + l32, n - 1) * Q::KQ, s, hf); };
+    auto qfrag = [&](int jb, int s) {
+        return frag_of(Lkq + (cap + min(jb * kTile + l32, n - 1)) * Q::KQ, s, hf);
+    };
+
+    // ---- Gram entries: wave w takes the nodes of block w (column block tj = w) against
+    // every block ti; node j's ancestor i, at path position depth(i) - 1, gets k_i . k_j
+    // and k_i . q_j.  The ancestors of j are a bit mask over node ids, so a candidate
+    // needs no path lookup, and the nb products of a wave are independent MFMA chains.
+    for (int tj = w; tj < nb; tj += WAVES) {
+        const int j = tj * kTile + l32;
+        uint32_t amask[NB];  // ancestors of node j (itself included), by block
+#pragma unroll
+        for (int t = 0; t < NB; ++t) amask[t] = 0u;
+        if (j < n) {
+            const int dj = Ldepth[j];
+#pragma unroll
+            for (int e = 0; e < kPath; ++e) {
+                const int an = Lanc[j * Q::PS + e];
+#pragma unroll
+                for (int t = 0; t < NB; ++t)
+                    if (e < dj && (an >> 5) == t) amask[t] |= 1u << (an & 31);
+            }
+        }
+        f32x16 gkk[NB], gkq[NB];
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+            gkk[t] = f32x16{};
+            gkq[t] = f32x16{};
+        }
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            const bf16x8 A = frag_of(L.kq + (ti * kTile + l32) * Q::KQ, s, hf);
-            const bf16x8 Bk = frag_of(L.kq + (tj * kTile + l32) * Q::KQ, s, hf);
-            const bf16x8 Bq = frag_of(L.kq + (NN + tj * kTile + l32) * Q::KQ, s, hf);
-            gkk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bk, gkk, 0, 0, 0);
-            gkq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bq, gkq, 0, 0, 0);
-        }
-        const int j = tj * kTile + l32;
-        if (j < n) {
-            const int dj = L.depth[j];
-            int er[16], ar[16];  // candidate i's path position in j's path, and who sits there
+            const bf16x8 Bk = kfrag(tj, s);
+            const bf16x8 Bq = qfrag(tj, s);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = ti * kTile + 8 * (r / 4) + 4 * hf + (r % 4);
-                er[r] = i < n ? L.depth[i] - 1 : kPath;
+            for (int ti = 0; ti < NB; ++ti) {
+                const bf16x8 A = kfrag(ti, s);
+                gkk[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bk, gkk[ti], 0, 0, 0);
+                gkq[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bq, gkq[ti], 0, 0, 0);
             }
+        }
+        if (j < n) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) ar[r] = L.anc[j * Q::PS + min(er[r], kPath - 1)];
+            for (int ti = 0; ti < NB; ++ti) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = ti * kTile + 8 * (r / 4) + 4 * hf + (r % 4);
-                if (er[r] < dj && ar[r] == i) {
-                    L.gk[j * Q::PS + er[r]] = gkk[r];
-                    L.gq[j * Q::PS + er[r]] = gkq[r];
+                for (int r = 0; r < 16; ++r) {
+                    const int il = 8 * (r / 4) + 4 * hf + (r % 4);  // candidate ti * 32 + il
+                    if (ti < nb && ((amask[ti] >> il) & 1u)) {
+                        const int e = Ldepth[ti * kTile + il] - 1;
+                        Lgk[j * Q::PS + e] = gkk[ti][r];
+                        Lgq[j * Q::PS + e] = gkq[ti][r];
+                    }
                 }
             }
         }
     }
     __syncthreads();
+    // the first head's state streams in under the coefficients and back substitution
+    // (issued earlier, it would have to share the registers of the Gram products)
+    load_state_frags<D>(s0, s_lane, st);
 
     // ---- per (head, node): ratios, coefficients, the output weights' right-hand sides
+#pragma unroll 1
     for (int t = tid; t < grp * n; t += NT) {
         const int hh = t / n, i = t % n;
-        const int di = L.depth[i];
-        const float bi = L.b[hh * NN + i];
+        const int di = Ldepth[i];
+        const float bi = Lb[hh * cap + i];
         float r = 1.0f;
 #pragma unroll
         for (int e = kPath - 1; e >= 0; --e) {
             const bool on = e < di - 1;
-            L.coefL[(hh * NN + i) * Q::PS + e] = on ? bi * r * L.gk[i * Q::PS + e] : 0.0f;
-            L.ysp[(hh * NN + i) * kPath + e] =
-                on ? r * L.gq[i * Q::PS + e] : (e == di - 1 ? L.gq[i * Q::PS + e] : 0.0f);
-            if (e < di) r *= L.a[hh * NN + max(L.anc[i * Q::PS + e], 0)];
+            LcoefL[(hh * cap + i) * Q::PS + e] = on ? bi * r * Lgk[i * Q::PS + e] : 0.0f;
+            Lysp[(hh * cap + i) * kPath + e] = on ? r * Lgq[i * Q::PS + e] : (e == di - 1 ? Lgq[i * Q::PS + e] : 0.0f);
+            if (e < di) r *= La[hh * cap + max(Lanc[i * Q::PS + e], 0)];
         }
-        L.gab[hh * NN + i] = make_float4(r, bi * r, bi, 0.0f);
+        Lgab[hh * cap + i] = make_float4(r, bi * r, bi, 0.0f);
     }
     __syncthreads();
     // back substitution, deepest weight first, in place
+#pragma unroll 1
     for (int t = tid; t < grp * n; t += NT) {
         const int hh = t / n, i = t % n;
-        const int di = L.depth[i];
+        const int di = Ldepth[i];
         int an_t[kPath];
 #pragma unroll
-        for (int e = 0; e < kPath; ++e) an_t[e] = max(L.anc[i * Q::PS + e], 0);
-        float *yr = L.ysp + (hh * NN + i) * kPath;
+        for (int e = 0; e < kPath; ++e) an_t[e] = max(Lanc[i * Q::PS + e], 0);
+        float *yr = Lysp + (hh * cap + i) * kPath;
         float y[kPath];
 #pragma unroll
         for (int e = kPath - 1; e >= 0; --e) {
             float acc = yr[e];
 #pragma unroll
-            for (int f = kPath - 1; f > e; --f) acc = fmaf(-y[f], L.coefL[(hh * NN + an_t[f]) * Q::PS + e], acc);
+            for (int f = kPath - 1; f > e; --f) acc = fmaf(-y[f], LcoefL[(hh * cap + an_t[f]) * Q::PS + e], acc);
             y[e] = e < di ? acc : 0.0f;
         }
 #pragma unroll
         for (int e = 0; e < kPath; ++e) yr[e] = y[e];
     }
+    __syncthreads();  // the coefficient tables are dead: their region becomes the output operator
+    // every head's operator has its nonzeros at the same places (the ancestors), so clearing
+    // once leaves each head's scatter a complete operator
+    for (int c = tid; c < cap * MS / 8; c += NT) {
+        reinterpret_cast<uint4 *>(Lmth)[c] = make_uint4(0u, 0u, 0u, 0u);
+        reinterpret_cast<uint4 *>(Lmtl)[c] = make_uint4(0u, 0u, 0u, 0u);
+    }
 
-    // ---- value heads
-    auto head = [&](const float (&st)[KS][8], int hh, const uint4 (&vr)[V_PER]) {
-        __syncthreads();  // the previous head is done with the operator and the values
-        // this head's values, and its dense output operator (bf16 hi + lo)
+    // ---- value heads (unrolled: a loop would carry its values across heads and spill)
 #pragma unroll
-        for (int u = 0; u < V_PER; ++u) {
-            const int c = tid + u * NT;
-            if (c < NN * (D / 8)) reinterpret_cast<uint4 *>(L.vst)[c] = vr[u];
-        }
-        if (hh == 0) {
-            // every head's operator has its nonzeros at the same places (the ancestors), so
-            // clearing once, before the first head, leaves each later head's scatter a
-            // complete operator
-            static_assert(Q::MS % 8 == 0, "16-byte operator rows");
-            for (int c = tid; c < nb * kTile * Q::MS / 8; c += NT) {
-                reinterpret_cast<uint4 *>(L.mth)[c] = make_uint4(0u, 0u, 0u, 0u);
-                reinterpret_cast<uint4 *>(L.mtl)[c] = make_uint4(0u, 0u, 0u, 0u);
-            }
-        }
-        __syncthreads();
-        for (int t = tid; t < n * kPath; t += NT) {
+    for (int hh = 0; hh < grp; ++hh) {
+        // the loop's own copies of the node count and the lane's output offset: what is
+        // derived from them is recomputed per head instead of being hoisted out of the
+        // loop and held (dozens of per-node indices and addresses) across it
+        int n_h = n;
+        unsigned lane_b = out_lane * 4u;  // byte offset of this lane's element in a (node, head) row
+        int hf4 = 4 * hf, l32_h = l32;    // the lane's node offset within an accumulator slot, its row
+        asm volatile("" : "+s"(n_h));
+        asm volatile("" : "+v"(lane_b));
+        asm volatile("" : "+v"(hf4));
+        asm volatile("" : "+v"(l32_h));
+        __syncthreads();  // the operator is cleared, or the previous head's products are done with it
+        for (int t = tid; t < n_h * kPath; t += NT) {
             const int i = t / kPath, e = t % kPath;
-            if (e < L.depth[i]) {
-                const int col = L.anc[i * Q::PS + e];
-                const float y = L.ysp[(hh * NN + i) * kPath + e];
+            if (e < Ldepth[i]) {
+                const int col = Lanc[i * Q::PS + e];
+                const float y = Lysp[(hh * cap + i) * kPath + e];
                 const __bf16 yh = static_cast<__bf16>(y);
-                L.mth[i * Q::MS + col] = __builtin_bit_cast(uint16_t, yh);
-                L.mtl[i * Q::MS + col] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(y - static_cast<float>(yh)));
+                Lmth[i * MS + col] = __builtin_bit_cast(uint16_t, yh);
+                Lmtl[i * MS + col] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(y - static_cast<float>(yh)));
             }
         }
         __syncthreads();
-        // X_j = K_j S0^T and Y_t = Q_t S0^T for every block in one pass over the state:
-        // the state is split once per k-step and the 2 NB accumulations are independent
-        // MFMA chains
-        f32x16 X[NB], Y[NB];
+        // this head's state (the first head's is already in flight) and values
+        if (hh > 0) load_state_frags<D>(s0 + (size_t)hh * D * D, s_lane, st);
+        load_v(hh, n_h, lane_b >> 1);
+        // Y_t = Q_t S0^T and X_j = K_j S0^T for every block, one product at a time (NB
+        // independent MFMA chains each), the state split into bf16 hi + lo one k-step at a
+        // time (only the fp32 state is held); blocks past the last node multiply zeros
+        auto state_products = [&](bool queries, f32x16 (&acc)[NB]) {
 #pragma unroll
-        for (int jb = 0; jb < NB; ++jb) {
-            X[jb] = f32x16{};
-            Y[jb] = f32x16{};
-        }
+            for (int jb = 0; jb < NB; ++jb) acc[jb] = f32x16{};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            bf16x8 shi, slo;
+            for (int s = 0; s < KS; ++s) {
+                bf16x8 shi, slo;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const __bf16 hb = static_cast<__bf16>(st[s][e]);
-                shi[e] = hb;
-                slo[e] = static_cast<__bf16>(st[s][e] - static_cast<float>(hb));
-            }
+                for (int e = 0; e < 8; ++e) {
+                    const __bf16 hb = static_cast<__bf16>(st[s][e]);
+                    shi[e] = hb;
+                    slo[e] = static_cast<__bf16>(st[s][e] - static_cast<float>(hb));
+                }
 #pragma unroll
-            for (int jb = 0; jb < NB; ++jb) {
-                if (jb < nb) {
-                    const bf16x8 Ak = frag_of(L.kq + (jb * kTile + l32) * Q::KQ, s, hf);
-                    const bf16x8 Aq = frag_of(L.kq + (NN + jb * kTile + l32) * Q::KQ, s, hf);
-                    X[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, shi, X[jb], 0, 0, 0);
-                    Y[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, shi, Y[jb], 0, 0, 0);
-                    X[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, slo, X[jb], 0, 0, 0);
-                    Y[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, slo, Y[jb], 0, 0, 0);
+                for (int jb = 0; jb < NB; ++jb) {
+                    const bf16x8 A = queries ? qfrag(jb, s) : kfrag(jb, s);
+                    acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, shi, acc[jb], 0, 0, 0);
+                    acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, slo, acc[jb], 0, 0, 0);
                 }
             }
-        }
-        // R_j = b v - alpha X_j, kept as bf16 hi + lo in the k-order of the output products
-        // (k-step u of block j: accumulator slots 8u .. 8u+7)
-        const float4 *gab = L.gab + hh * NN;
+        };
+        f32x16 Y[NB], X[NB];
+        state_products(true, Y);
+        state_products(false, X);
+        // per accumulator slot (node i of block jb): gamma Y and R_j = b v - alpha X_j, the
+        // latter as bf16 hi + lo in the k-order of the output products (k-step u of block j:
+        // slots 8u .. 8u+7)
+        const float4 *gab = Lgab + hh * cap;
         bf16x8 rhi[NB][2], rlo[NB][2];
 #pragma unroll
         for (int jb = 0; jb < NB; ++jb) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int i = jb * kTile + 8 * (r / 4) + 4 * hf + (r % 4);
-                const float4 q4 = gab[min(i, n - 1)];
-                const float vi = bf2f(L.vst[min(i, NN - 1) * D + row]);
-                const float rv = i < n ? fmaf(-q4.y, X[jb][r], q4.z * vi) : 0.0f;
+                const int i = jb * kTile + 8 * (r / 4) + hf4 + (r % 4);
+                const float4 q4 = gab[min(i, n_h - 1)];
+                const float vi = __uint_as_float((vv[jb][r / 2] >> (16 * (r % 2))) << 16);
+                // past the last node: zero (its X comes from a repeated key row)
+                const float rv = __uint_as_float(__float_as_uint(fmaf(-q4.y, X[jb][r], q4.z * vi)) &
+                                                 (i < n_h ? 0xffffffffu : 0u));
                 const __bf16 rb = static_cast<__bf16>(rv);
                 rhi[jb][r / 8][r % 8] = rb;
                 rlo[jb][r / 8][r % 8] = static_cast<__bf16>(rv - static_cast<float>(rb));
-                // gamma Y_t, the start of block t's outputs
-                Y[jb][r] = i < n ? q4.x * Y[jb][r] : 0.0f;
+                Y[jb][r] = q4.x * Y[jb][r];
             }
         }
-        // O_t = gamma Y_t + sum_j MT_tj R_j: for each operand block j, the NB output
-        // blocks' accumulations are independent chains
+        // per output block t: O_t = gamma Y_t + sum_j MT_tj R_j over the k-steps that hold
+        // nodes, then its stores
+        // outputs through a buffer resource over the sequence's rows of this head: stores
+        // past the last node are dropped by the hardware, so none is guarded
+        const __amdgpu_buffer_rsrc_t ro =
+            buffer_rsrc(P.out + ((size_t)lo * P.Hv + h0 + hh) * D, (unsigned)(n_h * hvd) * 4u);
 #pragma unroll
-        for (int jb = 0; jb < NB; ++jb) {
-            if (jb < nb) {
+        for (int t = 0; t < NB; ++t) {
+            if (t < nb) {
+                f32x16 Yt = Y[t];
+                // rows past the last node repeat the last operator row; they are not stored
+                const int it = min(t * kTile + l32_h, n_h - 1);
+                const uint16_t *mh = Lmth + it * MS + hf4;
+                const uint16_t *ml = Lmtl + it * MS + hf4;
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
+                for (int jb = 0; jb < NB; ++jb) {
 #pragma unroll
-                    for (int t = 0; t < NB; ++t) {
-                        if (t < nb) {
-                            const uint16_t *mh = L.mth + (t * kTile + l32) * Q::MS;
-                            const uint16_t *ml = L.mtl + (t * kTile + l32) * Q::MS;
-                            const int c0 = jb * kTile + 16 * u + 4 * hf;
+                    for (int u = 0; u < 2; ++u) {
+                        if (jb * kTile + 16 * u < n_h) {  // operand nodes past the last: zero weights
+                            const int c0 = jb * kTile + 16 * u;
                             const uint2 x0 = *reinterpret_cast<const uint2 *>(mh + c0);
                             const uint2 x1 = *reinterpret_cast<const uint2 *>(mh + c0 + 8);
                             const uint2 y0 = *reinterpret_cast<const uint2 *>(ml + c0);
                             const uint2 y1 = *reinterpret_cast<const uint2 *>(ml + c0 + 8);
                             const bf16x8 ahi = __builtin_bit_cast(bf16x8, make_uint4(x0.x, x0.y, x1.x, x1.y));
                             const bf16x8 alo = __builtin_bit_cast(bf16x8, make_uint4(y0.x, y0.y, y1.x, y1.y));
-                            Y[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, rhi[jb][u], Y[t], 0, 0, 0);
-                            Y[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, rlo[jb][u], Y[t], 0, 0, 0);
-                            Y[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, rhi[jb][u], Y[t], 0, 0, 0);
+                            Yt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, rhi[jb][u], Yt, 0, 0, 0);
+                            Yt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, rlo[jb][u], Yt, 0, 0, 0);
+                            Yt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, rhi[jb][u], Yt, 0, 0, 0);
                         }
                     }
                 }
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < NB; ++t) {
-            if (t < nb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    // node of half-wave 0 (uniform; half-wave 1 adds 4): a uniform base
-                    // per (node, head) plus the lane's fixed offset
+                    // node of half-wave 0 (uniform; half-wave 1 adds 4)
                     const int ir = t * kTile + 8 * (r / 4) + (r % 4);
-                    if (ir + 4 * hf < n) {
-                        float *ob = P.out + ((size_t)(lo + ir) * P.Hv + h0 + hh) * D;
-                        ob[out_lane] = Y[t][r];
-                    }
+                    // (the builtin takes the 32 bits as an integer: pass the bits, not the value)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Yt[r]), ro, (unsigned)(ir * hvd) * 4u + lane_b,
+                                                          0, 0);
                 }
             }
+            // one output block's operator fragments live at a time
+            __builtin_amdgcn_sched_barrier(0);
         }
-    };
-    if (grp > 1) {
-        load_state_frags<D>(s0 + (size_t)D * D, s_lane, sB);
-        fetch_v(1, vB);
     }
-    head(sA, 0, vA);
-    if (grp > 2) {
-        load_state_frags<D>(s0 + (size_t)2 * D * D, s_lane, sA);
-        fetch_v(2, vA);
-    }
-    if (grp > 1) head(sB, 1, vB);
-    if (grp > 3) {
-        load_state_frags<D>(s0 + (size_t)3 * D * D, s_lane, sB);
-        fetch_v(3, vB);
-    }
-    if (grp > 2) head(sA, 2, vA);
-    if (grp > 3) head(sB, 3, vB);
 }
 
 // ===========================================================================
@@ -1547,15 +1597,21 @@ hipError_t launch_with_lds(K kernel, dim3 grid, dim3 block, size_t lds, hipStrea
 }
 
 // Workgroups of Kernel (threads, dynamic LDS) resident at once on the current device:
-// compute units x workgroups per unit, queried once per (kernel, device).  0 when unknown.
+// compute units x workgroups per unit, queried once per (kernel, device, LDS size in
+// KiB).  0 when unknown.
 constexpr int kMaxDevices = 64;
+constexpr int kLdsBuckets = 161;  // 0 .. 160 KiB
 template <void (*Kernel)(Params)>
 int resident_workgroups(int threads, size_t lds) {
     const auto kernel = Kernel;
-    static std::atomic<int> cache[kMaxDevices];  // one per kernel; threads that race store the same value
+    // one table per kernel; threads that race store the same value
+    static std::atomic<int> cache[kMaxDevices][kLdsBuckets];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-    int known = cache[dev].load(std::memory_order_relaxed);
+    const size_t kib = (lds + 1023) / 1024;
+    if (kib >= (size_t)kLdsBuckets) return 0;
+    std::atomic<int> &slot = cache[dev][kib];
+    int known = slot.load(std::memory_order_relaxed);
     if (known == 0) {
         int cus = 0, per_cu = 0;
         if (lds > 65536 && hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
@@ -1566,7 +1622,7 @@ int resident_workgroups(int threads, size_t lds) {
                                                          lds) != hipSuccess)
             return 0;
         known = cus * per_cu;
-        cache[dev].store(known, std::memory_order_relaxed);
+        slot.store(known, std::memory_order_relaxed);
     }
     return known;
 }
@@ -1611,16 +1667,19 @@ hipError_t launch_verify_d(const Params &p, bool chain, hipStream_t s) {
     }
     const bool two = p.max_nodes <= 2 * kTile;
     const int gb = !chain && p.max_nodes <= 3 * kTile
-                       ? (two ? heads_per_workgroup<verify_blocks_kernel<D, 2, 1>>(p, VG<D>::THREADS, btab_bytes<D, 2>(1))
-                              : heads_per_workgroup<verify_blocks_kernel<D, 3, 1>>(p, VG<D>::THREADS, btab_bytes<D, 3>(1)))
+                       ? (two ? heads_per_workgroup<verify_blocks_kernel<D, 2, 1>>(p, VG<D>::THREADS,
+                                                                                  blocks_layout<D>(p.max_nodes, 1).total)
+                              : heads_per_workgroup<verify_blocks_kernel<D, 3, 1>>(p, VG<D>::THREADS,
+                                                                                  blocks_layout<D>(p.max_nodes, 1).total))
                        : grp;
     if (!chain && p.max_nodes <= 3 * kTile && gb <= kGroupMaxHeads) {
         const dim3 grid(p.B * (p.Hv / gb)), block(VG<D>::THREADS);
+        const size_t lds = blocks_layout<D>(p.max_nodes, gb).total;
         switch (gb) {
-#define GDN_BLOCKS_CASE(G)                                                                                          \
-    case G:                                                                                                         \
-        return two ? launch_with_lds(verify_blocks_kernel<D, 2, G>, grid, block, btab_bytes<D, 2>(G), s, p) \
-                   : launch_with_lds(verify_blocks_kernel<D, 3, G>, grid, block, btab_bytes<D, 3>(G), s, p);
+#define GDN_BLOCKS_CASE(G)                                                          \
+    case G:                                                                         \
+        return two ? launch_with_lds(verify_blocks_kernel<D, 2, G>, grid, block, lds, s, p) \
+                   : launch_with_lds(verify_blocks_kernel<D, 3, G>, grid, block, lds, s, p);
             GDN_BLOCKS_CASE(1)
             GDN_BLOCKS_CASE(2)
             GDN_BLOCKS_CASE(3)
