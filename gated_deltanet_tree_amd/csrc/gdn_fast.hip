@@ -793,7 +793,8 @@ verify_group_kernel(Params P) {
             ay[r] = i < n ? q4.x * ay[r] : 0.0f;                   // gamma y
         }
         // O = gamma y + MT R on bf16 MFMA with both operands split hi + lo (the lo x lo
-        // term, ~2^-32 relative, is dropped).  k-step u takes R from accumulator slots
+        // term is dropped: each lo is at most 2^-8 of its value, so the term is up to
+        // ~2^-16 of the product, the order of the state's own split).  k-step u takes R from accumulator slots
         // 8u .. 8u+7, i.e. nodes 16u + 8(e/4) + 4*half + e%4, and MT's columns in that order.
         const uint16_t *mh = L.mth + (hh * kTile + l32) * Q::MT, *ml = L.mtl + (hh * kTile + l32) * Q::MT;
 #pragma unroll
@@ -867,9 +868,10 @@ verify_group_kernel(Params P) {
 //  - the dense output operator has max_nodes rows and as many columns, rounded
 //    up to the 16 of one k-step, and shares its LDS with the Gram entries,
 //    coefficients and gates, which are dead once the path weights are formed;
-//  - one state register set: the next head's state is issued as soon as this
-//    head's products with the state are taken, and streams in while this head's
-//    R = diag(b)V - diag(alpha)X and output products are formed;
+//  - one state register set: the first head's state streams in under the
+//    coefficients and back substitution, each later head's is issued with its
+//    values right after that head's operator entries are written (the other
+//    workgroup on the CU keeps the memory system busy meanwhile);
 //  - k-steps and node blocks past the last node are skipped.
 // ===========================================================================
 template <int D>
