@@ -110,9 +110,9 @@ int gdn_tree_verify(const gdn_dims *dims, const void *q, const void *k, const vo
     p.out = out;
     p.ws = gdn::ws_ptrs(const_cast<void *>(ws), p.B, p.T, p.Hv);
     p.has_ws = 1;
-    // the MFMA verify covers trees of up to 96 nodes; larger trees walk the
-    // tree recurrently
-    if (!recurrent_forced() && gdn::fast_tree_supported(p.D, dims->qkv_dtype, dims->max_nodes))
+    // the MFMA verify covers every tree size a call takes, unless the coefficient
+    // tables of a very wide key-head group would not fit the LDS
+    if (!recurrent_forced() && gdn::fast_tree_supported(p.D, dims->qkv_dtype, dims->max_nodes, p.Hv / p.Hk))
         return launched(gdn::launch_tree_verify_fast(p, as_stream(stream)));
     return launched(gdn::launch_tree_verify_recurrent(p, dims->qkv_dtype, as_stream(stream)));
 }
@@ -148,7 +148,7 @@ int gdn_tree_verify_static(const gdn_dims *dims, const int32_t *parent, const in
     p.b = b;
     p.state_in = state_cache;
     p.out = out;
-    if (!recurrent_forced() && gdn::fast_tree_supported(p.D, dims->qkv_dtype, dims->max_nodes))
+    if (!recurrent_forced() && gdn::fast_tree_supported(p.D, dims->qkv_dtype, dims->max_nodes, p.Hv / p.Hk))
         return launched(gdn::launch_tree_verify_fast(p, s));
     return launched(gdn::launch_tree_verify_recurrent(p, dims->qkv_dtype, s));
 }

@@ -31,7 +31,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTile = 32;             // nodes per MFMA block
 constexpr int kPath = GDN_MAX_DEPTH;  // max ancestors per node (incl. itself)
-constexpr int kFastMaxNodes = 96;     // largest tree the MFMA verify takes (3 node blocks)
+constexpr int kFastMaxNodes = GDN_MAX_NODES;  // largest tree the MFMA verify takes (8 node blocks)
+constexpr int kMaskWords = GDN_MAX_NODES / 32;  // 32-node ancestor mask words per node
+constexpr size_t kLdsBudget = 160 * 1024;       // LDS of one compute unit
 
 __device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
 __device__ __forceinline__ float qnan_f() { return __int_as_float(0x7fc00000); }
@@ -115,7 +117,7 @@ constexpr int kCoefMaxHeadsPerPass = 8;
 struct CTab {
     int *anc;        // [cap][16]
     int *depth;      // [cap]
-    uint32_t *amask; // [cap][4]
+    uint32_t *amask; // [cap][kMaskWords]
     float *gk, *gq;  // [cap][16] path-indexed Gram entries
     float *a, *b;    // [grp][cap]
     float *coefL;    // [hpp][cap][16]
@@ -123,7 +125,16 @@ struct CTab {
 
 __host__ __device__ inline size_t ctab_bytes(int cap, int grp, int hpp) {
     const size_t c = (size_t)cap;
-    return c * kPath * 4 + c * 4 + c * 16 + 2 * c * kPath * 4 + 2 * (size_t)grp * c * 4 + (size_t)hpp * c * kPath * 4;
+    return c * kPath * 4 + c * 4 + c * kMaskWords * 4 + 2 * c * kPath * 4 + 2 * (size_t)grp * c * 4 +
+           (size_t)hpp * c * kPath * 4;
+}
+
+// Most value heads one coefficient pass takes for trees of up to cap nodes: what
+// the LDS holds, at most kCoefMaxHeadsPerPass (0: not even one fits)
+__host__ __device__ inline int coef_heads_per_pass(int cap, int grp) {
+    int h = grp < kCoefMaxHeadsPerPass ? grp : kCoefMaxHeadsPerPass;
+    while (h > 0 && ctab_bytes(cap, grp, h) > kLdsBudget) --h;
+    return h;
 }
 
 __device__ inline CTab ctab_carve(char *base, int cap, int grp, int hpp) {
@@ -133,7 +144,7 @@ __device__ inline CTab ctab_carve(char *base, int cap, int grp, int hpp) {
     L.gk = reinterpret_cast<float *>(base);       base += c * kPath * 4;
     L.gq = reinterpret_cast<float *>(base);       base += c * kPath * 4;
     L.coefL = reinterpret_cast<float *>(base);    base += (size_t)hpp * c * kPath * 4;
-    L.amask = reinterpret_cast<uint32_t *>(base); base += c * 16;
+    L.amask = reinterpret_cast<uint32_t *>(base); base += c * kMaskWords * 4;
     L.depth = reinterpret_cast<int *>(base);      base += c * 4;
     L.a = reinterpret_cast<float *>(base);        base += (size_t)grp * c * 4;
     L.b = reinterpret_cast<float *>(base);
@@ -152,7 +163,7 @@ __global__ __launch_bounds__(kCoefThreads) void coef_kernel(Params P) {
     if (sv.status != GDN_SEQ_OK || sv.n == 0) return;
     const int lo = sv.lo, n = sv.n;
     const int cap = CHAIN ? kPath : P.max_nodes;
-    const int hpp = max(1, min(min(grp, kCoefMaxHeadsPerPass), kCoefThreads / n));  // value heads per pass
+    const int hpp = max(1, min(coef_heads_per_pass(cap, grp), kCoefThreads / n));  // value heads per pass
     const CTab L = ctab_carve(lds_raw, cap, grp, hpp);
 
     // tree tables and ancestor masks, gates of every head of the group
@@ -161,14 +172,18 @@ __global__ __launch_bounds__(kCoefThreads) void coef_kernel(Params P) {
 #pragma unroll
         for (int e = 0; e < kPath; ++e) an[e] = anc_of<CHAIN>(P, lo, i, e);
         const int d = CHAIN ? i + 1 : P.ws.depth[lo + i];
-        uint32_t m[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int e = 0; e < kPath; ++e) {
-            L.anc[i * kPath + e] = an[e];
-            if (e < d) m[an[e] >> 5] |= 1u << (an[e] & 31);
+        for (int e = 0; e < kPath; ++e) L.anc[i * kPath + e] = an[e];
+        // one mask word at a time, so the word index stays a constant
+#pragma unroll
+        for (int t = 0; t < kMaskWords; ++t) {
+            uint32_t m = 0u;
+#pragma unroll
+            for (int e = 0; e < kPath; ++e)
+                if (e < d && (an[e] >> 5) == t) m |= 1u << (an[e] & 31);
+            L.amask[i * kMaskWords + t] = m;
         }
         L.depth[i] = d;
-        *reinterpret_cast<uint4 *>(L.amask + i * 4) = make_uint4(m[0], m[1], m[2], m[3]);
     }
     for (int idx = tid; idx < grp * n; idx += kCoefThreads) {
         const int hh = idx / n, i = idx % n;
@@ -196,7 +211,7 @@ __global__ __launch_bounds__(kCoefThreads) void coef_kernel(Params P) {
             gkq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bq, gkq, 0, 0, 0);
         }
         if (pj < n) {  // accumulator r: (candidate ancestor ti*32 + il, node pj)
-            const uint32_t mask = L.amask[pj * 4 + ti];
+            const uint32_t mask = L.amask[pj * kMaskWords + ti];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int il = 8 * (r / 4) + 4 * hf + (r % 4);
@@ -269,13 +284,14 @@ struct VTab {
     float *mt;      // [32][32] dense MT (single-block trees)
     float *rbuf;    // [cap][D] r rows (multi-block trees)
     float *y;       // [cap][16] path weights
-    int *anc;       // [cap][16]
+    uint8_t *anc;   // [cap][16] (local node ids, < 256)
     float4 *gabd;   // [cap] gamma, alpha, b, depth
 };
 
 __host__ __device__ inline size_t vtab_bytes(int cap, int D, bool single) {
     const size_t c = (size_t)cap;
-    return (single ? (size_t)2 * kTile * D * 2 + (size_t)kTile * kTile * 4 : c * D * 4) + 2 * c * kPath * 4 + c * 16;
+    return (single ? (size_t)2 * kTile * D * 2 + (size_t)kTile * kTile * 4 : c * D * 4) + c * kPath * 4 + c * kPath +
+           c * 16;
 }
 
 __device__ inline VTab vtab_carve(char *base, int cap, int D, bool single) {
@@ -286,7 +302,7 @@ __device__ inline VTab vtab_carve(char *base, int cap, int D, bool single) {
     L.mt = reinterpret_cast<float *>(base);     base += single ? (size_t)kTile * kTile * 4 : 0;
     L.rbuf = reinterpret_cast<float *>(base);   base += single ? 0 : c * D * 4;
     L.y = reinterpret_cast<float *>(base);      base += c * kPath * 4;
-    L.anc = reinterpret_cast<int *>(base);
+    L.anc = reinterpret_cast<uint8_t *>(base);
     return L;
 }
 
@@ -368,9 +384,12 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         ydst[1] = y1;
         ydst[2] = y2;
         ydst[3] = y3;
+        uint32_t packed[kPath / 4];
 #pragma unroll
         for (int e = 0; e < kPath; e += 4)
-            *reinterpret_cast<int4 *>(L.anc + i * kPath + e) = make_int4(an[e], an[e + 1], an[e + 2], an[e + 3]);
+            packed[e / 4] = (uint32_t)an[e] | (uint32_t)an[e + 1] << 8 | (uint32_t)an[e + 2] << 16 |
+                            (uint32_t)an[e + 3] << 24;
+        *reinterpret_cast<uint4 *>(L.anc + i * kPath) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
         L.gabd[i] = gabd;
     }
     if (kSingle) {
@@ -1647,7 +1666,8 @@ int heads_per_workgroup(const Params &p, int threads, size_t lds) {
 
 // trees of at most 32 nodes (and chains): one workgroup per key head and its value
 // heads, which share the coefficients' Gram entries; trees of up to 96 nodes: the same
-// over node blocks; else coefficients + verify
+// over node blocks; else (larger trees, or more than 4 value heads per key head at a
+// batch too large to split them) coefficients + verify
 template <int D>
 hipError_t launch_verify_d(const Params &p, bool chain, hipStream_t s) {
     const int grp = p.Hv / p.Hk;
@@ -1691,7 +1711,7 @@ hipError_t launch_verify_d(const Params &p, bool chain, hipStream_t s) {
     }
     const int cap = chain ? kPath : p.max_nodes;
     // LDS for the most value heads a pass can take (a one-node sequence)
-    const size_t clds = ctab_bytes(cap, grp, std::min(grp, kCoefMaxHeadsPerPass));
+    const size_t clds = ctab_bytes(cap, grp, coef_heads_per_pass(cap, grp));
     hipError_t e = chain ? launch_with_lds(coef_kernel<D, true>, dim3(p.B * p.Hk), dim3(kCoefThreads), clds, s, p)
                          : launch_with_lds(coef_kernel<D, false>, dim3(p.B * p.Hk), dim3(kCoefThreads), clds, s, p);
     if (e != hipSuccess) return e;
@@ -1699,7 +1719,10 @@ hipError_t launch_verify_d(const Params &p, bool chain, hipStream_t s) {
     if (chain) return launch_with_lds(verify_kernel<D, true, 1>, grid, block, vtab_bytes(kPath, D, true), s, p);
     if (p.max_nodes <= kTile)
         return launch_with_lds(verify_kernel<D, false, 1>, grid, block, vtab_bytes(p.max_nodes, D, true), s, p);
-    return launch_with_lds(verify_kernel<D, false, 3>, grid, block, vtab_bytes(p.max_nodes, D, false), s, p);
+    if (p.max_nodes <= 3 * kTile)
+        return launch_with_lds(verify_kernel<D, false, 3>, grid, block, vtab_bytes(p.max_nodes, D, false), s, p);
+    return launch_with_lds(verify_kernel<D, false, kFastMaxNodes / kTile>, grid, block,
+                           vtab_bytes(p.max_nodes, D, false), s, p);
 }
 
 // one workgroup per value head: four fit a CU, and their independent rounds overlap
@@ -1714,8 +1737,11 @@ hipError_t launch_replay_d(const Params &p, bool chain, hipStream_t s) {
 }  // namespace
 
 bool fast_path_supported(int D, int dtype) { return (D == 64 || D == 128) && dtype == GDN_BF16; }
-bool fast_tree_supported(int D, int dtype, int max_nodes) {
-    return fast_path_supported(D, dtype) && max_nodes <= kFastMaxNodes;
+// Trees of up to 96 nodes run the group or block kernels, larger ones the coefficient
+// + verify pair, whose tables must fit one compute unit's LDS
+bool fast_tree_supported(int D, int dtype, int max_nodes, int heads_per_key) {
+    if (!fast_path_supported(D, dtype) || max_nodes > kFastMaxNodes) return false;
+    return coef_heads_per_pass(max_nodes, heads_per_key) > 0 && vtab_bytes(max_nodes, D, false) <= kLdsBudget;
 }
 
 hipError_t launch_tree_verify_fast(const Params &p, hipStream_t s) {

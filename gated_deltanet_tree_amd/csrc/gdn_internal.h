@@ -121,7 +121,7 @@ hipError_t launch_tree_verify_store(const Params &p, int dtype, hipStream_t s);
 hipError_t launch_persist_copy(const Params &p, hipStream_t s);
 // MFMA path (D in {64, 128}, bf16 q/k/v)
 bool fast_path_supported(int D, int dtype);
-bool fast_tree_supported(int D, int dtype, int max_nodes);
+bool fast_tree_supported(int D, int dtype, int max_nodes, int heads_per_key);
 hipError_t launch_tree_verify_fast(const Params &p, hipStream_t s);
 hipError_t launch_chain_verify_fast(const Params &p, hipStream_t s);
 hipError_t launch_persist_fast(const Params &p, hipStream_t s);

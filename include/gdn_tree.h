@@ -43,7 +43,9 @@
  *    for each layer, then (after acceptance) gdn_tree_persist for each layer.
  *    k, v, a and b of the step must stay alive until persist has run.
  *  - Kernel choice is automatic: bf16 inputs with head_dim 64 or 128 run the
- *    matrix-core kernels (trees of up to 96 nodes), everything else the
+ *    matrix-core kernels (every tree size a call takes, unless the value
+ *    heads of one key head are so many that the coefficient tables of a tree
+ *    over 96 nodes would not fit one compute unit's LDS), everything else the
  *    per-node recurrent kernels.  Setting the environment variable
  *    GDN_KERNEL_PATH=recurrent makes every call use the recurrent kernels
  *    (read on each call); both agree to within the stated tolerance.  The

@@ -59,8 +59,8 @@ def test_long_chain_outputs_and_final_states(d_):
 
 @pytest.mark.parametrize("nodes", [96, 97, 256])
 def test_large_trees(nodes):
-    """96 nodes (the largest tree the MFMA verify takes), 97 (the smallest the
-    recurrent walk takes at d=128) and 256 (the per-call maximum)."""
+    """96 nodes (the largest tree of the node-block kernel), 97 (the smallest the
+    coefficient + verify pair takes) and 256 (the per-call maximum)."""
     G = require_gpu()
     rng = np.random.default_rng(22 + nodes)
     hk, hv, d_ = 1, 3, 128
