@@ -49,6 +49,7 @@ Params base_params(const gdn_dims *d) {
     p.D = d->head_dim;
     p.num_slots = d->num_slots;
     p.stack_slots = gdn::stack_bound(d->max_nodes, d->max_depth);
+    p.f32_in = d->qkv_dtype == GDN_F32;
     return p;
 }
 

@@ -1,5 +1,7 @@
 // gdn_fast.hip -- tree verify and accepted-path replay on the matrix cores for
-// D in {64, 128} with bf16 q/k/v.
+// D in {64, 128} with bf16 or fp32 q/k/v (fp32 keys and queries enter the
+// products split into bf16 hi + lo, fp32 values enter the vector arithmetic
+// as they are).
 //
 // Unrolling the gated delta rule along a root-to-node path gives, for node n
 // with path p_0 (root) ... p_{d-1} = n and G_n = a_{p_0} ... a_{p_{d-1}}:
@@ -19,6 +21,7 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "gdn_internal.h"
 
@@ -37,6 +40,26 @@ constexpr size_t kLdsBudget = 160 * 1024;       // LDS of one compute unit
 
 __device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
 __device__ __forceinline__ float qnan_f() { return __int_as_float(0x7fc00000); }
+
+// q/k/v element: bf16 bits, or fp32 (F32)
+template <bool F32>
+using InT = typename std::conditional<F32, float, uint16_t>::type;
+__device__ __forceinline__ float in2f(uint16_t x) { return bf2f(x); }
+__device__ __forceinline__ float in2f(float x) { return x; }
+
+// fp32 keys and queries enter the matrix cores as bf16 hi + lo (hi the nearest
+// bf16, lo the nearest bf16 to the remainder: about 16 significant bits).
+__device__ __forceinline__ uint32_t split_pair(float x, float y, uint32_t &lo) {
+    const __bf16 hx = static_cast<__bf16>(x), hy = static_cast<__bf16>(y);
+    const __bf16 lx = static_cast<__bf16>(x - static_cast<float>(hx));
+    const __bf16 ly = static_cast<__bf16>(y - static_cast<float>(hy));
+    lo = (uint32_t)__builtin_bit_cast(uint16_t, lx) | (uint32_t)__builtin_bit_cast(uint16_t, ly) << 16;
+    return (uint32_t)__builtin_bit_cast(uint16_t, hx) | (uint32_t)__builtin_bit_cast(uint16_t, hy) << 16;
+}
+__device__ __forceinline__ void split4(const float4 x, uint2 &hi, uint2 &lo) {
+    hi.x = split_pair(x.x, x.y, lo.x);
+    hi.y = split_pair(x.z, x.w, lo.y);
+}
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Buffer resource over `bytes` bytes from `base`: loads past the end return zero and
@@ -62,6 +85,25 @@ __device__ __forceinline__ bf16x8 frag_of(const uint16_t *vec, int s, int hf) {
     return __builtin_bit_cast(bf16x8, raw);
 }
 __device__ __forceinline__ bf16x8 zero_frag() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
+
+// acc + A B for operands split hi + lo: hi*hi + hi*lo + lo*hi (the lo*lo term, at
+// most ~2^-16 of the product, is dropped)
+__device__ __forceinline__ f32x16 mfma_split(bf16x8 ahi, bf16x8 alo, bf16x8 bhi, bf16x8 blo, f32x16 acc) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bhi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, blo, acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bhi, acc, 0, 0, 0);
+}
+
+// k-step s fragment (8 values, 16s + 8*half onwards) of an fp32 row, split hi + lo
+__device__ __forceinline__ void frag_split(const float *vec, int s, int hf, bf16x8 &hi, bf16x8 &lo) {
+    const float4 x0 = *reinterpret_cast<const float4 *>(vec + 16 * s + 8 * hf);
+    const float4 x1 = *reinterpret_cast<const float4 *>(vec + 16 * s + 8 * hf + 4);
+    uint2 h0, l0, h1, l1;
+    split4(x0, h0, l0);
+    split4(x1, h1, l1);
+    hi = __builtin_bit_cast(bf16x8, make_uint4(h0.x, h0.y, h1.x, h1.y));
+    lo = __builtin_bit_cast(bf16x8, make_uint4(l0.x, l0.y, l1.x, l1.y));
+}
 
 // Sequence view shared by the two verify kernels.  CHAIN: sequence b is the
 // chain of nodes [cu[b], cu[b+1]) (validated here); else the plan's verdict.
@@ -151,7 +193,7 @@ __device__ inline CTab ctab_carve(char *base, int cap, int grp, int hpp) {
     return L;
 }
 
-template <int D, bool CHAIN>
+template <int D, bool CHAIN, bool F32>
 __global__ __launch_bounds__(kCoefThreads) void coef_kernel(Params P) {
     extern __shared__ __attribute__((aligned(16))) char lds_raw[];
     constexpr int KS = D / 16;
@@ -194,8 +236,8 @@ __global__ __launch_bounds__(kCoefThreads) void coef_kernel(Params P) {
     __syncthreads();
 
     // Gram entries for every (ancestor, node) pair on the matrix cores
-    const uint16_t *kb = static_cast<const uint16_t *>(P.k) + ((size_t)lo * P.Hk + g) * D;
-    const uint16_t *qb = static_cast<const uint16_t *>(P.q) + ((size_t)lo * P.Hk + g) * D;
+    const InT<F32> *kb = static_cast<const InT<F32> *>(P.k) + ((size_t)lo * P.Hk + g) * D;
+    const InT<F32> *qb = static_cast<const InT<F32> *>(P.q) + ((size_t)lo * P.Hk + g) * D;
     const size_t kq_stride = (size_t)P.Hk * D;
     const int ntiles = (n + kTile - 1) / kTile;
     for (int pair = w; pair < ntiles * ntiles; pair += kCoefThreads / 64) {
@@ -204,11 +246,23 @@ __global__ __launch_bounds__(kCoefThreads) void coef_kernel(Params P) {
         f32x16 gkk = {}, gkq = {};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            const bf16x8 A = pi < n ? frag_of(kb + (size_t)pi * kq_stride, s, hf) : zero_frag();
-            const bf16x8 Bk = pj < n ? frag_of(kb + (size_t)pj * kq_stride, s, hf) : zero_frag();
-            const bf16x8 Bq = pj < n ? frag_of(qb + (size_t)pj * kq_stride, s, hf) : zero_frag();
-            gkk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bk, gkk, 0, 0, 0);
-            gkq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bq, gkq, 0, 0, 0);
+            if constexpr (F32) {
+                bf16x8 A = zero_frag(), Al = zero_frag(), Bk = zero_frag(), Bkl = zero_frag(), Bq = zero_frag(),
+                       Bql = zero_frag();
+                if (pi < n) frag_split(kb + (size_t)pi * kq_stride, s, hf, A, Al);
+                if (pj < n) {
+                    frag_split(kb + (size_t)pj * kq_stride, s, hf, Bk, Bkl);
+                    frag_split(qb + (size_t)pj * kq_stride, s, hf, Bq, Bql);
+                }
+                gkk = mfma_split(A, Al, Bk, Bkl, gkk);
+                gkq = mfma_split(A, Al, Bq, Bql, gkq);
+            } else {
+                const bf16x8 A = pi < n ? frag_of(kb + (size_t)pi * kq_stride, s, hf) : zero_frag();
+                const bf16x8 Bk = pj < n ? frag_of(kb + (size_t)pj * kq_stride, s, hf) : zero_frag();
+                const bf16x8 Bq = pj < n ? frag_of(qb + (size_t)pj * kq_stride, s, hf) : zero_frag();
+                gkk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bk, gkk, 0, 0, 0);
+                gkq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bq, gkq, 0, 0, 0);
+            }
         }
         if (pj < n) {  // accumulator r: (candidate ancestor ti*32 + il, node pj)
             const uint32_t mask = L.amask[pj * kMaskWords + ti];
@@ -280,7 +334,7 @@ __global__ __launch_bounds__(kCoefThreads) void coef_kernel(Params P) {
 // runs on fp32 MFMA straight from the accumulators of the first product).
 // ===========================================================================
 struct VTab {
-    uint16_t *kq;   // [2][32][D] bf16 keys / queries (single-block trees)
+    uint16_t *kq;   // [2][32][D] bf16 keys / queries (single-block trees); fp32 inputs: hi, then [2][32][D] lo
     float *mt;      // [32][32] dense MT (single-block trees)
     float *rbuf;    // [cap][D] r rows (multi-block trees)
     float *y;       // [cap][16] path weights
@@ -288,17 +342,17 @@ struct VTab {
     float4 *gabd;   // [cap] gamma, alpha, b, depth
 };
 
-__host__ __device__ inline size_t vtab_bytes(int cap, int D, bool single) {
+__host__ __device__ inline size_t vtab_bytes(int cap, int D, bool single, bool f32 = false) {
     const size_t c = (size_t)cap;
-    return (single ? (size_t)2 * kTile * D * 2 + (size_t)kTile * kTile * 4 : c * D * 4) + c * kPath * 4 + c * kPath +
-           c * 16;
+    const size_t kq = (size_t)(f32 ? 4 : 2) * kTile * D * 2;
+    return (single ? kq + (size_t)kTile * kTile * 4 : c * D * 4) + c * kPath * 4 + c * kPath + c * 16;
 }
 
-__device__ inline VTab vtab_carve(char *base, int cap, int D, bool single) {
+__device__ inline VTab vtab_carve(char *base, int cap, int D, bool single, bool f32 = false) {
     VTab L;
     const size_t c = (size_t)cap;
     L.gabd = reinterpret_cast<float4 *>(base);  base += c * 16;
-    L.kq = reinterpret_cast<uint16_t *>(base);  base += single ? (size_t)2 * kTile * D * 2 : 0;
+    L.kq = reinterpret_cast<uint16_t *>(base);  base += single ? (size_t)(f32 ? 4 : 2) * kTile * D * 2 : 0;
     L.mt = reinterpret_cast<float *>(base);     base += single ? (size_t)kTile * kTile * 4 : 0;
     L.rbuf = reinterpret_cast<float *>(base);   base += single ? 0 : c * D * 4;
     L.y = reinterpret_cast<float *>(base);      base += c * kPath * 4;
@@ -306,7 +360,7 @@ __device__ inline VTab vtab_carve(char *base, int cap, int D, bool single) {
     return L;
 }
 
-template <int D, bool CHAIN, int MT>
+template <int D, bool CHAIN, int MT, bool F32>
 __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(3))) void verify_kernel(Params P) {
     extern __shared__ __attribute__((aligned(16))) char lds_raw[];
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, hf = lane / 32, l32 = lane % 32;
@@ -337,10 +391,11 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
 
     constexpr bool kSingle = MT == 1;
     const int cap = CHAIN ? kPath : P.max_nodes;
-    const VTab L = vtab_carve(lds_raw, cap, D, kSingle);
-    const uint16_t *kb = static_cast<const uint16_t *>(P.k) + ((size_t)lo * P.Hk + g) * D;
-    const uint16_t *qb = static_cast<const uint16_t *>(P.q) + ((size_t)lo * P.Hk + g) * D;
-    const uint16_t *vb = static_cast<const uint16_t *>(P.v) + ((size_t)lo * P.Hv + h) * D + row;
+    const VTab L = vtab_carve(lds_raw, cap, D, kSingle, F32);
+    const InT<F32> *kb = static_cast<const InT<F32> *>(P.k) + ((size_t)lo * P.Hk + g) * D;
+    const InT<F32> *qb = static_cast<const InT<F32> *>(P.q) + ((size_t)lo * P.Hk + g) * D;
+    const InT<F32> *vb = static_cast<const InT<F32> *>(P.v) + ((size_t)lo * P.Hv + h) * D + row;
+    constexpr int EPC = F32 ? 4 : 8;  // values per 16-byte chunk
     const size_t kq_stride = (size_t)P.Hk * D, v_stride = (size_t)P.Hv * D;
 
     // ---- one round trip: every load is issued before any result is used
@@ -353,24 +408,24 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         sf[s][0] = x0.x; sf[s][1] = x0.y; sf[s][2] = x0.z; sf[s][3] = x0.w;
         sf[s][4] = x1.x; sf[s][5] = x1.y; sf[s][6] = x1.z; sf[s][7] = x1.w;
     }
-    constexpr int KQ_PER = kSingle ? (2 * kTile * D / 8 + VG<D>::THREADS - 1) / VG<D>::THREADS : 1;
+    constexpr int KQ_PER = kSingle ? (2 * kTile * D / EPC + VG<D>::THREADS - 1) / VG<D>::THREADS : 1;
     uint4 kqv[KQ_PER];
     if (kSingle) {
 #pragma unroll
         for (int u = 0; u < KQ_PER; ++u) {
             const int idx = tid + u * VG<D>::THREADS;
-            const int which = idx / (kTile * (D / 8)), rem = idx % (kTile * (D / 8));
-            const int i = rem / (D / 8), c8 = rem % (D / 8);
+            const int which = idx / (kTile * (D / EPC)), rem = idx % (kTile * (D / EPC));
+            const int i = rem / (D / EPC), c8 = rem % (D / EPC);
             kqv[u] = (which < 2 && i < n)
-                         ? *reinterpret_cast<const uint4 *>((which ? qb : kb) + (size_t)i * kq_stride + 8 * c8)
+                         ? *reinterpret_cast<const uint4 *>((which ? qb : kb) + (size_t)i * kq_stride + EPC * c8)
                          : make_uint4(0, 0, 0, 0);
         }
     }
-    uint16_t vraw[16];
+    InT<F32> vraw[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int i = 8 * (r / 4) + 4 * hf + (r % 4);
-        vraw[r] = i < n ? vb[(size_t)i * v_stride] : uint16_t(0);
+        vraw[r] = i < n ? vb[(size_t)i * v_stride] : InT<F32>(0);
     }
     const float *coef = P.ws.coef + ((size_t)lo * P.Hv + h) * kCoefFloats;
     for (int i = tid; i < n; i += VG<D>::THREADS) {
@@ -396,7 +451,16 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int u = 0; u < KQ_PER; ++u) {
             const int idx = tid + u * VG<D>::THREADS;
-            if (idx < 2 * kTile * (D / 8)) reinterpret_cast<uint4 *>(L.kq)[idx] = kqv[u];
+            if (idx < 2 * kTile * (D / EPC)) {
+                if constexpr (F32) {  // hi rows as the bf16 layout, lo rows 2*32 rows further
+                    uint2 hi, lo2;
+                    split4(__builtin_bit_cast(float4, kqv[u]), hi, lo2);
+                    reinterpret_cast<uint2 *>(L.kq)[idx] = hi;
+                    reinterpret_cast<uint2 *>(L.kq + 2 * kTile * D)[idx] = lo2;
+                } else {
+                    reinterpret_cast<uint4 *>(L.kq)[idx] = kqv[u];
+                }
+            }
         }
         for (int idx = tid; idx < kTile * kTile; idx += VG<D>::THREADS) L.mt[idx] = 0.0f;
     }
@@ -425,17 +489,24 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         for (int s = 0; s < VG<D>::KS; ++s) {
             const bf16x8 Ak = frag_of(kr, s, hf);
             const bf16x8 Aq = frag_of(qr, s, hf);
-            ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, shi[s], ax, 0, 0, 0);
-            ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, slo[s], ax, 0, 0, 0);
-            ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, shi[s], ay, 0, 0, 0);
-            ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, slo[s], ay, 0, 0, 0);
+            if constexpr (F32) {
+                const bf16x8 Akl = frag_of(kr + 2 * kTile * D, s, hf);
+                const bf16x8 Aql = frag_of(qr + 2 * kTile * D, s, hf);
+                ax = mfma_split(Ak, Akl, shi[s], slo[s], ax);
+                ay = mfma_split(Aq, Aql, shi[s], slo[s], ay);
+            } else {
+                ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, shi[s], ax, 0, 0, 0);
+                ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, slo[s], ax, 0, 0, 0);
+                ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, shi[s], ay, 0, 0, 0);
+                ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, slo[s], ay, 0, 0, 0);
+            }
         }
         f32x16 rr, oo;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int i = 8 * (r / 4) + 4 * hf + (r % 4);
             const float4 gabd = L.gabd[min(i, n - 1)];
-            rr[r] = i < n ? fmaf(-gabd.y, ax[r], gabd.z * bf2f(vraw[r])) : 0.0f;
+            rr[r] = i < n ? fmaf(-gabd.y, ax[r], gabd.z * in2f(vraw[r])) : 0.0f;
             oo[r] = i < n ? gabd.x * ay[r] : 0.0f;
         }
         __syncthreads();
@@ -460,23 +531,29 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int i = t * kTile + 8 * (r / 4) + 4 * hf + (r % 4);
-                    vraw[r] = i < n ? vb[(size_t)i * v_stride] : uint16_t(0);
+                    vraw[r] = i < n ? vb[(size_t)i * v_stride] : InT<F32>(0);
                 }
             }
             const int pi = t * kTile + l32;
             f32x16 ax = {};
 #pragma unroll
             for (int s = 0; s < VG<D>::KS; ++s) {
-                const bf16x8 Ak = pi < n ? frag_of(kb + (size_t)pi * kq_stride, s, hf) : zero_frag();
-                ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, shi[s], ax, 0, 0, 0);
-                ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, slo[s], ax, 0, 0, 0);
+                if constexpr (F32) {
+                    bf16x8 Ak = zero_frag(), Akl = zero_frag();
+                    if (pi < n) frag_split(kb + (size_t)pi * kq_stride, s, hf, Ak, Akl);
+                    ax = mfma_split(Ak, Akl, shi[s], slo[s], ax);
+                } else {
+                    const bf16x8 Ak = pi < n ? frag_of(kb + (size_t)pi * kq_stride, s, hf) : zero_frag();
+                    ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, shi[s], ax, 0, 0, 0);
+                    ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, slo[s], ax, 0, 0, 0);
+                }
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int i = t * kTile + 8 * (r / 4) + 4 * hf + (r % 4);
                 if (i < n) {
                     const float4 gabd = L.gabd[i];
-                    L.rbuf[(size_t)i * D + row] = fmaf(-gabd.y, ax[r], gabd.z * bf2f(vraw[r]));
+                    L.rbuf[(size_t)i * D + row] = fmaf(-gabd.y, ax[r], gabd.z * in2f(vraw[r]));
                 }
             }
         }
@@ -489,9 +566,15 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
             f32x16 ay = {};
 #pragma unroll
             for (int s = 0; s < VG<D>::KS; ++s) {
-                const bf16x8 Aq = pi < n ? frag_of(qb + (size_t)pi * kq_stride, s, hf) : zero_frag();
-                ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, shi[s], ay, 0, 0, 0);
-                ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, slo[s], ay, 0, 0, 0);
+                if constexpr (F32) {
+                    bf16x8 Aq = zero_frag(), Aql = zero_frag();
+                    if (pi < n) frag_split(qb + (size_t)pi * kq_stride, s, hf, Aq, Aql);
+                    ay = mfma_split(Aq, Aql, shi[s], slo[s], ay);
+                } else {
+                    const bf16x8 Aq = pi < n ? frag_of(qb + (size_t)pi * kq_stride, s, hf) : zero_frag();
+                    ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, shi[s], ay, 0, 0, 0);
+                    ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, slo[s], ay, 0, 0, 0);
+                }
             }
             // 16 nodes per lane; weights are zero past each node's depth
             float o[16];
@@ -542,8 +625,9 @@ struct GPad {
 
 template <int D>
 struct GTab {
-    uint16_t *kq;     // [2][32][KQ] keys / queries (bf16)
+    uint16_t *kq;     // [2][32][KQ] keys / queries (bf16); fp32 inputs: their hi parts, then [2][32][KQ] lo parts
     uint16_t *v;      // [32][grp][D] values of the group's heads (bf16), node-major as in memory
+    float *vf;        // the same for fp32 values
     float4 *gab;      // [grp][32] gamma, alpha, b
     uint16_t *mth, *mtl;  // [grp][32][MT] dense output operator, bf16 hi and lo parts
     float *coefL;     // [grp][32][PS]
@@ -554,19 +638,21 @@ struct GTab {
 };
 
 template <int D>
-__host__ __device__ inline size_t gtab_bytes(int grp) {
+__host__ __device__ inline size_t gtab_bytes(int grp, bool f32 = false) {
     using Q = GPad<D>;
-    return (size_t)2 * kTile * Q::KQ * 2 + (size_t)kTile * grp * D * 2 + (size_t)grp * kTile * 16 +
+    const size_t ew = f32 ? 4 : 2;  // bytes per value; fp32 keys/queries take two bf16 rows each
+    return (size_t)(f32 ? 4 : 2) * kTile * Q::KQ * 2 + (size_t)kTile * grp * D * ew + (size_t)grp * kTile * 16 +
            (size_t)grp * kTile * Q::MT * 4 + (size_t)grp * kTile * Q::PS * 4 + 3 * kTile * Q::PS * 4 +
            2 * (size_t)grp * kTile * 4 + kTile * 4;
 }
 
 template <int D>
-__device__ inline GTab<D> gtab_carve(char *base, int grp) {
+__device__ inline GTab<D> gtab_carve(char *base, int grp, bool f32 = false) {
     using Q = GPad<D>;
     GTab<D> L;
-    L.kq = reinterpret_cast<uint16_t *>(base);     base += (size_t)2 * kTile * Q::KQ * 2;
-    L.v = reinterpret_cast<uint16_t *>(base);      base += (size_t)kTile * grp * D * 2;
+    L.kq = reinterpret_cast<uint16_t *>(base);     base += (size_t)(f32 ? 4 : 2) * kTile * Q::KQ * 2;
+    L.v = reinterpret_cast<uint16_t *>(base);
+    L.vf = reinterpret_cast<float *>(base);        base += (size_t)kTile * grp * D * (f32 ? 4 : 2);
     L.gab = reinterpret_cast<float4 *>(base);      base += (size_t)grp * kTile * 16;
     L.mth = reinterpret_cast<uint16_t *>(base);    base += (size_t)grp * kTile * Q::MT * 2;
     L.mtl = reinterpret_cast<uint16_t *>(base);    base += (size_t)grp * kTile * Q::MT * 2;
@@ -594,7 +680,7 @@ __device__ __forceinline__ void load_state_frags(const float *head, unsigned lan
     }
 }
 
-template <int D, bool CHAIN, int HPW>
+template <int D, bool CHAIN, int HPW, bool F32>
 __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(HPW == 1 ? 3 : 2))) void
 verify_group_kernel(Params P) {
     extern __shared__ __attribute__((aligned(16))) char lds_raw[];
@@ -627,36 +713,38 @@ verify_group_kernel(Params P) {
     }
     if (n == 0) return;
     using Q = GPad<D>;
-    const GTab<D> L = gtab_carve<D>(lds_raw, grp);
-    const uint16_t *kb = static_cast<const uint16_t *>(P.k) + ((size_t)lo * P.Hk + g) * D;
-    const uint16_t *qb = static_cast<const uint16_t *>(P.q) + ((size_t)lo * P.Hk + g) * D;
+    const GTab<D> L = gtab_carve<D>(lds_raw, grp, F32);
+    const InT<F32> *kb = static_cast<const InT<F32> *>(P.k) + ((size_t)lo * P.Hk + g) * D;
+    const InT<F32> *qb = static_cast<const InT<F32> *>(P.q) + ((size_t)lo * P.Hk + g) * D;
     const size_t kq_stride = (size_t)P.Hk * D;
     const float *s0 = P.state_in + ((size_t)sv.slot * P.Hv + h0) * D * D;
     const unsigned s_lane = (unsigned)(row * D + 8 * hf);
 
-    // ---- one round trip: keys/queries, all heads' values, tree, gates
-    constexpr int KQ_PER = (2 * kTile * D / 8 + NT - 1) / NT;
+    // ---- one round trip: keys/queries, all heads' values, tree, gates (16-byte chunks:
+    // 8 bf16 or 4 fp32 values)
+    constexpr int EPC = F32 ? 4 : 8;  // values per 16-byte chunk
+    constexpr int KQ_PER = (2 * kTile * D / EPC + NT - 1) / NT;
     uint4 kqv[KQ_PER];
 #pragma unroll
     for (int u = 0; u < KQ_PER; ++u) {
         const int idx = tid + u * NT;
-        const int which = idx / (kTile * (D / 8)), rem = idx % (kTile * (D / 8));
-        const int i = rem / (D / 8), c8 = rem % (D / 8);
+        const int which = idx / (kTile * (D / EPC)), rem = idx % (kTile * (D / EPC));
+        const int i = rem / (D / EPC), c8 = rem % (D / EPC);
         kqv[u] = (which < 2 && i < n)
-                     ? *reinterpret_cast<const uint4 *>((which ? qb : kb) + (size_t)i * kq_stride + 8 * c8)
+                     ? *reinterpret_cast<const uint4 *>((which ? qb : kb) + (size_t)i * kq_stride + EPC * c8)
                      : make_uint4(0, 0, 0, 0);
     }
-    // values: node i's group heads are contiguous (grp*D bf16); kGroupMaxHeads*32*D/8/NT chunks at most
-    const uint16_t *vg = static_cast<const uint16_t *>(P.v) + ((size_t)lo * P.Hv + h0) * D;
-    const int vchunks = grp * D / 8;  // 16-byte chunks per node
-    constexpr int V_PER = (kGroupMaxHeads * kTile * D / 8 + NT - 1) / NT;
+    // values: node i's group heads are contiguous (grp*D values)
+    const InT<F32> *vg = static_cast<const InT<F32> *>(P.v) + ((size_t)lo * P.Hv + h0) * D;
+    const int vchunks = grp * D / EPC;  // 16-byte chunks per node
+    constexpr int V_PER = F32 ? (HPW * kTile * D / 4 + NT - 1) / NT : (kGroupMaxHeads * kTile * D / 8 + NT - 1) / NT;
     static_assert(kGroupMaxHeads * kTile <= NT, "one thread per (head, node) gate");
     uint4 vv[V_PER];
 #pragma unroll
     for (int u = 0; u < V_PER; ++u) {
         const int idx = tid + u * NT;
         const int i = idx / vchunks, c = idx % vchunks;
-        vv[u] = i < n ? *reinterpret_cast<const uint4 *>(vg + (size_t)i * P.Hv * D + 8 * c) : make_uint4(0, 0, 0, 0);
+        vv[u] = i < n ? *reinterpret_cast<const uint4 *>(vg + (size_t)i * P.Hv * D + EPC * c) : make_uint4(0, 0, 0, 0);
     }
     float ga = 0.0f, gb = 0.0f;  // gates of (head tid / n, node tid % n); grp * n <= NT
     if (tid < grp * n) {
@@ -684,8 +772,17 @@ verify_group_kernel(Params P) {
 #pragma unroll
     for (int u = 0; u < KQ_PER; ++u) {
         const int idx = tid + u * NT;
-        if (idx < 2 * kTile * (D / 8))
-            *reinterpret_cast<uint4 *>(L.kq + (idx / (D / 8)) * Q::KQ + 8 * (idx % (D / 8))) = kqv[u];
+        if (idx < 2 * kTile * (D / EPC)) {
+            if constexpr (F32) {  // hi rows as the bf16 layout, lo rows 2*32 rows further
+                uint2 hi, lo2;
+                split4(__builtin_bit_cast(float4, kqv[u]), hi, lo2);
+                uint16_t *dst = L.kq + (idx / (D / 4)) * Q::KQ + 4 * (idx % (D / 4));
+                *reinterpret_cast<uint2 *>(dst) = hi;
+                *reinterpret_cast<uint2 *>(dst + 2 * kTile * Q::KQ) = lo2;
+            } else {
+                *reinterpret_cast<uint4 *>(L.kq + (idx / (D / 8)) * Q::KQ + 8 * (idx % (D / 8))) = kqv[u];
+            }
+        }
     }
 #pragma unroll
     for (int u = 0; u < V_PER; ++u) {
@@ -710,8 +807,15 @@ verify_group_kernel(Params P) {
         for (int s = 0; s < KS; ++s) {
             const bf16x8 A = frag_of(L.kq + l32 * Q::KQ, s, hf);
             const bf16x8 Bq = frag_of(L.kq + (kTile + l32) * Q::KQ, s, hf);
-            gkk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, A, gkk, 0, 0, 0);
-            gkq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bq, gkq, 0, 0, 0);
+            if constexpr (F32) {
+                const bf16x8 Al = frag_of(L.kq + (2 * kTile + l32) * Q::KQ, s, hf);
+                const bf16x8 Bql = frag_of(L.kq + (3 * kTile + l32) * Q::KQ, s, hf);
+                gkk = mfma_split(A, Al, A, Al, gkk);
+                gkq = mfma_split(A, Al, Bq, Bql, gkq);
+            } else {
+                gkk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, A, gkk, 0, 0, 0);
+                gkq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bq, gkq, 0, 0, 0);
+            }
         }
         if (l32 < n) {  // accumulator r: (candidate ancestor il, node l32)
             const int dl = L.depth[l32];
@@ -794,20 +898,28 @@ verify_group_kernel(Params P) {
             }
             const bf16x8 Ak = frag_of(L.kq + l32 * Q::KQ, s, hf);
             const bf16x8 Aq = frag_of(L.kq + (kTile + l32) * Q::KQ, s, hf);
-            ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, shi, ax, 0, 0, 0);
-            ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, slo, ax, 0, 0, 0);
-            ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, shi, ay, 0, 0, 0);
-            ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, slo, ay, 0, 0, 0);
+            if constexpr (F32) {
+                const bf16x8 Akl = frag_of(L.kq + (2 * kTile + l32) * Q::KQ, s, hf);
+                const bf16x8 Aql = frag_of(L.kq + (3 * kTile + l32) * Q::KQ, s, hf);
+                ax = mfma_split(Ak, Akl, shi, slo, ax);
+                ay = mfma_split(Aq, Aql, shi, slo, ay);
+            } else {
+                ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, shi, ax, 0, 0, 0);
+                ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, slo, ax, 0, 0, 0);
+                ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, shi, ay, 0, 0, 0);
+                ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, slo, ay, 0, 0, 0);
+            }
         }
     };
     auto finish = [&](f32x16 ax, f32x16 ay, int hh) {
         const float4 *gab = L.gab + hh * kTile;
         const uint16_t *vh = L.v + hh * D + row;
+        const float *vhf = L.vf + hh * D + row;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int i = 8 * (r / 4) + 4 * hf + (r % 4);
             const float4 q4 = gab[min(i, n - 1)];
-            const float vi = bf2f(vh[i * grp * D]);
+            const float vi = F32 ? vhf[i * grp * D] : bf2f(vh[i * grp * D]);
             ax[r] = i < n ? fmaf(-q4.y, ax[r], q4.z * vi) : 0.0f;  // r = b v - alpha x
             ay[r] = i < n ? q4.x * ay[r] : 0.0f;                   // gamma y
         }
@@ -1315,7 +1427,9 @@ template <int D>
 struct PTab {
     uint16_t *k;      // [16][KP] path keys (bf16), rows >= L zero
     uint16_t *kt;     // [D][KT] the same keys transposed
+    uint16_t *klo, *ktlo;  // fp32 keys: the lo parts, laid out as k and kt (k, kt hold the hi parts)
     uint16_t *v;      // [16][grp][D] path values of the workgroup's heads
+    float *vf;        // the same for fp32 values
     float *gram;      // [16][17] k_e . k_p
     float *coefL;     // [grp][16][17]
     float4 *gaw;      // [grp][16] gamma, alpha, b, w
@@ -1325,19 +1439,26 @@ struct PTab {
 };
 
 template <int D>
-__host__ __device__ inline size_t ptab_bytes(int grp) {
-    return (size_t)kPath * PTab<D>::KP * 2 + (size_t)D * PTab<D>::KT * 2 + (size_t)kPath * grp * D * 2 +
-           kPath * (kPath + 1) * 4 + (size_t)grp * kPath * (kPath + 1) * 4 + (size_t)grp * kPath * 16 +
-           2 * (size_t)grp * kPath * 4;
+__host__ __device__ inline size_t ptab_bytes(int grp, bool f32 = false) {
+    const size_t keys = (size_t)kPath * PTab<D>::KP * 2 + (size_t)D * PTab<D>::KT * 2;
+    return keys * (f32 ? 2 : 1) + (size_t)kPath * grp * D * (f32 ? 4 : 2) + kPath * (kPath + 1) * 4 +
+           (size_t)grp * kPath * (kPath + 1) * 4 + (size_t)grp * kPath * 16 + 2 * (size_t)grp * kPath * 4;
 }
 
 template <int D>
-__device__ inline PTab<D> ptab_carve(char *base, int grp) {
+__device__ inline PTab<D> ptab_carve(char *base, int grp, bool f32 = false) {
     PTab<D> L;
     L.gaw = reinterpret_cast<float4 *>(base);      base += (size_t)grp * kPath * 16;
     L.k = reinterpret_cast<uint16_t *>(base);      base += (size_t)kPath * PTab<D>::KP * 2;
     L.kt = reinterpret_cast<uint16_t *>(base);     base += (size_t)D * PTab<D>::KT * 2;
-    L.v = reinterpret_cast<uint16_t *>(base);      base += (size_t)kPath * grp * D * 2;
+    L.klo = L.k;
+    L.ktlo = L.kt;
+    if (f32) {
+        L.klo = reinterpret_cast<uint16_t *>(base);  base += (size_t)kPath * PTab<D>::KP * 2;
+        L.ktlo = reinterpret_cast<uint16_t *>(base); base += (size_t)D * PTab<D>::KT * 2;
+    }
+    L.v = reinterpret_cast<uint16_t *>(base);
+    L.vf = reinterpret_cast<float *>(base);        base += (size_t)kPath * grp * D * (f32 ? 4 : 2);
     L.gram = reinterpret_cast<float *>(base);      base += kPath * (kPath + 1) * 4;
     L.coefL = reinterpret_cast<float *>(base);     base += (size_t)grp * kPath * (kPath + 1) * 4;
     L.a = reinterpret_cast<float *>(base);         base += (size_t)grp * kPath * 4;
@@ -1358,7 +1479,7 @@ __device__ __forceinline__ void load_state_tiles(const float *head, unsigned lan
         }
 }
 
-template <int D, bool CHAIN>
+template <int D, bool CHAIN, bool F32>
 __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(3))) void replay_kernel(
     Params P) {
     extern __shared__ __attribute__((aligned(16))) char lds_raw[];
@@ -1430,12 +1551,13 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
     }
 
     // ---- tables: path keys (both ways), values and gates of the workgroup's head
-    const PTab<D> L = ptab_carve<D>(lds_raw, grp);
-    const uint16_t *kb = static_cast<const uint16_t *>(P.k) + ((size_t)lo * P.Hk + g) * D;
-    const uint16_t *vg = static_cast<const uint16_t *>(P.v) + ((size_t)lo * P.Hv + h0) * D;
-    constexpr int KC = kPath * D / 8;  // 16-byte chunks of the path keys
+    const PTab<D> L = ptab_carve<D>(lds_raw, grp, F32);
+    const InT<F32> *kb = static_cast<const InT<F32> *>(P.k) + ((size_t)lo * P.Hk + g) * D;
+    const InT<F32> *vg = static_cast<const InT<F32> *>(P.v) + ((size_t)lo * P.Hv + h0) * D;
+    constexpr int EPC = F32 ? 4 : 8;   // values per 16-byte chunk
+    constexpr int KC = kPath * D / EPC;  // 16-byte chunks of the path keys
     constexpr int K_PER = (KC + NT - 1) / NT;
-    constexpr int VC = kPath * grp * D / 8;
+    constexpr int VC = kPath * grp * D / EPC;
     constexpr int V_PER = (VC + NT - 1) / NT;
     // the nodes each thread fetches for, looked up before any fetch is issued; every
     // fetch is unconditional (entries past the path read node 0 and are dropped), so
@@ -1449,17 +1571,18 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
     };
     int nk[K_PER], nv[V_PER];
 #pragma unroll
-    for (int u = 0; u < K_PER; ++u) nk[u] = node_of(((tid + u * NT) / (D / 8)) % kPath);
+    for (int u = 0; u < K_PER; ++u) nk[u] = node_of(((tid + u * NT) / (D / EPC)) % kPath);
 #pragma unroll
-    for (int u = 0; u < V_PER; ++u) nv[u] = node_of(((tid + u * NT) / (grp * D / 8)) % kPath);
+    for (int u = 0; u < V_PER; ++u) nv[u] = node_of(((tid + u * NT) / (grp * D / EPC)) % kPath);
     const int ng = node_of(tid % kPath);
     uint4 kr[K_PER], vr[V_PER];
 #pragma unroll
     for (int u = 0; u < K_PER; ++u)
-        kr[u] = *reinterpret_cast<const uint4 *>(kb + (size_t)nk[u] * P.Hk * D + 8 * ((tid + u * NT) % (D / 8)));
+        kr[u] = *reinterpret_cast<const uint4 *>(kb + (size_t)nk[u] * P.Hk * D + EPC * ((tid + u * NT) % (D / EPC)));
 #pragma unroll
     for (int u = 0; u < V_PER; ++u)
-        vr[u] = *reinterpret_cast<const uint4 *>(vg + (size_t)nv[u] * P.Hv * D + 8 * ((tid + u * NT) % (grp * D / 8)));
+        vr[u] = *reinterpret_cast<const uint4 *>(vg + (size_t)nv[u] * P.Hv * D +
+                                                 EPC * ((tid + u * NT) % (grp * D / EPC)));
     const bool gate_t = tid < grp * kPath;
     const size_t at = (size_t)(lo + ng) * P.Hv + h0 + (gate_t ? tid / kPath : 0);
     float ga = P.a[at], gb = P.b[at];
@@ -1468,17 +1591,31 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < K_PER; ++u) {
-        const int idx = tid + u * NT, e = idx / (D / 8), c8 = idx % (D / 8);
+        const int idx = tid + u * NT, e = idx / (D / EPC), c8 = idx % (D / EPC);
         const uint4 kv = e < len ? kr[u] : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4 *>(L.k + e * PTab<D>::KP + 8 * c8) = kv;
-        const uint16_t *hv = reinterpret_cast<const uint16_t *>(&kv);
+        if constexpr (F32) {  // four keys' values, split hi + lo, both ways
+            uint2 hi, lo2;
+            split4(__builtin_bit_cast(float4, kv), hi, lo2);
+            *reinterpret_cast<uint2 *>(L.k + e * PTab<D>::KP + 4 * c8) = hi;
+            *reinterpret_cast<uint2 *>(L.klo + e * PTab<D>::KP + 4 * c8) = lo2;
+            const uint16_t *hh2 = reinterpret_cast<const uint16_t *>(&hi);
+            const uint16_t *ll2 = reinterpret_cast<const uint16_t *>(&lo2);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) L.kt[(8 * c8 + i) * PTab<D>::KT + e] = hv[i];
+            for (int i = 0; i < 4; ++i) {
+                L.kt[(4 * c8 + i) * PTab<D>::KT + e] = hh2[i];
+                L.ktlo[(4 * c8 + i) * PTab<D>::KT + e] = ll2[i];
+            }
+        } else {
+            *reinterpret_cast<uint4 *>(L.k + e * PTab<D>::KP + 8 * c8) = kv;
+            const uint16_t *hv = reinterpret_cast<const uint16_t *>(&kv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) L.kt[(8 * c8 + i) * PTab<D>::KT + e] = hv[i];
+        }
     }
 #pragma unroll
     for (int u = 0; u < V_PER; ++u) {
         const int idx = tid + u * NT;
-        reinterpret_cast<uint4 *>(L.v)[idx] = idx / (grp * D / 8) < len ? vr[u] : make_uint4(0, 0, 0, 0);
+        reinterpret_cast<uint4 *>(L.v)[idx] = idx / (grp * D / EPC) < len ? vr[u] : make_uint4(0, 0, 0, 0);
     }
     if (gate_t) {
         const bool on = tid % kPath < len;
@@ -1493,7 +1630,12 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
             const bf16x8 A = l32 < kPath ? frag_of(L.k + l32 * PTab<D>::KP, s, hf) : zero_frag();
-            gk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, A, gk, 0, 0, 0);
+            if constexpr (F32) {
+                const bf16x8 Al = l32 < kPath ? frag_of(L.klo + l32 * PTab<D>::KP, s, hf) : zero_frag();
+                gk = mfma_split(A, Al, A, Al, gk);
+            } else {
+                gk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, A, gk, 0, 0, 0);
+            }
         }
         if (l32 < kPath) {
 #pragma unroll
@@ -1549,8 +1691,19 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
                 const uint2 k1 = *reinterpret_cast<const uint2 *>(krow + 32 * t + 16 * u + 8 + 4 * hf);
                 A = __builtin_bit_cast(bf16x8, make_uint4(k0.x, k0.y, k1.x, k1.y));
             }
-            ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, shi, ax, 0, 0, 0);
-            ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, slo, ax, 0, 0, 0);
+            if constexpr (F32) {
+                bf16x8 Al = zero_frag();
+                if (l32 < kPath) {
+                    const uint16_t *klrow = L.klo + l32 * PTab<D>::KP;
+                    const uint2 k0 = *reinterpret_cast<const uint2 *>(klrow + 32 * t + 16 * u + 4 * hf);
+                    const uint2 k1 = *reinterpret_cast<const uint2 *>(klrow + 32 * t + 16 * u + 8 + 4 * hf);
+                    Al = __builtin_bit_cast(bf16x8, make_uint4(k0.x, k0.y, k1.x, k1.y));
+                }
+                ax = mfma_split(A, Al, shi, slo, ax);
+            } else {
+                ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, shi, ax, 0, 0, 0);
+                ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, slo, ax, 0, 0, 0);
+            }
         }
         // x_e of this row: accumulator r < 8 holds e = 8(r/4) + 4*half + r%4, the other
         // half-wave the rest
@@ -1567,11 +1720,12 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         const float4 *gaw = L.gaw + hh * kPath;
         const float *cl = L.coefL + hh * kPath * (kPath + 1);
         const uint16_t *vh = L.v + hh * D + row;
+        const float *vhf = L.vf + hh * D + row;
         float c[kPath];
 #pragma unroll
         for (int p = 0; p < kPath; ++p) {
             const float4 q4 = gaw[p];
-            float acc = fmaf(-q4.y, x[p], q4.z * bf2f(vh[p * grp * D]));
+            float acc = fmaf(-q4.y, x[p], q4.z * (F32 ? vhf[p * grp * D] : bf2f(vh[p * grp * D])));
 #pragma unroll
             for (int e = 0; e < p; ++e) acc = fmaf(-cl[p * (kPath + 1) + e], c[e], acc);
             c[p] = p < len ? acc : 0.0f;
@@ -1595,8 +1749,14 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
                 bf16x8, *reinterpret_cast<const uint4 *>(L.kt + (32 * t + l32) * PTab<D>::KT + 8 * hf));
 #pragma unroll
             for (int r = 0; r < 16; ++r) S[t][r] *= gl;
-            S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, whi, S[t], 0, 0, 0);
-            S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wlo, S[t], 0, 0, 0);
+            if constexpr (F32) {
+                const bf16x8 Al = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const uint4 *>(L.ktlo + (32 * t + l32) * PTab<D>::KT + 8 * hf));
+                S[t] = mfma_split(A, Al, whi, wlo, S[t]);
+            } else {
+                S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, whi, S[t], 0, 0, 0);
+                S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wlo, S[t], 0, 0, 0);
+            }
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 *reinterpret_cast<float4 *>(dh + 32 * t + 8 * q) =
@@ -1666,20 +1826,23 @@ int heads_per_workgroup(const Params &p, int threads, size_t lds) {
 
 // trees of at most 32 nodes (and chains): one workgroup per key head and its value
 // heads, which share the coefficients' Gram entries; trees of up to 96 nodes: the same
-// over node blocks; else (larger trees, or more than 4 value heads per key head at a
-// batch too large to split them) coefficients + verify
-template <int D>
+// over node blocks (bf16 inputs); else (larger trees, fp32 inputs past 32 nodes, or more
+// than 4 value heads per key head at a batch too large to split them) coefficients + verify
+template <int D, bool F32>
 hipError_t launch_verify_d(const Params &p, bool chain, hipStream_t s) {
     const int grp = p.Hv / p.Hk;
-    const int hpw = chain ? heads_per_workgroup<verify_group_kernel<D, true, 1>>(p, VG<D>::THREADS, gtab_bytes<D>(1))
-                          : heads_per_workgroup<verify_group_kernel<D, false, 1>>(p, VG<D>::THREADS, gtab_bytes<D>(1));
+    const int hpw = chain ? heads_per_workgroup<verify_group_kernel<D, true, 1, F32>>(p, VG<D>::THREADS,
+                                                                                     gtab_bytes<D>(1, F32))
+                          : heads_per_workgroup<verify_group_kernel<D, false, 1, F32>>(p, VG<D>::THREADS,
+                                                                                      gtab_bytes<D>(1, F32));
     if ((chain || p.max_nodes <= kTile) && hpw <= kGroupMaxHeads) {
         const dim3 grid(p.B * (p.Hv / hpw)), block(VG<D>::THREADS);
+        const size_t lds = gtab_bytes<D>(hpw, F32);
         switch (hpw) {
-#define GDN_GROUP_CASE(G)                                                                                    \
-    case G:                                                                                                  \
-        return chain ? launch_with_lds(verify_group_kernel<D, true, G>, grid, block, gtab_bytes<D>(G), s, p) \
-                     : launch_with_lds(verify_group_kernel<D, false, G>, grid, block, gtab_bytes<D>(G), s, p);
+#define GDN_GROUP_CASE(G)                                                                         \
+    case G:                                                                                       \
+        return chain ? launch_with_lds(verify_group_kernel<D, true, G, F32>, grid, block, lds, s, p) \
+                     : launch_with_lds(verify_group_kernel<D, false, G, F32>, grid, block, lds, s, p);
             GDN_GROUP_CASE(1)
             GDN_GROUP_CASE(2)
             GDN_GROUP_CASE(3)
@@ -1687,58 +1850,78 @@ hipError_t launch_verify_d(const Params &p, bool chain, hipStream_t s) {
 #undef GDN_GROUP_CASE
         }
     }
-    const bool two = p.max_nodes <= 2 * kTile;
-    const int gb = !chain && p.max_nodes <= 3 * kTile
-                       ? (two ? heads_per_workgroup<verify_blocks_kernel<D, 2, 1>>(p, VG<D>::THREADS,
-                                                                                  blocks_layout<D>(p.max_nodes, 1).total)
-                              : heads_per_workgroup<verify_blocks_kernel<D, 3, 1>>(p, VG<D>::THREADS,
-                                                                                  blocks_layout<D>(p.max_nodes, 1).total))
-                       : grp;
-    if (!chain && p.max_nodes <= 3 * kTile && gb <= kGroupMaxHeads) {
-        const dim3 grid(p.B * (p.Hv / gb)), block(VG<D>::THREADS);
-        const size_t lds = blocks_layout<D>(p.max_nodes, gb).total;
-        switch (gb) {
-#define GDN_BLOCKS_CASE(G)                                                          \
-    case G:                                                                         \
+    if constexpr (!F32) {
+        const bool two = p.max_nodes <= 2 * kTile;
+        const int gb = !chain && p.max_nodes <= 3 * kTile
+                           ? (two ? heads_per_workgroup<verify_blocks_kernel<D, 2, 1>>(
+                                        p, VG<D>::THREADS, blocks_layout<D>(p.max_nodes, 1).total)
+                                  : heads_per_workgroup<verify_blocks_kernel<D, 3, 1>>(
+                                        p, VG<D>::THREADS, blocks_layout<D>(p.max_nodes, 1).total))
+                           : grp;
+        if (!chain && p.max_nodes <= 3 * kTile && gb <= kGroupMaxHeads) {
+            const dim3 grid(p.B * (p.Hv / gb)), block(VG<D>::THREADS);
+            const size_t lds = blocks_layout<D>(p.max_nodes, gb).total;
+            switch (gb) {
+#define GDN_BLOCKS_CASE(G)                                                                      \
+    case G:                                                                                     \
         return two ? launch_with_lds(verify_blocks_kernel<D, 2, G>, grid, block, lds, s, p) \
                    : launch_with_lds(verify_blocks_kernel<D, 3, G>, grid, block, lds, s, p);
-            GDN_BLOCKS_CASE(1)
-            GDN_BLOCKS_CASE(2)
-            GDN_BLOCKS_CASE(3)
-            GDN_BLOCKS_CASE(4)
+                GDN_BLOCKS_CASE(1)
+                GDN_BLOCKS_CASE(2)
+                GDN_BLOCKS_CASE(3)
+                GDN_BLOCKS_CASE(4)
 #undef GDN_BLOCKS_CASE
+            }
         }
     }
     const int cap = chain ? kPath : p.max_nodes;
     // LDS for the most value heads a pass can take (a one-node sequence)
     const size_t clds = ctab_bytes(cap, grp, coef_heads_per_pass(cap, grp));
-    hipError_t e = chain ? launch_with_lds(coef_kernel<D, true>, dim3(p.B * p.Hk), dim3(kCoefThreads), clds, s, p)
-                         : launch_with_lds(coef_kernel<D, false>, dim3(p.B * p.Hk), dim3(kCoefThreads), clds, s, p);
+    hipError_t e = chain ? launch_with_lds(coef_kernel<D, true, F32>, dim3(p.B * p.Hk), dim3(kCoefThreads), clds, s, p)
+                         : launch_with_lds(coef_kernel<D, false, F32>, dim3(p.B * p.Hk), dim3(kCoefThreads), clds, s, p);
     if (e != hipSuccess) return e;
     const dim3 grid(p.B * p.Hv), block(VG<D>::THREADS);
-    if (chain) return launch_with_lds(verify_kernel<D, true, 1>, grid, block, vtab_bytes(kPath, D, true), s, p);
+    if (chain)
+        return launch_with_lds(verify_kernel<D, true, 1, F32>, grid, block, vtab_bytes(kPath, D, true, F32), s, p);
     if (p.max_nodes <= kTile)
-        return launch_with_lds(verify_kernel<D, false, 1>, grid, block, vtab_bytes(p.max_nodes, D, true), s, p);
+        return launch_with_lds(verify_kernel<D, false, 1, F32>, grid, block, vtab_bytes(p.max_nodes, D, true, F32), s,
+                               p);
     if (p.max_nodes <= 3 * kTile)
-        return launch_with_lds(verify_kernel<D, false, 3>, grid, block, vtab_bytes(p.max_nodes, D, false), s, p);
-    return launch_with_lds(verify_kernel<D, false, kFastMaxNodes / kTile>, grid, block,
+        return launch_with_lds(verify_kernel<D, false, 3, F32>, grid, block, vtab_bytes(p.max_nodes, D, false), s, p);
+    return launch_with_lds(verify_kernel<D, false, kFastMaxNodes / kTile, F32>, grid, block,
                            vtab_bytes(p.max_nodes, D, false), s, p);
 }
 
 // one workgroup per value head: four fit a CU, and their independent rounds overlap
 // reading and writing better than a key head's workgroup walking its value heads
-template <int D>
+template <int D, bool F32>
 hipError_t launch_replay_d(const Params &p, bool chain, hipStream_t s) {
     const dim3 grid(p.B * p.Hv), block(VG<D>::THREADS);
-    return chain ? launch_with_lds(replay_kernel<D, true>, grid, block, ptab_bytes<D>(1), s, p)
-                 : launch_with_lds(replay_kernel<D, false>, grid, block, ptab_bytes<D>(1), s, p);
+    return chain ? launch_with_lds(replay_kernel<D, true, F32>, grid, block, ptab_bytes<D>(1, F32), s, p)
+                 : launch_with_lds(replay_kernel<D, false, F32>, grid, block, ptab_bytes<D>(1, F32), s, p);
+}
+
+template <bool F32>
+hipError_t verify_any_d(const Params &p, bool chain, hipStream_t s) {
+    return p.D == 64 ? launch_verify_d<64, F32>(p, chain, s) : launch_verify_d<128, F32>(p, chain, s);
+}
+hipError_t verify_any(const Params &p, bool chain, hipStream_t s) {
+    return p.f32_in ? verify_any_d<true>(p, chain, s) : verify_any_d<false>(p, chain, s);
+}
+template <bool F32>
+hipError_t replay_any_d(const Params &p, bool chain, hipStream_t s) {
+    return p.D == 64 ? launch_replay_d<64, F32>(p, chain, s) : launch_replay_d<128, F32>(p, chain, s);
+}
+hipError_t replay_any(const Params &p, bool chain, hipStream_t s) {
+    return p.f32_in ? replay_any_d<true>(p, chain, s) : replay_any_d<false>(p, chain, s);
 }
 
 }  // namespace
 
-bool fast_path_supported(int D, int dtype) { return (D == 64 || D == 128) && dtype == GDN_BF16; }
+bool fast_path_supported(int D, int dtype) { return (D == 64 || D == 128) && (dtype == GDN_BF16 || dtype == GDN_F32); }
 // Trees of up to 96 nodes run the group or block kernels, larger ones the coefficient
-// + verify pair, whose tables must fit one compute unit's LDS
+// + verify pair, whose tables must fit one compute unit's LDS (fp32 inputs take the pair
+// from 33 nodes on)
 bool fast_tree_supported(int D, int dtype, int max_nodes, int heads_per_key) {
     if (!fast_path_supported(D, dtype) || max_nodes > kFastMaxNodes) return false;
     return coef_heads_per_pass(max_nodes, heads_per_key) > 0 && vtab_bytes(max_nodes, D, false) <= kLdsBudget;
@@ -1746,11 +1929,11 @@ bool fast_tree_supported(int D, int dtype, int max_nodes, int heads_per_key) {
 
 hipError_t launch_tree_verify_fast(const Params &p, hipStream_t s) {
     if (p.B == 0) return hipSuccess;
-    return p.D == 64 ? launch_verify_d<64>(p, false, s) : launch_verify_d<128>(p, false, s);
+    return verify_any(p, false, s);
 }
 hipError_t launch_persist_fast(const Params &p, hipStream_t s) {
     if (p.B == 0) return hipSuccess;
-    return p.D == 64 ? launch_replay_d<64>(p, false, s) : launch_replay_d<128>(p, false, s);
+    return replay_any(p, false, s);
 }
 // Chains of at most 16 nodes: outputs from the verify kernel in chain order
 // (so a chain-shaped tree and a chain give the same bits) and the final state
@@ -1758,9 +1941,9 @@ hipError_t launch_persist_fast(const Params &p, hipStream_t s) {
 hipError_t launch_chain_verify_fast(const Params &p, hipStream_t s) {
     if (p.B == 0) return hipSuccess;
     hipError_t e = hipSuccess;
-    if (p.out || p.has_ws) e = p.D == 64 ? launch_verify_d<64>(p, true, s) : launch_verify_d<128>(p, true, s);
+    if (p.out || p.has_ws) e = verify_any(p, true, s);
     if (e != hipSuccess) return e;
-    if (p.final_state) e = p.D == 64 ? launch_replay_d<64>(p, true, s) : launch_replay_d<128>(p, true, s);
+    if (p.final_state) e = replay_any(p, true, s);
     return e;
 }
 

@@ -76,6 +76,7 @@ inline WsPtrs ws_ptrs(void *ws, int B, int T, int Hv = 0) {
 struct Params {
     int B, T, max_nodes, max_depth, Hk, Hv, D, num_slots;
     int stack_slots;             // LDS stack entries of the recurrent tree kernel
+    int f32_in;                  // q/k/v are fp32 (else bf16 bits)
     const int32_t *parent;       // plan
     const int32_t *cu_nodes;     // plan, chain
     const int32_t *slot_idx;
@@ -119,7 +120,7 @@ hipError_t launch_persist_recurrent(const Params &p, int dtype, hipStream_t s);
 // state in fp16, and a persist that copies the accepted node's stored state
 hipError_t launch_tree_verify_store(const Params &p, int dtype, hipStream_t s);
 hipError_t launch_persist_copy(const Params &p, hipStream_t s);
-// MFMA path (D in {64, 128}, bf16 q/k/v)
+// MFMA path (D in {64, 128}, bf16 or fp32 q/k/v)
 bool fast_path_supported(int D, int dtype);
 bool fast_tree_supported(int D, int dtype, int max_nodes, int heads_per_key);
 hipError_t launch_tree_verify_fast(const Params &p, hipStream_t s);

@@ -42,8 +42,8 @@
  *  - Stream order per decode step: gdn_tree_plan once, then gdn_tree_verify
  *    for each layer, then (after acceptance) gdn_tree_persist for each layer.
  *    k, v, a and b of the step must stay alive until persist has run.
- *  - Kernel choice is automatic: bf16 inputs with head_dim 64 or 128 run the
- *    matrix-core kernels (every tree size a call takes, unless the value
+ *  - Kernel choice is automatic: bf16 or fp32 inputs with head_dim 64 or 128
+ *    run the matrix-core kernels (every tree size a call takes, unless the value
  *    heads of one key head are so many that the coefficient tables of a tree
  *    over 96 nodes would not fit one compute unit's LDS), everything else the
  *    per-node recurrent kernels.  Setting the environment variable
