@@ -236,9 +236,9 @@ int gdn_chain_verify(const gdn_dims *dims, const int32_t *cu_nodes, const void *
     if (dims->total_nodes > 0 && (!k || !v || !a || !b)) return GDN_ERR_NULL;
     if (dims->num_seqs > 0 && (!state_cache || !slot_idx)) return GDN_ERR_NULL;
     if (ws && ws_bytes < gdn_workspace_bytes(dims)) return GDN_ERR_WORKSPACE;
-    const bool fast = !recurrent_forced() && gdn::fast_path_supported(dims->head_dim, dims->qkv_dtype) &&
-                      dims->max_nodes <= GDN_MAX_DEPTH;
-    if (fast && q && !ws) return GDN_ERR_NULL;  // the outputs need the workspace for coefficients
+    const bool fast = !recurrent_forced() && gdn::fast_path_supported(dims->head_dim, dims->qkv_dtype);
+    // chains of one drafting block keep per-node coefficients in the workspace
+    if (fast && dims->max_nodes <= GDN_MAX_DEPTH && q && !ws) return GDN_ERR_NULL;
     if (dims->num_seqs == 0) return GDN_OK;
     Params p = base_params(dims);
     p.cu_nodes = cu_nodes;
@@ -257,7 +257,7 @@ int gdn_chain_verify(const gdn_dims *dims, const int32_t *cu_nodes, const void *
         p.has_ws = 1;
     }
     // chains that fit one drafting block share the tree kernels' arithmetic;
-    // longer chains (e.g. prefill) run the sequential recurrence
+    // longer chains (e.g. prefill) run in chunks of one block on the matrix cores
     if (fast) return launched(gdn::launch_chain_verify_fast(p, as_stream(stream)));
     return launched(gdn::launch_chain_verify_recurrent(p, dims->qkv_dtype, as_stream(stream)));
 }

@@ -1766,6 +1766,377 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
     head(SA, 0);
 }
 
+// ===========================================================================
+// Chains longer than one drafting block (prefill-style gdn_chain_verify): one
+// workgroup per (sequence, value head), D/32 waves, the state held in
+// registers in the replay's tile layout for the whole chain and walked in
+// chunks of 16 tokens.  Per chunk, from the state S at its start, with
+// G_p = a_0 ... a_p and R(p,e) = a_{e+1} ... a_p inside the chunk:
+//   X = S K^T, Y = S Q^T                                  (MFMA, S split hi + lo)
+//   c_p = b_p v_p - b_p G_p x_p - sum_{e<p} b_p R(p,e) (k_e . k_p) c_e  (per row)
+//   o_p = G_p y_p + sum_{e<=p} R(p,e) (k_e . q_p) c_e                  (per row)
+//   S  <- G_{L-1} S + sum_e R(L-1,e) c_e k_e^T            (rank-16 MFMA update)
+// The state after final_len tokens, when that falls inside a chunk, is the same
+// update truncated to the chunk's first tokens.  The next chunk's keys, queries,
+// values and gates are loaded into registers while this chunk computes.
+// ===========================================================================
+template <int D>
+struct CkTab {
+    uint16_t *k, *kt, *q;        // [16][KP], [D][KT], [16][KP] bf16 (fp32 inputs: hi parts)
+    uint16_t *klo, *ktlo, *qlo;  // fp32 inputs: lo parts, same layouts
+    float *v;                    // [16][D] this head's values
+    float *gram, *gq;            // [16][17]: row p, column e: k_e . k_p and k_e . q_p
+    float *coefL, *coefM;        // [16][17]: b_p R(p,e) (k_e . k_p) (e < p), R(p,e) (k_e . q_p) (e <= p)
+    float4 *gaw;                 // [16] G_p, b_p G_p, b_p, R(L-1, p)
+    float *wf;                   // [16] R(f-1, p) for the final state f tokens into the chunk
+    float *a, *b;                // [16]
+    static constexpr int KP = D + 8;
+    static constexpr int KT = kPath + 8;
+    static constexpr int PS = kPath + 1;
+};
+
+template <int D>
+__host__ __device__ inline size_t cktab_bytes(bool f32) {
+    using Q = CkTab<D>;
+    const size_t keys = (size_t)2 * kPath * Q::KP * 2 + (size_t)D * Q::KT * 2;
+    return keys * (f32 ? 2 : 1) + (size_t)kPath * D * 4 + 4 * (size_t)kPath * Q::PS * 4 + kPath * 16 + 3 * kPath * 4;
+}
+
+template <int D>
+__device__ inline CkTab<D> cktab_carve(char *base, bool f32) {
+    using Q = CkTab<D>;
+    CkTab<D> L;
+    L.gaw = reinterpret_cast<float4 *>(base);      base += kPath * 16;
+    L.v = reinterpret_cast<float *>(base);         base += (size_t)kPath * D * 4;
+    L.k = reinterpret_cast<uint16_t *>(base);      base += (size_t)kPath * Q::KP * 2;
+    L.q = reinterpret_cast<uint16_t *>(base);      base += (size_t)kPath * Q::KP * 2;
+    L.kt = reinterpret_cast<uint16_t *>(base);     base += (size_t)D * Q::KT * 2;
+    L.klo = L.k;
+    L.qlo = L.q;
+    L.ktlo = L.kt;
+    if (f32) {
+        L.klo = reinterpret_cast<uint16_t *>(base);  base += (size_t)kPath * Q::KP * 2;
+        L.qlo = reinterpret_cast<uint16_t *>(base);  base += (size_t)kPath * Q::KP * 2;
+        L.ktlo = reinterpret_cast<uint16_t *>(base); base += (size_t)D * Q::KT * 2;
+    }
+    L.gram = reinterpret_cast<float *>(base);      base += kPath * Q::PS * 4;
+    L.gq = reinterpret_cast<float *>(base);        base += kPath * Q::PS * 4;
+    L.coefL = reinterpret_cast<float *>(base);     base += kPath * Q::PS * 4;
+    L.coefM = reinterpret_cast<float *>(base);     base += kPath * Q::PS * 4;
+    L.wf = reinterpret_cast<float *>(base);        base += kPath * 4;
+    L.a = reinterpret_cast<float *>(base);         base += kPath * 4;
+    L.b = reinterpret_cast<float *>(base);
+    return L;
+}
+
+// the lane's state tiles stored in the replay layout
+template <int D>
+__device__ __forceinline__ void store_state_tiles(float *head, unsigned lane_off, const f32x16 (&S)[D / 32]) {
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4 *>(head + lane_off + 32 * t + 8 * q) =
+                make_float4(S[t][4 * q], S[t][4 * q + 1], S[t][4 * q + 2], S[t][4 * q + 3]);
+}
+
+template <int D, bool F32>
+__global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2))) void chain_chunks_kernel(
+    Params P) {
+    extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+    using Q = CkTab<D>;
+    constexpr int NT = VG<D>::THREADS, NTILE = D / 32;
+    constexpr int EPC = F32 ? 4 : 8;               // values per 16-byte chunk
+    constexpr int RC = kPath * D / EPC;            // 16-byte chunks of one chunk's keys (queries, values)
+    constexpr int R_PER = RC / NT;
+    static_assert(RC % NT == 0, "whole rounds of chunk loads");
+    const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, hf = lane / 32, l32 = lane % 32;
+    const int row = w * 32 + l32;
+    const int b = blockIdx.x / P.Hv, h = blockIdx.x % P.Hv;
+    const int g = h / (P.Hv / P.Hk);
+    const SeqView sv = seq_view<true>(P, b);
+    if (P.has_ws && h == 0 && tid == 0) {
+        if (b == 0) {
+            P.ws.header[0] = kChainMagic;
+            P.ws.header[1] = P.B;
+            P.ws.header[2] = P.T;
+            P.ws.header[kHdrMisuse] = 0;
+        }
+        P.ws.seq_status[b] = sv.status;
+    }
+    const int lo = sv.lo, n = sv.n;
+    const bool want_out = P.q != nullptr && P.out != nullptr;
+    if (sv.status != GDN_SEQ_OK) {
+        if (P.out)
+            for (int t = tid; t < n * D; t += NT) P.out[((size_t)(lo + t / D) * P.Hv + h) * D + t % D] = qnan_f();
+        return;
+    }
+    const int flen = P.final_len ? P.final_len[b] : -1;
+    float *fin = (P.final_state && flen >= 0 && flen <= n) ? P.final_state + ((size_t)b * P.Hv + h) * D * D
+                                                            : nullptr;
+    if (!fin && !(want_out && n > 0)) return;
+    // an empty chain leaves its slot unchecked in the sequence view: only the committed
+    // state is wanted, from a valid slot
+    int slot = sv.slot;
+    if (n == 0) {
+        slot = P.slot_idx[b];
+        if (slot < 0 || slot >= P.num_slots) return;
+    }
+    const unsigned s_lane = (unsigned)(row * D + 4 * hf);
+    f32x16 S[NTILE];
+    load_state_tiles<D>(P.state_in + ((size_t)slot * P.Hv + h) * D * D, s_lane, S);
+    if (fin && flen == 0) store_state_tiles<D>(fin, s_lane, S);
+    // only the chunks up to the last output or the final state are walked
+    const int n_walk = want_out ? n : flen;
+    if (n_walk <= 0) return;
+
+    const CkTab<D> L = cktab_carve<D>(lds_raw, F32);
+    const InT<F32> *kb = static_cast<const InT<F32> *>(P.k) + ((size_t)lo * P.Hk + g) * D;
+    const InT<F32> *qb = want_out ? static_cast<const InT<F32> *>(P.q) + ((size_t)lo * P.Hk + g) * D : kb;
+    const InT<F32> *vb = static_cast<const InT<F32> *>(P.v) + ((size_t)lo * P.Hv + h) * D;
+    const size_t kq_stride = (size_t)P.Hk * D, v_stride = (size_t)P.Hv * D;
+    // one chunk's raw inputs: this thread's 16-byte pieces of keys, queries and values, and
+    // (threads < 16) a gate pair; entries past the chain read its last token and are dropped
+    uint4 rk[R_PER], rq[R_PER], rv[R_PER];
+    float ra = 1.0f, rb = 0.0f;
+    auto fetch = [&](int c0) {
+        const int len = min(kPath, n_walk - c0);
+#pragma unroll
+        for (int u = 0; u < R_PER; ++u) {
+            const int idx = tid + u * NT, e = min(idx / (D / EPC), len - 1), c8 = idx % (D / EPC);
+            rk[u] = *reinterpret_cast<const uint4 *>(kb + (size_t)(c0 + e) * kq_stride + EPC * c8);
+            rq[u] = *reinterpret_cast<const uint4 *>(qb + (size_t)(c0 + e) * kq_stride + EPC * c8);
+            rv[u] = *reinterpret_cast<const uint4 *>(vb + (size_t)(c0 + e) * v_stride + EPC * c8);
+        }
+        if (tid < kPath) {
+            const size_t at = (size_t)(lo + c0 + min(tid, len - 1)) * P.Hv + h;
+            ra = P.a[at];
+            rb = P.b[at];
+        }
+    };
+    fetch(0);
+
+#pragma unroll 1
+    for (int c0 = 0; c0 < n_walk; c0 += kPath) {
+        const int len = min(kPath, n_walk - c0);
+        __syncthreads();  // the previous chunk's tables are spent
+        // ---- stage the chunk: keys and queries both ways (hi + lo for fp32), values as fp32
+#pragma unroll
+        for (int u = 0; u < R_PER; ++u) {
+            const int idx = tid + u * NT, e = idx / (D / EPC), c8 = idx % (D / EPC);
+            const bool on = e < len;
+            const uint4 kv = on ? rk[u] : make_uint4(0, 0, 0, 0);
+            const uint4 qv = on ? rq[u] : make_uint4(0, 0, 0, 0);
+            const uint4 vw = on ? rv[u] : make_uint4(0, 0, 0, 0);
+            if constexpr (F32) {
+                uint2 kh, kl, qh, ql;
+                split4(__builtin_bit_cast(float4, kv), kh, kl);
+                split4(__builtin_bit_cast(float4, qv), qh, ql);
+                *reinterpret_cast<uint2 *>(L.k + e * Q::KP + 4 * c8) = kh;
+                *reinterpret_cast<uint2 *>(L.klo + e * Q::KP + 4 * c8) = kl;
+                *reinterpret_cast<uint2 *>(L.q + e * Q::KP + 4 * c8) = qh;
+                *reinterpret_cast<uint2 *>(L.qlo + e * Q::KP + 4 * c8) = ql;
+                const uint16_t *h2 = reinterpret_cast<const uint16_t *>(&kh);
+                const uint16_t *l2 = reinterpret_cast<const uint16_t *>(&kl);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    L.kt[(4 * c8 + i) * Q::KT + e] = h2[i];
+                    L.ktlo[(4 * c8 + i) * Q::KT + e] = l2[i];
+                }
+                *reinterpret_cast<uint4 *>(L.v + e * D + 4 * c8) = vw;
+            } else {
+                *reinterpret_cast<uint4 *>(L.k + e * Q::KP + 8 * c8) = kv;
+                *reinterpret_cast<uint4 *>(L.q + e * Q::KP + 8 * c8) = qv;
+                const uint16_t *k8 = reinterpret_cast<const uint16_t *>(&kv);
+                const uint16_t *v8 = reinterpret_cast<const uint16_t *>(&vw);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) L.kt[(8 * c8 + i) * Q::KT + e] = k8[i];
+                float4 *vd = reinterpret_cast<float4 *>(L.v + e * D + 8 * c8);
+                vd[0] = make_float4(bf2f(v8[0]), bf2f(v8[1]), bf2f(v8[2]), bf2f(v8[3]));
+                vd[1] = make_float4(bf2f(v8[4]), bf2f(v8[5]), bf2f(v8[6]), bf2f(v8[7]));
+            }
+        }
+        if (tid < kPath) {
+            L.a[tid] = tid < len ? ra : 1.0f;
+            L.b[tid] = tid < len ? rb : 0.0f;
+        }
+        // the next chunk's inputs stream in under this chunk's arithmetic
+        if (c0 + kPath < n_walk) fetch(c0 + kPath);
+        __syncthreads();
+
+        // ---- Gram entries: wave 0 k . k, wave 1 k . q (16 rows of one 32x32 tile)
+        if (w < 2) {
+            f32x16 acc = {};
+            const uint16_t *br = (w == 0 ? L.k : L.q) + l32 * Q::KP;
+            const uint16_t *brl = (w == 0 ? L.klo : L.qlo) + l32 * Q::KP;
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s) {
+                const bf16x8 A = l32 < kPath ? frag_of(L.k + l32 * Q::KP, s, hf) : zero_frag();
+                const bf16x8 B = l32 < kPath ? frag_of(br, s, hf) : zero_frag();
+                if constexpr (F32) {
+                    const bf16x8 Al = l32 < kPath ? frag_of(L.klo + l32 * Q::KP, s, hf) : zero_frag();
+                    const bf16x8 Bl = l32 < kPath ? frag_of(brl, s, hf) : zero_frag();
+                    acc = mfma_split(A, Al, B, Bl, acc);
+                } else {
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc, 0, 0, 0);
+                }
+            }
+            // accumulator r < 8: (key e = 8(r/4) + 4*half + r%4, column p = l32)
+            if (l32 < kPath) {
+                float *dst = (w == 0 ? L.gram : L.gq) + l32 * Q::PS;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) dst[8 * (r / 4) + 4 * hf + (r % 4)] = acc[r];
+            }
+        }
+        __syncthreads();
+        // ---- per token p of the chunk: ratios and coefficients
+        const int f = fin ? flen - c0 : 0;  // the final state's token count inside this chunk, if in (0, len]
+        if (tid < kPath) {
+            const int p = tid;
+            const float bp = L.b[p];
+            float r = 1.0f;  // R(p, e), e from p - 1 down
+#pragma unroll
+            for (int e = kPath - 1; e >= 0; --e) {
+                float vl = 0.0f, vm = 0.0f;
+                if (e < p) {
+                    r *= L.a[e + 1];
+                    vl = bp * r * L.gram[p * Q::PS + e];
+                    vm = r * L.gq[p * Q::PS + e];
+                } else if (e == p) {
+                    vm = L.gq[p * Q::PS + p];
+                }
+                L.coefL[p * Q::PS + e] = vl;
+                L.coefM[p * Q::PS + e] = vm;
+            }
+            float gm = 1.0f, wr = 1.0f, wfr = 1.0f;
+#pragma unroll
+            for (int t = 0; t < kPath; ++t) {
+                if (t <= p) gm *= L.a[t];
+                if (t > p && t < len) wr *= L.a[t];
+                if (t > p && t < f) wfr *= L.a[t];
+            }
+            L.gaw[p] = make_float4(gm, bp * gm, bp, p < len ? wr : 0.0f);
+            L.wf[p] = p < f ? wfr : 0.0f;
+        }
+        __syncthreads();
+
+        // ---- X = S K^T and Y = S Q^T (k-step s: tile s/2, registers 8(s%2) .. +7)
+        f32x16 ax = {}, ay = {};
+        const uint16_t *krow = L.k + l32 * Q::KP, *qrow = L.q + l32 * Q::KP;
+        const uint16_t *klrow = L.klo + l32 * Q::KP, *qlrow = L.qlo + l32 * Q::KP;
+        auto row_frag = [&](const uint16_t *rowp, int t, int u) {
+            bf16x8 A = zero_frag();
+            if (l32 < kPath) {
+                const uint2 x0 = *reinterpret_cast<const uint2 *>(rowp + 32 * t + 16 * u + 4 * hf);
+                const uint2 x1 = *reinterpret_cast<const uint2 *>(rowp + 32 * t + 16 * u + 8 + 4 * hf);
+                A = __builtin_bit_cast(bf16x8, make_uint4(x0.x, x0.y, x1.x, x1.y));
+            }
+            return A;
+        };
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            const int t = s / 2, u = s % 2;
+            bf16x8 shi, slo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = S[t][8 * u + e];
+                const __bf16 hb = static_cast<__bf16>(x);
+                shi[e] = hb;
+                slo[e] = static_cast<__bf16>(x - static_cast<float>(hb));
+            }
+            const bf16x8 Ak = row_frag(krow, t, u), Aq = row_frag(qrow, t, u);
+            if constexpr (F32) {
+                ax = mfma_split(Ak, row_frag(klrow, t, u), shi, slo, ax);
+                if (want_out) ay = mfma_split(Aq, row_frag(qlrow, t, u), shi, slo, ay);
+            } else {
+                ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, shi, ax, 0, 0, 0);
+                ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, slo, ax, 0, 0, 0);
+                if (want_out) {
+                    ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, shi, ay, 0, 0, 0);
+                    ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, slo, ay, 0, 0, 0);
+                }
+            }
+        }
+        // x_e, y_e of this row: accumulator r < 8 holds e = 8(r/4) + 4*half + r%4, the
+        // other half-wave the rest
+        float x[kPath], y[kPath];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int e_mine = 8 * (r / 4) + (r % 4);  // + 4*half
+            const float mx = ax[r], ox = __shfl_xor(mx, 32);
+            const float my = ay[r], oy = __shfl_xor(my, 32);
+            x[e_mine] = hf ? ox : mx;
+            x[e_mine + 4] = hf ? mx : ox;
+            y[e_mine] = hf ? oy : my;
+            y[e_mine + 4] = hf ? my : oy;
+        }
+        // ---- c_p per row
+        float c[kPath];
+#pragma unroll
+        for (int p = 0; p < kPath; ++p) {
+            const float4 q4 = L.gaw[p];
+            float acc = fmaf(-q4.y, x[p], q4.z * L.v[p * D + row]);
+#pragma unroll
+            for (int e = 0; e < p; ++e) acc = fmaf(-L.coefL[p * Q::PS + e], c[e], acc);
+            c[p] = p < len ? acc : 0.0f;
+        }
+        // ---- outputs: half-wave 0 tokens 0..7, half-wave 1 tokens 8..15
+        if (want_out) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int p = 8 * hf + j;
+                float o = L.gaw[p].x * y[p];
+#pragma unroll
+                for (int e = 0; e < kPath; ++e)
+                    if (e <= p) o = fmaf(L.coefM[p * Q::PS + e], c[e], o);
+                if (p < len) P.out[((size_t)(lo + c0 + p) * P.Hv + h) * D + row] = o;
+            }
+        }
+        // ---- the state after f tokens of this chunk, and the state after the chunk
+        auto rank16 = [&](const float *wsrc, float gam, bool final_out) {
+            bf16x8 whi, wlo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float wc = (hf ? wsrc[8 + e] * c[8 + e] : wsrc[e] * c[e]);
+                const __bf16 hb = static_cast<__bf16>(wc);
+                whi[e] = hb;
+                wlo[e] = static_cast<__bf16>(wc - static_cast<float>(hb));
+            }
+#pragma unroll
+            for (int t = 0; t < NTILE; ++t) {
+                const bf16x8 A = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const uint4 *>(L.kt + (32 * t + l32) * Q::KT + 8 * hf));
+                f32x16 T = S[t];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) T[r] *= gam;
+                if constexpr (F32) {
+                    const bf16x8 Al = __builtin_bit_cast(
+                        bf16x8, *reinterpret_cast<const uint4 *>(L.ktlo + (32 * t + l32) * Q::KT + 8 * hf));
+                    T = mfma_split(A, Al, whi, wlo, T);
+                } else {
+                    T = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, whi, T, 0, 0, 0);
+                    T = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wlo, T, 0, 0, 0);
+                }
+                if (final_out) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<float4 *>(fin + s_lane + 32 * t + 8 * q) =
+                            make_float4(T[4 * q], T[4 * q + 1], T[4 * q + 2], T[4 * q + 3]);
+                } else {
+                    S[t] = T;
+                }
+            }
+        };
+        if (f > 0 && f <= len) rank16(L.wf, L.gaw[f - 1].x, true);
+        if (c0 + kPath < n_walk) {
+            float wv[kPath];
+#pragma unroll
+            for (int e = 0; e < kPath; ++e) wv[e] = L.gaw[e].w;
+            rank16(wv, L.gaw[len - 1].x, false);
+        }
+    }
+}
+
 template <typename K>
 hipError_t launch_with_lds(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, const Params &p) {
     if (lds > 65536) {
@@ -1901,6 +2272,16 @@ hipError_t launch_replay_d(const Params &p, bool chain, hipStream_t s) {
                  : launch_with_lds(replay_kernel<D, false, F32>, grid, block, ptab_bytes<D>(1, F32), s, p);
 }
 
+template <int D, bool F32>
+hipError_t launch_chunks_d(const Params &p, hipStream_t s) {
+    return launch_with_lds(chain_chunks_kernel<D, F32>, dim3(p.B * p.Hv), dim3(VG<D>::THREADS), cktab_bytes<D>(F32), s,
+                           p);
+}
+hipError_t chunks_any(const Params &p, hipStream_t s) {
+    if (p.f32_in) return p.D == 64 ? launch_chunks_d<64, true>(p, s) : launch_chunks_d<128, true>(p, s);
+    return p.D == 64 ? launch_chunks_d<64, false>(p, s) : launch_chunks_d<128, false>(p, s);
+}
+
 template <bool F32>
 hipError_t verify_any_d(const Params &p, bool chain, hipStream_t s) {
     return p.D == 64 ? launch_verify_d<64, F32>(p, chain, s) : launch_verify_d<128, F32>(p, chain, s);
@@ -1937,9 +2318,11 @@ hipError_t launch_persist_fast(const Params &p, hipStream_t s) {
 }
 // Chains of at most 16 nodes: outputs from the verify kernel in chain order
 // (so a chain-shaped tree and a chain give the same bits) and the final state
-// from the replay kernel (so persist and chain give the same bits).
+// from the replay kernel (so persist and chain give the same bits).  Longer
+// chains: the chunked chain kernel, state in registers across chunks.
 hipError_t launch_chain_verify_fast(const Params &p, hipStream_t s) {
     if (p.B == 0) return hipSuccess;
+    if (p.max_nodes > kPath) return chunks_any(p, s);
     hipError_t e = hipSuccess;
     if (p.out || p.has_ws) e = verify_any(p, true, s);
     if (e != hipSuccess) return e;

@@ -246,9 +246,11 @@ int gdn_tree_persist_copy(const gdn_dims *dims, const int32_t *accepted_node, co
  * a value outside [0, n_b] writes nothing).  state_cache is only read and
  * final_state must not overlap it.  `ws` (sized by gdn_workspace_bytes for
  * the same dims) receives the per-sequence verdicts for gdn_tree_status; it
- * is required when outputs are requested for bf16 inputs with head_dim 64 or
- * 128 and chains of at most GDN_MAX_DEPTH nodes (the kernels keep per-node
- * coefficients there), and may be NULL otherwise.  The call marks the
+ * is required when outputs are requested for inputs with head_dim 64 or 128
+ * and chains of at most GDN_MAX_DEPTH nodes (the kernels keep per-node
+ * coefficients there), and may be NULL otherwise.  Longer chains at head_dim
+ * 64 or 128 run in chunks of GDN_MAX_DEPTH tokens on the matrix cores, the
+ * state kept in registers from chunk to chunk.  The call marks the
  * workspace as a chain workspace: gdn_tree_status reads its verdicts, and the
  * tree calls reject it until gdn_tree_plan runs on it again.
  */
