@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--no-stress", action="store_true", help="skip the stress-workload sub-object")
     ap.add_argument("--stress-steps", type=int, default=10)
     ap.add_argument("--stress-warmup", type=int, default=3)
+    ap.add_argument("--seqs", type=int, default=0,
+                    help="run the workload with this many sequences (its own slots) instead of its own count")
     ap.add_argument("--stress-distinct", type=int, default=4,
                     help="independently generated layers of the stress sub-object (the rest are copies)")
     return ap.parse_args()
@@ -433,6 +435,9 @@ def main():
         sys.exit(1)
     G.load_library()
     cfg = W.get_config(args.config)
+    if args.seqs > 0:  # the same tree recipe at another batch size
+        import dataclasses
+        cfg = dataclasses.replace(cfg, num_seqs=args.seqs, num_slots=args.seqs)
     res, ctx = measure(G, W, cfg, args, args.steps, args.warmup, distinct=args.distinct, path_label=args.path)
     # calibration for memory-traffic counters: one plain device copy of a known size
     # (256 MiB read + 256 MiB written), outside the timed region
