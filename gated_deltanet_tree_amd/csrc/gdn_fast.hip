@@ -626,8 +626,8 @@ struct GPad {
 template <int D>
 struct GTab {
     uint16_t *kq;     // [2][32][KQ] keys / queries (bf16); fp32 inputs: their hi parts, then [2][32][KQ] lo parts
-    uint16_t *v;      // [32][grp][D] values of the group's heads (bf16), node-major as in memory
-    float *vf;        // the same for fp32 values
+    uint16_t *v;      // [32][grp][D] values of the group's heads (bf16), node-major as in memory;
+                      // fp32 values are not staged (each head reads its own from memory)
     float4 *gab;      // [grp][32] gamma, alpha, b
     uint16_t *mth, *mtl;  // [grp][32][MT] dense output operator, bf16 hi and lo parts
     float *coefL;     // [grp][32][PS]
@@ -640,8 +640,8 @@ struct GTab {
 template <int D>
 __host__ __device__ inline size_t gtab_bytes(int grp, bool f32 = false) {
     using Q = GPad<D>;
-    const size_t ew = f32 ? 4 : 2;  // bytes per value; fp32 keys/queries take two bf16 rows each
-    return (size_t)(f32 ? 4 : 2) * kTile * Q::KQ * 2 + (size_t)kTile * grp * D * ew + (size_t)grp * kTile * 16 +
+    const size_t vb = f32 ? 0 : (size_t)kTile * grp * D * 2;  // fp32 keys/queries take two bf16 rows each
+    return (size_t)(f32 ? 4 : 2) * kTile * Q::KQ * 2 + vb + (size_t)grp * kTile * 16 +
            (size_t)grp * kTile * Q::MT * 4 + (size_t)grp * kTile * Q::PS * 4 + 3 * kTile * Q::PS * 4 +
            2 * (size_t)grp * kTile * 4 + kTile * 4;
 }
@@ -651,8 +651,7 @@ __device__ inline GTab<D> gtab_carve(char *base, int grp, bool f32 = false) {
     using Q = GPad<D>;
     GTab<D> L;
     L.kq = reinterpret_cast<uint16_t *>(base);     base += (size_t)(f32 ? 4 : 2) * kTile * Q::KQ * 2;
-    L.v = reinterpret_cast<uint16_t *>(base);
-    L.vf = reinterpret_cast<float *>(base);        base += (size_t)kTile * grp * D * (f32 ? 4 : 2);
+    L.v = reinterpret_cast<uint16_t *>(base);      base += f32 ? 0 : (size_t)kTile * grp * D * 2;
     L.gab = reinterpret_cast<float4 *>(base);      base += (size_t)grp * kTile * 16;
     L.mth = reinterpret_cast<uint16_t *>(base);    base += (size_t)grp * kTile * Q::MT * 2;
     L.mtl = reinterpret_cast<uint16_t *>(base);    base += (size_t)grp * kTile * Q::MT * 2;
@@ -737,9 +736,10 @@ verify_group_kernel(Params P) {
     // values: node i's group heads are contiguous (grp*D values)
     const InT<F32> *vg = static_cast<const InT<F32> *>(P.v) + ((size_t)lo * P.Hv + h0) * D;
     const int vchunks = grp * D / EPC;  // 16-byte chunks per node
-    constexpr int V_PER = F32 ? (HPW * kTile * D / 4 + NT - 1) / NT : (kGroupMaxHeads * kTile * D / 8 + NT - 1) / NT;
+    // bf16 values are staged; fp32 values are read per head as it runs
+    constexpr int V_PER = F32 ? 0 : (kGroupMaxHeads * kTile * D / 8 + NT - 1) / NT;
     static_assert(kGroupMaxHeads * kTile <= NT, "one thread per (head, node) gate");
-    uint4 vv[V_PER];
+    uint4 vv[V_PER > 0 ? V_PER : 1];
 #pragma unroll
     for (int u = 0; u < V_PER; ++u) {
         const int idx = tid + u * NT;
@@ -884,6 +884,21 @@ verify_group_kernel(Params P) {
     __syncthreads();
 
     // ---- value heads: X, Y from the state and K/Q; outputs from X, Y and the coefficients
+    // fp32 values of head hh at this lane's row for the 16 nodes of its accumulator slots,
+    // through a buffer resource over the sequence's value rows: past the last node the
+    // hardware returns zero, so no load is guarded
+    auto load_vf = [&](int hh, float (&vf)[16]) {
+        if constexpr (F32) {
+            const __amdgpu_buffer_rsrc_t rv =
+                buffer_rsrc(reinterpret_cast<const float *>(vg) + (size_t)hh * D, (unsigned)(n * P.Hv * D) * 4u);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = 8 * (r / 4) + 4 * hf + (r % 4);
+                vf[r] = __uint_as_float(
+                    __builtin_amdgcn_raw_buffer_load_b32(rv, (unsigned)(i * P.Hv * D + row) * 4u, 0, 0));
+            }
+        }
+    };
     auto xy = [&](const float (&st)[KS][8], f32x16 &ax, f32x16 &ay) {
         ax = f32x16{};
         ay = f32x16{};
@@ -911,15 +926,14 @@ verify_group_kernel(Params P) {
             }
         }
     };
-    auto finish = [&](f32x16 ax, f32x16 ay, int hh) {
+    auto finish = [&](f32x16 ax, f32x16 ay, int hh, const float (&vf)[16]) {
         const float4 *gab = L.gab + hh * kTile;
         const uint16_t *vh = L.v + hh * D + row;
-        const float *vhf = L.vf + hh * D + row;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int i = 8 * (r / 4) + 4 * hf + (r % 4);
             const float4 q4 = gab[min(i, n - 1)];
-            const float vi = F32 ? vhf[i * grp * D] : bf2f(vh[i * grp * D]);
+            const float vi = F32 ? vf[r] : bf2f(vh[i * grp * D]);
             ax[r] = i < n ? fmaf(-q4.y, ax[r], q4.z * vi) : 0.0f;  // r = b v - alpha x
             ay[r] = i < n ? q4.x * ay[r] : 0.0f;                   // gamma y
         }
@@ -958,25 +972,30 @@ verify_group_kernel(Params P) {
         }
     };
     // each register set is refilled as soon as its products are taken
+    float vf[16];  // fp32 inputs: the running head's values
     f32x16 x0, y0;
+    load_vf(0, vf);
     xy(sA, x0, y0);
-    finish(x0, y0, 0);
+    finish(x0, y0, 0, vf);
     if (grp > 2) load_state_frags<D>(s0 + (size_t)2 * D * D, s_lane, sA);
     if (grp > 1) {
         f32x16 x1, y1;
+        load_vf(1, vf);
         xy(sB, x1, y1);
-        finish(x1, y1, 1);
+        finish(x1, y1, 1, vf);
         if (grp > 3) load_state_frags<D>(s0 + (size_t)3 * D * D, s_lane, sB);
     }
     if (grp > 2) {
         f32x16 x2, y2;
+        load_vf(2, vf);
         xy(sA, x2, y2);
-        finish(x2, y2, 2);
+        finish(x2, y2, 2, vf);
     }
     if (grp > 3) {
         f32x16 x3, y3;
+        load_vf(3, vf);
         xy(sB, x3, y3);
-        finish(x3, y3, 3);
+        finish(x3, y3, 3, vf);
     }
 }
 
