@@ -1805,20 +1805,23 @@ struct CkTab {
     uint16_t *klo, *ktlo, *qlo;  // fp32 inputs: lo parts, same layouts
     float *v;                    // [16][D] this head's values
     float *gram, *gq;            // [16][17]: row p, column e: k_e . k_p and k_e . q_p
-    float *coefL, *coefM;        // [16][17]: b_p R(p,e) (k_e . k_p) (e < p), R(p,e) (k_e . q_p) (e <= p)
+    float *coefL;                // [16][17]: b_p R(p,e) (k_e . k_p) (e < p)
+    float *coefM;                // [16][MS]: R(p,e) (k_e . q_p) (e <= p), rows 16-byte aligned
     float4 *gaw;                 // [16] G_p, b_p G_p, b_p, R(L-1, p)
     float *wf;                   // [16] R(f-1, p) for the final state f tokens into the chunk
     float *a, *b;                // [16]
     static constexpr int KP = D + 8;
     static constexpr int KT = kPath + 8;
     static constexpr int PS = kPath + 1;
+    static constexpr int MS = kPath + 4;
 };
 
 template <int D>
 __host__ __device__ inline size_t cktab_bytes(bool f32) {
     using Q = CkTab<D>;
     const size_t keys = (size_t)2 * kPath * Q::KP * 2 + (size_t)D * Q::KT * 2;
-    return keys * (f32 ? 2 : 1) + (size_t)kPath * D * 4 + 4 * (size_t)kPath * Q::PS * 4 + kPath * 16 + 3 * kPath * 4;
+    return keys * (f32 ? 2 : 1) + (size_t)kPath * D * 4 + 3 * (size_t)kPath * Q::PS * 4 + (size_t)kPath * Q::MS * 4 +
+           kPath * 16 + 3 * kPath * 4;
 }
 
 template <int D>
@@ -1838,10 +1841,10 @@ __device__ inline CkTab<D> cktab_carve(char *base, bool f32) {
         L.qlo = reinterpret_cast<uint16_t *>(base);  base += (size_t)kPath * Q::KP * 2;
         L.ktlo = reinterpret_cast<uint16_t *>(base); base += (size_t)D * Q::KT * 2;
     }
+    L.coefM = reinterpret_cast<float *>(base);     base += kPath * Q::MS * 4;
     L.gram = reinterpret_cast<float *>(base);      base += kPath * Q::PS * 4;
     L.gq = reinterpret_cast<float *>(base);        base += kPath * Q::PS * 4;
     L.coefL = reinterpret_cast<float *>(base);     base += kPath * Q::PS * 4;
-    L.coefM = reinterpret_cast<float *>(base);     base += kPath * Q::PS * 4;
     L.wf = reinterpret_cast<float *>(base);        base += kPath * 4;
     L.a = reinterpret_cast<float *>(base);         base += kPath * 4;
     L.b = reinterpret_cast<float *>(base);
@@ -1986,15 +1989,19 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         // ---- Gram entries: wave 0 k . k, wave 1 k . q (16 rows of one 32x32 tile)
         if (w < 2) {
             f32x16 acc = {};
-            const uint16_t *br = (w == 0 ? L.k : L.q) + l32 * Q::KP;
-            const uint16_t *brl = (w == 0 ? L.klo : L.qlo) + l32 * Q::KP;
+            // rows 16..31 of the tile read row 15 and are zeroed (no branch around the reads)
+            const int rl = min(l32, kPath - 1);
+            const bool live = l32 < kPath;
+            const uint16_t *br = (w == 0 ? L.k : L.q) + rl * Q::KP;
+            const uint16_t *brl = (w == 0 ? L.klo : L.qlo) + rl * Q::KP;
+            auto keep = [&](bf16x8 x) { return live ? x : zero_frag(); };
 #pragma unroll
             for (int s = 0; s < D / 16; ++s) {
-                const bf16x8 A = l32 < kPath ? frag_of(L.k + l32 * Q::KP, s, hf) : zero_frag();
-                const bf16x8 B = l32 < kPath ? frag_of(br, s, hf) : zero_frag();
+                const bf16x8 A = keep(frag_of(L.k + rl * Q::KP, s, hf));
+                const bf16x8 B = keep(frag_of(br, s, hf));
                 if constexpr (F32) {
-                    const bf16x8 Al = l32 < kPath ? frag_of(L.klo + l32 * Q::KP, s, hf) : zero_frag();
-                    const bf16x8 Bl = l32 < kPath ? frag_of(brl, s, hf) : zero_frag();
+                    const bf16x8 Al = keep(frag_of(L.klo + rl * Q::KP, s, hf));
+                    const bf16x8 Bl = keep(frag_of(brl, s, hf));
                     acc = mfma_split(A, Al, B, Bl, acc);
                 } else {
                     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc, 0, 0, 0);
@@ -2016,23 +2023,20 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
             float r = 1.0f;  // R(p, e), e from p - 1 down
 #pragma unroll
             for (int e = kPath - 1; e >= 0; --e) {
-                float vl = 0.0f, vm = 0.0f;
-                if (e < p) {
-                    r *= L.a[e + 1];
-                    vl = bp * r * L.gram[p * Q::PS + e];
-                    vm = r * L.gq[p * Q::PS + e];
-                } else if (e == p) {
-                    vm = L.gq[p * Q::PS + p];
-                }
-                L.coefL[p * Q::PS + e] = vl;
-                L.coefM[p * Q::PS + e] = vm;
+                const bool lt = e < p;
+                const float ae = L.a[min(e + 1, kPath - 1)];
+                const float gk = L.gram[p * Q::PS + e], gqe = L.gq[p * Q::PS + e];
+                r = lt ? r * ae : r;
+                L.coefL[p * Q::PS + e] = lt ? bp * r * gk : 0.0f;
+                L.coefM[p * Q::MS + e] = lt ? r * gqe : (e == p ? gqe : 0.0f);
             }
             float gm = 1.0f, wr = 1.0f, wfr = 1.0f;
 #pragma unroll
             for (int t = 0; t < kPath; ++t) {
-                if (t <= p) gm *= L.a[t];
-                if (t > p && t < len) wr *= L.a[t];
-                if (t > p && t < f) wfr *= L.a[t];
+                const float at = L.a[t];
+                gm = t <= p ? gm * at : gm;
+                wr = (t > p && t < len) ? wr * at : wr;
+                wfr = (t > p && t < f) ? wfr * at : wfr;
             }
             L.gaw[p] = make_float4(gm, bp * gm, bp, p < len ? wr : 0.0f);
             L.wf[p] = p < f ? wfr : 0.0f;
@@ -2041,16 +2045,15 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
 
         // ---- X = S K^T and Y = S Q^T (k-step s: tile s/2, registers 8(s%2) .. +7)
         f32x16 ax = {}, ay = {};
-        const uint16_t *krow = L.k + l32 * Q::KP, *qrow = L.q + l32 * Q::KP;
-        const uint16_t *klrow = L.klo + l32 * Q::KP, *qlrow = L.qlo + l32 * Q::KP;
+        const int rl = min(l32, kPath - 1);
+        const uint16_t *krow = L.k + rl * Q::KP, *qrow = L.q + rl * Q::KP;
+        const uint16_t *klrow = L.klo + rl * Q::KP, *qlrow = L.qlo + rl * Q::KP;
+        // rows past the chunk's 16 read row 15 and are zeroed (no branch around the reads)
         auto row_frag = [&](const uint16_t *rowp, int t, int u) {
-            bf16x8 A = zero_frag();
-            if (l32 < kPath) {
-                const uint2 x0 = *reinterpret_cast<const uint2 *>(rowp + 32 * t + 16 * u + 4 * hf);
-                const uint2 x1 = *reinterpret_cast<const uint2 *>(rowp + 32 * t + 16 * u + 8 + 4 * hf);
-                A = __builtin_bit_cast(bf16x8, make_uint4(x0.x, x0.y, x1.x, x1.y));
-            }
-            return A;
+            const uint2 x0 = *reinterpret_cast<const uint2 *>(rowp + 32 * t + 16 * u + 4 * hf);
+            const uint2 x1 = *reinterpret_cast<const uint2 *>(rowp + 32 * t + 16 * u + 8 + 4 * hf);
+            const bf16x8 A = __builtin_bit_cast(bf16x8, make_uint4(x0.x, x0.y, x1.x, x1.y));
+            return l32 < kPath ? A : zero_frag();
         };
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
@@ -2104,10 +2107,21 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int p = 8 * hf + j;
-                float o = L.gaw[p].x * y[p];
+                // this half-wave's token p: the terms e > p are selected away (their weights
+                // are zero; a select keeps a non-finite later c_e out of this output)
+                const float yp = hf ? y[8 + j] : y[j];
+                float o = L.gaw[p].x * yp;
+                const float4 *mrow = reinterpret_cast<const float4 *>(L.coefM + p * Q::MS);
 #pragma unroll
-                for (int e = 0; e < kPath; ++e)
-                    if (e <= p) o = fmaf(L.coefM[p * Q::PS + e], c[e], o);
+                for (int e4 = 0; e4 < kPath / 4; ++e4) {
+                    const float4 m4 = mrow[e4];
+                    const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int e = 4 * e4 + i;
+                        o = fmaf(e <= p ? mv[i] : 0.0f, e <= p ? c[e] : 0.0f, o);
+                    }
+                }
                 if (p < len) P.out[((size_t)(lo + c0 + p) * P.Hv + h) * D + row] = o;
             }
         }
