@@ -691,26 +691,31 @@ verify_group_kernel(Params P) {
     const int b = blockIdx.x / nhg, h0 = blockIdx.x % nhg * grp;
     const int g = h0 / (P.Hv / P.Hk);
     const SeqView sv = seq_view<CHAIN>(P, b);
-    if (!CHAIN && !ws_plan_matches(P)) return;
-    if (CHAIN && P.has_ws && h0 == 0 && tid == 0) {
-        if (b == 0) {
-            P.ws.header[0] = kChainMagic;
-            P.ws.header[1] = P.B;
-            P.ws.header[2] = P.T;
-            P.ws.header[kHdrMisuse] = 0;
-        }
-        P.ws.seq_status[b] = sv.status;
-    }
-    if (!P.out) return;
+    const bool planned = CHAIN || ws_plan_matches(P);
     const int lo = sv.lo, n = sv.n;
     // out[node][h0 + hh][row]: uniform base per (node, head) + this lane's offset
     const unsigned out_lane = (unsigned)(4 * hf * P.Hv * D + row);
-    if (sv.status != GDN_SEQ_OK) {
-        for (int t = tid; t < n * grp * D; t += NT)
-            P.out[((size_t)(lo + t / (grp * D)) * P.Hv + h0) * D + t % (grp * D)] = qnan_f();
-        return;
+    // a planned tree's common case is tested on the plan check and the sequence's record
+    // at once, so the two loads are issued together
+    if (CHAIN || !(planned & (sv.status == GDN_SEQ_OK) & (n > 0) & (P.out != nullptr))) {
+        if (!planned) return;
+        if (CHAIN && P.has_ws && h0 == 0 && tid == 0) {
+            if (b == 0) {
+                P.ws.header[0] = kChainMagic;
+                P.ws.header[1] = P.B;
+                P.ws.header[2] = P.T;
+                P.ws.header[kHdrMisuse] = 0;
+            }
+            P.ws.seq_status[b] = sv.status;
+        }
+        if (!P.out) return;
+        if (sv.status != GDN_SEQ_OK) {
+            for (int t = tid; t < n * grp * D; t += NT)
+                P.out[((size_t)(lo + t / (grp * D)) * P.Hv + h0) * D + t % (grp * D)] = qnan_f();
+            return;
+        }
+        if (n == 0) return;
     }
-    if (n == 0) return;
     using Q = GPad<D>;
     const GTab<D> L = gtab_carve<D>(lds_raw, grp, F32);
     const InT<F32> *kb = static_cast<const InT<F32> *>(P.k) + ((size_t)lo * P.Hk + g) * D;
@@ -1528,16 +1533,17 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         const bool planned = ws_plan_matches(P);
         const int4 info = *reinterpret_cast<const int4 *>(P.ws.seq_info + b * kSeqInfoInts);
         const int m = P.accepted[b];
-        if (!planned) {  // no slot is written; gdn_tree_status reports the misuse
-            if (blockIdx.x == 0 && tid == 0) P.ws.header[kHdrMisuse] = 1;
-            return;
+        // the common case is tested on all three loads at once, so they are issued together
+        // instead of each waiting for the test on the one before
+        if (!(planned & (info.z == GDN_SEQ_OK) & (m >= 0) & (m < info.y))) {
+            if (!planned) {  // no slot is written; gdn_tree_status reports the misuse
+                if (blockIdx.x == 0 && tid == 0) P.ws.header[kHdrMisuse] = 1;
+                return;
+            }
+            if (info.z != GDN_SEQ_OK || info.y == 0) return;
+            if ((m < -1 || m >= info.y) && g == 0 && tid == 0) P.ws.seq_status[b] = GDN_SEQ_BAD_ACCEPT;
+            return;  // a rejected accepted node, or m = -1: nothing to persist
         }
-        if (info.z != GDN_SEQ_OK || info.y == 0) return;
-        if (m < -1 || m >= info.y) {
-            if (g == 0 && tid == 0) P.ws.seq_status[b] = GDN_SEQ_BAD_ACCEPT;
-            return;
-        }
-        if (m == -1) return;
         lo = uni(info.x);
         slot = uni(info.w);
         const int mu = uni(m);
