@@ -1207,6 +1207,9 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         return frag_of(Lkq + (cap + min(jb * kTile + l32, n - 1)) * Q::KQ, s, hf);
     };
 
+    // a wave with no Gram block (w >= nb) issues its first-head state now
+    const bool early = w >= nb;
+    if (early) load_state_frags<D>(s0, s_lane, st);
     // ---- Gram entries: wave w takes the nodes of block w (column block tj = w) against
     // every block ti; node j's ancestor i, at path position depth(i) - 1, gets k_i . k_j
     // and k_i . q_j.  The ancestors of j are a bit mask over node ids, so a candidate
@@ -1261,7 +1264,7 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
     __syncthreads();
     // the first head's state streams in under the coefficients and back substitution
     // (issued earlier, it would have to share the registers of the Gram products)
-    load_state_frags<D>(s0, s_lane, st);
+    if (!early) load_state_frags<D>(s0, s_lane, st);
 
     // ---- per (head, node): ratios, coefficients, the output weights' right-hand sides
 #pragma unroll 1
