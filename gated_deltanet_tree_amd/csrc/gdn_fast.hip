@@ -805,21 +805,20 @@ verify_group_kernel(Params P) {
     if (grp > 1) load_state_frags<D>(s0 + (size_t)D * D, s_lane, sB);
     __syncthreads();
 
-    // ---- Gram entries of the block (one wave)
-    if (w == 0) {
-        f32x16 gkk = {}, gkq = {};
+    // ---- Gram entries of the block: wave 0 k . k, wave 1 k . q
+    if (w < 2) {
+        const int bro = w == 0 ? 0 : kTile;  // B operand rows: the keys or the queries
+        f32x16 gacc = {};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const bf16x8 A = frag_of(L.kq + l32 * Q::KQ, s, hf);
-            const bf16x8 Bq = frag_of(L.kq + (kTile + l32) * Q::KQ, s, hf);
+            const bf16x8 B = frag_of(L.kq + (bro + l32) * Q::KQ, s, hf);
             if constexpr (F32) {
                 const bf16x8 Al = frag_of(L.kq + (2 * kTile + l32) * Q::KQ, s, hf);
-                const bf16x8 Bql = frag_of(L.kq + (3 * kTile + l32) * Q::KQ, s, hf);
-                gkk = mfma_split(A, Al, A, Al, gkk);
-                gkq = mfma_split(A, Al, Bq, Bql, gkq);
+                const bf16x8 Bl = frag_of(L.kq + (2 * kTile + bro + l32) * Q::KQ, s, hf);
+                gacc = mfma_split(A, Al, B, Bl, gacc);
             } else {
-                gkk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, A, gkk, 0, 0, 0);
-                gkq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bq, gkq, 0, 0, 0);
+                gacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, gacc, 0, 0, 0);
             }
         }
         if (l32 < n) {  // accumulator r: (candidate ancestor il, node l32)
@@ -828,14 +827,11 @@ verify_group_kernel(Params P) {
 #pragma unroll
             for (int e = 0; e < kPath; ++e)
                 if (e < dl) mask |= 1u << (L.anc[l32 * Q::PS + e] & 31);
+            float *gdst = (w == 0 ? L.gk : L.gq) + l32 * Q::PS;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int il = 8 * (r / 4) + 4 * hf + (r % 4);
-                if ((mask >> il) & 1u) {
-                    const int e = L.depth[il] - 1;
-                    L.gk[l32 * Q::PS + e] = gkk[r];
-                    L.gq[l32 * Q::PS + e] = gkq[r];
-                }
+                if ((mask >> il) & 1u) gdst[L.depth[il] - 1] = gacc[r];
             }
         }
     }
