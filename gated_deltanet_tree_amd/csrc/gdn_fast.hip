@@ -1332,8 +1332,7 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
             }
         }
         __syncthreads();
-        // this head's state (the first head's is already in flight) and values
-        if (hh > 0) load_state_frags<D>(s0 + (size_t)hh * D * D, s_lane, st);
+        // this head's values (its state is already in flight)
         load_v(hh, n_h, lane_b >> 1);
         // Y_t = Q_t S0^T and X_j = K_j S0^T for every block, one product at a time (NB
         // independent MFMA chains each), the state split into bf16 hi + lo one k-step at a
@@ -1426,6 +1425,9 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
             // one output block's operator fragments live at a time
             __builtin_amdgcn_sched_barrier(0);
         }
+        // the next head's state: its registers, Y and R are all spent here, and it streams
+        // in under the next head's operator scatter
+        if (hh + 1 < grp) load_state_frags<D>(s0 + (size_t)(hh + 1) * D * D, s_lane, st);
     }
 }
 
