@@ -70,6 +70,9 @@ def parse():
                     help="run the workload with this many sequences (its own slots) instead of its own count")
     ap.add_argument("--stress-distinct", type=int, default=4,
                     help="independently generated layers of the stress sub-object (the rest are copies)")
+    ap.add_argument("--sweep", default="64,128,256",
+                    help="sequence counts of the batch sweep sub-object (the same tree recipe; empty: none)")
+    ap.add_argument("--sweep-steps", type=int, default=20)
     return ap.parse_args()
 
 
@@ -492,6 +495,26 @@ def main():
                                                 layer_calls=1, single_thread=False)
         del sctx
         result["stress"] = sres
+    # the same tree recipe at larger batches: where the fixed per-workgroup latencies
+    # are amortized, the layer call's share of peak bandwidth
+    sweep = [int(x) for x in args.sweep.split(",") if x.strip()] if cfg.name == "batched" and args.seqs <= 0 else []
+    if sweep:
+        import dataclasses
+        rows = []
+        for nseq in sweep:
+            torch.cuda.empty_cache()
+            bcfg = dataclasses.replace(cfg, num_seqs=nseq, num_slots=nseq)
+            bres, bctx = measure(G, W, bcfg, args, args.sweep_steps, 3, distinct=2, path_label=args.path)
+            lc = bres["layer_call"]
+            rows.append({"sequences": nseq, "nodes": bres["config"]["nodes"], "verify_us": lc["verify_us"],
+                         "persist_us": lc["persist_us"], "verify_frac": lc["verify_gbs"] / HBM_PEAK_GBS,
+                         "persist_frac": lc["persist_gbs"] / HBM_PEAK_GBS, "hbm_gbs": lc["hbm_gbs"],
+                         "hbm_frac": lc["hbm_frac"], "layer_call_nodes_per_s": lc["nodes_per_s"],
+                         "step_nodes_per_s": bres["value"], "rotated_copies": bres["config"]["rotated_copies"]})
+            del bctx
+        result["batch_sweep"] = {"recipe": "the %s workload's trees and heads at other sequence counts" % cfg.name,
+                                 "timing": "graph replay of each call alone over the rotation (mean)",
+                                 "rows": rows}
     if not args.no_cpu_baseline:
         trees, cu, acc = W.make_trees(cfg), None, None
         cu = W.cu_from_trees(trees)
