@@ -828,10 +828,17 @@ verify_group_kernel(Params P) {
             for (int e = 0; e < kPath; ++e)
                 if (e < dl) mask |= 1u << (L.anc[l32 * Q::PS + e] & 31);
             float *gdst = (w == 0 ? L.gk : L.gq) + l32 * Q::PS;
+            // the candidates' depths four at a time, all read before any write; a candidate that
+            // is not an ancestor writes to the row's pad column, which nothing reads
+            int4 dq[4];
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) dq[g4] = *reinterpret_cast<const int4 *>(L.depth + 8 * g4 + 4 * hf);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int il = 8 * (r / 4) + 4 * hf + (r % 4);
-                if ((mask >> il) & 1u) gdst[L.depth[il] - 1] = gacc[r];
+                const int4 q4 = dq[r / 4];
+                const int dep = r % 4 == 0 ? q4.x : r % 4 == 1 ? q4.y : r % 4 == 2 ? q4.z : q4.w;
+                gdst[((mask >> il) & 1u) ? dep - 1 : kPath] = gacc[r];
             }
         }
     }
@@ -846,17 +853,24 @@ verify_group_kernel(Params P) {
     if (act) {
         d_t = L.depth[i_t];
         const float bi = L.b[hh_t * kTile + i_t];
-        float av[kPath];
+        // every table entry of the row, read before the first result is written (the writes
+        // would otherwise order each step's reads behind the previous step's)
+        float av[kPath], gk[kPath], gq[kPath];
 #pragma unroll
         for (int e = 0; e < kPath; ++e) an_t[e] = max(L.anc[i_t * Q::PS + e], 0);
 #pragma unroll
-        for (int e = 0; e < kPath; ++e) av[e] = e < d_t ? L.a[hh_t * kTile + an_t[e]] : 1.0f;
+        for (int e = 0; e < kPath; ++e) {
+            const float ae = L.a[hh_t * kTile + an_t[e]];
+            av[e] = e < d_t ? ae : 1.0f;
+            gk[e] = L.gk[i_t * Q::PS + e];
+            gq[e] = L.gq[i_t * Q::PS + e];
+        }
         float r = 1.0f;
 #pragma unroll
         for (int e = kPath - 1; e >= 0; --e) {
             const bool on = e < d_t - 1;
-            L.coefL[(hh_t * kTile + i_t) * Q::PS + e] = on ? bi * r * L.gk[i_t * Q::PS + e] : 0.0f;
-            mrow[e] = on ? r * L.gq[i_t * Q::PS + e] : (e == d_t - 1 ? L.gq[i_t * Q::PS + e] : 0.0f);
+            L.coefL[(hh_t * kTile + i_t) * Q::PS + e] = on ? bi * r * gk[e] : 0.0f;
+            mrow[e] = on ? r * gq[e] : (e == d_t - 1 ? gq[e] : 0.0f);
             r *= av[e];
         }
         L.gab[hh_t * kTile + i_t] = make_float4(r, bi * r, bi, 0.0f);
@@ -1047,7 +1061,8 @@ __host__ __device__ inline BLayout blocks_layout(int cap, int grp) {
     L.gab = off;   off += (size_t)grp * c * 16;
     L.ysp = off;   off += (size_t)grp * c * kPath * 4;
     L.anc = off;   off += c * Q::PS * 4;
-    L.depth = off; off += c * 4;
+    off = (off + 15) & ~size_t(15);
+    L.depth = off; off += (c + kTile - 1) / kTile * kTile * 4;  // whole node blocks, read four at a time
     off = (off + 15) & ~size_t(15);
     // the coefficient phase's tables and the output operator share one region
     L.gk = off;
@@ -1245,11 +1260,21 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         if (j < n) {
 #pragma unroll
             for (int ti = 0; ti < NB; ++ti) {
+                if (ti < nb) {
+                    // the depths of the lane's 16 candidates ti * 32 + il, four consecutive nodes
+                    // per read, all read before any write; a candidate that is not an ancestor
+                    // writes to the row's pad column, which nothing reads, so no write waits on a
+                    // branch (past the last node the depths are never used)
+                    int4 dq[4];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int il = 8 * (r / 4) + 4 * hf + (r % 4);  // candidate ti * 32 + il
-                    if (ti < nb && ((amask[ti] >> il) & 1u)) {
-                        const int e = Ldepth[ti * kTile + il] - 1;
+                    for (int g4 = 0; g4 < 4; ++g4)
+                        dq[g4] = *reinterpret_cast<const int4 *>(Ldepth + ti * kTile + 8 * g4 + 4 * hf);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int il = 8 * (r / 4) + 4 * hf + (r % 4);
+                        const int4 q4 = dq[r / 4];
+                        const int dep = r % 4 == 0 ? q4.x : r % 4 == 1 ? q4.y : r % 4 == 2 ? q4.z : q4.w;
+                        const int e = ((amask[ti] >> il) & 1u) ? dep - 1 : kPath;
                         Lgk[j * Q::PS + e] = gkk[ti][r];
                         Lgq[j * Q::PS + e] = gkq[ti][r];
                     }
@@ -1268,13 +1293,22 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         const int hh = t / n, i = t % n;
         const int di = Ldepth[i];
         const float bi = Lb[hh * cap + i];
+        // every table entry of the row, read before the first result is written (the writes
+        // would otherwise order each step's reads behind the previous step's)
+        float gk[kPath], gq[kPath], av[kPath];
+#pragma unroll
+        for (int e = 0; e < kPath; ++e) {
+            gk[e] = Lgk[i * Q::PS + e];
+            gq[e] = Lgq[i * Q::PS + e];
+            av[e] = La[hh * cap + max(Lanc[i * Q::PS + e], 0)];
+        }
         float r = 1.0f;
 #pragma unroll
         for (int e = kPath - 1; e >= 0; --e) {
             const bool on = e < di - 1;
-            LcoefL[(hh * cap + i) * Q::PS + e] = on ? bi * r * Lgk[i * Q::PS + e] : 0.0f;
-            Lysp[(hh * cap + i) * kPath + e] = on ? r * Lgq[i * Q::PS + e] : (e == di - 1 ? Lgq[i * Q::PS + e] : 0.0f);
-            if (e < di) r *= La[hh * cap + max(Lanc[i * Q::PS + e], 0)];
+            LcoefL[(hh * cap + i) * Q::PS + e] = on ? bi * r * gk[e] : 0.0f;
+            Lysp[(hh * cap + i) * kPath + e] = on ? r * gq[e] : (e == di - 1 ? gq[e] : 0.0f);
+            if (e < di) r *= av[e];
         }
         Lgab[hh * cap + i] = make_float4(r, bi * r, bi, 0.0f);
     }
