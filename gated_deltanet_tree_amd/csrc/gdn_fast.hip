@@ -158,7 +158,7 @@ constexpr int kCoefMaxHeadsPerPass = 8;
 
 struct CTab {
     int *anc;        // [cap][16]
-    int *depth;      // [cap]
+    int *depth;      // [cap rounded up to whole node blocks]
     uint32_t *amask; // [cap][kMaskWords]
     float *gk, *gq;  // [cap][16] path-indexed Gram entries
     float *a, *b;    // [grp][cap]
@@ -167,7 +167,8 @@ struct CTab {
 
 __host__ __device__ inline size_t ctab_bytes(int cap, int grp, int hpp) {
     const size_t c = (size_t)cap;
-    return c * kPath * 4 + c * 4 + c * kMaskWords * 4 + 2 * c * kPath * 4 + 2 * (size_t)grp * c * 4 +
+    const size_t depth = (c + kTile - 1) / kTile * kTile;  // whole node blocks, read four at a time
+    return c * kPath * 4 + depth * 4 + c * kMaskWords * 4 + 2 * c * kPath * 4 + 2 * (size_t)grp * c * 4 +
            (size_t)hpp * c * kPath * 4;
 }
 
@@ -187,7 +188,7 @@ __device__ inline CTab ctab_carve(char *base, int cap, int grp, int hpp) {
     L.gq = reinterpret_cast<float *>(base);       base += c * kPath * 4;
     L.coefL = reinterpret_cast<float *>(base);    base += (size_t)hpp * c * kPath * 4;
     L.amask = reinterpret_cast<uint32_t *>(base); base += c * kMaskWords * 4;
-    L.depth = reinterpret_cast<int *>(base);      base += c * 4;
+    L.depth = reinterpret_cast<int *>(base);      base += (c + kTile - 1) / kTile * kTile * 4;
     L.a = reinterpret_cast<float *>(base);        base += (size_t)grp * c * 4;
     L.b = reinterpret_cast<float *>(base);
     return L;
@@ -266,13 +267,19 @@ __global__ __launch_bounds__(kCoefThreads) void coef_kernel(Params P) {
         }
         if (pj < n) {  // accumulator r: (candidate ancestor ti*32 + il, node pj)
             const uint32_t mask = L.amask[pj * kMaskWords + ti];
+            // the candidates' depths four at a time, read before any write (past the last node
+            // the depths are never used)
+            int4 dq[4];
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) dq[g4] = *reinterpret_cast<const int4 *>(L.depth + ti * kTile + 8 * g4 + 4 * hf);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int il = 8 * (r / 4) + 4 * hf + (r % 4);
+                const int4 q4 = dq[r / 4];
+                const int dep = r % 4 == 0 ? q4.x : r % 4 == 1 ? q4.y : r % 4 == 2 ? q4.z : q4.w;
                 if ((mask >> il) & 1u) {
-                    const int e = L.depth[ti * kTile + il] - 1;
-                    L.gk[pj * kPath + e] = gkk[r];
-                    L.gq[pj * kPath + e] = gkq[r];
+                    L.gk[pj * kPath + dep - 1] = gkk[r];
+                    L.gq[pj * kPath + dep - 1] = gkq[r];
                 }
             }
         }
@@ -288,17 +295,23 @@ __global__ __launch_bounds__(kCoefThreads) void coef_kernel(Params P) {
         if (act) {
             d = L.depth[i];
             bi = L.b[hh * cap + i];
-            float av[kPath];
+            // every table entry of the row, read before the first coefficient is written
+            float av[kPath], gk[kPath], gq[kPath];
 #pragma unroll
             for (int e = 0; e < kPath; ++e) an[e] = L.anc[i * kPath + e];
 #pragma unroll
-            for (int e = 0; e < kPath; ++e) av[e] = e < d ? L.a[hh * cap + an[e]] : 1.0f;
+            for (int e = 0; e < kPath; ++e) {
+                const float ae = L.a[hh * cap + max(an[e], 0)];
+                av[e] = e < d ? ae : 1.0f;
+                gk[e] = L.gk[i * kPath + e];
+                gq[e] = L.gq[i * kPath + e];
+            }
             float r = 1.0f;
 #pragma unroll
             for (int e = kPath - 1; e >= 0; --e) {
                 const bool on = e < d - 1;
-                L.coefL[(slot_h * cap + i) * kPath + e] = on ? bi * r * L.gk[i * kPath + e] : 0.0f;
-                mrow[e] = on ? r * L.gq[i * kPath + e] : (e == d - 1 ? L.gq[i * kPath + e] : 0.0f);
+                L.coefL[(slot_h * cap + i) * kPath + e] = on ? bi * r * gk[e] : 0.0f;
+                mrow[e] = on ? r * gq[e] : (e == d - 1 ? gq[e] : 0.0f);
                 r *= av[e];
             }
             gamma = r;
@@ -1708,21 +1721,28 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         const int hh = tid / kPath, p = tid % kPath;
         const float *ah = L.a + hh * kPath;
         const float bp = L.b[tid];
+        // the gates and the row's Gram entries, read before the first coefficient is written
+        float av[kPath], gr[kPath];
+#pragma unroll
+        for (int e = 0; e < kPath; ++e) {
+            av[e] = ah[e];
+            gr[e] = L.gram[p * (kPath + 1) + e];
+        }
         float r = 1.0f;  // R(p, e), e from p-1 down
 #pragma unroll
         for (int e = kPath - 1; e >= 0; --e) {
             float v = 0.0f;
             if (e < p) {
-                r *= ah[e + 1];
-                v = p < len ? bp * r * L.gram[p * (kPath + 1) + e] : 0.0f;
+                r *= av[min(e + 1, kPath - 1)];
+                v = p < len ? bp * r * gr[e] : 0.0f;
             }
             L.coefL[(hh * kPath + p) * (kPath + 1) + e] = v;
         }
         float gm = 1.0f, wr = 1.0f;
 #pragma unroll
         for (int t = 0; t < kPath; ++t) {
-            if (t <= p) gm *= ah[t];
-            if (t > p && t < len) wr *= ah[t];
+            if (t <= p) gm *= av[t];
+            if (t > p && t < len) wr *= av[t];
         }
         L.gaw[tid] = make_float4(gm, bp * gm, bp, p < len ? wr : 0.0f);
     }
@@ -2061,12 +2081,21 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         if (tid < kPath) {
             const int p = tid;
             const float bp = L.b[p];
+            // the gates and the row's Gram entries, read before the first coefficient is
+            // written (the writes would otherwise order each step's reads behind the last's)
+            float av[kPath], gkr[kPath], gqr[kPath];
+#pragma unroll
+            for (int e = 0; e < kPath; ++e) {
+                av[e] = L.a[e];
+                gkr[e] = L.gram[p * Q::PS + e];
+                gqr[e] = L.gq[p * Q::PS + e];
+            }
             float r = 1.0f;  // R(p, e), e from p - 1 down
 #pragma unroll
             for (int e = kPath - 1; e >= 0; --e) {
                 const bool lt = e < p;
-                const float ae = L.a[min(e + 1, kPath - 1)];
-                const float gk = L.gram[p * Q::PS + e], gqe = L.gq[p * Q::PS + e];
+                const float ae = av[min(e + 1, kPath - 1)];
+                const float gk = gkr[e], gqe = gqr[e];
                 r = lt ? r * ae : r;
                 L.coefL[p * Q::PS + e] = lt ? bp * r * gk : 0.0f;
                 L.coefM[p * Q::MS + e] = lt ? r * gqe : (e == p ? gqe : 0.0f);
@@ -2074,7 +2103,7 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
             float gm = 1.0f, wr = 1.0f, wfr = 1.0f;
 #pragma unroll
             for (int t = 0; t < kPath; ++t) {
-                const float at = L.a[t];
+                const float at = av[t];
                 gm = t <= p ? gm * at : gm;
                 wr = (t > p && t < len) ? wr * at : wr;
                 wfr = (t > p && t < f) ? wfr * at : wfr;
