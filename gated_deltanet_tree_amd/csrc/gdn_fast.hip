@@ -561,13 +561,20 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
                     ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, slo[s], ax, 0, 0, 0);
                 }
             }
+            // the gates of the lane's 16 nodes are read before any r row is written (a read under
+            // the store's branch would wait for its data once per node)
+            float gy[16], gz[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float4 gabd = L.gabd[min(t * kTile + 8 * (r / 4) + 4 * hf + (r % 4), n - 1)];
+                gy[r] = gabd.y;
+                gz[r] = gabd.z;
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int i = t * kTile + 8 * (r / 4) + 4 * hf + (r % 4);
-                if (i < n) {
-                    const float4 gabd = L.gabd[i];
-                    L.rbuf[(size_t)i * D + row] = fmaf(-gabd.y, ax[r], gabd.z * in2f(vraw[r]));
-                }
+                const float rv = fmaf(-gy[r], ax[r], gz[r] * in2f(vraw[r]));
+                if (i < n) L.rbuf[(size_t)i * D + row] = rv;
             }
         }
     }
@@ -835,11 +842,14 @@ verify_group_kernel(Params P) {
             }
         }
         if (l32 < n) {  // accumulator r: (candidate ancestor il, node l32)
-            const int dl = L.depth[l32];
-            uint32_t mask = 0u;  // ancestors of node l32 within the block
+            // ancestors of node l32 within the block: its path entries (-1 past its depth), all
+            // read before any is tested, so no read waits under a branch
+            int anl[kPath];
 #pragma unroll
-            for (int e = 0; e < kPath; ++e)
-                if (e < dl) mask |= 1u << (L.anc[l32 * Q::PS + e] & 31);
+            for (int e = 0; e < kPath; ++e) anl[e] = L.anc[l32 * Q::PS + e];
+            uint32_t mask = 0u;
+#pragma unroll
+            for (int e = 0; e < kPath; ++e) mask |= anl[e] >= 0 ? 1u << (anl[e] & 31) : 0u;
             float *gdst = (w == 0 ? L.gk : L.gq) + l32 * Q::PS;
             // the candidates' depths four at a time, all read before any write; a candidate that
             // is not an ancestor writes to the row's pad column, which nothing reads
