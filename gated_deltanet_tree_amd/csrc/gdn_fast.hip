@@ -623,15 +623,15 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
 // ===========================================================================
 // Verify for trees of at most 32 nodes: one workgroup per (sequence, group of
 // HPW value heads of one key head), D/32 waves; HPW is all of the key head's
-// value heads, or one when a small batch leaves room for a workgroup per head.  One round trip brings the keys,
-// queries, values, gates and paths into LDS; the first two heads' states are
-// issued as soon as those have landed (issued with them they would queue ahead
-// of them).  While the states arrive the workgroup forms the coefficients once
-// for all its heads (the Gram entries are shared through the key head); then
-// each head's products are taken as its state lands, and a register set takes
-// the next head's state as soon as its products are done.  No barrier after
-// the coefficients.  Same algebra as the two-kernel path (coef_kernel +
-// verify_kernel).
+// value heads, or one when a small batch leaves room for a workgroup per head.
+// One round trip brings the keys, queries, values, gates and paths into LDS.
+// Then wave 0 alone forms the coefficients once for all the heads (the Gram
+// entries are shared through the key head), with no barrier inside that phase,
+// while the other waves issue their first two heads' states; wave 0 issues its
+// own after one barrier that publishes the output operator.  Each head's
+// products are taken as its state lands, and a register set takes the next
+// head's state as soon as its products are done.  Same algebra as the
+// two-kernel path (coef_kernel + verify_kernel).
 // ===========================================================================
 constexpr int kGroupMaxHeads = 4;  // value heads per key head this kernel takes
 
@@ -818,108 +818,136 @@ verify_group_kernel(Params P) {
         reinterpret_cast<uint32_t *>(L.mth)[idx] = 0u;
         reinterpret_cast<uint32_t *>(L.mtl)[idx] = 0u;
     }
-    // the states go out only now: issued together with the small loads above they would queue
-    // ahead of them and hold back the coefficients, which gate every output
     float sA[KS][8], sB[KS][8];
-    load_state_frags<D>(s0, s_lane, sA);
-    if (grp > 1) load_state_frags<D>(s0 + (size_t)D * D, s_lane, sB);
-    __syncthreads();
+    __syncthreads();  // the tables are in LDS
 
-    // ---- Gram entries of the block: wave 0 k . k, wave 1 k . q
-    if (w < 2) {
-        const int bro = w == 0 ? 0 : kTile;  // B operand rows: the keys or the queries
-        f32x16 gacc = {};
+    // ---- the coefficient phase runs on wave 0 alone, with no barrier inside it, while the
+    // other waves issue their first two heads' states.  A wave that issues loads into a
+    // saturated memory system stalls until they are taken; with a barrier inside the phase
+    // every such stall would hold back the coefficients, which gate every output.  Wave 0
+    // issues its own states once the phase is done.
+    if (uni(w) == 0) {
+        // Gram entries of the block: k . k, then k . q
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const bf16x8 A = frag_of(L.kq + l32 * Q::KQ, s, hf);
-            const bf16x8 B = frag_of(L.kq + (bro + l32) * Q::KQ, s, hf);
-            if constexpr (F32) {
-                const bf16x8 Al = frag_of(L.kq + (2 * kTile + l32) * Q::KQ, s, hf);
-                const bf16x8 Bl = frag_of(L.kq + (2 * kTile + bro + l32) * Q::KQ, s, hf);
-                gacc = mfma_split(A, Al, B, Bl, gacc);
-            } else {
-                gacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, gacc, 0, 0, 0);
+        for (int which = 0; which < 2; ++which) {
+            const int bro = which == 0 ? 0 : kTile;  // B operand rows: the keys or the queries
+            f32x16 gacc = {};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const bf16x8 A = frag_of(L.kq + l32 * Q::KQ, s, hf);
+                const bf16x8 B = frag_of(L.kq + (bro + l32) * Q::KQ, s, hf);
+                if constexpr (F32) {
+                    const bf16x8 Al = frag_of(L.kq + (2 * kTile + l32) * Q::KQ, s, hf);
+                    const bf16x8 Bl = frag_of(L.kq + (2 * kTile + bro + l32) * Q::KQ, s, hf);
+                    gacc = mfma_split(A, Al, B, Bl, gacc);
+                } else {
+                    gacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, gacc, 0, 0, 0);
+                }
+            }
+            if (l32 < n) {  // accumulator r: (candidate ancestor il, node l32)
+                // ancestors of node l32 within the block: its path entries (-1 past its depth),
+                // all read before any is tested, so no read waits under a branch
+                int anl[kPath];
+#pragma unroll
+                for (int e = 0; e < kPath; ++e) anl[e] = L.anc[l32 * Q::PS + e];
+                uint32_t mask = 0u;
+#pragma unroll
+                for (int e = 0; e < kPath; ++e) mask |= anl[e] >= 0 ? 1u << (anl[e] & 31) : 0u;
+                float *gdst = (which == 0 ? L.gk : L.gq) + l32 * Q::PS;
+                // the candidates' depths four at a time, all read before any write; a candidate
+                // that is not an ancestor writes to the row's pad column, which nothing reads
+                int4 dq[4];
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4)
+                    dq[g4] = *reinterpret_cast<const int4 *>(L.depth + 8 * g4 + 4 * hf);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int il = 8 * (r / 4) + 4 * hf + (r % 4);
+                    const int4 q4 = dq[r / 4];
+                    const int dep = r % 4 == 0 ? q4.x : r % 4 == 1 ? q4.y : r % 4 == 2 ? q4.z : q4.w;
+                    gdst[((mask >> il) & 1u) ? dep - 1 : kPath] = gacc[r];
+                }
             }
         }
-        if (l32 < n) {  // accumulator r: (candidate ancestor il, node l32)
-            // ancestors of node l32 within the block: its path entries (-1 past its depth), all
-            // read before any is tested, so no read waits under a branch
-            int anl[kPath];
-#pragma unroll
-            for (int e = 0; e < kPath; ++e) anl[e] = L.anc[l32 * Q::PS + e];
-            uint32_t mask = 0u;
-#pragma unroll
-            for (int e = 0; e < kPath; ++e) mask |= anl[e] >= 0 ? 1u << (anl[e] & 31) : 0u;
-            float *gdst = (w == 0 ? L.gk : L.gq) + l32 * Q::PS;
-            // the candidates' depths four at a time, all read before any write; a candidate that
-            // is not an ancestor writes to the row's pad column, which nothing reads
-            int4 dq[4];
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) dq[g4] = *reinterpret_cast<const int4 *>(L.depth + 8 * g4 + 4 * hf);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int il = 8 * (r / 4) + 4 * hf + (r % 4);
-                const int4 q4 = dq[r / 4];
-                const int dep = r % 4 == 0 ? q4.x : r % 4 == 1 ? q4.y : r % 4 == 2 ? q4.z : q4.w;
-                gdst[((mask >> il) & 1u) ? dep - 1 : kPath] = gacc[r];
-            }
-        }
-    }
-    __syncthreads();
+        // one wave's LDS accesses take effect in program order: only the compiler must keep them
+        __builtin_amdgcn_wave_barrier();
 
-    // ---- per (value head, node): ratios, coefficients, output weights
-    const bool act = tid < grp * n;
-    const int hh_t = act ? tid / n : 0, i_t = act ? tid % n : 0;
-    float mrow[kPath];
-    int an_t[kPath];
-    int d_t = 0;
-    if (act) {
-        d_t = L.depth[i_t];
-        const float bi = L.b[hh_t * kTile + i_t];
-        // every table entry of the row, read before the first result is written (the writes
-        // would otherwise order each step's reads behind the previous step's)
-        float av[kPath], gk[kPath], gq[kPath];
+        // per (value head, node) pair, lane and lane + 64: ratios, coefficients, output weights
+        constexpr int RND = (kGroupMaxHeads * kTile + 63) / 64;
+        float mrow[RND][kPath];
+        int an_t[RND][kPath];
+        int d_t[RND], hh_t[RND], i_t[RND];
+        bool act[RND];
 #pragma unroll
-        for (int e = 0; e < kPath; ++e) an_t[e] = max(L.anc[i_t * Q::PS + e], 0);
+        for (int rd = 0; rd < RND; ++rd) {
+            const int pr = lane + 64 * rd;
+            act[rd] = pr < grp * n;
+            hh_t[rd] = act[rd] ? pr / n : 0;
+            i_t[rd] = act[rd] ? pr % n : 0;
+            d_t[rd] = 0;
+            if (act[rd]) {
+                const int hh = hh_t[rd], i = i_t[rd];
+                const int di = L.depth[i];
+                d_t[rd] = di;
+                const float bi = L.b[hh * kTile + i];
+                // every table entry of the row, read before the first result is written (the
+                // writes would otherwise order each step's reads behind the previous step's)
+                float av[kPath], gk[kPath], gq[kPath];
 #pragma unroll
-        for (int e = 0; e < kPath; ++e) {
-            const float ae = L.a[hh_t * kTile + an_t[e]];
-            av[e] = e < d_t ? ae : 1.0f;
-            gk[e] = L.gk[i_t * Q::PS + e];
-            gq[e] = L.gq[i_t * Q::PS + e];
-        }
-        float r = 1.0f;
+                for (int e = 0; e < kPath; ++e) an_t[rd][e] = max(L.anc[i * Q::PS + e], 0);
 #pragma unroll
-        for (int e = kPath - 1; e >= 0; --e) {
-            const bool on = e < d_t - 1;
-            L.coefL[(hh_t * kTile + i_t) * Q::PS + e] = on ? bi * r * gk[e] : 0.0f;
-            mrow[e] = on ? r * gq[e] : (e == d_t - 1 ? gq[e] : 0.0f);
-            r *= av[e];
-        }
-        L.gab[hh_t * kTile + i_t] = make_float4(r, bi * r, bi, 0.0f);
-    }
-    __syncthreads();
-    if (act) {
-        float y[kPath];
+                for (int e = 0; e < kPath; ++e) {
+                    const float ae = L.a[hh * kTile + an_t[rd][e]];
+                    av[e] = e < di ? ae : 1.0f;
+                    gk[e] = L.gk[i * Q::PS + e];
+                    gq[e] = L.gq[i * Q::PS + e];
+                }
+                float r = 1.0f;
 #pragma unroll
-        for (int e = kPath - 1; e >= 0; --e) {
-            float acc = mrow[e];
-            // deepest terms first: y_{e+1}, the last one known, enters last
-#pragma unroll
-            for (int f = kPath - 1; f > e; --f)
-                acc = fmaf(-y[f], L.coefL[(hh_t * kTile + an_t[f]) * Q::PS + e], acc);
-            y[e] = e < d_t ? acc : 0.0f;
-        }
-        uint16_t *mh = L.mth + (hh_t * kTile + i_t) * Q::MT, *ml = L.mtl + (hh_t * kTile + i_t) * Q::MT;
-#pragma unroll
-        for (int e = 0; e < kPath; ++e)
-            if (e < d_t) {  // stored as bf16 hi + lo for the matrix cores
-                const __bf16 yh = static_cast<__bf16>(y[e]);
-                mh[an_t[e]] = __builtin_bit_cast(uint16_t, yh);
-                ml[an_t[e]] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(y[e] - static_cast<float>(yh)));
+                for (int e = kPath - 1; e >= 0; --e) {
+                    const bool on = e < di - 1;
+                    L.coefL[(hh * kTile + i) * Q::PS + e] = on ? bi * r * gk[e] : 0.0f;
+                    mrow[rd][e] = on ? r * gq[e] : (e == di - 1 ? gq[e] : 0.0f);
+                    r *= av[e];
+                }
+                L.gab[hh * kTile + i] = make_float4(r, bi * r, bi, 0.0f);
             }
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int rd = 0; rd < RND; ++rd) {
+            if (act[rd]) {
+                const int hh = hh_t[rd], i = i_t[rd];
+                float y[kPath];
+#pragma unroll
+                for (int e = kPath - 1; e >= 0; --e) {
+                    float acc = mrow[rd][e];
+                    // deepest terms first: y_{e+1}, the last one known, enters last
+#pragma unroll
+                    for (int f = kPath - 1; f > e; --f)
+                        acc = fmaf(-y[f], L.coefL[(hh * kTile + an_t[rd][f]) * Q::PS + e], acc);
+                    y[e] = e < d_t[rd] ? acc : 0.0f;
+                }
+                uint16_t *mh = L.mth + (hh * kTile + i) * Q::MT, *ml = L.mtl + (hh * kTile + i) * Q::MT;
+#pragma unroll
+                for (int e = 0; e < kPath; ++e)
+                    if (e < d_t[rd]) {  // stored as bf16 hi + lo for the matrix cores
+                        const __bf16 yh = static_cast<__bf16>(y[e]);
+                        mh[an_t[rd][e]] = __builtin_bit_cast(uint16_t, yh);
+                        ml[an_t[rd][e]] =
+                            __builtin_bit_cast(uint16_t, static_cast<__bf16>(y[e] - static_cast<float>(yh)));
+                    }
+            }
+        }
+    } else {
+        load_state_frags<D>(s0, s_lane, sA);
+        if (grp > 1) load_state_frags<D>(s0 + (size_t)D * D, s_lane, sB);
     }
-    __syncthreads();
+    __syncthreads();  // the output operator and the gates are in LDS
+    if (uni(w) == 0) {
+        load_state_frags<D>(s0, s_lane, sA);
+        if (grp > 1) load_state_frags<D>(s0 + (size_t)D * D, s_lane, sB);
+    }
 
     // ---- value heads: X, Y from the state and K/Q; outputs from X, Y and the coefficients
     // fp32 values of head hh at this lane's row for the 16 nodes of its accumulator slots,
