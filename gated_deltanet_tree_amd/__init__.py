@@ -33,12 +33,13 @@ GDN_MAX_DRAFT_WIDTH = 16
 GDN_BF16, GDN_F32 = 0, 1
 
 SEQ_STATUS = {0: "OK", 1: "BAD_NODES", 2: "BAD_SLOT", 3: "DUP_SLOT", 4: "BAD_PARENT",
-              5: "CYCLE_OR_DEPTH", 6: "BAD_ACCEPT"}
+              5: "CYCLE_OR_DEPTH", 6: "BAD_ACCEPT", 7: "NOT_PERSISTED"}
 
 EXPORTS = ["gdn_workspace_bytes", "gdn_tree_plan", "gdn_tree_verify", "gdn_tree_persist",
            "gdn_chain_verify", "gdn_tree_accept", "gdn_draft_topk", "gdn_ddtree_nodes", "gdn_ddtree_build",
            "gdn_state_copy", "gdn_tree_verify_store", "gdn_tree_persist_copy", "gdn_tree_read_metadata",
-           "gdn_tree_status", "gdn_strerror", "gdn_tree_verify_static", "gdn_probe_stream"]
+           "gdn_tree_status", "gdn_strerror", "gdn_tree_verify_static", "gdn_probe_stream",
+           "gdn_tree_persist_verify"]
 
 
 class GdnError(RuntimeError):
@@ -82,6 +83,8 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_tree_plan.argtypes = [dp, vp, vp, vp, vp, sz, vp]
     lib.gdn_tree_verify.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdn_tree_persist.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdn_tree_persist_verify.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, dp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                            sz, vp]
     lib.gdn_tree_verify_static.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_probe_stream.argtypes = [ctypes.c_int32, vp, vp, sz, sz, vp]
     lib.gdn_chain_verify.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -209,6 +212,27 @@ def gdn_tree_persist(dims, k, v, a, b, accepted_node, state_cache, slot_idx, ws,
         _ptr(state_cache, "state_cache", torch.float32, dims.num_slots * Hv * D * D),
         _ptr(slot_idx, "slot_idx", torch.int32, B), _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)),
         "gdn_tree_persist")
+
+
+def gdn_tree_persist_verify(prev_dims, prev_k, prev_v, prev_a, prev_b, accepted_node, prev_ws, dims, q, k, v, a, b,
+                            state_cache, slot_idx, out, ws, stream=None):
+    """gdn_tree_persist of the previous step (prev_* and its workspace) followed by
+    gdn_tree_verify of the next (dims, inputs, outputs, workspace) in one pass over the
+    state cache."""
+    Tp, T, B = prev_dims.total_nodes, dims.total_nodes, dims.num_seqs
+    Hk, Hv, D = dims.num_k_heads, dims.num_v_heads, dims.head_dim
+    dtp, dt = _qkv_dtype(prev_dims), _qkv_dtype(dims)
+    _check(load_library().gdn_tree_persist_verify(
+        ctypes.byref(prev_dims), _ptr(prev_k, "prev_k", dtp, Tp * prev_dims.num_k_heads * prev_dims.head_dim),
+        _ptr(prev_v, "prev_v", dtp, Tp * prev_dims.num_v_heads * prev_dims.head_dim),
+        _ptr(prev_a, "prev_a", torch.float32, Tp * prev_dims.num_v_heads),
+        _ptr(prev_b, "prev_b", torch.float32, Tp * prev_dims.num_v_heads),
+        _ptr(accepted_node, "accepted_node", torch.int32, B), _ptr(prev_ws, "prev_ws", torch.uint8),
+        prev_ws.numel(), ctypes.byref(dims), _ptr(q, "q", dt, T * Hk * D), _ptr(k, "k", dt, T * Hk * D),
+        _ptr(v, "v", dt, T * Hv * D), _ptr(a, "a", torch.float32, T * Hv), _ptr(b, "b", torch.float32, T * Hv),
+        _ptr(state_cache, "state_cache", torch.float32, dims.num_slots * Hv * D * D),
+        _ptr(slot_idx, "slot_idx", torch.int32, B), _ptr(out, "out", torch.float32, T * Hv * D),
+        _ptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)), "gdn_tree_persist_verify")
 
 
 def gdn_tree_verify_store(dims, q, k, v, a, b, state_cache, slot_idx, out, node_states, ws, stream=None):

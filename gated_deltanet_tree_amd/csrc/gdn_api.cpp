@@ -180,6 +180,61 @@ int gdn_tree_persist(const gdn_dims *dims, const void *k, const void *v, const f
     return launched(gdn::launch_persist_recurrent(p, dims->qkv_dtype, as_stream(stream)));
 }
 
+int gdn_tree_persist_verify(const gdn_dims *prev_dims, const void *prev_k, const void *prev_v,
+                            const float *prev_a, const float *prev_b, const int32_t *accepted_node,
+                            void *prev_ws, size_t prev_ws_bytes, const gdn_dims *dims, const void *q,
+                            const void *k, const void *v, const float *a, const float *b,
+                            float *state_cache, const int32_t *slot_idx, float *out, void *ws,
+                            size_t ws_bytes, void *stream) {
+    int rc = check_dims(prev_dims, GDN_MAX_NODES);
+    if (rc) return rc;
+    rc = check_dims(dims, GDN_MAX_NODES);
+    if (rc) return rc;
+    if (prev_dims->num_seqs != dims->num_seqs || prev_dims->num_k_heads != dims->num_k_heads ||
+        prev_dims->num_v_heads != dims->num_v_heads || prev_dims->head_dim != dims->head_dim ||
+        prev_dims->num_slots != dims->num_slots || prev_dims->qkv_dtype != dims->qkv_dtype)
+        return GDN_ERR_SHAPE;
+    if (!prev_ws || !ws) return GDN_ERR_NULL;
+    if (prev_dims->total_nodes > 0 && (!prev_k || !prev_v || !prev_a || !prev_b)) return GDN_ERR_NULL;
+    if (dims->total_nodes > 0 && (!q || !k || !v || !a || !b || !out)) return GDN_ERR_NULL;
+    if (dims->num_seqs > 0 && (!state_cache || !slot_idx || !accepted_node)) return GDN_ERR_NULL;
+    if (prev_ws_bytes < gdn_workspace_bytes(prev_dims) || ws_bytes < gdn_workspace_bytes(dims))
+        return GDN_ERR_WORKSPACE;
+    if (dims->num_seqs == 0) return GDN_OK;
+    const bool fused = !recurrent_forced() && dims->total_nodes > 0 && prev_dims->total_nodes > 0 &&
+                       gdn::fused_supported(dims->head_dim, dims->qkv_dtype, dims->max_nodes);
+    if (!fused) {
+        rc = gdn_tree_persist(prev_dims, prev_k, prev_v, prev_a, prev_b, accepted_node, state_cache, slot_idx,
+                              prev_ws, prev_ws_bytes, stream);
+        if (rc) return rc;
+        return gdn_tree_verify(dims, q, k, v, a, b, state_cache, slot_idx, out, ws, ws_bytes, stream);
+    }
+    Params pp = base_params(prev_dims);
+    pp.k = prev_k;
+    pp.v = prev_v;
+    pp.a = prev_a;
+    pp.b = prev_b;
+    pp.accepted = accepted_node;
+    pp.state_in = state_cache;
+    pp.state_out = state_cache;
+    pp.slot_idx = slot_idx;
+    pp.ws = gdn::ws_ptrs(prev_ws, pp.B, pp.T, pp.Hv);
+    pp.has_ws = 1;
+    Params pn = base_params(dims);
+    pn.q = q;
+    pn.k = k;
+    pn.v = v;
+    pn.a = a;
+    pn.b = b;
+    pn.state_in = state_cache;
+    pn.state_out = state_cache;
+    pn.slot_idx = slot_idx;
+    pn.out = out;
+    pn.ws = gdn::ws_ptrs(ws, pn.B, pn.T, pn.Hv);
+    pn.has_ws = 1;
+    return launched(gdn::launch_persist_verify_fast(pp, pn, as_stream(stream)));
+}
+
 int gdn_tree_verify_store(const gdn_dims *dims, const void *q, const void *k, const void *v, const float *a,
                           const float *b, const float *state_cache, const int32_t *slot_idx, float *out,
                           uint16_t *node_states, const void *ws, size_t ws_bytes, void *stream) {

@@ -699,6 +699,130 @@ __device__ __forceinline__ void load_state_frags(const float *head, unsigned lan
     }
 }
 
+// The group verify's coefficient phase, run by one wave (lanes `lane`, halves `hf`,
+// rows `l32`) on tables already in LDS: the Gram entries k.k and k.q of the block
+// scattered into path order, then per (value head, node) pair the ratios, the
+// coefficients and the back substitution that gives the output operator's rows
+// (bf16 hi + lo) and the gates gamma, alpha, b.
+template <int D, bool F32, int GRP>
+__device__ __forceinline__ void group_coefficients(const GTab<D> &L, int n, int lane, int hf, int l32) {
+    constexpr int KS = VG<D>::KS;
+    constexpr int grp = GRP;
+    using Q = GPad<D>;
+    // Gram entries of the block: k . k, then k . q
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+        const int bro = which == 0 ? 0 : kTile;  // B operand rows: the keys or the queries
+        f32x16 gacc = {};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const bf16x8 A = frag_of(L.kq + l32 * Q::KQ, s, hf);
+            const bf16x8 B = frag_of(L.kq + (bro + l32) * Q::KQ, s, hf);
+            if constexpr (F32) {
+                const bf16x8 Al = frag_of(L.kq + (2 * kTile + l32) * Q::KQ, s, hf);
+                const bf16x8 Bl = frag_of(L.kq + (2 * kTile + bro + l32) * Q::KQ, s, hf);
+                gacc = mfma_split(A, Al, B, Bl, gacc);
+            } else {
+                gacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, gacc, 0, 0, 0);
+            }
+        }
+        if (l32 < n) {  // accumulator r: (candidate ancestor il, node l32)
+            // ancestors of node l32 within the block: its path entries (-1 past its depth),
+            // all read before any is tested, so no read waits under a branch
+            int anl[kPath];
+#pragma unroll
+            for (int e = 0; e < kPath; ++e) anl[e] = L.anc[l32 * Q::PS + e];
+            uint32_t mask = 0u;
+#pragma unroll
+            for (int e = 0; e < kPath; ++e) mask |= anl[e] >= 0 ? 1u << (anl[e] & 31) : 0u;
+            float *gdst = (which == 0 ? L.gk : L.gq) + l32 * Q::PS;
+            // the candidates' depths four at a time, all read before any write; a candidate
+            // that is not an ancestor writes to the row's pad column, which nothing reads
+            int4 dq[4];
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4)
+                dq[g4] = *reinterpret_cast<const int4 *>(L.depth + 8 * g4 + 4 * hf);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int il = 8 * (r / 4) + 4 * hf + (r % 4);
+                const int4 q4 = dq[r / 4];
+                const int dep = r % 4 == 0 ? q4.x : r % 4 == 1 ? q4.y : r % 4 == 2 ? q4.z : q4.w;
+                gdst[((mask >> il) & 1u) ? dep - 1 : kPath] = gacc[r];
+            }
+        }
+    }
+    // one wave's LDS accesses take effect in program order: only the compiler must keep them
+    __builtin_amdgcn_wave_barrier();
+
+    // per (value head, node) pair, lane and lane + 64: ratios, coefficients, output weights
+    constexpr int RND = (kGroupMaxHeads * kTile + 63) / 64;
+    float mrow[RND][kPath];
+    int an_t[RND][kPath];
+    int d_t[RND], hh_t[RND], i_t[RND];
+    bool act[RND];
+#pragma unroll
+    for (int rd = 0; rd < RND; ++rd) {
+        const int pr = lane + 64 * rd;
+        act[rd] = pr < grp * n;
+        hh_t[rd] = act[rd] ? pr / n : 0;
+        i_t[rd] = act[rd] ? pr % n : 0;
+        d_t[rd] = 0;
+        if (act[rd]) {
+            const int hh = hh_t[rd], i = i_t[rd];
+            const int di = L.depth[i];
+            d_t[rd] = di;
+            const float bi = L.b[hh * kTile + i];
+            // every table entry of the row, read before the first result is written (the
+            // writes would otherwise order each step's reads behind the previous step's)
+            float av[kPath], gk[kPath], gq[kPath];
+#pragma unroll
+            for (int e = 0; e < kPath; ++e) an_t[rd][e] = max(L.anc[i * Q::PS + e], 0);
+#pragma unroll
+            for (int e = 0; e < kPath; ++e) {
+                const float ae = L.a[hh * kTile + an_t[rd][e]];
+                av[e] = e < di ? ae : 1.0f;
+                gk[e] = L.gk[i * Q::PS + e];
+                gq[e] = L.gq[i * Q::PS + e];
+            }
+            float r = 1.0f;
+#pragma unroll
+            for (int e = kPath - 1; e >= 0; --e) {
+                const bool on = e < di - 1;
+                L.coefL[(hh * kTile + i) * Q::PS + e] = on ? bi * r * gk[e] : 0.0f;
+                mrow[rd][e] = on ? r * gq[e] : (e == di - 1 ? gq[e] : 0.0f);
+                r *= av[e];
+            }
+            L.gab[hh * kTile + i] = make_float4(r, bi * r, bi, 0.0f);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int rd = 0; rd < RND; ++rd) {
+        if (act[rd]) {
+            const int hh = hh_t[rd], i = i_t[rd];
+            float y[kPath];
+#pragma unroll
+            for (int e = kPath - 1; e >= 0; --e) {
+                float acc = mrow[rd][e];
+                // deepest terms first: y_{e+1}, the last one known, enters last
+#pragma unroll
+                for (int f = kPath - 1; f > e; --f)
+                    acc = fmaf(-y[f], L.coefL[(hh * kTile + an_t[rd][f]) * Q::PS + e], acc);
+                y[e] = e < d_t[rd] ? acc : 0.0f;
+            }
+            uint16_t *mh = L.mth + (hh * kTile + i) * Q::MT, *ml = L.mtl + (hh * kTile + i) * Q::MT;
+#pragma unroll
+            for (int e = 0; e < kPath; ++e)
+                if (e < d_t[rd]) {  // stored as bf16 hi + lo for the matrix cores
+                    const __bf16 yh = static_cast<__bf16>(y[e]);
+                    mh[an_t[rd][e]] = __builtin_bit_cast(uint16_t, yh);
+                    ml[an_t[rd][e]] =
+                        __builtin_bit_cast(uint16_t, static_cast<__bf16>(y[e] - static_cast<float>(yh)));
+                }
+        }
+    }
+}
+
 template <int D, bool CHAIN, int HPW, bool F32>
 __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(HPW == 1 ? 3 : 2))) void
 verify_group_kernel(Params P) {
@@ -827,118 +951,7 @@ verify_group_kernel(Params P) {
     // every such stall would hold back the coefficients, which gate every output.  Wave 0
     // issues its own states once the phase is done.
     if (uni(w) == 0) {
-        // Gram entries of the block: k . k, then k . q
-#pragma unroll
-        for (int which = 0; which < 2; ++which) {
-            const int bro = which == 0 ? 0 : kTile;  // B operand rows: the keys or the queries
-            f32x16 gacc = {};
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const bf16x8 A = frag_of(L.kq + l32 * Q::KQ, s, hf);
-                const bf16x8 B = frag_of(L.kq + (bro + l32) * Q::KQ, s, hf);
-                if constexpr (F32) {
-                    const bf16x8 Al = frag_of(L.kq + (2 * kTile + l32) * Q::KQ, s, hf);
-                    const bf16x8 Bl = frag_of(L.kq + (2 * kTile + bro + l32) * Q::KQ, s, hf);
-                    gacc = mfma_split(A, Al, B, Bl, gacc);
-                } else {
-                    gacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, gacc, 0, 0, 0);
-                }
-            }
-            if (l32 < n) {  // accumulator r: (candidate ancestor il, node l32)
-                // ancestors of node l32 within the block: its path entries (-1 past its depth),
-                // all read before any is tested, so no read waits under a branch
-                int anl[kPath];
-#pragma unroll
-                for (int e = 0; e < kPath; ++e) anl[e] = L.anc[l32 * Q::PS + e];
-                uint32_t mask = 0u;
-#pragma unroll
-                for (int e = 0; e < kPath; ++e) mask |= anl[e] >= 0 ? 1u << (anl[e] & 31) : 0u;
-                float *gdst = (which == 0 ? L.gk : L.gq) + l32 * Q::PS;
-                // the candidates' depths four at a time, all read before any write; a candidate
-                // that is not an ancestor writes to the row's pad column, which nothing reads
-                int4 dq[4];
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4)
-                    dq[g4] = *reinterpret_cast<const int4 *>(L.depth + 8 * g4 + 4 * hf);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int il = 8 * (r / 4) + 4 * hf + (r % 4);
-                    const int4 q4 = dq[r / 4];
-                    const int dep = r % 4 == 0 ? q4.x : r % 4 == 1 ? q4.y : r % 4 == 2 ? q4.z : q4.w;
-                    gdst[((mask >> il) & 1u) ? dep - 1 : kPath] = gacc[r];
-                }
-            }
-        }
-        // one wave's LDS accesses take effect in program order: only the compiler must keep them
-        __builtin_amdgcn_wave_barrier();
-
-        // per (value head, node) pair, lane and lane + 64: ratios, coefficients, output weights
-        constexpr int RND = (kGroupMaxHeads * kTile + 63) / 64;
-        float mrow[RND][kPath];
-        int an_t[RND][kPath];
-        int d_t[RND], hh_t[RND], i_t[RND];
-        bool act[RND];
-#pragma unroll
-        for (int rd = 0; rd < RND; ++rd) {
-            const int pr = lane + 64 * rd;
-            act[rd] = pr < grp * n;
-            hh_t[rd] = act[rd] ? pr / n : 0;
-            i_t[rd] = act[rd] ? pr % n : 0;
-            d_t[rd] = 0;
-            if (act[rd]) {
-                const int hh = hh_t[rd], i = i_t[rd];
-                const int di = L.depth[i];
-                d_t[rd] = di;
-                const float bi = L.b[hh * kTile + i];
-                // every table entry of the row, read before the first result is written (the
-                // writes would otherwise order each step's reads behind the previous step's)
-                float av[kPath], gk[kPath], gq[kPath];
-#pragma unroll
-                for (int e = 0; e < kPath; ++e) an_t[rd][e] = max(L.anc[i * Q::PS + e], 0);
-#pragma unroll
-                for (int e = 0; e < kPath; ++e) {
-                    const float ae = L.a[hh * kTile + an_t[rd][e]];
-                    av[e] = e < di ? ae : 1.0f;
-                    gk[e] = L.gk[i * Q::PS + e];
-                    gq[e] = L.gq[i * Q::PS + e];
-                }
-                float r = 1.0f;
-#pragma unroll
-                for (int e = kPath - 1; e >= 0; --e) {
-                    const bool on = e < di - 1;
-                    L.coefL[(hh * kTile + i) * Q::PS + e] = on ? bi * r * gk[e] : 0.0f;
-                    mrow[rd][e] = on ? r * gq[e] : (e == di - 1 ? gq[e] : 0.0f);
-                    r *= av[e];
-                }
-                L.gab[hh * kTile + i] = make_float4(r, bi * r, bi, 0.0f);
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int rd = 0; rd < RND; ++rd) {
-            if (act[rd]) {
-                const int hh = hh_t[rd], i = i_t[rd];
-                float y[kPath];
-#pragma unroll
-                for (int e = kPath - 1; e >= 0; --e) {
-                    float acc = mrow[rd][e];
-                    // deepest terms first: y_{e+1}, the last one known, enters last
-#pragma unroll
-                    for (int f = kPath - 1; f > e; --f)
-                        acc = fmaf(-y[f], L.coefL[(hh * kTile + an_t[rd][f]) * Q::PS + e], acc);
-                    y[e] = e < d_t[rd] ? acc : 0.0f;
-                }
-                uint16_t *mh = L.mth + (hh * kTile + i) * Q::MT, *ml = L.mtl + (hh * kTile + i) * Q::MT;
-#pragma unroll
-                for (int e = 0; e < kPath; ++e)
-                    if (e < d_t[rd]) {  // stored as bf16 hi + lo for the matrix cores
-                        const __bf16 yh = static_cast<__bf16>(y[e]);
-                        mh[an_t[rd][e]] = __builtin_bit_cast(uint16_t, yh);
-                        ml[an_t[rd][e]] =
-                            __builtin_bit_cast(uint16_t, static_cast<__bf16>(y[e] - static_cast<float>(yh)));
-                    }
-            }
-        }
+        group_coefficients<D, F32, grp>(L, n, lane, hf, l32);
     } else {
         load_state_frags<D>(s0, s_lane, sA);
         if (grp > 1) load_state_frags<D>(s0 + (size_t)D * D, s_lane, sB);
@@ -1589,6 +1602,163 @@ __device__ __forceinline__ void load_state_tiles(const float *head, unsigned lan
         }
 }
 
+// Gram entries k_e . k_p of the path keys in LDS, formed by one wave (one 32x32
+// tile, 16 rows used) and written to L.gram.
+template <int D, bool F32>
+__device__ __forceinline__ void replay_gram(const PTab<D> &L, int l32, int hf) {
+    f32x16 gk = {};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+        const bf16x8 A = l32 < kPath ? frag_of(L.k + l32 * PTab<D>::KP, s, hf) : zero_frag();
+        if constexpr (F32) {
+            const bf16x8 Al = l32 < kPath ? frag_of(L.klo + l32 * PTab<D>::KP, s, hf) : zero_frag();
+            gk = mfma_split(A, Al, A, Al, gk);
+        } else {
+            gk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, A, gk, 0, 0, 0);
+        }
+    }
+    if (l32 < kPath) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) L.gram[l32 * (kPath + 1) + 8 * (r / 4) + 4 * hf + (r % 4)] = gk[r];
+    }
+}
+
+// The replay's coefficient phase for (head hh, path entry p): the ratios R(p, e),
+// the row Lc[p][.] of the recurrence and the gates gamma_p, alpha_p, b_p, w_p, from
+// the gates and Gram entries in LDS.
+template <int D>
+__device__ __forceinline__ void replay_coef_entry(const PTab<D> &L, int len, int hh, int p) {
+    const int tid = hh * kPath + p;
+    const float *ah = L.a + hh * kPath;
+    const float bp = L.b[tid];
+    // the gates and the row's Gram entries, read before the first coefficient is written
+    float av[kPath], gr[kPath];
+#pragma unroll
+    for (int e = 0; e < kPath; ++e) {
+        av[e] = ah[e];
+        gr[e] = L.gram[p * (kPath + 1) + e];
+    }
+    float r = 1.0f;  // R(p, e), e from p-1 down
+#pragma unroll
+    for (int e = kPath - 1; e >= 0; --e) {
+        float v = 0.0f;
+        if (e < p) {
+            r *= av[min(e + 1, kPath - 1)];
+            v = p < len ? bp * r * gr[e] : 0.0f;
+        }
+        L.coefL[(hh * kPath + p) * (kPath + 1) + e] = v;
+    }
+    float gm = 1.0f, wr = 1.0f;
+#pragma unroll
+    for (int t = 0; t < kPath; ++t) {
+        if (t <= p) gm *= av[t];
+        if (t > p && t < len) wr *= av[t];
+    }
+    L.gaw[tid] = make_float4(gm, bp * gm, bp, p < len ? wr : 0.0f);
+}
+
+// One value head of the replay, on the path tables in LDS: X = S0 K^T for the path
+// keys (MFMA, the state split hi + lo), the per-row recurrence for c, then
+// S <- gamma_{L-1} S + sum_e w_e c_e k_e^T accumulated onto the lane's state tiles
+// and stored from them to dst's head hh (s_lane: the lane's first element of a head).
+template <int D, bool F32>
+__device__ __forceinline__ void replay_head(f32x16 (&S)[D / 32], const PTab<D> &L, int grp, int hh, int len, int l32,
+                                            int hf, int row, float *dst, unsigned s_lane) {
+    constexpr int NTILE = D / 32;
+    // X = S0 K^T: k-step s takes tile s/2, registers 8(s%2) .. 8(s%2)+7 (columns
+    // 32t + 16u + 8(e/4) + 4*half + e%4), the keys read in the same column order
+    f32x16 ax = {};
+    const uint16_t *krow = L.k + l32 * PTab<D>::KP;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+        const int t = s / 2, u = s % 2;
+        bf16x8 shi, slo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = S[t][8 * u + e];
+            const __bf16 hb = static_cast<__bf16>(x);
+            shi[e] = hb;
+            slo[e] = static_cast<__bf16>(x - static_cast<float>(hb));
+        }
+        bf16x8 A = zero_frag();
+        if (l32 < kPath) {
+            const uint2 k0 = *reinterpret_cast<const uint2 *>(krow + 32 * t + 16 * u + 4 * hf);
+            const uint2 k1 = *reinterpret_cast<const uint2 *>(krow + 32 * t + 16 * u + 8 + 4 * hf);
+            A = __builtin_bit_cast(bf16x8, make_uint4(k0.x, k0.y, k1.x, k1.y));
+        }
+        if constexpr (F32) {
+            bf16x8 Al = zero_frag();
+            if (l32 < kPath) {
+                const uint16_t *klrow = L.klo + l32 * PTab<D>::KP;
+                const uint2 k0 = *reinterpret_cast<const uint2 *>(klrow + 32 * t + 16 * u + 4 * hf);
+                const uint2 k1 = *reinterpret_cast<const uint2 *>(klrow + 32 * t + 16 * u + 8 + 4 * hf);
+                Al = __builtin_bit_cast(bf16x8, make_uint4(k0.x, k0.y, k1.x, k1.y));
+            }
+            ax = mfma_split(A, Al, shi, slo, ax);
+        } else {
+            ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, shi, ax, 0, 0, 0);
+            ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, slo, ax, 0, 0, 0);
+        }
+    }
+    // x_e of this row: accumulator r < 8 holds e = 8(r/4) + 4*half + r%4, the other
+    // half-wave the rest
+    float x[kPath];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const float mine = ax[r];
+        const float other = __shfl_xor(mine, 32);
+        const int e_mine = 8 * (r / 4) + (r % 4);  // + 4*half
+        x[e_mine] = hf ? other : mine;
+        x[e_mine + 4] = hf ? mine : other;
+    }
+    // c_p = b_p v_p - alpha_p x_p - sum_{e<p} Lc[p][e] c_e
+    const float4 *gaw = L.gaw + hh * kPath;
+    const float *cl = L.coefL + hh * kPath * (kPath + 1);
+    const uint16_t *vh = L.v + hh * D + row;
+    const float *vhf = L.vf + hh * D + row;
+    float c[kPath];
+#pragma unroll
+    for (int p = 0; p < kPath; ++p) {
+        const float4 q4 = gaw[p];
+        float acc = fmaf(-q4.y, x[p], q4.z * (F32 ? vhf[p * grp * D] : bf2f(vh[p * grp * D])));
+#pragma unroll
+        for (int e = 0; e < p; ++e) acc = fmaf(-cl[p * (kPath + 1) + e], c[e], acc);
+        c[p] = p < len ? acc : 0.0f;
+    }
+    // B operand of the update: this half-wave's entries w_e c_e, e = 8*half .. 8*half+7
+    bf16x8 whi, wlo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int ee = e;  // entry 8*half + e
+        const float wc = (hf ? gaw[8 + ee].w * c[8 + ee] : gaw[ee].w * c[ee]);
+        const __bf16 hb = static_cast<__bf16>(wc);
+        whi[e] = hb;
+        wlo[e] = static_cast<__bf16>(wc - static_cast<float>(hb));
+    }
+    const float gl = gaw[len - 1].x;
+    float *dh = dst + (size_t)hh * D * D + s_lane;
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) {
+        // A: k_e[32t + l32] for e = 8*half .. 8*half+7 (transposed keys)
+        const bf16x8 A = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4 *>(L.kt + (32 * t + l32) * PTab<D>::KT + 8 * hf));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[t][r] *= gl;
+        if constexpr (F32) {
+            const bf16x8 Al = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const uint4 *>(L.ktlo + (32 * t + l32) * PTab<D>::KT + 8 * hf));
+            S[t] = mfma_split(A, Al, whi, wlo, S[t]);
+        } else {
+            S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, whi, S[t], 0, 0, 0);
+            S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wlo, S[t], 0, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4 *>(dh + 32 * t + 8 * q) =
+                make_float4(S[t][4 * q], S[t][4 * q + 1], S[t][4 * q + 2], S[t][4 * q + 3]);
+    }
+}
+
 template <int D, bool CHAIN, bool F32>
 __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(3))) void replay_kernel(
     Params P) {
@@ -1736,152 +1906,14 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
     __syncthreads();
 
     // ---- Gram entries of the path keys (one wave, one 32x32 tile, 16 rows used)
-    if (w == 0) {
-        f32x16 gk = {};
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            const bf16x8 A = l32 < kPath ? frag_of(L.k + l32 * PTab<D>::KP, s, hf) : zero_frag();
-            if constexpr (F32) {
-                const bf16x8 Al = l32 < kPath ? frag_of(L.klo + l32 * PTab<D>::KP, s, hf) : zero_frag();
-                gk = mfma_split(A, Al, A, Al, gk);
-            } else {
-                gk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, A, gk, 0, 0, 0);
-            }
-        }
-        if (l32 < kPath) {
-#pragma unroll
-            for (int r = 0; r < 8; ++r) L.gram[l32 * (kPath + 1) + 8 * (r / 4) + 4 * hf + (r % 4)] = gk[r];
-        }
-    }
+    if (w == 0) replay_gram<D, F32>(L, l32, hf);
     __syncthreads();
     // ---- per (head, path entry p): ratios, coefficients
-    if (tid < grp * kPath) {
-        const int hh = tid / kPath, p = tid % kPath;
-        const float *ah = L.a + hh * kPath;
-        const float bp = L.b[tid];
-        // the gates and the row's Gram entries, read before the first coefficient is written
-        float av[kPath], gr[kPath];
-#pragma unroll
-        for (int e = 0; e < kPath; ++e) {
-            av[e] = ah[e];
-            gr[e] = L.gram[p * (kPath + 1) + e];
-        }
-        float r = 1.0f;  // R(p, e), e from p-1 down
-#pragma unroll
-        for (int e = kPath - 1; e >= 0; --e) {
-            float v = 0.0f;
-            if (e < p) {
-                r *= av[min(e + 1, kPath - 1)];
-                v = p < len ? bp * r * gr[e] : 0.0f;
-            }
-            L.coefL[(hh * kPath + p) * (kPath + 1) + e] = v;
-        }
-        float gm = 1.0f, wr = 1.0f;
-#pragma unroll
-        for (int t = 0; t < kPath; ++t) {
-            if (t <= p) gm *= av[t];
-            if (t > p && t < len) wr *= av[t];
-        }
-        L.gaw[tid] = make_float4(gm, bp * gm, bp, p < len ? wr : 0.0f);
-    }
+    if (tid < grp * kPath) replay_coef_entry<D>(L, len, tid / kPath, tid % kPath);
     __syncthreads();
 
     // ---- value heads
-    auto head = [&](f32x16 (&S)[NTILE], int hh) {
-        // X = S0 K^T: k-step s takes tile s/2, registers 8(s%2) .. 8(s%2)+7 (columns
-        // 32t + 16u + 8(e/4) + 4*half + e%4), the keys read in the same column order
-        f32x16 ax = {};
-        const uint16_t *krow = L.k + l32 * PTab<D>::KP;
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            const int t = s / 2, u = s % 2;
-            bf16x8 shi, slo;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = S[t][8 * u + e];
-                const __bf16 hb = static_cast<__bf16>(x);
-                shi[e] = hb;
-                slo[e] = static_cast<__bf16>(x - static_cast<float>(hb));
-            }
-            bf16x8 A = zero_frag();
-            if (l32 < kPath) {
-                const uint2 k0 = *reinterpret_cast<const uint2 *>(krow + 32 * t + 16 * u + 4 * hf);
-                const uint2 k1 = *reinterpret_cast<const uint2 *>(krow + 32 * t + 16 * u + 8 + 4 * hf);
-                A = __builtin_bit_cast(bf16x8, make_uint4(k0.x, k0.y, k1.x, k1.y));
-            }
-            if constexpr (F32) {
-                bf16x8 Al = zero_frag();
-                if (l32 < kPath) {
-                    const uint16_t *klrow = L.klo + l32 * PTab<D>::KP;
-                    const uint2 k0 = *reinterpret_cast<const uint2 *>(klrow + 32 * t + 16 * u + 4 * hf);
-                    const uint2 k1 = *reinterpret_cast<const uint2 *>(klrow + 32 * t + 16 * u + 8 + 4 * hf);
-                    Al = __builtin_bit_cast(bf16x8, make_uint4(k0.x, k0.y, k1.x, k1.y));
-                }
-                ax = mfma_split(A, Al, shi, slo, ax);
-            } else {
-                ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, shi, ax, 0, 0, 0);
-                ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, slo, ax, 0, 0, 0);
-            }
-        }
-        // x_e of this row: accumulator r < 8 holds e = 8(r/4) + 4*half + r%4, the other
-        // half-wave the rest
-        float x[kPath];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const float mine = ax[r];
-            const float other = __shfl_xor(mine, 32);
-            const int e_mine = 8 * (r / 4) + (r % 4);  // + 4*half
-            x[e_mine] = hf ? other : mine;
-            x[e_mine + 4] = hf ? mine : other;
-        }
-        // c_p = b_p v_p - alpha_p x_p - sum_{e<p} Lc[p][e] c_e
-        const float4 *gaw = L.gaw + hh * kPath;
-        const float *cl = L.coefL + hh * kPath * (kPath + 1);
-        const uint16_t *vh = L.v + hh * D + row;
-        const float *vhf = L.vf + hh * D + row;
-        float c[kPath];
-#pragma unroll
-        for (int p = 0; p < kPath; ++p) {
-            const float4 q4 = gaw[p];
-            float acc = fmaf(-q4.y, x[p], q4.z * (F32 ? vhf[p * grp * D] : bf2f(vh[p * grp * D])));
-#pragma unroll
-            for (int e = 0; e < p; ++e) acc = fmaf(-cl[p * (kPath + 1) + e], c[e], acc);
-            c[p] = p < len ? acc : 0.0f;
-        }
-        // B operand of the update: this half-wave's entries w_e c_e, e = 8*half .. 8*half+7
-        bf16x8 whi, wlo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int ee = e;  // entry 8*half + e
-            const float wc = (hf ? gaw[8 + ee].w * c[8 + ee] : gaw[ee].w * c[ee]);
-            const __bf16 hb = static_cast<__bf16>(wc);
-            whi[e] = hb;
-            wlo[e] = static_cast<__bf16>(wc - static_cast<float>(hb));
-        }
-        const float gl = gaw[len - 1].x;
-        float *dh = dst + (size_t)hh * D * D + s_lane;
-#pragma unroll
-        for (int t = 0; t < NTILE; ++t) {
-            // A: k_e[32t + l32] for e = 8*half .. 8*half+7 (transposed keys)
-            const bf16x8 A = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const uint4 *>(L.kt + (32 * t + l32) * PTab<D>::KT + 8 * hf));
-#pragma unroll
-            for (int r = 0; r < 16; ++r) S[t][r] *= gl;
-            if constexpr (F32) {
-                const bf16x8 Al = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const uint4 *>(L.ktlo + (32 * t + l32) * PTab<D>::KT + 8 * hf));
-                S[t] = mfma_split(A, Al, whi, wlo, S[t]);
-            } else {
-                S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, whi, S[t], 0, 0, 0);
-                S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wlo, S[t], 0, 0, 0);
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<float4 *>(dh + 32 * t + 8 * q) =
-                    make_float4(S[t][4 * q], S[t][4 * q + 1], S[t][4 * q + 2], S[t][4 * q + 3]);
-        }
-    };
-    head(SA, 0);
+    replay_head<D, F32>(SA, L, grp, 0, len, l32, hf, row, dst, s_lane);
 }
 
 // ===========================================================================
@@ -2278,6 +2310,346 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
     }
 }
 
+// ===========================================================================
+// Persist fused with the next verify (trees of at most 32 nodes, bf16 inputs).
+// In a decode loop a layer's state is read by that layer's verify and read and
+// written by its persist.  Deferring step t's persist to the layer's verify of
+// step t+1 lets one pass over the state serve both: the workgroup of (sequence,
+// value head) loads S once, replays step t's accepted path in registers with
+// the replay's own tables and arithmetic, writes the result in place, and forms
+// step t+1's products X = S K^T and Y = S Q^T from the same registers, reading
+// the tree's keys and queries in the column order of the state tiles (the order
+// the replay uses for its path keys).  Coefficients and outputs follow the group
+// verify.  Pp holds the previous step (plan, inputs, accepted nodes), Pn the new
+// one (plan, inputs, outputs); both address the same state cache.
+// Slots.  Sequence b is persisted into its previous slot and verified from its
+// new slot.  When the two are equal and the new tree is verified here, the new
+// plan guarantees no other verified sequence reads that slot.  Otherwise the
+// workgroup checks every sequence's new record: if another verified sequence
+// reads the slot it would write, the persist is skipped and the sequence is
+// marked GDN_SEQ_NOT_PERSISTED in the previous workspace, so no slot is ever
+// written by one workgroup while another reads it.
+// ===========================================================================
+template <int D>
+__host__ __device__ inline size_t fused_new_bytes() {
+    using Q = GPad<D>;
+    return (size_t)2 * kTile * Q::KQ * 2 + (size_t)kTile * 16 + (size_t)kTile * Q::MT * 4 + 4 * (size_t)kTile * Q::PS * 4 +
+           2 * (size_t)kTile * 4 + kTile * 4;
+}
+
+// the group verify's tables for one value head, without the staged values
+template <int D>
+__device__ inline GTab<D> fused_new_carve(char *base) {
+    using Q = GPad<D>;
+    GTab<D> L;
+    L.kq = reinterpret_cast<uint16_t *>(base);     base += (size_t)2 * kTile * Q::KQ * 2;
+    L.v = nullptr;
+    L.gab = reinterpret_cast<float4 *>(base);      base += (size_t)kTile * 16;
+    L.mth = reinterpret_cast<uint16_t *>(base);    base += (size_t)kTile * Q::MT * 2;
+    L.mtl = reinterpret_cast<uint16_t *>(base);    base += (size_t)kTile * Q::MT * 2;
+    L.coefL = reinterpret_cast<float *>(base);     base += (size_t)kTile * Q::PS * 4;
+    L.gk = reinterpret_cast<float *>(base);        base += kTile * Q::PS * 4;
+    L.gq = reinterpret_cast<float *>(base);        base += kTile * Q::PS * 4;
+    L.anc = reinterpret_cast<int *>(base);         base += kTile * Q::PS * 4;
+    L.a = reinterpret_cast<float *>(base);         base += (size_t)kTile * 4;
+    L.b = reinterpret_cast<float *>(base);         base += (size_t)kTile * 4;
+    L.depth = reinterpret_cast<int *>(base);
+    return L;
+}
+
+template <int D>
+size_t fused_lds_bytes() {
+    return ptab_bytes<D>(1, false) + fused_new_bytes<D>();
+}
+
+template <int D>
+__global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(3))) void persist_verify_kernel(
+    Params Pp, Params Pn) {
+    extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+    constexpr int NT = VG<D>::THREADS, KS = VG<D>::KS;
+    using Q = GPad<D>;
+    const int tid = threadIdx.x, w = tid / 64, lane = tid % 64, hf = lane / 32, l32 = lane % 32;
+    const int row = w * 32 + l32;
+    const int b = blockIdx.x / Pn.Hv, h = blockIdx.x % Pn.Hv;
+    const int g = h / (Pn.Hv / Pn.Hk);
+
+    // ---- both plans' checks and records and the accepted node, loaded together
+    const bool plan_p = ws_plan_matches(Pp), plan_n = ws_plan_matches(Pn);
+    const int4 ip = *reinterpret_cast<const int4 *>(Pp.ws.seq_info + b * kSeqInfoInts);
+    const int4 in4 = *reinterpret_cast<const int4 *>(Pn.ws.seq_info + b * kSeqInfoInts);
+    const int m = Pp.accepted[b];
+    if (!(plan_p & plan_n)) {  // nothing is written; gdn_tree_status reports the misuse
+        if (blockIdx.x == 0 && tid == 0) {
+            if (!plan_p) Pp.ws.header[kHdrMisuse] = 1;
+            if (!plan_n) Pn.ws.header[kHdrMisuse] = 1;
+        }
+        return;
+    }
+    const int lo = uni(in4.x), n = uni(in4.y), slot = uni(in4.w);
+    const bool new_ok = in4.z == GDN_SEQ_OK;
+    const bool verified = new_ok & (n > 0);
+    // what gdn_tree_persist would do for this sequence: replay the path to m
+    const bool prev_live = (ip.z == GDN_SEQ_OK) & (ip.y > 0);
+    const bool want = prev_live & (m >= 0) & (m < ip.y);
+    const int pslot = uni(ip.w);
+    bool persist = want;
+    if (want && !(verified && pslot == slot)) {
+        // the slot it would write must not be another verified sequence's source
+        int clash = 0;
+        for (int j = tid; j < Pn.B; j += NT) {
+            const int4 r = *reinterpret_cast<const int4 *>(Pn.ws.seq_info + j * kSeqInfoInts);
+            clash |= (j != b) & (r.z == GDN_SEQ_OK) & (r.y > 0) & (r.w == pslot);
+        }
+        persist = !__syncthreads_or(clash);
+    }
+    if (h == 0 && tid == 0 && prev_live) {
+        if (m < -1 || m >= ip.y) Pp.ws.seq_status[b] = GDN_SEQ_BAD_ACCEPT;
+        else if (want && !persist) Pp.ws.seq_status[b] = GDN_SEQ_NOT_PERSISTED;
+    }
+    if (!new_ok) {  // a rejected new tree: NaN outputs, as verify writes them
+        if (hf == 0)
+            for (int i = 0; i < n; ++i) Pn.out[((size_t)(lo + i) * Pn.Hv + h) * D + row] = qnan_f();
+    }
+    if (!persist && !verified) return;
+
+    // ---- the accepted path (lane e < 16 of every wave: entry e, root first) and the
+    // new tree's path rows; each table's loads are issued before any test
+    int pl = 0, len = 0;
+    if (persist) {
+        const int mu = uni(m), pl0 = uni(ip.x);
+        pl = Pp.ws.nodepath[(size_t)(pl0 + mu) * GDN_MAX_DEPTH + lane % kPath];
+        len = Pp.ws.depth[pl0 + mu];
+    }
+    int an[kPath], d = 0;
+    if (verified && tid < n) {
+        d = Pn.ws.depth[lo + tid];
+#pragma unroll
+        for (int e = 0; e < kPath; ++e) an[e] = Pn.ws.nodepath[(size_t)(lo + tid) * GDN_MAX_DEPTH + e];
+    }
+    len = uni(len);
+    if (persist && h == 0 && tid < GDN_MAX_DEPTH) {
+        Pp.ws.path[b * GDN_MAX_DEPTH + tid] = pl;
+        if (tid == 0) Pp.ws.path_len[b] = len;
+    }
+
+    const PTab<D> Lp = ptab_carve<D>(lds_raw, 1, false);
+    const GTab<D> Ln = fused_new_carve<D>(lds_raw + ptab_bytes<D>(1, false));
+    const size_t kq_stride = (size_t)Pn.Hk * D;
+
+    // previous step: path keys, values and gates (as the replay stages them)
+    const uint16_t *kbp = static_cast<const uint16_t *>(Pp.k) + ((size_t)ip.x * Pp.Hk + g) * D;
+    const uint16_t *vgp = static_cast<const uint16_t *>(Pp.v) + ((size_t)ip.x * Pp.Hv + h) * D;
+    constexpr int KC = kPath * D / 8, K_PER = (KC + NT - 1) / NT;
+    constexpr int VC = kPath * D / 8, V_PER = (VC + NT - 1) / NT;
+    static_assert(KC % NT == 0 && VC % NT == 0, "whole table rounds");
+    auto node_of = [&](int e) {
+        const int x = __shfl(pl, e);  // every lane takes part in the shuffle
+        return e < len ? max(x, 0) : 0;
+    };
+    uint4 kr[K_PER], vr[V_PER];
+    float pga = 0.0f, pgb = 0.0f;
+    if (persist) {
+        int nk[K_PER], nv[V_PER];
+#pragma unroll
+        for (int u = 0; u < K_PER; ++u) nk[u] = node_of(((tid + u * NT) / (D / 8)) % kPath);
+#pragma unroll
+        for (int u = 0; u < V_PER; ++u) nv[u] = node_of(((tid + u * NT) / (D / 8)) % kPath);
+        const int ng = node_of(tid % kPath);
+#pragma unroll
+        for (int u = 0; u < K_PER; ++u)
+            kr[u] = *reinterpret_cast<const uint4 *>(kbp + (size_t)nk[u] * Pp.Hk * D + 8 * ((tid + u * NT) % (D / 8)));
+#pragma unroll
+        for (int u = 0; u < V_PER; ++u)
+            vr[u] = *reinterpret_cast<const uint4 *>(vgp + (size_t)nv[u] * Pp.Hv * D + 8 * ((tid + u * NT) % (D / 8)));
+        const size_t at = (size_t)(ip.x + ng) * Pp.Hv + h;
+        pga = Pp.a[at];
+        pgb = Pp.b[at];
+    }
+    // new step: keys and queries of the tree, the head's gates, the lane's values
+    const uint16_t *kbn = static_cast<const uint16_t *>(Pn.k) + ((size_t)lo * Pn.Hk + g) * D;
+    const uint16_t *qbn = static_cast<const uint16_t *>(Pn.q) + ((size_t)lo * Pn.Hk + g) * D;
+    constexpr int KQ_PER = (2 * kTile * D / 8 + NT - 1) / NT;
+    uint4 kqv[KQ_PER];
+    uint16_t vraw[16];
+    float nga = 0.0f, ngb = 0.0f;
+    if (verified) {
+#pragma unroll
+        for (int u = 0; u < KQ_PER; ++u) {
+            const int idx = tid + u * NT;
+            const int which = idx / (kTile * (D / 8)), rem = idx % (kTile * (D / 8));
+            const int i = rem / (D / 8), c8 = rem % (D / 8);
+            kqv[u] = (which < 2 && i < n)
+                         ? *reinterpret_cast<const uint4 *>((which ? qbn : kbn) + (size_t)i * kq_stride + 8 * c8)
+                         : make_uint4(0, 0, 0, 0);
+        }
+        if (tid < n) {
+            const size_t at = (size_t)(lo + tid) * Pn.Hv + h;
+            nga = Pn.a[at];
+            ngb = Pn.b[at];
+        }
+    }
+    // the state (the persist's source: its previous slot) and the lane's values of the new
+    // tree, issued per wave once the tables are in LDS
+    const float *s0 = Pn.state_in + ((size_t)slot * Pn.Hv + h) * D * D;
+    const float *sp = Pn.state_in + ((size_t)(persist ? pslot : slot) * Pn.Hv + h) * D * D;
+    const unsigned s_lane = (unsigned)(row * D + 4 * hf);
+    const uint16_t *vl = static_cast<const uint16_t *>(Pn.v) + ((size_t)lo * Pn.Hv + h) * D + row;
+    f32x16 SA[D / 32];
+    auto issue = [&]() {
+        load_state_tiles<D>(sp, s_lane, SA);
+        if (verified) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = 8 * (r / 4) + 4 * hf + (r % 4);
+                vraw[r] = i < n ? vl[(size_t)i * Pn.Hv * D] : (uint16_t)0;
+            }
+        }
+    };
+
+    // ---- tables into LDS
+    if (persist) {
+#pragma unroll
+        for (int u = 0; u < K_PER; ++u) {
+            const int idx = tid + u * NT, e = idx / (D / 8), c8 = idx % (D / 8);
+            const uint4 kv = e < len ? kr[u] : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4 *>(Lp.k + e * PTab<D>::KP + 8 * c8) = kv;
+            const uint16_t *hv = reinterpret_cast<const uint16_t *>(&kv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) Lp.kt[(8 * c8 + i) * PTab<D>::KT + e] = hv[i];
+        }
+#pragma unroll
+        for (int u = 0; u < V_PER; ++u) {
+            const int idx = tid + u * NT;
+            reinterpret_cast<uint4 *>(Lp.v)[idx] = idx / (D / 8) < len ? vr[u] : make_uint4(0, 0, 0, 0);
+        }
+        if (tid < kPath) {
+            const bool on = tid < len;
+            Lp.a[tid] = on ? pga : 1.0f;
+            Lp.b[tid] = on ? pgb : 0.0f;
+        }
+    }
+    if (verified) {
+        if (tid < n) {
+#pragma unroll
+            for (int e = 0; e < kPath; ++e) Ln.anc[tid * Q::PS + e] = an[e];
+            Ln.depth[tid] = d;
+            Ln.a[tid] = nga;
+            Ln.b[tid] = ngb;
+        }
+#pragma unroll
+        for (int u = 0; u < KQ_PER; ++u) {
+            const int idx = tid + u * NT;
+            if (idx < 2 * kTile * (D / 8))
+                *reinterpret_cast<uint4 *>(Ln.kq + (idx / (D / 8)) * Q::KQ + 8 * (idx % (D / 8))) = kqv[u];
+        }
+        for (int idx = tid; idx < kTile * Q::MT / 2; idx += NT) {
+            reinterpret_cast<uint32_t *>(Ln.mth)[idx] = 0u;
+            reinterpret_cast<uint32_t *>(Ln.mtl)[idx] = 0u;
+        }
+    }
+    __syncthreads();
+
+    // ---- coefficients: the new tree's on wave 0, the accepted path's on wave 1, no
+    // barrier inside either (one wave's LDS accesses take effect in program order).  The
+    // other waves issue their states meanwhile; wave 0 issues its own after the phase.
+    if (uni(w) == 0) {
+        if (verified) group_coefficients<D, false, 1>(Ln, n, lane, hf, l32);
+    } else {
+        issue();
+        if (uni(w) == 1 && persist) {
+            replay_gram<D, false>(Lp, l32, hf);
+            __builtin_amdgcn_wave_barrier();
+            if (lane < kPath) replay_coef_entry<D>(Lp, len, 0, lane);
+        }
+    }
+    __syncthreads();
+    if (uni(w) == 0) issue();
+
+    // ---- the persist: S <- the state after the accepted path, written in place
+    if (persist) replay_head<D, false>(SA, Lp, 1, 0, len, l32, hf, row,
+                                       Pn.state_out + ((size_t)pslot * Pn.Hv + h) * D * D, s_lane);
+    if (!verified) return;
+    if (persist && pslot != slot) load_state_tiles<D>(s0, s_lane, SA);  // the verify's own source
+
+    // ---- the verify from the registers: X = S K^T, Y = S Q^T, k-step s over tile s/2,
+    // registers 8(s%2) .. 8(s%2)+7 (columns 32t + 16u + 8(e/4) + 4*half + e%4)
+    f32x16 ax = {}, ay = {};
+    const uint16_t *krow = Ln.kq + l32 * Q::KQ, *qrow = Ln.kq + (kTile + l32) * Q::KQ;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const int t = s / 2, u = s % 2;
+        bf16x8 shi, slo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = SA[t][8 * u + e];
+            const __bf16 hb = static_cast<__bf16>(x);
+            shi[e] = hb;
+            slo[e] = static_cast<__bf16>(x - static_cast<float>(hb));
+        }
+        const uint2 k0 = *reinterpret_cast<const uint2 *>(krow + 32 * t + 16 * u + 4 * hf);
+        const uint2 k1 = *reinterpret_cast<const uint2 *>(krow + 32 * t + 16 * u + 8 + 4 * hf);
+        const uint2 q0 = *reinterpret_cast<const uint2 *>(qrow + 32 * t + 16 * u + 4 * hf);
+        const uint2 q1 = *reinterpret_cast<const uint2 *>(qrow + 32 * t + 16 * u + 8 + 4 * hf);
+        const bf16x8 Ak = __builtin_bit_cast(bf16x8, make_uint4(k0.x, k0.y, k1.x, k1.y));
+        const bf16x8 Aq = __builtin_bit_cast(bf16x8, make_uint4(q0.x, q0.y, q1.x, q1.y));
+        ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, shi, ax, 0, 0, 0);
+        ax = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak, slo, ax, 0, 0, 0);
+        ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, shi, ay, 0, 0, 0);
+        ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq, slo, ay, 0, 0, 0);
+    }
+    // r = b v - alpha x and gamma y in the accumulator layout (node 8(r/4) + 4*half + r%4)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int i = 8 * (r / 4) + 4 * hf + (r % 4);
+        const float4 q4 = Ln.gab[min(i, n - 1)];
+        ax[r] = i < n ? fmaf(-q4.y, ax[r], q4.z * bf2f(vraw[r])) : 0.0f;
+        ay[r] = i < n ? q4.x * ay[r] : 0.0f;
+    }
+    // O = gamma y + MT R on bf16 MFMA, both operands split hi + lo (lo x lo dropped)
+    const uint16_t *mh = Ln.mth + l32 * Q::MT, *ml = Ln.mtl + l32 * Q::MT;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const uint2 h0 = *reinterpret_cast<const uint2 *>(mh + 16 * u + 4 * hf);
+        const uint2 h1 = *reinterpret_cast<const uint2 *>(mh + 16 * u + 8 + 4 * hf);
+        const uint2 l0 = *reinterpret_cast<const uint2 *>(ml + 16 * u + 4 * hf);
+        const uint2 l1 = *reinterpret_cast<const uint2 *>(ml + 16 * u + 8 + 4 * hf);
+        const bf16x8 ahi = __builtin_bit_cast(bf16x8, make_uint4(h0.x, h0.y, h1.x, h1.y));
+        const bf16x8 alo = __builtin_bit_cast(bf16x8, make_uint4(l0.x, l0.y, l1.x, l1.y));
+        bf16x8 bhi, blo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float rv = ax[8 * u + e];
+            const __bf16 rb = static_cast<__bf16>(rv);
+            bhi[e] = rb;
+            blo[e] = static_cast<__bf16>(rv - static_cast<float>(rb));
+        }
+        ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bhi, ay, 0, 0, 0);
+        ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, blo, ay, 0, 0, 0);
+        ay = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bhi, ay, 0, 0, 0);
+    }
+    const unsigned out_lane = (unsigned)(4 * hf * Pn.Hv * D + row);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int ir = 8 * (r / 4) + (r % 4);  // node of half-wave 0; half-wave 1 adds 4
+        if (ir + 4 * hf < n) {
+            float *ob = Pn.out + ((size_t)(lo + ir) * Pn.Hv + h) * D;
+            ob[out_lane] = ay[r];
+        }
+    }
+}
+
+template <int D>
+hipError_t launch_fused_d(const Params &pp, const Params &pn, hipStream_t s) {
+    const size_t lds = fused_lds_bytes<D>();
+    if (lds > 65536) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(persist_verify_kernel<D>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(persist_verify_kernel<D>, dim3(pn.B * pn.Hv), dim3(VG<D>::THREADS), lds, s, pp, pn);
+    return hipGetLastError();
+}
+
 template <typename K>
 hipError_t launch_with_lds(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, const Params &p) {
     if (lds > 65536) {
@@ -2456,6 +2828,14 @@ hipError_t launch_tree_verify_fast(const Params &p, hipStream_t s) {
 hipError_t launch_persist_fast(const Params &p, hipStream_t s) {
     if (p.B == 0) return hipSuccess;
     return replay_any(p, false, s);
+}
+// The fused persist + verify: bf16 inputs, D 64 or 128, new trees of at most 32 nodes.
+bool fused_supported(int D, int dtype, int max_nodes) {
+    return (D == 64 || D == 128) && dtype == GDN_BF16 && max_nodes <= kTile;
+}
+hipError_t launch_persist_verify_fast(const Params &prev, const Params &next, hipStream_t s) {
+    if (next.B == 0) return hipSuccess;
+    return next.D == 64 ? launch_fused_d<64>(prev, next, s) : launch_fused_d<128>(prev, next, s);
 }
 // Chains of at most 16 nodes: outputs from the verify kernel in chain order
 // (so a chain-shaped tree and a chain give the same bits) and the final state

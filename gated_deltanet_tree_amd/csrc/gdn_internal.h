@@ -126,6 +126,8 @@ bool fast_tree_supported(int D, int dtype, int max_nodes, int heads_per_key);
 hipError_t launch_tree_verify_fast(const Params &p, hipStream_t s);
 hipError_t launch_chain_verify_fast(const Params &p, hipStream_t s);
 hipError_t launch_persist_fast(const Params &p, hipStream_t s);
+bool fused_supported(int D, int dtype, int max_nodes);
+hipError_t launch_persist_verify_fast(const Params &prev, const Params &next, hipStream_t s);
 // greedy acceptance over the verify logits
 hipError_t launch_accept(const Params &p, hipStream_t s);
 // draft candidates and the DDTree builder

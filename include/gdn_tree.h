@@ -108,7 +108,10 @@ typedef enum gdn_seq_status {
     GDN_SEQ_DUP_SLOT = 3,       /* slot shared by two non-empty sequences (both flagged) */
     GDN_SEQ_BAD_PARENT = 4,     /* parent outside {-1} U [0, n) or a node's own id */
     GDN_SEQ_CYCLE_OR_DEPTH = 5, /* an ancestor walk does not reach a root within max_depth nodes */
-    GDN_SEQ_BAD_ACCEPT = 6      /* accepted_node outside {-1} U [0, n) (set by persist) */
+    GDN_SEQ_BAD_ACCEPT = 6,     /* accepted_node outside {-1} U [0, n) (set by persist) */
+    GDN_SEQ_NOT_PERSISTED = 7   /* (gdn_tree_persist_verify, in the previous step's workspace) the
+                                   slot the accepted path would be written to is read by another
+                                   sequence's verify in the same call; the slot was not written */
 } gdn_seq_status;
 
 /* Traversal action word (one per visited position, see gdn_tree_plan). */
@@ -205,6 +208,51 @@ int gdn_tree_verify_static(const gdn_dims *dims, const int32_t *parent, const in
 int gdn_tree_persist(const gdn_dims *dims, const void *k, const void *v, const float *a,
                      const float *b, const int32_t *accepted_node, float *state_cache,
                      const int32_t *slot_idx, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * gdn_tree_persist_verify -- gdn_tree_persist of one decode step followed by
+ * gdn_tree_verify of the next, on one layer, in one pass over the state.  A
+ * layer's state is read by its verify and read and written by its persist
+ * (GreenGames page, "Key wins": the persist-write kernel writes the accepted
+ * node's state in place after acceptance; magik.net page, "The Broader
+ * Context": the tree of the next step is verified from that committed state).
+ * Deferring step t's persist until the layer's verify of step t+1 lets each
+ * (sequence, value head) load its state once, replay the accepted path of
+ * step t in registers, write the result in place and take step t+1's outputs
+ * from the same registers: two state passes per layer call instead of three.
+ *
+ * prev_dims, prev_k/v/a/b, accepted_node and prev_ws are exactly the
+ * arguments gdn_tree_persist would take for step t (prev_ws from
+ * gdn_tree_plan of step t; it receives the accepted path and the per-sequence
+ * verdicts of the persist).  dims, q/k/v/a/b, slot_idx, out and ws are those of
+ * gdn_tree_verify for step t+1 (ws from gdn_tree_plan of step t+1 with
+ * slot_idx); state_cache is the one cache both steps address, written in
+ * place.  The two dims must agree in num_seqs, heads, head_dim, num_slots and
+ * qkv_dtype (GDN_ERR_SHAPE otherwise); total_nodes, max_nodes and max_depth
+ * may differ.  Sequence b of one step is sequence b of the other; its slot in
+ * each step is the one that step's plan recorded.
+ *
+ * Results: out equals what gdn_tree_verify writes after gdn_tree_persist, to
+ * within the verify's rounding (the products sum the state's columns in
+ * another order), and every persisted slot holds the same bits gdn_tree_persist
+ * writes.  One exception keeps the call free of races: a sequence whose
+ * accepted path would be written to a slot that another sequence of step t+1
+ * verifies from is not persisted and is marked GDN_SEQ_NOT_PERSISTED in
+ * prev_ws (gdn_tree_status on prev_ws reports it); the caller may persist it
+ * with gdn_tree_persist and accepted_node = -1 for every other sequence.  A
+ * sequence whose step t+1 tree is rejected gets NaN outputs, as in verify.
+ * Either workspace planned for other dims makes the call write nothing and
+ * marks that workspace, as persist does.  Bf16 inputs with head_dim 64 or 128
+ * and step t+1 trees of at most 32 nodes run the fused kernel; every other
+ * shape runs gdn_tree_persist then gdn_tree_verify on `stream` (which never
+ * marks GDN_SEQ_NOT_PERSISTED: it persists before any verify reads).
+ */
+int gdn_tree_persist_verify(const gdn_dims *prev_dims, const void *prev_k, const void *prev_v,
+                            const float *prev_a, const float *prev_b, const int32_t *accepted_node,
+                            void *prev_ws, size_t prev_ws_bytes, const gdn_dims *dims, const void *q,
+                            const void *k, const void *v, const float *a, const float *b,
+                            float *state_cache, const int32_t *slot_idx, float *out, void *ws,
+                            size_t ws_bytes, void *stream);
 
 /*
  * gdn_tree_verify_store and gdn_tree_persist_copy -- the pages' own tree path,

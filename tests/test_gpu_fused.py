@@ -1,0 +1,281 @@
+"""GPU parity of gdn_tree_persist_verify: the persist of one decode step fused
+with the verify of the next on one layer.
+
+Bars: every slot the fused call writes holds the same bits as gdn_tree_persist
+followed by gdn_tree_verify (the replay arithmetic is shared); outputs within
+2e-3 per (sequence, value head) slice of the oracle's verify from the oracle's
+persisted states; slots nobody persists stay bitwise untouched; verdicts and
+the recorded accepted path as gdn_tree_persist leaves them."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_support import TOL, require_gpu, slice_rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _step(cfg, trees, layer):
+    cu = W.cu_from_trees(trees)
+    inp = W.make_layer_inputs(cfg, layer, trees)
+    return dict(trees=trees, cu=cu, inp=inp)
+
+
+def _dims(G, cfg, step, num_slots, max_nodes):
+    return G.make_dims(cfg.num_seqs, int(step["cu"][-1]), max_nodes, cfg.num_k_heads, cfg.num_v_heads, cfg.head_dim,
+                       num_slots, G.GDN_BF16, max_depth=cfg.max_depth)
+
+
+def _plan(G, dims, step, slots):
+    ws = G.new_workspace(dims)
+    parent = np.concatenate(step["trees"]).astype(np.int32) if len(step["trees"]) else np.zeros(0, np.int32)
+    G.gdn_tree_plan(dims, to_dev(parent), to_dev(step["cu"].astype(np.int32)), to_dev(slots.astype(np.int32)), ws)
+    return ws
+
+
+def _dev_inputs(step):
+    return {k: to_dev(v) for k, v in step["inp"].items()}
+
+
+def _expected_states(prev, S0_by_seq, acc):
+    """The oracle's persisted state per sequence (None where nothing is persisted)."""
+    res = oracle.persist_batch(prev["trees"], prev["cu"], prev["inp"], S0_by_seq, acc)
+    return [r[0] for r in res]
+
+
+def _run_pair(G, cfg, prev, nxt, slots_prev, slots_next, acc, cache0, num_slots, fused):
+    """Either gdn_tree_persist then gdn_tree_verify, or gdn_tree_persist_verify, on
+    a copy of cache0; returns outputs, cache and both workspaces."""
+    dp = _dims(G, cfg, prev, num_slots, max(int(np.diff(prev["cu"]).max(initial=1)), 1))
+    dn = _dims(G, cfg, nxt, num_slots, max(int(np.diff(nxt["cu"]).max(initial=1)), 1))
+    wsp = _plan(G, dp, prev, slots_prev)
+    wsn = _plan(G, dn, nxt, slots_next)
+    xp, xn = _dev_inputs(prev), _dev_inputs(nxt)
+    cache = to_dev(cache0.copy())
+    T = int(nxt["cu"][-1])
+    out = torch.full((max(T, 1), cfg.num_v_heads, cfg.head_dim), float("inf"), device="cuda")[:T]
+    acc_d = to_dev(acc.astype(np.int32))
+    sl_p, sl_n = to_dev(slots_prev.astype(np.int32)), to_dev(slots_next.astype(np.int32))
+    if fused:
+        G.gdn_tree_persist_verify(dp, xp["k"], xp["v"], xp["a"], xp["b"], acc_d, wsp, dn, xn["q"], xn["k"], xn["v"],
+                                  xn["a"], xn["b"], cache, sl_n, out, wsn)
+    else:
+        G.gdn_tree_persist(dp, xp["k"], xp["v"], xp["a"], xp["b"], acc_d, cache, sl_p, wsp)
+        G.gdn_tree_verify(dn, xn["q"], xn["k"], xn["v"], xn["a"], xn["b"], cache, sl_n, out, wsn)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), cache.cpu().numpy(), (dp, wsp), (dn, wsn)
+
+
+def _check_outputs(cfg, nxt, out, S_by_seq, ok_seqs):
+    # sequences left out of the check get a chain of their size for the oracle (a rejected
+    # tree is not a tree)
+    trees = [t if s in ok_seqs else W.chain_tree(len(t)) for s, t in enumerate(nxt["trees"])]
+    exp = oracle.verify_batch(trees, nxt["cu"], nxt["inp"], S_by_seq)
+    hv = cfg.num_v_heads
+    worst = 0.0
+    for s in ok_seqs:
+        lo, hi = int(nxt["cu"][s]), int(nxt["cu"][s + 1])
+        if hi == lo:
+            continue
+        e = slice_rel_err(out[lo:hi].transpose(1, 0, 2).reshape(hv, -1), exp[lo:hi].transpose(1, 0, 2).reshape(hv, -1))
+        assert e <= TOL, (s, e)
+        worst = max(worst, e)
+    return worst
+
+
+@pytest.mark.parametrize("d_", [64, 128])
+def test_fused_equals_persist_then_verify_batched(d_):
+    """32 sequences of budget-22 DDTrees (48/16 heads) for both steps, new trees and
+    inputs in the second, some sequences with nothing accepted; every slot bitwise
+    equal to the two-call path, outputs against the oracle, spare slots untouched."""
+    G = require_gpu()
+    base = W.get_config("batched")
+    cfg = dataclasses.replace(base, head_dim=d_)
+    cfg2 = dataclasses.replace(cfg, index=cfg.index + 40)
+    prev = _step(cfg, W.make_trees(cfg), 0)
+    nxt = _step(cfg2, W.make_trees(cfg2), 1)
+    slots = W.make_slots(cfg)
+    acc = W.make_accepts(cfg, prev["trees"]).copy()
+    acc[::5] = -1
+    num_slots = cfg.num_slots + 3
+    S0 = oracle.initial_states(W.make_prefill(cfg, 0), cfg.num_v_heads, d_)
+    rng = np.random.default_rng(5)
+    cache0 = rng.standard_normal((num_slots, cfg.num_v_heads, d_, d_)).astype(np.float32)
+    cache0[slots] = S0
+    print("fused batched d=%d" % d_, flush=True)
+    o_sep, c_sep, (_, wsp_sep), _ = _run_pair(G, cfg, prev, nxt, slots, slots, acc, cache0, num_slots, False)
+    o_fu, c_fu, (dp, wsp), (dn, wsn) = _run_pair(G, cfg, prev, nxt, slots, slots, acc, cache0, num_slots, True)
+    assert np.array_equal(c_fu.view(np.uint32), c_sep.view(np.uint32))
+    spare = np.setdiff1d(np.arange(num_slots), slots)
+    assert np.array_equal(c_fu[spare].view(np.uint32), cache0[spare].view(np.uint32))
+    S1 = _expected_states(prev, S0, acc)
+    S_new = np.stack([S1[s] if S1[s] is not None else S0[s] for s in range(cfg.num_seqs)])
+    for s in range(cfg.num_seqs):
+        assert slice_rel_err(c_fu[slots[s]].reshape(cfg.num_v_heads, -1), S_new[s].reshape(cfg.num_v_heads, -1)) <= TOL
+    worst = _check_outputs(cfg, nxt, o_fu, S_new, set(range(cfg.num_seqs)))
+    # the two paths' outputs differ only by the order the products sum the state's columns
+    assert np.abs(o_fu - o_sep).max() <= 1e-4 * np.abs(o_sep).max()
+    rc, bad, code = G.gdn_tree_status(wsp)
+    assert rc == 0, (rc, bad, code)
+    md_f = {k: v.cpu().numpy() for k, v in G.read_metadata(dp, wsp).items()}
+    md_s = {k: v.cpu().numpy() for k, v in G.read_metadata(dp, wsp_sep).items()}
+    live = acc >= 0
+    assert np.array_equal(md_f["path_len"][live], md_s["path_len"][live])
+    assert np.array_equal(md_f["path"][live], md_s["path"][live])
+    print("fused batched d=%d: worst output error %.2e" % (d_, worst), flush=True)
+
+
+def _ragged_case(d_=64):
+    cfg = dataclasses.replace(W.get_config("batched"), num_seqs=6, num_k_heads=2, num_v_heads=4, head_dim=d_,
+                              num_slots=8, index=77)
+    rng = np.random.default_rng(31)
+    sizes_p = [5, 23, 1, 17, 9, 32]
+    sizes_n = [12, 0, 7, 3, 32, 20]
+    trees_p = [W.random_tree(rng, n, 16) for n in sizes_p]
+    trees_n = [W.random_tree(rng, n, 16) for n in sizes_n]
+    return cfg, trees_p, trees_n
+
+
+def test_fused_ragged_empty_rejected_and_skipped():
+    """Six sequences at d = 64, two value heads per key head: a skipped accept, an
+    empty new tree, a rejected new tree (its sequence is still persisted: no other
+    verified sequence reads its slot), ragged sizes up to 32 nodes, two spare slots."""
+    G = require_gpu()
+    cfg, trees_p, trees_n = _ragged_case()
+    trees_n[3] = np.array([-1, 0, 2], dtype=np.int32)  # node 2 is its own parent: rejected
+    slots = np.array([3, 0, 5, 1, 4, 2])
+    acc = np.array([2, -1, 0, 16, 4, 31])
+    prev = _step(cfg, trees_p, 0)
+    nxt = _step(cfg, trees_n, 1)
+    num_slots = cfg.num_slots
+    S0 = oracle.initial_states(W.make_prefill(cfg, 0), cfg.num_v_heads, cfg.head_dim)
+    cache0 = np.random.default_rng(8).standard_normal((num_slots, cfg.num_v_heads, cfg.head_dim,
+                                                      cfg.head_dim)).astype(np.float32)
+    cache0[slots] = S0
+    print("fused ragged", flush=True)
+    o_sep, c_sep, _, _ = _run_pair(G, cfg, prev, nxt, slots, slots, acc, cache0, num_slots, False)
+    o_fu, c_fu, (dp, wsp), (dn, wsn) = _run_pair(G, cfg, prev, nxt, slots, slots, acc, cache0, num_slots, True)
+    assert np.array_equal(c_fu.view(np.uint32), c_sep.view(np.uint32))
+    assert np.array_equal(c_fu[[6, 7]].view(np.uint32), cache0[[6, 7]].view(np.uint32))
+    S1 = _expected_states(prev, S0, acc)
+    S_new = np.stack([S1[s] if S1[s] is not None else S0[s] for s in range(cfg.num_seqs)])
+    _check_outputs(cfg, nxt, o_fu, S_new, {0, 2, 4, 5})
+    lo, hi = int(nxt["cu"][3]), int(nxt["cu"][4])
+    assert np.isnan(o_fu[lo:hi]).all()
+    assert G.gdn_tree_status(wsp)[0] == 0
+    rc, bad, code = G.gdn_tree_status(wsn)
+    assert (rc, bad, code) == (-6, 3, 4)  # GDN_ERR_TREE: sequence 3, GDN_SEQ_BAD_PARENT
+
+
+def test_fused_slot_clash_is_not_persisted():
+    """Two sequences swap slots between the steps: each would write the slot the
+    other verifies from, so neither is persisted (both marked NOT_PERSISTED, both
+    slots untouched) and each is verified from the committed state in its new slot;
+    the other sequences are persisted and verified as usual."""
+    G = require_gpu()
+    cfg, trees_p, trees_n = _ragged_case()
+    trees_n[1] = W.random_tree(np.random.default_rng(4), 6, 16)
+    slots_p = np.array([3, 0, 5, 1, 4, 2])
+    slots_n = np.array([0, 3, 5, 1, 4, 2])
+    acc = np.array([2, 11, 0, 16, 4, 31])
+    prev = _step(cfg, trees_p, 0)
+    nxt = _step(cfg, trees_n, 1)
+    num_slots = cfg.num_slots
+    S0 = oracle.initial_states(W.make_prefill(cfg, 0), cfg.num_v_heads, cfg.head_dim)
+    cache0 = np.random.default_rng(9).standard_normal((num_slots, cfg.num_v_heads, cfg.head_dim,
+                                                      cfg.head_dim)).astype(np.float32)
+    cache0[slots_p] = S0
+    print("fused clash", flush=True)
+    o_fu, c_fu, (dp, wsp), _ = _run_pair(G, cfg, prev, nxt, slots_p, slots_n, acc, cache0, num_slots, True)
+    for sl in (0, 3, 6, 7):
+        assert np.array_equal(c_fu[sl].view(np.uint32), cache0[sl].view(np.uint32)), sl
+    S1 = _expected_states(prev, S0, acc)
+    for s in (2, 3, 4, 5):
+        assert slice_rel_err(c_fu[slots_p[s]].reshape(cfg.num_v_heads, -1),
+                             S1[s].reshape(cfg.num_v_heads, -1)) <= TOL
+    # the state each sequence is verified from: its new slot after the call
+    S_ver = np.stack([c_fu[slots_n[s]].astype(np.float64) if s in (0, 1) else S1[s] for s in range(cfg.num_seqs)])
+    _check_outputs(cfg, nxt, o_fu, S_ver, set(range(cfg.num_seqs)))
+    md = {k: v.cpu().numpy() for k, v in G.read_metadata(dp, wsp).items()}
+    assert list(md["seq_status"]) == [7, 7, 0, 0, 0, 0]
+    assert G.gdn_tree_status(wsp)[1:] == (0, 7)
+
+
+def test_fused_rejects_a_workspace_planned_for_other_dims():
+    """A previous-step workspace planned for another node count: nothing is
+    written (cache and outputs untouched) and that workspace reports misuse."""
+    G = require_gpu()
+    cfg, trees_p, trees_n = _ragged_case()
+    slots = np.array([3, 0, 5, 1, 4, 2])
+    acc = np.array([2, -1, 0, 16, 4, 31])
+    prev = _step(cfg, trees_p, 0)
+    nxt = _step(cfg, trees_n, 1)
+    cache0 = np.random.default_rng(10).standard_normal((cfg.num_slots, cfg.num_v_heads, cfg.head_dim,
+                                                       cfg.head_dim)).astype(np.float32)
+    dp = _dims(G, cfg, prev, cfg.num_slots, 32)
+    dn = _dims(G, cfg, nxt, cfg.num_slots, 32)
+    wsp = _plan(G, dp, prev, slots)
+    wsn = _plan(G, dn, nxt, slots)
+    dp_other = _dims(G, cfg, prev, cfg.num_slots, 24)  # the plan was made for max_nodes 32
+    xp, xn = _dev_inputs(prev), _dev_inputs(nxt)
+    cache = to_dev(cache0.copy())
+    out = torch.full((int(nxt["cu"][-1]), cfg.num_v_heads, cfg.head_dim), 7.0, device="cuda")
+    G.gdn_tree_persist_verify(dp_other, xp["k"], xp["v"], xp["a"], xp["b"], to_dev(acc.astype(np.int32)), wsp, dn,
+                              xn["q"], xn["k"], xn["v"], xn["a"], xn["b"], cache, to_dev(slots.astype(np.int32)), out,
+                              wsn)
+    torch.cuda.synchronize()
+    assert np.array_equal(cache.cpu().numpy().view(np.uint32), cache0.view(np.uint32))
+    assert (out.cpu().numpy() == 7.0).all()
+    assert G.gdn_tree_status(wsp)[0] == -4  # GDN_ERR_WORKSPACE
+
+
+def test_fused_graph_replays_match_eager():
+    """The fused call captured in a HIP graph: four replays (eager work and a
+    synchronization between them) each equal to the eager call bit for bit."""
+    G = require_gpu()
+    cfg, trees_p, trees_n = _ragged_case(128)
+    slots = np.array([3, 0, 5, 1, 4, 2])
+    acc = np.array([2, -1, 0, 16, 4, 31])
+    prev = _step(cfg, trees_p, 0)
+    nxt = _step(cfg, trees_n, 1)
+    cache0 = np.random.default_rng(12).standard_normal((cfg.num_slots, cfg.num_v_heads, cfg.head_dim,
+                                                       cfg.head_dim)).astype(np.float32)
+    dp = _dims(G, cfg, prev, cfg.num_slots, 32)
+    dn = _dims(G, cfg, nxt, cfg.num_slots, 32)
+    wsp = _plan(G, dp, prev, slots)
+    wsn = _plan(G, dn, nxt, slots)
+    xp, xn = _dev_inputs(prev), _dev_inputs(nxt)
+    acc_d, sl_d = to_dev(acc.astype(np.int32)), to_dev(slots.astype(np.int32))
+    src = to_dev(cache0.copy())
+    cache = src.clone()
+    out = torch.zeros((int(nxt["cu"][-1]), cfg.num_v_heads, cfg.head_dim), device="cuda")
+
+    def call():
+        G.gdn_tree_persist_verify(dp, xp["k"], xp["v"], xp["a"], xp["b"], acc_d, wsp, dn, xn["q"], xn["k"], xn["v"],
+                                  xn["a"], xn["b"], cache, sl_d, out, wsn)
+
+    call()
+    torch.cuda.synchronize()
+    ref_out, ref_cache = out.clone(), cache.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        cache.copy_(src)
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for _ in range(4):
+        cache.copy_(src)
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out)
+        assert torch.equal(cache.view(torch.int32), ref_cache.view(torch.int32))
