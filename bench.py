@@ -349,6 +349,39 @@ def measure(G, W, cfg, args, steps, warmup, distinct=0, path_label="auto"):
     gv = graph_us(verify_call, rotate * layers)
     gs = graph_us(persist_call, rotate * layers)
     g_plan, g_ver, g_per = gp["mean"] * 1e-6, gv["mean"] * 1e-6, gs["mean"] * 1e-6
+
+    # the fused layer call of a decode loop that defers each layer's persist to its next
+    # verify: gdn_tree_persist_verify replays the previous step's accepted path into the
+    # cache and verifies this step's trees from the same registers (one state read and one
+    # write instead of two reads and a write).  The previous step's inputs come from the
+    # copy half a rotation away, as persist's do above; both steps use the workload's trees.
+    fused = None
+    if cfg.dtype == "bf16" and cfg.head_dim in (64, 128) and cfg.max_nodes <= 32 and path_label == "auto":
+        ws_prev = G.new_workspace(dims)
+        G.gdn_tree_plan(dims, parent_d, cu_d, slot_d, ws_prev)
+        G.gdn_tree_plan(dims, parent_d, cu_d, slot_d, ws)
+
+        def fused_call(r):
+            rp = (r + rotate // 2) % rotate if layers == 1 else r
+            for l in range(layers):
+                d, p = sets[r * layers + l], sets[rp * layers + l]
+                G.gdn_tree_persist_verify(dims, p["k"], p["v"], p["a"], p["b"], acc_d, ws_prev, dims, d["q"], d["k"],
+                                          d["v"], d["a"], d["b"], d["cache"], slot_d, d["out"], ws)
+
+        gf = graph_us(fused_call, rotate * layers)
+        rc, bad, code = G.gdn_tree_status(ws_prev)
+        if rc != 0:
+            print(json.dumps({"error": "fused call rejected the %s workload: %d %d %d" % (cfg.name, rc, bad, code)}))
+            sys.exit(1)
+        g_fu = gf["mean"] * 1e-6
+        state_bytes = cfg.num_seqs * cfg.num_v_heads * cfg.head_dim * cfg.head_dim * 4
+        fbytes = vbytes + pbytes - state_bytes  # one state read fewer than verify + persist
+        fused = {"us": g_fu * 1e6, "us_pct": gf, "bytes": fbytes, "hbm_gbs": fbytes / g_fu / 1e9,
+                 "hbm_frac": fbytes / g_fu / 1e9 / HBM_PEAK_GBS, "nodes_per_s": T / g_fu,
+                 "vs_verify_plus_persist": (g_ver + g_per) / g_fu,
+                 "bytes_note": "verify + persist bytes less one read of the touched state slices",
+                 "timing": "graph replay of the fused call alone over the rotation (mean; spread in us_pct)"}
+        del ws_prev
     G.gdn_tree_plan(dims, parent_d, cu_d, slot_d, ws)
     torch.cuda.synchronize()
 
@@ -408,6 +441,8 @@ def measure(G, W, cfg, args, steps, warmup, distinct=0, path_label="auto"):
                        "eager": {"verify_us": t_ver * 1e6, "persist_us": t_per * 1e6, "plan_us": t_plan * 1e6}},
         "roofline": roof,
     }
+    if fused is not None:
+        res["fused_layer_call"] = fused
     ctx = dict(trees=trees, cu=cu, acc=acc, dims=dims, parent_d=parent_d, cu_d=cu_d, slot_d=slot_d, acc_d=acc_d,
                ws=ws, sets=sets, rotate=rotate, layers=layers, vbytes=vbytes, pbytes=pbytes, t_ver=t_ver,
                t_per=t_per)
@@ -511,6 +546,9 @@ def main():
                          "persist_frac": lc["persist_gbs"] / HBM_PEAK_GBS, "hbm_gbs": lc["hbm_gbs"],
                          "hbm_frac": lc["hbm_frac"], "layer_call_nodes_per_s": lc["nodes_per_s"],
                          "step_nodes_per_s": bres["value"], "rotated_copies": bres["config"]["rotated_copies"]})
+            if "fused_layer_call" in bres:
+                fl = bres["fused_layer_call"]
+                rows[-1]["fused"] = {"us": fl["us"], "hbm_frac": fl["hbm_frac"], "nodes_per_s": fl["nodes_per_s"]}
             del bctx
         result["batch_sweep"] = {"recipe": "the %s workload's trees and heads at other sequence counts" % cfg.name,
                                  "timing": "graph replay of each call alone over the rotation (mean)",

@@ -754,8 +754,9 @@ __device__ __forceinline__ void group_coefficients(const GTab<D> &L, int n, int 
     // one wave's LDS accesses take effect in program order: only the compiler must keep them
     __builtin_amdgcn_wave_barrier();
 
-    // per (value head, node) pair, lane and lane + 64: ratios, coefficients, output weights
-    constexpr int RND = (kGroupMaxHeads * kTile + 63) / 64;
+    // per (value head, node) pair, lane (and lane + 64 for more than two heads): ratios,
+    // coefficients, output weights
+    constexpr int RND = (GRP * kTile + 63) / 64;  // rounds of 64 (head, node) pairs
     float mrow[RND][kPath];
     int an_t[RND][kPath];
     int d_t[RND], hh_t[RND], i_t[RND];
@@ -2330,36 +2331,86 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
 // marked GDN_SEQ_NOT_PERSISTED in the previous workspace, so no slot is ever
 // written by one workgroup while another reads it.
 // ===========================================================================
+// LDS of the fused kernel, 39 KiB at D = 128 (three workgroups share a CU, as many as
+// its registers allow; 49 KiB kept the same three and measured 2 us slower per call):
+//  - the replay's tables that its coefficient phase needs (path keys, gates, Gram
+//    entries, coefficients);
+//  - the new tree's keys and queries, gates and output operator;
+//  - one region used twice: first the new tree's coefficient scratch (Gram entries in
+//    path order, coefficients, paths, gates, depths), then, once those are spent, the
+//    replay's transposed path keys and path values.
 template <int D>
-__host__ __device__ inline size_t fused_new_bytes() {
+struct FusedLayout {
     using Q = GPad<D>;
-    return (size_t)2 * kTile * Q::KQ * 2 + (size_t)kTile * 16 + (size_t)kTile * Q::MT * 4 + 4 * (size_t)kTile * Q::PS * 4 +
-           2 * (size_t)kTile * 4 + kTile * 4;
+    static constexpr size_t P_GAW = 0;
+    static constexpr size_t P_K = P_GAW + (size_t)kPath * 16;
+    static constexpr size_t P_GRAM = P_K + (size_t)kPath * PTab<D>::KP * 2;
+    static constexpr size_t P_COEF = P_GRAM + (size_t)kPath * (kPath + 1) * 4;
+    static constexpr size_t P_A = P_COEF + (size_t)kPath * (kPath + 1) * 4;
+    static constexpr size_t P_B = P_A + (size_t)kPath * 4;
+    static constexpr size_t N_KQ = P_B + (size_t)kPath * 4;
+    static constexpr size_t N_GAB = N_KQ + (size_t)2 * kTile * Q::KQ * 2;
+    static constexpr size_t N_MTH = N_GAB + (size_t)kTile * 16;
+    static constexpr size_t N_MTL = N_MTH + (size_t)kTile * Q::MT * 2;
+    static constexpr size_t U = N_MTL + (size_t)kTile * Q::MT * 2;  // the shared region
+    // first use: the new tree's coefficient scratch
+    static constexpr size_t N_COEF = U;
+    static constexpr size_t N_GK = N_COEF + (size_t)kTile * Q::PS * 4;
+    static constexpr size_t N_GQ = N_GK + (size_t)kTile * Q::PS * 4;
+    static constexpr size_t N_ANC = N_GQ + (size_t)kTile * Q::PS * 4;
+    static constexpr size_t N_A = N_ANC + (size_t)kTile * Q::PS * 4;
+    static constexpr size_t N_B = N_A + (size_t)kTile * 4;
+    static constexpr size_t N_DEPTH = N_B + (size_t)kTile * 4;
+    static constexpr size_t N_END = N_DEPTH + (size_t)kTile * 4;
+    // second use: the replay's transposed keys and values
+    static constexpr size_t P_KT = U;
+    static constexpr size_t P_V = P_KT + (size_t)D * PTab<D>::KT * 2;
+    static constexpr size_t P_END = P_V + (size_t)kPath * D * 2;
+    static constexpr size_t BYTES = N_END > P_END ? N_END : P_END;
+    static_assert(P_K % 16 == 0 && N_KQ % 16 == 0 && N_GAB % 16 == 0 && N_MTH % 8 == 0 && U % 16 == 0 &&
+                      N_DEPTH % 16 == 0 && P_V % 16 == 0,
+                  "16-byte aligned tables");
+};
+
+template <int D>
+__device__ inline PTab<D> fused_prev_carve(char *base) {
+    using F = FusedLayout<D>;
+    PTab<D> L;
+    L.gaw = reinterpret_cast<float4 *>(base + F::P_GAW);
+    L.k = L.klo = reinterpret_cast<uint16_t *>(base + F::P_K);
+    L.kt = L.ktlo = reinterpret_cast<uint16_t *>(base + F::P_KT);
+    L.v = reinterpret_cast<uint16_t *>(base + F::P_V);
+    L.vf = reinterpret_cast<float *>(base + F::P_V);
+    L.gram = reinterpret_cast<float *>(base + F::P_GRAM);
+    L.coefL = reinterpret_cast<float *>(base + F::P_COEF);
+    L.a = reinterpret_cast<float *>(base + F::P_A);
+    L.b = reinterpret_cast<float *>(base + F::P_B);
+    return L;
 }
 
 // the group verify's tables for one value head, without the staged values
 template <int D>
 __device__ inline GTab<D> fused_new_carve(char *base) {
-    using Q = GPad<D>;
+    using F = FusedLayout<D>;
     GTab<D> L;
-    L.kq = reinterpret_cast<uint16_t *>(base);     base += (size_t)2 * kTile * Q::KQ * 2;
+    L.kq = reinterpret_cast<uint16_t *>(base + F::N_KQ);
     L.v = nullptr;
-    L.gab = reinterpret_cast<float4 *>(base);      base += (size_t)kTile * 16;
-    L.mth = reinterpret_cast<uint16_t *>(base);    base += (size_t)kTile * Q::MT * 2;
-    L.mtl = reinterpret_cast<uint16_t *>(base);    base += (size_t)kTile * Q::MT * 2;
-    L.coefL = reinterpret_cast<float *>(base);     base += (size_t)kTile * Q::PS * 4;
-    L.gk = reinterpret_cast<float *>(base);        base += kTile * Q::PS * 4;
-    L.gq = reinterpret_cast<float *>(base);        base += kTile * Q::PS * 4;
-    L.anc = reinterpret_cast<int *>(base);         base += kTile * Q::PS * 4;
-    L.a = reinterpret_cast<float *>(base);         base += (size_t)kTile * 4;
-    L.b = reinterpret_cast<float *>(base);         base += (size_t)kTile * 4;
-    L.depth = reinterpret_cast<int *>(base);
+    L.gab = reinterpret_cast<float4 *>(base + F::N_GAB);
+    L.mth = reinterpret_cast<uint16_t *>(base + F::N_MTH);
+    L.mtl = reinterpret_cast<uint16_t *>(base + F::N_MTL);
+    L.coefL = reinterpret_cast<float *>(base + F::N_COEF);
+    L.gk = reinterpret_cast<float *>(base + F::N_GK);
+    L.gq = reinterpret_cast<float *>(base + F::N_GQ);
+    L.anc = reinterpret_cast<int *>(base + F::N_ANC);
+    L.a = reinterpret_cast<float *>(base + F::N_A);
+    L.b = reinterpret_cast<float *>(base + F::N_B);
+    L.depth = reinterpret_cast<int *>(base + F::N_DEPTH);
     return L;
 }
 
 template <int D>
 size_t fused_lds_bytes() {
-    return ptab_bytes<D>(1, false) + fused_new_bytes<D>();
+    return FusedLayout<D>::BYTES;
 }
 
 template <int D>
@@ -2432,8 +2483,8 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         if (tid == 0) Pp.ws.path_len[b] = len;
     }
 
-    const PTab<D> Lp = ptab_carve<D>(lds_raw, 1, false);
-    const GTab<D> Ln = fused_new_carve<D>(lds_raw + ptab_bytes<D>(1, false));
+    const PTab<D> Lp = fused_prev_carve<D>(lds_raw);
+    const GTab<D> Ln = fused_new_carve<D>(lds_raw);
     const size_t kq_stride = (size_t)Pn.Hk * D;
 
     // previous step: path keys, values and gates (as the replay stages them)
@@ -2489,14 +2540,13 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         }
     }
     // the state (the persist's source: its previous slot) and the lane's values of the new
-    // tree, issued per wave once the tables are in LDS
+    // tree, issued right behind the tables so that waiting for the tables does not wait for them
     const float *s0 = Pn.state_in + ((size_t)slot * Pn.Hv + h) * D * D;
     const float *sp = Pn.state_in + ((size_t)(persist ? pslot : slot) * Pn.Hv + h) * D * D;
     const unsigned s_lane = (unsigned)(row * D + 4 * hf);
     const uint16_t *vl = static_cast<const uint16_t *>(Pn.v) + ((size_t)lo * Pn.Hv + h) * D + row;
     f32x16 SA[D / 32];
-    auto issue = [&]() {
-        load_state_tiles<D>(sp, s_lane, SA);
+    auto issue_values = [&]() {
         if (verified) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -2513,14 +2563,6 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
             const int idx = tid + u * NT, e = idx / (D / 8), c8 = idx % (D / 8);
             const uint4 kv = e < len ? kr[u] : make_uint4(0, 0, 0, 0);
             *reinterpret_cast<uint4 *>(Lp.k + e * PTab<D>::KP + 8 * c8) = kv;
-            const uint16_t *hv = reinterpret_cast<const uint16_t *>(&kv);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) Lp.kt[(8 * c8 + i) * PTab<D>::KT + e] = hv[i];
-        }
-#pragma unroll
-        for (int u = 0; u < V_PER; ++u) {
-            const int idx = tid + u * NT;
-            reinterpret_cast<uint4 *>(Lp.v)[idx] = idx / (D / 8) < len ? vr[u] : make_uint4(0, 0, 0, 0);
         }
         if (tid < kPath) {
             const bool on = tid < len;
@@ -2549,13 +2591,14 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
     }
     __syncthreads();
 
-    // ---- coefficients: the new tree's on wave 0, the accepted path's on wave 1, no
-    // barrier inside either (one wave's LDS accesses take effect in program order).  The
-    // other waves issue their states meanwhile; wave 0 issues its own after the phase.
+    // ---- coefficients, while the states stream in: the new tree's on wave 0, the accepted
+    // path's on wave 1, no barrier inside either (one wave's LDS accesses take effect in
+    // program order)
     if (uni(w) == 0) {
         if (verified) group_coefficients<D, false, 1>(Ln, n, lane, hf, l32);
     } else {
-        issue();
+        load_state_tiles<D>(sp, s_lane, SA);
+        issue_values();
         if (uni(w) == 1 && persist) {
             replay_gram<D, false>(Lp, l32, hf);
             __builtin_amdgcn_wave_barrier();
@@ -2563,7 +2606,28 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         }
     }
     __syncthreads();
-    if (uni(w) == 0) issue();
+    if (uni(w) == 0) {
+        load_state_tiles<D>(sp, s_lane, SA);
+        issue_values();
+    }
+    if (persist) {
+        // the coefficient scratch is spent: the replay's transposed keys (from the keys in
+        // LDS) and its values take its place
+#pragma unroll
+        for (int u = 0; u < K_PER; ++u) {
+            const int idx = tid + u * NT, e = idx / (D / 8), c8 = idx % (D / 8);
+            const uint4 kv = *reinterpret_cast<const uint4 *>(Lp.k + e * PTab<D>::KP + 8 * c8);
+            const uint16_t *hv = reinterpret_cast<const uint16_t *>(&kv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) Lp.kt[(8 * c8 + i) * PTab<D>::KT + e] = hv[i];
+        }
+#pragma unroll
+        for (int u = 0; u < V_PER; ++u) {
+            const int idx = tid + u * NT;
+            reinterpret_cast<uint4 *>(Lp.v)[idx] = idx / (D / 8) < len ? vr[u] : make_uint4(0, 0, 0, 0);
+        }
+        __syncthreads();
+    }
 
     // ---- the persist: S <- the state after the accepted path, written in place
     if (persist) replay_head<D, false>(SA, Lp, 1, 0, len, l32, hf, row,
