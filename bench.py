@@ -377,7 +377,8 @@ def measure(G, W, cfg, args, steps, warmup, distinct=0, path_label="auto"):
         state_bytes = cfg.num_seqs * cfg.num_v_heads * cfg.head_dim * cfg.head_dim * 4
         fbytes = vbytes + pbytes - state_bytes  # one state read fewer than verify + persist
         fused = {"us": g_fu * 1e6, "us_pct": gf, "bytes": fbytes, "hbm_gbs": fbytes / g_fu / 1e9,
-                 "hbm_frac": fbytes / g_fu / 1e9 / HBM_PEAK_GBS, "nodes_per_s": T / g_fu,
+                 "hbm_frac": fbytes / g_fu / 1e9 / HBM_PEAK_GBS, "traffic": measured_traffic("fused", cfg.name),
+                 "nodes_per_s": T / g_fu,
                  "vs_verify_plus_persist": (g_ver + g_per) / g_fu,
                  "bytes_note": "verify + persist bytes less one read of the touched state slices",
                  "timing": "graph replay of the fused call alone over the rotation (mean; spread in us_pct)"}
@@ -714,6 +715,7 @@ def bench_snapshot(G, cfg, sets, slot_d, rotate, layers, steps):
 KERNEL_SOURCES = {
     "tree_verify": ("gdn_fast.hip", "gdn_internal.h"),
     "persist": ("gdn_fast.hip", "gdn_internal.h"),
+    "fused": ("gdn_fast.hip", "gdn_internal.h"),
     "accept": ("gdn_accept.hip", "gdn_internal.h"),
     "draft_topk": ("gdn_ddtree.hip", "gdn_internal.h"),
     "snapshot": ("gdn_snapshot.hip", "gdn_internal.h"),
