@@ -279,3 +279,55 @@ def test_fused_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(out, ref_out)
         assert torch.equal(cache.view(torch.int32), ref_cache.view(torch.int32))
+
+
+@pytest.mark.parametrize("shape", [("40 nodes", 128, "bf16", 40), ("fp32 inputs", 64, "f32", 20),
+                                   ("d = 32", 32, "bf16", 20)])
+def test_fused_entry_point_falls_back_to_the_two_calls(shape):
+    """Shapes the fused kernel does not take (trees over 32 nodes, fp32 inputs, a head
+    dim of 32) run gdn_tree_persist then gdn_tree_verify inside the call: outputs and
+    every slot bit for bit those of the two calls, and within 2e-3 of the oracle."""
+    G = require_gpu()
+    label, d_, dt, nmax = shape
+    cfg = dataclasses.replace(W.get_config("batched"), num_seqs=4, num_k_heads=2, num_v_heads=4, head_dim=d_,
+                              num_slots=6, index=91, dtype=dt)
+    rng = np.random.default_rng(17)
+    trees_p = [W.random_tree(rng, n, 16) for n in (nmax, 7, nmax - 3, 12)]
+    trees_n = [W.random_tree(rng, n, 16) for n in (9, nmax, 5, nmax - 1)]
+    slots = np.array([4, 1, 0, 3])
+    acc = np.array([nmax - 1, 3, -1, 11])
+    prev = _step(cfg, trees_p, 0)
+    nxt = _step(cfg, trees_n, 1)
+    S0 = oracle.initial_states(W.make_prefill(cfg, 0), cfg.num_v_heads, d_)
+    cache0 = np.random.default_rng(18).standard_normal((cfg.num_slots, cfg.num_v_heads, d_, d_)).astype(np.float32)
+    cache0[slots] = S0
+    qkv = G.GDN_F32 if dt == "f32" else G.GDN_BF16
+
+    def run(fused):
+        dp = G.make_dims(cfg.num_seqs, int(prev["cu"][-1]), nmax, cfg.num_k_heads, cfg.num_v_heads, d_,
+                         cfg.num_slots, qkv)
+        dn = G.make_dims(cfg.num_seqs, int(nxt["cu"][-1]), nmax, cfg.num_k_heads, cfg.num_v_heads, d_,
+                         cfg.num_slots, qkv)
+        wsp, wsn = _plan(G, dp, prev, slots), _plan(G, dn, nxt, slots)
+        xp, xn = _dev_inputs(prev), _dev_inputs(nxt)
+        cache = to_dev(cache0.copy())
+        out = torch.zeros((int(nxt["cu"][-1]), cfg.num_v_heads, d_), device="cuda")
+        acc_d, sl = to_dev(acc.astype(np.int32)), to_dev(slots.astype(np.int32))
+        if fused:
+            G.gdn_tree_persist_verify(dp, xp["k"], xp["v"], xp["a"], xp["b"], acc_d, wsp, dn, xn["q"], xn["k"],
+                                      xn["v"], xn["a"], xn["b"], cache, sl, out, wsn)
+        else:
+            G.gdn_tree_persist(dp, xp["k"], xp["v"], xp["a"], xp["b"], acc_d, cache, sl, wsp)
+            G.gdn_tree_verify(dn, xn["q"], xn["k"], xn["v"], xn["a"], xn["b"], cache, sl, out, wsn)
+        torch.cuda.synchronize()
+        assert G.gdn_tree_status(wsp)[0] == 0 and G.gdn_tree_status(wsn)[0] == 0
+        return out.cpu().numpy(), cache.cpu().numpy()
+
+    print("fused fallback:", label, flush=True)
+    o_f, c_f = run(True)
+    o_s, c_s = run(False)
+    assert np.array_equal(o_f.view(np.uint32), o_s.view(np.uint32))
+    assert np.array_equal(c_f.view(np.uint32), c_s.view(np.uint32))
+    S1 = _expected_states(prev, S0, acc)
+    S_new = np.stack([S1[s] if S1[s] is not None else S0[s] for s in range(cfg.num_seqs)])
+    _check_outputs(cfg, nxt, o_f, S_new, set(range(cfg.num_seqs)))
