@@ -379,6 +379,8 @@ def measure(G, W, cfg, args, steps, warmup, distinct=0, path_label="auto"):
         fused = {"us": g_fu * 1e6, "us_pct": gf, "bytes": fbytes, "hbm_gbs": fbytes / g_fu / 1e9,
                  "hbm_frac": fbytes / g_fu / 1e9 / HBM_PEAK_GBS, "traffic": measured_traffic("fused", cfg.name),
                  "nodes_per_s": T / g_fu,
+                 # a decode step of this schedule: the plan, then the fused call for each layer
+                 "step_nodes_per_s": T * layers / (g_plan + layers * g_fu),
                  "vs_verify_plus_persist": (g_ver + g_per) / g_fu,
                  "bytes_note": "verify + persist bytes less one read of the touched state slices",
                  "timing": "graph replay of the fused call alone over the rotation (mean; spread in us_pct)"}

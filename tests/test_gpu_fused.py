@@ -331,3 +331,41 @@ def test_fused_entry_point_falls_back_to_the_two_calls(shape):
     S1 = _expected_states(prev, S0, acc)
     S_new = np.stack([S1[s] if S1[s] is not None else S0[s] for s in range(cfg.num_seqs)])
     _check_outputs(cfg, nxt, o_f, S_new, set(range(cfg.num_seqs)))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_fused_seeded_sweep(seed):
+    """Seeded shapes for the fused kernel: 1-40 sequences, trees of 1-32 nodes (random
+    and chains), 1-4 value heads per key head, d 64 or 128, accepted nodes anywhere or
+    -1, a slot permutation with spare slots; slots and outputs bitwise equal to the two
+    calls' where the kernels share arithmetic (slots), outputs against the oracle."""
+    G = require_gpu()
+    rng = np.random.default_rng(1000 + seed)
+    d_ = int(rng.choice([64, 128]))
+    hk = int(rng.integers(1, 3))
+    ratio = int(rng.integers(1, 5))
+    B = int(rng.integers(1, 41))
+    cfg = dataclasses.replace(W.get_config("batched"), num_seqs=B, num_k_heads=hk, num_v_heads=hk * ratio,
+                              head_dim=d_, num_slots=B + 2, index=200 + seed)
+
+    def tree():
+        n = int(rng.integers(1, 33))
+        return W.chain_tree(min(n, 16)) if rng.random() < 0.2 else W.random_tree(rng, n, 16)
+
+    trees_p = [tree() for _ in range(B)]
+    trees_n = [tree() for _ in range(B)]
+    acc = np.array([int(rng.integers(-1, len(t))) for t in trees_p])
+    slots = rng.permutation(B + 2)[:B]
+    prev = _step(cfg, trees_p, 0)
+    nxt = _step(cfg, trees_n, 1)
+    S0 = oracle.initial_states(W.make_prefill(cfg, 0), cfg.num_v_heads, d_)
+    cache0 = rng.standard_normal((B + 2, cfg.num_v_heads, d_, d_)).astype(np.float32)
+    cache0[slots] = S0
+    print("fused sweep seed %d: B=%d hk=%d hv=%d d=%d" % (seed, B, hk, hk * ratio, d_), flush=True)
+    o_s, c_s, _, _ = _run_pair(G, cfg, prev, nxt, slots, slots, acc, cache0, B + 2, False)
+    o_f, c_f, (_, wsp), _ = _run_pair(G, cfg, prev, nxt, slots, slots, acc, cache0, B + 2, True)
+    assert np.array_equal(c_f.view(np.uint32), c_s.view(np.uint32))
+    assert G.gdn_tree_status(wsp)[0] == 0
+    S1 = _expected_states(prev, S0, acc)
+    S_new = np.stack([S1[s] if S1[s] is not None else S0[s] for s in range(B)])
+    _check_outputs(cfg, nxt, o_f, S_new, set(range(B)))
