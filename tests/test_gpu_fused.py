@@ -369,3 +369,53 @@ def test_fused_seeded_sweep(seed):
     S1 = _expected_states(prev, S0, acc)
     S_new = np.stack([S1[s] if S1[s] is not None else S0[s] for s in range(B)])
     _check_outputs(cfg, nxt, o_f, S_new, set(range(B)))
+
+
+def test_fused_off_path_inputs_leave_results_bitwise():
+    """P-anc through the fused call: perturbing the previous step's inputs off each
+    accepted path leaves every persisted slot unchanged bit for bit, and perturbing
+    the new trees' leaves (no node's ancestors) leaves every other node's outputs
+    unchanged bit for bit (32 sequences of 23-node DDTrees, 48/16 heads, d = 128)."""
+    G = require_gpu()
+    cfg = W.get_config("batched")
+    cfg2 = dataclasses.replace(cfg, index=cfg.index + 41)
+    prev = _step(cfg, W.make_trees(cfg), 0)
+    nxt = _step(cfg2, W.make_trees(cfg2), 1)
+    slots = W.make_slots(cfg)
+    acc = W.make_accepts(cfg, prev["trees"])
+    S0 = oracle.initial_states(W.make_prefill(cfg, 0), cfg.num_v_heads, cfg.head_dim)
+    cache0 = np.zeros((cfg.num_slots, cfg.num_v_heads, cfg.head_dim, cfg.head_dim), np.float32)
+    cache0[slots] = S0
+    rng = np.random.default_rng(77)
+
+    def perturb(step, rows):
+        out = dict(step)
+        inp = {k: v.copy() for k, v in step["inp"].items()}
+        for k, v in inp.items():
+            if v.dtype == np.uint16:  # bf16 bits: flip low mantissa bits
+                v[rows] ^= rng.integers(1, 64, size=v[rows].shape, dtype=np.uint16)
+            else:
+                v[rows] = v[rows] * np.float32(0.5) + np.float32(0.25)
+        out["inp"] = inp
+        return out
+
+    off_path, leaves = [], []
+    for s in range(cfg.num_seqs):
+        par, lo = prev["trees"][s], int(prev["cu"][s])
+        on, m = set(), int(acc[s])
+        while m >= 0:
+            on.add(m)
+            m = int(par[m])
+        off_path += [lo + i for i in range(len(par)) if i not in on]
+        parn, lon = nxt["trees"][s], int(nxt["cu"][s])
+        has_child = set(int(p) for p in parn if p >= 0)
+        leaves += [lon + i for i in range(len(parn)) if i not in has_child]
+    off_path, leaves = np.array(off_path), np.array(leaves)
+    print("fused P-anc: %d off-path nodes, %d leaves" % (len(off_path), len(leaves)), flush=True)
+    o_a, c_a, _, _ = _run_pair(G, cfg, prev, nxt, slots, slots, acc, cache0, cfg.num_slots, True)
+    o_b, c_b, _, _ = _run_pair(G, cfg, perturb(prev, off_path), perturb(nxt, leaves), slots, slots, acc, cache0,
+                               cfg.num_slots, True)
+    assert np.array_equal(c_a.view(np.uint32), c_b.view(np.uint32))
+    keep = np.setdiff1d(np.arange(o_a.shape[0]), leaves)
+    assert np.array_equal(o_a[keep].view(np.uint32), o_b[keep].view(np.uint32))
+    assert not np.array_equal(o_a[leaves], o_b[leaves])  # the perturbation reached the leaves
