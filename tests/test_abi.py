@@ -112,3 +112,38 @@ def test_package_never_imports_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
                 assert "oracle/" not in text, f
+
+
+def test_persist_verify_host_checks(lib):
+    """gdn_tree_persist_verify's argument errors are reported before anything is
+    enqueued: the two steps' dims must agree in batch, heads, head dim, slots and
+    dtype; required pointers; both workspaces large enough."""
+    import gated_deltanet_tree_amd as G
+    one = ctypes.c_void_p(16)
+    prev = G.make_dims(4, 60, 23, 2, 4, 64, 6, G.GDN_BF16)
+    nxt = G.make_dims(4, 50, 20, 2, 4, 64, 6, G.GDN_BF16)   # node counts may differ
+    n_p, n_n = G.workspace_bytes(prev), G.workspace_bytes(nxt)
+
+    def call(dp, dn, ws_p=one, nb_p=n_p, ws_n=one, nb_n=n_n, acc=one, out=one):
+        return lib.gdn_tree_persist_verify(ctypes.byref(dp) if dp is not None else None, one, one, one, one, acc,
+                                           ws_p, nb_p, ctypes.byref(dn) if dn is not None else None, one, one, one,
+                                           one, one, one, one, out, ws_n, nb_n, None)
+
+    assert call(None, nxt) == -1
+    assert call(prev, None) == -1
+    for field, value in [("num_seqs", 5), ("num_k_heads", 1), ("num_v_heads", 8), ("head_dim", 128),
+                         ("num_slots", 7), ("qkv_dtype", G.GDN_F32)]:
+        other = G.make_dims(4, 50, 20, 2, 4, 64, 6, G.GDN_BF16)
+        setattr(other, field, value)
+        if field == "num_seqs":
+            other.num_slots = 6
+        assert call(prev, other) == -2, field
+    assert call(prev, nxt, ws_p=None) == -1
+    assert call(prev, nxt, ws_n=None) == -1
+    assert call(prev, nxt, acc=None) == -1
+    assert call(prev, nxt, out=None) == -1
+    assert call(prev, nxt, nb_p=n_p - 1) == -4
+    assert call(prev, nxt, nb_n=n_n - 1) == -4
+    empty = G.make_dims(0, 0, 1, 2, 4, 64, 0, G.GDN_BF16)
+    n_e = G.workspace_bytes(empty)
+    assert call(empty, empty, nb_p=n_e, nb_n=n_e) == 0  # nothing to do: returns before any launch
