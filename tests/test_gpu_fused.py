@@ -419,3 +419,36 @@ def test_fused_off_path_inputs_leave_results_bitwise():
     keep = np.setdiff1d(np.arange(o_a.shape[0]), leaves)
     assert np.array_equal(o_a[keep].view(np.uint32), o_b[keep].view(np.uint32))
     assert not np.array_equal(o_a[leaves], o_b[leaves])  # the perturbation reached the leaves
+
+
+def test_fused_rejected_previous_tree_and_bad_accept():
+    """A previous-step tree the plan rejected is not persisted, and an accepted node
+    out of range marks GDN_SEQ_BAD_ACCEPT and persists nothing, exactly as
+    gdn_tree_persist does; both sequences are still verified from their committed
+    state.  Slots and verdicts equal to the two calls', outputs against the oracle."""
+    G = require_gpu()
+    cfg, trees_p, trees_n = _ragged_case(128)
+    trees_p[2] = np.array([-1, 0, 5], dtype=np.int32)  # parent 5 outside the 3-node tree: rejected
+    slots = np.array([3, 0, 5, 1, 4, 2])
+    acc = np.array([2, 40, 0, 16, 4, 31])  # sequence 1's 23-node tree has no node 40
+    prev = _step(cfg, trees_p, 0)
+    nxt = _step(cfg, trees_n, 1)
+    S0 = oracle.initial_states(W.make_prefill(cfg, 0), cfg.num_v_heads, cfg.head_dim)
+    cache0 = np.random.default_rng(21).standard_normal((cfg.num_slots, cfg.num_v_heads, cfg.head_dim,
+                                                       cfg.head_dim)).astype(np.float32)
+    cache0[slots] = S0
+    print("fused rejected previous tree, bad accept", flush=True)
+    o_s, c_s, (dp, wsp_s), _ = _run_pair(G, cfg, prev, nxt, slots, slots, acc, cache0, cfg.num_slots, False)
+    o_f, c_f, (_, wsp_f), _ = _run_pair(G, cfg, prev, nxt, slots, slots, acc, cache0, cfg.num_slots, True)
+    assert np.array_equal(c_f.view(np.uint32), c_s.view(np.uint32))
+    for sl in (slots[1], slots[2]):
+        assert np.array_equal(c_f[sl].view(np.uint32), cache0[sl].view(np.uint32))
+    st_f = G.read_metadata(dp, wsp_f)["seq_status"].cpu().numpy()
+    st_s = G.read_metadata(dp, wsp_s)["seq_status"].cpu().numpy()
+    assert np.array_equal(st_f, st_s) and st_f[1] == 6 and st_f[2] == 4, (st_f, st_s)
+    acc_ok = acc.copy()
+    acc_ok[[1, 2]] = -1
+    S1 = _expected_states(dict(prev, trees=[t if s != 2 else W.chain_tree(3) for s, t in enumerate(prev["trees"])]),
+                          S0, acc_ok)
+    S_new = np.stack([S1[s] if S1[s] is not None else S0[s] for s in range(cfg.num_seqs)])
+    _check_outputs(cfg, nxt, o_f, S_new, set(range(cfg.num_seqs)) - {1})  # sequence 1's new tree is empty
