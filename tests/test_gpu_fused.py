@@ -452,3 +452,29 @@ def test_fused_rejected_previous_tree_and_bad_accept():
                           S0, acc_ok)
     S_new = np.stack([S1[s] if S1[s] is not None else S0[s] for s in range(cfg.num_seqs)])
     _check_outputs(cfg, nxt, o_f, S_new, set(range(cfg.num_seqs)) - {1})  # sequence 1's new tree is empty
+
+
+def test_fused_after_a_step_with_large_trees():
+    """The fused kernel is chosen by the new step's trees (at most 32 nodes); the
+    previous step's may be larger (here 60-200 nodes: its accepted path is still at
+    most 16 nodes).  Slots bitwise equal to the two calls, outputs against the oracle."""
+    G = require_gpu()
+    cfg = dataclasses.replace(W.get_config("batched"), num_seqs=5, num_k_heads=2, num_v_heads=6, head_dim=128,
+                              num_slots=7, index=131)
+    rng = np.random.default_rng(41)
+    trees_p = [W.random_tree(rng, n, 16) for n in (60, 200, 97, 128, 75)]
+    trees_n = [W.random_tree(rng, n, 16) for n in (32, 9, 23, 1, 30)]
+    slots = np.array([6, 2, 0, 4, 3])
+    acc = np.array([int(rng.integers(0, len(t))) for t in trees_p])
+    prev = _step(cfg, trees_p, 0)
+    nxt = _step(cfg, trees_n, 1)
+    S0 = oracle.initial_states(W.make_prefill(cfg, 0), cfg.num_v_heads, cfg.head_dim)
+    cache0 = rng.standard_normal((cfg.num_slots, cfg.num_v_heads, cfg.head_dim, cfg.head_dim)).astype(np.float32)
+    cache0[slots] = S0
+    print("fused after large trees", flush=True)
+    o_s, c_s, _, _ = _run_pair(G, cfg, prev, nxt, slots, slots, acc, cache0, cfg.num_slots, False)
+    o_f, c_f, (_, wsp), _ = _run_pair(G, cfg, prev, nxt, slots, slots, acc, cache0, cfg.num_slots, True)
+    assert np.array_equal(c_f.view(np.uint32), c_s.view(np.uint32))
+    assert G.gdn_tree_status(wsp)[0] == 0
+    S1 = _expected_states(prev, S0, acc)
+    _check_outputs(cfg, nxt, o_f, np.stack(S1), set(range(cfg.num_seqs)))
