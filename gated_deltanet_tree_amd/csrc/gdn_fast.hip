@@ -2487,35 +2487,16 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
     const GTab<D> Ln = fused_new_carve<D>(lds_raw);
     const size_t kq_stride = (size_t)Pn.Hk * D;
 
-    // previous step: path keys, values and gates (as the replay stages them)
+    // previous step: path keys, values and gates (as the replay stages them), loaded below
     const uint16_t *kbp = static_cast<const uint16_t *>(Pp.k) + ((size_t)ip.x * Pp.Hk + g) * D;
     const uint16_t *vgp = static_cast<const uint16_t *>(Pp.v) + ((size_t)ip.x * Pp.Hv + h) * D;
-    constexpr int KC = kPath * D / 8, K_PER = (KC + NT - 1) / NT;
-    constexpr int VC = kPath * D / 8, V_PER = (VC + NT - 1) / NT;
-    static_assert(KC % NT == 0 && VC % NT == 0, "whole table rounds");
+    constexpr int KC = kPath * D / 8, K_PER = KC / NT;  // 16-byte chunks of the path keys
+    constexpr int VC = kPath * D / 8;                    // and of the path values
+    static_assert(KC % NT == 0 && KC % 64 == 0 && VC % 64 == 0, "whole table rounds");
     auto node_of = [&](int e) {
-        const int x = __shfl(pl, e);  // every lane takes part in the shuffle
+        const int x = __shfl(pl, e);  // every lane of the wave takes part in the shuffle
         return e < len ? max(x, 0) : 0;
     };
-    uint4 kr[K_PER], vr[V_PER];
-    float pga = 0.0f, pgb = 0.0f;
-    if (persist) {
-        int nk[K_PER], nv[V_PER];
-#pragma unroll
-        for (int u = 0; u < K_PER; ++u) nk[u] = node_of(((tid + u * NT) / (D / 8)) % kPath);
-#pragma unroll
-        for (int u = 0; u < V_PER; ++u) nv[u] = node_of(((tid + u * NT) / (D / 8)) % kPath);
-        const int ng = node_of(tid % kPath);
-#pragma unroll
-        for (int u = 0; u < K_PER; ++u)
-            kr[u] = *reinterpret_cast<const uint4 *>(kbp + (size_t)nk[u] * Pp.Hk * D + 8 * ((tid + u * NT) % (D / 8)));
-#pragma unroll
-        for (int u = 0; u < V_PER; ++u)
-            vr[u] = *reinterpret_cast<const uint4 *>(vgp + (size_t)nv[u] * Pp.Hv * D + 8 * ((tid + u * NT) % (D / 8)));
-        const size_t at = (size_t)(ip.x + ng) * Pp.Hv + h;
-        pga = Pp.a[at];
-        pgb = Pp.b[at];
-    }
     // new step: keys and queries of the tree, the head's gates, the lane's values
     const uint16_t *kbn = static_cast<const uint16_t *>(Pn.k) + ((size_t)lo * Pn.Hk + g) * D;
     const uint16_t *qbn = static_cast<const uint16_t *>(Pn.q) + ((size_t)lo * Pn.Hk + g) * D;
@@ -2539,6 +2520,28 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
             ngb = Pn.b[at];
         }
     }
+    // previous step, wave 1 alone: it stages the path's keys, values and gates and forms
+    // their Gram entries and coefficients, so no other wave waits for this round trip
+    constexpr int K1 = KC / 64, V1 = VC / 64;  // 16-byte chunks per lane of wave 1
+    uint4 kr[K1], vr[V1];
+    float pga = 0.0f, pgb = 0.0f;
+    if (persist && uni(w) == 1) {
+        int nk[K1], nv[V1];
+#pragma unroll
+        for (int u = 0; u < K1; ++u) nk[u] = node_of(((lane + u * 64) / (D / 8)) % kPath);
+#pragma unroll
+        for (int u = 0; u < V1; ++u) nv[u] = node_of(((lane + u * 64) / (D / 8)) % kPath);
+        const int ng = node_of(lane % kPath);
+#pragma unroll
+        for (int u = 0; u < K1; ++u)
+            kr[u] = *reinterpret_cast<const uint4 *>(kbp + (size_t)nk[u] * Pp.Hk * D + 8 * ((lane + u * 64) % (D / 8)));
+#pragma unroll
+        for (int u = 0; u < V1; ++u)
+            vr[u] = *reinterpret_cast<const uint4 *>(vgp + (size_t)nv[u] * Pp.Hv * D + 8 * ((lane + u * 64) % (D / 8)));
+        const size_t at = (size_t)(ip.x + ng) * Pp.Hv + h;
+        pga = Pp.a[at];
+        pgb = Pp.b[at];
+    }
     // the state (the persist's source: its previous slot) and the lane's values of the new
     // tree, issued right behind the tables so that waiting for the tables does not wait for them
     const float *s0 = Pn.state_in + ((size_t)slot * Pn.Hv + h) * D * D;
@@ -2556,20 +2559,7 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
         }
     };
 
-    // ---- tables into LDS
-    if (persist) {
-#pragma unroll
-        for (int u = 0; u < K_PER; ++u) {
-            const int idx = tid + u * NT, e = idx / (D / 8), c8 = idx % (D / 8);
-            const uint4 kv = e < len ? kr[u] : make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4 *>(Lp.k + e * PTab<D>::KP + 8 * c8) = kv;
-        }
-        if (tid < kPath) {
-            const bool on = tid < len;
-            Lp.a[tid] = on ? pga : 1.0f;
-            Lp.b[tid] = on ? pgb : 0.0f;
-        }
-    }
+    // ---- the new tree's tables into LDS
     if (verified) {
         if (tid < n) {
 #pragma unroll
@@ -2592,14 +2582,26 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
     __syncthreads();
 
     // ---- coefficients, while the states stream in: the new tree's on wave 0, the accepted
-    // path's on wave 1, no barrier inside either (one wave's LDS accesses take effect in
-    // program order)
+    // path's on wave 1 (after staging its tables), no barrier inside either (one wave's LDS
+    // accesses take effect in program order)
     if (uni(w) == 0) {
         if (verified) group_coefficients<D, false, 1>(Ln, n, lane, hf, l32);
     } else {
         load_state_tiles<D>(sp, s_lane, SA);
         issue_values();
         if (uni(w) == 1 && persist) {
+#pragma unroll
+            for (int u = 0; u < K1; ++u) {
+                const int idx = lane + u * 64, e = idx / (D / 8), c8 = idx % (D / 8);
+                const uint4 kv = e < len ? kr[u] : make_uint4(0, 0, 0, 0);
+                *reinterpret_cast<uint4 *>(Lp.k + e * PTab<D>::KP + 8 * c8) = kv;
+            }
+            if (lane < kPath) {
+                const bool on = lane < len;
+                Lp.a[lane] = on ? pga : 1.0f;
+                Lp.b[lane] = on ? pgb : 0.0f;
+            }
+            __builtin_amdgcn_wave_barrier();
             replay_gram<D, false>(Lp, l32, hf);
             __builtin_amdgcn_wave_barrier();
             if (lane < kPath) replay_coef_entry<D>(Lp, len, 0, lane);
@@ -2621,10 +2623,12 @@ __global__ __launch_bounds__(VG<D>::THREADS) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
             for (int i = 0; i < 8; ++i) Lp.kt[(8 * c8 + i) * PTab<D>::KT + e] = hv[i];
         }
+        if (uni(w) == 1) {
 #pragma unroll
-        for (int u = 0; u < V_PER; ++u) {
-            const int idx = tid + u * NT;
-            reinterpret_cast<uint4 *>(Lp.v)[idx] = idx / (D / 8) < len ? vr[u] : make_uint4(0, 0, 0, 0);
+            for (int u = 0; u < V1; ++u) {
+                const int idx = lane + u * 64;
+                reinterpret_cast<uint4 *>(Lp.v)[idx] = idx / (D / 8) < len ? vr[u] : make_uint4(0, 0, 0, 0);
+            }
         }
         __syncthreads();
     }
