@@ -21,6 +21,10 @@ launches instead).  Per-call durations come from one graph per call kind
 kernels' stream); a separate eager pass with an event pair around every call
 gives the eager breakdown, which adds the host's launch gaps.
 
+`--schedule fused` times the deferred-persist schedule instead: a step is the
+plan and, per layer, one gdn_tree_persist_verify (the previous step's persist
+fused with this step's verify); two workspaces alternate between steps.
+
 Prints ONE JSON line.  `value` = tree nodes verified per second per layer call
 (plan + verify + persist); `roofline` describes the dominant kernel, timed with
 HIP events on the stream it runs on; `cpu_baseline` times the fp64 CPU oracle
@@ -73,6 +77,9 @@ def parse():
     ap.add_argument("--sweep", default="64,128,256",
                     help="sequence counts of the batch sweep sub-object (the same tree recipe; empty: none)")
     ap.add_argument("--sweep-steps", type=int, default=20)
+    ap.add_argument("--schedule", choices=["separate", "fused"], default="separate",
+                    help="fused: a step is the plan and one gdn_tree_persist_verify per layer (the previous "
+                         "step's persist with this step's verify), for workloads the fused kernel takes")
     return ap.parse_args()
 
 
@@ -151,8 +158,15 @@ def memory_ceilings(G, dev):
     return res
 
 
-def measure(G, W, cfg, args, steps, warmup, distinct=0, path_label="auto"):
-    """Times one workload: a step = plan + verify and persist for each layer.
+def fused_supported(cfg):
+    """The workloads gdn_tree_persist_verify runs as one kernel (other shapes run the two calls)."""
+    return cfg.dtype == "bf16" and cfg.head_dim in (64, 128) and cfg.max_nodes <= 32
+
+
+def measure(G, W, cfg, args, steps, warmup, distinct=0, path_label="auto", schedule="separate"):
+    """Times one workload: a step = plan + verify and persist for each layer, or with
+    schedule "fused" the plan + one fused persist + verify call per layer (each layer's
+    persist deferred to its next verify; two workspaces alternate between steps).
     Returns the workload's result fields and the state the extra measurements use."""
     import torch
     dev = torch.device("cuda:0")
@@ -189,6 +203,9 @@ def measure(G, W, cfg, args, steps, warmup, distinct=0, path_label="auto"):
     parent_d = to_dev(np.concatenate(trees).astype(np.int32))
     cu_d = to_dev(cu.astype(np.int32))
     ws = G.new_workspace(dims)
+    wss = [ws, G.new_workspace(dims)] if schedule == "fused" else [ws]
+    for w_ in wss[1:]:
+        G.gdn_tree_plan(dims, parent_d, cu_d, slot_d, w_)
     # committed states: each generated copy's cache is filled by the library's own
     # chain kernel running that copy's prefill tokens from a zero state
     pre_cu = torch.arange(0, (cfg.num_seqs + 1) * cfg.prefill_steps, cfg.prefill_steps, dtype=torch.int32,
@@ -225,6 +242,23 @@ def measure(G, W, cfg, args, steps, warmup, distinct=0, path_label="auto"):
 
     def step(i, events=None):
         r = i % rotate
+        if schedule == "fused":
+            # this step's plan goes to one workspace; the other holds the previous step's
+            # plan (the same trees), whose accepted paths the fused calls persist
+            wn, wp = wss[i % 2], wss[(i + 1) % 2]
+            rp = (r + rotate // 2) % rotate if layers == 1 else r
+            if events:
+                events[0].record(stream)
+            G.gdn_tree_plan(dims, parent_d, cu_d, slot_d, wn)
+            if events:
+                events[1].record(stream)
+            for l in range(layers):
+                d, p = sets[r * layers + l], sets[rp * layers + l]
+                G.gdn_tree_persist_verify(dims, p["k"], p["v"], p["a"], p["b"], acc_d, wp, dims, d["q"], d["k"],
+                                          d["v"], d["a"], d["b"], d["cache"], slot_d, d["out"], wn)
+                if events:
+                    events[2 + l].record(stream)
+            return
         if events:
             events[0].record(stream)
         G.gdn_tree_plan(dims, parent_d, cu_d, slot_d, ws)
@@ -248,7 +282,10 @@ def measure(G, W, cfg, args, steps, warmup, distinct=0, path_label="auto"):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    rc, bad, code = G.gdn_tree_status(ws)
+    for w_ in wss:
+        rc, bad, code = G.gdn_tree_status(w_)
+        if rc != 0:
+            break
     if rc != 0:
         print(json.dumps({"error": "library rejected the %s workload: %d %d %d" % (cfg.name, rc, bad, code)}))
         sys.exit(1)
@@ -356,7 +393,7 @@ def measure(G, W, cfg, args, steps, warmup, distinct=0, path_label="auto"):
     # write instead of two reads and a write).  The previous step's inputs come from the
     # copy half a rotation away, as persist's do above; both steps use the workload's trees.
     fused = None
-    if cfg.dtype == "bf16" and cfg.head_dim in (64, 128) and cfg.max_nodes <= 32 and path_label == "auto":
+    if fused_supported(cfg) and path_label == "auto":
         ws_prev = G.new_workspace(dims)
         G.gdn_tree_plan(dims, parent_d, cu_d, slot_d, ws_prev)
         G.gdn_tree_plan(dims, parent_d, cu_d, slot_d, ws)
@@ -388,10 +425,15 @@ def measure(G, W, cfg, args, steps, warmup, distinct=0, path_label="auto"):
     G.gdn_tree_plan(dims, parent_d, cu_d, slot_d, ws)
     torch.cuda.synchronize()
 
-    plan_ms, ver_ms, per_ms = [], [], []
+    plan_ms, ver_ms, per_ms, fu_ms = [], [], [], []
     for e in ev:
         plan_ms.append(e[0].elapsed_time(e[1]))
         prev = e[1]
+        if schedule == "fused":
+            for l in range(layers):
+                fu_ms.append(prev.elapsed_time(e[2 + l]))
+                prev = e[2 + l]
+            continue
         for l in range(layers):
             ver_ms.append(prev.elapsed_time(e[2 + l]))
             prev = e[2 + l]
@@ -399,8 +441,9 @@ def measure(G, W, cfg, args, steps, warmup, distinct=0, path_label="auto"):
             per_ms.append(prev.elapsed_time(e[2 + layers + l]))
             prev = e[2 + layers + l]
     t_plan = float(np.mean(plan_ms)) * 1e-3
-    t_ver = float(np.mean(ver_ms)) * 1e-3
-    t_per = float(np.mean(per_ms)) * 1e-3
+    # eager per-call figures of the calls the timed steps make
+    t_ver = float(np.mean(ver_ms)) * 1e-3 if ver_ms else None
+    t_per = float(np.mean(per_ms)) * 1e-3 if per_ms else None
     nodes_per_s = T * layers / (ms_per_step * 1e-3)
     hbm_gbs = (vbytes + pbytes) / (g_ver + g_per) / 1e9
 
@@ -408,7 +451,10 @@ def measure(G, W, cfg, args, steps, warmup, distinct=0, path_label="auto"):
     # ridge point of the matrix cores, so the bound is HBM bandwidth.  Its launch duration
     # is the graph-replay mean (the timed loop's launch mode); the eager figure, which adds
     # the host launch gap, is reported beside it.
-    if g_ver >= g_per:
+    if schedule == "fused":  # one kernel per layer call
+        dom, t_dom, t_dom_eager, dom_bytes, dom_pct = ("fused", fused["us"] * 1e-6, float(np.mean(fu_ms)) * 1e-3,
+                                                       fused["bytes"], fused["us_pct"])
+    elif g_ver >= g_per:
         dom, t_dom, t_dom_eager, dom_bytes, dom_pct = "tree_verify", g_ver, t_ver, vbytes, gv
     else:
         dom, t_dom, t_dom_eager, dom_bytes, dom_pct = "persist", g_per, t_per, pbytes, gs
@@ -429,7 +475,7 @@ def measure(G, W, cfg, args, steps, warmup, distinct=0, path_label="auto"):
         "config": {"workload": cfg.name, "sequences": cfg.num_seqs, "layers": layers, "nodes": T,
                    "v_heads": cfg.num_v_heads, "k_heads": cfg.num_k_heads, "head_dim": cfg.head_dim,
                    "qkv": cfg.dtype, "rotated_copies": rotate, "generated_copies": n_gen, "seed": cfg.seed,
-                   "kernels": path_label,
+                   "kernels": path_label, "schedule": schedule,
                    "launch": "eager" if args.eager else "hip_graph_per_%d_steps" % rotate},
         "layer_call": {"verify_us": g_ver * 1e6, "persist_us": g_per * 1e6, "plan_us": g_plan * 1e6,
                        "verify_us_pct": gv, "persist_us_pct": gs, "plan_us_pct": gp,
@@ -441,7 +487,9 @@ def measure(G, W, cfg, args, steps, warmup, distinct=0, path_label="auto"):
                        "verify_gbs": vbytes / g_ver / 1e9, "persist_gbs": pbytes / g_per / 1e9,
                        "nodes_per_s": T / (g_ver + g_per),
                        "timing": "graph replay of each call alone over the rotation (mean; spread in *_pct)",
-                       "eager": {"verify_us": t_ver * 1e6, "persist_us": t_per * 1e6, "plan_us": t_plan * 1e6}},
+                       "eager": ({"verify_us": t_ver * 1e6, "persist_us": t_per * 1e6, "plan_us": t_plan * 1e6}
+                                 if schedule == "separate" else
+                                 {"fused_us": float(np.mean(fu_ms)) * 1e3, "plan_us": t_plan * 1e6})},
         "roofline": roof,
     }
     if fused is not None:
@@ -479,7 +527,12 @@ def main():
     if args.seqs > 0:  # the same tree recipe at another batch size
         import dataclasses
         cfg = dataclasses.replace(cfg, num_seqs=args.seqs, num_slots=args.seqs)
-    res, ctx = measure(G, W, cfg, args, args.steps, args.warmup, distinct=args.distinct, path_label=args.path)
+    if args.schedule == "fused" and (not fused_supported(cfg) or args.path != "auto"):
+        print(json.dumps({"error": "--schedule fused needs bf16 inputs, head dim 64 or 128, trees of at most 32 "
+                                   "nodes and the default kernels; workload %s does not qualify" % cfg.name}))
+        sys.exit(2)
+    res, ctx = measure(G, W, cfg, args, args.steps, args.warmup, distinct=args.distinct, path_label=args.path,
+                       schedule=args.schedule)
     # calibration for memory-traffic counters: one plain device copy of a known size
     # (256 MiB read + 256 MiB written), outside the timed region
     cal_src = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -511,7 +564,7 @@ def main():
                                         ctx["slot_d"], args.accept_steps)
     if not args.no_draft and cfg.tree[0] == "ddtree":
         result["draft"] = bench_draft(G, W, cfg, args.accept_steps)
-    if not args.no_store_path and ctx["layers"] == 1:
+    if not args.no_store_path and ctx["layers"] == 1 and ctx["t_ver"] is not None:  # beside the two-call steps
         result["store_path"] = bench_store_path(G, cfg, ctx["dims"], ctx["sets"], ctx["slot_d"], ctx["acc_d"],
                                                 ctx["ws"], ctx["rotate"], args.accept_steps, ctx["vbytes"],
                                                 ctx["pbytes"], ctx["t_ver"], ctx["t_per"])

@@ -36,3 +36,22 @@ def test_rotation_bounds():
     for per_copy in (1e3, 1e6, 5e6, 1e8, 1e9):
         r = bench.rotation(per_copy, 1)
         assert 4 <= r <= 128 and (r == 128 or r * per_copy >= 512e6 or r == 4)
+
+
+def test_fused_schedule_takes_the_fused_kernels_workloads():
+    """--schedule fused is offered for the workloads the fused kernel runs (bf16, head
+    dim 64 or 128, trees of at most 32 nodes): the batched, chain and 23-node tree
+    workloads, not the 65-node stress trees or the fp32 tiny tree."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import workloads as W
+    assert [bench.fused_supported(W.get_config(n)) for n in ("tiny", "chain", "ddtree22", "batched", "stress")] == \
+        [False, True, True, True, False]
+    old = sys.argv
+    try:
+        sys.argv = ["bench.py", "--schedule", "fused"]
+        assert bench.parse().schedule == "fused"
+        sys.argv = ["bench.py"]
+        assert bench.parse().schedule == "separate"
+    finally:
+        sys.argv = old
