@@ -16,7 +16,9 @@
 // Replay (persist) needs S^m for one root-to-node path of <= 16 nodes: it
 // reads S0 once, forms S0 k_e for the path keys on the matrix cores, runs the
 // same recurrence per row and writes G_m S0 + sum_e R(m,e) c_e k_e^T in place
-// as a rank-16 update accumulated onto the scaled state.
+// as a rank-16 update accumulated onto the scaled state.  The fused persist + verify
+// runs both on one load of S: the replay's update in registers, stored in
+// place, then the next tree's products S K^T and S Q^T from the same registers.
 #include <algorithm>
 #include <atomic>
 #include <cstdlib>
