@@ -478,3 +478,74 @@ def test_fused_after_a_step_with_large_trees():
     assert G.gdn_tree_status(wsp)[0] == 0
     S1 = _expected_states(prev, S0, acc)
     _check_outputs(cfg, nxt, o_f, np.stack(S1), set(range(cfg.num_seqs)))
+
+
+def test_deferred_persist_decode_loop_over_four_steps():
+    """The decode loop the fused call is for, on one layer over four steps with new
+    trees, inputs and accepted nodes each step: step 0 verify; steps 1-3 fused (persist
+    of the step before + verify); a final plain persist.  Every step's outputs and the
+    final cache against the oracle's sequential loop (verify then persist per step),
+    and the final cache bitwise equal to the same loop run with the two calls."""
+    G = require_gpu()
+    base = dataclasses.replace(W.get_config("batched"), num_seqs=8, num_slots=10)
+    steps = [dataclasses.replace(base, index=300 + t) for t in range(4)]
+    trees = [W.make_trees(c) for c in steps]
+    data = [_step(c, tr, t) for t, (c, tr) in enumerate(zip(steps, trees))]
+    accs = [W.make_accepts(c, tr) for c, tr in zip(steps, trees)]
+    accs[1] = accs[1].copy()
+    accs[1][3] = -1  # a sequence that accepts nothing in one step
+    slots = W.make_slots(base)
+    S0 = oracle.initial_states(W.make_prefill(base, 0), base.num_v_heads, base.head_dim)
+    cache0 = np.random.default_rng(61).standard_normal((base.num_slots, base.num_v_heads, base.head_dim,
+                                                       base.head_dim)).astype(np.float32)
+    cache0[slots] = S0
+    # the oracle's loop
+    S = S0.astype(np.float64)
+    exp_out = []
+    for t in range(4):
+        exp_out.append(oracle.verify_batch(data[t]["trees"], data[t]["cu"], data[t]["inp"], S))
+        st = _expected_states(data[t], S, accs[t])
+        S = np.stack([st[s] if st[s] is not None else S[s] for s in range(base.num_seqs)])
+
+    def run(fused):
+        dims = [_dims(G, base, d, base.num_slots, 32) for d in data]
+        wss = [_plan(G, dm, d, slots) for dm, d in zip(dims, data)]
+        xs = [_dev_inputs(d) for d in data]
+        acc_d = [to_dev(a.astype(np.int32)) for a in accs]
+        sl = to_dev(slots.astype(np.int32))
+        cache = to_dev(cache0.copy())
+        outs = []
+        for t in range(4):
+            out = torch.zeros((int(data[t]["cu"][-1]), base.num_v_heads, base.head_dim), device="cuda")
+            x = xs[t]
+            if t == 0 or not fused:
+                if t > 0:
+                    p = xs[t - 1]
+                    G.gdn_tree_persist(dims[t - 1], p["k"], p["v"], p["a"], p["b"], acc_d[t - 1], cache, sl, wss[t - 1])
+                G.gdn_tree_verify(dims[t], x["q"], x["k"], x["v"], x["a"], x["b"], cache, sl, out, wss[t])
+            else:
+                p = xs[t - 1]
+                G.gdn_tree_persist_verify(dims[t - 1], p["k"], p["v"], p["a"], p["b"], acc_d[t - 1], wss[t - 1], dims[t],
+                                          x["q"], x["k"], x["v"], x["a"], x["b"], cache, sl, out, wss[t])
+            outs.append(out)
+        p = xs[3]
+        G.gdn_tree_persist(dims[3], p["k"], p["v"], p["a"], p["b"], acc_d[3], cache, sl, wss[3])
+        torch.cuda.synchronize()
+        for w_ in wss:
+            assert G.gdn_tree_status(w_)[0] == 0
+        return [o.cpu().numpy() for o in outs], cache.cpu().numpy()
+
+    print("deferred-persist decode loop", flush=True)
+    outs_f, cache_f = run(True)
+    outs_s, cache_s = run(False)
+    assert np.array_equal(cache_f.view(np.uint32), cache_s.view(np.uint32))
+    for t in range(4):
+        hv = base.num_v_heads
+        for s in range(base.num_seqs):
+            lo, hi = int(data[t]["cu"][s]), int(data[t]["cu"][s + 1])
+            e = slice_rel_err(outs_f[t][lo:hi].transpose(1, 0, 2).reshape(hv, -1),
+                              exp_out[t][lo:hi].transpose(1, 0, 2).reshape(hv, -1))
+            assert e <= TOL, (t, s, e)
+    for s in range(base.num_seqs):
+        assert slice_rel_err(cache_f[slots[s]].reshape(base.num_v_heads, -1),
+                             S[s].reshape(base.num_v_heads, -1)) <= TOL, s
