@@ -200,6 +200,10 @@ int gdn_tree_persist_verify(const gdn_dims *prev_dims, const void *prev_k, const
     if (dims->num_seqs > 0 && (!state_cache || !slot_idx || !accepted_node)) return GDN_ERR_NULL;
     if (prev_ws_bytes < gdn_workspace_bytes(prev_dims) || ws_bytes < gdn_workspace_bytes(dims))
         return GDN_ERR_WORKSPACE;
+    // Step t's plan and path records and step t+1's plan live side by side:
+    // one workspace for both would let one step's tables overwrite the other's.
+    const uintptr_t wp = reinterpret_cast<uintptr_t>(prev_ws), wn = reinterpret_cast<uintptr_t>(ws);
+    if (wp < wn + gdn_workspace_bytes(dims) && wn < wp + gdn_workspace_bytes(prev_dims)) return GDN_ERR_WORKSPACE;
     if (dims->num_seqs == 0) return GDN_OK;
     const bool fused = !recurrent_forced() && dims->total_nodes > 0 && prev_dims->total_nodes > 0 &&
                        gdn::fused_supported(dims->head_dim, dims->qkv_dtype, dims->max_nodes);

@@ -229,8 +229,10 @@ int gdn_tree_persist(const gdn_dims *dims, const void *k, const void *v, const f
  * slot_idx); state_cache is the one cache both steps address, written in
  * place.  The two dims must agree in num_seqs, heads, head_dim, num_slots and
  * qkv_dtype (GDN_ERR_SHAPE otherwise); total_nodes, max_nodes and max_depth
- * may differ.  Sequence b of one step is sequence b of the other; its slot in
- * each step is the one that step's plan recorded.
+ * may differ.  prev_ws and ws are two workspaces: their first
+ * gdn_workspace_bytes(prev_dims) and gdn_workspace_bytes(dims) bytes must not
+ * overlap (GDN_ERR_WORKSPACE otherwise).  Sequence b of one step is sequence b
+ * of the other; its slot in each step is the one that step's plan recorded.
  *
  * Results: out equals what gdn_tree_verify writes after gdn_tree_persist, to
  * within the verify's rounding (the products sum the state's columns in

@@ -117,14 +117,15 @@ def test_package_never_imports_the_oracle():
 def test_persist_verify_host_checks(lib):
     """gdn_tree_persist_verify's argument errors are reported before anything is
     enqueued: the two steps' dims must agree in batch, heads, head dim, slots and
-    dtype; required pointers; both workspaces large enough."""
+    dtype; required pointers; both workspaces large enough and apart."""
     import gated_deltanet_tree_amd as G
     one = ctypes.c_void_p(16)
     prev = G.make_dims(4, 60, 23, 2, 4, 64, 6, G.GDN_BF16)
     nxt = G.make_dims(4, 50, 20, 2, 4, 64, 6, G.GDN_BF16)   # node counts may differ
     n_p, n_n = G.workspace_bytes(prev), G.workspace_bytes(nxt)
+    far = ctypes.c_void_p(1 << 40)
 
-    def call(dp, dn, ws_p=one, nb_p=n_p, ws_n=one, nb_n=n_n, acc=one, out=one):
+    def call(dp, dn, ws_p=one, nb_p=n_p, ws_n=far, nb_n=n_n, acc=one, out=one):
         return lib.gdn_tree_persist_verify(ctypes.byref(dp) if dp is not None else None, one, one, one, one, acc,
                                            ws_p, nb_p, ctypes.byref(dn) if dn is not None else None, one, one, one,
                                            one, one, one, one, out, ws_n, nb_n, None)
@@ -144,6 +145,9 @@ def test_persist_verify_host_checks(lib):
     assert call(prev, nxt, out=None) == -1
     assert call(prev, nxt, nb_p=n_p - 1) == -4
     assert call(prev, nxt, nb_n=n_n - 1) == -4
+    assert call(prev, nxt, ws_n=one) == -4                            # one workspace for both steps
+    assert call(prev, nxt, ws_n=ctypes.c_void_p(16 + n_p - 256)) == -4  # step t+1's starts inside step t's
+    assert call(prev, nxt, ws_p=ctypes.c_void_p((1 << 40) + n_n - 256)) == -4
     empty = G.make_dims(0, 0, 1, 2, 4, 64, 0, G.GDN_BF16)
     n_e = G.workspace_bytes(empty)
     assert call(empty, empty, nb_p=n_e, nb_n=n_e) == 0  # nothing to do: returns before any launch
