@@ -16,6 +16,8 @@
 // contraction; every fused multiply-add is an explicit fmaf.
 #include <hip/hip_fp16.h>
 
+#include <type_traits>
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -53,6 +55,35 @@ __device__ __forceinline__ void load_cols(const Tin *base, int j, float (&x)[Geo
             const uint2 w = *reinterpret_cast<const uint2 *>(base + col);
             x[4 * c + 0] = bf16_lo(w.x); x[4 * c + 1] = bf16_hi(w.x);
             x[4 * c + 2] = bf16_lo(w.y); x[4 * c + 3] = bf16_hi(w.y);
+        }
+    }
+}
+
+// A lane's CPL columns of a length-D vector as loaded: bf16 stays packed two
+// to a register until unpack_cols, so a prefetched node costs half the
+// registers of its fp32 form.
+template <int D, typename Tin>
+struct RawCols {
+    using W = std::conditional_t<sizeof(Tin) == 4, float4, uint2>;
+    W w[Geo<D>::NCH];
+};
+
+template <int D, typename Tin>
+__device__ __forceinline__ void load_raw(const Tin *base, int j, RawCols<D, Tin> &r) {
+#pragma unroll
+    for (int c = 0; c < Geo<D>::NCH; ++c)
+        r.w[c] = *reinterpret_cast<const typename RawCols<D, Tin>::W *>(base + col_of<D>(j, c));
+}
+
+template <int D, typename Tin>
+__device__ __forceinline__ void unpack_cols(const RawCols<D, Tin> &r, float (&x)[Geo<D>::CPL]) {
+#pragma unroll
+    for (int c = 0; c < Geo<D>::NCH; ++c) {
+        if constexpr (sizeof(Tin) == 4) {
+            x[4 * c + 0] = r.w[c].x; x[4 * c + 1] = r.w[c].y; x[4 * c + 2] = r.w[c].z; x[4 * c + 3] = r.w[c].w;
+        } else {
+            x[4 * c + 0] = bf16_lo(r.w[c].x); x[4 * c + 1] = bf16_hi(r.w[c].x);
+            x[4 * c + 2] = bf16_lo(r.w[c].y); x[4 * c + 3] = bf16_hi(r.w[c].y);
         }
     }
 }
@@ -212,10 +243,10 @@ __global__ __launch_bounds__(64) void tree_verify_kernel(Params P) {
     load_state<D>(S0, t.j, S);
     int sp = 0;
 
-    float kn[G::CPL], qn[G::CPL];
+    RawCols<D, Tin> kn, qn;
     int node = s_order[0];
-    load_cols<D, Tin>(kbase + node * kq_stride, t.j, kn);
-    load_cols<D, Tin>(qbase + node * kq_stride, t.j, qn);
+    load_raw<D, Tin>(kbase + node * kq_stride, t.j, kn);
+    load_raw<D, Tin>(qbase + node * kq_stride, t.j, qn);
     float vn = load_one<Tin>(vbase + node * v_stride);
 
     for (int p = 0; p < n; ++p) {
@@ -223,13 +254,13 @@ __global__ __launch_bounds__(64) void tree_verify_kernel(Params P) {
         const float a = s_a[p], bb = s_b[p];
         const int cur = node;
         float k[G::CPL], q[G::CPL];
-#pragma unroll
-        for (int i = 0; i < G::CPL; ++i) { k[i] = kn[i]; q[i] = qn[i]; }
+        unpack_cols<D, Tin>(kn, k);
+        unpack_cols<D, Tin>(qn, q);
         const float v = vn;
         if (p + 1 < n) {  // prefetch the next node's inputs
             node = s_order[p + 1];
-            load_cols<D, Tin>(kbase + node * kq_stride, t.j, kn);
-            load_cols<D, Tin>(qbase + node * kq_stride, t.j, qn);
+            load_raw<D, Tin>(kbase + node * kq_stride, t.j, kn);
+            load_raw<D, Tin>(qbase + node * kq_stride, t.j, qn);
             vn = load_one<Tin>(vbase + node * v_stride);
         }
         // parent state
