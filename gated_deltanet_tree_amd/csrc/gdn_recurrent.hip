@@ -202,14 +202,16 @@ __device__ __forceinline__ Tile tile_of(const Params &P) {
 template <int D, typename Tin, bool STORE>
 __global__ __launch_bounds__(64) void tree_verify_kernel(Params P) {
     using G = Geo<D>;
-    extern __shared__ float4 lds_stack[];  // [stack_slots][NCH][64 lanes]
-    __shared__ int s_order[GDN_MAX_NODES];
-    __shared__ int s_act[GDN_MAX_NODES];
-    __shared__ float s_a[GDN_MAX_NODES];
-    __shared__ float s_b[GDN_MAX_NODES];
+    // [stack_slots][NCH][64 lanes] float4, then the preorder, actions and
+    // gates of up to max_nodes nodes; sized by tree_lds_bytes
+    extern __shared__ float4 lds_stack[];
+    int *s_order = reinterpret_cast<int *>(lds_stack + (size_t)P.stack_slots * G::NCH * 64);
+    int *s_act = s_order + P.max_nodes;
+    float *s_a = reinterpret_cast<float *>(s_act + P.max_nodes);
+    float *s_b = s_a + P.max_nodes;
 
     const Tile t = tile_of<D>(P);
-    if (!planned(P)) return;
+    if (!planned(P)) return;  // a planned workspace bounds every tree by max_nodes
     const int lo = P.ws.seq_info[t.b * kSeqInfoInts + 0];
     const int n = P.ws.seq_info[t.b * kSeqInfoInts + 1];
     const int status = P.ws.seq_status[t.b];
@@ -454,16 +456,22 @@ int grid_of(const Params &p) {
     return p.B * p.Hv * Geo<D>::SLICES;
 }
 
+// the tree kernel's LDS: its state stack and four per-node tables
+template <int D>
+size_t tree_lds_bytes(const Params &p) {
+    return (size_t)p.stack_slots * Geo<D>::NCH * 64 * sizeof(float4) + (size_t)4 * p.max_nodes * sizeof(int);
+}
+
 template <int D, typename Tin>
 hipError_t launch_tree_d(const Params &p, hipStream_t s) {
-    const size_t lds = (size_t)p.stack_slots * Geo<D>::NCH * 64 * sizeof(float4);
-    hipLaunchKernelGGL((tree_verify_kernel<D, Tin, false>), dim3(grid_of<D>(p)), dim3(64), lds, s, p);
+    hipLaunchKernelGGL((tree_verify_kernel<D, Tin, false>), dim3(grid_of<D>(p)), dim3(64), tree_lds_bytes<D>(p), s,
+                       p);
     return hipGetLastError();
 }
 template <int D, typename Tin>
 hipError_t launch_tree_store_d(const Params &p, hipStream_t s) {
-    const size_t lds = (size_t)p.stack_slots * Geo<D>::NCH * 64 * sizeof(float4);
-    hipLaunchKernelGGL((tree_verify_kernel<D, Tin, true>), dim3(grid_of<D>(p)), dim3(64), lds, s, p);
+    hipLaunchKernelGGL((tree_verify_kernel<D, Tin, true>), dim3(grid_of<D>(p)), dim3(64), tree_lds_bytes<D>(p), s,
+                       p);
     return hipGetLastError();
 }
 
