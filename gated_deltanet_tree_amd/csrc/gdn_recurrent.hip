@@ -167,6 +167,11 @@ __device__ __forceinline__ void update_row(float (&S)[CPL], const float (&k)[CPL
 
 __device__ __forceinline__ float qnan() { return __int_as_float(0x7fc00000); }
 
+// state stack entries the tree kernel keeps in LDS: all but the top
+__host__ __device__ __forceinline__ int lds_stack_entries(const Params &P) {
+    return P.stack_slots > 1 ? P.stack_slots - 1 : 0;
+}
+
 // the plan was made for these dims, including the stack size its preorder assumes
 __device__ __forceinline__ bool planned(const Params &P) {
     return ws_plan_matches(P) && P.ws.header[5] == P.stack_slots;
@@ -202,10 +207,11 @@ __device__ __forceinline__ Tile tile_of(const Params &P) {
 template <int D, typename Tin, bool STORE>
 __global__ __launch_bounds__(64) void tree_verify_kernel(Params P) {
     using G = Geo<D>;
-    // [stack_slots][NCH][64 lanes] float4, then the preorder, actions and
-    // gates of up to max_nodes nodes; sized by tree_lds_bytes
+    // The state stack's top entry is held in registers; the entries below it
+    // are [stack_slots - 1][NCH][64 lanes] float4 in LDS, followed by the
+    // preorder, actions and gates of up to max_nodes nodes (tree_lds_bytes).
     extern __shared__ float4 lds_stack[];
-    int *s_order = reinterpret_cast<int *>(lds_stack + (size_t)P.stack_slots * G::NCH * 64);
+    int *s_order = reinterpret_cast<int *>(lds_stack + (size_t)lds_stack_entries(P) * G::NCH * 64);
     int *s_act = s_order + P.max_nodes;
     float *s_a = reinterpret_cast<float *>(s_act + P.max_nodes);
     float *s_b = s_a + P.max_nodes;
@@ -243,6 +249,9 @@ __global__ __launch_bounds__(64) void tree_verify_kernel(Params P) {
 
     float S[G::CPL];
     load_state<D>(S0, t.j, S);
+    float top[G::CPL];  // the stack's top entry when sp > 0
+#pragma unroll
+    for (int i = 0; i < G::CPL; ++i) top[i] = 0.0f;
     int sp = 0;
 
     RawCols<D, Tin> kn, qn;
@@ -270,13 +279,16 @@ __global__ __launch_bounds__(64) void tree_verify_kernel(Params P) {
         if (kind == GDN_ACT_INIT) {
             if (p > 0) load_state<D>(S0, t.j, S);
         } else if (kind != GDN_ACT_CONTINUE && sp > 0) {  // the plan never restores from an empty stack
-            const float4 *src = lds_stack + (size_t)(sp - 1) * G::NCH * 64;
 #pragma unroll
-            for (int c = 0; c < G::NCH; ++c) {
-                const float4 f = src[c * 64 + t.lane];
-                S[4 * c + 0] = f.x; S[4 * c + 1] = f.y; S[4 * c + 2] = f.z; S[4 * c + 3] = f.w;
+            for (int i = 0; i < G::CPL; ++i) S[i] = top[i];
+            if (kind == GDN_ACT_POP && --sp > 0) {  // the entry below becomes the top
+                const float4 *src = lds_stack + (size_t)(sp - 1) * G::NCH * 64;
+#pragma unroll
+                for (int c = 0; c < G::NCH; ++c) {
+                    const float4 f = src[c * 64 + t.lane];
+                    top[4 * c + 0] = f.x; top[4 * c + 1] = f.y; top[4 * c + 2] = f.z; top[4 * c + 3] = f.w;
+                }
             }
-            if (kind == GDN_ACT_POP) --sp;
         }
         // node step
         const float u = group_sum<G::LPR>(lane_dot<G::CPL>(S, k));
@@ -293,10 +305,15 @@ __global__ __launch_bounds__(64) void tree_verify_kernel(Params P) {
                 store_state_f16<D>(P.node_states + (((size_t)(lo + cur) * P.Hv + t.h) * D + t.row) * D, t.j, S);
             if ((act & GDN_ACT_PUSH) && sp < P.stack_slots) {  // the plan's order never exceeds the bound
                 __syncthreads();
-                float4 *dst = lds_stack + (size_t)sp * G::NCH * 64;
+                if (sp > 0) {  // the old top moves to LDS entry sp - 1 <= stack_slots - 2
+                    float4 *dst = lds_stack + (size_t)(sp - 1) * G::NCH * 64;
 #pragma unroll
-                for (int c4 = 0; c4 < G::NCH; ++c4)
-                    dst[c4 * 64 + t.lane] = make_float4(S[4 * c4 + 0], S[4 * c4 + 1], S[4 * c4 + 2], S[4 * c4 + 3]);
+                    for (int c4 = 0; c4 < G::NCH; ++c4)
+                        dst[c4 * 64 + t.lane] =
+                            make_float4(top[4 * c4 + 0], top[4 * c4 + 1], top[4 * c4 + 2], top[4 * c4 + 3]);
+                }
+#pragma unroll
+                for (int i = 0; i < G::CPL; ++i) top[i] = S[i];
                 ++sp;
                 __syncthreads();
             }
@@ -456,10 +473,10 @@ int grid_of(const Params &p) {
     return p.B * p.Hv * Geo<D>::SLICES;
 }
 
-// the tree kernel's LDS: its state stack and four per-node tables
+// the tree kernel's LDS: the stack entries below the top and four per-node tables
 template <int D>
 size_t tree_lds_bytes(const Params &p) {
-    return (size_t)p.stack_slots * Geo<D>::NCH * 64 * sizeof(float4) + (size_t)4 * p.max_nodes * sizeof(int);
+    return (size_t)lds_stack_entries(p) * Geo<D>::NCH * 64 * sizeof(float4) + (size_t)4 * p.max_nodes * sizeof(int);
 }
 
 template <int D, typename Tin>
