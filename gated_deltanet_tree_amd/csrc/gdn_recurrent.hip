@@ -1,5 +1,6 @@
 // gdn_recurrent.hip -- recurrent kernels: chain verify, tree verify (depth-first
-// with a state stack in LDS) and accepted-path persist.
+// with a state stack: its top in registers, the rest in LDS) and accepted-path
+// persist.
 //
 // One 64-lane workgroup owns one (sequence, value head, slice of RPW state
 // rows).  Each state row of D fp32 values is spread over LPR lanes (LPR*4
@@ -199,7 +200,8 @@ __device__ __forceinline__ Tile tile_of(const Params &P) {
 
 // ---------------------------------------------------------------------------
 // Tree verify: walk the plan's preorder, keep the state in VGPRs, save
-// states that later siblings need on an LDS stack.  STORE also writes every
+// states that later siblings need on a stack (top entry in VGPRs, the rest in
+// LDS).  STORE also writes every
 // node's state (leaves included) in fp16 to P.node_states: the pages' own
 // tree path, which keeps per-node states for the later commit (GreenGames
 // page, "Key wins": the f16 intermediate cache).
